@@ -1,0 +1,184 @@
+"""fp64 CPU oracle for the (Complex) Kimi Delta Attention recurrence.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+benchmark's CPU-baseline leg import this package.  The GPU library never
+imports, links or calls it, and the two share no code.
+
+The arithmetic lives in ``ckda_oracle.c`` (plain C, fp64, OpenMP across the
+independent (batch, head) recurrences); this module only compiles it with gcc
+and marshals numpy arrays into it.  Inputs are handed over as raw element
+bytes exactly as the GPU receives them: ``float32``, ``float64``, or
+``uint16`` arrays holding bf16 bit patterns.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ckda_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libckda_oracle.so")
+
+F32, BF16, F64 = 0, 1, 2
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile ckda_oracle.c into libckda_oracle.so with gcc (-O2, OpenMP)."""
+    global _lib
+    if not force and os.path.exists(_LIB_PATH):
+        return _LIB_PATH
+    tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
+           "-Wall", "-Wextra", _SRC, "-o", tmp, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB_PATH)
+    _lib = None
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build()
+        lib = ctypes.CDLL(_LIB_PATH)
+        vp, i = ctypes.c_void_p, ctypes.c_int
+        lib.ckda_oracle_fwd.argtypes = [vp, vp, vp, vp, vp, i, vp, i, vp, vp,
+                                        i, i, i, i, i, i]
+        lib.ckda_oracle_fwd.restype = i
+        lib.ckda_oracle_decode.argtypes = [vp, vp, vp, vp, vp, i, vp, vp,
+                                           i, i, i, i, i]
+        lib.ckda_oracle_decode.restype = i
+        lib.ckda_oracle_num_threads.argtypes = []
+        lib.ckda_oracle_num_threads.restype = i
+        _lib = lib
+    return _lib
+
+
+def _code(a: np.ndarray) -> int:
+    if a.dtype == np.float32:
+        return F32
+    if a.dtype == np.float64:
+        return F64
+    if a.dtype == np.uint16:
+        return BF16
+    raise TypeError(f"oracle inputs must be float32, float64 or uint16(bf16 bits), got {a.dtype}")
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def num_threads() -> int:
+    return _load().ckda_oracle_num_threads()
+
+
+def fwd(q, k, v, alpha, beta, h0=None, want_o=True, nthreads=0):
+    """Sequential fp64 forward.
+
+    q, k, alpha: [B,H,T,dk]; v: [B,H,T,dv]; beta: [B,H,T]; all one dtype.
+    h0: [B,H,dk,dv] float32 or float64, or None for a zero state.
+    Returns (o [B,H,T,dv] float64 or None, hT [B,H,dk,dv] float64).
+    """
+    q, k, v, alpha, beta = (np.ascontiguousarray(x) for x in (q, k, v, alpha, beta))
+    code = _code(q)
+    for x in (k, v, alpha, beta):
+        if _code(x) != code:
+            raise TypeError("q, k, v, alpha, beta must share one dtype")
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    if k.shape != q.shape or alpha.shape != q.shape or v.shape != (B, H, T, dv) \
+            or beta.shape != (B, H, T):
+        raise ValueError("inconsistent shapes")
+    h0c, h0code = None, F32
+    if h0 is not None:
+        h0c = np.ascontiguousarray(h0)
+        if h0c.shape != (B, H, dk, dv):
+            raise ValueError("h0 shape")
+        h0code = _code(h0c)
+        if h0code == BF16:
+            raise TypeError("h0 must be float32 or float64")
+    o = np.empty((B, H, T, dv), np.float64) if want_o else None
+    hT = np.empty((B, H, dk, dv), np.float64)
+    rc = _load().ckda_oracle_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), code,
+                                 _ptr(h0c), h0code, _ptr(o), _ptr(hT),
+                                 B, H, T, dk, dv, int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"ckda_oracle_fwd failed with code {rc}")
+    return o, hT
+
+
+def decode(q, k, v, alpha, beta, S, nthreads=0):
+    """One recurrent step applied in place to the fp64 state S [N,H,dk,dv].
+
+    q, k, alpha: [N,H,dk]; v: [N,H,dv]; beta: [N,H].  Returns o [N,H,dv] float64.
+    """
+    q, k, v, alpha, beta = (np.ascontiguousarray(x) for x in (q, k, v, alpha, beta))
+    code = _code(q)
+    for x in (k, v, alpha, beta):
+        if _code(x) != code:
+            raise TypeError("q, k, v, alpha, beta must share one dtype")
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    if not (isinstance(S, np.ndarray) and S.dtype == np.float64 and S.flags.c_contiguous
+            and S.shape == (N, H, dk, dv)):
+        raise ValueError("S must be a C-contiguous float64 [N,H,dk,dv] array")
+    if k.shape != q.shape or alpha.shape != q.shape or v.shape != (N, H, dv) \
+            or beta.shape != (N, H):
+        raise ValueError("inconsistent shapes")
+    o = np.empty((N, H, dv), np.float64)
+    rc = _load().ckda_oracle_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), code,
+                                    _ptr(S), _ptr(o), N, H, dk, dv, int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"ckda_oracle_decode failed with code {rc}")
+    return o
+
+
+class Variant:
+    """An oracle bound to another build of ckda_oracle.c (same ABI).
+
+    Used only by the mutation tests, which compile deliberately broken copies
+    of the source to show that the pins catch each planted mistake."""
+
+    def __init__(self, lib_path: str):
+        self._path = lib_path
+
+    def _swap(self, fn, *a, **kw):
+        global _lib
+        saved = _lib
+        lib = ctypes.CDLL(self._path)
+        vp, i = ctypes.c_void_p, ctypes.c_int
+        lib.ckda_oracle_fwd.argtypes = [vp, vp, vp, vp, vp, i, vp, i, vp, vp, i, i, i, i, i, i]
+        lib.ckda_oracle_fwd.restype = i
+        lib.ckda_oracle_decode.argtypes = [vp, vp, vp, vp, vp, i, vp, vp, i, i, i, i, i]
+        lib.ckda_oracle_decode.restype = i
+        _lib = lib
+        try:
+            return fn(*a, **kw)
+        finally:
+            _lib = saved
+
+    def fwd(self, *a, **kw):
+        return self._swap(fwd, *a, **kw)
+
+    def decode(self, *a, **kw):
+        return self._swap(decode, *a, **kw)
+
+
+def build_variant(source_text: str, out_path: str) -> "Variant":
+    """Compile a modified copy of the oracle source (mutation tests only)."""
+    src = out_path + ".c"
+    with open(src, "w") as f:
+        f.write(source_text)
+    subprocess.run(["gcc", "-O1", "-std=c11", "-fopenmp", "-fPIC", "-shared", src, "-o", out_path, "-lm"],
+                   check=True)
+    return Variant(out_path)
+
+
+def source() -> str:
+    with open(_SRC) as f:
+        return f.read()

@@ -1,0 +1,172 @@
+/*
+ * ckda_oracle.c -- plain sequential fp64 CPU oracle for the (Complex) Kimi
+ * Delta Attention recurrence.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the correctness reference that the
+ * GPU library is checked against.  Only the test suite, the smoke check and
+ * the benchmark's CPU-baseline leg load it.  It shares no source, header,
+ * table or helper with the GPU library, and the GPU library never calls it.
+ *
+ * What it computes (one head, one sequence; heads are independent states that
+ * receive the same layer input -- "Complex KDA" paper, App. B.2, paragraph
+ * "Heads and layers"):
+ *
+ *   H_t = (I - beta_t k_t k_t^T) Diag(alpha_t) H_{t-1} + beta_t k_t v_t^T
+ *   o_t = H_t^T q_t                       (read-out of the post-update state)
+ *
+ * ("Complex KDA" discussion slides, frame "CKDA keeps the original
+ * gate--delta--readout structure", Eq. (1) of the paper; App. B.2, Eq. (9).)
+ *
+ * It is evaluated in the gate / read / compare / correct order of the KDA
+ * course lesson (session 17, "Mechanism map" and "Worked case -- full trace",
+ * part B):
+ *
+ *   Hbar = Diag(alpha_t) H_{t-1}          row i (key channel i) times alpha_t[i]
+ *   s    = Hbar^T k_t                     the state's current prediction for k_t
+ *   H_t  = Hbar + beta_t k_t (v_t - s)^T  delta correction
+ *
+ * which is the same matrix as the first form: (I - b k k^T) Hbar + b k v^T
+ * = Hbar + b k (v - Hbar^T k)^T.  The state is n x d_v with row i = key
+ * channel i.  No log-space, no sign handling, no chunking: alpha is applied
+ * as the signed real number it is (negative and zero gates included, App. B.2
+ * "These theoretical ranges include their endpoints and zero gates").  No
+ * query scaling and no key normalisation are applied; inputs are used exactly
+ * as given (bf16 and fp32 inputs are widened exactly to fp64).
+ *
+ * Parallel only across the independent (batch, head) recurrences (OpenMP).
+ *
+ * Layouts (C order): q, k, alpha [B,H,T,dk]; v [B,H,T,dv]; beta [B,H,T];
+ * h0 [B,H,dk,dv]; o [B,H,T,dv]; hT [B,H,dk,dv].
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { ORACLE_F32 = 0, ORACLE_BF16 = 1, ORACLE_F64 = 2 };
+
+/* Widen element i of a raw buffer of the given dtype to double (exact). */
+static double widen(const void* base, long long i, int dtype) {
+  if (dtype == ORACLE_F64) return ((const double*)base)[i];
+  if (dtype == ORACLE_F32) return (double)((const float*)base)[i];
+  /* bf16: the upper 16 bits of an IEEE binary32 */
+  uint32_t bits = (uint32_t)((const uint16_t*)base)[i] << 16;
+  float f;
+  memcpy(&f, &bits, sizeof f);
+  return (double)f;
+}
+
+static int valid_dtype(int d) { return d == ORACLE_F32 || d == ORACLE_BF16 || d == ORACLE_F64; }
+
+/* One recurrence step on a dk x dv fp64 state S (row-major, row = key channel).
+ * a, kk, qq: length dk; vv: length dv; s: scratch length dv; out: length dv. */
+static void step(double* S, const double* a, const double* kk, const double* qq,
+                 const double* vv, double b, double* s, double* out, int dk, int dv) {
+  /* gate: Hbar = Diag(alpha) H */
+  for (int i = 0; i < dk; ++i)
+    for (int j = 0; j < dv; ++j) S[(long)i * dv + j] *= a[i];
+  /* read: s = Hbar^T k */
+  for (int j = 0; j < dv; ++j) s[j] = 0.0;
+  for (int i = 0; i < dk; ++i)
+    for (int j = 0; j < dv; ++j) s[j] += S[(long)i * dv + j] * kk[i];
+  /* correct: H = Hbar + beta k (v - s)^T */
+  for (int i = 0; i < dk; ++i)
+    for (int j = 0; j < dv; ++j) S[(long)i * dv + j] += b * kk[i] * (vv[j] - s[j]);
+  /* query the updated state: o = H^T q */
+  if (out) {
+    for (int j = 0; j < dv; ++j) out[j] = 0.0;
+    for (int i = 0; i < dk; ++i)
+      for (int j = 0; j < dv; ++j) out[j] += S[(long)i * dv + j] * qq[i];
+  }
+}
+
+/* Full-sequence forward.  h0 may be NULL (zero initial state); its dtype is
+ * h0_dtype (F32 or F64).  o may be NULL (outputs not wanted); hT may be NULL.
+ * Returns 0 on success, nonzero on bad arguments or allocation failure. */
+int ckda_oracle_fwd(const void* q, const void* k, const void* v, const void* alpha,
+                    const void* beta, int dtype, const void* h0, int h0_dtype,
+                    double* o, double* hT, int B, int H, int T, int dk, int dv,
+                    int nthreads) {
+  if (!q || !k || !v || !alpha || !beta) return 1;
+  if (B < 0 || H < 0 || T < 0 || dk <= 0 || dv <= 0) return 2;
+  if (!valid_dtype(dtype) || (h0 && !valid_dtype(h0_dtype))) return 3;
+  long long BH = (long long)B * H;
+  int failed = 0;
+#ifdef _OPENMP
+  int nt = nthreads > 0 ? nthreads : omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : failed) num_threads(nt)
+#else
+  (void)nthreads;
+#endif
+  for (long long bh = 0; bh < BH; ++bh) {
+    double* S = (double*)malloc(sizeof(double) * (size_t)dk * dv);
+    double* buf = (double*)malloc(sizeof(double) * (size_t)(3 * dk + 3 * dv));
+    if (!S || !buf) { free(S); free(buf); failed |= 1; continue; }
+    double *a = buf, *kk = a + dk, *qq = kk + dk, *vv = qq + dk, *s = vv + dv, *ot = s + dv;
+    long long sbase = bh * (long long)dk * dv;
+    for (long long e = 0; e < (long long)dk * dv; ++e)
+      S[e] = h0 ? widen(h0, sbase + e, h0_dtype) : 0.0;
+    for (int t = 0; t < T; ++t) {
+      long long tk = (bh * T + t) * (long long)dk, tv = (bh * T + t) * (long long)dv;
+      for (int i = 0; i < dk; ++i) {
+        a[i] = widen(alpha, tk + i, dtype);
+        kk[i] = widen(k, tk + i, dtype);
+        qq[i] = widen(q, tk + i, dtype);
+      }
+      for (int j = 0; j < dv; ++j) vv[j] = widen(v, tv + j, dtype);
+      double b = widen(beta, bh * T + t, dtype);
+      step(S, a, kk, qq, vv, b, s, o ? ot : NULL, dk, dv);
+      if (o) memcpy(o + tv, ot, sizeof(double) * dv);
+    }
+    if (hT) memcpy(hT + sbase, S, sizeof(double) * (size_t)dk * dv);
+    free(S);
+    free(buf);
+  }
+  return failed ? 4 : 0;
+}
+
+/* Single-token step for N sequences x H heads, state updated in place.
+ * q, k, alpha [N,H,dk]; v [N,H,dv]; beta [N,H]; S_inout [N,H,dk,dv] fp64;
+ * o [N,H,dv] fp64 (may be NULL).  Applies exactly the step above. */
+int ckda_oracle_decode(const void* q, const void* k, const void* v, const void* alpha,
+                       const void* beta, int dtype, double* S_inout, double* o,
+                       int N, int H, int dk, int dv, int nthreads) {
+  if (!q || !k || !v || !alpha || !beta || !S_inout) return 1;
+  if (N < 0 || H < 0 || dk <= 0 || dv <= 0) return 2;
+  if (!valid_dtype(dtype)) return 3;
+  long long NH = (long long)N * H;
+  int failed = 0;
+#ifdef _OPENMP
+  int nt = nthreads > 0 ? nthreads : omp_get_max_threads();
+#pragma omp parallel for schedule(static) reduction(| : failed) num_threads(nt)
+#else
+  (void)nthreads;
+#endif
+  for (long long nh = 0; nh < NH; ++nh) {
+    double* buf = (double*)malloc(sizeof(double) * (size_t)(3 * dk + 3 * dv));
+    if (!buf) { failed |= 1; continue; }
+    double *a = buf, *kk = a + dk, *qq = kk + dk, *vv = qq + dk, *s = vv + dv, *ot = s + dv;
+    for (int i = 0; i < dk; ++i) {
+      a[i] = widen(alpha, nh * dk + i, dtype);
+      kk[i] = widen(k, nh * dk + i, dtype);
+      qq[i] = widen(q, nh * dk + i, dtype);
+    }
+    for (int j = 0; j < dv; ++j) vv[j] = widen(v, nh * dv + j, dtype);
+    double b = widen(beta, nh, dtype);
+    step(S_inout + nh * (long long)dk * dv, a, kk, qq, vv, b, s, o ? ot : NULL, dk, dv);
+    if (o) memcpy(o + nh * dv, ot, sizeof(double) * dv);
+    free(buf);
+  }
+  return failed ? 4 : 0;
+}
+
+int ckda_oracle_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}

@@ -1,0 +1,80 @@
+"""Each plausible slip planted in a copy of the oracle (on the CPU) must fail at
+least one pin.  This shows the pins constrain every part of the step: the
+order gate -> read -> correct -> query, the sign and weight of the correction,
+the row/column role of the gate, and the signed gates."""
+import pytest
+
+import oracle
+import test_oracle_pins as pins
+
+ORIG_GATE = "S[(long)i * dv + j] *= a[i];"
+ORIG_READ = "s[j] += S[(long)i * dv + j] * kk[i];"
+ORIG_CORR = "S[(long)i * dv + j] += b * kk[i] * (vv[j] - s[j]);"
+
+MUTANTS = {
+    # query the state before the update
+    "readout_before_update": [("  /* gate: Hbar = Diag(alpha) H */",
+                               "  if (out) { for (int j = 0; j < dv; ++j) { out[j] = 0.0; "
+                               "for (int i = 0; i < dk; ++i) out[j] += S[(long)i * dv + j] * qq[i]; } }\n"
+                               "  /* gate: Hbar = Diag(alpha) H */"),
+                              ("  if (out) {\n    for (int j = 0; j < dv; ++j) out[j] = 0.0;",
+                               "  if (0) {\n    for (int j = 0; j < dv; ++j) out[j] = 0.0;")],
+    # apply the gate after the correction instead of before it
+    "gate_after_correction": [(ORIG_GATE, "(void)0;"),
+                              ("  /* query the updated state: o = H^T q */",
+                               "  for (int i = 0; i < dk; ++i) for (int j = 0; j < dv; ++j) "
+                               "S[(long)i * dv + j] *= a[i];\n  /* query the updated state: o = H^T q */")],
+    "correction_sign_flipped": [(ORIG_CORR, "S[(long)i * dv + j] -= b * kk[i] * (vv[j] - s[j]);")],
+    "beta_dropped": [(ORIG_CORR, "S[(long)i * dv + j] += kk[i] * (vv[j] - s[j]);")],
+    "beta_squared": [(ORIG_CORR, "S[(long)i * dv + j] += b * b * kk[i] * (vv[j] - s[j]);")],
+    "gate_on_columns": [(ORIG_GATE, "S[(long)i * dv + j] *= a[j % dk];")],
+    "gate_sign_dropped": [(ORIG_GATE, "S[(long)i * dv + j] *= fabs(a[i]);")],
+    "read_before_gate": [(ORIG_GATE, "(void)0;"),
+                         ("  /* correct: H = Hbar + beta k (v - s)^T */",
+                          "  for (int i = 0; i < dk; ++i) for (int j = 0; j < dv; ++j) "
+                          "S[(long)i * dv + j] *= a[i];\n  /* correct: H = Hbar + beta k (v - s)^T */")],
+    "prediction_with_query": [(ORIG_READ, "s[j] += S[(long)i * dv + j] * qq[i];")],
+    "value_not_subtracted": [(ORIG_CORR, "S[(long)i * dv + j] += b * kk[i] * vv[j];")],
+    "query_reads_gated_state": [("      for (int j = 0; j < dv; ++j) out[j] += S[(long)i * dv + j] * qq[i];",
+                                 "      for (int j = 0; j < dv; ++j) out[j] += (S[(long)i * dv + j] - b * kk[i] * "
+                                 "(vv[j] - s[j])) * qq[i];")],
+}
+
+PIN_CALLS = [
+    lambda o: pins.test_worked_trace_decay(o),
+    lambda o: pins.test_worked_trace_of_one(o),
+    lambda o: pins.test_worked_trace_write(o),
+    lambda o: pins.test_two_reflections_make_rotation(o),
+    lambda o: pins.test_one_step_modular_counter(o, 3),
+    lambda o: pins.test_eq2_planar_transition(o, -0.7, 0.3),
+    lambda o: pins.test_eq3_diagonal_as_axis_householders(o),
+    lambda o: pins.test_transitions_non_expansive_and_spectrum(o),
+    lambda o: pins.test_brute_force_tiny(o, 1),
+    lambda o: pins.test_brute_force_tiny(o, 2),
+    lambda o: pins.test_exact_retrieval_at_beta_one(o),
+    lambda o: pins.test_pure_decay_at_beta_zero(o),
+    lambda o: pins.test_gauge_sign_absorption(o),
+]
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    src = oracle.source()
+    for old, new in MUTANTS[name]:
+        assert old in src, (name, old)
+        src = src.replace(old, new, 1)
+    mutant = oracle.build_variant(src, str(tmp_path / f"libmut_{name}.so"))
+    caught = 0
+    for call in PIN_CALLS:
+        try:
+            call(mutant)
+        except AssertionError:
+            caught += 1
+    assert caught > 0, f"mutant {name} passed every pin"
+
+
+def test_unmutated_copy_passes(tmp_path):
+    """Control: the same harness on an unmodified copy passes every pin."""
+    clean = oracle.build_variant(oracle.source(), str(tmp_path / "libclean.so"))
+    for call in PIN_CALLS:
+        call(clean)
