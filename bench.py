@@ -1,0 +1,221 @@
+#!/usr/bin/env python3
+"""Benchmark of the CKDA hot path on one MI355X.
+
+One step = one chunkwise forward of the ckda_bf16 workload (B4 H16 T4096,
+d_k = d_v = 128, chunk 64, full CKDA gate ranges, h0 ~ N(0, 0.1)): gate sign
+and magnitude split, Gram matrices, triangular solve, state pass and output,
+plus the final state.  The decode step (256 sequences x 32 heads, d128, fp32
+state updated in place) is timed in the same run and reported under "decode".
+
+Prints ONE JSON line.  `value` is tokens/s of the forward (a token is one
+(batch, position) across all heads), inputs resident in HBM, timed with HIP
+events on the stream the kernels run on; `ms_per_step` is the wall time of the
+K timed steps (synchronised on both sides) divided by K.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix cores, TFLOP/s
+METRIC = "CKDA chunkwise fwd tokens/s (B4 H16 T4096 d128, %MFMA) + decode state GB/s"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--decode-steps", type=int, default=128)
+    p.add_argument("--workload", default="ckda_bf16",
+                   help="forward workload name (default: the headline ckda_bf16)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-sample-tokens", type=int, default=0,
+                   help="tokens per head the oracle runs on (0 = choose ~15 s of work)")
+    return p.parse_args()
+
+
+def fwd_algorithmic(w):
+    """Algorithmic HBM bytes and matrix-core flops of one chunkwise forward.
+    Bytes: q, k, alpha, v read, o written ((3 dk + 2 dv + 1) elements per
+    token-head, beta included), plus the state read (h0) and written (hT).
+    Flops: 6 dk dv + 3 C dk + 2 C dv per token-head (the products W H, Q H,
+    KR U at 2 dk dv each; the Gram matrices A, M and T (beta K) at ~C dk each;
+    T (beta V) and M U at ~C dv each; triangles counted once)."""
+    es = 2 if w.dtype == "bf16" else 4
+    th = w.B * w.H * w.T
+    state = w.B * w.H * w.dk * w.dv * 4 * (2 if w.h0 == "normal" else 1)
+    nbytes = th * (3 * w.dk + 2 * w.dv + 1) * es + state
+    flops = th * (6 * w.dk * w.dv + 3 * w.chunk * w.dk + 2 * w.chunk * w.dv)
+    return nbytes, flops
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
+                          "(heads and decode states shard across GPUs without exchange, "
+                          "but no multi-GPU path is built)"}))
+        return 2
+
+    import numpy as np
+    import torch
+
+    import gated_delta_rule_ckda_amd as ck
+    from gated_delta_rule_ckda_amd import inputs as gen
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = gen.WORKLOADS[a.workload]
+    log = lambda m: print(m, file=sys.stderr, flush=True)
+    log(f"[bench] generating {w}")
+    inp = gen.make_inputs(w)
+    d = {k: (None if v is None else v.to(dev)) for k, v in inp.items()}
+    ws = torch.empty(ck.workspace_size(w.B, w.H, w.T, w.dk, w.dv, w.chunk, ck.DTYPE_BF16 if w.dtype == "bf16"
+                                       else ck.DTYPE_F32), dtype=torch.uint8, device=dev)
+    o = torch.empty((w.B, w.H, w.T, w.dv), dtype=d["q"].dtype, device=dev)
+    hT = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device=dev)
+
+    def step():
+        ck.chunk_fwd(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["h0"], chunk=w.chunk,
+                     workspace=ws, o=o, hT=hT)
+
+    log(f"[bench] warmup {a.warmup}")
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(a.steps)]
+    log(f"[bench] timing {a.steps} forward steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(a.steps):
+        ev[s][0].record(stream)
+        step()
+        ev[s][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_call_ms = [e0.elapsed_time(e1) for e0, e1 in ev]
+    call_ms = float(np.mean(per_call_ms))
+    call_ms_median = float(np.median(per_call_ms))
+    ms_per_step = wall * 1e3 / a.steps
+    tokens = w.B * w.T
+    value = tokens / (ms_per_step * 1e-3)
+    nbytes, flops = fwd_algorithmic(w)
+    achieved_gbs = nbytes / (call_ms * 1e-3) / 1e9
+    achieved_tflops = flops / (call_ms * 1e-3) / 1e12
+
+    # ---- decode: 256 x 32 states, fp32 128x128 each, updated in place
+    dec = gen.DECODE
+    log(f"[bench] decode {dec}")
+    S = gen.decode_state(dec).to(dev)
+    dsteps = [gen.decode_step_inputs(s % 8, dec) for s in range(8)]
+    dsteps = [{k: v.to(dev) for k, v in x.items()} for x in dsteps]
+    do = torch.empty((dec.N, dec.H, dec.dv), dtype=torch.bfloat16, device=dev)
+
+    def dstep(s):
+        x = dsteps[s % 8]
+        ck.decode_step(x["q"], x["k"], x["v"], x["alpha"], x["beta"], S, o=do)
+
+    for s in range(a.warmup):
+        dstep(s)
+    torch.cuda.synchronize()
+    dev_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(a.decode_steps)]
+    t1 = time.perf_counter()
+    for s in range(a.decode_steps):
+        dev_ev[s][0].record(stream)
+        dstep(s)
+        dev_ev[s][1].record(stream)
+    torch.cuda.synchronize()
+    dwall = time.perf_counter() - t1
+    dms = [e0.elapsed_time(e1) for e0, e1 in dev_ev]
+    dec_ms = float(np.mean(dms))
+    state_bytes = dec.N * dec.H * dec.dk * dec.dv * 4 * 2
+    io_bytes = dec.N * dec.H * (3 * dec.dk + 2 * dec.dv + 1) * 2
+    dec_gbs_state = state_bytes / (dec_ms * 1e-3) / 1e9
+    dec_gbs_total = (state_bytes + io_bytes) / (dec_ms * 1e-3) / 1e9
+
+    # ---- reference device copy of the decode state's size (practical ceiling)
+    src = torch.empty(dec.N * dec.H * dec.dk * dec.dv, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    ce0, ce1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ce0.record(stream)
+    for _ in range(10):
+        dst.copy_(src)
+    ce1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 2 * src.numel() * 4 / (ce0.elapsed_time(ce1) / 10 * 1e-3) / 1e9
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "dk": w.dk, "dv": w.dv,
+                   "chunk": w.chunk, "gates": w.gates, "h0": w.h0},
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "ckda_chunk_fwd (chunk_prep_kernel + chunk_state_kernel)",
+            "achieved": round(achieved_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "algorithmic_bytes": nbytes,
+            "call_ms_mean": round(call_ms, 4),
+            "call_ms_median": round(call_ms_median, 4),
+            "mfma_algorithmic_tflops": round(achieved_tflops, 2),
+            "mfma_frac_of_bf16_peak": round(achieved_tflops / BF16_PEAK_TFLOPS, 4),
+        },
+        "decode": {
+            "workload": dec.name, "steps": a.decode_steps,
+            "ms_per_step_events": round(dec_ms, 4),
+            "ms_per_step_wall": round(dwall * 1e3 / a.decode_steps, 4),
+            "state_GB_s": round(dec_gbs_state, 1),
+            "total_GB_s": round(dec_gbs_total, 1),
+            "frac_of_hbm_peak": round(dec_gbs_total / HBM_PEAK_GBS, 4),
+            "device_copy_GB_s": round(copy_gbs, 1),
+        },
+    }
+
+    if not a.no_cpu_baseline:
+        import oracle
+        from gated_delta_rule_ckda_amd.inputs import raw
+        T_s = a.cpu_sample_tokens or min(w.T, 1024)
+        sl = lambda t: t[:, :, :T_s].contiguous()
+        args = [raw(sl(inp[n])) for n in ("q", "k", "v", "alpha", "beta")]
+        h0 = None if inp["h0"] is None else raw(inp["h0"])
+        nt = oracle.num_threads()
+        log(f"[bench] oracle cpu baseline: {w.B}x{w.H} heads x {T_s} tokens, {nt} threads")
+        c0 = time.perf_counter()
+        oracle.fwd(*args, h0=h0)
+        csec = time.perf_counter() - c0
+        out["cpu_baseline"] = {"value": round(w.B * T_s / csec, 1), "unit": "tokens/s", "cores": nt,
+                               "kind": "oracle",
+                               "sample": f"{w.name} first {T_s} of {w.T} positions, all {w.B * w.H} heads, "
+                                         f"{csec:.2f} s"}
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,138 @@
+"""MI355X (gfx950) CKDA / KDA kernels: Python binding of the C ABI in include/ckda.h.
+
+Only argument marshalling happens here: torch supplies device memory and the
+current HIP stream, and every step of the computation runs in the HIP
+kernels of libckda.so.  There is no fallback: if the library is missing or
+fails to load, every call raises.
+
+    o, hT = chunk_fwd(q, k, v, alpha, beta, h0=None, chunk=64)
+    o = decode_step(q, k, v, alpha, beta, H)          # H updated in place
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libckda.so")
+
+DTYPE_F32, DTYPE_BF16 = 0, 1
+STATUS = {0: "CKDA_OK", 1: "CKDA_ERR_NULL", 2: "CKDA_ERR_DIM", 3: "CKDA_ERR_UNSUPPORTED",
+          4: "CKDA_ERR_ALIAS", 5: "CKDA_ERR_WORKSPACE", 6: "CKDA_ERR_HIP"}
+EXPORTS = ("ckda_chunk_fwd_workspace_size", "ckda_chunk_fwd", "ckda_decode_step",
+           "ckda_status_string", "ckda_last_error", "ckda_abi_version")
+
+_lib = None
+
+
+class CkdaError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{STATUS.get(status, status)}: {detail}")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libckda.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with gated_delta_rule_ckda_amd/build.py "
+                               "(or __graft_entry__.build())")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+        L.ckda_chunk_fwd_workspace_size.argtypes = [i] * 7
+        L.ckda_chunk_fwd_workspace_size.restype = sz
+        L.ckda_chunk_fwd.argtypes = [vp] * 8 + [i] * 7 + [vp, sz, vp]
+        L.ckda_chunk_fwd.restype = i
+        L.ckda_decode_step.argtypes = [vp] * 7 + [i] * 5 + [vp]
+        L.ckda_decode_step.restype = i
+        L.ckda_status_string.argtypes = [i]
+        L.ckda_status_string.restype = ctypes.c_char_p
+        L.ckda_last_error.argtypes = []
+        L.ckda_last_error.restype = ctypes.c_char_p
+        L.ckda_abi_version.argtypes = []
+        L.ckda_abi_version.restype = i
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise CkdaError(status, lib().ckda_last_error().decode())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return DTYPE_BF16
+    if t.dtype == torch.float32:
+        return DTYPE_F32
+    raise TypeError(f"inputs must be bfloat16 or float32, got {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _require(ts, dtype):
+    for name, t in ts.items():
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.dtype != dtype:
+            raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+
+
+def workspace_size(B, H, T, dk, dv, chunk, dtype) -> int:
+    code = dtype if isinstance(dtype, int) else _dtype_code(torch.empty(0, dtype=dtype))
+    return int(lib().ckda_chunk_fwd_workspace_size(B, H, T, dk, dv, chunk, code))
+
+
+def chunk_fwd(q, k, v, alpha, beta, h0=None, chunk=64, workspace=None, o=None, hT=None,
+              want_state=True, stream=None):
+    """Chunkwise forward.  q, k, alpha [B,H,T,dk]; v [B,H,T,dv]; beta [B,H,T];
+    h0 [B,H,dk,dv] fp32 or None.  Returns (o [B,H,T,dv], hT [B,H,dk,dv] fp32 or None).
+
+    `workspace` (uint8 GPU tensor of at least workspace_size() bytes), `o` and
+    `hT` may be passed in to avoid allocations (e.g. in timed loops)."""
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    _require(dict(q=q, k=k, v=v, alpha=alpha, beta=beta), q.dtype)
+    code = _dtype_code(q)
+    if h0 is not None:
+        _require(dict(h0=h0), torch.float32)
+    need = workspace_size(B, H, T, dk, dv, chunk, code)
+    if need == 0:
+        raise CkdaError(3, f"unsupported sizes dk={dk} dv={dv} chunk={chunk}")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if o is None:
+        o = torch.empty((B, H, T, dv), dtype=q.dtype, device=q.device)
+    if hT is None and want_state:
+        hT = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
+    _check(lib().ckda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(h0), _ptr(o),
+                                _ptr(hT), B, H, T, dk, dv, chunk, code, _ptr(workspace),
+                                workspace.numel() * workspace.element_size(), _stream(stream)))
+    return o, hT
+
+
+def decode_step(q, k, v, alpha, beta, H, o=None, stream=None):
+    """One decode step.  q, k, alpha [N,Hh,dk]; v [N,Hh,dv]; beta [N,Hh];
+    H [N,Hh,dk,dv] fp32 updated in place.  Returns o [N,Hh,dv]."""
+    N, Hh, dk = q.shape
+    dv = v.shape[-1]
+    _require(dict(q=q, k=k, v=v, alpha=alpha, beta=beta), q.dtype)
+    _require(dict(H=H), torch.float32)
+    code = _dtype_code(q)
+    if o is None:
+        o = torch.empty((N, Hh, dv), dtype=q.dtype, device=q.device)
+    _check(lib().ckda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(H), _ptr(o),
+                                  N, Hh, dk, dv, code, _stream(stream)))
+    return o

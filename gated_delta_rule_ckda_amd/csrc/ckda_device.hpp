@@ -1,0 +1,133 @@
+// ckda_device.hpp -- gfx950 device building blocks shared by the CKDA kernels:
+// element conversion, 16-byte MFMA operand fragments and the matrix-core
+// products built on them.
+//
+// Fragment convention.  Every matrix-core product here produces 16x16 fp32
+// tiles in the MFMA accumulator layout: lane l (g = l / 16, r = l % 16) holds
+// rows 4g .. 4g+3 of column r.  Operands are moved as 16-byte fragments, one
+// per lane, covering a 16-row tile of a row-major operand over one "K block"
+// of its contraction index:
+//   bf16 : K block of 32; lane (g, r) holds 8 values at k = kappa(g, e),
+//          kappa(g, e) = 4g + e for e < 4 and 16 + 4g + (e - 4) for e >= 4;
+//          consumed by one v_mfma_f32_16x16x32_bf16.
+//   fp32 : K block of 16; lane (g, r) holds 4 values at k = 4g + e;
+//          consumed by four v_mfma_f32_16x16x4_f32 (sub-step e uses value e).
+// With this K order the accumulator registers of the 16x16 tiles covering a
+// K block are, converted element-wise, exactly the B-operand fragment of that
+// K block (bf16: two tiles, rows 0-15 then 16-31; fp32: one tile), so a
+// product's result feeds the next product without a shuffle.  Any operand
+// that meets it on the other side must be laid out in the same K order, which
+// the chunk preparation kernel does when it writes its outputs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ckda {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------- elements
+
+struct bf16_t {
+  uint16_t bits;
+};
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16_t x) { return __uint_as_float((uint32_t)x.bits << 16); }
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) {
+  __bf16 h = (__bf16)x;  // round to nearest even (v_cvt_pk_bf16_f32)
+  bf16_t r;
+  r.bits = __builtin_bit_cast(uint16_t, h);
+  return r;
+}
+
+// Two floats -> packed bf16 pair (low = a).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  bf16x2 v;
+  v[0] = (__bf16)a;
+  v[1] = (__bf16)b;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// ---------------------------------------------------------------- fragments
+
+// A 16-byte operand fragment held by one lane.
+struct Frag {
+  u32x4 w;
+};
+
+template <typename T> struct FragTraits;
+template <> struct FragTraits<bf16_t> {
+  static constexpr int KB = 32;  // contraction length covered by one fragment
+  static constexpr int EPL = 8;  // elements per lane
+};
+template <> struct FragTraits<float> {
+  static constexpr int KB = 16;
+  static constexpr int EPL = 4;
+};
+
+// K offset of element e held by lane group g within a K block.
+template <typename T> __host__ __device__ constexpr int kappa(int g, int e);
+template <> __host__ __device__ constexpr int kappa<bf16_t>(int g, int e) {
+  return e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4);
+}
+template <> __host__ __device__ constexpr int kappa<float>(int g, int e) { return 4 * g + e; }
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// acc += A_frag * B_frag over one K block.
+template <typename T> __device__ __forceinline__ f32x4 mma(f32x4 acc, Frag a, Frag b);
+
+template <> __device__ __forceinline__ f32x4 mma<bf16_t>(f32x4 acc, Frag a, Frag b) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a.w),
+                                                 __builtin_bit_cast(bf16x8, b.w), acc, 0, 0, 0);
+}
+template <> __device__ __forceinline__ f32x4 mma<float>(f32x4 acc, Frag a, Frag b) {
+  f32x4 fa = __builtin_bit_cast(f32x4, a.w), fb = __builtin_bit_cast(f32x4, b.w);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[0], fb[0], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[1], fb[1], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[2], fb[2], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[3], fb[3], acc, 0, 0, 0);
+  return acc;
+}
+
+// Accumulator tiles -> B fragment of the K block they cover.
+// bf16: lo = tile of K rows 0-15, hi = tile of K rows 16-31 (may be zero).
+__device__ __forceinline__ Frag frag_from_acc_bf16(f32x4 lo, f32x4 hi) {
+  Frag f;
+  f.w[0] = pack_bf16x2(lo[0], lo[1]);
+  f.w[1] = pack_bf16x2(lo[2], lo[3]);
+  f.w[2] = pack_bf16x2(hi[0], hi[1]);
+  f.w[3] = pack_bf16x2(hi[2], hi[3]);
+  return f;
+}
+__device__ __forceinline__ Frag frag_from_acc_f32(f32x4 t) {
+  Frag f;
+  f.w = __builtin_bit_cast(u32x4, t);
+  return f;
+}
+
+__device__ __forceinline__ Frag load_frag(const void* p) {
+  Frag f;
+  f.w = *reinterpret_cast<const u32x4*>(p);
+  return f;
+}
+__device__ __forceinline__ void store_frag(void* p, Frag f) { *reinterpret_cast<u32x4*>(p) = f.w; }
+
+// Wave-wide sum (wave64) via cross-lane shuffles.
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+  return x;
+}
+
+}  // namespace ckda

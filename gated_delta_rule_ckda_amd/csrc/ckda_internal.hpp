@@ -1,0 +1,38 @@
+// ckda_internal.hpp -- host-side launch descriptors shared between the C ABI
+// layer (argument checking, dispatch) and the kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace ckda {
+
+struct DecodeArgs {
+  const void *q, *k, *v, *alpha, *beta;
+  float* H_inout;
+  void* o;
+  int N, H, dk, dv, dtype;
+  hipStream_t stream;
+};
+
+struct ChunkArgs {
+  const void *q, *k, *v, *alpha, *beta;
+  const float* h0;
+  void* o;
+  float* hT;
+  int B, H, T, dk, dv, chunk, dtype;
+  void* workspace;
+  hipStream_t stream;
+};
+
+// Layout of the per-chunk operand records the preparation kernel writes and
+// the state-pass kernel reads (byte offsets inside one chunk's record).
+struct ChunkRecord {
+  size_t w_off, q_off, kr_off, t_off, m_off, d_off, bytes;
+};
+ChunkRecord chunk_record_layout(int dk, int chunk, int dtype);
+
+hipError_t launch_decode(const DecodeArgs& a);
+hipError_t launch_chunk_fwd(const ChunkArgs& a);
+
+}  // namespace ckda

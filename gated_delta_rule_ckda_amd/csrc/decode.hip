@@ -1,0 +1,142 @@
+// decode.hip -- single-token CKDA/KDA step with the fp32 state updated in place.
+//
+// One workgroup per (sequence, head) state.  The state is read from HBM once
+// into registers (16-byte vector loads, each wave covering whole contiguous
+// rows), the two column reductions s = H^T (alpha . k) and r = H^T (alpha . q)
+// are formed from those registers, and the updated state
+// H' = Diag(alpha) H + k u^T with u = beta (v - s) is written back once.
+// The read-out uses o = H'^T q = r + (k^T q) u, so H' never has to be read
+// again.  This is the read-compare-correct step of the KDA course lesson
+// (session 17, "Mechanism map"), queried after the update as in the paper's
+// Eq. (1); the diagonal-plus-rank-one transition keeps it at O(dk dv) work
+// per token (discussion slides, "The transition remains non-expansive and
+// inexpensive").  The kernel is HBM-bound: 2 * dk * dv * 4 bytes of state
+// traffic per state and step, against a few flops per byte.
+#include "ckda_device.hpp"
+#include "ckda_internal.hpp"
+
+namespace ckda {
+
+constexpr int kDecodeThreads = 256;
+
+template <typename T, int DK, int DV>
+__global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const T* __restrict__ alpha, const T* __restrict__ beta, float* __restrict__ H,
+    T* __restrict__ o) {
+  constexpr int TPR = DV / 4;                    // threads per state row (4 columns each)
+  constexpr int RPI = kDecodeThreads / TPR;      // rows covered per pass
+  constexpr int ITER = (DK + RPI - 1) / RPI;     // passes over the rows
+  static_assert(DV % 4 == 0 && kDecodeThreads % TPR == 0, "decode tiling");
+
+  __shared__ float s_a[DK], s_ak[DK], s_aq[DK], s_k[DK], s_q[DK];
+  __shared__ f32x4 s_ps[RPI][TPR], s_pr[RPI][TPR];
+  __shared__ float s_kq;
+
+  const long long st = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int cg = tid % TPR, rg = tid / TPR;
+
+  for (int i = tid; i < DK; i += kDecodeThreads) {
+    float a = to_f32(alpha[st * DK + i]), kk = to_f32(k[st * DK + i]), qq = to_f32(q[st * DK + i]);
+    s_a[i] = a;
+    s_k[i] = kk;
+    s_q[i] = qq;
+    s_ak[i] = a * kk;
+    s_aq[i] = a * qq;
+  }
+
+  float* Hs = H + st * (long long)DK * DV;
+  f32x4 h[ITER];
+#pragma unroll
+  for (int j = 0; j < ITER; ++j) {
+    const int row = rg + j * RPI;
+    if (row < DK) h[j] = *reinterpret_cast<const f32x4*>(Hs + row * DV + 4 * cg);
+  }
+  __syncthreads();
+
+  if (tid < 64) {
+    float p = 0.f;
+    for (int i = tid; i < DK; i += 64) p += s_k[i] * s_q[i];
+    p = wave_sum(p);
+    if (tid == 0) s_kq = p;
+  }
+
+  f32x4 ps = zero4(), pr = zero4();
+#pragma unroll
+  for (int j = 0; j < ITER; ++j) {
+    const int row = rg + j * RPI;
+    if (row < DK) {
+      ps += s_ak[row] * h[j];
+      pr += s_aq[row] * h[j];
+    }
+  }
+  s_ps[rg][cg] = ps;
+  s_pr[rg][cg] = pr;
+  __syncthreads();
+
+  f32x4 sc = zero4(), rc = zero4();
+#pragma unroll 8
+  for (int g = 0; g < RPI; ++g) {
+    sc += s_ps[g][cg];
+    rc += s_pr[g][cg];
+  }
+  const float b = to_f32(beta[st]);
+  f32x4 vv;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) vv[e] = to_f32(v[st * DV + 4 * cg + e]);
+  const f32x4 u = b * (vv - sc);
+
+  if (rg == 0) {
+    const f32x4 oc = rc + s_kq * u;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[st * DV + 4 * cg + e] = from_f32<T>(oc[e]);
+  }
+
+#pragma unroll
+  for (int j = 0; j < ITER; ++j) {
+    const int row = rg + j * RPI;
+    if (row < DK) {
+      const f32x4 hn = s_a[row] * h[j] + s_k[row] * u;
+      *reinterpret_cast<f32x4*>(Hs + row * DV + 4 * cg) = hn;
+    }
+  }
+}
+
+template <typename T, int DK, int DV>
+static hipError_t launch_decode_t(const DecodeArgs& a) {
+  const long long states = (long long)a.N * a.H;
+  if (states == 0) return hipSuccess;
+  hipLaunchKernelGGL((decode_kernel<T, DK, DV>), dim3((unsigned)states), dim3(kDecodeThreads), 0,
+                     a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.alpha,
+                     (const T*)a.beta, a.H_inout, (T*)a.o);
+  return hipGetLastError();
+}
+
+template <typename T, int DK>
+static hipError_t dispatch_dv(const DecodeArgs& a) {
+  switch (a.dv) {
+    case 16: return launch_decode_t<T, DK, 16>(a);
+    case 32: return launch_decode_t<T, DK, 32>(a);
+    case 64: return launch_decode_t<T, DK, 64>(a);
+    case 128: return launch_decode_t<T, DK, 128>(a);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename T>
+static hipError_t dispatch_dk(const DecodeArgs& a) {
+  switch (a.dk) {
+    case 16: return dispatch_dv<T, 16>(a);
+    case 32: return dispatch_dv<T, 32>(a);
+    case 64: return dispatch_dv<T, 64>(a);
+    case 128: return dispatch_dv<T, 128>(a);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode(const DecodeArgs& a) {
+  return a.dtype == 1 ? dispatch_dk<bf16_t>(a) : dispatch_dk<float>(a);
+}
+
+}  // namespace ckda

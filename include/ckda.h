@@ -1,0 +1,146 @@
+/*
+ * ckda.h -- C ABI of the MI355X (gfx950) CKDA / KDA kernel library.
+ *
+ * The library computes the (Complex) Kimi Delta Attention recurrence, one
+ * independent state per (batch, head):
+ *
+ *   H_t = (I - beta_t k_t k_t^T) Diag(alpha_t) H_{t-1} + beta_t k_t v_t^T
+ *   o_t = H_t^T q_t
+ *
+ * with H_t of shape d_k x d_v (row i = key channel i) and unit-norm keys
+ * ("Complex KDA", Eq. (1); discussion slides, frame "CKDA keeps the original
+ * gate--delta--readout structure").  KDA ranges (alpha in (0,1], beta in
+ * [0,1]) and CKDA ranges (alpha in [-1,1], beta in [0,2], Sec. 3 "CKDA")
+ * run through the same code: signed gates are split into a sign and a
+ * magnitude and the cumulative signs are absorbed into keys and queries
+ * inside the kernels (discussion slides, frame "Absorb cumulative signs into
+ * keys and queries"; paper Prop. 2 for sign(0) = +1).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Pointers are DEVICE pointers owned by the caller.  The library allocates
+ *   no device memory and keeps no state between calls apart from a
+ *   thread-local error string.
+ * - Tensors are contiguous, C order, base addresses 16-byte aligned.
+ * - `dtype` (ckda_dtype_t) is the element type of q, k, v, alpha, beta and o.
+ *   States (h0, hT, H_inout) are always fp32.
+ * - q is not scaled and k is not normalised: the caller supplies ||k_t|| = 1.
+ *   alpha and beta are used as given (no clamping of range violations), except
+ *   that the chunked forward replaces gate magnitudes below 2^-15 by 2^-15
+ *   (sign kept, sign(0) = +1), which bounds the deviation from the exact
+ *   recurrence by 2^-15 relative per affected step; see ckda_chunk_fwd.
+ * - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
+ *   and the call returns without waiting.  The return value reports argument
+ *   errors (detected before anything is launched) and launch errors; faults
+ *   during execution surface at the caller's next synchronisation.
+ * - Errors: every function returns a ckda_status_t; nothing aborts or throws
+ *   across the ABI.  ckda_last_error() returns a thread-local description of
+ *   the last non-OK status.
+ * - Results are bitwise deterministic run to run (no atomics, fixed
+ *   reduction order).  Calls on different streams with disjoint buffers may
+ *   run concurrently.
+ */
+#ifndef CKDA_H
+#define CKDA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CKDA_ABI_VERSION 1
+
+typedef enum { CKDA_DTYPE_F32 = 0, CKDA_DTYPE_BF16 = 1 } ckda_dtype_t;
+
+typedef enum {
+  CKDA_OK = 0,
+  CKDA_ERR_NULL = 1,        /* a required pointer is NULL */
+  CKDA_ERR_DIM = 2,         /* a size is negative or inconsistent */
+  CKDA_ERR_UNSUPPORTED = 3, /* valid but not supported (dtype, d_k, d_v, chunk) */
+  CKDA_ERR_ALIAS = 4,       /* an output overlaps an input it may not overlap */
+  CKDA_ERR_WORKSPACE = 5,   /* workspace missing, too small or misaligned */
+  CKDA_ERR_HIP = 6          /* the HIP runtime reported an error at launch */
+} ckda_status_t;
+
+/* Bytes of device workspace ckda_chunk_fwd needs for these sizes, or 0 when
+ * the sizes are invalid or unsupported (ckda_chunk_fwd then reports why).
+ * The workspace holds, per chunk of every (batch, head), the operands the
+ * state pass consumes (see ckda_chunk_fwd); it is about
+ * B*H*ceil(T/chunk)*(3*chunk*d_k + 2*chunk*chunk) elements of dtype plus
+ * d_k floats per chunk. */
+size_t ckda_chunk_fwd_workspace_size(int B, int H, int T, int dk, int dv, int chunk, int dtype);
+
+/* Chunkwise-parallel forward over a whole sequence for every (batch, head).
+ *
+ *   q, k, alpha : [B, H, T, dk]  dtype
+ *   v           : [B, H, T, dv]  dtype
+ *   beta        : [B, H, T]      dtype
+ *   h0          : [B, H, dk, dv] fp32 initial states, or NULL for zeros
+ *   o           : [B, H, T, dv]  dtype, o_t = H_t^T q_t (post-update state)
+ *   hT          : [B, H, dk, dv] fp32 final states, or NULL to skip
+ *   workspace   : device buffer of at least ckda_chunk_fwd_workspace_size()
+ *                 bytes, 256-byte aligned; contents on entry are ignored and
+ *                 on return are unspecified.  It must not overlap any other
+ *                 argument.
+ *
+ * Supported: dtype F32 or BF16; dk, dv in {16, 32, 64, 128}; chunk in
+ * {16, 32, 64}; any T >= 0 (T = 0 copies h0 to hT, or zeros).  A last chunk
+ * shorter than `chunk` is handled exactly (the missing positions act as
+ * identity steps and are not stored).
+ *
+ * Aliasing: o must not overlap any input; hT may equal h0 exactly (in-place
+ * continuation of a state) but must not otherwise overlap an input.
+ *
+ * The result equals the sequential recurrence up to floating-point rounding
+ * (the KDA course lesson, "Chunkwise execution": chunking changes cost, not
+ * the numbers), computed in two kernels: a per-chunk preparation kernel that
+ * splits the gates into sign parity and magnitude products, forms the
+ * intra-chunk Gram matrices and solves the unit lower-triangular (UT/WY)
+ * system, and a state-pass kernel that carries the fp32 state from chunk to
+ * chunk and emits the outputs.  bf16 inputs are multiplied on bf16 matrix
+ * cores with fp32 accumulation; fp32 inputs on fp32 matrix cores. */
+int ckda_chunk_fwd(const void* q, const void* k, const void* v, const void* alpha,
+                   const void* beta, const float* h0, void* o, float* hT,
+                   int B, int H, int T, int dk, int dv, int chunk, int dtype,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* One recurrent decode step for N sequences x H heads, state in place.
+ *
+ *   q, k, alpha : [N, H, dk]     dtype
+ *   v           : [N, H, dv]     dtype
+ *   beta        : [N, H]         dtype
+ *   H_inout     : [N, H, dk, dv] fp32, read and overwritten with H_t
+ *   o           : [N, H, dv]     dtype, o = H_t^T q
+ *
+ * Computes, per state, in a single read and a single write of H:
+ *   s = H^T (alpha . k),  r = H^T (alpha . q),  u = beta (v - s),
+ *   o = r + (k^T q) u,    H <- Diag(alpha) H + k u^T
+ * which is the read-compare-correct step of the KDA course lesson
+ * ("Mechanism map": S' = diag(a) S, S = S' + beta k (v - S'^T k)^T) read out
+ * after the update; the state's diagonal-plus-rank-one structure keeps the
+ * work at O(dk dv) per token (discussion slides, "The transition remains
+ * non-expansive and inexpensive").  All arithmetic is fp32; no gate floor.
+ *
+ * Supported: dtype F32 or BF16; dk, dv in {16, 32, 64, 128}; N, H >= 0.
+ * Aliasing: o must not overlap H_inout or any input; H_inout must not overlap
+ * any input. */
+int ckda_decode_step(const void* q, const void* k, const void* v, const void* alpha,
+                     const void* beta, float* H_inout, void* o,
+                     int N, int H, int dk, int dv, int dtype, void* stream);
+
+/* Static description of a status code. */
+const char* ckda_status_string(int status);
+
+/* Thread-local detail of the last non-OK status returned on this thread
+ * (empty string if none).  Valid until the next call on this thread. */
+const char* ckda_last_error(void);
+
+/* CKDA_ABI_VERSION of the built library. */
+int ckda_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CKDA_H */

@@ -1,0 +1,124 @@
+"""The C ABI without a GPU: the library loads, exports every function that
+include/ckda.h declares, and rejects bad arguments before launching anything
+(so these calls never reach the device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_delta_rule_ckda_amd as ck
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ckda.h")
+
+BASE = 0x7F0000000000   # fake, never-dereferenced device addresses
+MB = 1 << 20
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ckda_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    L = ck.lib()
+    names = declared_functions()
+    assert set(names) == set(ck.EXPORTS)
+    for n in names:
+        assert hasattr(L, n), n
+    assert L.ckda_abi_version() == 1
+
+
+def test_status_strings():
+    L = ck.lib()
+    for s in range(7):
+        assert L.ckda_status_string(s)
+    assert L.ckda_status_string(99) == b"unknown status"
+
+
+def test_workspace_size():
+    L = ck.lib()
+    ws = L.ckda_chunk_fwd_workspace_size
+    # bf16, d128, chunk 64: 4 A-operand fragments of 1 KB per (row tile, K block) ...
+    per_chunk = ws(1, 1, 64, 128, 128, 64, 1)
+    assert per_chunk == 1024 * (2 * 4 * 4 + 8 * 2 + 2 * 4 * 2) + 512
+    assert ws(4, 16, 4096, 128, 128, 64, 1) == 64 * 64 * per_chunk
+    assert ws(1, 1, 65, 128, 128, 64, 1) == 2 * per_chunk       # ragged tail = one more chunk
+    assert ws(1, 1, 64, 128, 128, 48, 1) == 0                  # unsupported chunk
+    assert ws(1, 1, 64, 96, 128, 64, 1) == 0                   # unsupported dk
+    assert ws(1, 1, 64, 128, 128, 64, 7) == 0                  # unsupported dtype
+    assert ws(-1, 1, 64, 128, 128, 64, 1) == 0
+    assert ws(1, 1, 64, 16, 16, 16, 0) > 0
+
+
+def call_fwd(**kw):
+    L = ck.lib()
+    B, H, T, dk, dv = kw.get("B", 1), kw.get("H", 2), kw.get("T", 64), kw.get("dk", 64), kw.get("dv", 64)
+    chunk, dtype = kw.get("chunk", 64), kw.get("dtype", 1)
+    p = dict(q=BASE, k=BASE + 1 * MB, v=BASE + 2 * MB, alpha=BASE + 3 * MB, beta=BASE + 4 * MB,
+             h0=BASE + 5 * MB, o=BASE + 6 * MB, hT=BASE + 7 * MB, ws=BASE + 8 * MB)
+    p.update({k: v for k, v in kw.items() if k in p})
+    wsb = kw.get("wsb", 64 * MB)
+    rc = L.ckda_chunk_fwd(p["q"], p["k"], p["v"], p["alpha"], p["beta"], p["h0"], p["o"], p["hT"],
+                          B, H, T, dk, dv, chunk, dtype, p["ws"], wsb, None)
+    return rc, L.ckda_last_error().decode()
+
+
+def call_dec(**kw):
+    L = ck.lib()
+    N, H, dk, dv, dtype = kw.get("N", 2), kw.get("H", 2), kw.get("dk", 64), kw.get("dv", 64), kw.get("dtype", 1)
+    p = dict(q=BASE, k=BASE + MB, v=BASE + 2 * MB, alpha=BASE + 3 * MB, beta=BASE + 4 * MB,
+             S=BASE + 5 * MB, o=BASE + 6 * MB)
+    p.update({k: v for k, v in kw.items() if k in p})
+    rc = L.ckda_decode_step(p["q"], p["k"], p["v"], p["alpha"], p["beta"], p["S"], p["o"], N, H, dk, dv, dtype,
+                            None)
+    return rc, L.ckda_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(o=None), 1), (dict(beta=None), 1),
+    (dict(T=-1), 2), (dict(B=-2), 2),
+    (dict(dk=48), 3), (dict(dv=256), 3), (dict(chunk=128), 3), (dict(dtype=2), 3),
+    (dict(q=BASE + 2), 2),                                        # misaligned
+    (dict(o=BASE + 2 * MB + 64), 4),                              # o overlaps v
+    (dict(hT=BASE + 16), 4),                                      # hT overlaps q
+    (dict(hT=BASE + 5 * MB + 16), 4),                             # hT partially overlaps h0
+    (dict(ws=BASE + 6 * MB), 4),                                  # workspace overlaps o
+    (dict(ws=None), 5), (dict(wsb=1024), 5), (dict(ws=BASE + 8 * MB + 16), 5),
+])
+def test_chunk_fwd_rejects(kw, status):
+    rc, msg = call_fwd(**kw)
+    assert rc == status, (rc, msg)
+    assert msg.startswith("ckda_chunk_fwd")
+
+
+def test_chunk_fwd_empty_problems_are_noops():
+    assert call_fwd(B=0)[0] == 0
+    assert call_fwd(H=0, q=None, o=None)[0] == 0
+    assert call_fwd(T=0, hT=None, q=None, k=None, v=None, alpha=None, beta=None, o=None, ws=None)[0] == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(S=None), 1), (dict(o=None), 1),
+    (dict(N=-1), 2), (dict(dk=8), 3), (dict(dtype=5), 3),
+    (dict(o=BASE + 5 * MB), 4),                                   # o overlaps the state
+    (dict(S=BASE + 16), 4),                                       # state overlaps q
+    (dict(alpha=BASE + 3 * MB + 4), 2),                           # misaligned
+])
+def test_decode_rejects(kw, status):
+    rc, msg = call_dec(**kw)
+    assert rc == status, (rc, msg)
+    assert msg.startswith("ckda_decode_step")
+
+
+def test_decode_empty_is_noop():
+    assert call_dec(N=0, q=None)[0] == 0
+
+
+def test_python_binding_requires_gpu_tensors():
+    import torch
+    x = torch.zeros((1, 1, 16, 16), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        ck.chunk_fwd(x, x, x, x, torch.zeros((1, 1, 16), dtype=torch.bfloat16), chunk=16)
