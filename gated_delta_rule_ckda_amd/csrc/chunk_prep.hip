@@ -36,14 +36,16 @@
 
 namespace ckda {
 
-constexpr int kPrepThreads = 256;
+constexpr int kPrepThreads = 512;
+constexpr int kPrepWaves = kPrepThreads / 64;
 constexpr float kGateFloor = 4.656612873077393e-10f;  // 2^-31
 
 template <typename T, int DK, int C>
 struct PrepCfg : ChunkGeom<T, DK, C> {
   using G = ChunkGeom<T, DK, C>;
   static constexpr int NSB = C / 16;                              // 16-row sub-blocks
-  static constexpr int CG = DK < 256 / NSB ? DK : 256 / NSB;      // channels per group
+  static constexpr int NHB = C / 8;                               // 8-row half blocks
+  static constexpr int CG = DK < kPrepThreads / NHB ? DK : kPrepThreads / NHB;  // channels per group
   static constexpr int NG = DK / CG;                              // channel groups
   static constexpr int CGP = CG > G::KB ? CG : G::KB;             // padded row length
   static constexpr int RS = CGP * G::E + (G::E == 2 ? 8 : 16);    // LDS row stride (bytes)
@@ -59,11 +61,11 @@ struct PrepCfg : ChunkGeom<T, DK, C> {
   static constexpr int R_Y2 = R_X2Q + C / 2;                      // rows 0-7 of each sub-block
   static constexpr int ROWS = R_Y2 + C / 2;
   static constexpr int OPER_BYTES = ROWS * RS;
-  static constexpr int SCR_BYTES = 3 * C * C * 4 + 4 * 16 * 16 * 4;
+  static constexpr int SCR_BYTES = 3 * C * C * 4 + kPrepWaves * 16 * 16 * 4;
   static constexpr int MAIN_BYTES = OPER_BYTES > SCR_BYTES ? OPER_BYTES : SCR_BYTES;
   static constexpr int NT1 = NSB * (NSB + 1);                     // A and M tiles (I >= J)
   static constexpr int NTILE = NT1 + 2 * NSB;                     // + lower-left diagonal quadrants
-  static constexpr int TPW = (NTILE + 3) / 4;                     // tiles per wave
+  static constexpr int TPW = (NTILE + kPrepWaves - 1) / kPrepWaves;
 };
 
 // Pair index of sub-blocks (I, J), I > J, in J-major order.
@@ -76,21 +78,15 @@ __device__ __forceinline__ int pair_index(int I, int J, int nsb) {
 // Byte offset, inside an A-operand region with `nkb` K blocks, of element
 // (row m, contraction index k).
 template <typename T>
-__device__ __forceinline__ size_t a_elem_offset(int m, int k, int nkb) {
+__host__ __device__ constexpr size_t a_elem_offset(int m, int k, int nkb) {
   constexpr int KB = FragTraits<T>::KB;
-  const int kb = k / KB, kk = k % KB, half = kk / 16, k16 = kk % 16;
-  const int g = k16 / 4, e = half * 4 + (k16 % 4);
-  return frag_slot(m / 16, kb, nkb, g * 16 + (m % 16)) + (size_t)e * sizeof(T);
+  return frag_slot(m / 16, k / KB, nkb, ((k % KB) % 16) / 4 * 16 + (m % 16)) +
+         (size_t)(((k % KB) / 16) * 4 + (k % KB) % 4) * sizeof(T);
 }
 
 template <typename T>
-__device__ __forceinline__ void st_elem(unsigned char* base, size_t off, float x) {
-  *reinterpret_cast<T*>(base + off) = from_f32<T>(x);
-}
-
-template <typename T>
-__device__ __forceinline__ void lds_put(unsigned char* lds, int rs, int row, int col, float x) {
-  *reinterpret_cast<T*>(lds + row * rs + col * (int)sizeof(T)) = from_f32<T>(x);
+__device__ __forceinline__ void st_elem(unsigned char* p, float x) {
+  *reinterpret_cast<T*>(p) = from_f32<T>(x);
 }
 
 // Row fragment from an LDS operand array: lane (g, r) gets row r0 + r at the
@@ -140,15 +136,15 @@ __device__ __forceinline__ f32x4 block_mac(f32x4 acc, const float* X, int xs, co
 }
 
 template <typename T, int DK, int C>
-__global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(
+__global__ __launch_bounds__(kPrepThreads, 4) void chunk_prep_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ alpha,
     const T* __restrict__ beta, unsigned char* __restrict__ ws, int T_len, int nchunks) {
   using P = PrepCfg<T, DK, C>;
-  constexpr int NSB = P::NSB, CG = P::CG, RS = P::RS;
+  constexpr int NSB = P::NSB, NHB = P::NHB, CG = P::CG, RS = P::RS, E = P::E, KB = P::KB;
   __shared__ __attribute__((aligned(16))) unsigned char smem[P::MAIN_BYTES];
   __shared__ float s_beta[C];
-  __shared__ float s_bp[NSB][CG];
-  __shared__ unsigned s_bpar[NSB][CG];
+  __shared__ float s_hp[NHB][CG];
+  __shared__ unsigned s_hpar[NHB][CG];
 
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
   const int g = lane / 16, r = lane % 16;
@@ -166,25 +162,26 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(
   }
   if constexpr (P::CGP > CG) {  // zero the padding columns once (bf16 with DK = 16)
     for (int i = tid; i < P::OPER_BYTES / 4; i += kPrepThreads) reinterpret_cast<unsigned*>(smem)[i] = 0u;
-    __syncthreads();
+    lds_barrier();
   }
 
   f32x4 acc[P::TPW];
 #pragma unroll
   for (int j = 0; j < P::TPW; ++j) acc[j] = zero4();
 
-  const int task = tid;
-  const bool has_task = task < CG * NSB;
-  const int cl = task % CG, sb = task / CG;
+  // gate task of this thread: channel cl of the group, 8-row half block hb
+  const bool has_task = tid < CG * NHB;
+  const int cl = tid % CG, hb = tid / CG;
+  const int sb = hb / 2, hh = hb % 2;                 // 16-row sub-block, half inside it
 
   for (int grp = 0; grp < P::NG; ++grp) {
     const int c = grp * CG + cl;
-    float m[16], kk[16], qq[16];
+    float m[8], kk[8], qq[8];
     unsigned sg = 0;
     if (has_task) {
 #pragma unroll
-      for (int l = 0; l < 16; ++l) {
-        const int t = sb * 16 + l;
+      for (int l = 0; l < 8; ++l) {
+        const int t = hb * 8 + l;
         const bool valid = t < cv;
         const long long ix = (row0 + min(t, cv - 1)) * DK + c;   // index kept in range
         const float a0 = to_f32(alpha[ix]), k0 = to_f32(k[ix]), q0 = to_f32(q[ix]);
@@ -195,111 +192,118 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(
         const float mag = fabsf(a);
         m[l] = mag < kGateFloor ? kGateFloor : mag;   // NaN propagates
       }
-      float bp = 1.f;
+      float hp = 1.f;
 #pragma unroll
-      for (int l = 0; l < 16; ++l) bp *= m[l];
-      s_bp[sb][cl] = bp;
-      s_bpar[sb][cl] = __builtin_popcount(sg) & 1u;
+      for (int l = 0; l < 8; ++l) hp *= m[l];
+      s_hp[hb][cl] = hp;
+      s_hpar[hb][cl] = __builtin_popcount(sg) & 1u;
     }
-    __syncthreads();
+    lds_barrier();
 
     if (has_task) {
-      // whole-sub-block products before / after this one, chunk totals, and
-      // the products of the sub-blocks strictly between sb and each later I
-      float bpre = 1.f, bsuf = 1.f, gC = 1.f;
-      unsigned ppre = 0, pC = 0;
-      float mid[NSB];
+      // products of the half blocks before / after this one, of the other half
+      // of this sub-block, of the whole chunk, and of the sub-blocks strictly
+      // between this one and each later sub-block I
+      float before = 1.f, after = 1.f, gC = 1.f, other = 1.f;
+      unsigned pbefore = 0, pC = 0;
+      float hps[NHB];
 #pragma unroll
-      for (int b = 0; b < NSB; ++b) {
-        const float bp = s_bp[b][cl];
-        const unsigned pp = s_bpar[b][cl];
-        gC *= bp;
+      for (int h = 0; h < NHB; ++h) {
+        hps[h] = s_hp[h][cl];
+        const unsigned pp = s_hpar[h][cl];
+        gC *= hps[h];
         pC ^= pp;
-        if (b < sb) { bpre *= bp; ppre ^= pp; }
-        if (b > sb) bsuf *= bp;
+        if (h < hb) { before *= hps[h]; pbefore ^= pp; }
+        if (h > hb) after *= hps[h];
       }
+      other = hps[hb ^ 1];
+      float mid[NSB];
       {
         float run = 1.f;
 #pragma unroll
         for (int I = 0; I < NSB; ++I) {
-          mid[I] = run;                          // prod of sub-blocks sb+1 .. I-1
-          if (I > sb) run *= s_bp[I][cl];
+          mid[I] = run;                              // prod of sub-blocks sb+1 .. I-1
+          if (I > sb) run *= hps[2 * I] * hps[2 * I + 1];
         }
       }
-      // suffix products inside the sub-block; quadrant split factors: pre8
-      // (rows 8-15, from row 8) and suf8 (rows 0-7, up to row 7) for the
-      // lower-left quadrant, am / bm around the midpoint of each 8-row quadrant
-      float suf[16], am[16], bm[16], q8[16];
-      suf[15] = 1.f;
+      // within-half prefix (inclusive) and suffix (exclusive) products, and
+      // the split factors around the half's midpoint (between rows 3 and 4)
+      float wpre[8], wsuf[8], am[8], bm[8];
+      wpre[0] = m[0];
 #pragma unroll
-      for (int l = 14; l >= 0; --l) suf[l] = suf[l + 1] * m[l + 1];
-      q8[7] = 1.f;
+      for (int l = 1; l < 8; ++l) wpre[l] = wpre[l - 1] * m[l];
+      wsuf[7] = 1.f;
 #pragma unroll
-      for (int l = 6; l >= 0; --l) q8[l] = q8[l + 1] * m[l + 1];      // suf8
-      q8[8] = m[8];
+      for (int l = 6; l >= 0; --l) wsuf[l] = wsuf[l + 1] * m[l + 1];
+      bm[3] = 1.f;
 #pragma unroll
-      for (int l = 9; l < 16; ++l) q8[l] = q8[l - 1] * m[l];          // pre8
+      for (int l = 2; l >= 0; --l) bm[l] = bm[l + 1] * m[l + 1];
+      am[4] = m[4];
 #pragma unroll
-      for (int base = 0; base < 16; base += 8) {
-        bm[base + 3] = 1.f;
+      for (int l = 5; l < 8; ++l) am[l] = am[l - 1] * m[l];
 #pragma unroll
-        for (int l = base + 2; l >= base; --l) bm[l] = bm[l + 1] * m[l + 1];
-        am[base + 4] = m[base + 4];
+      for (int l = 0; l < 4; ++l) am[l] = __builtin_amdgcn_rcpf(bm[l]);
 #pragma unroll
-        for (int l = base + 5; l < base + 8; ++l) am[l] = am[l - 1] * m[l];
-#pragma unroll
-        for (int l = base; l < base + 4; ++l) am[l] = __builtin_amdgcn_rcpf(bm[l]);
-#pragma unroll
-        for (int l = base + 4; l < base + 8; ++l) bm[l] = __builtin_amdgcn_rcpf(am[l]);
-      }
+      for (int l = 4; l < 8; ++l) bm[l] = __builtin_amdgcn_rcpf(am[l]);
 
-      float pre = 1.f;
-      unsigned par = ppre;
+      // per-thread bases of the record elements this thread writes; the row
+      // inside the half block only adds a constant to them
+      unsigned char* w_base = rec + P::W_OFF + a_elem_offset<T>(hb * 8, c, P::KBN);
+      unsigned char* q_base = rec + P::Q_OFF + a_elem_offset<T>(hb * 8, c, P::KBN);
+      unsigned char* kr_base = rec + P::KR_OFF + a_elem_offset<T>(c, hb * 8, P::KBC);
+      unsigned char* lrow = smem + cl * E + (8 * hh) * RS;
+      unsigned char* y_base[NSB];
 #pragma unroll
-      for (int l = 0; l < 16; ++l) {
-        const int t = sb * 16 + l;
-        pre *= m[l];
+      for (int I = 0; I < NSB; ++I)
+        y_base[I] = smem + cl * E + (P::R_Y + (I > sb ? pair_index(I, sb, NSB) : 0) * 16 + 8 * hh) * RS;
+
+      unsigned par = pbefore;
+#pragma unroll
+      for (int l = 0; l < 8; ++l) {
         par ^= (sg >> l) & 1u;
         const float kt = par ? -kk[l] : kk[l];
         const float qt = par ? -qq[l] : qq[l];
-        const float gam = bpre * pre;
-        st_elem<T>(rec, P::W_OFF + a_elem_offset<T>(t, c, P::KBN), -kt * gam);
-        st_elem<T>(rec, P::Q_OFF + a_elem_offset<T>(t, c, P::KBN), qt * gam);
-        const float kr = suf[l] * bsuf;
-        st_elem<T>(rec, P::KR_OFF + a_elem_offset<T>(c, t, P::KBC), (pC ^ par) ? -kk[l] * kr : kk[l] * kr);
-        if constexpr (C < P::KB)  // zero the K padding of the positions operand
-          st_elem<T>(rec, P::KR_OFF + a_elem_offset<T>(c, t + 16, P::KBC), 0.f);
-        if constexpr (DK < P::KB) {  // zero the K padding of the channel operands
-          st_elem<T>(rec, P::W_OFF + a_elem_offset<T>(t, c + 16, P::KBN), 0.f);
-          st_elem<T>(rec, P::Q_OFF + a_elem_offset<T>(t, c + 16, P::KBN), 0.f);
+        const float gam = before * wpre[l];                  // gamma_t
+        const float pre = (hh ? other : 1.f) * wpre[l];      // prefix inside the sub-block
+        const float suf = wsuf[l] * (hh ? 1.f : other);      // suffix inside the sub-block
+        const float kr = wsuf[l] * after;                    // gamma_C / gamma_t
+        st_elem<T>(w_base + l * 16, -kt * gam);
+        st_elem<T>(q_base + l * 16, qt * gam);
+        st_elem<T>(kr_base + (l / 4) * 256 + (l % 4) * E, (pC ^ par) ? -kk[l] * kr : kk[l] * kr);
+        if constexpr (C < KB)  // zero the K padding of the positions operand
+          st_elem<T>(kr_base + (l / 4) * 256 + (l % 4) * E + 4 * E, 0.f);
+        if constexpr (DK < KB) {  // zero the K padding of the channel operands
+          st_elem<T>(w_base + l * 16 + 4 * E, 0.f);
+          st_elem<T>(q_base + l * 16 + 4 * E, 0.f);
         }
         // Gram operands for this channel group
+        unsigned char* rowp = lrow + l * RS;
         if (sb >= 1) {
-          lds_put<T>(smem, RS, P::R_XK + (sb - 1) * 16 + l, cl, kt * pre);
-          lds_put<T>(smem, RS, P::R_XQ + (sb - 1) * 16 + l, cl, qt * pre);
+          st_elem<T>(rowp + (P::R_XK + (sb - 1) * 16) * RS, kt * pre);
+          st_elem<T>(rowp + (P::R_XQ + (sb - 1) * 16) * RS, qt * pre);
         }
 #pragma unroll
         for (int I = 0; I < NSB; ++I)
-          if (I > sb) lds_put<T>(smem, RS, P::R_Y + pair_index(I, sb, NSB) * 16 + l, cl, kt * suf[l] * mid[I]);
-        lds_put<T>(smem, RS, P::R_XKD + t, cl, kt * am[l]);
-        lds_put<T>(smem, RS, P::R_XQD + t, cl, qt * am[l]);
-        lds_put<T>(smem, RS, P::R_YD + t, cl, kt * bm[l]);
-        if (l >= 8) {
-          lds_put<T>(smem, RS, P::R_X2K + sb * 8 + (l - 8), cl, kt * q8[l]);
-          lds_put<T>(smem, RS, P::R_X2Q + sb * 8 + (l - 8), cl, qt * q8[l]);
-        } else {
-          lds_put<T>(smem, RS, P::R_Y2 + sb * 8 + l, cl, kt * q8[l]);
+          if (I > sb) st_elem<T>(y_base[I] + l * RS, kt * suf * mid[I]);
+        st_elem<T>(rowp + (P::R_XKD + sb * 16) * RS, kt * am[l]);
+        st_elem<T>(rowp + (P::R_XQD + sb * 16) * RS, qt * am[l]);
+        st_elem<T>(rowp + (P::R_YD + sb * 16) * RS, kt * bm[l]);
+        if (hh) {   // rows 8-15: prefix from row 8
+          st_elem<T>(rowp + (P::R_X2K + sb * 8 - 8) * RS, kt * wpre[l]);
+          st_elem<T>(rowp + (P::R_X2Q + sb * 8 - 8) * RS, qt * wpre[l]);
+        } else {    // rows 0-7: suffix up to row 7
+          st_elem<T>(rowp + (P::R_Y2 + sb * 8) * RS, kt * wsuf[l]);
         }
       }
-      if (sb == 0) reinterpret_cast<float*>(rec + P::D_OFF)[c] = pC ? -gC : gC;
+      if (hb == 0) reinterpret_cast<float*>(rec + P::D_OFF)[c] = pC ? -gC : gC;
     }
-    __syncthreads();
+    lds_barrier();
 
     // Gram tiles: tile index tau -> (kind, I, J), kind 0 = A (keys), 1 = M
     // (queries); tau >= NT1 are the lower-left quadrants of diagonal tiles
 #pragma unroll
     for (int j = 0; j < P::TPW; ++j) {
-      const int tau = wave + 4 * j;
+      const int tau = wave + kPrepWaves * j;
       if (tau < P::NT1) {
         const int kind = tau & 1, pr = tau >> 1;
         int I = 0, J = pr;
@@ -313,18 +317,18 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(
           yr = P::R_YD + J * 16;
         }
 #pragma unroll
-        for (int kb = 0; kb < P::CGP / P::KB; ++kb)
+        for (int kb = 0; kb < P::CGP / KB; ++kb)
           acc[j] = mma<T>(acc[j], lds_row_frag<T>(smem, RS, xr, kb, lane), lds_row_frag<T>(smem, RS, yr, kb, lane));
       } else if (tau < P::NTILE) {
         const int kind = (tau - P::NT1) & 1, I = (tau - P::NT1) >> 1;
         const int xr = (kind ? P::R_X2Q : P::R_X2K) + I * 8, yr = P::R_Y2 + I * 8;
 #pragma unroll
-        for (int kb = 0; kb < P::CGP / P::KB; ++kb)
+        for (int kb = 0; kb < P::CGP / KB; ++kb)
           acc[j] = mma<T>(acc[j], lds_half_frag<T>(smem, RS, xr, kb, lane, true),
                           lds_half_frag<T>(smem, RS, yr, kb, lane, false));
       }
     }
-    __syncthreads();
+    lds_barrier();
   }
 
   // ---- A and M to LDS (fp32), then the triangular solve
@@ -333,12 +337,12 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(
   float* Ts = Ms + C * C;
   float* Ss = Ts + C * C;  // per-wave 16x16 scratch
   for (int i = tid; i < 3 * C * C; i += kPrepThreads) As[i] = 0.f;
-  __syncthreads();
+  lds_barrier();
   // masked write: off-diagonal tiles whole, diagonal tiles only inside their
   // two diagonal quadrants (elsewhere the midpoint factors are not valid)
 #pragma unroll
   for (int j = 0; j < P::TPW; ++j) {
-    const int tau = wave + 4 * j;
+    const int tau = wave + kPrepWaves * j;
     if (tau < P::NT1) {
       const int kind = tau & 1, pr = tau >> 1;
       int I = 0, J = pr;
@@ -353,11 +357,11 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(
       }
     }
   }
-  __syncthreads();
+  lds_barrier();
   // add the lower-left quadrants of the diagonal tiles
 #pragma unroll
   for (int j = 0; j < P::TPW; ++j) {
-    const int tau = wave + 4 * j;
+    const int tau = wave + kPrepWaves * j;
     if (tau >= P::NT1 && tau < P::NTILE) {
       const int kind = (tau - P::NT1) & 1, I = (tau - P::NT1) >> 1;
 #pragma unroll
@@ -370,7 +374,7 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(
       }
     }
   }
-  __syncthreads();
+  lds_barrier();
 
   // diagonal 16x16 blocks of T by forward substitution: lane (blk, jcol)
   if (wave == 0 && lane < 16 * NSB) {
@@ -386,11 +390,11 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(
 #pragma unroll
     for (int i = 0; i < 16; ++i) Ts[(o + i) * C + o + jc] = tcol[i];
   }
-  __syncthreads();
+  lds_barrier();
 
   // off-diagonal blocks by distance: T_IJ = -T_II sum_{K=J}^{I-1} A_IK T_KJ
   for (int d = 1; d < NSB; ++d) {
-    for (int J = wave; J + d < NSB; J += 4) {
+    for (int J = wave; J + d < NSB; J += kPrepWaves) {
       const int I = J + d;
       f32x4 s = zero4();
       for (int K = J; K < I; ++K)
@@ -398,17 +402,17 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(
       float* S = Ss + wave * 256;
       const int rr = lane / 4, cc = 4 * (lane % 4);
       *reinterpret_cast<f32x4*>(S + rr * 16 + cc) = s;
-      __threadfence_block();
+      lds_wave_fence();
       f32x4 t = block_mac(zero4(), Ts + (16 * I) * C + 16 * I, C, S, 16, lane);
       *reinterpret_cast<f32x4*>(Ts + (16 * I + rr) * C + 16 * J + cc) = -t;
-      __threadfence_block();
+      lds_wave_fence();
     }
-    __syncthreads();
+    lds_barrier();
   }
 
   // ---- emit T Diag(beta) and M as A-operand fragments (K order of the positions)
   constexpr int NF = P::RT * P::KBC;
-  for (int f = wave; f < 2 * NF; f += 4) {
+  for (int f = wave; f < 2 * NF; f += kPrepWaves) {
     const bool isT = f < NF;
     const int ff = isT ? f : f - NF;
     const int rt = ff / P::KBC, kb = ff % P::KBC;
@@ -417,7 +421,7 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(
     float vals[8];
 #pragma unroll
     for (int e = 0; e < P::EPL; ++e) {
-      const int col = kb * P::KB + kappa<T>(g, e);
+      const int col = kb * KB + kappa<T>(g, e);
       float v = 0.f;
       if (col < C) {
         v = src[row * C + col];

@@ -25,11 +25,11 @@ constexpr int kStateThreads = 256;
 
 template <typename T, int DK, int C, int NCT>
 __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(
-    const T* __restrict__ v, const float* __restrict__ h0, T* __restrict__ o, float* __restrict__ hT,
-    const unsigned char* __restrict__ ws, int T_len, int nchunks, int dv, int slices, int xcd_map) {
+    const T* __restrict__ v, const float* __restrict__ h0, T* o, float* __restrict__ hT,
+    const unsigned char* ws, int T_len, int nchunks, int dv, int slices, int xcd_map) {
   using G = ChunkGeom<T, DK, C>;
   constexpr int RT = G::RT, RH = G::RH, KBN = G::KBN, KBC = G::KBC, HALVES = G::HALVES;
-  constexpr int NHT = (RH * NCT + 3) / 4;  // state tiles per wave
+  constexpr int NRH = (RH + 3) / 4;  // state row tiles per wave (row tile rh = wave + 4 j)
   __shared__ __attribute__((aligned(16))) Frag s_h[KBN][NCT][64];
   __shared__ __attribute__((aligned(16))) Frag s_x[KBC][NCT][64];
   __shared__ __attribute__((aligned(16))) Frag s_u[KBC][NCT][64];
@@ -63,7 +63,7 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(
     else if (i < (int)(sizeof(s_h) + sizeof(s_x)) / 16) (&s_x[0][0][0])[i - sizeof(s_h) / 16] = z;
     else (&s_u[0][0][0])[i - (sizeof(s_h) + sizeof(s_x)) / 16] = z;
   }
-  __syncthreads();
+  lds_barrier();
 
   // write one accumulator tile (row tile rt) into a B-fragment exchange slot
   auto put = [&](Frag* base, int rt, int ct, f32x4 t) {
@@ -78,78 +78,134 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(
 
   // initial state
   const long long sbase = (long long)bh * DK * dv;
-  f32x4 hacc[NHT];
+  f32x4 hacc[NRH][NCT];
 #pragma unroll
-  for (int j = 0; j < NHT; ++j) {
-    hacc[j] = zero4();
-    const int tau = wave + 4 * j;
-    if (tau < RH * NCT) {
-      const int rh = tau / NCT, ct = tau % NCT;
-      if (h0) {
+  for (int j = 0; j < NRH; ++j) {
+    const int rh = wave + 4 * j;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) hacc[j][i] = h0[sbase + (long long)(16 * rh + 4 * g + i) * dv + col0 + 16 * ct + r];
+    for (int ct = 0; ct < NCT; ++ct) {
+      hacc[j][ct] = zero4();
+      if (rh < RH) {
+        if (h0) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            hacc[j][ct][i] = h0[sbase + (long long)(16 * rh + 4 * g + i) * dv + col0 + 16 * ct + r];
+        }
+        put(&s_h[0][0][0], rh, ct, hacc[j][ct]);
       }
-      put(&s_h[0][0][0], rh, ct, hacc[j]);
     }
   }
-  __syncthreads();
 
+  // operands of one chunk that this wave needs, loaded one chunk ahead
+  struct Ops {
+    Frag w[KBN], q[KBN], t[KBC], m[KBC], kr[NRH][KBC];
+    f32x4 d[NRH];
+    T v[NCT][4];     // raw values; masked and widened when used
+  };
   const long long vbase = (long long)bh * T_len;
-  for (int c = 0; c < nchunks; ++c) {
+  // waves that own a row tile of X, U and O (all of them when C = 64), and
+  // whether every wave's state row tiles exist (DK >= 64): compile-time where
+  // possible, so that the prefetch below is straight-line code
+  const bool xrow = RT >= 4 || wave < RT;
+  constexpr bool all_rh = RH % 4 == 0;
+  auto fetch = [&](Ops& x, int c) {
     const unsigned char* rec = ws + ((size_t)bh * nchunks + c) * G::BYTES;
+    const int t0 = c * C, cv = min(C, T_len - t0);
+    if (xrow) {
+#pragma unroll
+      for (int kb = 0; kb < KBN; ++kb) {
+        x.w[kb] = load_frag(rec + G::W_OFF + frag_slot(wave, kb, KBN, lane));
+        x.q[kb] = load_frag(rec + G::Q_OFF + frag_slot(wave, kb, KBN, lane));
+      }
+#pragma unroll
+      for (int kb = 0; kb < KBC; ++kb) {
+        x.t[kb] = load_frag(rec + G::T_OFF + frag_slot(wave, kb, KBC, lane));
+        x.m[kb] = load_frag(rec + G::M_OFF + frag_slot(wave, kb, KBC, lane));
+      }
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = 16 * wave + 4 * g + i;
+          x.v[ct][i] = v[(vbase + t0 + min(t, cv - 1)) * dv + col0 + 16 * ct + r];
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < NRH; ++j) {
+      const int rh = wave + 4 * j;
+      if (all_rh || rh < RH) {
+        x.d[j] = *reinterpret_cast<const f32x4*>(rec + G::D_OFF + (16 * rh + 4 * g) * 4);
+#pragma unroll
+        for (int kb = 0; kb < KBC; ++kb) x.kr[j][kb] = load_frag(rec + G::KR_OFF + frag_slot(rh, kb, KBC, lane));
+      }
+    }
+  };
+
+  // one chunk: consume `cur`, prefetch chunk c + 1 into `nxt`
+  auto step = [&](Ops& cur, Ops& nxt, int c) {
+    fetch(nxt, min(c + 1, nchunks - 1));   // the last step re-reads its own chunk (unused)
     const int t0 = c * C;
     const int cv = min(C, T_len - t0);
     f32x4 oacc[NCT];
-    if (wave < RT) {
+    if (xrow) {
       f32x4 xacc[NCT];
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int t = 16 * wave + 4 * g + i;
-          const float x = to_f32(v[(vbase + t0 + min(t, cv - 1)) * dv + col0 + 16 * ct + r]);
-          xacc[ct][i] = t < cv ? x : 0.f;
-        }
+        for (int i = 0; i < 4; ++i) xacc[ct][i] = 16 * wave + 4 * g + i < cv ? to_f32(cur.v[ct][i]) : 0.f;
         oacc[ct] = zero4();
       }
 #pragma unroll
       for (int kb = 0; kb < KBN; ++kb) {
-        const Frag wf = load_frag(rec + G::W_OFF + frag_slot(wave, kb, KBN, lane));
-        const Frag qf = load_frag(rec + G::Q_OFF + frag_slot(wave, kb, KBN, lane));
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
           const Frag hb = s_h[kb][ct][lane];
-          xacc[ct] = mma<T>(xacc[ct], wf, hb);
-          oacc[ct] = mma<T>(oacc[ct], qf, hb);
+          xacc[ct] = mma<T>(xacc[ct], cur.w[kb], hb);
+          oacc[ct] = mma<T>(oacc[ct], cur.q[kb], hb);
         }
       }
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) put(&s_x[0][0][0], wave, ct, xacc[ct]);
     }
-    __syncthreads();
+    lds_barrier();
 
-    if (wave < RT) {
+    if (xrow) {
       f32x4 uacc[NCT];
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) uacc[ct] = zero4();
 #pragma unroll
-      for (int kb = 0; kb < KBC; ++kb) {
-        const Frag tf = load_frag(rec + G::T_OFF + frag_slot(wave, kb, KBC, lane));
+      for (int kb = 0; kb < KBC; ++kb)
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) uacc[ct] = mma<T>(uacc[ct], tf, s_x[kb][ct][lane]);
-      }
+        for (int ct = 0; ct < NCT; ++ct) uacc[ct] = mma<T>(uacc[ct], cur.t[kb], s_x[kb][ct][lane]);
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) put(&s_u[0][0][0], wave, ct, uacc[ct]);
     }
-    __syncthreads();
+    lds_barrier();
 
-    if (wave < RT) {
+    Frag ub[KBC][NCT];
 #pragma unroll
-      for (int kb = 0; kb < KBC; ++kb) {
-        const Frag mf = load_frag(rec + G::M_OFF + frag_slot(wave, kb, KBC, lane));
+    for (int kb = 0; kb < KBC; ++kb)
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) oacc[ct] = mma<T>(oacc[ct], mf, s_u[kb][ct][lane]);
+      for (int ct = 0; ct < NCT; ++ct) ub[kb][ct] = s_u[kb][ct][lane];
+#pragma unroll
+    for (int j = 0; j < NRH; ++j) {
+      const int rh = wave + 4 * j;
+      if (all_rh || rh < RH) {
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+          f32x4 h = cur.d[j] * hacc[j][ct];
+#pragma unroll
+          for (int kb = 0; kb < KBC; ++kb) h = mma<T>(h, cur.kr[j][kb], ub[kb][ct]);
+          hacc[j][ct] = h;
+          put(&s_h[0][0][0], rh, ct, h);
+        }
       }
+    }
+    if (xrow) {
+#pragma unroll
+      for (int kb = 0; kb < KBC; ++kb)
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) oacc[ct] = mma<T>(oacc[ct], cur.m[kb], ub[kb][ct]);
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
 #pragma unroll
@@ -159,33 +215,30 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(
         }
       }
     }
-#pragma unroll
-    for (int j = 0; j < NHT; ++j) {
-      const int tau = wave + 4 * j;
-      if (tau < RH * NCT) {
-        const int rh = tau / NCT, ct = tau % NCT;
-        const f32x4 d = *reinterpret_cast<const f32x4*>(rec + G::D_OFF + (16 * rh + 4 * g) * 4);
-        f32x4 h = d * hacc[j];
-#pragma unroll
-        for (int kb = 0; kb < KBC; ++kb) {
-          const Frag kf = load_frag(rec + G::KR_OFF + frag_slot(rh, kb, KBC, lane));
-          h = mma<T>(h, kf, s_u[kb][ct][lane]);
-        }
-        hacc[j] = h;
-        put(&s_h[0][0][0], rh, ct, h);
-      }
-    }
-    __syncthreads();
+    lds_barrier();
+  };
+
+  // two operand buffers used in turn, so prefetched registers are never copied
+  Ops bufA, bufB;
+  if (nchunks > 0) fetch(bufA, 0);
+  lds_barrier();
+  int c = 0;
+  for (; c + 1 < nchunks; c += 2) {
+    step(bufA, bufB, c);
+    step(bufB, bufA, c + 1);
   }
+  if (c < nchunks) step(bufA, bufB, c);
 
   if (hT) {
 #pragma unroll
-    for (int j = 0; j < NHT; ++j) {
-      const int tau = wave + 4 * j;
-      if (tau < RH * NCT) {
-        const int rh = tau / NCT, ct = tau % NCT;
+    for (int j = 0; j < NRH; ++j) {
+      const int rh = wave + 4 * j;
+      if (rh < RH) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) hT[sbase + (long long)(16 * rh + 4 * g + i) * dv + col0 + 16 * ct + r] = hacc[j][i];
+        for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            hT[sbase + (long long)(16 * rh + 4 * g + i) * dv + col0 + 16 * ct + r] = hacc[j][ct][i];
       }
     }
   }

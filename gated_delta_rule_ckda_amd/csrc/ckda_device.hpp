@@ -123,6 +123,18 @@ __device__ __forceinline__ Frag load_frag(const void* p) {
 }
 __device__ __forceinline__ void store_frag(void* p, Frag f) { *reinterpret_cast<u32x4*>(p) = f.w; }
 
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS
+// operations, then s_barrier.  Unlike __syncthreads() it does not wait for
+// outstanding global loads and stores (on gfx9-family GPUs the vector memory
+// counter covers both), so prefetches and output stores stay in flight across
+// it.  Use it only where the waves exchange data through LDS alone.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Orders this wave's LDS writes before its later LDS reads (by any lane).
+__device__ __forceinline__ void lds_wave_fence() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
 // Wave-wide sum (wave64) via cross-lane shuffles.
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
