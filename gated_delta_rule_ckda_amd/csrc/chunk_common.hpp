@@ -1,21 +1,29 @@
 // chunk_common.hpp -- compile-time geometry of the chunkwise forward, shared by
-// the preparation kernel (writer of the per-chunk operand records) and the
-// state-pass kernel (their reader).
+// the Gram kernel (writer of the per-chunk records) and the state-pass kernel
+// (their reader).
 //
-// Per chunk of C positions of one (batch, head), with d_k = DK channels, the
-// record holds five matrix-core A operands, each as 1 KB fragments (64 lanes x
-// 16 bytes, K order of ckda_device.hpp) indexed [row tile][K block]:
-//   W   [C  x DK] = -(K~ . gamma)     keys with signs absorbed, decayed to their position
-//   Q   [C  x DK] =   Q~ . gamma      queries likewise
-//   KR  [DK x C ] = P_C (K~ . gamma_C / gamma)^T   keys decayed to the chunk end
-//   TB  [C  x C ] = (I + A)^-1 Diag(beta)          the UT/WY triangular solve
-//   M   [C  x C ] = causal (incl. diagonal) decayed query-key products
-// followed by DK floats d = P_C gamma_C (the signed decay of the whole chunk).
+// Per chunk of C positions of one (batch, head), the record holds two
+// matrix-core A operands over the chunk's positions, each as 1 KB fragments
+// (64 lanes x 16 bytes, K order of ckda_device.hpp) indexed [row tile][K block]:
+//   TB [C x C] = (I + Diag(beta) A)^-1 Diag(beta)    the UT/WY triangular solve
+//   M  [C x C] = causal (incl. diagonal) decayed query-key products
+// The gate-decayed keys and queries that multiply the state are rebuilt from
+// the inputs by the state-pass kernel itself, so they never pass through HBM.
+//
+// Padded fragments.  Operands that are assembled in LDS by threads that own a
+// pair of channels over a run of rows use a padded fragment: lane (g, r)'s
+// 16-byte slot sits at g * kFragGroupBytes + r * 16 (272-byte group stride
+// instead of 256).  A wave that stores one row of all channel pairs then hits
+// 64 distinct LDS banks, and a wave that reads the fragment (16 lanes of one
+// group at a time) hits 64 distinct banks as well.
 #pragma once
 
 #include "ckda_device.hpp"
 
 namespace ckda {
+
+constexpr int kFragGroupBytes = 16 * 16 + 16;        // 272
+constexpr int kFragPadBytes = 4 * kFragGroupBytes;   // 1088
 
 template <typename T, int DK, int C>
 struct ChunkGeom {
@@ -28,19 +36,104 @@ struct ChunkGeom {
   static constexpr int KBN = (DK + KB - 1) / KB;    // K blocks over channels
   static constexpr int KBC = (C + KB - 1) / KB;     // K blocks over positions
   static constexpr size_t FRAG = 1024;
-  static constexpr size_t W_OFF = 0;
-  static constexpr size_t Q_OFF = W_OFF + (size_t)RT * KBN * FRAG;
-  static constexpr size_t KR_OFF = Q_OFF + (size_t)RT * KBN * FRAG;
-  static constexpr size_t T_OFF = KR_OFF + (size_t)RH * KBC * FRAG;
+  static constexpr size_t T_OFF = 0;
   static constexpr size_t M_OFF = T_OFF + (size_t)RT * KBC * FRAG;
-  static constexpr size_t D_OFF = M_OFF + (size_t)RT * KBC * FRAG;
-  static constexpr size_t BYTES = (D_OFF + (size_t)DK * 4 + 255) / 256 * 256;
+  static constexpr size_t BYTES = (M_OFF + (size_t)RT * KBC * FRAG + 255) / 256 * 256;
 };
 
 // Byte offset of lane `lane`'s 16-byte slot in fragment (tile, kblock) of an
-// operand with `nkb` K blocks.
+// operand with `nkb` K blocks (unpadded layout, used in global memory).
 __host__ __device__ constexpr size_t frag_slot(int tile, int kblock, int nkb, int lane) {
   return (((size_t)tile * nkb + kblock) * 64 + lane) * 16;
 }
+
+// Position of K index `kk` (0 <= kk < DK or C) in a padded fragment row:
+// byte offset of its element relative to the start of row 0 of the fragment
+// block for K block 0, i.e. kb * kFragPadBytes + g * kFragGroupBytes + e * sizeof(T).
+template <typename T>
+__host__ __device__ constexpr int padded_col_offset(int kk) {
+  const int kb = kk / FragTraits<T>::KB, o = kk % FragTraits<T>::KB;
+  const int g = (sizeof(T) == 2 && o >= 16) ? (o - 16) / 4 : o / 4;
+  const int e = (sizeof(T) == 2 && o >= 16) ? 4 + (o - 16) % 4 : o % 4;
+  return kb * kFragPadBytes + g * kFragGroupBytes + e * (int)sizeof(T);
+}
+
+// Lane `lane`'s slot of padded fragment `f` of a buffer.
+__device__ __forceinline__ int padded_slot(int f, int lane) {
+  return f * kFragPadBytes + (lane >> 4) * kFragGroupBytes + (lane & 15) * 16;
+}
+
+// ---- raw element pairs: two adjacent channels of one row, loaded as one unit
+template <typename T> struct Pair;
+template <> struct Pair<bf16_t> {
+  typedef uint32_t raw;
+  static __device__ __forceinline__ raw load(const bf16_t* p) { return *reinterpret_cast<const uint32_t*>(p); }
+  static __device__ __forceinline__ float lo(raw w) { return __uint_as_float(w << 16); }
+  static __device__ __forceinline__ float hi(raw w) { return __uint_as_float(w & 0xFFFF0000u); }
+  static __device__ __forceinline__ raw ones() { return 0x3F803F80u; }
+  static __device__ __forceinline__ raw zeros() { return 0u; }
+  // store two values (channels c, c + 1) of one padded-fragment row
+  static __device__ __forceinline__ void put(unsigned char* p, float a, float b) {
+    *reinterpret_cast<uint32_t*>(p) = pack_bf16x2(a, b);
+  }
+};
+template <> struct Pair<float> {
+  typedef float __attribute__((ext_vector_type(2))) raw;
+  static __device__ __forceinline__ raw load(const float* p) { return *reinterpret_cast<const raw*>(p); }
+  static __device__ __forceinline__ float lo(raw w) { return w[0]; }
+  static __device__ __forceinline__ float hi(raw w) { return w[1]; }
+  static __device__ __forceinline__ raw ones() { return raw{1.f, 1.f}; }
+  static __device__ __forceinline__ raw zeros() { return raw{0.f, 0.f}; }
+  static __device__ __forceinline__ void put(unsigned char* p, float a, float b) {
+    *reinterpret_cast<raw*>(p) = raw{a, b};
+  }
+};
+
+// ---- four adjacent channels of one row, loaded as one unit
+template <typename T> struct Quad;
+template <> struct Quad<bf16_t> {
+  u32x2 w;
+  static __device__ __forceinline__ Quad load(const bf16_t* p) {
+    Quad x;
+    x.w = *reinterpret_cast<const u32x2*>(p);
+    return x;
+  }
+  static __device__ __forceinline__ Quad load(__amdgpu_buffer_rsrc_t r, int byte_off) {
+    Quad x;
+    x.w = __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, 0);
+    return x;
+  }
+  __device__ __forceinline__ float get(int j) const {
+    const uint32_t x = w[j >> 1];
+    return __uint_as_float((j & 1) ? (x & 0xFFFF0000u) : (x << 16));
+  }
+  __device__ __forceinline__ void pin() { ckda::pin(w); }
+  static __device__ __forceinline__ Quad ones() { return Quad{u32x2{0x3F803F80u, 0x3F803F80u}}; }
+  static __device__ __forceinline__ Quad zeros() { return Quad{u32x2{0u, 0u}}; }
+  // store four values as consecutive elements
+  static __device__ __forceinline__ void put(unsigned char* p, const float* v) {
+    *reinterpret_cast<u32x2*>(p) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+  }
+};
+template <> struct Quad<float> {
+  f32x4 w;
+  static __device__ __forceinline__ Quad load(const float* p) {
+    Quad x;
+    x.w = *reinterpret_cast<const f32x4*>(p);
+    return x;
+  }
+  static __device__ __forceinline__ Quad load(__amdgpu_buffer_rsrc_t r, int byte_off) {
+    Quad x;
+    x.w = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+    return x;
+  }
+  __device__ __forceinline__ float get(int j) const { return w[j]; }
+  __device__ __forceinline__ void pin() { ckda::pin(w); }
+  static __device__ __forceinline__ Quad ones() { return Quad{f32x4{1.f, 1.f, 1.f, 1.f}}; }
+  static __device__ __forceinline__ Quad zeros() { return Quad{f32x4{0.f, 0.f, 0.f, 0.f}}; }
+  static __device__ __forceinline__ void put(unsigned char* p, const float* v) {
+    *reinterpret_cast<f32x4*>(p) = f32x4{v[0], v[1], v[2], v[3]};
+  }
+};
 
 }  // namespace ckda

@@ -1,0 +1,542 @@
+// chunk_gram.hip -- the state-independent part of the chunkwise CKDA forward:
+// for every chunk of every (batch, head) at once, the decayed Gram matrices on
+// the matrix cores and the unit lower-triangular (UT/WY) solve, written as the
+// chunk's record (TB and M, chunk_common.hpp).
+//
+// Chunk form (derived from the recurrence of the "Complex KDA" paper, Eq. (1);
+// the pages do not print it).  For a chunk with local positions t and the
+// signed segment products of the gates
+//     G(t, j) = alpha_{j+1} ... alpha_t      (per channel, element-wise; 1 if t = j),
+//     A[t, j] = beta_t sum_c k_tc k_jc G_c(t, j)        (j < t)
+//     M[t, j] =        sum_c q_tc k_jc G_c(t, j)        (j <= t)
+//     TB = (I + A)^-1 Diag(beta).
+// Keeping the signs inside the products is the sign absorption of the
+// discussion slides ("Absorb cumulative signs into keys and queries"): the
+// parities P_t P_j of the absorbed keys are exactly the sign of G(t, j).
+//
+// Factorisation.  A decay G(t, j) enters a matrix-core product as x_t * y_j,
+// a row factor times a column factor around a reference point s, j <= s <= t.
+// With p_t the product of the gates of t's 16-row tile from its first row up
+// to t, s_j the product after j up to the end of j's tile, and P_b the product
+// over all of tile b, the lower triangle is covered by:
+//   * tile pairs (I, J), I > J: x_t = p_t, y_j = s_j, except that x carries
+//     P_2 when I = 3 and J <= 1 and y carries P_1 when J = 0 and I >= 2 --
+//     reference points at the tile boundary for adjacent tiles and between
+//     rows 31 and 32 for the lower-left 32 x 32 block of a 64-row chunk;
+//   * rows 8-15 x 0-7 of each diagonal tile ("LL" quadrant): s at row 8;
+//   * the two diagonal 8 x 8 quadrants of each tile: s at the quadrant's
+//     midpoint, the far-side factor being the reciprocal of a product of at
+//     most 4 gate magnitudes.
+// All factors but the last kind are products of gates, of modulus at most 1.
+// Gate magnitudes are floored at 2^-31 (sign kept), so the reciprocals stay
+// below 2^124; a power-of-two scale of 2^16 on one side centres the quadrant
+// factors in 2^-109 .. 2^109, keeping the bf16 operands (keys are unit
+// vectors) clear of the subnormal range.  Entries on the wrong side of the
+// diagonal, where the factors may overflow, are discarded by selection, never
+// by multiplication.  The floor changes a decay only where the true value is
+// below 2^-31 already.
+//
+// Thread layout.  Thread (tile b, pair u) owns channels 2u, 2u + 1 over the
+// 16 rows of row tile b: every product along the rows is a running product
+// inside the thread, and one load of a channel pair per row reads a whole row
+// per wave.  The factors are multiplied into keys and queries and stored, one
+// row at a time, into padded fragment buffers in LDS, from which the waves
+// feed the matrix cores.  Three stages (diagonal quadrants, LL quadrants, tile
+// pairs) reuse one LDS area; the tile products P_b go through LDS.
+#include "chunk_common.hpp"
+#include "ckda_internal.hpp"
+
+namespace ckda {
+
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
+
+constexpr float kQuadScale = 65536.f;           // 2^16
+constexpr float kQuadScaleInv = 1.f / 65536.f;
+
+// Floor gate magnitudes at 2^-31 on raw element bits, keeping the sign
+// (exponent field below that of 2^-31, zero and subnormals included, becomes
+// exactly +-2^-31).  NaN and infinity pass through.
+template <typename T> __device__ __forceinline__ typename Pair<T>::raw floor_gates(typename Pair<T>::raw w);
+template <>
+__device__ __forceinline__ uint32_t floor_gates<bf16_t>(uint32_t w) {
+  const uint32_t elo = w & 0x7F80u, ehi = w & 0x7F800000u;   // 2^-31: biased exponent 96
+  w = elo < 0x3000u ? ((w & 0xFFFF8000u) | 0x3000u) : w;
+  w = ehi < 0x30000000u ? ((w & 0x8000FFFFu) | 0x30000000u) : w;
+  return w;
+}
+template <>
+__device__ __forceinline__ Pair<float>::raw floor_gates<float>(Pair<float>::raw w) {
+  Pair<float>::raw out;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const uint32_t b = __float_as_uint(w[i]);
+    out[i] = __uint_as_float((b & 0x7F800000u) < 0x30000000u ? ((b & 0x80000000u) | 0x30000000u) : b);
+  }
+  return out;
+}
+
+template <typename T, int DK, int C>
+struct GramCfg : ChunkGeom<T, DK, C> {
+  using G = ChunkGeom<T, DK, C>;
+  static constexpr int RT = G::RT;
+  static constexpr int NU = DK / 2;               // channel pairs
+  static constexpr int NTH = (NU * RT + 63) / 64 * 64;
+  static constexpr int NW = NTH / 64;
+  static constexpr int TOPB = G::KBN * kFragPadBytes;   // one 16-row operand tile
+  // operand tiles of the tile-pair stage: key / query prefixes of tiles 1..RT-1,
+  // key suffixes of tiles 0..RT-2, and for RT = 4 the rescaled tile-3 rows and
+  // tile-0 columns of the 32 x 32 block
+  static constexpr int NSLOT_P = 3 * (RT - 1) + (RT == 4 ? 3 : 0);
+  static constexpr int NSLOT_C = 3 * RT;                // per tile: XDk, XDq, YD
+  static constexpr int NSLOT_D = 2 * RT;                // per tile: LLk, LLq
+  static constexpr int NSLOT = cmax(NSLOT_P, cmax(NSLOT_C, NSLOT_D));
+  static constexpr int LD = C + 4;                      // row stride of the fp32 scratch
+  static constexpr int SCR_BYTES = 3 * C * LD * 4;      // A, M, T in fp32
+  static constexpr int AREA = cmax(NSLOT * TOPB, SCR_BYTES);
+  static constexpr int BETA_OFF = AREA;
+  static constexpr int TOT_OFF = BETA_OFF + C * 4;      // [RT][DK] tile products
+  static constexpr int LDS_BYTES = TOT_OFF + RT * DK * 4;
+  // products (A and M of each block) per stage, and per wave
+  static constexpr int NBLK = RT * (RT - 1) / 2;
+  static constexpr int NPP = 2 * NBLK;
+  static constexpr int NPC = 2 * RT;                    // diagonal stages alike
+  static constexpr int PP = cmax((NPP + NW - 1) / NW, 1);
+  static constexpr int PC = cmax((NPC + NW - 1) / NW, 1);
+  // slots of the tile-pair stage
+  static constexpr __device__ int pk(int b) { return b - 1; }
+  static constexpr __device__ int pq(int b) { return RT - 1 + b - 1; }
+  static constexpr __device__ int sk(int b) { return 2 * (RT - 1) + b; }
+  static constexpr int X32K = 3 * (RT - 1), X32Q = X32K + 1, Y32 = X32K + 2;
+};
+
+// Tile pair n of the tile-pair stage: (I, J) and the operand slots of its key
+// rows, query rows and columns.
+template <typename P>
+__device__ __forceinline__ void tile_pair(int n, int& I, int& J, int& xk, int& xq, int& ys) {
+  if (n < P::RT - 1) {            // adjacent tiles, reference at their boundary
+    J = n;
+    I = n + 1;
+    xk = P::pk(I);
+    xq = P::pq(I);
+    ys = P::sk(J);
+  } else {                        // the 32 x 32 block of a 64-row chunk: (2,0), (3,1), (3,0)
+    const int m = n - (P::RT - 1);
+    I = m == 0 ? 2 : 3;
+    J = m == 1 ? 1 : 0;
+    xk = I == 2 ? P::pk(2) : P::X32K;
+    xq = I == 2 ? P::pq(2) : P::X32Q;
+    ys = J == 1 ? P::sk(1) : P::Y32;
+  }
+}
+
+template <typename T, int DK, int C>
+__global__ __launch_bounds__((GramCfg<T, DK, C>::NTH)) void chunk_gram_kernel(
+    const T* q, const T* k, const T* alpha, const T* beta, unsigned char* __restrict__ ws, int T_len,
+    int nchunks) {
+  using P = GramCfg<T, DK, C>;
+  using PR = Pair<T>;
+  typedef typename PR::raw raw;
+  constexpr int NU = P::NU, NW = P::NW, NTH = P::NTH, RT = P::RT, KBN = P::KBN, KBC = P::KBC,
+                TOPB = P::TOPB, EPL = P::EPL, KB = P::KB;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[P::LDS_BYTES];
+  unsigned char* area = lds;
+  float* s_beta = reinterpret_cast<float*>(lds + P::BETA_OFF);
+  float* s_tot = reinterpret_cast<float*>(lds + P::TOT_OFF);
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int g = lane >> 4, r = lane & 15;
+  const long long chunk_id = blockIdx.x;
+  const long long bh = chunk_id / nchunks;
+  const int t0 = (int)(chunk_id % nchunks) * C;
+  const int cv = min(C, T_len - t0);
+  const long long row0 = bh * (long long)T_len + t0;
+
+  if (tid < C) s_beta[tid] = tid < cv ? to_f32(beta[row0 + tid]) : 0.f;
+
+  const int b = tid / NU, u = tid % NU;
+  const bool act = b < RT;
+  const int c0 = 2 * u;
+  const int colofs = padded_col_offset<T>(c0);
+
+  // ---- this thread's rows: signed gates (floored), keys, queries
+  raw ra[16], rk[16], rq[16];
+  if (act) {
+    const size_t base = (size_t)(row0 + 16 * b) * DK + c0;
+    if (cv == C) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        ra[i] = PR::load(alpha + base + (size_t)i * DK);
+        rk[i] = PR::load(k + base + (size_t)i * DK);
+        rq[i] = PR::load(q + base + (size_t)i * DK);
+      }
+    } else {
+      // ragged last chunk: rows past the end act as identity steps (gate 1, no key)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int t = 16 * b + i;
+        const size_t off = base + (size_t)(min(t, cv - 1) - 16 * b) * DK;
+        const raw a = PR::load(alpha + off), kk = PR::load(k + off), qq = PR::load(q + off);
+        ra[i] = PR::ones();
+        rk[i] = PR::zeros();
+        rq[i] = PR::zeros();
+        if (t < cv) {
+          ra[i] = a;
+          rk[i] = kk;
+          rq[i] = qq;
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) ra[i] = floor_gates<T>(ra[i]);
+  }
+
+  // K blocks only partly covered by channels (bf16, DK = 16): the uncovered
+  // half of every fragment must read as zero in all stages
+  if constexpr (DK % KB != 0) {
+    for (int i = tid; i < P::NSLOT * TOPB / 16; i += NTH)
+      reinterpret_cast<u32x4*>(area)[i] = u32x4{0u, 0u, 0u, 0u};
+    lds_barrier();
+  }
+
+  // store the value pair of tile row i into operand tile `slot`
+  auto put = [&](int slot, int i, float v0, float v1) {
+    PR::put(area + slot * TOPB + colofs + i * 16, v0, v1);
+  };
+  // acc += X[xs] Y[ys]^T over all channels
+  auto gram = [&](f32x4 acc, int xs, int ys) {
+#pragma unroll
+    for (int kb = 0; kb < KBN; ++kb)
+      acc = mma<T>(acc, load_frag(area + xs * TOPB + padded_slot(kb, lane)),
+                   load_frag(area + ys * TOPB + padded_slot(kb, lane)));
+    return acc;
+  };
+#define LO(x) PR::lo(x)
+#define HI(x) PR::hi(x)
+
+  // ---- stage 1: the diagonal 8 x 8 quadrants, reference at their midpoints;
+  // tile products to LDS
+  f32x4 accC[P::PC];
+  {
+    if (act) {
+#pragma unroll
+      for (int q0 = 0; q0 < 16; q0 += 8) {
+        float p0 = kQuadScale, p1 = kQuadScale;
+#pragma unroll
+        for (int i = q0 + 4; i < q0 + 8; ++i) {   // am = scale x prefix from the midpoint, bm = 1 / am
+          p0 *= LO(ra[i]);
+          p1 *= HI(ra[i]);
+          const float b0 = __builtin_amdgcn_rcpf(p0), b1 = __builtin_amdgcn_rcpf(p1);
+          put(3 * b, i, LO(rk[i]) * p0, HI(rk[i]) * p1);
+          put(3 * b + 1, i, LO(rq[i]) * p0, HI(rq[i]) * p1);
+          put(3 * b + 2, i, LO(rk[i]) * b0, HI(rk[i]) * b1);
+        }
+        float s0 = kQuadScaleInv, s1 = kQuadScaleInv;
+#pragma unroll
+        for (int i = q0 + 3; i >= q0; --i) {      // bm = suffix up to the midpoint / scale, am = 1 / bm
+          const float a0 = __builtin_amdgcn_rcpf(s0), a1 = __builtin_amdgcn_rcpf(s1);
+          put(3 * b, i, LO(rk[i]) * a0, HI(rk[i]) * a1);
+          put(3 * b + 1, i, LO(rq[i]) * a0, HI(rq[i]) * a1);
+          put(3 * b + 2, i, LO(rk[i]) * s0, HI(rk[i]) * s1);
+          s0 *= LO(ra[i]);
+          s1 *= HI(ra[i]);
+        }
+      }
+      if constexpr (RT == 4) {
+        float p0 = 1.f, p1 = 1.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          p0 *= LO(ra[i]);
+          p1 *= HI(ra[i]);
+        }
+        *reinterpret_cast<float2*>(&s_tot[b * DK + c0]) = make_float2(p0, p1);
+      }
+    }
+    lds_barrier();
+#pragma unroll
+    for (int j = 0; j < P::PC; ++j) {
+      const int p = wave + NW * j;
+      accC[j] = zero4();
+      if (p < P::NPC) accC[j] = gram(accC[j], 3 * (p >> 1) + (p & 1), 3 * (p >> 1) + 2);
+    }
+    lds_barrier();
+  }
+
+  // ---- stage 2: rows 8-15 x 0-7 of each tile, reference at row 8.  LLk holds
+  // the column operand in rows 0-7 and the key row operand in rows 8-15, so
+  // LLk LLk^T and LLq LLk^T carry the block in their lower-left quadrant.
+  f32x4 accD[P::PC];
+  {
+    if (act) {
+      float x0 = 1.f, x1 = 1.f;
+#pragma unroll
+      for (int i = 8; i < 16; ++i) {
+        x0 *= LO(ra[i]);
+        x1 *= HI(ra[i]);
+        put(2 * b, i, LO(rk[i]) * x0, HI(rk[i]) * x1);
+        put(2 * b + 1, i, LO(rq[i]) * x0, HI(rq[i]) * x1);
+      }
+      float y0 = 1.f, y1 = 1.f;
+#pragma unroll
+      for (int i = 7; i >= 0; --i) {
+        put(2 * b, i, LO(rk[i]) * y0, HI(rk[i]) * y1);
+        y0 *= LO(ra[i]);
+        y1 *= HI(ra[i]);
+      }
+    }
+    lds_barrier();
+#pragma unroll
+    for (int j = 0; j < P::PC; ++j) {
+      const int p = wave + NW * j;
+      accD[j] = zero4();
+      if (p < P::NPC) accD[j] = gram(accD[j], 2 * (p >> 1) + (p & 1), 2 * (p >> 1));
+    }
+    lds_barrier();
+  }
+
+  // ---- stage 3: tile pairs below the diagonal
+  f32x4 accP[P::PP];
+  if constexpr (P::NPP > 0) {
+    if (act) {
+      // products over the tiles between: P_2 for tile-3 rows, P_1 for tile-0 columns
+      float m0 = 1.f, m1 = 1.f;
+      if (RT == 4 && (b == 3 || b == 0)) {
+        const float2 tt = *reinterpret_cast<const float2*>(&s_tot[(b == 3 ? 2 : 1) * DK + c0]);
+        m0 = tt.x;
+        m1 = tt.y;
+      }
+      if (b >= 1) {                // row operands: prefix inside the tile
+        float x0 = 1.f, x1 = 1.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          x0 *= LO(ra[i]);
+          x1 *= HI(ra[i]);
+          put(P::pk(b), i, LO(rk[i]) * x0, HI(rk[i]) * x1);
+          put(P::pq(b), i, LO(rq[i]) * x0, HI(rq[i]) * x1);
+          if (RT == 4 && b == 3) {
+            const float z0 = x0 * m0, z1 = x1 * m1;
+            put(P::X32K, i, LO(rk[i]) * z0, HI(rk[i]) * z1);
+            put(P::X32Q, i, LO(rq[i]) * z0, HI(rq[i]) * z1);
+          }
+        }
+      }
+      if (b <= RT - 2) {           // column operands: suffix inside the tile
+        float y0 = 1.f, y1 = 1.f;
+#pragma unroll
+        for (int i = 15; i >= 0; --i) {
+          put(P::sk(b), i, LO(rk[i]) * y0, HI(rk[i]) * y1);
+          if (RT == 4 && b == 0) put(P::Y32, i, LO(rk[i]) * (y0 * m0), HI(rk[i]) * (y1 * m1));
+          y0 *= LO(ra[i]);
+          y1 *= HI(ra[i]);
+        }
+      }
+    }
+    lds_barrier();
+#pragma unroll
+    for (int j = 0; j < P::PP; ++j) {
+      const int p = wave + NW * j;
+      accP[j] = zero4();
+      if (p < P::NPP) {
+        int I, J, xk, xq, ys;
+        tile_pair<P>(p >> 1, I, J, xk, xq, ys);
+        accP[j] = gram(accP[j], (p & 1) ? xq : xk, ys);
+      }
+    }
+    lds_barrier();
+  }
+#undef LO
+#undef HI
+
+  // ---- A (rows scaled by beta, strictly lower) and M (lower incl.) to LDS, fp32
+  float* As = reinterpret_cast<float*>(area);
+  constexpr int LD = P::LD;
+  float* Ms = As + C * LD;
+  float* Ts = Ms + C * LD;
+  for (int i = tid; i < C * C; i += NTH) {
+    const int row = i / C, col = i % C;
+    if (col / 16 > row / 16) {
+      As[row * LD + col] = 0.f;
+      Ms[row * LD + col] = 0.f;
+    }
+    Ts[row * LD + col] = 0.f;
+  }
+  auto put_tile = [&](int I, int J, int kind, f32x4 acc) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 16 * I + 4 * g + i, col = 16 * J + r;
+      if (kind == 0) As[row * LD + col] = acc[i] * s_beta[row];
+      else Ms[row * LD + col] = acc[i];
+    }
+  };
+  if constexpr (P::NPP > 0) {
+#pragma unroll
+    for (int j = 0; j < P::PP; ++j) {
+      const int p = wave + NW * j;
+      if (p < P::NPP) {
+        int I, J, xk, xq, ys;
+        tile_pair<P>(p >> 1, I, J, xk, xq, ys);
+        put_tile(I, J, p & 1, accP[j]);
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < P::PC; ++j) {
+    const int p = wave + NW * j;
+    if (p < P::NPC) {
+      const int tt = p >> 1, kind = p & 1;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int lr = 4 * g + i, row = 16 * tt + lr, col = 16 * tt + r;
+        const bool diagq = (lr >> 3) == (r >> 3);
+        const bool ll = lr >= 8 && r < 8;
+        if (kind == 0) {
+          const float a = diagq ? (r < lr ? accC[j][i] : 0.f) : (ll ? accD[j][i] : 0.f);
+          As[row * LD + col] = a * s_beta[row];
+        } else {
+          Ms[row * LD + col] = diagq ? (r <= lr ? accC[j][i] : 0.f) : (ll ? accD[j][i] : 0.f);
+        }
+      }
+    }
+  }
+  lds_barrier();
+
+  // ---- T = (I + A)^-1: diagonal 16x16 blocks by forward substitution
+  if (tid < 16 * RT) {
+    const int blk = tid >> 4, jc = tid & 15, o = 16 * blk;
+    float tcol[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float s = (i == jc) ? 1.f : 0.f;
+      const float* arow = As + (o + i) * LD + o;
+#pragma unroll
+      for (int k4 = 0; k4 < i; k4 += 4) {
+        const f32x4 av = *reinterpret_cast<const f32x4*>(arow + k4);
+#pragma unroll
+        for (int uu = 0; uu < 4; ++uu)
+          if (k4 + uu < i) s -= av[uu] * tcol[k4 + uu];
+      }
+      tcol[i] = s;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) Ts[(o + i) * LD + o + jc] = tcol[i];
+  }
+  lds_barrier();
+
+  // ---- off-diagonal blocks by distance on fp32 matrix cores:
+  //      T_IJ = -T_II sum_{K=J}^{I-1} A_IK T_KJ
+  for (int d = 1; d < RT; ++d) {
+    for (int J = wave; J + d < RT; J += NW) {
+      const int I = J + d;
+      f32x4 s = zero4();
+      for (int K = J; K < I; ++K) {
+        const float* arow = As + (16 * I + r) * LD + 16 * K;
+        const float* tb = Ts + (16 * K) * LD + 16 * J + r;
+        Frag fa, fb;
+        fa.w = __builtin_bit_cast(u32x4, *reinterpret_cast<const f32x4*>(arow + 4 * g));
+        fb.w = __builtin_bit_cast(u32x4, f32x4{tb[(4 * g + 0) * LD], tb[(4 * g + 1) * LD], tb[(4 * g + 2) * LD],
+                                               tb[(4 * g + 3) * LD]});
+        s = mma<float>(s, fa, fb);
+      }
+      const float* trow = Ts + (16 * I + r) * LD + 16 * I;
+      Frag fa;
+      fa.w = __builtin_bit_cast(u32x4, *reinterpret_cast<const f32x4*>(trow + 4 * g));
+      const f32x4 tij = mma<float>(zero4(), fa, frag_from_acc_f32(s));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Ts[(16 * I + 4 * g + i) * LD + 16 * J + r] = -tij[i];
+    }
+    lds_barrier();
+  }
+
+  // ---- record: T Diag(beta) and M fragments
+  constexpr int NF = RT * KBC;
+  unsigned char* rec = ws + (size_t)chunk_id * P::BYTES;
+  for (int f = wave; f < 2 * NF; f += NW) {
+    const bool isT = f < NF;
+    const int ff = isT ? f : f - NF;
+    const int rt = ff / KBC, kb = ff % KBC;
+    const float* src = (isT ? Ts : Ms) + (16 * rt + r) * LD;
+    float vals[8];
+    // K order: elements 0-3 are 4 consecutive columns, so are 4-7 (bf16)
+#pragma unroll
+    for (int hh = 0; hh < EPL / 4; ++hh) {
+      const int col = kb * KB + kappa<T>(g, 4 * hh);
+      f32x4 x = zero4();
+      if (col < C) {
+        x = *reinterpret_cast<const f32x4*>(src + col);
+        if (isT) x *= *reinterpret_cast<const f32x4*>(s_beta + col);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) vals[4 * hh + e] = x[e];
+    }
+    Frag out;
+    if constexpr (sizeof(T) == 2) {
+      out.w = u32x4{pack_bf16x2(vals[0], vals[1]), pack_bf16x2(vals[2], vals[3]), pack_bf16x2(vals[4], vals[5]),
+                    pack_bf16x2(vals[6], vals[7])};
+    } else {
+      out.w = __builtin_bit_cast(u32x4, f32x4{vals[0], vals[1], vals[2], vals[3]});
+    }
+    store_frag(rec + (isT ? P::T_OFF : P::M_OFF) + frag_slot(rt, kb, KBC, lane), out);
+  }
+}
+
+template <typename T, int DK, int C>
+hipError_t launch_gram_t(const ChunkArgs& a, long long total_chunks, int nchunks) {
+  using P = GramCfg<T, DK, C>;
+  hipLaunchKernelGGL((chunk_gram_kernel<T, DK, C>), dim3((unsigned)total_chunks), dim3(P::NTH), 0, a.stream,
+                     (const T*)a.q, (const T*)a.k, (const T*)a.alpha, (const T*)a.beta,
+                     (unsigned char*)a.workspace, a.T, nchunks);
+  return hipGetLastError();
+}
+
+template <typename T, int DK>
+hipError_t gram_chunk_dispatch(const ChunkArgs& a, long long total, int nch) {
+  switch (a.chunk) {
+    case 16: return launch_gram_t<T, DK, 16>(a, total, nch);
+    case 32: return launch_gram_t<T, DK, 32>(a, total, nch);
+    case 64: return launch_gram_t<T, DK, 64>(a, total, nch);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename T>
+hipError_t gram_dk_dispatch(const ChunkArgs& a, long long total, int nch) {
+  switch (a.dk) {
+    case 16: return gram_chunk_dispatch<T, 16>(a, total, nch);
+    case 32: return gram_chunk_dispatch<T, 32>(a, total, nch);
+    case 64: return gram_chunk_dispatch<T, 64>(a, total, nch);
+    case 128: return gram_chunk_dispatch<T, 128>(a, total, nch);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_chunk_gram(const ChunkArgs& a, long long total_chunks, int nchunks) {
+  if (total_chunks == 0) return hipSuccess;
+  return a.dtype == 1 ? gram_dk_dispatch<bf16_t>(a, total_chunks, nchunks)
+                      : gram_dk_dispatch<float>(a, total_chunks, nchunks);
+}
+
+template <typename T, int DK>
+static ChunkRecord record_c(int chunk) {
+  switch (chunk) {
+    case 16: return {ChunkGeom<T, DK, 16>::T_OFF, ChunkGeom<T, DK, 16>::M_OFF, ChunkGeom<T, DK, 16>::BYTES};
+    case 32: return {ChunkGeom<T, DK, 32>::T_OFF, ChunkGeom<T, DK, 32>::M_OFF, ChunkGeom<T, DK, 32>::BYTES};
+    case 64: return {ChunkGeom<T, DK, 64>::T_OFF, ChunkGeom<T, DK, 64>::M_OFF, ChunkGeom<T, DK, 64>::BYTES};
+  }
+  return {0, 0, 0};
+}
+
+template <typename T>
+static ChunkRecord record_t(int dk, int chunk) {
+  switch (dk) {
+    case 16: return record_c<T, 16>(chunk);
+    case 32: return record_c<T, 32>(chunk);
+    case 64: return record_c<T, 64>(chunk);
+    case 128: return record_c<T, 128>(chunk);
+  }
+  return {0, 0, 0};
+}
+
+ChunkRecord chunk_record_layout(int dk, int chunk, int dtype) {
+  return dtype == 1 ? record_t<bf16_t>(dk, chunk) : record_t<float>(dk, chunk);
+}
+
+}  // namespace ckda

@@ -135,6 +135,50 @@ __device__ __forceinline__ void lds_barrier() {
 // Orders this wave's LDS writes before its later LDS reads (by any lane).
 __device__ __forceinline__ void lds_wave_fence() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
+// ---- register-level helpers
+// Ties a value to this point of the program: the compiler may not move its
+// uses above it, so a widening of prefetched bits cannot be hoisted into an
+// earlier phase (which would make that phase wait for the prefetch).
+__device__ __forceinline__ void pin(uint32_t& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void pin(u32x2& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void pin(f32x4& x) { asm volatile("" : "+v"(x)); }
+
+__device__ __forceinline__ uint32_t elem_bits(bf16_t x) { return x.bits; }
+__device__ __forceinline__ uint32_t elem_bits(float x) { return __float_as_uint(x); }
+template <typename T> __device__ __forceinline__ float bits_to_f32(uint32_t u);
+template <> __device__ __forceinline__ float bits_to_f32<bf16_t>(uint32_t u) { return __uint_as_float(u << 16); }
+template <> __device__ __forceinline__ float bits_to_f32<float>(uint32_t u) { return __uint_as_float(u); }
+
+// DPP lane permutation inside groups of four lanes (quad_perm selector).
+enum : int {
+  kDppQuad1032 = 1 | (0 << 2) | (3 << 4) | (2 << 6),   // swap neighbouring lanes
+};
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// ---- range-checked buffer access
+// A raw buffer resource over `bytes` bytes from `base` (stride 0, so an access
+// at byte offset >= bytes is out of range: stores are dropped, loads read 0).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+template <typename T> __device__ __forceinline__ uint32_t load_elem_bits(__amdgpu_buffer_rsrc_t r, int byte_off);
+template <> __device__ __forceinline__ uint32_t load_elem_bits<float>(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0);
+}
+template <> __device__ __forceinline__ uint32_t load_elem_bits<bf16_t>(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, byte_off, 0, 0);
+}
+template <typename T> __device__ __forceinline__ void store_elem(__amdgpu_buffer_rsrc_t r, int byte_off, float x);
+template <> __device__ __forceinline__ void store_elem<float>(__amdgpu_buffer_rsrc_t r, int byte_off, float x) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, byte_off, 0, 0);
+}
+template <> __device__ __forceinline__ void store_elem<bf16_t>(__amdgpu_buffer_rsrc_t r, int byte_off, float x) {
+  __builtin_amdgcn_raw_buffer_store_b16(from_f32<bf16_t>(x).bits, r, byte_off, 0, 0);
+}
+
 // Wave-wide sum (wave64) via cross-lane shuffles.
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll

@@ -25,10 +25,10 @@ struct ChunkArgs {
   hipStream_t stream;
 };
 
-// Layout of the per-chunk operand records the preparation kernel writes and
-// the state-pass kernel reads (byte offsets inside one chunk's record).
+// Layout of the per-chunk records the Gram kernel writes and the state-pass
+// kernel reads (byte offsets inside one chunk's record).
 struct ChunkRecord {
-  size_t w_off, q_off, kr_off, t_off, m_off, d_off, bytes;
+  size_t t_off, m_off, bytes;
 };
 ChunkRecord chunk_record_layout(int dk, int chunk, int dtype);
 

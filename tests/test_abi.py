@@ -41,9 +41,12 @@ def test_status_strings():
 def test_workspace_size():
     L = ck.lib()
     ws = L.ckda_chunk_fwd_workspace_size
-    # bf16, d128, chunk 64: 4 A-operand fragments of 1 KB per (row tile, K block) ...
+    # bf16, chunk 64: the record holds TB and M, 4 row tiles x 2 K blocks of
+    # 1 KB fragments each, independent of d_k
     per_chunk = ws(1, 1, 64, 128, 128, 64, 1)
-    assert per_chunk == 1024 * (2 * 4 * 4 + 8 * 2 + 2 * 4 * 2) + 512
+    assert per_chunk == 1024 * (2 * 4 * 2)
+    assert ws(1, 1, 64, 64, 128, 64, 1) == per_chunk
+    assert ws(1, 1, 64, 128, 128, 64, 0) == 1024 * (2 * 4 * 4)  # fp32: K blocks of 16
     assert ws(4, 16, 4096, 128, 128, 64, 1) == 64 * 64 * per_chunk
     assert ws(1, 1, 65, 128, 128, 64, 1) == 2 * per_chunk       # ragged tail = one more chunk
     assert ws(1, 1, 64, 128, 128, 48, 1) == 0                  # unsupported chunk
@@ -80,6 +83,7 @@ def call_dec(**kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(q=None), 1), (dict(o=None), 1), (dict(beta=None), 1),
     (dict(T=-1), 2), (dict(B=-2), 2),
+    (dict(T=1 << 24, dv=128), 2),                                 # one head's output over 2 GiB
     (dict(dk=48), 3), (dict(dv=256), 3), (dict(chunk=128), 3), (dict(dtype=2), 3),
     (dict(q=BASE + 2), 2),                                        # misaligned
     (dict(o=BASE + 2 * MB + 64), 4),                              # o overlaps v
