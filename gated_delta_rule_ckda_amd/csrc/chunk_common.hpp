@@ -108,6 +108,10 @@ template <> struct Quad<bf16_t> {
     return __uint_as_float((j & 1) ? (x & 0xFFFF0000u) : (x << 16));
   }
   __device__ __forceinline__ void pin() { ckda::pin(w); }
+  // element j's bits to LDS unchanged
+  __device__ __forceinline__ void store_raw(unsigned char* p, int j) const {
+    *reinterpret_cast<uint16_t*>(p) = (uint16_t)((j & 1) ? (w[j >> 1] >> 16) : w[j >> 1]);
+  }
   static __device__ __forceinline__ Quad ones() { return Quad{u32x2{0x3F803F80u, 0x3F803F80u}}; }
   static __device__ __forceinline__ Quad zeros() { return Quad{u32x2{0u, 0u}}; }
   // store four values as consecutive elements
@@ -129,6 +133,7 @@ template <> struct Quad<float> {
   }
   __device__ __forceinline__ float get(int j) const { return w[j]; }
   __device__ __forceinline__ void pin() { ckda::pin(w); }
+  __device__ __forceinline__ void store_raw(unsigned char* p, int j) const { *reinterpret_cast<float*>(p) = w[j]; }
   static __device__ __forceinline__ Quad ones() { return Quad{f32x4{1.f, 1.f, 1.f, 1.f}}; }
   static __device__ __forceinline__ Quad zeros() { return Quad{f32x4{0.f, 0.f, 0.f, 0.f}}; }
   static __device__ __forceinline__ void put(unsigned char* p, const float* v) {

@@ -351,14 +351,8 @@ __global__ __launch_bounds__((GramCfg<T, DK, C>::NTH)) void chunk_gram_kernel(
   constexpr int LD = P::LD;
   float* Ms = As + C * LD;
   float* Ts = Ms + C * LD;
-  for (int i = tid; i < C * C; i += NTH) {
-    const int row = i / C, col = i % C;
-    if (col / 16 > row / 16) {
-      As[row * LD + col] = 0.f;
-      Ms[row * LD + col] = 0.f;
-    }
-    Ts[row * LD + col] = 0.f;
-  }
+  // Only the blocks on and below the diagonal are written and read; the
+  // record's blocks above the diagonal are emitted as zeros.
   auto put_tile = [&](int I, int J, int kind, f32x4 acc) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -460,7 +454,7 @@ __global__ __launch_bounds__((GramCfg<T, DK, C>::NTH)) void chunk_gram_kernel(
     for (int hh = 0; hh < EPL / 4; ++hh) {
       const int col = kb * KB + kappa<T>(g, 4 * hh);
       f32x4 x = zero4();
-      if (col < C) {
+      if (col < C && col / 16 <= rt) {
         x = *reinterpret_cast<const f32x4*>(src + col);
         if (isT) x *= *reinterpret_cast<const f32x4*>(s_beta + col);
       }

@@ -18,9 +18,12 @@
 // U for O and H), so the matrix waves exchange nothing.  The decay of H is
 // applied element-wise in fp32; the state itself is never rounded.
 //
-// Four "build waves" assemble the A operands of the next chunk in LDS while
+// Four "build waves" assemble the operands of the next chunk in LDS while
 // the matrix waves work on the current one: W, Q~ and KR^T from the chunk's
-// keys, queries and gates, d, and a copy of TB and M from the record.  Build
+// keys, queries and gates, d, a copy of TB and M from the record, and the
+// slice's values V.  So the matrix waves issue no global loads, only the
+// output stores: with loads and stores in flight together, every wait for a
+// load would also wait for all stores.  Build
 // thread (tile bb, channel quad cq, half hf) owns channels 4 cq .. 4 cq + 3
 // over rows 16 bb + 8 hf .. + 7: the gate products along the rows are running
 // products inside the thread, the two halves of a tile meet through a DPP
@@ -49,7 +52,10 @@ struct StateCfg : ChunkGeom<T, DK, C> {
   static constexpr int KR_OFF = Q_OFF + G::RT * G::KBN * kFragPadBytes;
   static constexpr int TM_OFF = KR_OFF + G::RH * G::KBC * kFragPadBytes;
   static constexpr int D_OFF = TM_OFF + NTM * 1024;
-  static constexpr int SET_BYTES = D_OFF + DK * 4;
+  // V of the slice in accumulator order: [matrix wave][row tile][lane][4]
+  static constexpr int V_OFF = D_OFF + DK * 4;
+  static constexpr int V_BYTES = NMW * G::RT * 64 * 4 * (int)sizeof(T);
+  static constexpr int SET_BYTES = V_OFF + V_BYTES;
   static constexpr int TOT_BYTES = 2 * G::RT * DK * 4;      // tile products of two chunks
   static constexpr int NBUF = 2 * SET_BYTES + TOT_BYTES <= 160 * 1024 ? 2 : 1;
   static constexpr int LDS_BYTES = NBUF * SET_BYTES + TOT_BYTES;
@@ -87,9 +93,6 @@ __device__ __forceinline__ void with_slot(int c, F&& f) {
     if (j == 2) f(std::integral_constant<int, (NPF > 2 ? 2 : 0)>{});
   }
 }
-
-// Matrix-wave prefetch depth (chunks of V values).
-constexpr int kMatrixPrefetch = 2;
 
 template <typename T, int DK, int C, int NMW>
 __global__ __launch_bounds__((StateCfg<T, DK, C, NMW>::NTHREADS)) void chunk_state_kernel(
@@ -137,12 +140,10 @@ __global__ __launch_bounds__((StateCfg<T, DK, C, NMW>::NTHREADS)) void chunk_sta
 
   if (matrix) {
     // ============================================================ matrix waves
-    // This head's value and output rows as range-checked buffers: rows past
-    // the end of the sequence read as zero and their stores are dropped.
-    const __amdgpu_buffer_rsrc_t vrsrc = make_rsrc(v + rowbase * dv, (uint32_t)((size_t)T_len * dv * E));
+    // This head's output rows as a range-checked buffer: stores to rows past
+    // the end of the sequence are dropped.
     const __amdgpu_buffer_rsrc_t orsrc = make_rsrc(o + rowbase * dv, (uint32_t)((size_t)T_len * dv * E));
     const int col = slice * 16 * NMW + 16 * wave + r;       // this lane's value column
-    const int v_voff = ((4 * g) * dv + col) * E;
     const long long sbase = (long long)bh * DK * dv;
     f32x4 hacc[RH];
 #pragma unroll
@@ -153,32 +154,15 @@ __global__ __launch_bounds__((StateCfg<T, DK, C, NMW>::NTHREADS)) void chunk_sta
         for (int i = 0; i < 4; ++i) hacc[j][i] = h0[sbase + (long long)(16 * j + 4 * g + i) * dv + col];
       }
     }
-    struct VRaw {
-      uint32_t x[RT][4];
-    };
-    VRaw vr[kMatrixPrefetch];
-    auto vfetch = [&](VRaw& x, int c) __attribute__((always_inline)) {
-      c = min(c, nchunks - 1);
-      const int ofs = v_voff + c * C * dv * E;
-#pragma unroll
-      for (int pt = 0; pt < RT; ++pt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) x.x[pt][i] = load_elem_bits<T>(vrsrc, ofs + ((16 * pt + i) * dv) * E);
-    };
     // B operand of K block kb from accumulator tiles (bf16: two tiles)
     auto bfrag = [&](const f32x4* acc, int kb, int ntiles) __attribute__((always_inline)) {
       if constexpr (BF) return frag_from_acc_bf16(acc[2 * kb], 2 * kb + 1 < ntiles ? acc[2 * kb + 1] : zero4());
       else return frag_from_acc_f32(acc[kb]);
     };
-    if (nchunks > 0) {
-#pragma unroll
-      for (int j = 0; j < kMatrixPrefetch; ++j) vfetch(vr[j], j);
-    }
     lds_barrier();   // the build waves prepare chunk 0
     lds_barrier();
 
-    auto iter = [&](int c, auto jconst) __attribute__((always_inline)) {
-      constexpr int J = decltype(jconst)::value;
+    auto iter = [&](int c, auto) __attribute__((always_inline)) {
       const unsigned char* set = set_of(c);
       // Operand fragments are read from LDS one group ahead of the products
       // that use them; the scheduling barriers keep each group of reads
@@ -230,11 +214,7 @@ __global__ __launch_bounds__((StateCfg<T, DK, C, NMW>::NTHREADS)) void chunk_sta
           ld_wq(pt);
         }
         __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          pin(vr[J].x[pt][i]);   // keeps the widening (and its wait) in this chunk
-          xacc[pt][i] = bits_to_f32<T>(vr[J].x[pt][i]);
-        }
+        xacc[pt] = load_vals4<T>(set + S::V_OFF + ((wave * RT + pt) * 64 + lane) * 4 * E);
         oacc[pt] = zero4();
 #pragma unroll
         for (int kb = 0; kb < KBN; ++kb) {
@@ -244,7 +224,6 @@ __global__ __launch_bounds__((StateCfg<T, DK, C, NMW>::NTHREADS)) void chunk_sta
         __builtin_amdgcn_sched_barrier(0);
       }
       if constexpr (DB == 1) ld_tm(tf, 0);
-      vfetch(vr[J], c + kMatrixPrefetch);
       if constexpr (DB == 2) ld_tm(mf, 1);
       __builtin_amdgcn_sched_barrier(0);
       // U = TB X
@@ -290,9 +269,11 @@ __global__ __launch_bounds__((StateCfg<T, DK, C, NMW>::NTHREADS)) void chunk_sta
         __builtin_amdgcn_sched_barrier(0);
       }
       lds_barrier();
-      if constexpr (NBUF == 1) lds_barrier();   // the build waves rewrite the one set
+      if constexpr (NBUF == 1) {
+        lds_barrier();   // the build waves rewrite the one set
+      }
     };
-    run_chunks<kMatrixPrefetch>(nchunks, iter);
+    run_chunks<1>(nchunks, iter);
 
     if (hT) {
 #pragma unroll
@@ -319,17 +300,26 @@ __global__ __launch_bounds__((StateCfg<T, DK, C, NMW>::NTHREADS)) void chunk_sta
     // bf16 inputs are prefetched whole; for fp32 (twice the registers) keys
     // and queries are loaded when the build needs them
     constexpr bool KQ_AHEAD = BF;
+    // values of the slice: thread vt reads 8 consecutive columns of one row
+    constexpr int VCG = 2 * NMW;                     // 8-column groups per row
+    const int vrow = bt / VCG, vcg = bt % VCG;
+    const bool vact = bt < C * VCG;
+    const __amdgpu_buffer_rsrc_t vrsrc = make_rsrc(v + rowbase * dv, (uint32_t)((size_t)T_len * dv * E));
+    const int v_voff = (vrow * dv + slice * 16 * NMW + 8 * vcg) * E;
     struct BRaw {
       Quad<T> a[8], k[KQ_AHEAD ? 8 : 1], q[KQ_AHEAD ? 8 : 1];
     };
     BRaw br[BPF];
-    Frag tm[NTMW];          // TB and M fragments on their way to LDS
+    // TB and M fragments and 8 values on their way to LDS (loaded at the start
+    // of an iteration, stored at its end)
+    Frag tm[NTMW];
+    Quad<T> vv[2];
     // products of the other half of the tile before / after this half, from
     // btotals of a chunk to its bbuild one iteration later
     float pre[4], suf[4];
     Quad<T> kq_k[8], kq_q[8];                    // fp32: keys and queries of the chunk being built
-    // the record's TB and M fragments, copied by every build wave whatever
-    // its share of the channel work
+    // the record's TB and M fragments and the slice's values, moved by every
+    // build wave whatever its share of the channel work
     auto tmload = [&](int c) __attribute__((always_inline)) {
       c = min(c, nchunks - 1);
 #pragma unroll
@@ -337,6 +327,9 @@ __global__ __launch_bounds__((StateCfg<T, DK, C, NMW>::NTHREADS)) void chunk_sta
         const int f = min(bw + 4 * j, NTM - 1);
         tm[j].w = __builtin_amdgcn_raw_buffer_load_b128(rrsrc, c * (int)S::BYTES + (f * 64 + lane) * 16, 0, 0);
       }
+      const int ofs = v_voff + c * C * dv * E;
+      vv[0] = Quad<T>::load(vrsrc, ofs);
+      vv[1] = Quad<T>::load(vrsrc, ofs + 4 * E);
     };
     auto tmstore = [&](int c) __attribute__((always_inline)) {
       unsigned char* set = set_of(c);
@@ -344,6 +337,15 @@ __global__ __launch_bounds__((StateCfg<T, DK, C, NMW>::NTHREADS)) void chunk_sta
       for (int j = 0; j < NTMW; ++j) {
         const int f = bw + 4 * j;
         if (f < NTM) store_frag(set + S::TM_OFF + (f * 64 + lane) * 16, tm[j]);
+      }
+      if (vact) {
+        // element (row vrow, column 8 vcg + e) -> matrix wave mw, lane (g, r), slot i
+        const int pt = vrow / 16, vg = (vrow % 16) / 4, vi = vrow % 4;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int cc = 8 * vcg + e, mw = cc / 16, rr = cc % 16;
+          vv[e >> 2].store_raw(set + S::V_OFF + (((mw * RT + pt) * 64 + vg * 16 + rr) * 4 + vi) * E, e & 3);
+        }
       }
     };
     // inputs of chunk c (clamped to the last chunk); rows past the end read 0
@@ -441,24 +443,29 @@ __global__ __launch_bounds__((StateCfg<T, DK, C, NMW>::NTHREADS)) void chunk_sta
         *reinterpret_cast<f32x4*>(set + S::D_OFF + bc0 * 4) =
             f32x4{gm[0] * suf[0] * after[0], gm[1] * suf[1] * after[1], gm[2] * suf[2] * after[2],
                   gm[3] * suf[3] * after[3]};
-      // KR^T = (K . G(C, .))^T: rows = channels, K = positions brow0 .. brow0 + 7
-      float e[4], kr[4][8];
+      // KR^T = (K . G(C, .))^T: rows = channels, K = positions brow0 .. brow0 + 7,
+      // written four positions at a time
+      float e[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) e[j] = suf[j] * after[j];
 #pragma unroll
-      for (int i = 7; i >= 0; --i) {
+      for (int hq = 1; hq >= 0; --hq) {
+        float kr[4][4];
+#pragma unroll
+        for (int i = 3; i >= 0; --i) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            kr[j][i] = kk[4 * hq + i].get(j) * e[j];
+            e[j] *= x.a[4 * hq + i].get(j);
+          }
+        }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          kr[j][i] = kk[i].get(j) * e[j];
-          e[j] *= x.a[i].get(j);
+          const int ch = bc0 + j;
+          Quad<T>::put(set + S::KR_OFF + (ch >> 4) * KBC * kFragPadBytes + (ch & 15) * 16 +
+                           padded_col_offset<T>(brow0 + 4 * hq),
+                       kr[j]);
         }
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int ch = bc0 + j;
-        unsigned char* base = set + S::KR_OFF + (ch >> 4) * KBC * kFragPadBytes + (ch & 15) * 16;
-        Quad<T>::put(base + padded_col_offset<T>(brow0), &kr[j][0]);
-        Quad<T>::put(base + padded_col_offset<T>(brow0 + 4), &kr[j][4]);
       }
     };
 
@@ -494,7 +501,9 @@ __global__ __launch_bounds__((StateCfg<T, DK, C, NMW>::NTHREADS)) void chunk_sta
     auto iter = [&](int c, auto jconst, bool fix) __attribute__((always_inline)) {
       constexpr int J = decltype(jconst)::value;
       constexpr int JA = (J + 1) % BPF;
-      if constexpr (NBUF == 1) lds_barrier();    // the matrix waves are done with the one set
+      if constexpr (NBUF == 1) {
+        lds_barrier();   // the matrix waves are done with the one set
+      }
       tmload(c + 1);
       if (bact) {
         bbuild(br[JA], c + 1);

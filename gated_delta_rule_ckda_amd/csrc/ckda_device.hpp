@@ -171,6 +171,23 @@ template <> __device__ __forceinline__ uint32_t load_elem_bits<float>(__amdgpu_b
 template <> __device__ __forceinline__ uint32_t load_elem_bits<bf16_t>(__amdgpu_buffer_rsrc_t r, int byte_off) {
   return __builtin_amdgcn_raw_buffer_load_b16(r, byte_off, 0, 0);
 }
+// one element to LDS in the storage type; four consecutive elements from LDS
+template <typename T> __device__ __forceinline__ void store_elem_lds(unsigned char* p, float x);
+template <> __device__ __forceinline__ void store_elem_lds<float>(unsigned char* p, float x) {
+  *reinterpret_cast<float*>(p) = x;
+}
+template <> __device__ __forceinline__ void store_elem_lds<bf16_t>(unsigned char* p, float x) {
+  *reinterpret_cast<uint16_t*>(p) = from_f32<bf16_t>(x).bits;
+}
+template <typename T> __device__ __forceinline__ f32x4 load_vals4(const unsigned char* p);
+template <> __device__ __forceinline__ f32x4 load_vals4<float>(const unsigned char* p) {
+  return *reinterpret_cast<const f32x4*>(p);
+}
+template <> __device__ __forceinline__ f32x4 load_vals4<bf16_t>(const unsigned char* p) {
+  const u32x2 w = *reinterpret_cast<const u32x2*>(p);
+  return f32x4{__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xFFFF0000u), __uint_as_float(w[1] << 16),
+               __uint_as_float(w[1] & 0xFFFF0000u)};
+}
 template <typename T> __device__ __forceinline__ void store_elem(__amdgpu_buffer_rsrc_t r, int byte_off, float x);
 template <> __device__ __forceinline__ void store_elem<float>(__amdgpu_buffer_rsrc_t r, int byte_off, float x) {
   __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, byte_off, 0, 0);
