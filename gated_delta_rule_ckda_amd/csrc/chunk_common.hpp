@@ -2,14 +2,17 @@
 // the Gram kernel (writer of the per-chunk records) and the state-pass kernel
 // (their reader).
 //
-// Per chunk of C positions of one (batch, head), the record holds two
-// matrix-core A operands over the chunk's positions, each as 1 KB fragments
-// (64 lanes x 16 bytes, K order of ckda_device.hpp) indexed [row tile][K block]:
-//   TB [C x C] = (I + Diag(beta) A)^-1 Diag(beta)    the UT/WY triangular solve
-//   M  [C x C] = causal (incl. diagonal) decayed query-key products
-// The gate-decayed keys and queries that multiply the state are rebuilt from
-// the inputs by the state-pass kernel itself, so they never pass through HBM.
-//
+// Per chunk of C positions of one (batch, head), the record holds the
+// matrix-core A operands of the state pass as 1 KB fragments (64 lanes x 16
+// bytes, K order of ckda_device.hpp), each operand indexed [row tile][K block]:
+//   TB  [C x C]  = (I + Diag(beta) A)^-1 Diag(beta)    the UT/WY triangular solve
+//   M   [C x C]  = causal (incl. diagonal) decayed query-key products
+//   W   [C x DK] = -(K . gamma)      gamma_t: signed gate product from the chunk start to t
+//   Q   [C x DK] =   Q . gamma
+//   KR  [DK x C] = (K . G(C, .))^T   G(C, t): signed gate product after t to the chunk end
+// followed by d = gamma at the last position (DK floats, fp32), padded to a
+// whole fragment so that the record is a sequence of 1 KB blocks.
+
 // Padded fragments.  Operands that are assembled in LDS by threads that own a
 // pair of channels over a run of rows use a padded fragment: lane (g, r)'s
 // 16-byte slot sits at g * kFragGroupBytes + r * 16 (272-byte group stride
@@ -36,9 +39,18 @@ struct ChunkGeom {
   static constexpr int KBN = (DK + KB - 1) / KB;    // K blocks over channels
   static constexpr int KBC = (C + KB - 1) / KB;     // K blocks over positions
   static constexpr size_t FRAG = 1024;
+  static constexpr int NF_T = RT * KBC;             // fragments of TB (and of M)
+  static constexpr int NF_W = RT * KBN;             // fragments of W (and of Q)
+  static constexpr int NF_KR = RH * KBC;            // fragments of KR
+  static constexpr int NF_D = (DK * 4 + 1023) / 1024;
+  static constexpr int NFR = 2 * NF_T + 2 * NF_W + NF_KR + NF_D;
   static constexpr size_t T_OFF = 0;
-  static constexpr size_t M_OFF = T_OFF + (size_t)RT * KBC * FRAG;
-  static constexpr size_t BYTES = (M_OFF + (size_t)RT * KBC * FRAG + 255) / 256 * 256;
+  static constexpr size_t M_OFF = T_OFF + NF_T * FRAG;
+  static constexpr size_t W_OFF = M_OFF + NF_T * FRAG;
+  static constexpr size_t Q_OFF = W_OFF + NF_W * FRAG;
+  static constexpr size_t KR_OFF = Q_OFF + NF_W * FRAG;
+  static constexpr size_t D_OFF = KR_OFF + NF_KR * FRAG;
+  static constexpr size_t BYTES = NFR * FRAG;
 };
 
 // Byte offset of lane `lane`'s 16-byte slot in fragment (tile, kblock) of an

@@ -1,7 +1,7 @@
 // chunk_gram.hip -- the state-independent part of the chunkwise CKDA forward:
 // for every chunk of every (batch, head) at once, the decayed Gram matrices on
 // the matrix cores and the unit lower-triangular (UT/WY) solve, written as the
-// chunk's record (TB and M, chunk_common.hpp).
+// chunk's record (TB, M, W, Q~, KR and d, chunk_common.hpp).
 //
 // Chunk form (derived from the recurrence of the "Complex KDA" paper, Eq. (1);
 // the pages do not print it).  For a chunk with local positions t and the
@@ -92,7 +92,10 @@ struct GramCfg : ChunkGeom<T, DK, C> {
   static constexpr int NSLOT = cmax(NSLOT_P, cmax(NSLOT_C, NSLOT_D));
   static constexpr int LD = C + 4;                      // row stride of the fp32 scratch
   static constexpr int SCR_BYTES = 3 * C * LD * 4;      // A, M, T in fp32
-  static constexpr int AREA = cmax(NSLOT * TOPB, SCR_BYTES);
+  // phase 0: padded fragments of W, Q~ and KR, in record order
+  static constexpr int NF3 = 2 * G::NF_W + G::NF_KR;
+  static constexpr int KR_AREA = 2 * G::NF_W * kFragPadBytes;
+  static constexpr int AREA = cmax(cmax(NSLOT * TOPB, SCR_BYTES), NF3 * kFragPadBytes);
   static constexpr int BETA_OFF = AREA;
   static constexpr int TOT_OFF = BETA_OFF + C * 4;      // [RT][DK] tile products
   static constexpr int LDS_BYTES = TOT_OFF + RT * DK * 4;
@@ -186,15 +189,15 @@ __global__ __launch_bounds__((GramCfg<T, DK, C>::NTH)) void chunk_gram_kernel(
         }
       }
     }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) ra[i] = floor_gates<T>(ra[i]);
   }
 
-  // K blocks only partly covered by channels (bf16, DK = 16): the uncovered
-  // half of every fragment must read as zero in all stages
-  if constexpr (DK % KB != 0) {
-    for (int i = tid; i < P::NSLOT * TOPB / 16; i += NTH)
-      reinterpret_cast<u32x4*>(area)[i] = u32x4{0u, 0u, 0u, 0u};
+  // K blocks only partly covered (bf16: channels when DK = 16, positions of
+  // KR when C = 16): the uncovered half of every fragment must read as zero
+  auto zero_area = [&]() {
+    for (int i = tid; i < P::AREA / 16; i += NTH) reinterpret_cast<u32x4*>(area)[i] = u32x4{0u, 0u, 0u, 0u};
+  };
+  if constexpr (DK % KB != 0 || C % KB != 0) {
+    zero_area();
     lds_barrier();
   }
 
@@ -202,6 +205,83 @@ __global__ __launch_bounds__((GramCfg<T, DK, C>::NTH)) void chunk_gram_kernel(
   auto put = [&](int slot, int i, float v0, float v1) {
     PR::put(area + slot * TOPB + colofs + i * 16, v0, v1);
   };
+#define LO(x) PR::lo(x)
+#define HI(x) PR::hi(x)
+
+  // ---- phase 0: the gate-product operands of the state pass.  Only products
+  // of gates occur (modulus at most 1), so the gates are used as given.
+  //   W = -(K . gamma), Q~ = Q . gamma, KR = (K . G(C, .))^T, d = gamma_{C-1},
+  // gamma_t being the product from the chunk start to t and G(C, t) the
+  // product after t to the chunk end; rows past a ragged end have gate 1 and
+  // zero key and query.
+  unsigned char* rec = ws + (size_t)chunk_id * P::BYTES;
+  {
+    if (act) {
+      float p0 = 1.f, p1 = 1.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        p0 *= LO(ra[i]);
+        p1 *= HI(ra[i]);
+      }
+      *reinterpret_cast<float2*>(&s_tot[b * DK + c0]) = make_float2(p0, p1);
+    }
+    lds_barrier();
+    if (act) {
+      float bf0 = 1.f, bf1 = 1.f, af0 = 1.f, af1 = 1.f;   // tiles before / after this one
+#pragma unroll
+      for (int J = 0; J < RT; ++J) {
+        const float2 tt = *reinterpret_cast<const float2*>(&s_tot[J * DK + c0]);
+        if (J < b) {
+          bf0 *= tt.x;
+          bf1 *= tt.y;
+        }
+        if (J > b) {
+          af0 *= tt.x;
+          af1 *= tt.y;
+        }
+      }
+      float g0 = bf0, g1 = bf1;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        g0 *= LO(ra[i]);
+        g1 *= HI(ra[i]);
+        put(b, i, -LO(rk[i]) * g0, -HI(rk[i]) * g1);
+        put(RT + b, i, LO(rq[i]) * g0, HI(rq[i]) * g1);
+      }
+      if (b == RT - 1) *reinterpret_cast<float2*>(rec + P::D_OFF + c0 * 4) = make_float2(g0, g1);
+      // KR^T: rows = channels c0, c0 + 1; K = positions, four at a time
+      float e0 = af0, e1 = af1;
+#pragma unroll
+      for (int m = 3; m >= 0; --m) {
+        float kr0[4], kr1[4];
+#pragma unroll
+        for (int i = 3; i >= 0; --i) {
+          kr0[i] = LO(rk[4 * m + i]) * e0;
+          kr1[i] = HI(rk[4 * m + i]) * e1;
+          e0 *= LO(ra[4 * m + i]);
+          e1 *= HI(ra[4 * m + i]);
+        }
+        unsigned char* base = area + P::KR_AREA + padded_col_offset<T>(16 * b + 4 * m);
+        Quad<T>::put(base + (c0 >> 4) * KBC * kFragPadBytes + (c0 & 15) * 16, kr0);
+        Quad<T>::put(base + ((c0 + 1) >> 4) * KBC * kFragPadBytes + ((c0 + 1) & 15) * 16, kr1);
+      }
+    }
+    lds_barrier();
+    // padded fragments [W][Q~][KR] -> the record, unpadded, same order
+    for (int f = wave; f < P::NF3; f += NW)
+      store_frag(rec + P::W_OFF + (size_t)f * 1024 + lane * 16, load_frag(area + padded_slot(f, lane)));
+    lds_barrier();
+    if constexpr (DK % KB != 0) {
+      zero_area();
+      lds_barrier();
+    }
+  }
+
+  // Gate magnitudes floored for the Gram stages (see the file comment)
+  if (act) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) ra[i] = floor_gates<T>(ra[i]);
+  }
   // acc += X[xs] Y[ys]^T over all channels
   auto gram = [&](f32x4 acc, int xs, int ys) {
 #pragma unroll
@@ -210,8 +290,6 @@ __global__ __launch_bounds__((GramCfg<T, DK, C>::NTH)) void chunk_gram_kernel(
                    load_frag(area + ys * TOPB + padded_slot(kb, lane)));
     return acc;
   };
-#define LO(x) PR::lo(x)
-#define HI(x) PR::hi(x)
 
   // ---- stage 1: the diagonal 8 x 8 quadrants, reference at their midpoints;
   // tile products to LDS
@@ -442,7 +520,6 @@ __global__ __launch_bounds__((GramCfg<T, DK, C>::NTH)) void chunk_gram_kernel(
 
   // ---- record: T Diag(beta) and M fragments
   constexpr int NF = RT * KBC;
-  unsigned char* rec = ws + (size_t)chunk_id * P::BYTES;
   for (int f = wave; f < 2 * NF; f += NW) {
     const bool isT = f < NF;
     const int ff = isT ? f : f - NF;

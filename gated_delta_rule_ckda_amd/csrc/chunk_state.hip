@@ -18,21 +18,16 @@
 // U for O and H), so the matrix waves exchange nothing.  The decay of H is
 // applied element-wise in fp32; the state itself is never rounded.
 //
-// Four "build waves" assemble the operands of the next chunk in LDS while
-// the matrix waves work on the current one: W, Q~ and KR^T from the chunk's
-// keys, queries and gates, d, a copy of TB and M from the record, and the
-// slice's values V.  So the matrix waves issue no global loads, only the
-// output stores: with loads and stores in flight together, every wait for a
-// load would also wait for all stores.  Build
-// thread (tile bb, channel quad cq, half hf) owns channels 4 cq .. 4 cq + 3
-// over rows 16 bb + 8 hf .. + 7: the gate products along the rows are running
-// products inside the thread, the two halves of a tile meet through a DPP
-// swap, and whole-tile products go through LDS one chunk ahead.  Every factor
-// is a product of gates of modulus at most 1: no floor or reciprocal here.
-//
-// Operand sets are double-buffered (one copy when two do not fit in LDS), so
-// one workgroup barrier per chunk separates "build chunk c + 1" from "use
-// chunk c".
+// Every operand of a chunk but the values is state-independent and sits in
+// the chunk's record (chunk_gram.hip).  Four "copy waves" move the records and
+// the slice's values V (gathered into accumulator order) into a double-
+// buffered operand set in LDS, staging them in registers: a chunk's loads are
+// issued two chunks before it is placed, which keeps enough bytes in flight
+// per CU to cover the memory latency.  So the matrix waves issue no global
+// loads, only the output stores, and the copy waves only loads: with loads
+// and stores in flight together, every wait for a load would also wait for
+// all stores.  One workgroup barrier per chunk hands a filled set to the
+// matrix waves.
 #include <type_traits>
 
 #include "chunk_common.hpp"
@@ -43,69 +38,37 @@ namespace ckda {
 template <typename T, int DK, int C, int NMW>
 struct StateCfg : ChunkGeom<T, DK, C> {
   using G = ChunkGeom<T, DK, C>;
-  static constexpr int NTHREADS = (NMW + 4) * 64;
-  static constexpr int NTM = 2 * G::RT * G::KBC;            // TB and M fragments of a record
-  // one operand set: padded fragments of W, Q~ [RT][KBN], KR^T [RH][KBC];
-  // TB and M as stored in the record; d
-  static constexpr int W_OFF = 0;
-  static constexpr int Q_OFF = W_OFF + G::RT * G::KBN * kFragPadBytes;
-  static constexpr int KR_OFF = Q_OFF + G::RT * G::KBN * kFragPadBytes;
-  static constexpr int TM_OFF = KR_OFF + G::RH * G::KBC * kFragPadBytes;
-  static constexpr int D_OFF = TM_OFF + NTM * 1024;
-  // V of the slice in accumulator order: [matrix wave][row tile][lane][4]
-  static constexpr int V_OFF = D_OFF + DK * 4;
-  static constexpr int V_BYTES = NMW * G::RT * 64 * 4 * (int)sizeof(T);
+  static constexpr int NCW = 4;                              // copy waves
+  static constexpr int NTHREADS = (NMW + NCW) * 64;
+  // one operand set: the chunk's record as stored, then the slice's value
+  // rows (VRB bytes each) at a padded stride VS: the four rows 4 g + i that
+  // lane groups g = 0..3 of a matrix wave read together fall in four
+  // different 16-bank groups
+  static constexpr int V_OFF = (int)G::BYTES;
+  static constexpr int VRB = NMW * 16 * (int)sizeof(T);
+  static constexpr int VS = VRB + 16;
+  static constexpr int V_BYTES = C * VS;
   static constexpr int SET_BYTES = V_OFF + V_BYTES;
-  static constexpr int TOT_BYTES = 2 * G::RT * DK * 4;      // tile products of two chunks
-  static constexpr int NBUF = 2 * SET_BYTES + TOT_BYTES <= 160 * 1024 ? 2 : 1;
-  static constexpr int LDS_BYTES = NBUF * SET_BYTES + TOT_BYTES;
+  static constexpr int NSET = 2 * SET_BYTES <= 160 * 1024 ? 2 : 1;
+  static constexpr int LDS_BYTES = NSET * SET_BYTES;
+  // per copy lane and chunk: record fragments and 16-byte pieces of value rows
+  static constexpr int NFL = (G::NFR + NCW - 1) / NCW;
+  static constexpr int NVP = C * VRB / 16;
+  static constexpr int NVI = (NVP + NCW * 64 - 1) / (NCW * 64);
+  // register sets: a chunk's loads are issued NR iterations before they are
+  // placed in LDS (two when they fit beside the loop's other registers)
+  static constexpr int NR = 2 * 4 * (NFL + NVI) <= 144 ? 2 : 1;
 };
-
-// Calls f(c, integral_constant<c % NPF>) for c = 0 .. n-1.  Whole groups of
-// NPF chunks run in a loop whose body has no conditional part, so that the
-// compiler sees the same outstanding prefetches on every path through it and
-// waits for exactly the loads a chunk needs; the remainder follows the loop.
-template <int NPF, typename F>
-__device__ __forceinline__ void run_chunks(int n, F&& f) {
-  int cb = 0;
-  for (; cb + NPF <= n; cb += NPF) {
-    f(cb, std::integral_constant<int, 0>{});
-    if constexpr (NPF > 1) f(cb + 1, std::integral_constant<int, (NPF > 1 ? 1 : 0)>{});
-    if constexpr (NPF > 2) f(cb + 2, std::integral_constant<int, (NPF > 2 ? 2 : 0)>{});
-  }
-  if constexpr (NPF > 1) {
-    if (cb < n) f(cb, std::integral_constant<int, 0>{});
-  }
-  if constexpr (NPF > 2) {
-    if (cb + 1 < n) f(cb + 1, std::integral_constant<int, (NPF > 2 ? 1 : 0)>{});
-  }
-}
-
-// Calls f(integral_constant<c % NPF>) for a chunk index known only at run time.
-template <int NPF, typename F>
-__device__ __forceinline__ void with_slot(int c, F&& f) {
-  const int j = c % NPF;
-  if (j == 0) f(std::integral_constant<int, 0>{});
-  if constexpr (NPF > 1) {
-    if (j == 1) f(std::integral_constant<int, (NPF > 1 ? 1 : 0)>{});
-  }
-  if constexpr (NPF > 2) {
-    if (j == 2) f(std::integral_constant<int, (NPF > 2 ? 2 : 0)>{});
-  }
-}
 
 template <typename T, int DK, int C, int NMW>
 __global__ __launch_bounds__((StateCfg<T, DK, C, NMW>::NTHREADS)) void chunk_state_kernel(
-    const T* q, const T* k, const T* alpha, const T* v, const float* __restrict__ h0, T* o,
-    float* __restrict__ hT, const unsigned char* rec, int T_len, int nchunks, int dv, int slices,
-    int xcd_map) {
+    const T* v, const float* __restrict__ h0, T* o, float* __restrict__ hT, const unsigned char* rec, int T_len,
+    int nchunks, int dv, int slices, int xcd_map) {
   using S = StateCfg<T, DK, C, NMW>;
-  constexpr int RT = S::RT, RH = S::RH, KBN = S::KBN, KBC = S::KBC, NBUF = S::NBUF, NTM = S::NTM;
+  constexpr int RT = S::RT, RH = S::RH, KBN = S::KBN, KBC = S::KBC, NSET = S::NSET;
   constexpr int E = (int)sizeof(T);
   constexpr bool BF = sizeof(T) == 2;
   __shared__ __attribute__((aligned(16))) unsigned char lds[S::LDS_BYTES];
-  unsigned char* const sets = lds;
-  float* const s_tot = reinterpret_cast<float*>(lds + NBUF * S::SET_BYTES);   // [2][RT][DK]
 
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
   const int g = lane / 16, r = lane % 16;
@@ -126,17 +89,8 @@ __global__ __launch_bounds__((StateCfg<T, DK, C, NMW>::NTHREADS)) void chunk_sta
       slice = id % slices;
     }
   }
-
-  // zero the operand sets once: fragment slots that no thread writes
-  // (channels or positions past DK or C inside a K block) must read as zero
-  for (int i = tid; i < NBUF * S::SET_BYTES / 16; i += S::NTHREADS)
-    reinterpret_cast<u32x4*>(sets)[i] = u32x4{0u, 0u, 0u, 0u};
-  lds_barrier();
-
-  const long long rowbase = (long long)bh * T_len;   // first input row of this (batch, head)
-  const __amdgpu_buffer_rsrc_t rrsrc =
-      make_rsrc(rec + (size_t)bh * nchunks * S::BYTES, (uint32_t)((size_t)nchunks * S::BYTES));
-  auto set_of = [&](int c) __attribute__((always_inline)) { return sets + (NBUF == 2 ? (c & 1) : 0) * S::SET_BYTES; };
+  const long long rowbase = (long long)bh * T_len;   // first row of this (batch, head)
+  auto set_of = [&](int c) __attribute__((always_inline)) { return lds + (c % NSET) * S::SET_BYTES; };
 
   if (matrix) {
     // ============================================================ matrix waves
@@ -159,11 +113,13 @@ __global__ __launch_bounds__((StateCfg<T, DK, C, NMW>::NTHREADS)) void chunk_sta
       if constexpr (BF) return frag_from_acc_bf16(acc[2 * kb], 2 * kb + 1 < ntiles ? acc[2 * kb + 1] : zero4());
       else return frag_from_acc_f32(acc[kb]);
     };
-    lds_barrier();   // the build waves prepare chunk 0
-    lds_barrier();
+    lds_barrier();   // the copy waves fill the first set(s)
 
-    auto iter = [&](int c, auto) __attribute__((always_inline)) {
+    for (int c = 0; c < nchunks; ++c) {
       const unsigned char* set = set_of(c);
+      auto frag = [&](size_t off, int f) __attribute__((always_inline)) {
+        return load_frag(set + off + (f * 64 + lane) * 16);
+      };
       // Operand fragments are read from LDS one group ahead of the products
       // that use them; the scheduling barriers keep each group of reads
       // together so that their latencies overlap.  (fp32 fragments are twice
@@ -173,16 +129,15 @@ __global__ __launch_bounds__((StateCfg<T, DK, C, NMW>::NTHREADS)) void chunk_sta
       auto ld_wq = [&](int pt) __attribute__((always_inline)) {
 #pragma unroll
         for (int kb = 0; kb < KBN; ++kb) {
-          wf[pt % DB][kb] = load_frag(set + S::W_OFF + padded_slot(pt * KBN + kb, lane));
-          qf[pt % DB][kb] = load_frag(set + S::Q_OFF + padded_slot(pt * KBN + kb, lane));
+          wf[pt % DB][kb] = frag(S::W_OFF, pt * KBN + kb);
+          qf[pt % DB][kb] = frag(S::Q_OFF, pt * KBN + kb);
         }
       };
-      auto ld_tm = [&](Frag (*dst)[KBC], int which) __attribute__((always_inline)) {
+      auto ld_tm = [&](Frag (*dst)[KBC], size_t off) __attribute__((always_inline)) {
 #pragma unroll
         for (int pt = 0; pt < RT; ++pt)
 #pragma unroll
-          for (int kb = 0; kb < KBC; ++kb)
-            dst[pt][kb] = load_frag(set + S::TM_OFF + (((which * RT + pt) * KBC + kb) * 64 + lane) * 16);
+          for (int kb = 0; kb < KBC; ++kb) dst[pt][kb] = frag(off, pt * KBC + kb);
       };
       constexpr int RHG = RH < 2 ? RH : 2;   // state row tiles per group of reads
       constexpr int NG = RH / RHG;
@@ -194,8 +149,7 @@ __global__ __launch_bounds__((StateCfg<T, DK, C, NMW>::NTHREADS)) void chunk_sta
           const int rh = grp * RHG + j;
           dd[grp & 1][j] = *reinterpret_cast<const f32x4*>(set + S::D_OFF + (16 * rh + 4 * g) * 4);
 #pragma unroll
-          for (int kb = 0; kb < KBC; ++kb)
-            kf[grp & 1][j][kb] = load_frag(set + S::KR_OFF + padded_slot(rh * KBC + kb, lane));
+          for (int kb = 0; kb < KBC; ++kb) kf[grp & 1][j][kb] = frag(S::KR_OFF, rh * KBC + kb);
         }
       };
 
@@ -209,12 +163,17 @@ __global__ __launch_bounds__((StateCfg<T, DK, C, NMW>::NTHREADS)) void chunk_sta
       for (int pt = 0; pt < RT; ++pt) {
         if constexpr (DB == 2) {
           if (pt + 1 < RT) ld_wq(pt + 1);
-          else ld_tm(tf, 0);
+          else ld_tm(tf, S::T_OFF);
         } else {
           ld_wq(pt);
         }
         __builtin_amdgcn_sched_barrier(0);
-        xacc[pt] = load_vals4<T>(set + S::V_OFF + ((wave * RT + pt) * 64 + lane) * 4 * E);
+        {
+          // rows 16 pt + 4 g + i of this lane's column
+          const unsigned char* vp = set + S::V_OFF + (16 * pt + 4 * g) * S::VS + (16 * wave + r) * E;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) xacc[pt][i] = load_elem_lds<T>(vp + i * S::VS);
+        }
         oacc[pt] = zero4();
 #pragma unroll
         for (int kb = 0; kb < KBN; ++kb) {
@@ -223,8 +182,8 @@ __global__ __launch_bounds__((StateCfg<T, DK, C, NMW>::NTHREADS)) void chunk_sta
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      if constexpr (DB == 1) ld_tm(tf, 0);
-      if constexpr (DB == 2) ld_tm(mf, 1);
+      if constexpr (DB == 1) ld_tm(tf, S::T_OFF);
+      if constexpr (DB == 2) ld_tm(mf, S::M_OFF);
       __builtin_amdgcn_sched_barrier(0);
       // U = TB X
       Frag xb[KBC];
@@ -237,7 +196,7 @@ __global__ __launch_bounds__((StateCfg<T, DK, C, NMW>::NTHREADS)) void chunk_sta
 #pragma unroll
         for (int kb = 0; kb < KBC; ++kb) uacc[pt] = mma<T>(uacc[pt], tf[pt][kb], xb[kb]);
       }
-      if constexpr (DB == 1) ld_tm(mf, 1);
+      if constexpr (DB == 1) ld_tm(mf, S::M_OFF);
       ld_kr(0);
       __builtin_amdgcn_sched_barrier(0);
       Frag ub[KBC];
@@ -269,11 +228,10 @@ __global__ __launch_bounds__((StateCfg<T, DK, C, NMW>::NTHREADS)) void chunk_sta
         __builtin_amdgcn_sched_barrier(0);
       }
       lds_barrier();
-      if constexpr (NBUF == 1) {
-        lds_barrier();   // the build waves rewrite the one set
+      if constexpr (NSET == 1) {
+        lds_barrier();   // the copy waves refill the one set
       }
-    };
-    run_chunks<1>(nchunks, iter);
+    }
 
     if (hT) {
 #pragma unroll
@@ -282,243 +240,90 @@ __global__ __launch_bounds__((StateCfg<T, DK, C, NMW>::NTHREADS)) void chunk_sta
         for (int i = 0; i < 4; ++i) hT[sbase + (long long)(16 * j + 4 * g + i) * dv + col] = hacc[j][i];
     }
   } else {
-    // ============================================================ build waves
-    constexpr int NCQ = DK / 4;
-    constexpr int BPF = 2;                       // input slots: chunk x lives in slot x % 2
-    constexpr int NTMW = (NTM + 3) / 4;          // record fragments copied per build wave
-    const int bw = wave - NMW;                   // build wave 0..3
-    const int bt = tid - NMW * 64;
-    const int hf = bt & 1, cq = (bt >> 1) % NCQ, bb = bt / (2 * NCQ);
-    // every build thread is busy when the tiles fill the 256 build threads
-    const bool bact = 2 * NCQ * RT >= 256 || bb < RT;
-    const int bc0 = 4 * cq, brow0 = 16 * bb + 8 * hf;
-    const uint32_t in_bytes = (uint32_t)((size_t)T_len * DK * E);
-    const __amdgpu_buffer_rsrc_t arsrc = make_rsrc(alpha + rowbase * DK, in_bytes);
-    const __amdgpu_buffer_rsrc_t krsrc = make_rsrc(k + rowbase * DK, in_bytes);
-    const __amdgpu_buffer_rsrc_t qrsrc = make_rsrc(q + rowbase * DK, in_bytes);
-    const int in_voff = (brow0 * DK + bc0) * E;
-    // bf16 inputs are prefetched whole; for fp32 (twice the registers) keys
-    // and queries are loaded when the build needs them
-    constexpr bool KQ_AHEAD = BF;
-    // values of the slice: thread vt reads 8 consecutive columns of one row
-    constexpr int VCG = 2 * NMW;                     // 8-column groups per row
-    const int vrow = bt / VCG, vcg = bt % VCG;
-    const bool vact = bt < C * VCG;
+    // ============================================================ copy waves
+    constexpr int NFL = S::NFL, NVI = S::NVI, NR = S::NR, NCT = S::NCW * 64;
+    const int cw = wave - NMW;   // copy wave 0 .. NCW-1
+    const int ct = tid - NMW * 64;
+    const __amdgpu_buffer_rsrc_t rrsrc =
+        make_rsrc(rec + (size_t)bh * nchunks * S::BYTES, (uint32_t)((size_t)nchunks * S::BYTES));
     const __amdgpu_buffer_rsrc_t vrsrc = make_rsrc(v + rowbase * dv, (uint32_t)((size_t)T_len * dv * E));
-    const int v_voff = (vrow * dv + slice * 16 * NMW + 8 * vcg) * E;
-    struct BRaw {
-      Quad<T> a[8], k[KQ_AHEAD ? 8 : 1], q[KQ_AHEAD ? 8 : 1];
+    // value pieces: piece it = row it / (VRB / 16), 16 bytes at (it % (VRB / 16)) 16
+    // of the slice's columns (rows past the end read as zero)
+    constexpr int PPR = S::VRB / 16;
+    int v_goff[NVI], v_loff[NVI];
+    bool v_act[NVI];
+#pragma unroll
+    for (int j = 0; j < NVI; ++j) {
+      const int it = ct + NCT * j;
+      v_act[j] = it < S::NVP;
+      const int row = min(it, S::NVP - 1) / PPR, piece = it % PPR;
+      v_goff[j] = (row * dv + slice * 16 * NMW) * E + piece * 16;
+      v_loff[j] = S::V_OFF + row * S::VS + piece * 16;
+    }
+    struct Regs {
+      Frag f[NFL];
+      Frag v[NVI];
     };
-    BRaw br[BPF];
-    // TB and M fragments and 8 values on their way to LDS (loaded at the start
-    // of an iteration, stored at its end)
-    Frag tm[NTMW];
-    Quad<T> vv[2];
-    // products of the other half of the tile before / after this half, from
-    // btotals of a chunk to its bbuild one iteration later
-    float pre[4], suf[4];
-    Quad<T> kq_k[8], kq_q[8];                    // fp32: keys and queries of the chunk being built
-    // the record's TB and M fragments and the slice's values, moved by every
-    // build wave whatever its share of the channel work
-    auto tmload = [&](int c) __attribute__((always_inline)) {
-      c = min(c, nchunks - 1);
+    Regs rr[NR];
+    // Register set d holds chunk xs: place it in its operand set, each
+    // register refilled with the same piece of chunk xl (clamped to the last
+    // chunk) right after its store, so that LDS writes and global loads
+    // overlap.
+    // The slices of one head read the same record at about the same time;
+    // each starts at a different fragment so that their requests spread over
+    // the L2 channels instead of queueing on one.
+    const int rot = slice * S::NFR / slices;
+    int fr[NFL];
 #pragma unroll
-      for (int j = 0; j < NTMW; ++j) {
-        const int f = min(bw + 4 * j, NTM - 1);
-        tm[j].w = __builtin_amdgcn_raw_buffer_load_b128(rrsrc, c * (int)S::BYTES + (f * 64 + lane) * 16, 0, 0);
+    for (int j = 0; j < NFL; ++j) {
+      const int q = cw + S::NCW * j;
+      fr[j] = q < S::NFR ? (q + rot) % S::NFR : -1;   // -1: a spare register (load repeated, not stored)
+    }
+    auto swap = [&](Regs& d, int xs, int xl, bool store) __attribute__((always_inline)) {
+      unsigned char* set = set_of(xs);
+      const int cc = min(xl, nchunks - 1);
+#pragma unroll
+      for (int j = 0; j < NFL; ++j) {
+        const int f = fr[j];
+        if (store && f >= 0) store_frag(set + (f * 64 + lane) * 16, d.f[j]);
+        d.f[j].w = __builtin_amdgcn_raw_buffer_load_b128(rrsrc, cc * (int)S::BYTES + (max(f, 0) * 64 + lane) * 16, 0, 0);
       }
-      const int ofs = v_voff + c * C * dv * E;
-      vv[0] = Quad<T>::load(vrsrc, ofs);
-      vv[1] = Quad<T>::load(vrsrc, ofs + 4 * E);
-    };
-    auto tmstore = [&](int c) __attribute__((always_inline)) {
-      unsigned char* set = set_of(c);
 #pragma unroll
-      for (int j = 0; j < NTMW; ++j) {
-        const int f = bw + 4 * j;
-        if (f < NTM) store_frag(set + S::TM_OFF + (f * 64 + lane) * 16, tm[j]);
-      }
-      if (vact) {
-        // element (row vrow, column 8 vcg + e) -> matrix wave mw, lane (g, r), slot i
-        const int pt = vrow / 16, vg = (vrow % 16) / 4, vi = vrow % 4;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int cc = 8 * vcg + e, mw = cc / 16, rr = cc % 16;
-          vv[e >> 2].store_raw(set + S::V_OFF + (((mw * RT + pt) * 64 + vg * 16 + rr) * 4 + vi) * E, e & 3);
-        }
-      }
-    };
-    // inputs of chunk c (clamped to the last chunk); rows past the end read 0
-    auto bload = [&](BRaw& x, int c) __attribute__((always_inline)) {
-      c = min(c, nchunks - 1);
-      const int ofs = in_voff + c * C * DK * E;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        x.a[i] = Quad<T>::load(arsrc, ofs + i * DK * E);
-        if constexpr (KQ_AHEAD) {
-          x.k[i] = Quad<T>::load(krsrc, ofs + i * DK * E);
-          x.q[i] = Quad<T>::load(qrsrc, ofs + i * DK * E);
-        }
-      }
-    };
-    // ragged last chunk: rows past the end are identity steps (gate 1; their
-    // keys and queries already read as zero)
-    auto bfix = [&](BRaw& x, int c) __attribute__((always_inline)) {
-      const int cv = T_len - c * C;
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        if (brow0 + i >= cv) x.a[i] = Quad<T>::ones();
-    };
-    // products of this tile's gates -> s_tot[c % 2]
-    auto btotals = [&](BRaw& x, int c) __attribute__((always_inline)) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) x.a[i].pin();
-      float tot[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float p = 1.f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) p *= x.a[i].get(j);
-        const float other = dpp<kDppQuad1032>(p);
-        pre[j] = hf ? other : 1.f;
-        suf[j] = hf ? 1.f : other;
-        tot[j] = hf ? other * p : p * other;   // lower half first in both lanes
-      }
-      if (hf == 0)
-        *reinterpret_cast<f32x4*>(&s_tot[((c & 1) * RT + bb) * DK + bc0]) = f32x4{tot[0], tot[1], tot[2], tot[3]};
-    };
-    // the operand set of chunk c (tile products already in s_tot[c % 2])
-    auto bbuild = [&](BRaw& x, int c) __attribute__((always_inline)) {
-      unsigned char* set = set_of(c);
-      Quad<T>* kk = kq_k;
-      Quad<T>* qq = kq_q;
-      if constexpr (KQ_AHEAD) {
-        kk = x.k;
-        qq = x.q;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          x.k[i].pin();
-          x.q[i].pin();
-        }
-      } else {
-        const int ofs = in_voff + min(c, nchunks - 1) * C * DK * E;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          kq_k[i] = Quad<T>::load(krsrc, ofs + i * DK * E);
-          kq_q[i] = Quad<T>::load(qrsrc, ofs + i * DK * E);
-        }
-      }
-      // products over the tiles before and after this one
-      float before[4] = {1.f, 1.f, 1.f, 1.f}, after[4] = {1.f, 1.f, 1.f, 1.f};
-      const float* tot = s_tot + (c & 1) * RT * DK;
-#pragma unroll
-      for (int J = 0; J < RT; ++J) {
-        const f32x4 tj = *reinterpret_cast<const f32x4*>(&tot[J * DK + bc0]);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if (J < bb) before[j] *= tj[j];
-          if (J > bb) after[j] *= tj[j];
-        }
-      }
-      // W = -(K . gamma), Q~ = Q . gamma (rows of tile bb)
-      const int wq = bb * KBN * kFragPadBytes + padded_col_offset<T>(bc0);
-      float gm[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) gm[j] = before[j] * pre[j];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        float w[4], qv[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          gm[j] *= x.a[i].get(j);
-          w[j] = -kk[i].get(j) * gm[j];
-          qv[j] = qq[i].get(j) * gm[j];
-        }
-        const int rr = (8 * hf + i) * 16;
-        Quad<T>::put(set + S::W_OFF + wq + rr, w);
-        Quad<T>::put(set + S::Q_OFF + wq + rr, qv);
-      }
-      // d: the whole chunk's decay
-      if (bb == 0 && hf == 0)
-        *reinterpret_cast<f32x4*>(set + S::D_OFF + bc0 * 4) =
-            f32x4{gm[0] * suf[0] * after[0], gm[1] * suf[1] * after[1], gm[2] * suf[2] * after[2],
-                  gm[3] * suf[3] * after[3]};
-      // KR^T = (K . G(C, .))^T: rows = channels, K = positions brow0 .. brow0 + 7,
-      // written four positions at a time
-      float e[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) e[j] = suf[j] * after[j];
-#pragma unroll
-      for (int hq = 1; hq >= 0; --hq) {
-        float kr[4][4];
-#pragma unroll
-        for (int i = 3; i >= 0; --i) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            kr[j][i] = kk[4 * hq + i].get(j) * e[j];
-            e[j] *= x.a[4 * hq + i].get(j);
-          }
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int ch = bc0 + j;
-          Quad<T>::put(set + S::KR_OFF + (ch >> 4) * KBC * kFragPadBytes + (ch & 15) * 16 +
-                           padded_col_offset<T>(brow0 + 4 * hq),
-                       kr[j]);
-        }
+      for (int j = 0; j < NVI; ++j) {
+        if (store && v_act[j]) store_frag(set + v_loff[j], d.v[j]);
+        d.v[j].w = __builtin_amdgcn_raw_buffer_load_b128(vrsrc, cc * C * dv * E + v_goff[j], 0, 0);
       }
     };
 
-    // The last chunk is ragged when T is not a multiple of C; only its tile
-    // products need the gate fix (done in place, before the build uses them).
-    const bool ragged = nchunks > 0 && T_len - (nchunks - 1) * C < C;
-    // ---- chunks 0 and 1 in flight; products of chunk 0; build chunk 0, products of chunk 1
-    if (nchunks > 0) {
-      tmload(0);
-      if (bact) {
-        bload(br[0], 0);
-        bload(br[1], 1);
-        if (ragged && nchunks == 1) bfix(br[0], 0);
-        btotals(br[0], 0);
-      }
-    }
+    // Chunk x is loaded into register set x % NR in iteration x - NR - 1 (the
+    // prologue for the first ones) and placed in LDS in iteration x - 1.
+    // Prologue: chunks 0 .. NR-1 requested, chunk 0 placed, chunk NR
+    // requested: the loads in flight are then those one loop pass leaves.
+    swap(rr[0], 0, 0, false);
+    if constexpr (NR > 1) swap(rr[NR > 1 ? 1 : 0], 0, 1, false);
+    swap(rr[0], 0, NR, true);
     lds_barrier();
-    if (nchunks > 0) {
-      tmstore(0);
-      if (bact) {
-        bbuild(br[0], 0);
-        if (ragged && nchunks == 2) bfix(br[1], 1);
-        btotals(br[1], 1);
-        bload(br[0], 2);
-      }
-    }
-    lds_barrier();
-
-    // ---- while the matrix waves run chunk c: build chunk c + 1 (slot
-    // (c + 1) % 2), products of chunk c + 2 (slot c % 2), refill slot (c + 1) % 2
-    // with chunk c + 3.  Past the last chunk this repeats work on a copy of it
-    // that nobody reads, so the work stays unconditional.
-    auto iter = [&](int c, auto jconst, bool fix) __attribute__((always_inline)) {
-      constexpr int J = decltype(jconst)::value;
-      constexpr int JA = (J + 1) % BPF;
-      if constexpr (NBUF == 1) {
+    // Chunk c in use by the matrix waves: place chunk c + 1, then reuse its
+    // registers for chunk c + 1 + NR.  Past the last chunk this repeats the
+    // last chunk's loads into sets nobody reads.
+    auto iter = [&](int c, auto jconst) __attribute__((always_inline)) {
+      constexpr int J = decltype(jconst)::value;   // (c + 1) % NR
+      if constexpr (NSET == 1) {
         lds_barrier();   // the matrix waves are done with the one set
       }
-      tmload(c + 1);
-      if (bact) {
-        bbuild(br[JA], c + 1);
-        if (fix) bfix(br[J], c + 2);
-        btotals(br[J], c + 2);
-        bload(br[JA], c + 3);
-      }
-      tmstore(c + 1);
+      swap(rr[J], c + 1, c + 1 + NR, true);
       lds_barrier();
     };
-    // chunk c + 2 is the ragged last one in iteration nchunks - 3
-    const int cend = ragged && nchunks >= 3 ? nchunks - 3 : nchunks;
-    run_chunks<BPF>(cend, [&](int c, auto jc) __attribute__((always_inline)) { iter(c, jc, false); });
-    for (int c = cend; c < nchunks; ++c)
-      with_slot<BPF>(c, [&](auto jc) __attribute__((always_inline)) { iter(c, jc, c + 2 == nchunks - 1); });
+    // the register set is a compile-time index: whole groups of NR chunks per
+    // loop pass, so that every pass sees the same loads in flight
+    int c = 0;
+    for (; c + NR <= nchunks; c += NR) {
+      iter(c, std::integral_constant<int, 1 % NR>{});
+      if constexpr (NR > 1) iter(c + 1, std::integral_constant<int, 0>{});
+    }
+    if constexpr (NR > 1) {
+      if (c < nchunks) iter(c, std::integral_constant<int, 1 % NR>{});
+    }
   }
 }
 
@@ -530,8 +335,8 @@ hipError_t launch_state_nmw(const ChunkArgs& a, int nchunks) {
   const long long wgs = (long long)BH * slices;
   const int xcd_map = (BH % 8 == 0) ? 1 : 0;
   hipLaunchKernelGGL((chunk_state_kernel<T, DK, C, NMW>), dim3((unsigned)wgs), dim3(S::NTHREADS), 0, a.stream,
-                     (const T*)a.q, (const T*)a.k, (const T*)a.alpha, (const T*)a.v, a.h0, (T*)a.o, a.hT,
-                     (const unsigned char*)a.workspace, a.T, nchunks, a.dv, slices, xcd_map);
+                     (const T*)a.v, a.h0, (T*)a.o, a.hT, (const unsigned char*)a.workspace, a.T, nchunks, a.dv,
+                     slices, xcd_map);
   return hipGetLastError();
 }
 

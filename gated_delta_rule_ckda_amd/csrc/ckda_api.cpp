@@ -111,6 +111,9 @@ int ckda_chunk_fwd(const void* q, const void* k, const void* v, const void* alph
     return fail(CKDA_ERR_DIM, "ckda_chunk_fwd: B*H too large");
   if (((size_t)T + 64) * dv * es > (size_t)INT32_MAX)
     return fail(CKDA_ERR_DIM, "ckda_chunk_fwd: T=%d too long: one head's output must stay below 2 GiB", T);
+  const size_t head_records = (((size_t)T + chunk - 1) / chunk) * ckda::chunk_record_layout(dk, chunk, dtype).bytes;
+  if (head_records > (size_t)INT32_MAX)
+    return fail(CKDA_ERR_DIM, "ckda_chunk_fwd: T=%d too long: one head's chunk records must stay below 2 GiB", T);
   if (T > 0) {
     if (!workspace) return fail(CKDA_ERR_WORKSPACE, "ckda_chunk_fwd: workspace is NULL");
     if (workspace_bytes < need)

@@ -139,6 +139,10 @@ __device__ __forceinline__ void lds_wave_fence() { asm volatile("s_waitcnt lgkmc
 // Ties a value to this point of the program: the compiler may not move its
 // uses above it, so a widening of prefetched bits cannot be hoisted into an
 // earlier phase (which would make that phase wait for the prefetch).
+// s_waitcnt operand that waits for every vector memory access of the wave
+// (vmcnt 0; expcnt and lgkmcnt at their maxima, i.e. not waited for)
+constexpr int kWaitVmcnt0 = 0x0F70;
+
 __device__ __forceinline__ void pin(uint32_t& x) { asm volatile("" : "+v"(x)); }
 __device__ __forceinline__ void pin(u32x2& x) { asm volatile("" : "+v"(x)); }
 __device__ __forceinline__ void pin(f32x4& x) { asm volatile("" : "+v"(x)); }
@@ -178,6 +182,13 @@ template <> __device__ __forceinline__ void store_elem_lds<float>(unsigned char*
 }
 template <> __device__ __forceinline__ void store_elem_lds<bf16_t>(unsigned char* p, float x) {
   *reinterpret_cast<uint16_t*>(p) = from_f32<bf16_t>(x).bits;
+}
+template <typename T> __device__ __forceinline__ float load_elem_lds(const unsigned char* p);
+template <> __device__ __forceinline__ float load_elem_lds<float>(const unsigned char* p) {
+  return *reinterpret_cast<const float*>(p);
+}
+template <> __device__ __forceinline__ float load_elem_lds<bf16_t>(const unsigned char* p) {
+  return __uint_as_float((uint32_t)*reinterpret_cast<const uint16_t*>(p) << 16);
 }
 template <typename T> __device__ __forceinline__ f32x4 load_vals4(const unsigned char* p);
 template <> __device__ __forceinline__ f32x4 load_vals4<float>(const unsigned char* p) {
