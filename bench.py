@@ -8,9 +8,10 @@ plus the final state.  The decode step (256 sequences x 32 heads, d128, fp32
 state updated in place) is timed in the same run and reported under "decode".
 
 Prints ONE JSON line.  `value` is tokens/s of the forward (a token is one
-(batch, position) across all heads), inputs resident in HBM, timed with HIP
-events on the stream the kernels run on; `ms_per_step` is the wall time of the
-K timed steps (synchronised on both sides) divided by K.
+(batch, position) across all heads), inputs resident in HBM: tokens per step
+divided by `ms_per_step`, the wall time of the K timed steps (synchronised on
+both sides) divided by K.  HIP events on the kernels' stream give the per-call
+time and, in a second run of K steps, each kernel's duration ("roofline").
 """
 from __future__ import annotations
 
@@ -37,9 +38,42 @@ def parse():
     p.add_argument("--workload", default="ckda_bf16",
                    help="forward workload name (default: the headline ckda_bf16)")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-sample-tokens", type=int, default=0,
-                   help="tokens per head the oracle runs on (0 = choose ~15 s of work)")
+    p.add_argument("--cpu-seconds", type=float, default=15.0,
+                   help="about this much oracle work for the CPU baseline (whole-workload passes)")
     return p.parse_args()
+
+
+def kernel_algorithmic(w):
+    """Algorithmic HBM bytes of each of the forward's two kernels: the method's
+    own inputs and outputs that the kernel reads or writes.  The Gram kernel
+    reads q, k, alpha and beta; the state-pass kernel reads v and h0 and writes
+    o and hT.  The chunk records the first writes and the second reads are
+    this design's intermediate ("record_bytes"), not algorithmic traffic."""
+    es = 2 if w.dtype == "bf16" else 4
+    th = w.B * w.H * w.T
+    state = w.B * w.H * w.dk * w.dv * 4 * (2 if w.h0 == "normal" else 1)
+    return {"chunk_gram_kernel": th * (3 * w.dk + 1) * es,
+            "chunk_state_kernel": th * 2 * w.dv * es + state}
+
+
+def traffic_from_profile(kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary,
+    or None when the kernel's source changed after the counters were taken."""
+    import hashlib
+    import re
+    path = os.path.join(ROOT, "profiles", f"{kernel}_ckda_bf16_hbm_counters.md")
+    src = os.path.join(ROOT, "gated_delta_rule_ckda_amd", "csrc",
+                       {"chunk_gram_kernel": "chunk_gram.hip", "chunk_state_kernel": "chunk_state.hip"}[kernel])
+    try:
+        text = open(path).read()
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    m_sha = re.search(r"source sha256: `([0-9a-f]{64})`", text)
+    m_b = re.search(r"HBM bytes per launch: ([0-9]+)", text)
+    if not m_sha or not m_b or m_sha.group(1) != sha:
+        return None
+    return int(m_b.group(1))
 
 
 def fwd_algorithmic(w):
@@ -83,15 +117,17 @@ def main():
     o = torch.empty((w.B, w.H, w.T, w.dv), dtype=d["q"].dtype, device=dev)
     hT = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device=dev)
 
-    def step():
+    stream = torch.cuda.current_stream()
+
+    def step(events=None):
         ck.chunk_fwd(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["h0"], chunk=w.chunk,
-                     workspace=ws, o=o, hT=hT)
+                     workspace=ws, o=o, hT=hT, events=events)
 
     log(f"[bench] warmup {a.warmup}")
     for _ in range(a.warmup):
         step()
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
+    # Timed region 1: K steps bracketed by synchronisation, events before and
+    # after each call (the tokens/s value and the per-call time).
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(a.steps)]
     log(f"[bench] timing {a.steps} forward steps")
     torch.cuda.synchronize()
@@ -103,14 +139,32 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     per_call_ms = [e0.elapsed_time(e1) for e0, e1 in ev]
+    # Timed region 2: K more steps through ckda_chunk_fwd_timed, whose events
+    # (recorded by the library on this stream before the Gram kernel, between
+    # the kernels and after the state-pass kernel) give each kernel's duration.
+    kev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(a.steps)]
+    for e3 in kev:
+        for e in e3:
+            e.record(stream)   # creates the event
+    torch.cuda.synchronize()
+    for s in range(a.steps):
+        step(kev[s])
+    torch.cuda.synchronize()
+    gram_ms = [e[0].elapsed_time(e[1]) for e in kev]
+    state_ms = [e[1].elapsed_time(e[2]) for e in kev]
     call_ms = float(np.mean(per_call_ms))
     call_ms_median = float(np.median(per_call_ms))
+    kern_ms = {"chunk_gram_kernel": float(np.mean(gram_ms)), "chunk_state_kernel": float(np.mean(state_ms))}
     ms_per_step = wall * 1e3 / a.steps
     tokens = w.B * w.T
     value = tokens / (ms_per_step * 1e-3)
     nbytes, flops = fwd_algorithmic(w)
     achieved_gbs = nbytes / (call_ms * 1e-3) / 1e9
     achieved_tflops = flops / (call_ms * 1e-3) / 1e12
+    kbytes = kernel_algorithmic(w)
+    record_bytes = ws.numel()
+    dominant = max(kern_ms, key=kern_ms.get)
+    dom_gbs = kbytes[dominant] / (kern_ms[dominant] * 1e-3) / 1e9
 
     # ---- decode: 256 x 32 states, fp32 128x128 each, updated in place
     dec = gen.DECODE
@@ -174,17 +228,23 @@ def main():
                    "chunk": w.chunk, "gates": w.gates, "h0": w.h0},
         "roofline": {
             "bound": "hbm",
-            "kernel": "ckda_chunk_fwd (chunk_prep_kernel + chunk_state_kernel)",
-            "achieved": round(achieved_gbs, 1),
+            "kernel": dominant,
+            "achieved": round(dom_gbs, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
-            "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
-            "traffic": None,
-            "algorithmic_bytes": nbytes,
-            "call_ms_mean": round(call_ms, 4),
-            "call_ms_median": round(call_ms_median, 4),
-            "mfma_algorithmic_tflops": round(achieved_tflops, 2),
-            "mfma_frac_of_bf16_peak": round(achieved_tflops / BF16_PEAK_TFLOPS, 4),
+            "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
+            "traffic": traffic_from_profile(dominant),
+            "algorithmic_bytes": kbytes[dominant],
+            "kernel_us_mean": round(kern_ms[dominant] * 1e3, 2),
+            "kernels": {k: {"us_mean": round(kern_ms[k] * 1e3, 2), "algorithmic_bytes": kbytes[k],
+                            "algorithmic_GB_s": round(kbytes[k] / (kern_ms[k] * 1e-3) / 1e9, 1),
+                            "record_bytes": record_bytes,
+                            "traffic": traffic_from_profile(k)} for k in kern_ms},
+            "forward": {"call_ms_mean": round(call_ms, 4), "call_ms_median": round(call_ms_median, 4),
+                        "algorithmic_bytes": nbytes, "algorithmic_GB_s": round(achieved_gbs, 1),
+                        "frac_of_hbm_peak": round(achieved_gbs / HBM_PEAK_GBS, 4),
+                        "mfma_algorithmic_tflops": round(achieved_tflops, 2),
+                        "mfma_frac_of_bf16_peak": round(achieved_tflops / BF16_PEAK_TFLOPS, 4)},
         },
         "decode": {
             "workload": dec.name, "steps": a.decode_steps,
@@ -200,19 +260,23 @@ def main():
     if not a.no_cpu_baseline:
         import oracle
         from gated_delta_rule_ckda_amd.inputs import raw
-        T_s = a.cpu_sample_tokens or min(w.T, 1024)
-        sl = lambda t: t[:, :, :T_s].contiguous()
-        args = [raw(sl(inp[n])) for n in ("q", "k", "v", "alpha", "beta")]
+        args = [raw(inp[n]) for n in ("q", "k", "v", "alpha", "beta")]
         h0 = None if inp["h0"] is None else raw(inp["h0"])
         nt = oracle.num_threads()
-        log(f"[bench] oracle cpu baseline: {w.B}x{w.H} heads x {T_s} tokens, {nt} threads")
+        log(f"[bench] oracle cpu baseline: whole workload passes for ~{a.cpu_seconds:.0f} s, {nt} threads")
         c0 = time.perf_counter()
         oracle.fwd(*args, h0=h0)
+        passes = 1
+        first = time.perf_counter() - c0
+        more = max(0, int(a.cpu_seconds / max(first, 1e-3)) - 1)
+        for _ in range(more):
+            oracle.fwd(*args, h0=h0)
+        passes += more
         csec = time.perf_counter() - c0
-        out["cpu_baseline"] = {"value": round(w.B * T_s / csec, 1), "unit": "tokens/s", "cores": nt,
+        out["cpu_baseline"] = {"value": round(passes * w.B * w.T / csec, 1), "unit": "tokens/s", "cores": nt,
                                "kind": "oracle",
-                               "sample": f"{w.name} first {T_s} of {w.T} positions, all {w.B * w.H} heads, "
-                                         f"{csec:.2f} s"}
+                               "sample": f"the whole {w.name} forward ({w.B * w.H} heads x {w.T} positions) "
+                                         f"{passes} times, {csec:.1f} s"}
     print(json.dumps(out), flush=True)
     return 0
 

@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(_HERE, "libckda.so")
 DTYPE_F32, DTYPE_BF16 = 0, 1
 STATUS = {0: "CKDA_OK", 1: "CKDA_ERR_NULL", 2: "CKDA_ERR_DIM", 3: "CKDA_ERR_UNSUPPORTED",
           4: "CKDA_ERR_ALIAS", 5: "CKDA_ERR_WORKSPACE", 6: "CKDA_ERR_HIP"}
-EXPORTS = ("ckda_chunk_fwd_workspace_size", "ckda_chunk_fwd", "ckda_decode_step",
+EXPORTS = ("ckda_chunk_fwd_workspace_size", "ckda_chunk_fwd", "ckda_chunk_fwd_timed", "ckda_decode_step",
            "ckda_status_string", "ckda_last_error", "ckda_abi_version")
 
 _lib = None
@@ -46,6 +46,8 @@ def lib() -> ctypes.CDLL:
         L.ckda_chunk_fwd_workspace_size.restype = sz
         L.ckda_chunk_fwd.argtypes = [vp] * 8 + [i] * 7 + [vp, sz, vp]
         L.ckda_chunk_fwd.restype = i
+        L.ckda_chunk_fwd_timed.argtypes = [vp] * 8 + [i] * 7 + [vp, sz, vp, vp, vp, vp]
+        L.ckda_chunk_fwd_timed.restype = i
         L.ckda_decode_step.argtypes = [vp] * 7 + [i] * 5 + [vp]
         L.ckda_decode_step.restype = i
         L.ckda_status_string.argtypes = [i]
@@ -96,12 +98,15 @@ def workspace_size(B, H, T, dk, dv, chunk, dtype) -> int:
 
 
 def chunk_fwd(q, k, v, alpha, beta, h0=None, chunk=64, workspace=None, o=None, hT=None,
-              want_state=True, stream=None):
+              want_state=True, stream=None, events=None):
     """Chunkwise forward.  q, k, alpha [B,H,T,dk]; v [B,H,T,dv]; beta [B,H,T];
     h0 [B,H,dk,dv] fp32 or None.  Returns (o [B,H,T,dv], hT [B,H,dk,dv] fp32 or None).
 
     `workspace` (uint8 GPU tensor of at least workspace_size() bytes), `o` and
-    `hT` may be passed in to avoid allocations (e.g. in timed loops)."""
+    `hT` may be passed in to avoid allocations (e.g. in timed loops).
+    `events`, three recorded-once torch.cuda.Event objects (or None), are
+    recorded before the Gram kernel, between the kernels and after the
+    state-pass kernel (ckda_chunk_fwd_timed)."""
     B, H, T, dk = q.shape
     dv = v.shape[-1]
     _require(dict(q=q, k=k, v=v, alpha=alpha, beta=beta), q.dtype)
@@ -117,9 +122,14 @@ def chunk_fwd(q, k, v, alpha, beta, h0=None, chunk=64, workspace=None, o=None, h
         o = torch.empty((B, H, T, dv), dtype=q.dtype, device=q.device)
     if hT is None and want_state:
         hT = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
-    _check(lib().ckda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(h0), _ptr(o),
-                                _ptr(hT), B, H, T, dk, dv, chunk, code, _ptr(workspace),
-                                workspace.numel() * workspace.element_size(), _stream(stream)))
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(h0), _ptr(o), _ptr(hT),
+            B, H, T, dk, dv, chunk, code, _ptr(workspace), workspace.numel() * workspace.element_size(),
+            _stream(stream))
+    if events is None:
+        _check(lib().ckda_chunk_fwd(*args))
+    else:
+        handles = [None if e is None else ctypes.c_void_p(e.cuda_event) for e in events]
+        _check(lib().ckda_chunk_fwd_timed(*args, *handles))
     return o, hT
 
 

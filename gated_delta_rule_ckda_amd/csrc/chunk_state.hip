@@ -372,9 +372,14 @@ hipError_t launch_chunk_gram(const ChunkArgs& a, long long total_chunks, int nch
 hipError_t launch_chunk_fwd(const ChunkArgs& a) {
   const int nchunks = (a.T + a.chunk - 1) / a.chunk;
   const long long BH = (long long)a.B * a.H;
-  hipError_t e = launch_chunk_gram(a, BH * nchunks, nchunks);
+  hipError_t e;
+  if (a.ev[0] && (e = hipEventRecord(a.ev[0], a.stream)) != hipSuccess) return e;
+  if ((e = launch_chunk_gram(a, BH * nchunks, nchunks)) != hipSuccess) return e;
+  if (a.ev[1] && (e = hipEventRecord(a.ev[1], a.stream)) != hipSuccess) return e;
+  e = a.dtype == 1 ? state_dk_dispatch<bf16_t>(a, nchunks) : state_dk_dispatch<float>(a, nchunks);
   if (e != hipSuccess) return e;
-  return a.dtype == 1 ? state_dk_dispatch<bf16_t>(a, nchunks) : state_dk_dispatch<float>(a, nchunks);
+  if (a.ev[2] && (e = hipEventRecord(a.ev[2], a.stream)) != hipSuccess) return e;
+  return hipSuccess;
 }
 
 }  // namespace ckda

@@ -84,10 +84,9 @@ size_t ckda_chunk_fwd_workspace_size(int B, int H, int T, int dk, int dv, int ch
   return bytes == 0 ? 256 : bytes;  // never 0 for valid sizes: 0 means "invalid"
 }
 
-int ckda_chunk_fwd(const void* q, const void* k, const void* v, const void* alpha,
-                   const void* beta, const float* h0, void* o, float* hT,
-                   int B, int H, int T, int dk, int dv, int chunk, int dtype,
-                   void* workspace, size_t workspace_bytes, void* stream) {
+static int chunk_fwd_impl(const void* q, const void* k, const void* v, const void* alpha, const void* beta,
+                          const float* h0, void* o, float* hT, int B, int H, int T, int dk, int dv, int chunk,
+                          int dtype, void* workspace, size_t workspace_bytes, void* stream, void* const ev[3]) {
   if (B < 0 || H < 0 || T < 0)
     return fail(CKDA_ERR_DIM, "ckda_chunk_fwd: negative size (B=%d H=%d T=%d)", B, H, T);
   if (!supported_dtype(dtype))
@@ -144,11 +143,30 @@ int ckda_chunk_fwd(const void* q, const void* k, const void* v, const void* alph
     return fail(CKDA_ERR_ALIAS, "ckda_chunk_fwd: workspace overlaps an output");
 
   ckda::ChunkArgs a{q, k, v, alpha, beta, h0, o, hT, B, H, T, dk, dv, chunk, dtype, workspace,
-                    (hipStream_t)stream};
+                    (hipStream_t)stream, {(hipEvent_t)ev[0], (hipEvent_t)ev[1], (hipEvent_t)ev[2]}};
   hipError_t e = ckda::launch_chunk_fwd(a);
   if (e != hipSuccess)
     return fail(CKDA_ERR_HIP, "ckda_chunk_fwd: launch failed: %s", hipGetErrorString(e));
   return ok();
+}
+
+int ckda_chunk_fwd(const void* q, const void* k, const void* v, const void* alpha,
+                   const void* beta, const float* h0, void* o, float* hT,
+                   int B, int H, int T, int dk, int dv, int chunk, int dtype,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  void* const none[3] = {nullptr, nullptr, nullptr};
+  return chunk_fwd_impl(q, k, v, alpha, beta, h0, o, hT, B, H, T, dk, dv, chunk, dtype, workspace, workspace_bytes,
+                        stream, none);
+}
+
+int ckda_chunk_fwd_timed(const void* q, const void* k, const void* v, const void* alpha,
+                         const void* beta, const float* h0, void* o, float* hT,
+                         int B, int H, int T, int dk, int dv, int chunk, int dtype,
+                         void* workspace, size_t workspace_bytes, void* stream,
+                         void* ev_start, void* ev_mid, void* ev_end) {
+  void* const ev[3] = {ev_start, ev_mid, ev_end};
+  return chunk_fwd_impl(q, k, v, alpha, beta, h0, o, hT, B, H, T, dk, dv, chunk, dtype, workspace, workspace_bytes,
+                        stream, ev);
 }
 
 int ckda_decode_step(const void* q, const void* k, const void* v, const void* alpha,

@@ -17,7 +17,7 @@
 // K block (bf16: two tiles, rows 0-15 then 16-31; fp32: one tile), so a
 // product's result feeds the next product without a shuffle.  Any operand
 // that meets it on the other side must be laid out in the same K order, which
-// the chunk preparation kernel does when it writes its outputs.
+// the Gram kernel does when it writes the chunk records.
 #pragma once
 
 #include <hip/hip_runtime.h>

@@ -23,6 +23,7 @@ struct ChunkArgs {
   int B, H, T, dk, dv, chunk, dtype;
   void* workspace;
   hipStream_t stream;
+  hipEvent_t ev[3];   // recorded before the Gram kernel, between the kernels, after the state kernel (if set)
 };
 
 // Layout of the per-chunk records the Gram kernel writes and the state-pass

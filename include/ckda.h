@@ -25,10 +25,11 @@
  * - `dtype` (ckda_dtype_t) is the element type of q, k, v, alpha, beta and o.
  *   States (h0, hT, H_inout) are always fp32.
  * - q is not scaled and k is not normalised: the caller supplies ||k_t|| = 1.
- *   alpha and beta are used as given (no clamping of range violations), except
- *   that the chunked forward replaces gate magnitudes below 2^-15 by 2^-15
- *   (sign kept, sign(0) = +1), which bounds the deviation from the exact
- *   recurrence by 2^-15 relative per affected step; see ckda_chunk_fwd.
+ *   alpha and beta are used as given (no clamping of range violations).  The
+ *   one exception is internal to the chunked forward's intra-chunk Gram
+ *   matrices, where a gate magnitude below 2^-31 counts as 2^-31 (sign kept):
+ *   that changes a decay only where its exact value is below 2^-31 already;
+ *   see ckda_chunk_fwd.
  * - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
  *   and the call returns without waiting.  The return value reports argument
  *   errors (detected before anything is launched) and launch errors; faults
@@ -66,9 +67,9 @@ typedef enum {
 /* Bytes of device workspace ckda_chunk_fwd needs for these sizes, or 0 when
  * the sizes are invalid or unsupported (ckda_chunk_fwd then reports why).
  * The workspace holds, per chunk of every (batch, head), the operands the
- * state pass consumes (see ckda_chunk_fwd); it is about
- * B*H*ceil(T/chunk)*(3*chunk*d_k + 2*chunk*chunk) elements of dtype plus
- * d_k floats per chunk. */
+ * state pass consumes (see ckda_chunk_fwd): 2*chunk*chunk + 3*chunk*d_k
+ * elements of dtype and d_k floats, each part rounded up to whole 1 KB
+ * blocks (bf16, chunk 64, d_k 128: 65 KB per chunk). */
 size_t ckda_chunk_fwd_workspace_size(int B, int H, int T, int dk, int dv, int chunk, int dtype);
 
 /* Chunkwise-parallel forward over a whole sequence for every (batch, head).
@@ -94,16 +95,30 @@ size_t ckda_chunk_fwd_workspace_size(int B, int H, int T, int dk, int dv, int ch
  *
  * The result equals the sequential recurrence up to floating-point rounding
  * (the KDA course lesson, "Chunkwise execution": chunking changes cost, not
- * the numbers), computed in two kernels: a per-chunk preparation kernel that
- * splits the gates into sign parity and magnitude products, forms the
- * intra-chunk Gram matrices and solves the unit lower-triangular (UT/WY)
- * system, and a state-pass kernel that carries the fp32 state from chunk to
- * chunk and emits the outputs.  bf16 inputs are multiplied on bf16 matrix
- * cores with fp32 accumulation; fp32 inputs on fp32 matrix cores. */
+ * the numbers), computed in two kernels.  A Gram kernel, parallel over all
+ * chunks, forms each chunk's signed gate products, its decayed Gram matrices
+ * and the unit lower-triangular (UT/WY) solve, and writes the chunk's state-
+ * independent operands to the workspace.  A state-pass kernel carries the
+ * fp32 state from chunk to chunk and emits the outputs.  bf16 inputs are
+ * multiplied on bf16 matrix cores with fp32 accumulation; fp32 inputs on fp32
+ * matrix cores. */
 int ckda_chunk_fwd(const void* q, const void* k, const void* v, const void* alpha,
                    const void* beta, const float* h0, void* o, float* hT,
                    int B, int H, int T, int dk, int dv, int chunk, int dtype,
                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* ckda_chunk_fwd with timing marks, for measurement: identical arguments,
+ * checks and results, and in addition each non-NULL event (a hipEvent_t the
+ * caller created on the current device) is recorded on `stream` -- ev_start
+ * before the Gram kernel, ev_mid between the Gram and the state-pass kernel,
+ * ev_end after the state-pass kernel -- so that the caller can read each
+ * kernel's duration with hipEventElapsedTime after synchronising.  The events
+ * stay owned by the caller. */
+int ckda_chunk_fwd_timed(const void* q, const void* k, const void* v, const void* alpha,
+                         const void* beta, const float* h0, void* o, float* hT,
+                         int B, int H, int T, int dk, int dv, int chunk, int dtype,
+                         void* workspace, size_t workspace_bytes, void* stream,
+                         void* ev_start, void* ev_mid, void* ev_end);
 
 /* One recurrent decode step for N sequences x H heads, state in place.
  *

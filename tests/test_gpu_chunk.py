@@ -163,3 +163,21 @@ def test_nan_gate_propagates_to_its_head_only():
     assert torch.isnan(o[0, 1, 40:]).any() and torch.isnan(hT[0, 1]).any()
     assert torch.isfinite(o[0, 0]).all() and torch.isfinite(o[0, 2]).all()
     assert torch.isfinite(o[0, 1, :32]).all()
+
+
+def test_timed_entry_point_matches_and_times():
+    """ckda_chunk_fwd_timed gives the same bits as ckda_chunk_fwd and its
+    events bracket the two kernels in order."""
+    w = gen.Workload("timed_small", 2, 3, 300, 64, 32, 64, "bf16", "ckda_tanh", "normal", 77)
+    log(f"chunk_fwd_timed {w}")
+    d = to_dev(gen.make_inputs(w))
+    o1, h1 = ck.chunk_fwd(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["h0"], chunk=w.chunk)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    for e in ev:
+        e.record()   # creates the events
+    o2, h2 = ck.chunk_fwd(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["h0"], chunk=w.chunk, events=ev)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(h1, h2)
+    t_gram, t_state = ev[0].elapsed_time(ev[1]), ev[1].elapsed_time(ev[2])
+    log(f"  gram {t_gram * 1e3:.1f} us, state {t_state * 1e3:.1f} us")
+    assert t_gram > 0 and t_state > 0
