@@ -90,15 +90,22 @@ struct GramCfg : ChunkGeom<T, DK, C> {
   static constexpr int NSLOT_C = 3 * RT;                // per tile: XDk, XDq, YD
   static constexpr int NSLOT_D = 2 * RT;                // per tile: LLk, LLq
   static constexpr int NSLOT = cmax(NSLOT_P, cmax(NSLOT_C, NSLOT_D));
-  static constexpr int LD = C + 4;                      // row stride of the fp32 scratch
+  // row stride of the fp32 scratch: 272 bytes like a padded-fragment group,
+  // so that every layout of the area leaves bytes 256..271 of each 272-byte
+  // group unused (see pad_float)
+  static constexpr int LD = kFragGroupBytes / 4;
   static constexpr int SCR_BYTES = 3 * C * LD * 4;      // A, M, T in fp32
   // phase 0: padded fragments of W, Q~ and KR, in record order
   static constexpr int NF3 = 2 * G::NF_W + G::NF_KR;
   static constexpr int KR_AREA = 2 * G::NF_W * kFragPadBytes;
   static constexpr int AREA = cmax(cmax(NSLOT * TOPB, SCR_BYTES), NF3 * kFragPadBytes);
-  static constexpr int BETA_OFF = AREA;
-  static constexpr int TOT_OFF = BETA_OFF + C * 4;      // [RT][DK] tile products
-  static constexpr int LDS_BYTES = TOT_OFF + RT * DK * 4;
+  // The tile products [RT][DK] and beta [C] live in those unused 16-byte
+  // pads: no LDS beyond the area, which lets three workgroups share a CU.
+  static constexpr int TOT_F = 0;
+  static constexpr int BETA_F = RT * DK;
+  static constexpr int NPADF = RT * DK + C;
+  static_assert(AREA % kFragGroupBytes == 0 && NPADF <= AREA / kFragGroupBytes * 4, "pad space");
+  static constexpr int LDS_BYTES = AREA;
   // products (A and M of each block) per stage, and per wave
   static constexpr int NBLK = RT * (RT - 1) / 2;
   static constexpr int NPP = 2 * NBLK;
@@ -143,8 +150,12 @@ __global__ __launch_bounds__((GramCfg<T, DK, C>::NTH)) void chunk_gram_kernel(
                 TOPB = P::TOPB, EPL = P::EPL, KB = P::KB;
   __shared__ __attribute__((aligned(16))) unsigned char lds[P::LDS_BYTES];
   unsigned char* area = lds;
-  float* s_beta = reinterpret_cast<float*>(lds + P::BETA_OFF);
-  float* s_tot = reinterpret_cast<float*>(lds + P::TOT_OFF);
+  // float i of the pad space: 4 floats in the last 16 bytes of each 272-byte group
+  auto pad_float = [&](int i) __attribute__((always_inline)) {
+    return reinterpret_cast<float*>(area + (i >> 2) * kFragGroupBytes + 256 + (i & 3) * 4);
+  };
+  auto s_tot = [&](int i) __attribute__((always_inline)) { return pad_float(P::TOT_F + i); };
+  auto s_beta = [&](int i) __attribute__((always_inline)) { return pad_float(P::BETA_F + i); };
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int g = lane >> 4, r = lane & 15;
@@ -154,7 +165,7 @@ __global__ __launch_bounds__((GramCfg<T, DK, C>::NTH)) void chunk_gram_kernel(
   const int cv = min(C, T_len - t0);
   const long long row0 = bh * (long long)T_len + t0;
 
-  if (tid < C) s_beta[tid] = tid < cv ? to_f32(beta[row0 + tid]) : 0.f;
+  if (tid < C) *s_beta(tid) = tid < cv ? to_f32(beta[row0 + tid]) : 0.f;
 
   const int b = tid / NU, u = tid % NU;
   const bool act = b < RT;
@@ -193,8 +204,10 @@ __global__ __launch_bounds__((GramCfg<T, DK, C>::NTH)) void chunk_gram_kernel(
 
   // K blocks only partly covered (bf16: channels when DK = 16, positions of
   // KR when C = 16): the uncovered half of every fragment must read as zero
+  // (the pads, 16-byte unit 16 of every 17, hold beta and the tile products)
   auto zero_area = [&]() {
-    for (int i = tid; i < P::AREA / 16; i += NTH) reinterpret_cast<u32x4*>(area)[i] = u32x4{0u, 0u, 0u, 0u};
+    for (int i = tid; i < P::AREA / 16; i += NTH)
+      if (i % 17 != 16) reinterpret_cast<u32x4*>(area)[i] = u32x4{0u, 0u, 0u, 0u};
   };
   if constexpr (DK % KB != 0 || C % KB != 0) {
     zero_area();
@@ -223,14 +236,14 @@ __global__ __launch_bounds__((GramCfg<T, DK, C>::NTH)) void chunk_gram_kernel(
         p0 *= LO(ra[i]);
         p1 *= HI(ra[i]);
       }
-      *reinterpret_cast<float2*>(&s_tot[b * DK + c0]) = make_float2(p0, p1);
+      *reinterpret_cast<float2*>(s_tot(b * DK + c0)) = make_float2(p0, p1);
     }
     lds_barrier();
     if (act) {
       float bf0 = 1.f, bf1 = 1.f, af0 = 1.f, af1 = 1.f;   // tiles before / after this one
 #pragma unroll
       for (int J = 0; J < RT; ++J) {
-        const float2 tt = *reinterpret_cast<const float2*>(&s_tot[J * DK + c0]);
+        const float2 tt = *reinterpret_cast<const float2*>(s_tot(J * DK + c0));
         if (J < b) {
           bf0 *= tt.x;
           bf1 *= tt.y;
@@ -326,7 +339,7 @@ __global__ __launch_bounds__((GramCfg<T, DK, C>::NTH)) void chunk_gram_kernel(
           p0 *= LO(ra[i]);
           p1 *= HI(ra[i]);
         }
-        *reinterpret_cast<float2*>(&s_tot[b * DK + c0]) = make_float2(p0, p1);
+        *reinterpret_cast<float2*>(s_tot(b * DK + c0)) = make_float2(p0, p1);
       }
     }
     lds_barrier();
@@ -378,7 +391,7 @@ __global__ __launch_bounds__((GramCfg<T, DK, C>::NTH)) void chunk_gram_kernel(
       // products over the tiles between: P_2 for tile-3 rows, P_1 for tile-0 columns
       float m0 = 1.f, m1 = 1.f;
       if (RT == 4 && (b == 3 || b == 0)) {
-        const float2 tt = *reinterpret_cast<const float2*>(&s_tot[(b == 3 ? 2 : 1) * DK + c0]);
+        const float2 tt = *reinterpret_cast<const float2*>(s_tot((b == 3 ? 2 : 1) * DK + c0));
         m0 = tt.x;
         m1 = tt.y;
       }
@@ -435,7 +448,7 @@ __global__ __launch_bounds__((GramCfg<T, DK, C>::NTH)) void chunk_gram_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = 16 * I + 4 * g + i, col = 16 * J + r;
-      if (kind == 0) As[row * LD + col] = acc[i] * s_beta[row];
+      if (kind == 0) As[row * LD + col] = acc[i] * *s_beta(row);
       else Ms[row * LD + col] = acc[i];
     }
   };
@@ -462,7 +475,7 @@ __global__ __launch_bounds__((GramCfg<T, DK, C>::NTH)) void chunk_gram_kernel(
         const bool ll = lr >= 8 && r < 8;
         if (kind == 0) {
           const float a = diagq ? (r < lr ? accC[j][i] : 0.f) : (ll ? accD[j][i] : 0.f);
-          As[row * LD + col] = a * s_beta[row];
+          As[row * LD + col] = a * *s_beta(row);
         } else {
           Ms[row * LD + col] = diagq ? (r <= lr ? accC[j][i] : 0.f) : (ll ? accD[j][i] : 0.f);
         }
@@ -533,7 +546,7 @@ __global__ __launch_bounds__((GramCfg<T, DK, C>::NTH)) void chunk_gram_kernel(
       f32x4 x = zero4();
       if (col < C && col / 16 <= rt) {
         x = *reinterpret_cast<const f32x4*>(src + col);
-        if (isT) x *= *reinterpret_cast<const f32x4*>(s_beta + col);
+        if (isT) x *= *reinterpret_cast<const f32x4*>(s_beta(col));
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) vals[4 * hh + e] = x[e];
