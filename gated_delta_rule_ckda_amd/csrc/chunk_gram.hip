@@ -159,9 +159,15 @@ __global__ __launch_bounds__((GramCfg<T, DK, C>::NTH)) void chunk_gram_kernel(
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int g = lane >> 4, r = lane & 15;
-  const long long chunk_id = blockIdx.x;
-  const long long bh = chunk_id / nchunks;
-  const int t0 = (int)(chunk_id % nchunks) * C;
+  // Workgroups run chunk-major from the last chunk back: the records the
+  // state pass reads first are written last (most likely still cached), and
+  // when the number of (batch, head) pairs is a multiple of 8 a head's chunks
+  // run on the XCD its state pass will use (ids equal modulo 8).
+  const long long nbh = gridDim.x / nchunks;
+  const long long bh = blockIdx.x % nbh;
+  const int c = nchunks - 1 - (int)(blockIdx.x / nbh);
+  const long long chunk_id = bh * nchunks + c;
+  const int t0 = c * C;
   const int cv = min(C, T_len - t0);
   const long long row0 = bh * (long long)T_len + t0;
 

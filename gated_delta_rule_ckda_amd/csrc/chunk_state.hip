@@ -98,6 +98,7 @@ __global__ __launch_bounds__((StateCfg<T, DK, C, NMW>::NTHREADS)) void chunk_sta
     // the end of the sequence are dropped.
     const __amdgpu_buffer_rsrc_t orsrc = make_rsrc(o + rowbase * dv, (uint32_t)((size_t)T_len * dv * E));
     const int col = slice * 16 * NMW + 16 * wave + r;       // this lane's value column
+    const int ocol = slice * 16 * NMW + 16 * wave + 4 * g;  // first of its four output columns
     const long long sbase = (long long)bh * DK * dv;
     f32x4 hacc[RH];
 #pragma unroll
@@ -178,7 +179,7 @@ __global__ __launch_bounds__((StateCfg<T, DK, C, NMW>::NTHREADS)) void chunk_sta
 #pragma unroll
         for (int kb = 0; kb < KBN; ++kb) {
           xacc[pt] = mma<T>(xacc[pt], wf[pt % DB][kb], hb[kb]);
-          oacc[pt] = mma<T>(oacc[pt], qf[pt % DB][kb], hb[kb]);
+          oacc[pt] = mma<T>(oacc[pt], hb[kb], qf[pt % DB][kb]);   // O^T: H^T Q~^T
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -207,10 +208,10 @@ __global__ __launch_bounds__((StateCfg<T, DK, C, NMW>::NTHREADS)) void chunk_sta
 #pragma unroll
       for (int pt = 0; pt < RT; ++pt) {
 #pragma unroll
-        for (int kb = 0; kb < KBC; ++kb) oacc[pt] = mma<T>(oacc[pt], mf[pt][kb], ub[kb]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          store_elem<T>(orsrc, ((t0 + 16 * pt + 4 * g + i) * dv + col) * E, oacc[pt][i]);
+        for (int kb = 0; kb < KBC; ++kb) oacc[pt] = mma<T>(oacc[pt], ub[kb], mf[pt][kb]);   // + U^T M^T
+        // lane (g, r) holds O^T rows 4 g .. 4 g + 3 of column r: four consecutive
+        // value columns of output row 16 pt + r
+        store4<T>(orsrc, ((t0 + 16 * pt + r) * dv + ocol) * E, oacc[pt]);
       }
       // H <- d . H + KR^T U
 #pragma unroll

@@ -207,6 +207,15 @@ template <> __device__ __forceinline__ void store_elem<bf16_t>(__amdgpu_buffer_r
   __builtin_amdgcn_raw_buffer_store_b16(from_f32<bf16_t>(x).bits, r, byte_off, 0, 0);
 }
 
+// four consecutive elements to global memory in the storage type
+template <typename T> __device__ __forceinline__ void store4(__amdgpu_buffer_rsrc_t r, int byte_off, f32x4 x);
+template <> __device__ __forceinline__ void store4<float>(__amdgpu_buffer_rsrc_t r, int byte_off, f32x4 x) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), r, byte_off, 0, 0);
+}
+template <> __device__ __forceinline__ void store4<bf16_t>(__amdgpu_buffer_rsrc_t r, int byte_off, f32x4 x) {
+  __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])}, r, byte_off, 0, 0);
+}
+
 // Wave-wide sum (wave64) via cross-lane shuffles.
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
