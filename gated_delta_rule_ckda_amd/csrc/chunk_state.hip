@@ -22,7 +22,7 @@
 // the chunk's record (chunk_gram.hip).  Four "copy waves" move the records and
 // the slice's values V (gathered into accumulator order) into a double-
 // buffered operand set in LDS, staging them in registers: a chunk's loads are
-// issued two chunks before it is placed, which keeps enough bytes in flight
+// issued two (or three) chunks before it is placed, which keeps enough bytes in flight
 // per CU to cover the memory latency.  So the matrix waves issue no global
 // loads, only the output stores, and the copy waves only loads: with loads
 // and stores in flight together, every wait for a load would also wait for
@@ -57,7 +57,7 @@ struct StateCfg : ChunkGeom<T, DK, C> {
   static constexpr int NVI = (NVP + NCW * 64 - 1) / (NCW * 64);
   // register sets: a chunk's loads are issued NR iterations before they are
   // placed in LDS (two when they fit beside the loop's other registers)
-  static constexpr int NR = 2 * 4 * (NFL + NVI) <= 144 ? 2 : 1;
+  static constexpr int NR = 3 * 4 * (NFL + NVI) <= 160 ? 3 : 2 * 4 * (NFL + NVI) <= 144 ? 2 : 1;
 };
 
 template <typename T, int DK, int C, int NMW>
@@ -300,8 +300,8 @@ __global__ __launch_bounds__((StateCfg<T, DK, C, NMW>::NTHREADS)) void chunk_sta
     // prologue for the first ones) and placed in LDS in iteration x - 1.
     // Prologue: chunks 0 .. NR-1 requested, chunk 0 placed, chunk NR
     // requested: the loads in flight are then those one loop pass leaves.
-    swap(rr[0], 0, 0, false);
-    if constexpr (NR > 1) swap(rr[NR > 1 ? 1 : 0], 0, 1, false);
+#pragma unroll
+    for (int j = 0; j < NR; ++j) swap(rr[j], 0, j, false);
     swap(rr[0], 0, NR, true);
     lds_barrier();
     // Chunk c in use by the matrix waves: place chunk c + 1, then reuse its
@@ -320,10 +320,14 @@ __global__ __launch_bounds__((StateCfg<T, DK, C, NMW>::NTHREADS)) void chunk_sta
     int c = 0;
     for (; c + NR <= nchunks; c += NR) {
       iter(c, std::integral_constant<int, 1 % NR>{});
-      if constexpr (NR > 1) iter(c + 1, std::integral_constant<int, 0>{});
+      if constexpr (NR > 1) iter(c + 1, std::integral_constant<int, 2 % NR>{});
+      if constexpr (NR > 2) iter(c + 2, std::integral_constant<int, 3 % NR>{});
     }
     if constexpr (NR > 1) {
       if (c < nchunks) iter(c, std::integral_constant<int, 1 % NR>{});
+    }
+    if constexpr (NR > 2) {
+      if (c + 1 < nchunks) iter(c + 1, std::integral_constant<int, 2 % NR>{});
     }
   }
 }
