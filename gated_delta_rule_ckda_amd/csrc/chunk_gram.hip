@@ -233,6 +233,8 @@ __global__ __launch_bounds__((GramCfg<T, DK, C>::NTH)) void chunk_gram_kernel(
   // gamma_t being the product from the chunk start to t and G(C, t) the
   // product after t to the chunk end; rows past a ragged end have gate 1 and
   // zero key and query.
+  // (records are written with streaming stores: nothing reads them before
+  // the state pass, and keeping them out of the caches speeds this kernel up)
   unsigned char* rec = ws + (size_t)chunk_id * P::BYTES;
   {
     if (act) {
@@ -288,7 +290,7 @@ __global__ __launch_bounds__((GramCfg<T, DK, C>::NTH)) void chunk_gram_kernel(
     lds_barrier();
     // padded fragments [W][Q~][KR] -> the record, unpadded, same order
     for (int f = wave; f < P::NF3; f += NW)
-      store_frag(rec + P::W_OFF + (size_t)f * 1024 + lane * 16, load_frag(area + padded_slot(f, lane)));
+      store_frag_stream(rec + P::W_OFF + (size_t)f * 1024 + lane * 16, load_frag(area + padded_slot(f, lane)));
     lds_barrier();
     if constexpr (DK % KB != 0) {
       zero_area();
@@ -564,7 +566,7 @@ __global__ __launch_bounds__((GramCfg<T, DK, C>::NTH)) void chunk_gram_kernel(
     } else {
       out.w = __builtin_bit_cast(u32x4, f32x4{vals[0], vals[1], vals[2], vals[3]});
     }
-    store_frag(rec + (isT ? P::T_OFF : P::M_OFF) + frag_slot(rt, kb, KBC, lane), out);
+    store_frag_stream(rec + (isT ? P::T_OFF : P::M_OFF) + frag_slot(rt, kb, KBC, lane), out);
   }
 }
 

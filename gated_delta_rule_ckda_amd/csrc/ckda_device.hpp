@@ -122,6 +122,10 @@ __device__ __forceinline__ Frag load_frag(const void* p) {
   return f;
 }
 __device__ __forceinline__ void store_frag(void* p, Frag f) { *reinterpret_cast<u32x4*>(p) = f.w; }
+// global memory, nontemporal (streaming) store
+__device__ __forceinline__ void store_frag_stream(void* p, Frag f) {
+  __builtin_nontemporal_store(f.w, reinterpret_cast<u32x4*>(p));
+}
 
 // Workgroup barrier for LDS traffic only: waits for this wave's LDS
 // operations, then s_barrier.  Unlike __syncthreads() it does not wait for
