@@ -208,6 +208,18 @@ __global__ __launch_bounds__((GramCfg<T, DK, C>::NTH)) void chunk_gram_kernel(
     }
   }
 
+  // keys and queries widened to fp32 once: every operand below multiplies
+  // them (the gates stay packed: widened as well they would cost the third
+  // workgroup per CU its registers)
+  float kl[16], kh[16], ql[16], qh[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    kl[i] = PR::lo(rk[i]);
+    kh[i] = PR::hi(rk[i]);
+    ql[i] = PR::lo(rq[i]);
+    qh[i] = PR::hi(rq[i]);
+  }
+
   // K blocks only partly covered (bf16: channels when DK = 16, positions of
   // KR when C = 16): the uncovered half of every fragment must read as zero
   // (the pads, 16-byte unit 16 of every 17, hold beta and the tile products)
@@ -266,8 +278,8 @@ __global__ __launch_bounds__((GramCfg<T, DK, C>::NTH)) void chunk_gram_kernel(
       for (int i = 0; i < 16; ++i) {
         g0 *= LO(ra[i]);
         g1 *= HI(ra[i]);
-        put(b, i, -LO(rk[i]) * g0, -HI(rk[i]) * g1);
-        put(RT + b, i, LO(rq[i]) * g0, HI(rq[i]) * g1);
+        put(b, i, -kl[i] * g0, -kh[i] * g1);
+        put(RT + b, i, ql[i] * g0, qh[i] * g1);
       }
       if (b == RT - 1) *reinterpret_cast<float2*>(rec + P::D_OFF + c0 * 4) = make_float2(g0, g1);
       // KR^T: rows = channels c0, c0 + 1; K = positions, four at a time
@@ -277,8 +289,8 @@ __global__ __launch_bounds__((GramCfg<T, DK, C>::NTH)) void chunk_gram_kernel(
         float kr0[4], kr1[4];
 #pragma unroll
         for (int i = 3; i >= 0; --i) {
-          kr0[i] = LO(rk[4 * m + i]) * e0;
-          kr1[i] = HI(rk[4 * m + i]) * e1;
+          kr0[i] = kl[4 * m + i] * e0;
+          kr1[i] = kh[4 * m + i] * e1;
           e0 *= LO(ra[4 * m + i]);
           e1 *= HI(ra[4 * m + i]);
         }
@@ -325,17 +337,17 @@ __global__ __launch_bounds__((GramCfg<T, DK, C>::NTH)) void chunk_gram_kernel(
           p0 *= LO(ra[i]);
           p1 *= HI(ra[i]);
           const float b0 = __builtin_amdgcn_rcpf(p0), b1 = __builtin_amdgcn_rcpf(p1);
-          put(3 * b, i, LO(rk[i]) * p0, HI(rk[i]) * p1);
-          put(3 * b + 1, i, LO(rq[i]) * p0, HI(rq[i]) * p1);
-          put(3 * b + 2, i, LO(rk[i]) * b0, HI(rk[i]) * b1);
+          put(3 * b, i, kl[i] * p0, kh[i] * p1);
+          put(3 * b + 1, i, ql[i] * p0, qh[i] * p1);
+          put(3 * b + 2, i, kl[i] * b0, kh[i] * b1);
         }
         float s0 = kQuadScaleInv, s1 = kQuadScaleInv;
 #pragma unroll
         for (int i = q0 + 3; i >= q0; --i) {      // bm = suffix up to the midpoint / scale, am = 1 / bm
           const float a0 = __builtin_amdgcn_rcpf(s0), a1 = __builtin_amdgcn_rcpf(s1);
-          put(3 * b, i, LO(rk[i]) * a0, HI(rk[i]) * a1);
-          put(3 * b + 1, i, LO(rq[i]) * a0, HI(rq[i]) * a1);
-          put(3 * b + 2, i, LO(rk[i]) * s0, HI(rk[i]) * s1);
+          put(3 * b, i, kl[i] * a0, kh[i] * a1);
+          put(3 * b + 1, i, ql[i] * a0, qh[i] * a1);
+          put(3 * b + 2, i, kl[i] * s0, kh[i] * s1);
           s0 *= LO(ra[i]);
           s1 *= HI(ra[i]);
         }
@@ -371,13 +383,13 @@ __global__ __launch_bounds__((GramCfg<T, DK, C>::NTH)) void chunk_gram_kernel(
       for (int i = 8; i < 16; ++i) {
         x0 *= LO(ra[i]);
         x1 *= HI(ra[i]);
-        put(2 * b, i, LO(rk[i]) * x0, HI(rk[i]) * x1);
-        put(2 * b + 1, i, LO(rq[i]) * x0, HI(rq[i]) * x1);
+        put(2 * b, i, kl[i] * x0, kh[i] * x1);
+        put(2 * b + 1, i, ql[i] * x0, qh[i] * x1);
       }
       float y0 = 1.f, y1 = 1.f;
 #pragma unroll
       for (int i = 7; i >= 0; --i) {
-        put(2 * b, i, LO(rk[i]) * y0, HI(rk[i]) * y1);
+        put(2 * b, i, kl[i] * y0, kh[i] * y1);
         y0 *= LO(ra[i]);
         y1 *= HI(ra[i]);
       }
@@ -409,12 +421,12 @@ __global__ __launch_bounds__((GramCfg<T, DK, C>::NTH)) void chunk_gram_kernel(
         for (int i = 0; i < 16; ++i) {
           x0 *= LO(ra[i]);
           x1 *= HI(ra[i]);
-          put(P::pk(b), i, LO(rk[i]) * x0, HI(rk[i]) * x1);
-          put(P::pq(b), i, LO(rq[i]) * x0, HI(rq[i]) * x1);
+          put(P::pk(b), i, kl[i] * x0, kh[i] * x1);
+          put(P::pq(b), i, ql[i] * x0, qh[i] * x1);
           if (RT == 4 && b == 3) {
             const float z0 = x0 * m0, z1 = x1 * m1;
-            put(P::X32K, i, LO(rk[i]) * z0, HI(rk[i]) * z1);
-            put(P::X32Q, i, LO(rq[i]) * z0, HI(rq[i]) * z1);
+            put(P::X32K, i, kl[i] * z0, kh[i] * z1);
+            put(P::X32Q, i, ql[i] * z0, qh[i] * z1);
           }
         }
       }
@@ -422,8 +434,8 @@ __global__ __launch_bounds__((GramCfg<T, DK, C>::NTH)) void chunk_gram_kernel(
         float y0 = 1.f, y1 = 1.f;
 #pragma unroll
         for (int i = 15; i >= 0; --i) {
-          put(P::sk(b), i, LO(rk[i]) * y0, HI(rk[i]) * y1);
-          if (RT == 4 && b == 0) put(P::Y32, i, LO(rk[i]) * (y0 * m0), HI(rk[i]) * (y1 * m1));
+          put(P::sk(b), i, kl[i] * y0, kh[i] * y1);
+          if (RT == 4 && b == 0) put(P::Y32, i, kl[i] * (y0 * m0), kh[i] * (y1 * m1));
           y0 *= LO(ra[i]);
           y1 *= HI(ra[i]);
         }
