@@ -301,8 +301,21 @@ __global__ __launch_bounds__((GramCfg<T, DK, C>::NTH)) void chunk_gram_kernel(
     }
     lds_barrier();
     // padded fragments [W][Q~][KR] -> the record, unpadded, same order
-    for (int f = wave; f < P::NF3; f += NW)
-      store_frag_stream(rec + P::W_OFF + (size_t)f * 1024 + lane * 16, load_frag(area + padded_slot(f, lane)));
+    {
+      // unrolled, so that all of a wave's LDS reads are in flight together
+      constexpr int NPW = (P::NF3 + NW - 1) / NW;
+      Frag fr[NPW];
+#pragma unroll
+      for (int j = 0; j < NPW; ++j) {
+        const int f = wave + NW * j;
+        if (f < P::NF3) fr[j] = load_frag(area + padded_slot(f, lane));
+      }
+#pragma unroll
+      for (int j = 0; j < NPW; ++j) {
+        const int f = wave + NW * j;
+        if (f < P::NF3) store_frag_stream(rec + P::W_OFF + (size_t)f * 1024 + lane * 16, fr[j]);
+      }
+    }
     lds_barrier();
     if constexpr (DK % KB != 0) {
       zero_area();
@@ -553,7 +566,11 @@ __global__ __launch_bounds__((GramCfg<T, DK, C>::NTH)) void chunk_gram_kernel(
 
   // ---- record: T Diag(beta) and M fragments
   constexpr int NF = RT * KBC;
-  for (int f = wave; f < 2 * NF; f += NW) {
+  constexpr int NEW = (2 * NF + NW - 1) / NW;   // fragments per wave, unrolled
+#pragma unroll
+  for (int j = 0; j < NEW; ++j) {
+    const int f = wave + NW * j;
+    if (f >= 2 * NF) break;
     const bool isT = f < NF;
     const int ff = isT ? f : f - NF;
     const int rt = ff / KBC, kb = ff % KBC;
