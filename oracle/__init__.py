@@ -55,6 +55,8 @@ def _load():
         lib.ckda_oracle_decode.restype = i
         lib.ckda_oracle_num_threads.argtypes = []
         lib.ckda_oracle_num_threads.restype = i
+        lib.ckda_oracle_prologue.argtypes = [vp, vp, vp, vp, i, i, ctypes.c_longlong, i, vp, vp, vp, vp]
+        lib.ckda_oracle_prologue.restype = i
         _lib = lib
     return _lib
 
@@ -138,6 +140,55 @@ def decode(q, k, v, alpha, beta, S, nthreads=0):
     return o
 
 
+# flags of the per-token prologue (ckda_oracle.c)
+GATES, NORM_K, NORM_Q = 1, 2, 4
+
+
+def prologue(a, b, k, q, flags):
+    """Practical gates from logits and unit-norm keys / queries, in fp64.
+
+    a, k, q: [..., dk]; b: [...]; one dtype.  With GATES, a and b are the
+    logits of alpha and beta; NORM_K / NORM_Q scale k / q to unit norm per
+    token.  Returns fp64 (alpha, beta, k, q); a step whose flag is off returns
+    its input widened."""
+    a, b, k, q = (np.ascontiguousarray(x) for x in (a, b, k, q))
+    code = _code(a)
+    for x in (b, k, q):
+        if _code(x) != code:
+            raise TypeError("a, b, k, q must share one dtype")
+    if k.shape != a.shape or q.shape != a.shape or b.shape != a.shape[:-1]:
+        raise ValueError("inconsistent shapes")
+    dk = a.shape[-1]
+    ntok = int(np.prod(a.shape[:-1], dtype=np.int64))
+    alpha, kk, qq = (np.empty(a.shape, np.float64) for _ in range(3))
+    beta = np.empty(b.shape, np.float64)
+    rc = _load().ckda_oracle_prologue(_ptr(a), _ptr(b), _ptr(k), _ptr(q), code, int(flags), ntok, dk,
+                                      _ptr(alpha), _ptr(beta), _ptr(kk), _ptr(qq))
+    if rc != 0:
+        raise RuntimeError(f"ckda_oracle_prologue failed with code {rc}")
+    return alpha, beta, kk, qq
+
+
+def _widen(x):
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.uint16:
+        return (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return x.astype(np.float64)
+
+
+def fwd_fused(q, k, v, a, b, h0=None, flags=GATES | NORM_K, want_o=True, nthreads=0):
+    """fwd() after the per-token prologue: the recurrence runs on the fp64
+    gates and unit vectors the prologue produces (v widened exactly)."""
+    alpha, beta, kk, qq = prologue(a, b, k, q, flags)
+    return fwd(qq, kk, _widen(v), alpha, beta, h0=h0, want_o=want_o, nthreads=nthreads)
+
+
+def decode_fused(q, k, v, a, b, S, flags=GATES | NORM_K, nthreads=0):
+    """decode() after the per-token prologue."""
+    alpha, beta, kk, qq = prologue(a, b, k, q, flags)
+    return decode(qq, kk, _widen(v), alpha, beta, S, nthreads=nthreads)
+
+
 class Variant:
     """An oracle bound to another build of ckda_oracle.c (same ABI).
 
@@ -156,6 +207,8 @@ class Variant:
         lib.ckda_oracle_fwd.restype = i
         lib.ckda_oracle_decode.argtypes = [vp, vp, vp, vp, vp, i, vp, vp, i, i, i, i, i]
         lib.ckda_oracle_decode.restype = i
+        lib.ckda_oracle_prologue.argtypes = [vp, vp, vp, vp, i, i, ctypes.c_longlong, i, vp, vp, vp, vp]
+        lib.ckda_oracle_prologue.restype = i
         _lib = lib
         try:
             return fn(*a, **kw)
@@ -167,6 +220,12 @@ class Variant:
 
     def decode(self, *a, **kw):
         return self._swap(decode, *a, **kw)
+
+    def prologue(self, *a, **kw):
+        return self._swap(prologue, *a, **kw)
+
+    def fwd_fused(self, *a, **kw):
+        return self._swap(fwd_fused, *a, **kw)
 
 
 def build_variant(source_text: str, out_path: str) -> "Variant":

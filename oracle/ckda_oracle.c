@@ -170,3 +170,67 @@ int ckda_oracle_num_threads(void) {
   return 1;
 #endif
 }
+
+/* ---------------------------------------------------------------- prologue
+ *
+ * The practical gate and key parameterisation of the "Complex KDA" discussion
+ * slides (frame "Backup: practical gates differ from exact theoretical
+ * endpoints"; paper App. E--G.1), applied per token before the recurrence:
+ *
+ *   r = tanh(a / 2),  s = +1 if r >= 0 else -1,
+ *   alpha = s (eps + (1 - eps) |r|),  eps = e^-5,       so log|alpha| in [-5, 0]
+ *   beta  = 2 sigma(b),
+ *
+ * and keys (optionally queries) scaled to unit Euclidean norm per token (the
+ * recurrence assumes ||k_t|| = 1; slides, frame "Absorb cumulative signs into
+ * keys and queries", fuses the sign application with this normalisation).
+ * The pages give no guard for a zero vector; here x / sqrt(sum x^2 + 1e-6),
+ * which maps a zero vector to zero and changes a unit vector by 5e-7.
+ *
+ * Flags: 1 = alpha and beta arguments are the logits a and b; 2 = normalise k;
+ * 4 = normalise q.  A step whose flag is off copies its input (widened).
+ * Layouts: a, k, q [ntok, dk]; b [ntok]; outputs fp64 of the same shapes.
+ * Returns 0, or 1 for invalid arguments. */
+#define PRO_GATES 1
+#define PRO_NORM_K 2
+#define PRO_NORM_Q 4
+
+static double practical_alpha(double a) {
+  const double eps = exp(-5.0);
+  const double r = tanh(0.5 * a);
+  const double s = r >= 0.0 ? 1.0 : -1.0;
+  return s * (eps + (1.0 - eps) * fabs(r));
+}
+
+static double practical_beta(double b) { return 2.0 / (1.0 + exp(-b)); }
+
+static void unit_rows(const void* x, int dtype, long long ntok, int dk, int on, double* out) {
+  for (long long t = 0; t < ntok; ++t) {
+    double ss = 0.0;
+    for (int i = 0; i < dk; ++i) {
+      const double e = widen(x, t * dk + i, dtype);
+      out[t * dk + i] = e;
+      ss += e * e;
+    }
+    if (on) {
+      const double inv = 1.0 / sqrt(ss + 1e-6);
+      for (int i = 0; i < dk; ++i) out[t * dk + i] *= inv;
+    }
+  }
+}
+
+int ckda_oracle_prologue(const void* a, const void* b, const void* k, const void* q, int dtype, int flags,
+                         long long ntok, int dk, double* alpha, double* beta, double* kk, double* qq) {
+  if (!valid_dtype(dtype) || ntok < 0 || dk <= 0 || (flags & ~7) != 0) return 1;
+  for (long long i = 0; i < ntok * dk; ++i) {
+    const double e = widen(a, i, dtype);
+    alpha[i] = (flags & PRO_GATES) ? practical_alpha(e) : e;
+  }
+  for (long long t = 0; t < ntok; ++t) {
+    const double e = widen(b, t, dtype);
+    beta[t] = (flags & PRO_GATES) ? practical_beta(e) : e;
+  }
+  unit_rows(k, dtype, ntok, dk, flags & PRO_NORM_K, kk);
+  unit_rows(q, dtype, ntok, dk, flags & PRO_NORM_Q, qq);
+  return 0;
+}

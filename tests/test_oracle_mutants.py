@@ -1,7 +1,8 @@
 """Each plausible slip planted in a copy of the oracle (on the CPU) must fail at
 least one pin.  This shows the pins constrain every part of the step: the
 order gate -> read -> correct -> query, the sign and weight of the correction,
-the row/column role of the gate, and the signed gates."""
+the row/column role of the gate, the signed gates, and the per-token prologue
+(practical gates from logits, unit-norm keys and queries)."""
 import pytest
 
 import oracle
@@ -38,6 +39,18 @@ MUTANTS = {
     "query_reads_gated_state": [("      for (int j = 0; j < dv; ++j) out[j] += S[(long)i * dv + j] * qq[i];",
                                  "      for (int j = 0; j < dv; ++j) out[j] += (S[(long)i * dv + j] - b * kk[i] * "
                                  "(vv[j] - s[j])) * qq[i];")],
+    # prologue (practical gates, unit-norm keys and queries)
+    "gate_eps_wrong": [("  const double eps = exp(-5.0);", "  const double eps = exp(-4.0);")],
+    "gate_tanh_without_half": [("  const double r = tanh(0.5 * a);", "  const double r = tanh(a);")],
+    "gate_sign_negative_at_zero": [("  const double s = r >= 0.0 ? 1.0 : -1.0;", "  const double s = r > 0.0 ? 1.0 : -1.0;")],
+    "gate_sign_dropped_in_prologue": [("  return s * (eps + (1.0 - eps) * fabs(r));", "  return (eps + (1.0 - eps) * fabs(r));")],
+    "beta_not_doubled": [("static double practical_beta(double b) { return 2.0 / (1.0 + exp(-b)); }",
+                          "static double practical_beta(double b) { return 1.0 / (1.0 + exp(-b)); }")],
+    "beta_logit_sign": [("static double practical_beta(double b) { return 2.0 / (1.0 + exp(-b)); }",
+                         "static double practical_beta(double b) { return 2.0 / (1.0 + exp(b)); }")],
+    "norm_without_sqrt": [("      const double inv = 1.0 / sqrt(ss + 1e-6);", "      const double inv = 1.0 / (ss + 1e-6);")],
+    "norm_flags_swapped": [("  unit_rows(k, dtype, ntok, dk, flags & PRO_NORM_K, kk);",
+                            "  unit_rows(k, dtype, ntok, dk, flags & PRO_NORM_Q, kk);")],
 }
 
 PIN_CALLS = [
@@ -54,6 +67,12 @@ PIN_CALLS = [
     lambda o: pins.test_exact_retrieval_at_beta_one(o),
     lambda o: pins.test_pure_decay_at_beta_zero(o),
     lambda o: pins.test_gauge_sign_absorption(o),
+    lambda o: pins.test_practical_gate_endpoints_and_zero(o),
+    lambda o: pins.test_practical_gate_matches_sigmoid_form(o),
+    lambda o: pins.test_practical_gate_sign_symmetry_and_range(o),
+    lambda o: pins.test_practical_beta(o),
+    lambda o: pins.test_unit_norm_keys_and_queries(o),
+    lambda o: pins.test_fused_forward_is_the_recurrence_on_prepared_inputs(o),
 ]
 
 

@@ -420,3 +420,108 @@ def test_bf16_reader_widens_exactly(oracle_lib):
     o, _ = oracle_lib.fwd(raw(xb), raw(xb), raw(xb), raw(torch.ones_like(xb)),
                           raw(torch.zeros((1, 1, 1), dtype=torch.bfloat16)), h0=h0)
     np.testing.assert_array_equal(o, xb.to(torch.float64).numpy())
+
+
+# --------------------------------------------------------------------------
+# Per-token prologue: the practical gate parameterisation of the discussion
+# slides (frame "Backup: practical gates differ from exact theoretical
+# endpoints") and unit-norm keys / queries.  Pinned through identities and
+# limits stated on the pages, not by re-deriving the oracle's own formula.
+
+G, NK, NQ = 1, 2, 4
+
+
+def pro(oracle_lib, a, b, k=None, q=None, flags=G):
+    a = np.atleast_2d(np.asarray(a, np.float64))
+    b = np.asarray(b, np.float64).reshape(a.shape[:-1])
+    k = np.ones_like(a) if k is None else np.atleast_2d(np.asarray(k, np.float64))
+    q = np.ones_like(a) if q is None else np.atleast_2d(np.asarray(q, np.float64))
+    return oracle_lib.prologue(a, b, k, q, flags)
+
+
+def test_practical_gate_endpoints_and_zero(oracle_lib):
+    """log|alpha| spans [-5, 0]: alpha(0) = +e^-5 (s = +1 at r = 0) and the
+    gate tends to +-1 as the logit grows (reached in fp64 at |a| = 80)."""
+    al, be, _, _ = pro(oracle_lib, [0.0, 80.0, -80.0], [0.0])
+    assert al[0, 0] == math.exp(-5.0)
+    assert al[0, 1] == 1.0 and al[0, 2] == -1.0
+    assert be[0] == 1.0                      # beta = 2 sigma(0) = 1
+
+
+def test_practical_gate_matches_sigmoid_form(oracle_lib):
+    """tanh(a/2) = 2 sigma(a) - 1 (both forms are given for r): the gate built
+    from the sigmoid form agrees, for logits of both signs."""
+    rng = np.random.default_rng(7)
+    a = rng.normal(0.0, 3.0, 512)
+    al, _, _, _ = pro(oracle_lib, a, [0.0])
+    r = 2.0 / (1.0 + np.exp(-a)) - 1.0
+    eps = math.exp(-5.0)
+    want = np.where(r >= 0, 1.0, -1.0) * (eps + (1.0 - eps) * np.abs(r))
+    assert np.max(np.abs(al[0] - want)) < 1e-14
+
+
+def test_practical_gate_sign_symmetry_and_range(oracle_lib):
+    """The gate carries the logit's sign, is odd away from zero, and its
+    magnitude grows with |a| inside [e^-5, 1]."""
+    a = np.linspace(0.01, 20.0, 400)
+    al_p, _, _, _ = pro(oracle_lib, a, [0.0])
+    al_m, _, _, _ = pro(oracle_lib, -a, [0.0])
+    assert np.all(al_p[0] > 0) and np.all(al_m[0] < 0)
+    assert np.array_equal(al_m[0], -al_p[0])
+    assert np.all(np.diff(al_p[0]) > 0)
+    la = np.log(np.abs(al_p[0]))
+    assert la.min() >= -5.0 and la.max() <= 0.0
+
+
+def test_practical_beta(oracle_lib):
+    """beta = 2 sigma(b): beta(b) + beta(-b) = 2, range (0, 2), beta(0) = 1."""
+    b = np.linspace(-12.0, 12.0, 241)
+    _, bp, _, _ = pro(oracle_lib, np.zeros((241, 1)), b)
+    _, bm, _, _ = pro(oracle_lib, np.zeros((241, 1)), -b)
+    assert np.max(np.abs(bp + bm - 2.0)) < 1e-15
+    assert np.all(bp > 0) and np.all(bp < 2) and bp[120] == 1.0
+
+
+def test_unit_norm_keys_and_queries(oracle_lib):
+    """(3, 4) -> (0.6, 0.8) up to the 1e-6 guard; random rows come out with
+    unit norm in their own direction; a zero row stays zero; with its flag off
+    a vector passes through unchanged."""
+    k = np.array([[3.0, 4.0, 0.0, 0.0], [0.0, 0.0, 0.0, 0.0]])
+    q = np.array([[1.0, 2.0, 2.0, 0.0], [0.0, 0.0, 0.0, 0.0]])
+    _, _, kk, qq = pro(oracle_lib, np.zeros((2, 4)), [0.0, 0.0], k, q, NK)
+    assert np.max(np.abs(kk[0] - [0.6, 0.8, 0.0, 0.0])) < 1e-7
+    assert np.all(kk[1] == 0.0)
+    assert np.array_equal(qq, q)                     # NORM_Q off
+    _, _, _, qq = pro(oracle_lib, np.zeros((2, 4)), [0.0, 0.0], k, q, NQ)
+    assert np.max(np.abs(qq[0] - np.array([1.0, 2.0, 2.0, 0.0]) / 3.0)) < 1e-7
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((64, 128)) * rng.uniform(0.1, 10.0, (64, 1))
+    _, _, kk, _ = pro(oracle_lib, np.zeros_like(x), np.zeros(64), x, x, NK)
+    n = np.linalg.norm(kk, axis=1)
+    assert np.max(np.abs(n - 1.0)) < 1e-6
+    cos = np.sum(kk * x, axis=1) / np.linalg.norm(x, axis=1)
+    assert np.max(np.abs(cos - 1.0)) < 1e-6
+
+
+def test_fused_forward_is_the_recurrence_on_prepared_inputs(oracle_lib):
+    """fwd_fused = the plain recurrence on gates built by the sigmoid form of
+    the slides and keys scaled by numpy's norm (tolerance for the 1e-6 guard)."""
+    rng = np.random.default_rng(11)
+    T, n, dv = 24, 6, 5
+    a = rng.normal(0, 2, (T, n))
+    b = rng.normal(0, 1, T)
+    k = rng.normal(0, 1, (T, n))
+    q = rng.normal(0, 1, (T, n))
+    v = rng.normal(0, 1, (T, dv))
+    h0 = rng.normal(0, 0.1, (n, dv))
+    e = lambda x: x[None, None]
+    o_f, h_f = oracle_lib.fwd_fused(e(q), e(k), e(v), e(a), b[None, None], h0=h0[None, None], flags=G | NK | NQ)
+    r = 2.0 / (1.0 + np.exp(-a)) - 1.0
+    eps = math.exp(-5.0)
+    al = np.where(r >= 0, 1.0, -1.0) * (eps + (1.0 - eps) * np.abs(r))
+    be = 2.0 / (1.0 + np.exp(-b))
+    kn = k / np.linalg.norm(k, axis=1, keepdims=True)
+    qn = q / np.linalg.norm(q, axis=1, keepdims=True)
+    o_p, h_p = run(oracle_lib, qn, kn, v, al, be, h0)
+    assert np.max(np.abs(o_f[0, 0] - o_p)) < 1e-5 * max(1.0, np.max(np.abs(o_p)))
+    assert np.max(np.abs(h_f[0, 0] - h_p)) < 1e-5 * max(1.0, np.max(np.abs(h_p)))
