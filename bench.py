@@ -5,7 +5,9 @@ One step = one chunkwise forward of the ckda_bf16 workload (B4 H16 T4096,
 d_k = d_v = 128, chunk 64, full CKDA gate ranges, h0 ~ N(0, 0.1)): gate sign
 and magnitude split, Gram matrices, triangular solve, state pass and output,
 plus the final state.  The decode step (256 sequences x 32 heads, d128, fp32
-state updated in place) is timed in the same run and reported under "decode".
+state updated in place) is timed in the same run and reported under "decode",
+and both again with the per-token prologue fused (gates from logits, unit-norm
+keys) under "fused_prologue".
 
 Prints ONE JSON line.  `value` is tokens/s of the forward (a token is one
 (batch, position) across all heads), inputs resident in HBM: tokens per step
@@ -197,6 +199,40 @@ def main():
     dec_gbs_state = state_bytes / (dec_ms * 1e-3) / 1e9
     dec_gbs_total = (state_bytes + io_bytes) / (dec_ms * 1e-3) / 1e9
 
+    # ---- the same forward and decode step with the per-token prologue fused
+    # (gates and beta from logits, unit-norm keys): ckda_chunk_fwd_ex and
+    # ckda_decode_step_ex, per-call HIP events on the same stream
+    fuse = ck.FUSE_GATES | ck.FUSE_NORM_K
+    log(f"[bench] fused prologue, flags {fuse}")
+    lg = {k: (None if v is None else v.to(dev)) for k, v in gen.make_logit_inputs(w).items()}
+
+    def fstep():
+        ck.chunk_fwd(lg["q"], lg["k"], lg["v"], lg["alpha"], lg["beta"], lg["h0"], chunk=w.chunk,
+                     workspace=ws, o=o, hT=hT, fuse=fuse)
+
+    for _ in range(a.warmup):
+        fstep()
+    torch.cuda.synchronize()
+    fev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(a.steps)]
+    for s in range(a.steps):
+        fev[s][0].record(stream)
+        fstep()
+        fev[s][1].record(stream)
+    torch.cuda.synchronize()
+    fused_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in fev]))
+    dlg = [{k: v.to(dev) for k, v in gen.decode_logit_inputs(s, dec).items()} for s in range(8)]
+    for s in range(a.warmup):
+        x = dlg[s % 8]
+        ck.decode_step(x["q"], x["k"], x["v"], x["alpha"], x["beta"], S, o=do, fuse=fuse)
+    torch.cuda.synchronize()
+    for s in range(a.decode_steps):
+        x = dlg[s % 8]
+        dev_ev[s][0].record(stream)
+        ck.decode_step(x["q"], x["k"], x["v"], x["alpha"], x["beta"], S, o=do, fuse=fuse)
+        dev_ev[s][1].record(stream)
+    torch.cuda.synchronize()
+    fdec_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in dev_ev]))
+
     # ---- reference device copy of the decode state's size (practical ceiling)
     src = torch.empty(dec.N * dec.H * dec.dk * dec.dv, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
@@ -254,6 +290,15 @@ def main():
             "total_GB_s": round(dec_gbs_total, 1),
             "frac_of_hbm_peak": round(dec_gbs_total / HBM_PEAK_GBS, 4),
             "device_copy_GB_s": round(copy_gbs, 1),
+        },
+        "fused_prologue": {
+            "flags": "CKDA_FUSE_GATES | CKDA_FUSE_NORM_K",
+            "inputs": "gate and beta logits, unnormalised keys (same shapes)",
+            "forward_call_ms_mean": round(fused_ms, 4),
+            "forward_tokens_per_s": round(tokens / (fused_ms * 1e-3), 1),
+            "forward_overhead_vs_plain": round(fused_ms / call_ms - 1.0, 4),
+            "decode_ms_per_step_events": round(fdec_ms, 4),
+            "decode_total_GB_s": round((state_bytes + io_bytes) / (fdec_ms * 1e-3) / 1e9, 1),
         },
     }
 

@@ -7,6 +7,9 @@ fails to load, every call raises.
 
     o, hT = chunk_fwd(q, k, v, alpha, beta, h0=None, chunk=64)
     o = decode_step(q, k, v, alpha, beta, H)          # H updated in place
+
+With fuse=FUSE_GATES | FUSE_NORM_K (| FUSE_NORM_Q) the kernels first apply the
+per-token prologue: alpha and beta are logits, keys (queries) are normalised.
 """
 from __future__ import annotations
 
@@ -20,9 +23,11 @@ LIB_PATH = os.path.join(_HERE, "libckda.so")
 
 DTYPE_F32, DTYPE_BF16 = 0, 1
 STATUS = {0: "CKDA_OK", 1: "CKDA_ERR_NULL", 2: "CKDA_ERR_DIM", 3: "CKDA_ERR_UNSUPPORTED",
-          4: "CKDA_ERR_ALIAS", 5: "CKDA_ERR_WORKSPACE", 6: "CKDA_ERR_HIP"}
-EXPORTS = ("ckda_chunk_fwd_workspace_size", "ckda_chunk_fwd", "ckda_chunk_fwd_timed", "ckda_decode_step",
-           "ckda_status_string", "ckda_last_error", "ckda_abi_version")
+          4: "CKDA_ERR_ALIAS", 5: "CKDA_ERR_WORKSPACE", 6: "CKDA_ERR_HIP", 7: "CKDA_ERR_FLAGS"}
+FUSE_GATES, FUSE_NORM_K, FUSE_NORM_Q = 1, 2, 4       # CKDA_FUSE_*
+EXPORTS = ("ckda_chunk_fwd_workspace_size", "ckda_chunk_fwd", "ckda_chunk_fwd_timed", "ckda_chunk_fwd_ex",
+           "ckda_decode_step", "ckda_decode_step_ex", "ckda_status_string", "ckda_last_error",
+           "ckda_abi_version")
 
 _lib = None
 
@@ -48,8 +53,12 @@ def lib() -> ctypes.CDLL:
         L.ckda_chunk_fwd.restype = i
         L.ckda_chunk_fwd_timed.argtypes = [vp] * 8 + [i] * 7 + [vp, sz, vp, vp, vp, vp]
         L.ckda_chunk_fwd_timed.restype = i
+        L.ckda_chunk_fwd_ex.argtypes = [vp] * 8 + [i] * 8 + [vp, sz, vp]
+        L.ckda_chunk_fwd_ex.restype = i
         L.ckda_decode_step.argtypes = [vp] * 7 + [i] * 5 + [vp]
         L.ckda_decode_step.restype = i
+        L.ckda_decode_step_ex.argtypes = [vp] * 7 + [i] * 6 + [vp]
+        L.ckda_decode_step_ex.restype = i
         L.ckda_status_string.argtypes = [i]
         L.ckda_status_string.restype = ctypes.c_char_p
         L.ckda_last_error.argtypes = []
@@ -98,7 +107,7 @@ def workspace_size(B, H, T, dk, dv, chunk, dtype) -> int:
 
 
 def chunk_fwd(q, k, v, alpha, beta, h0=None, chunk=64, workspace=None, o=None, hT=None,
-              want_state=True, stream=None, events=None):
+              want_state=True, stream=None, events=None, fuse=0):
     """Chunkwise forward.  q, k, alpha [B,H,T,dk]; v [B,H,T,dv]; beta [B,H,T];
     h0 [B,H,dk,dv] fp32 or None.  Returns (o [B,H,T,dv], hT [B,H,dk,dv] fp32 or None).
 
@@ -106,7 +115,9 @@ def chunk_fwd(q, k, v, alpha, beta, h0=None, chunk=64, workspace=None, o=None, h
     `hT` may be passed in to avoid allocations (e.g. in timed loops).
     `events`, three recorded-once torch.cuda.Event objects (or None), are
     recorded before the Gram kernel, between the kernels and after the
-    state-pass kernel (ckda_chunk_fwd_timed)."""
+    state-pass kernel (ckda_chunk_fwd_timed).  `fuse` (FUSE_* bits) applies
+    the per-token prologue (ckda_chunk_fwd_ex); it cannot be combined with
+    `events`."""
     B, H, T, dk = q.shape
     dv = v.shape[-1]
     _require(dict(q=q, k=k, v=v, alpha=alpha, beta=beta), q.dtype)
@@ -125,7 +136,12 @@ def chunk_fwd(q, k, v, alpha, beta, h0=None, chunk=64, workspace=None, o=None, h
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(h0), _ptr(o), _ptr(hT),
             B, H, T, dk, dv, chunk, code, _ptr(workspace), workspace.numel() * workspace.element_size(),
             _stream(stream))
-    if events is None:
+    if fuse:
+        if events is not None:
+            raise ValueError("events are recorded by the plain forward only (fuse=0)")
+        args = args[:15] + (int(fuse),) + args[15:]
+        _check(lib().ckda_chunk_fwd_ex(*args))
+    elif events is None:
         _check(lib().ckda_chunk_fwd(*args))
     else:
         handles = [None if e is None else ctypes.c_void_p(e.cuda_event) for e in events]
@@ -133,9 +149,10 @@ def chunk_fwd(q, k, v, alpha, beta, h0=None, chunk=64, workspace=None, o=None, h
     return o, hT
 
 
-def decode_step(q, k, v, alpha, beta, H, o=None, stream=None):
+def decode_step(q, k, v, alpha, beta, H, o=None, stream=None, fuse=0):
     """One decode step.  q, k, alpha [N,Hh,dk]; v [N,Hh,dv]; beta [N,Hh];
-    H [N,Hh,dk,dv] fp32 updated in place.  Returns o [N,Hh,dv]."""
+    H [N,Hh,dk,dv] fp32 updated in place.  Returns o [N,Hh,dv].  `fuse`
+    (FUSE_* bits) applies the per-token prologue first (ckda_decode_step_ex)."""
     N, Hh, dk = q.shape
     dv = v.shape[-1]
     _require(dict(q=q, k=k, v=v, alpha=alpha, beta=beta), q.dtype)
@@ -143,6 +160,9 @@ def decode_step(q, k, v, alpha, beta, H, o=None, stream=None):
     code = _dtype_code(q)
     if o is None:
         o = torch.empty((N, Hh, dv), dtype=q.dtype, device=q.device)
-    _check(lib().ckda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(H), _ptr(o),
-                                  N, Hh, dk, dv, code, _stream(stream)))
+    ptrs = (_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(H), _ptr(o))
+    if fuse:
+        _check(lib().ckda_decode_step_ex(*ptrs, N, Hh, dk, dv, code, int(fuse), _stream(stream)))
+    else:
+        _check(lib().ckda_decode_step(*ptrs, N, Hh, dk, dv, code, _stream(stream)))
     return o

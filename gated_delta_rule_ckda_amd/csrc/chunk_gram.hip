@@ -43,6 +43,8 @@
 // row at a time, into padded fragment buffers in LDS, from which the waves
 // feed the matrix cores.  Three stages (diagonal quadrants, LL quadrants, tile
 // pairs) reuse one LDS area; the tile products P_b go through LDS.
+#include <type_traits>
+
 #include "chunk_common.hpp"
 #include "ckda_internal.hpp"
 
@@ -139,13 +141,19 @@ __device__ __forceinline__ void tile_pair(int n, int& I, int& J, int& xk, int& x
   }
 }
 
-template <typename T, int DK, int C>
+// PRO: the per-token prologue of ckda.h (flags CKDA_FUSE_*) runs on the loads:
+// gates from their logits, beta from its logit, unit-norm keys and queries.
+// The gates are then kept in fp32 (a rounded computed gate would compound
+// over the chunk's products).
+template <typename T, int DK, int C, bool PRO>
 __global__ __launch_bounds__((GramCfg<T, DK, C>::NTH)) void chunk_gram_kernel(
     const T* q, const T* k, const T* alpha, const T* beta, unsigned char* __restrict__ ws, int T_len,
-    int nchunks) {
+    int nchunks, int flags) {
   using P = GramCfg<T, DK, C>;
   using PR = Pair<T>;
   typedef typename PR::raw raw;
+  using GR = Pair<typename std::conditional<PRO, float, T>::type>;   // storage of the gates
+  typedef typename GR::raw graw;
   constexpr int NU = P::NU, NW = P::NW, NTH = P::NTH, RT = P::RT, KBN = P::KBN, KBC = P::KBC,
                 TOPB = P::TOPB, EPL = P::EPL, KB = P::KB;
   __shared__ __attribute__((aligned(16))) unsigned char lds[P::LDS_BYTES];
@@ -171,7 +179,11 @@ __global__ __launch_bounds__((GramCfg<T, DK, C>::NTH)) void chunk_gram_kernel(
   const int cv = min(C, T_len - t0);
   const long long row0 = bh * (long long)T_len + t0;
 
-  if (tid < C) *s_beta(tid) = tid < cv ? to_f32(beta[row0 + tid]) : 0.f;
+  if (tid < C) {
+    float bt = tid < cv ? to_f32(beta[row0 + tid]) : 0.f;
+    if (PRO && (flags & kFuseGates) && tid < cv) bt = practical_beta(bt);
+    *s_beta(tid) = bt;
+  }
 
   const int b = tid / NU, u = tid % NU;
   const bool act = b < RT;
@@ -179,13 +191,27 @@ __global__ __launch_bounds__((GramCfg<T, DK, C>::NTH)) void chunk_gram_kernel(
   const int colofs = padded_col_offset<T>(c0);
 
   // ---- this thread's rows: signed gates (floored), keys, queries
-  raw ra[16], rk[16], rq[16];
+  // gate pair as stored, or (prologue) as computed from its logits
+  auto gate_pair = [&](raw x) __attribute__((always_inline)) {
+    if constexpr (PRO) {
+      float a0 = PR::lo(x), a1 = PR::hi(x);
+      if (flags & kFuseGates) {
+        a0 = practical_gate(a0);
+        a1 = practical_gate(a1);
+      }
+      return graw{a0, a1};
+    } else {
+      return x;
+    }
+  };
+  graw ra[16];
+  raw rk[16], rq[16];
   if (act) {
     const size_t base = (size_t)(row0 + 16 * b) * DK + c0;
     if (cv == C) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        ra[i] = PR::load(alpha + base + (size_t)i * DK);
+        ra[i] = gate_pair(PR::load(alpha + base + (size_t)i * DK));
         rk[i] = PR::load(k + base + (size_t)i * DK);
         rq[i] = PR::load(q + base + (size_t)i * DK);
       }
@@ -195,8 +221,9 @@ __global__ __launch_bounds__((GramCfg<T, DK, C>::NTH)) void chunk_gram_kernel(
       for (int i = 0; i < 16; ++i) {
         const int t = 16 * b + i;
         const size_t off = base + (size_t)(min(t, cv - 1) - 16 * b) * DK;
-        const raw a = PR::load(alpha + off), kk = PR::load(k + off), qq = PR::load(q + off);
-        ra[i] = PR::ones();
+        const raw kk = PR::load(k + off), qq = PR::load(q + off);
+        const graw a = gate_pair(PR::load(alpha + off));
+        ra[i] = GR::ones();
         rk[i] = PR::zeros();
         rq[i] = PR::zeros();
         if (t < cv) {
@@ -219,6 +246,23 @@ __global__ __launch_bounds__((GramCfg<T, DK, C>::NTH)) void chunk_gram_kernel(
     ql[i] = PR::lo(rq[i]);
     qh[i] = PR::hi(rq[i]);
   }
+  if constexpr (PRO) {
+    // unit rows: the NU lanes holding one row (NU-aligned within the wave)
+    // sum their squares by butterfly shuffles
+    auto unit_rows = [&](float* lo, float* hi) __attribute__((always_inline)) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float ss = lo[i] * lo[i] + hi[i] * hi[i];
+#pragma unroll
+        for (int off = NU / 2; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
+        const float inv = 1.f / sqrtf(ss + kUnitGuard);
+        lo[i] *= inv;
+        hi[i] *= inv;
+      }
+    };
+    if (flags & kFuseNormK) unit_rows(kl, kh);
+    if (flags & kFuseNormQ) unit_rows(ql, qh);
+  }
 
   // K blocks only partly covered (bf16: channels when DK = 16, positions of
   // KR when C = 16): the uncovered half of every fragment must read as zero
@@ -236,8 +280,8 @@ __global__ __launch_bounds__((GramCfg<T, DK, C>::NTH)) void chunk_gram_kernel(
   auto put = [&](int slot, int i, float v0, float v1) {
     PR::put(area + slot * TOPB + colofs + i * 16, v0, v1);
   };
-#define LO(x) PR::lo(x)
-#define HI(x) PR::hi(x)
+#define LO(x) GR::lo(x)
+#define HI(x) GR::hi(x)
 
   // ---- phase 0: the gate-product operands of the state pass.  Only products
   // of gates occur (modulus at most 1), so the gates are used as given.
@@ -326,7 +370,7 @@ __global__ __launch_bounds__((GramCfg<T, DK, C>::NTH)) void chunk_gram_kernel(
   // Gate magnitudes floored for the Gram stages (see the file comment)
   if (act) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) ra[i] = floor_gates<T>(ra[i]);
+    for (int i = 0; i < 16; ++i) ra[i] = floor_gates<typename std::conditional<PRO, float, T>::type>(ra[i]);
   }
   // acc += X[xs] Y[ys]^T over all channels
   auto gram = [&](f32x4 acc, int xs, int ys) {
@@ -602,9 +646,14 @@ __global__ __launch_bounds__((GramCfg<T, DK, C>::NTH)) void chunk_gram_kernel(
 template <typename T, int DK, int C>
 hipError_t launch_gram_t(const ChunkArgs& a, long long total_chunks, int nchunks) {
   using P = GramCfg<T, DK, C>;
-  hipLaunchKernelGGL((chunk_gram_kernel<T, DK, C>), dim3((unsigned)total_chunks), dim3(P::NTH), 0, a.stream,
-                     (const T*)a.q, (const T*)a.k, (const T*)a.alpha, (const T*)a.beta,
-                     (unsigned char*)a.workspace, a.T, nchunks);
+  if (a.flags != 0)
+    hipLaunchKernelGGL((chunk_gram_kernel<T, DK, C, true>), dim3((unsigned)total_chunks), dim3(P::NTH), 0,
+                       a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.alpha, (const T*)a.beta,
+                       (unsigned char*)a.workspace, a.T, nchunks, a.flags);
+  else
+    hipLaunchKernelGGL((chunk_gram_kernel<T, DK, C, false>), dim3((unsigned)total_chunks), dim3(P::NTH), 0,
+                       a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.alpha, (const T*)a.beta,
+                       (unsigned char*)a.workspace, a.T, nchunks, 0);
   return hipGetLastError();
 }
 

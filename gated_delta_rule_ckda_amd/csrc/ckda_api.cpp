@@ -53,6 +53,8 @@ bool overlap(const Range& a, const Range& b) {
 
 bool misaligned(const void* p) { return ((uintptr_t)p & 15u) != 0; }
 
+constexpr int kFuseAll = CKDA_FUSE_GATES | CKDA_FUSE_NORM_K | CKDA_FUSE_NORM_Q;
+
 }  // namespace
 
 extern "C" {
@@ -66,6 +68,7 @@ const char* ckda_status_string(int status) {
     case CKDA_ERR_ALIAS: return "an output overlaps an input";
     case CKDA_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
     case CKDA_ERR_HIP: return "HIP runtime error";
+    case CKDA_ERR_FLAGS: return "unknown prologue flag bits";
   }
   return "unknown status";
 }
@@ -86,7 +89,10 @@ size_t ckda_chunk_fwd_workspace_size(int B, int H, int T, int dk, int dv, int ch
 
 static int chunk_fwd_impl(const void* q, const void* k, const void* v, const void* alpha, const void* beta,
                           const float* h0, void* o, float* hT, int B, int H, int T, int dk, int dv, int chunk,
-                          int dtype, void* workspace, size_t workspace_bytes, void* stream, void* const ev[3]) {
+                          int dtype, int flags, void* workspace, size_t workspace_bytes, void* stream,
+                          void* const ev[3]) {
+  if ((flags & ~kFuseAll) != 0)
+    return fail(CKDA_ERR_FLAGS, "ckda_chunk_fwd: flags 0x%x has bits outside CKDA_FUSE_* (0x%x)", flags, kFuseAll);
   if (B < 0 || H < 0 || T < 0)
     return fail(CKDA_ERR_DIM, "ckda_chunk_fwd: negative size (B=%d H=%d T=%d)", B, H, T);
   if (!supported_dtype(dtype))
@@ -142,7 +148,7 @@ static int chunk_fwd_impl(const void* q, const void* k, const void* v, const voi
   if (overlap(rw, ro) || overlap(rw, rh))
     return fail(CKDA_ERR_ALIAS, "ckda_chunk_fwd: workspace overlaps an output");
 
-  ckda::ChunkArgs a{q, k, v, alpha, beta, h0, o, hT, B, H, T, dk, dv, chunk, dtype, workspace,
+  ckda::ChunkArgs a{q, k, v, alpha, beta, h0, o, hT, B, H, T, dk, dv, chunk, dtype, flags, workspace,
                     (hipStream_t)stream, {(hipEvent_t)ev[0], (hipEvent_t)ev[1], (hipEvent_t)ev[2]}};
   hipError_t e = ckda::launch_chunk_fwd(a);
   if (e != hipSuccess)
@@ -155,8 +161,17 @@ int ckda_chunk_fwd(const void* q, const void* k, const void* v, const void* alph
                    int B, int H, int T, int dk, int dv, int chunk, int dtype,
                    void* workspace, size_t workspace_bytes, void* stream) {
   void* const none[3] = {nullptr, nullptr, nullptr};
-  return chunk_fwd_impl(q, k, v, alpha, beta, h0, o, hT, B, H, T, dk, dv, chunk, dtype, workspace, workspace_bytes,
-                        stream, none);
+  return chunk_fwd_impl(q, k, v, alpha, beta, h0, o, hT, B, H, T, dk, dv, chunk, dtype, 0, workspace,
+                        workspace_bytes, stream, none);
+}
+
+int ckda_chunk_fwd_ex(const void* q, const void* k, const void* v, const void* alpha,
+                      const void* beta, const float* h0, void* o, float* hT,
+                      int B, int H, int T, int dk, int dv, int chunk, int dtype, int flags,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  void* const none[3] = {nullptr, nullptr, nullptr};
+  return chunk_fwd_impl(q, k, v, alpha, beta, h0, o, hT, B, H, T, dk, dv, chunk, dtype, flags, workspace,
+                        workspace_bytes, stream, none);
 }
 
 int ckda_chunk_fwd_timed(const void* q, const void* k, const void* v, const void* alpha,
@@ -165,13 +180,14 @@ int ckda_chunk_fwd_timed(const void* q, const void* k, const void* v, const void
                          void* workspace, size_t workspace_bytes, void* stream,
                          void* ev_start, void* ev_mid, void* ev_end) {
   void* const ev[3] = {ev_start, ev_mid, ev_end};
-  return chunk_fwd_impl(q, k, v, alpha, beta, h0, o, hT, B, H, T, dk, dv, chunk, dtype, workspace, workspace_bytes,
-                        stream, ev);
+  return chunk_fwd_impl(q, k, v, alpha, beta, h0, o, hT, B, H, T, dk, dv, chunk, dtype, 0, workspace,
+                        workspace_bytes, stream, ev);
 }
 
-int ckda_decode_step(const void* q, const void* k, const void* v, const void* alpha,
-                     const void* beta, float* H_inout, void* o,
-                     int N, int H, int dk, int dv, int dtype, void* stream) {
+static int decode_impl(const void* q, const void* k, const void* v, const void* alpha, const void* beta,
+                       float* H_inout, void* o, int N, int H, int dk, int dv, int dtype, int flags, void* stream) {
+  if ((flags & ~kFuseAll) != 0)
+    return fail(CKDA_ERR_FLAGS, "ckda_decode_step: flags 0x%x has bits outside CKDA_FUSE_* (0x%x)", flags, kFuseAll);
   if (N < 0 || H < 0) return fail(CKDA_ERR_DIM, "ckda_decode_step: negative size (N=%d H=%d)", N, H);
   if (!supported_dtype(dtype))
     return fail(CKDA_ERR_UNSUPPORTED, "ckda_decode_step: dtype %d is not F32(0) or BF16(1)", dtype);
@@ -197,11 +213,23 @@ int ckda_decode_step(const void* q, const void* k, const void* v, const void* al
   }
   if (overlap(ro, rs)) return fail(CKDA_ERR_ALIAS, "ckda_decode_step: o overlaps H_inout");
 
-  ckda::DecodeArgs a{q, k, v, alpha, beta, H_inout, o, N, H, dk, dv, dtype, (hipStream_t)stream};
+  ckda::DecodeArgs a{q, k, v, alpha, beta, H_inout, o, N, H, dk, dv, dtype, flags, (hipStream_t)stream};
   hipError_t e = ckda::launch_decode(a);
   if (e != hipSuccess)
     return fail(CKDA_ERR_HIP, "ckda_decode_step: launch failed: %s", hipGetErrorString(e));
   return ok();
+}
+
+int ckda_decode_step(const void* q, const void* k, const void* v, const void* alpha,
+                     const void* beta, float* H_inout, void* o,
+                     int N, int H, int dk, int dv, int dtype, void* stream) {
+  return decode_impl(q, k, v, alpha, beta, H_inout, o, N, H, dk, dv, dtype, 0, stream);
+}
+
+int ckda_decode_step_ex(const void* q, const void* k, const void* v, const void* alpha,
+                        const void* beta, float* H_inout, void* o,
+                        int N, int H, int dk, int dv, int dtype, int flags, void* stream) {
+  return decode_impl(q, k, v, alpha, beta, H_inout, o, N, H, dk, dv, dtype, flags, stream);
 }
 
 }  // extern "C"

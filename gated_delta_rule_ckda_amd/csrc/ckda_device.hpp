@@ -49,6 +49,27 @@ template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) {
   return r;
 }
 
+// ---------------------------------------------------------------- prologue
+// The per-token prologue the fused entry points apply (ckda.h, CKDA_FUSE_*):
+// the practical gate parameterisation of the "Complex KDA" discussion slides
+// (frame "Backup: practical gates differ from exact theoretical endpoints")
+// and unit-norm keys and queries.
+constexpr int kFuseGates = 1, kFuseNormK = 2, kFuseNormQ = 4;   // as CKDA_FUSE_GATES, _NORM_K, _NORM_Q
+constexpr float kUnitGuard = 1e-6f;                 // x / sqrt(sum x^2 + guard)
+constexpr float kGateFloor = 0.006737946999085467f;  // e^-5: log|alpha| >= -5
+
+// alpha = sign(a) (eps + (1 - eps) |tanh(a / 2)|), sign(0) = +1.  With
+// m = e^-|a| - 1 (expm1f, exact for small |a|), |tanh(a / 2)| = -m / (2 + m).
+__device__ __forceinline__ float practical_gate(float a) {
+  const float m = expm1f(-fabsf(a));
+  const float r = -m / (2.f + m);
+  const float g = kGateFloor + (1.f - kGateFloor) * r;
+  return a >= 0.f ? g : -g;
+}
+
+// beta = 2 sigma(b) in [0, 2].
+__device__ __forceinline__ float practical_beta(float b) { return 2.f / (1.f + expf(-b)); }
+
 // Two floats -> packed bf16 pair (low = a).
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));

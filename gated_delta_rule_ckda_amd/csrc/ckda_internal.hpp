@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 
+#include "ckda.h"
+
 namespace ckda {
 
 struct DecodeArgs {
@@ -12,6 +14,7 @@ struct DecodeArgs {
   float* H_inout;
   void* o;
   int N, H, dk, dv, dtype;
+  int flags;   // CKDA_FUSE_* prologue steps (0: inputs used as given)
   hipStream_t stream;
 };
 
@@ -21,6 +24,7 @@ struct ChunkArgs {
   void* o;
   float* hT;
   int B, H, T, dk, dv, chunk, dtype;
+  int flags;   // CKDA_FUSE_* prologue steps (0: inputs used as given)
   void* workspace;
   hipStream_t stream;
   hipEvent_t ev[3];   // recorded before the Gram kernel, between the kernels, after the state kernel (if set)

@@ -15,18 +15,25 @@
 // loads are issued before anything else, and the updated state is written
 // with nontemporal (streaming) stores, which lifts the step from about 5.3 to
 // about 6.9 TB/s on MI355X.
+//
+// PRO instantiation: the per-token prologue (ckda.h, CKDA_FUSE_*) runs on the
+// loaded token before the step: gates and beta from their logits, keys and
+// queries scaled to unit norm (one wave reduces each vector).
 #include "ckda_device.hpp"
 #include "ckda_internal.hpp"
 
 namespace ckda {
 
+static_assert(kFuseGates == CKDA_FUSE_GATES && kFuseNormK == CKDA_FUSE_NORM_K && kFuseNormQ == CKDA_FUSE_NORM_Q,
+              "prologue flags");
+
 constexpr int kDecodeThreads = 256;
 
-template <typename T, int DK, int DV>
+template <typename T, int DK, int DV, bool PRO>
 __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ alpha, const T* __restrict__ beta, float* __restrict__ H,
-    T* __restrict__ o) {
+    T* __restrict__ o, int flags) {
   constexpr int TPR = DV / 4;                    // threads per state row (4 columns each)
   constexpr int RPI = kDecodeThreads / TPR;      // rows covered per pass
   constexpr int ITER = (DK + RPI - 1) / RPI;     // passes over the rows
@@ -34,7 +41,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
 
   __shared__ float s_a[DK], s_ak[DK], s_aq[DK], s_k[DK], s_q[DK];
   __shared__ f32x4 s_ps[RPI][TPR], s_pr[RPI][TPR];
-  __shared__ float s_kq;
+  __shared__ float s_kq, s_inv[2];
 
   const long long st = blockIdx.x;
   const int tid = threadIdx.x;
@@ -48,13 +55,40 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     const int row = rg + j * RPI;
     if (row < DK) h[j] = *reinterpret_cast<const f32x4*>(Hs + row * DV + 4 * cg);
   }
-  for (int i = tid; i < DK; i += kDecodeThreads) {
-    float a = to_f32(alpha[st * DK + i]), kk = to_f32(k[st * DK + i]), qq = to_f32(q[st * DK + i]);
-    s_a[i] = a;
-    s_k[i] = kk;
-    s_q[i] = qq;
-    s_ak[i] = a * kk;
-    s_aq[i] = a * qq;
+  if constexpr (PRO) {
+    for (int i = tid; i < DK; i += kDecodeThreads) {
+      const float a = to_f32(alpha[st * DK + i]);
+      s_a[i] = (flags & kFuseGates) ? practical_gate(a) : a;
+      s_k[i] = to_f32(k[st * DK + i]);
+      s_q[i] = to_f32(q[st * DK + i]);
+    }
+    __syncthreads();
+    const int w = tid >> 6;
+    if (w < 2) {   // wave 0: |k|, wave 1: |q|
+      const float* x = w == 0 ? s_k : s_q;
+      float ss = 0.f;
+      for (int i = tid & 63; i < DK; i += 64) ss += x[i] * x[i];
+      ss = wave_sum(ss);
+      const bool on = (flags & (w == 0 ? kFuseNormK : kFuseNormQ)) != 0;
+      if ((tid & 63) == 0) s_inv[w] = on ? 1.f / sqrtf(ss + kUnitGuard) : 1.f;
+    }
+    __syncthreads();
+    for (int i = tid; i < DK; i += kDecodeThreads) {
+      const float a = s_a[i], kk = s_k[i] * s_inv[0], qq = s_q[i] * s_inv[1];
+      s_k[i] = kk;
+      s_q[i] = qq;
+      s_ak[i] = a * kk;
+      s_aq[i] = a * qq;
+    }
+  } else {
+    for (int i = tid; i < DK; i += kDecodeThreads) {
+      float a = to_f32(alpha[st * DK + i]), kk = to_f32(k[st * DK + i]), qq = to_f32(q[st * DK + i]);
+      s_a[i] = a;
+      s_k[i] = kk;
+      s_q[i] = qq;
+      s_ak[i] = a * kk;
+      s_aq[i] = a * qq;
+    }
   }
   __syncthreads();
 
@@ -84,7 +118,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     sc += s_ps[g][cg];
     rc += s_pr[g][cg];
   }
-  const float b = to_f32(beta[st]);
+  float b = to_f32(beta[st]);
+  if (PRO && (flags & kFuseGates)) b = practical_beta(b);
   f32x4 vv;
 #pragma unroll
   for (int e = 0; e < 4; ++e) vv[e] = to_f32(v[st * DV + 4 * cg + e]);
@@ -111,9 +146,14 @@ template <typename T, int DK, int DV>
 static hipError_t launch_decode_t(const DecodeArgs& a) {
   const long long states = (long long)a.N * a.H;
   if (states == 0) return hipSuccess;
-  hipLaunchKernelGGL((decode_kernel<T, DK, DV>), dim3((unsigned)states), dim3(kDecodeThreads), 0,
-                     a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.alpha,
-                     (const T*)a.beta, a.H_inout, (T*)a.o);
+  if (a.flags != 0)
+    hipLaunchKernelGGL((decode_kernel<T, DK, DV, true>), dim3((unsigned)states), dim3(kDecodeThreads), 0,
+                       a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.alpha,
+                       (const T*)a.beta, a.H_inout, (T*)a.o, a.flags);
+  else
+    hipLaunchKernelGGL((decode_kernel<T, DK, DV, false>), dim3((unsigned)states), dim3(kDecodeThreads), 0,
+                       a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.alpha,
+                       (const T*)a.beta, a.H_inout, (T*)a.o, 0);
   return hipGetLastError();
 }
 

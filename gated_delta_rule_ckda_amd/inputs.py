@@ -17,6 +17,9 @@ beta in [0,2], "Complex KDA" Sec. 3):
 * decode               256 sequences x 32 heads, d128, 128 steps, bf16 inputs,
                        alpha~U[-1,1], beta~U[0,2], fp32 state ~N(0,0.1)
 
+The fused prologue's inputs (make_logit_inputs, decode_logit_inputs) are
+logits and unnormalised vectors of the same shapes.
+
 N(mu, s) means standard deviation s.  Draw order per workload: q, k, v, alpha,
 beta, h0, each as a full C-order float32 array from numpy's PCG64 stream
 seeded with the workload's seed.  k is L2-normalised per (b, h, t) in fp32
@@ -148,6 +151,48 @@ def make_inputs(w: Workload, repeated_keys: bool = False):
         raise ValueError(w.h0)
     return dict(q=_to(q, w.dtype), k=_to(k, w.dtype), v=_to(v, w.dtype),
                 alpha=_to(a, w.dtype), beta=_to(b, w.dtype), h0=h0)
+
+
+def make_logit_inputs(w: Workload, zero_rows: float = 0.0):
+    """Inputs for the fused prologue: dict(q, k, v, a, b, h0) of CPU tensors.
+
+    a, b are logits of alpha and beta (a ~ N(0, 3): gates from the e^-5 floor
+    to 1 with both signs; b ~ N(0, 1.5)); q and k are N(0, 1) and NOT
+    normalised.  zero_rows: fraction of (b, h, t) whose key and query rows are
+    all zero (exercises the zero-vector guard).  w.gates is ignored.
+    Draw order: q, k, v, a, b, zero mask, h0."""
+    rng = np.random.default_rng(w.seed)
+    B, H, T, dk, dv = w.B, w.H, w.T, w.dk, w.dv
+    q = rng.standard_normal((B, H, T, dk), dtype=np.float32)
+    k = rng.standard_normal((B, H, T, dk), dtype=np.float32)
+    v = rng.standard_normal((B, H, T, dv), dtype=np.float32)
+    a = np.float32(3.0) * rng.standard_normal((B, H, T, dk), dtype=np.float32)
+    bl = np.float32(1.5) * rng.standard_normal((B, H, T), dtype=np.float32)
+    zero = rng.uniform(size=(B, H, T, 1)) < zero_rows
+    q = np.where(zero, np.float32(0.0), q)
+    k = np.where(zero, np.float32(0.0), k)
+    if w.h0 == "normal":
+        h0 = torch.from_numpy(np.float32(0.1) * rng.standard_normal((B, H, dk, dv), dtype=np.float32))
+    elif w.h0 == "zero":
+        h0 = torch.zeros((B, H, dk, dv), dtype=torch.float32)
+    else:
+        h0 = None
+    return dict(q=_to(q, w.dtype), k=_to(k, w.dtype), v=_to(v, w.dtype),
+                alpha=_to(a, w.dtype), beta=_to(bl, w.dtype), h0=h0)
+
+
+def decode_logit_inputs(step: int, d: DecodeWorkload = DECODE, N=None, H=None):
+    """Decode-step inputs for the fused prologue (laws of make_logit_inputs)."""
+    N = d.N if N is None else N
+    H = d.H if H is None else H
+    rng = np.random.default_rng(d.step_seed + step)
+    q = rng.standard_normal((N, H, d.dk), dtype=np.float32)
+    k = rng.standard_normal((N, H, d.dk), dtype=np.float32)
+    v = rng.standard_normal((N, H, d.dv), dtype=np.float32)
+    a = np.float32(3.0) * rng.standard_normal((N, H, d.dk), dtype=np.float32)
+    bl = np.float32(1.5) * rng.standard_normal((N, H), dtype=np.float32)
+    return dict(q=_to(q, d.dtype), k=_to(k, d.dtype), v=_to(v, d.dtype),
+                alpha=_to(a, d.dtype), beta=_to(bl, d.dtype))
 
 
 def decode_state(d: DecodeWorkload = DECODE, N=None, H=None):

@@ -24,12 +24,13 @@
  * - Tensors are contiguous, C order, base addresses 16-byte aligned.
  * - `dtype` (ckda_dtype_t) is the element type of q, k, v, alpha, beta and o.
  *   States (h0, hT, H_inout) are always fp32.
- * - q is not scaled and k is not normalised: the caller supplies ||k_t|| = 1.
- *   alpha and beta are used as given (no clamping of range violations).  The
- *   one exception is internal to the chunked forward's intra-chunk Gram
- *   matrices, where a gate magnitude below 2^-31 counts as 2^-31 (sign kept):
- *   that changes a decay only where its exact value is below 2^-31 already;
- *   see ckda_chunk_fwd.
+ * - q is not scaled and k is not normalised: the caller supplies ||k_t|| = 1
+ *   (the *_ex entry points can normalise both and form the gates from
+ *   logits, see CKDA_FUSE_*).  alpha and beta are used as given (no clamping
+ *   of range violations).  The one exception is internal to the chunked
+ *   forward's intra-chunk Gram matrices, where a gate magnitude below 2^-31
+ *   counts as 2^-31 (sign kept): that changes a decay only where its exact
+ *   value is below 2^-31 already; see ckda_chunk_fwd.
  * - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
  *   and the call returns without waiting.  The return value reports argument
  *   errors (detected before anything is launched) and launch errors; faults
@@ -61,8 +62,33 @@ typedef enum {
   CKDA_ERR_UNSUPPORTED = 3, /* valid but not supported (dtype, d_k, d_v, chunk) */
   CKDA_ERR_ALIAS = 4,       /* an output overlaps an input it may not overlap */
   CKDA_ERR_WORKSPACE = 5,   /* workspace missing, too small or misaligned */
-  CKDA_ERR_HIP = 6          /* the HIP runtime reported an error at launch */
+  CKDA_ERR_HIP = 6,         /* the HIP runtime reported an error at launch */
+  CKDA_ERR_FLAGS = 7        /* prologue flags hold bits outside CKDA_FUSE_* */
 } ckda_status_t;
+
+/* Per-token prologue steps of the *_ex entry points (bitwise OR; 0 = none,
+ * the inputs are used as given, exactly as by the plain entry points).  They
+ * follow the practical parameterisation of the "Complex KDA" discussion
+ * slides (frame "Backup: practical gates differ from exact theoretical
+ * endpoints") and the unit-norm keys the recurrence assumes (frame "Absorb
+ * cumulative signs into keys and queries"), and are computed in fp32 inside
+ * the kernels, with no extra pass over memory:
+ *
+ *   CKDA_FUSE_GATES   alpha and beta hold logits a, b:
+ *                       alpha = s (eps + (1 - eps) |tanh(a / 2)|),  eps = e^-5,
+ *                       s = +1 for a >= 0 (a = -0 included), else -1,
+ *                       beta  = 2 sigmoid(b),
+ *                     so |alpha| in [e^-5, 1] (fp32), sign free, beta in [0, 2].
+ *   CKDA_FUSE_NORM_K  each key row is scaled to unit norm: k / sqrt(|k|^2 + 1e-6)
+ *                     (the guard, which the pages do not give, maps a zero key
+ *                     to zero and moves a unit key by 5e-7).
+ *   CKDA_FUSE_NORM_Q  the same for each query row.
+ *
+ * In the chunked forward with CKDA_FUSE_GATES the computed gates stay fp32
+ * (they are not rounded to dtype) before they enter the chunk products. */
+#define CKDA_FUSE_GATES 1
+#define CKDA_FUSE_NORM_K 2
+#define CKDA_FUSE_NORM_Q 4
 
 /* Bytes of device workspace ckda_chunk_fwd needs for these sizes, or 0 when
  * the sizes are invalid or unsupported (ckda_chunk_fwd then reports why).
@@ -120,6 +146,17 @@ int ckda_chunk_fwd_timed(const void* q, const void* k, const void* v, const void
                          void* workspace, size_t workspace_bytes, void* stream,
                          void* ev_start, void* ev_mid, void* ev_end);
 
+/* ckda_chunk_fwd with the per-token prologue `flags` (CKDA_FUSE_*) applied
+ * to the inputs first: alpha and beta may be logits, k and q are normalised
+ * per token.  The prologue's results are not written anywhere.  Same
+ * arguments, layouts, aliasing rules and workspace as ckda_chunk_fwd; flags
+ * = 0 gives ckda_chunk_fwd's results exactly.  Returns CKDA_ERR_FLAGS for
+ * bits outside CKDA_FUSE_*. */
+int ckda_chunk_fwd_ex(const void* q, const void* k, const void* v, const void* alpha,
+                      const void* beta, const float* h0, void* o, float* hT,
+                      int B, int H, int T, int dk, int dv, int chunk, int dtype, int flags,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
 /* One recurrent decode step for N sequences x H heads, state in place.
  *
  *   q, k, alpha : [N, H, dk]     dtype
@@ -143,6 +180,14 @@ int ckda_chunk_fwd_timed(const void* q, const void* k, const void* v, const void
 int ckda_decode_step(const void* q, const void* k, const void* v, const void* alpha,
                      const void* beta, float* H_inout, void* o,
                      int N, int H, int dk, int dv, int dtype, void* stream);
+
+/* ckda_decode_step with the per-token prologue `flags` (CKDA_FUSE_*) applied
+ * to the token first (fp32 throughout).  Same arguments and rules as
+ * ckda_decode_step; flags = 0 gives its results exactly.  Returns
+ * CKDA_ERR_FLAGS for bits outside CKDA_FUSE_*. */
+int ckda_decode_step_ex(const void* q, const void* k, const void* v, const void* alpha,
+                        const void* beta, float* H_inout, void* o,
+                        int N, int H, int dk, int dv, int dtype, int flags, void* stream);
 
 /* Static description of a status code. */
 const char* ckda_status_string(int status);

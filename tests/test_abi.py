@@ -33,8 +33,8 @@ def test_library_exports_every_declared_function():
 
 def test_status_strings():
     L = ck.lib()
-    for s in range(7):
-        assert L.ckda_status_string(s)
+    for s in range(8):
+        assert L.ckda_status_string(s) != b"unknown status"
     assert L.ckda_status_string(99) == b"unknown status"
 
 
@@ -66,8 +66,11 @@ def call_fwd(**kw):
              h0=BASE + 5 * MB, o=BASE + 6 * MB, hT=BASE + 7 * MB, ws=BASE + 8 * MB)
     p.update({k: v for k, v in kw.items() if k in p})
     wsb = kw.get("wsb", 64 * MB)
-    rc = L.ckda_chunk_fwd(p["q"], p["k"], p["v"], p["alpha"], p["beta"], p["h0"], p["o"], p["hT"],
-                          B, H, T, dk, dv, chunk, dtype, p["ws"], wsb, None)
+    args = (p["q"], p["k"], p["v"], p["alpha"], p["beta"], p["h0"], p["o"], p["hT"], B, H, T, dk, dv, chunk, dtype)
+    if "flags" in kw:
+        rc = L.ckda_chunk_fwd_ex(*args, kw["flags"], p["ws"], wsb, None)
+    else:
+        rc = L.ckda_chunk_fwd(*args, p["ws"], wsb, None)
     return rc, L.ckda_last_error().decode()
 
 
@@ -77,8 +80,11 @@ def call_dec(**kw):
     p = dict(q=BASE, k=BASE + MB, v=BASE + 2 * MB, alpha=BASE + 3 * MB, beta=BASE + 4 * MB,
              S=BASE + 5 * MB, o=BASE + 6 * MB)
     p.update({k: v for k, v in kw.items() if k in p})
-    rc = L.ckda_decode_step(p["q"], p["k"], p["v"], p["alpha"], p["beta"], p["S"], p["o"], N, H, dk, dv, dtype,
-                            None)
+    args = (p["q"], p["k"], p["v"], p["alpha"], p["beta"], p["S"], p["o"], N, H, dk, dv, dtype)
+    if "flags" in kw:
+        rc = L.ckda_decode_step_ex(*args, kw["flags"], None)
+    else:
+        rc = L.ckda_decode_step(*args, None)
     return rc, L.ckda_last_error().decode()
 
 
@@ -98,6 +104,37 @@ def test_chunk_fwd_rejects(kw, status):
     rc, msg = call_fwd(**kw)
     assert rc == status, (rc, msg)
     assert msg.startswith("ckda_chunk_fwd")
+
+
+@pytest.mark.parametrize("flags", [8, 16, -1, 1 << 30])
+def test_fused_entry_points_reject_unknown_flags(flags):
+    rc, msg = call_fwd(flags=flags)
+    assert rc == 7 and msg.startswith("ckda_chunk_fwd"), (rc, msg)
+    rc, msg = call_dec(flags=flags)
+    assert rc == 7 and msg.startswith("ckda_decode_step"), (rc, msg)
+
+
+@pytest.mark.parametrize("flags", [0, 1, 2, 3, 4, 7])
+def test_fused_entry_points_check_arguments_like_the_plain_ones(flags):
+    # valid flags reach the same argument checks (these all fail before a launch)
+    assert call_fwd(flags=flags, q=None)[0] == 1
+    assert call_fwd(flags=flags, dk=48)[0] == 3
+    assert call_fwd(flags=flags, o=BASE + 2 * MB + 64)[0] == 4
+    assert call_fwd(flags=flags, wsb=1024)[0] == 5
+    assert call_fwd(flags=flags, B=0)[0] == 0
+    assert call_dec(flags=flags, S=None)[0] == 1
+    assert call_dec(flags=flags, o=BASE + 5 * MB)[0] == 4
+    assert call_dec(flags=flags, N=0, q=None)[0] == 0
+
+
+def test_prologue_flag_values_agree():
+    text = open(HEADER).read()
+    defs = dict(re.findall(r"#define (CKDA_FUSE_\w+) (\d+)", text))
+    assert {k: int(v) for k, v in defs.items()} == {"CKDA_FUSE_GATES": ck.FUSE_GATES,
+                                                     "CKDA_FUSE_NORM_K": ck.FUSE_NORM_K,
+                                                     "CKDA_FUSE_NORM_Q": ck.FUSE_NORM_Q}
+    import oracle
+    assert (oracle.GATES, oracle.NORM_K, oracle.NORM_Q) == (ck.FUSE_GATES, ck.FUSE_NORM_K, ck.FUSE_NORM_Q)
 
 
 def test_chunk_fwd_empty_problems_are_noops():
