@@ -191,27 +191,13 @@ __global__ __launch_bounds__((GramCfg<T, DK, C>::NTH)) void chunk_gram_kernel(
   const int colofs = padded_col_offset<T>(c0);
 
   // ---- this thread's rows: signed gates (floored), keys, queries
-  // gate pair as stored, or (prologue) as computed from its logits
-  auto gate_pair = [&](raw x) __attribute__((always_inline)) {
-    if constexpr (PRO) {
-      float a0 = PR::lo(x), a1 = PR::hi(x);
-      if (flags & kFuseGates) {
-        a0 = practical_gate(a0);
-        a1 = practical_gate(a1);
-      }
-      return graw{a0, a1};
-    } else {
-      return x;
-    }
-  };
-  graw ra[16];
-  raw rk[16], rq[16];
+  raw rl[16], rk[16], rq[16];   // gates (or, with the prologue, their logits) as loaded
   if (act) {
     const size_t base = (size_t)(row0 + 16 * b) * DK + c0;
     if (cv == C) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        ra[i] = gate_pair(PR::load(alpha + base + (size_t)i * DK));
+        rl[i] = PR::load(alpha + base + (size_t)i * DK);
         rk[i] = PR::load(k + base + (size_t)i * DK);
         rq[i] = PR::load(q + base + (size_t)i * DK);
       }
@@ -221,47 +207,87 @@ __global__ __launch_bounds__((GramCfg<T, DK, C>::NTH)) void chunk_gram_kernel(
       for (int i = 0; i < 16; ++i) {
         const int t = 16 * b + i;
         const size_t off = base + (size_t)(min(t, cv - 1) - 16 * b) * DK;
-        const raw kk = PR::load(k + off), qq = PR::load(q + off);
-        const graw a = gate_pair(PR::load(alpha + off));
-        ra[i] = GR::ones();
+        const raw a = PR::load(alpha + off), kk = PR::load(k + off), qq = PR::load(q + off);
+        rl[i] = PR::ones();
         rk[i] = PR::zeros();
         rq[i] = PR::zeros();
         if (t < cv) {
-          ra[i] = a;
+          rl[i] = a;
           rk[i] = kk;
           rq[i] = qq;
         }
       }
     }
   }
+  // Prologue gates: transformed after all loads are in flight, under one
+  // branch (a branch per row would split the loads into separate blocks,
+  // each waiting for its own).  Ragged rows stay identity steps.
+  graw ra[16];
+  if constexpr (PRO) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) ra[i] = graw{PR::lo(rl[i]), PR::hi(rl[i])};
+    if (flags & kFuseGates) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const bool keep = 16 * b + i >= cv;
+        ra[i] = graw{keep ? 1.f : practical_gate(ra[i][0]), keep ? 1.f : practical_gate(ra[i][1])};
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) ra[i] = rl[i];
+  }
 
   // keys and queries widened to fp32 once: every operand below multiplies
   // them (the gates stay packed: widened as well they would cost the third
   // workgroup per CU its registers)
+  // (In the bf16 prologue instantiation the queries stay packed and are
+  // widened at each use, behind an opaque copy so that the widened values
+  // are not kept: the fp32 gates take those registers, which keeps the third
+  // workgroup per CU.)
+  constexpr bool QPACK = PRO && std::is_same<T, bf16_t>::value;
   float kl[16], kh[16], ql[16], qh[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     kl[i] = PR::lo(rk[i]);
     kh[i] = PR::hi(rk[i]);
-    ql[i] = PR::lo(rq[i]);
-    qh[i] = PR::hi(rq[i]);
+    if constexpr (!QPACK) {
+      ql[i] = PR::lo(rq[i]);
+      qh[i] = PR::hi(rq[i]);
+    }
   }
+  auto qraw = [&](int i) __attribute__((always_inline)) {
+    raw t = rq[i];
+    if constexpr (QPACK) pin(t);
+    return t;
+  };
+#define QL(i) (QPACK ? PR::lo(qraw(i)) : ql[i])
+#define QH(i) (QPACK ? PR::hi(qraw(i)) : qh[i])
   if constexpr (PRO) {
-    // unit rows: the NU lanes holding one row (NU-aligned within the wave)
-    // sum their squares by butterfly shuffles
+    // unit rows: the NU lanes holding one row (an aligned lane group) sum
+    // their squares; v_rsq_f32 gives the inverse norm
     auto unit_rows = [&](float* lo, float* hi) __attribute__((always_inline)) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        float ss = lo[i] * lo[i] + hi[i] * hi[i];
-#pragma unroll
-        for (int off = NU / 2; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
-        const float inv = 1.f / sqrtf(ss + kUnitGuard);
+        const float ss = group_sum<NU>(__builtin_fmaf(lo[i], lo[i], hi[i] * hi[i]));
+        const float inv = __builtin_amdgcn_rsqf(ss + kUnitGuard);
         lo[i] *= inv;
         hi[i] *= inv;
       }
     };
     if (flags & kFuseNormK) unit_rows(kl, kh);
-    if (flags & kFuseNormQ) unit_rows(ql, qh);
+    if (flags & kFuseNormQ) {
+      if constexpr (QPACK) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float l = PR::lo(rq[i]), h = PR::hi(rq[i]);
+          const float inv = __builtin_amdgcn_rsqf(group_sum<NU>(__builtin_fmaf(l, l, h * h)) + kUnitGuard);
+          rq[i] = pack_bf16x2(l * inv, h * inv);
+        }
+      } else {
+        unit_rows(ql, qh);
+      }
+    }
   }
 
   // K blocks only partly covered (bf16: channels when DK = 16, positions of
@@ -323,7 +349,7 @@ __global__ __launch_bounds__((GramCfg<T, DK, C>::NTH)) void chunk_gram_kernel(
         g0 *= LO(ra[i]);
         g1 *= HI(ra[i]);
         put(b, i, -kl[i] * g0, -kh[i] * g1);
-        put(RT + b, i, ql[i] * g0, qh[i] * g1);
+        put(RT + b, i, QL(i) * g0, QH(i) * g1);
       }
       if (b == RT - 1) *reinterpret_cast<float2*>(rec + P::D_OFF + c0 * 4) = make_float2(g0, g1);
       // KR^T: rows = channels c0, c0 + 1; K = positions, four at a time
@@ -395,7 +421,7 @@ __global__ __launch_bounds__((GramCfg<T, DK, C>::NTH)) void chunk_gram_kernel(
           p1 *= HI(ra[i]);
           const float b0 = __builtin_amdgcn_rcpf(p0), b1 = __builtin_amdgcn_rcpf(p1);
           put(3 * b, i, kl[i] * p0, kh[i] * p1);
-          put(3 * b + 1, i, ql[i] * p0, qh[i] * p1);
+          put(3 * b + 1, i, QL(i) * p0, QH(i) * p1);
           put(3 * b + 2, i, kl[i] * b0, kh[i] * b1);
         }
         float s0 = kQuadScaleInv, s1 = kQuadScaleInv;
@@ -403,7 +429,7 @@ __global__ __launch_bounds__((GramCfg<T, DK, C>::NTH)) void chunk_gram_kernel(
         for (int i = q0 + 3; i >= q0; --i) {      // bm = suffix up to the midpoint / scale, am = 1 / bm
           const float a0 = __builtin_amdgcn_rcpf(s0), a1 = __builtin_amdgcn_rcpf(s1);
           put(3 * b, i, kl[i] * a0, kh[i] * a1);
-          put(3 * b + 1, i, ql[i] * a0, qh[i] * a1);
+          put(3 * b + 1, i, QL(i) * a0, QH(i) * a1);
           put(3 * b + 2, i, kl[i] * s0, kh[i] * s1);
           s0 *= LO(ra[i]);
           s1 *= HI(ra[i]);
@@ -441,7 +467,7 @@ __global__ __launch_bounds__((GramCfg<T, DK, C>::NTH)) void chunk_gram_kernel(
         x0 *= LO(ra[i]);
         x1 *= HI(ra[i]);
         put(2 * b, i, kl[i] * x0, kh[i] * x1);
-        put(2 * b + 1, i, ql[i] * x0, qh[i] * x1);
+        put(2 * b + 1, i, QL(i) * x0, QH(i) * x1);
       }
       float y0 = 1.f, y1 = 1.f;
 #pragma unroll
@@ -479,11 +505,11 @@ __global__ __launch_bounds__((GramCfg<T, DK, C>::NTH)) void chunk_gram_kernel(
           x0 *= LO(ra[i]);
           x1 *= HI(ra[i]);
           put(P::pk(b), i, kl[i] * x0, kh[i] * x1);
-          put(P::pq(b), i, ql[i] * x0, qh[i] * x1);
+          put(P::pq(b), i, QL(i) * x0, QH(i) * x1);
           if (RT == 4 && b == 3) {
             const float z0 = x0 * m0, z1 = x1 * m1;
             put(P::X32K, i, kl[i] * z0, kh[i] * z1);
-            put(P::X32Q, i, ql[i] * z0, qh[i] * z1);
+            put(P::X32Q, i, QL(i) * z0, QH(i) * z1);
           }
         }
       }
@@ -513,6 +539,8 @@ __global__ __launch_bounds__((GramCfg<T, DK, C>::NTH)) void chunk_gram_kernel(
   }
 #undef LO
 #undef HI
+#undef QL
+#undef QH
 
   // ---- A (rows scaled by beta, strictly lower) and M (lower incl.) to LDS, fp32
   float* As = reinterpret_cast<float*>(area);

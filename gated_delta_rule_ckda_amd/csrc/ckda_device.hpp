@@ -58,12 +58,26 @@ constexpr int kFuseGates = 1, kFuseNormK = 2, kFuseNormQ = 4;   // as CKDA_FUSE_
 constexpr float kUnitGuard = 1e-6f;                 // x / sqrt(sum x^2 + guard)
 constexpr float kGateFloor = 0.006737946999085467f;  // e^-5: log|alpha| >= -5
 
-// alpha = sign(a) (eps + (1 - eps) |tanh(a / 2)|), sign(0) = +1.  With
-// m = e^-|a| - 1 (expm1f, exact for small |a|), |tanh(a / 2)| = -m / (2 + m).
+// alpha = sign(a) (eps + (1 - eps) |tanh(a / 2)|), sign(0) = +1, in a few
+// VALU operations.  With x = |a| / 2:
+//   x < 5/16: the Maclaurin series of tanh, x - x^3/3 + 2x^5/15 - 17x^7/315
+//             + 62x^9/2835 - 1382x^11/155925 (next term below 2^-27 x);
+//   else:     (1 - e) / (1 + e), e = e^-2x by v_exp_f32 and v_rcp_f32
+//             (1 - e > 0.46, no cancellation).
+// Both branches are evaluated and selected (no divergence); a few ulp.
 __device__ __forceinline__ float practical_gate(float a) {
-  const float m = expm1f(-fabsf(a));
-  const float r = -m / (2.f + m);
-  const float g = kGateFloor + (1.f - kGateFloor) * r;
+  const float x = 0.5f * fabsf(a);
+  const float z = x * x;
+  float p = -1382.f / 155925.f;
+  p = __builtin_fmaf(p, z, 62.f / 2835.f);
+  p = __builtin_fmaf(p, z, -17.f / 315.f);
+  p = __builtin_fmaf(p, z, 2.f / 15.f);
+  p = __builtin_fmaf(p, z, -1.f / 3.f);
+  const float small = __builtin_fmaf(p * z, x, x);
+  const float e = __builtin_amdgcn_exp2f(-2.8853900817779268f * x);   // 2 log2(e) = 2.88539...
+  const float large = (1.f - e) * __builtin_amdgcn_rcpf(1.f + e);
+  const float r = x < 0.3125f ? small : large;
+  const float g = __builtin_fmaf(1.f - kGateFloor, r, kGateFloor);
   return a >= 0.f ? g : -g;
 }
 
@@ -242,6 +256,37 @@ template <> __device__ __forceinline__ void store4<bf16_t>(__amdgpu_buffer_rsrc_
 }
 
 // Wave-wide sum (wave64) via cross-lane shuffles.
+// Sum over aligned groups of N lanes (N = 2 .. 64), every lane of a group
+// receiving its group's sum; all lanes of the wave must be active.  Within a
+// 16-lane row the steps are DPP moves (swap neighbours, swap pairs, mirror
+// each half row, mirror the row: after the sums so far, each mirror partner
+// lies in the other half); across rows, DPP row broadcasts accumulate the
+// group's sum in its last lane, which v_readlane hands to the group.
+template <int CTRL> __device__ __forceinline__ float dpp_add(float x) {
+  return x + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
+}
+template <int N> __device__ __forceinline__ float group_sum(float x) {
+  static_assert(N >= 2 && N <= 64 && (N & (N - 1)) == 0, "group size");
+  x = dpp_add<0xB1>(x);                            // quad_perm [1,0,3,2]
+  if constexpr (N >= 4) x = dpp_add<0x4E>(x);      // quad_perm [2,3,0,1]
+  if constexpr (N >= 8) x = dpp_add<0x141>(x);     // row_half_mirror
+  if constexpr (N >= 16) x = dpp_add<0x140>(x);    // row_mirror
+  if constexpr (N >= 32) {
+    // row_bcast:15 into rows 1 and 3: they now hold the sums of rows 0-1, 2-3
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x142, 0xA, 0xF, false));
+    if constexpr (N == 32) {
+      const float lo = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 31));
+      const float hi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
+      x = (threadIdx.x & 32) ? hi : lo;
+    } else {
+      // row_bcast:31 into rows 2 and 3: row 3 now holds the wave's sum
+      x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x143, 0xC, 0xF, false));
+      x = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
+    }
+  }
+  return x;
+}
+
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
