@@ -6,8 +6,9 @@ d_k = d_v = 128, chunk 64, full CKDA gate ranges, h0 ~ N(0, 0.1)): gate sign
 and magnitude split, Gram matrices, triangular solve, state pass and output,
 plus the final state.  The decode step (256 sequences x 32 heads, d128, fp32
 state updated in place) is timed in the same run and reported under "decode",
-and both again with the per-token prologue fused (gates from logits, unit-norm
-keys) under "fused_prologue".
+both again with the per-token prologue fused (gates from logits, unit-norm
+keys) under "fused_prologue", and the state-reduced workload (B2 H32 T32768,
+d_k 64 kept of 128 channels by an in-kernel gather) under "channel_gather".
 
 Prints ONE JSON line.  `value` is tokens/s of the forward (a token is one
 (batch, position) across all heads), inputs resident in HBM: tokens per step
@@ -233,6 +234,41 @@ def main():
     torch.cuda.synchronize()
     fdec_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in dev_ev]))
 
+    # ---- state-reduced workload (B2 H32 T32768, d_k 64 kept of 128 channels,
+    # d_v 128) with the channel gather inside the kernels, beside the plain
+    # forward on inputs gathered beforehand
+    gw, dk_in = gen.WORKLOADS["ckda_long_dk64"], 128
+    log(f"[bench] channel gather {gw} from {dk_in} channels")
+    gidx = gen.retained_channels(gw.H, dk_in, gw.dk, 4242)
+    gin = gen.make_gather_inputs(gw, dk_in, gidx)
+    gd = {k: (None if v is None else v.to(dev)) for k, v in gin.items()}
+    gidx_d = gidx.to(dev)
+    pre = {n: torch.stack([gd[n][:, h].index_select(-1, gidx_d[h].long()) for h in range(gw.H)], 1).contiguous()
+           for n in ("q", "k", "alpha")}
+    gws = torch.empty(ck.workspace_size(gw.B, gw.H, gw.T, gw.dk, gw.dv, gw.chunk, ck.DTYPE_BF16), dtype=torch.uint8,
+                      device=dev)
+    go = torch.empty((gw.B, gw.H, gw.T, gw.dv), dtype=torch.bfloat16, device=dev)
+    ghT = torch.empty((gw.B, gw.H, gw.dk, gw.dv), dtype=torch.float32, device=dev)
+
+    def timed(fn, n):
+        for _ in range(max(1, a.warmup)):
+            fn()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for e0, e1 in evs:
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+
+    gsteps = max(3, a.steps // 3)
+    gather_ms = timed(lambda: ck.chunk_fwd(gd["q"], gd["k"], gd["v"], gd["alpha"], gd["beta"], gd["h0"],
+                                           chunk=gw.chunk, workspace=gws, o=go, hT=ghT, idx=gidx_d), gsteps)
+    pregathered_ms = timed(lambda: ck.chunk_fwd(pre["q"], pre["k"], gd["v"], pre["alpha"], gd["beta"], gd["h0"],
+                                                chunk=gw.chunk, workspace=gws, o=go, hT=ghT), gsteps)
+    del pre, gd, gws, go
+
     # ---- reference device copy of the decode state's size (practical ceiling)
     src = torch.empty(dec.N * dec.H * dec.dk * dec.dv, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
@@ -290,6 +326,13 @@ def main():
             "total_GB_s": round(dec_gbs_total, 1),
             "frac_of_hbm_peak": round(dec_gbs_total / HBM_PEAK_GBS, 4),
             "device_copy_GB_s": round(copy_gbs, 1),
+        },
+        "channel_gather": {
+            "workload": f"{gw.name} (d_k {gw.dk} kept of {dk_in})",
+            "forward_call_ms_mean": round(gather_ms, 4),
+            "forward_tokens_per_s": round(gw.B * gw.T / (gather_ms * 1e-3), 1),
+            "pregathered_plain_call_ms_mean": round(pregathered_ms, 4),
+            "gather_overhead_vs_pregathered": round(gather_ms / pregathered_ms - 1.0, 4),
         },
         "fused_prologue": {
             "flags": "CKDA_FUSE_GATES | CKDA_FUSE_NORM_K",

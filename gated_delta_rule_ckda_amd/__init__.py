@@ -26,8 +26,8 @@ STATUS = {0: "CKDA_OK", 1: "CKDA_ERR_NULL", 2: "CKDA_ERR_DIM", 3: "CKDA_ERR_UNSU
           4: "CKDA_ERR_ALIAS", 5: "CKDA_ERR_WORKSPACE", 6: "CKDA_ERR_HIP", 7: "CKDA_ERR_FLAGS"}
 FUSE_GATES, FUSE_NORM_K, FUSE_NORM_Q = 1, 2, 4       # CKDA_FUSE_*
 EXPORTS = ("ckda_chunk_fwd_workspace_size", "ckda_chunk_fwd", "ckda_chunk_fwd_timed", "ckda_chunk_fwd_ex",
-           "ckda_decode_step", "ckda_decode_step_ex", "ckda_status_string", "ckda_last_error",
-           "ckda_abi_version")
+           "ckda_chunk_fwd_gather", "ckda_decode_step", "ckda_decode_step_ex", "ckda_decode_step_gather",
+           "ckda_status_string", "ckda_last_error", "ckda_abi_version")
 
 _lib = None
 
@@ -55,6 +55,10 @@ def lib() -> ctypes.CDLL:
         L.ckda_chunk_fwd_timed.restype = i
         L.ckda_chunk_fwd_ex.argtypes = [vp] * 8 + [i] * 8 + [vp, sz, vp]
         L.ckda_chunk_fwd_ex.restype = i
+        L.ckda_chunk_fwd_gather.argtypes = [vp] * 8 + [i] * 4 + [vp] + [i] * 5 + [vp, sz, vp]
+        L.ckda_chunk_fwd_gather.restype = i
+        L.ckda_decode_step_gather.argtypes = [vp] * 7 + [i] * 3 + [vp] + [i] * 4 + [vp]
+        L.ckda_decode_step_gather.restype = i
         L.ckda_decode_step.argtypes = [vp] * 7 + [i] * 5 + [vp]
         L.ckda_decode_step.restype = i
         L.ckda_decode_step_ex.argtypes = [vp] * 7 + [i] * 6 + [vp]
@@ -107,7 +111,7 @@ def workspace_size(B, H, T, dk, dv, chunk, dtype) -> int:
 
 
 def chunk_fwd(q, k, v, alpha, beta, h0=None, chunk=64, workspace=None, o=None, hT=None,
-              want_state=True, stream=None, events=None, fuse=0):
+              want_state=True, stream=None, events=None, fuse=0, idx=None):
     """Chunkwise forward.  q, k, alpha [B,H,T,dk]; v [B,H,T,dv]; beta [B,H,T];
     h0 [B,H,dk,dv] fp32 or None.  Returns (o [B,H,T,dv], hT [B,H,dk,dv] fp32 or None).
 
@@ -117,8 +121,16 @@ def chunk_fwd(q, k, v, alpha, beta, h0=None, chunk=64, workspace=None, o=None, h
     recorded before the Gram kernel, between the kernels and after the
     state-pass kernel (ckda_chunk_fwd_timed).  `fuse` (FUSE_* bits) applies
     the per-token prologue (ckda_chunk_fwd_ex); it cannot be combined with
-    `events`."""
+    `events`.  `idx` ([H, dk] int32 GPU tensor) gathers each head's retained
+    key channels from full-width q, k, alpha rows [B,H,T,dk_in] inside the
+    kernels (ckda_chunk_fwd_gather); states then have dk rows."""
     B, H, T, dk = q.shape
+    dk_in = dk
+    if idx is not None:
+        _require(dict(idx=idx), torch.int32)
+        if idx.dim() != 2 or idx.shape[0] != H:
+            raise ValueError(f"idx must be [H, dk], got {tuple(idx.shape)}")
+        dk = idx.shape[1]
     dv = v.shape[-1]
     _require(dict(q=q, k=k, v=v, alpha=alpha, beta=beta), q.dtype)
     code = _dtype_code(q)
@@ -136,7 +148,11 @@ def chunk_fwd(q, k, v, alpha, beta, h0=None, chunk=64, workspace=None, o=None, h
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(h0), _ptr(o), _ptr(hT),
             B, H, T, dk, dv, chunk, code, _ptr(workspace), workspace.numel() * workspace.element_size(),
             _stream(stream))
-    if fuse:
+    if idx is not None:
+        if events is not None:
+            raise ValueError("events are recorded by the plain forward only")
+        _check(lib().ckda_chunk_fwd_gather(*args[:11], dk_in, _ptr(idx), *args[11:15], int(fuse), *args[15:]))
+    elif fuse:
         if events is not None:
             raise ValueError("events are recorded by the plain forward only (fuse=0)")
         args = args[:15] + (int(fuse),) + args[15:]
@@ -149,11 +165,19 @@ def chunk_fwd(q, k, v, alpha, beta, h0=None, chunk=64, workspace=None, o=None, h
     return o, hT
 
 
-def decode_step(q, k, v, alpha, beta, H, o=None, stream=None, fuse=0):
+def decode_step(q, k, v, alpha, beta, H, o=None, stream=None, fuse=0, idx=None):
     """One decode step.  q, k, alpha [N,Hh,dk]; v [N,Hh,dv]; beta [N,Hh];
     H [N,Hh,dk,dv] fp32 updated in place.  Returns o [N,Hh,dv].  `fuse`
-    (FUSE_* bits) applies the per-token prologue first (ckda_decode_step_ex)."""
+    (FUSE_* bits) applies the per-token prologue first (ckda_decode_step_ex).
+    `idx` ([Hh, dk] int32) gathers retained key channels from rows of dk_in
+    (ckda_decode_step_gather)."""
     N, Hh, dk = q.shape
+    dk_in = dk
+    if idx is not None:
+        _require(dict(idx=idx), torch.int32)
+        if idx.dim() != 2 or idx.shape[0] != Hh:
+            raise ValueError(f"idx must be [H, dk], got {tuple(idx.shape)}")
+        dk = idx.shape[1]
     dv = v.shape[-1]
     _require(dict(q=q, k=k, v=v, alpha=alpha, beta=beta), q.dtype)
     _require(dict(H=H), torch.float32)
@@ -161,7 +185,9 @@ def decode_step(q, k, v, alpha, beta, H, o=None, stream=None, fuse=0):
     if o is None:
         o = torch.empty((N, Hh, dv), dtype=q.dtype, device=q.device)
     ptrs = (_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(H), _ptr(o))
-    if fuse:
+    if idx is not None:
+        _check(lib().ckda_decode_step_gather(*ptrs, N, Hh, dk_in, _ptr(idx), dk, dv, code, int(fuse), _stream(stream)))
+    elif fuse:
         _check(lib().ckda_decode_step_ex(*ptrs, N, Hh, dk, dv, code, int(fuse), _stream(stream)))
     else:
         _check(lib().ckda_decode_step(*ptrs, N, Hh, dk, dv, code, _stream(stream)))

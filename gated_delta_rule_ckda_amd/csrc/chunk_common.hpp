@@ -84,6 +84,7 @@ template <> struct Pair<bf16_t> {
   static __device__ __forceinline__ float hi(raw w) { return __uint_as_float(w & 0xFFFF0000u); }
   static __device__ __forceinline__ raw ones() { return 0x3F803F80u; }
   static __device__ __forceinline__ raw zeros() { return 0u; }
+  static __device__ __forceinline__ raw pack(bf16_t a, bf16_t b) { return (uint32_t)a.bits | ((uint32_t)b.bits << 16); }
   // store two values (channels c, c + 1) of one padded-fragment row
   static __device__ __forceinline__ void put(unsigned char* p, float a, float b) {
     *reinterpret_cast<uint32_t*>(p) = pack_bf16x2(a, b);
@@ -96,6 +97,7 @@ template <> struct Pair<float> {
   static __device__ __forceinline__ float hi(raw w) { return w[1]; }
   static __device__ __forceinline__ raw ones() { return raw{1.f, 1.f}; }
   static __device__ __forceinline__ raw zeros() { return raw{0.f, 0.f}; }
+  static __device__ __forceinline__ raw pack(float a, float b) { return raw{a, b}; }
   static __device__ __forceinline__ void put(unsigned char* p, float a, float b) {
     *reinterpret_cast<raw*>(p) = raw{a, b};
   }

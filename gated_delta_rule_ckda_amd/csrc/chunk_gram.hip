@@ -144,11 +144,13 @@ __device__ __forceinline__ void tile_pair(int n, int& I, int& J, int& xk, int& x
 // PRO: the per-token prologue of ckda.h (flags CKDA_FUSE_*) runs on the loads:
 // gates from their logits, beta from its logit, unit-norm keys and queries.
 // The gates are then kept in fp32 (a rounded computed gate would compound
-// over the chunk's products).
+// over the chunk's products).  The same instantiation gathers each head's
+// retained key channels when gidx is set (q, k, alpha rows of dk_in channels;
+// gidx [nheads][DK] channel indices).
 template <typename T, int DK, int C, bool PRO>
 __global__ __launch_bounds__((GramCfg<T, DK, C>::NTH)) void chunk_gram_kernel(
     const T* q, const T* k, const T* alpha, const T* beta, unsigned char* __restrict__ ws, int T_len,
-    int nchunks, int flags) {
+    int nchunks, int flags, const int* __restrict__ gidx, int dk_in, int nheads) {
   using P = GramCfg<T, DK, C>;
   using PR = Pair<T>;
   typedef typename PR::raw raw;
@@ -192,22 +194,22 @@ __global__ __launch_bounds__((GramCfg<T, DK, C>::NTH)) void chunk_gram_kernel(
 
   // ---- this thread's rows: signed gates (floored), keys, queries
   raw rl[16], rk[16], rq[16];   // gates (or, with the prologue, their logits) as loaded
-  if (act) {
-    const size_t base = (size_t)(row0 + 16 * b) * DK + c0;
+  // ld(x, i): this thread's channel pair of row 16 b + i of x
+  auto load_rows = [&](auto ld) __attribute__((always_inline)) {
     if (cv == C) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        rl[i] = PR::load(alpha + base + (size_t)i * DK);
-        rk[i] = PR::load(k + base + (size_t)i * DK);
-        rq[i] = PR::load(q + base + (size_t)i * DK);
+        rl[i] = ld(alpha, i);
+        rk[i] = ld(k, i);
+        rq[i] = ld(q, i);
       }
     } else {
       // ragged last chunk: rows past the end act as identity steps (gate 1, no key)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int t = 16 * b + i;
-        const size_t off = base + (size_t)(min(t, cv - 1) - 16 * b) * DK;
-        const raw a = PR::load(alpha + off), kk = PR::load(k + off), qq = PR::load(q + off);
+        const int ii = min(t, cv - 1) - 16 * b;
+        const raw a = ld(alpha, ii), kk = ld(k, ii), qq = ld(q, ii);
         rl[i] = PR::ones();
         rk[i] = PR::zeros();
         rq[i] = PR::zeros();
@@ -217,6 +219,22 @@ __global__ __launch_bounds__((GramCfg<T, DK, C>::NTH)) void chunk_gram_kernel(
           rq[i] = qq;
         }
       }
+    }
+  };
+  if (act) {
+    if (PRO && gidx) {
+      // channel gather: rows of dk_in channels, this head's retained index
+      // set picks channels 2u and 2u + 1 (indices clamped into the row)
+      const int* hidx = gidx + (bh % nheads) * DK;
+      const int g0 = min(max(hidx[c0], 0), dk_in - 1), g1 = min(max(hidx[c0 + 1], 0), dk_in - 1);
+      const size_t rb = (size_t)(row0 + 16 * b) * dk_in;
+      load_rows([&](const T* x, int i) __attribute__((always_inline)) {
+        const T* r = x + rb + (size_t)i * dk_in;
+        return PR::pack(r[g0], r[g1]);
+      });
+    } else {
+      const size_t base = (size_t)(row0 + 16 * b) * DK + c0;
+      load_rows([&](const T* x, int i) __attribute__((always_inline)) { return PR::load(x + base + (size_t)i * DK); });
     }
   }
   // Prologue gates: transformed after all loads are in flight, under one
@@ -674,14 +692,14 @@ __global__ __launch_bounds__((GramCfg<T, DK, C>::NTH)) void chunk_gram_kernel(
 template <typename T, int DK, int C>
 hipError_t launch_gram_t(const ChunkArgs& a, long long total_chunks, int nchunks) {
   using P = GramCfg<T, DK, C>;
-  if (a.flags != 0)
+  if (a.flags != 0 || a.gidx)
     hipLaunchKernelGGL((chunk_gram_kernel<T, DK, C, true>), dim3((unsigned)total_chunks), dim3(P::NTH), 0,
                        a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.alpha, (const T*)a.beta,
-                       (unsigned char*)a.workspace, a.T, nchunks, a.flags);
+                       (unsigned char*)a.workspace, a.T, nchunks, a.flags, a.gidx, a.gidx ? a.dk_in : DK, a.H);
   else
     hipLaunchKernelGGL((chunk_gram_kernel<T, DK, C, false>), dim3((unsigned)total_chunks), dim3(P::NTH), 0,
                        a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.alpha, (const T*)a.beta,
-                       (unsigned char*)a.workspace, a.T, nchunks, 0);
+                       (unsigned char*)a.workspace, a.T, nchunks, 0, nullptr, DK, 1);
   return hipGetLastError();
 }
 

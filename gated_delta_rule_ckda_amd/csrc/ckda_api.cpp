@@ -54,6 +54,7 @@ bool overlap(const Range& a, const Range& b) {
 bool misaligned(const void* p) { return ((uintptr_t)p & 15u) != 0; }
 
 constexpr int kFuseAll = CKDA_FUSE_GATES | CKDA_FUSE_NORM_K | CKDA_FUSE_NORM_Q;
+constexpr int kMaxDkIn = 65536;   // row width of gathered inputs
 
 }  // namespace
 
@@ -90,9 +91,12 @@ size_t ckda_chunk_fwd_workspace_size(int B, int H, int T, int dk, int dv, int ch
 static int chunk_fwd_impl(const void* q, const void* k, const void* v, const void* alpha, const void* beta,
                           const float* h0, void* o, float* hT, int B, int H, int T, int dk, int dv, int chunk,
                           int dtype, int flags, void* workspace, size_t workspace_bytes, void* stream,
-                          void* const ev[3]) {
+                          void* const ev[3], const int* gidx = nullptr, int dk_in = 0) {
   if ((flags & ~kFuseAll) != 0)
     return fail(CKDA_ERR_FLAGS, "ckda_chunk_fwd: flags 0x%x has bits outside CKDA_FUSE_* (0x%x)", flags, kFuseAll);
+  if (!gidx) dk_in = dk;
+  if (dk_in < 1 || dk_in > kMaxDkIn)
+    return fail(CKDA_ERR_DIM, "ckda_chunk_fwd: dk_in=%d outside 1..%d", dk_in, kMaxDkIn);
   if (B < 0 || H < 0 || T < 0)
     return fail(CKDA_ERR_DIM, "ckda_chunk_fwd: negative size (B=%d H=%d T=%d)", B, H, T);
   if (!supported_dtype(dtype))
@@ -103,7 +107,7 @@ static int chunk_fwd_impl(const void* q, const void* k, const void* v, const voi
     return fail(CKDA_ERR_UNSUPPORTED, "ckda_chunk_fwd: chunk=%d (supported: 16, 32, 64)", chunk);
   const size_t BH = (size_t)B * H;
   const size_t es = dtype_bytes(dtype);
-  const size_t nk = BH * T * dk, nv = BH * T * dv, nb = BH * T, ns = BH * dk * dv;
+  const size_t nk = BH * T * dk_in, nv = BH * T * dv, nb = BH * T, ns = BH * dk * dv;
   if (BH == 0) return ok();
   if (T > 0 && (!q || !k || !v || !alpha || !beta || !o))
     return fail(CKDA_ERR_NULL, "ckda_chunk_fwd: q, k, v, alpha, beta and o are required");
@@ -126,15 +130,16 @@ static int chunk_fwd_impl(const void* q, const void* k, const void* v, const voi
     if (((uintptr_t)workspace & 255u) != 0)
       return fail(CKDA_ERR_WORKSPACE, "ckda_chunk_fwd: workspace not 256-byte aligned");
   }
-  const void* ptrs[] = {q, k, v, alpha, beta, h0, o, hT};
-  const char* names[] = {"q", "k", "v", "alpha", "beta", "h0", "o", "hT"};
-  for (int i = 0; i < 8; ++i)
+  const void* ptrs[] = {q, k, v, alpha, beta, h0, o, hT, gidx};
+  const char* names[] = {"q", "k", "v", "alpha", "beta", "h0", "o", "hT", "idx"};
+  for (int i = 0; i < 9; ++i)
     if (ptrs[i] && misaligned(ptrs[i]))
       return fail(CKDA_ERR_DIM, "ckda_chunk_fwd: %s is not 16-byte aligned", names[i]);
 
   const Range in[] = {range("q", q, T ? nk * es : 0),     range("k", k, T ? nk * es : 0),
                       range("v", v, T ? nv * es : 0),     range("alpha", alpha, T ? nk * es : 0),
-                      range("beta", beta, T ? nb * es : 0), range("h0", h0, h0 ? ns * 4 : 0)};
+                      range("beta", beta, T ? nb * es : 0), range("h0", h0, h0 ? ns * 4 : 0),
+                      range("idx", gidx, gidx ? (size_t)H * dk * 4 : 0)};
   const Range ro = range("o", o, T ? nv * es : 0);
   const Range rh = range("hT", hT, hT ? ns * 4 : 0);
   const Range rw = range("workspace", workspace, T ? need : 0);
@@ -149,7 +154,7 @@ static int chunk_fwd_impl(const void* q, const void* k, const void* v, const voi
     return fail(CKDA_ERR_ALIAS, "ckda_chunk_fwd: workspace overlaps an output");
 
   ckda::ChunkArgs a{q, k, v, alpha, beta, h0, o, hT, B, H, T, dk, dv, chunk, dtype, flags, workspace,
-                    (hipStream_t)stream, {(hipEvent_t)ev[0], (hipEvent_t)ev[1], (hipEvent_t)ev[2]}};
+                    (hipStream_t)stream, {(hipEvent_t)ev[0], (hipEvent_t)ev[1], (hipEvent_t)ev[2]}, gidx, dk_in};
   hipError_t e = ckda::launch_chunk_fwd(a);
   if (e != hipSuccess)
     return fail(CKDA_ERR_HIP, "ckda_chunk_fwd: launch failed: %s", hipGetErrorString(e));
@@ -174,6 +179,16 @@ int ckda_chunk_fwd_ex(const void* q, const void* k, const void* v, const void* a
                         workspace_bytes, stream, none);
 }
 
+int ckda_chunk_fwd_gather(const void* q, const void* k, const void* v, const void* alpha,
+                          const void* beta, const float* h0, void* o, float* hT,
+                          int B, int H, int T, int dk_in, const int* idx, int dk, int dv, int chunk, int dtype,
+                          int flags, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!idx && B > 0 && H > 0) return fail(CKDA_ERR_NULL, "ckda_chunk_fwd: idx is required");
+  void* const none[3] = {nullptr, nullptr, nullptr};
+  return chunk_fwd_impl(q, k, v, alpha, beta, h0, o, hT, B, H, T, dk, dv, chunk, dtype, flags, workspace,
+                        workspace_bytes, stream, none, idx, dk_in);
+}
+
 int ckda_chunk_fwd_timed(const void* q, const void* k, const void* v, const void* alpha,
                          const void* beta, const float* h0, void* o, float* hT,
                          int B, int H, int T, int dk, int dv, int chunk, int dtype,
@@ -185,9 +200,13 @@ int ckda_chunk_fwd_timed(const void* q, const void* k, const void* v, const void
 }
 
 static int decode_impl(const void* q, const void* k, const void* v, const void* alpha, const void* beta,
-                       float* H_inout, void* o, int N, int H, int dk, int dv, int dtype, int flags, void* stream) {
+                       float* H_inout, void* o, int N, int H, int dk, int dv, int dtype, int flags, void* stream,
+                       const int* gidx = nullptr, int dk_in = 0) {
   if ((flags & ~kFuseAll) != 0)
     return fail(CKDA_ERR_FLAGS, "ckda_decode_step: flags 0x%x has bits outside CKDA_FUSE_* (0x%x)", flags, kFuseAll);
+  if (!gidx) dk_in = dk;
+  if (dk_in < 1 || dk_in > kMaxDkIn)
+    return fail(CKDA_ERR_DIM, "ckda_decode_step: dk_in=%d outside 1..%d", dk_in, kMaxDkIn);
   if (N < 0 || H < 0) return fail(CKDA_ERR_DIM, "ckda_decode_step: negative size (N=%d H=%d)", N, H);
   if (!supported_dtype(dtype))
     return fail(CKDA_ERR_UNSUPPORTED, "ckda_decode_step: dtype %d is not F32(0) or BF16(1)", dtype);
@@ -198,13 +217,15 @@ static int decode_impl(const void* q, const void* k, const void* v, const void* 
   if (NH > (size_t)INT32_MAX) return fail(CKDA_ERR_DIM, "ckda_decode_step: N*H exceeds the launch grid");
   if (!q || !k || !v || !alpha || !beta || !H_inout || !o)
     return fail(CKDA_ERR_NULL, "ckda_decode_step: every pointer is required");
-  const void* ptrs[] = {q, k, v, alpha, beta, H_inout, o};
-  const char* names[] = {"q", "k", "v", "alpha", "beta", "H_inout", "o"};
-  for (int i = 0; i < 7; ++i)
-    if (misaligned(ptrs[i])) return fail(CKDA_ERR_DIM, "ckda_decode_step: %s is not 16-byte aligned", names[i]);
+  const void* ptrs[] = {q, k, v, alpha, beta, H_inout, o, gidx};
+  const char* names[] = {"q", "k", "v", "alpha", "beta", "H_inout", "o", "idx"};
+  for (int i = 0; i < 8; ++i)
+    if (ptrs[i] && misaligned(ptrs[i]))
+      return fail(CKDA_ERR_DIM, "ckda_decode_step: %s is not 16-byte aligned", names[i]);
   const size_t es = dtype_bytes(dtype);
-  const Range in[] = {range("q", q, NH * dk * es), range("k", k, NH * dk * es), range("v", v, NH * dv * es),
-                      range("alpha", alpha, NH * dk * es), range("beta", beta, NH * es)};
+  const Range in[] = {range("q", q, NH * dk_in * es), range("k", k, NH * dk_in * es), range("v", v, NH * dv * es),
+                      range("alpha", alpha, NH * dk_in * es), range("beta", beta, NH * es),
+                      range("idx", gidx, gidx ? (size_t)H * dk * 4 : 0)};
   const Range rs = range("H_inout", H_inout, NH * dk * dv * 4);
   const Range ro = range("o", o, NH * dv * es);
   for (const Range& r : in) {
@@ -213,7 +234,7 @@ static int decode_impl(const void* q, const void* k, const void* v, const void* 
   }
   if (overlap(ro, rs)) return fail(CKDA_ERR_ALIAS, "ckda_decode_step: o overlaps H_inout");
 
-  ckda::DecodeArgs a{q, k, v, alpha, beta, H_inout, o, N, H, dk, dv, dtype, flags, (hipStream_t)stream};
+  ckda::DecodeArgs a{q, k, v, alpha, beta, H_inout, o, N, H, dk, dv, dtype, flags, (hipStream_t)stream, gidx, dk_in};
   hipError_t e = ckda::launch_decode(a);
   if (e != hipSuccess)
     return fail(CKDA_ERR_HIP, "ckda_decode_step: launch failed: %s", hipGetErrorString(e));
@@ -224,6 +245,14 @@ int ckda_decode_step(const void* q, const void* k, const void* v, const void* al
                      const void* beta, float* H_inout, void* o,
                      int N, int H, int dk, int dv, int dtype, void* stream) {
   return decode_impl(q, k, v, alpha, beta, H_inout, o, N, H, dk, dv, dtype, 0, stream);
+}
+
+int ckda_decode_step_gather(const void* q, const void* k, const void* v, const void* alpha,
+                            const void* beta, float* H_inout, void* o,
+                            int N, int H, int dk_in, const int* idx, int dk, int dv, int dtype, int flags,
+                            void* stream) {
+  if (!idx && N > 0 && H > 0) return fail(CKDA_ERR_NULL, "ckda_decode_step: idx is required");
+  return decode_impl(q, k, v, alpha, beta, H_inout, o, N, H, dk, dv, dtype, flags, stream, idx, dk_in);
 }
 
 int ckda_decode_step_ex(const void* q, const void* k, const void* v, const void* alpha,

@@ -16,6 +16,8 @@ struct DecodeArgs {
   int N, H, dk, dv, dtype;
   int flags;   // CKDA_FUSE_* prologue steps (0: inputs used as given)
   hipStream_t stream;
+  const int* gidx = nullptr;   // [H][dk] retained channel indices into rows of dk_in (NULL: no gather)
+  int dk_in = 0;
 };
 
 struct ChunkArgs {
@@ -28,6 +30,8 @@ struct ChunkArgs {
   void* workspace;
   hipStream_t stream;
   hipEvent_t ev[3];   // recorded before the Gram kernel, between the kernels, after the state kernel (if set)
+  const int* gidx = nullptr;   // [H][dk] retained channel indices into rows of dk_in (NULL: no gather)
+  int dk_in = 0;
 };
 
 // Layout of the per-chunk records the Gram kernel writes and the state-pass

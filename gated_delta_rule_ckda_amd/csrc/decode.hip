@@ -18,7 +18,9 @@
 //
 // PRO instantiation: the per-token prologue (ckda.h, CKDA_FUSE_*) runs on the
 // loaded token before the step: gates and beta from their logits, keys and
-// queries scaled to unit norm (one wave reduces each vector).
+// queries scaled to unit norm (one wave reduces each vector).  It also
+// gathers each head's retained key channels from rows of dk_in when gidx is
+// set.
 #include "ckda_device.hpp"
 #include "ckda_internal.hpp"
 
@@ -33,7 +35,7 @@ template <typename T, int DK, int DV, bool PRO>
 __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ alpha, const T* __restrict__ beta, float* __restrict__ H,
-    T* __restrict__ o, int flags) {
+    T* __restrict__ o, int flags, const int* __restrict__ gidx, int dk_in, int nheads) {
   constexpr int TPR = DV / 4;                    // threads per state row (4 columns each)
   constexpr int RPI = kDecodeThreads / TPR;      // rows covered per pass
   constexpr int ITER = (DK + RPI - 1) / RPI;     // passes over the rows
@@ -57,10 +59,13 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
   }
   if constexpr (PRO) {
     for (int i = tid; i < DK; i += kDecodeThreads) {
-      const float a = to_f32(alpha[st * DK + i]);
+      // channel gather: element i of the retained set (index clamped into the row)
+      const long long e = gidx ? st * (long long)dk_in + min(max(gidx[(st % nheads) * DK + i], 0), dk_in - 1)
+                               : st * DK + i;
+      const float a = to_f32(alpha[e]);
       s_a[i] = (flags & kFuseGates) ? practical_gate(a) : a;
-      s_k[i] = to_f32(k[st * DK + i]);
-      s_q[i] = to_f32(q[st * DK + i]);
+      s_k[i] = to_f32(k[e]);
+      s_q[i] = to_f32(q[e]);
     }
     __syncthreads();
     const int w = tid >> 6;
@@ -146,14 +151,14 @@ template <typename T, int DK, int DV>
 static hipError_t launch_decode_t(const DecodeArgs& a) {
   const long long states = (long long)a.N * a.H;
   if (states == 0) return hipSuccess;
-  if (a.flags != 0)
+  if (a.flags != 0 || a.gidx)
     hipLaunchKernelGGL((decode_kernel<T, DK, DV, true>), dim3((unsigned)states), dim3(kDecodeThreads), 0,
                        a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.alpha,
-                       (const T*)a.beta, a.H_inout, (T*)a.o, a.flags);
+                       (const T*)a.beta, a.H_inout, (T*)a.o, a.flags, a.gidx, a.gidx ? a.dk_in : DK, a.H);
   else
     hipLaunchKernelGGL((decode_kernel<T, DK, DV, false>), dim3((unsigned)states), dim3(kDecodeThreads), 0,
                        a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.alpha,
-                       (const T*)a.beta, a.H_inout, (T*)a.o, 0);
+                       (const T*)a.beta, a.H_inout, (T*)a.o, 0, nullptr, DK, 1);
   return hipGetLastError();
 }
 

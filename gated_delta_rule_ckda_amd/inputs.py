@@ -195,6 +195,45 @@ def decode_logit_inputs(step: int, d: DecodeWorkload = DECODE, N=None, H=None):
                 alpha=_to(a, d.dtype), beta=_to(bl, d.dtype))
 
 
+def retained_channels(H: int, dk_in: int, dk: int, seed: int) -> torch.Tensor:
+    """A per-head retained channel set [H, dk] int32: dk distinct channels of
+    dk_in per head, drawn uniformly (a stand-in for a calibrated selection),
+    in increasing order."""
+    rng = np.random.default_rng(seed)
+    idx = np.stack([np.sort(rng.choice(dk_in, dk, replace=False)) for _ in range(H)])
+    return torch.from_numpy(idx.astype(np.int32))
+
+
+def make_gather_inputs(w: Workload, dk_in: int, idx: torch.Tensor):
+    """Full-width inputs for the channel gather: dict(q, k, v, alpha, beta, h0)
+    with q, k, alpha [B, H, T, dk_in] (w.dk is the kept width).  Laws as
+    make_inputs; the kept channels of each key row have unit norm, the others
+    are N(0, 1).  Draw order: q, k, v, alpha, beta, h0."""
+    rng = np.random.default_rng(w.seed)
+    B, H, T, dv = w.B, w.H, w.T, w.dv
+    q = rng.standard_normal((B, H, T, dk_in), dtype=np.float32)
+    k = rng.standard_normal((B, H, T, dk_in), dtype=np.float32)
+    ix = idx.numpy().astype(np.int64)
+    for h in range(H):
+        k[:, h][..., ix[h]] = _normalise(k[:, h][..., ix[h]])
+    v = rng.standard_normal((B, H, T, dv), dtype=np.float32)
+    a, b = _gates(rng, w.gates, (B, H, T, dk_in), (B, H, T))
+    if w.h0 == "normal":
+        h0 = torch.from_numpy(np.float32(0.1) * rng.standard_normal((B, H, w.dk, dv), dtype=np.float32))
+    elif w.h0 == "zero":
+        h0 = torch.zeros((B, H, w.dk, dv), dtype=torch.float32)
+    else:
+        h0 = None
+    return dict(q=_to(q, w.dtype), k=_to(k, w.dtype), v=_to(v, w.dtype),
+                alpha=_to(a, w.dtype), beta=_to(b, w.dtype), h0=h0)
+
+
+def gather_channels(x: torch.Tensor, idx: torch.Tensor) -> torch.Tensor:
+    """x[b, h, ..., idx[h]] for x [B, H, ..., dk_in] (CPU; for the oracle side)."""
+    out = [x[:, h][..., idx[h].long()] for h in range(x.shape[1])]
+    return torch.stack(out, dim=1).contiguous()
+
+
 def decode_state(d: DecodeWorkload = DECODE, N=None, H=None):
     """Initial fp32 decode state [N,H,dk,dv] ~ N(0, 0.1)."""
     N = d.N if N is None else N

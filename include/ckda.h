@@ -157,6 +157,28 @@ int ckda_chunk_fwd_ex(const void* q, const void* k, const void* v, const void* a
                       int B, int H, int T, int dk, int dv, int chunk, int dtype, int flags,
                       void* workspace, size_t workspace_bytes, void* stream);
 
+/* ckda_chunk_fwd_ex on a retained subset of key channels, gathered inside
+ * the kernels (the state-reduction setting of the "On State Reduction in
+ * Linear Attention" presentation: a per-head index set keeps dk of the dk_in
+ * key/query channels, and the recurrence runs on the kept ones).
+ *
+ *   q, k, alpha : [B, H, T, dk_in] dtype, full-width rows
+ *   idx         : [H, dk] int32 DEVICE array; head h uses channels
+ *                 idx[h][0..dk-1] of its rows, in that order (repeats
+ *                 allowed).  An index outside [0, dk_in) is clamped into it
+ *                 (no fault; the result is then unspecified).
+ *   v, beta, h0, o, hT, workspace : as ckda_chunk_fwd, with dk the KEPT width
+ *                 (states [B, H, dk, dv]; workspace size for dk).
+ *
+ * Equivalent to ckda_chunk_fwd_ex on q, k, alpha gathered beforehand
+ * (x[..., idx[h]]) without that extra pass over memory; with CKDA_FUSE_NORM_K
+ * the keys are normalised over the kept channels.  1 <= dk_in <= 65536; idx
+ * must be 16-byte aligned and must not overlap an output. */
+int ckda_chunk_fwd_gather(const void* q, const void* k, const void* v, const void* alpha,
+                          const void* beta, const float* h0, void* o, float* hT,
+                          int B, int H, int T, int dk_in, const int* idx, int dk, int dv, int chunk, int dtype,
+                          int flags, void* workspace, size_t workspace_bytes, void* stream);
+
 /* One recurrent decode step for N sequences x H heads, state in place.
  *
  *   q, k, alpha : [N, H, dk]     dtype
@@ -188,6 +210,15 @@ int ckda_decode_step(const void* q, const void* k, const void* v, const void* al
 int ckda_decode_step_ex(const void* q, const void* k, const void* v, const void* alpha,
                         const void* beta, float* H_inout, void* o,
                         int N, int H, int dk, int dv, int dtype, int flags, void* stream);
+
+/* ckda_decode_step_ex on a retained subset of key channels gathered inside
+ * the kernel: q, k, alpha are [N, H, dk_in] full-width rows, idx [H, dk]
+ * int32 device indices (as ckda_chunk_fwd_gather), the state [N, H, dk, dv]
+ * covers the kept channels. */
+int ckda_decode_step_gather(const void* q, const void* k, const void* v, const void* alpha,
+                            const void* beta, float* H_inout, void* o,
+                            int N, int H, int dk_in, const int* idx, int dk, int dv, int dtype, int flags,
+                            void* stream);
 
 /* Static description of a status code. */
 const char* ckda_status_string(int status);

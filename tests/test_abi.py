@@ -127,6 +127,46 @@ def test_fused_entry_points_check_arguments_like_the_plain_ones(flags):
     assert call_dec(flags=flags, N=0, q=None)[0] == 0
 
 
+def call_fwd_gather(**kw):
+    L = ck.lib()
+    B, H, T, dk, dv, dk_in = kw.get("B", 1), kw.get("H", 2), kw.get("T", 64), kw.get("dk", 64), 64, kw.get("dk_in", 128)
+    p = dict(q=BASE, k=BASE + 1 * MB, v=BASE + 2 * MB, alpha=BASE + 3 * MB, beta=BASE + 4 * MB,
+             h0=BASE + 5 * MB, o=BASE + 6 * MB, hT=BASE + 7 * MB, ws=BASE + 8 * MB, idx=BASE + 80 * MB)
+    p.update({k: v for k, v in kw.items() if k in p})
+    rc = L.ckda_chunk_fwd_gather(p["q"], p["k"], p["v"], p["alpha"], p["beta"], p["h0"], p["o"], p["hT"], B, H, T,
+                                 dk_in, p["idx"], dk, dv, 64, 1, kw.get("flags", 0), p["ws"], 64 * MB, None)
+    return rc, L.ckda_last_error().decode()
+
+
+def call_dec_gather(**kw):
+    L = ck.lib()
+    p = dict(q=BASE, k=BASE + MB, v=BASE + 2 * MB, alpha=BASE + 3 * MB, beta=BASE + 4 * MB,
+             S=BASE + 5 * MB, o=BASE + 6 * MB, idx=BASE + 80 * MB)
+    p.update({k: v for k, v in kw.items() if k in p})
+    rc = L.ckda_decode_step_gather(p["q"], p["k"], p["v"], p["alpha"], p["beta"], p["S"], p["o"], 2, 2,
+                                   kw.get("dk_in", 128), p["idx"], 64, 64, 1, kw.get("flags", 0), None)
+    return rc, L.ckda_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(idx=None), 1), (dict(dk_in=0), 2), (dict(dk_in=1 << 20), 2), (dict(idx=BASE + 80 * MB + 4), 2),
+    (dict(o=BASE + 80 * MB), 4),                       # o overlaps idx
+    (dict(flags=8), 7), (dict(dk=48), 3),
+    (dict(o=BASE + 20000), 4),                       # o inside q's full-width rows (past its kept width)
+])
+def test_gather_entry_points_reject(kw, status):
+    rc, msg = call_fwd_gather(**kw)
+    assert rc == status, (rc, msg)
+    if "dk" not in kw and kw.get("o") != BASE + 20000:
+        rc, msg = call_dec_gather(**kw)
+        assert rc == status and msg.startswith("ckda_decode_step"), (rc, msg)
+
+
+def test_gather_entry_points_accept_valid_empty_calls():
+    assert call_fwd_gather(B=0, idx=None)[0] == 0
+    assert call_fwd_gather(H=0, idx=None)[0] == 0
+
+
 def test_prologue_flag_values_agree():
     text = open(HEADER).read()
     defs = dict(re.findall(r"#define (CKDA_FUSE_\w+) (\d+)", text))
