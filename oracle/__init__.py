@@ -40,24 +40,29 @@ def build(force: bool = True) -> str:
     return _LIB_PATH
 
 
+def _declare(lib):
+    vp, i = ctypes.c_void_p, ctypes.c_int
+    lib.ckda_oracle_fwd.argtypes = [vp, vp, vp, vp, vp, i, vp, i, vp, vp, i, i, i, i, i, i]
+    lib.ckda_oracle_fwd.restype = i
+    lib.ckda_oracle_decode.argtypes = [vp, vp, vp, vp, vp, i, vp, vp, i, i, i, i, i]
+    lib.ckda_oracle_decode.restype = i
+    lib.ckda_oracle_num_threads.argtypes = []
+    lib.ckda_oracle_num_threads.restype = i
+    lib.ckda_oracle_prologue.argtypes = [vp, vp, vp, vp, i, i, ctypes.c_longlong, i, vp, vp, vp, vp]
+    lib.ckda_oracle_prologue.restype = i
+    lib.ckda_oracle_deltaproduct2.argtypes = [vp, vp, vp, vp, vp, i, vp, i, vp, vp, i, i, i, i, i, i]
+    lib.ckda_oracle_deltaproduct2.restype = i
+    lib.ckda_oracle_deltaproduct2_decode.argtypes = [vp, vp, vp, vp, vp, i, vp, vp, i, i, i, i]
+    lib.ckda_oracle_deltaproduct2_decode.restype = i
+    return lib
+
+
 def _load():
     global _lib
     if _lib is None:
         if not os.path.exists(_LIB_PATH):
             build()
-        lib = ctypes.CDLL(_LIB_PATH)
-        vp, i = ctypes.c_void_p, ctypes.c_int
-        lib.ckda_oracle_fwd.argtypes = [vp, vp, vp, vp, vp, i, vp, i, vp, vp,
-                                        i, i, i, i, i, i]
-        lib.ckda_oracle_fwd.restype = i
-        lib.ckda_oracle_decode.argtypes = [vp, vp, vp, vp, vp, i, vp, vp,
-                                           i, i, i, i, i]
-        lib.ckda_oracle_decode.restype = i
-        lib.ckda_oracle_num_threads.argtypes = []
-        lib.ckda_oracle_num_threads.restype = i
-        lib.ckda_oracle_prologue.argtypes = [vp, vp, vp, vp, i, i, ctypes.c_longlong, i, vp, vp, vp, vp]
-        lib.ckda_oracle_prologue.restype = i
-        _lib = lib
+        _lib = _declare(ctypes.CDLL(_LIB_PATH))
     return _lib
 
 
@@ -189,6 +194,56 @@ def decode_fused(q, k, v, a, b, S, flags=GATES | NORM_K, nthreads=0):
     return decode(qq, kk, _widen(v), alpha, beta, S, nthreads=nthreads)
 
 
+def deltaproduct2(q, k, v, alpha, beta, h0=None, nthreads=0):
+    """DeltaProduct_2 forward in fp64 (ckda_oracle_deltaproduct2).
+
+    q: [B,H,T,dk]; k: [B,H,T,2,dk]; v: [B,H,T,2,dv]; beta: [B,H,T,2];
+    alpha: [B,H,T] scalar gates or None (ungated); one dtype.  h0 as fwd().
+    Returns (o [B,H,T,dv], hT [B,H,dk,dv]) float64."""
+    q, k, v, beta = (np.ascontiguousarray(x) for x in (q, k, v, beta))
+    alpha = None if alpha is None else np.ascontiguousarray(alpha)
+    code = _code(q)
+    for x in (k, v, beta) + (() if alpha is None else (alpha,)):
+        if _code(x) != code:
+            raise TypeError("inputs must share one dtype")
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    if k.shape != (B, H, T, 2, dk) or v.shape != (B, H, T, 2, dv) or beta.shape != (B, H, T, 2) \
+            or (alpha is not None and alpha.shape != (B, H, T)):
+        raise ValueError("inconsistent shapes")
+    h0c, h0code = None, F32
+    if h0 is not None:
+        h0c = np.ascontiguousarray(h0)
+        if h0c.shape != (B, H, dk, dv):
+            raise ValueError("h0 shape")
+        h0code = _code(h0c)
+    o = np.empty((B, H, T, dv), np.float64)
+    hT = np.empty((B, H, dk, dv), np.float64)
+    rc = _load().ckda_oracle_deltaproduct2(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), code, _ptr(h0c),
+                                           h0code, _ptr(o), _ptr(hT), B, H, T, dk, dv, int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"ckda_oracle_deltaproduct2 failed with code {rc}")
+    return o, hT
+
+
+def deltaproduct2_decode(q, k, v, alpha, beta, S):
+    """One DeltaProduct_2 token applied in place to the fp64 state S [N,H,dk,dv].
+    q [N,H,dk]; k [N,H,2,dk]; v [N,H,2,dv]; beta [N,H,2]; alpha [N,H] or None."""
+    q, k, v, beta = (np.ascontiguousarray(x) for x in (q, k, v, beta))
+    alpha = None if alpha is None else np.ascontiguousarray(alpha)
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    if not (isinstance(S, np.ndarray) and S.dtype == np.float64 and S.flags.c_contiguous
+            and S.shape == (N, H, dk, dv)):
+        raise ValueError("S must be a C-contiguous float64 [N,H,dk,dv] array")
+    o = np.empty((N, H, dv), np.float64)
+    rc = _load().ckda_oracle_deltaproduct2_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _code(q),
+                                                  _ptr(S), _ptr(o), N, H, dk, dv)
+    if rc != 0:
+        raise RuntimeError(f"ckda_oracle_deltaproduct2_decode failed with code {rc}")
+    return o
+
+
 class Variant:
     """An oracle bound to another build of ckda_oracle.c (same ABI).
 
@@ -201,15 +256,7 @@ class Variant:
     def _swap(self, fn, *a, **kw):
         global _lib
         saved = _lib
-        lib = ctypes.CDLL(self._path)
-        vp, i = ctypes.c_void_p, ctypes.c_int
-        lib.ckda_oracle_fwd.argtypes = [vp, vp, vp, vp, vp, i, vp, i, vp, vp, i, i, i, i, i, i]
-        lib.ckda_oracle_fwd.restype = i
-        lib.ckda_oracle_decode.argtypes = [vp, vp, vp, vp, vp, i, vp, vp, i, i, i, i, i]
-        lib.ckda_oracle_decode.restype = i
-        lib.ckda_oracle_prologue.argtypes = [vp, vp, vp, vp, i, i, ctypes.c_longlong, i, vp, vp, vp, vp]
-        lib.ckda_oracle_prologue.restype = i
-        _lib = lib
+        _lib = _declare(ctypes.CDLL(self._path))
         try:
             return fn(*a, **kw)
         finally:
@@ -226,6 +273,12 @@ class Variant:
 
     def fwd_fused(self, *a, **kw):
         return self._swap(fwd_fused, *a, **kw)
+
+    def deltaproduct2(self, *a, **kw):
+        return self._swap(deltaproduct2, *a, **kw)
+
+    def deltaproduct2_decode(self, *a, **kw):
+        return self._swap(deltaproduct2_decode, *a, **kw)
 
 
 def build_variant(source_text: str, out_path: str) -> "Variant":

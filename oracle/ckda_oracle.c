@@ -234,3 +234,98 @@ int ckda_oracle_prologue(const void* a, const void* b, const void* k, const void
   unit_rows(q, dtype, ntok, dk, flags & PRO_NORM_Q, qq);
   return 0;
 }
+
+/* ---------------------------------------------------------------- DeltaProduct_2
+ *
+ * The DeltaProduct_2 comparator of the "Complex KDA" paper (Fig. 5 and the
+ * implementation paragraph of Sec. 6: two delta-rule updates per token,
+ * ungated there; App. C, "Consequences for CKDA and Gated DeltaProduct": the
+ * gated form scales the product of the per-token Householder factors
+ * (I - beta_j k_j k_j^T), j = 1, 2, by one scalar gate alpha_t).  Per token:
+ *
+ *   H <- alpha_t H                                  (omitted when ungated)
+ *   for j = 1, 2:  H <- (I - beta_tj k_tj k_tj^T) H + beta_tj k_tj v_tj^T
+ *   o_t = H^T q_t
+ *
+ * The additive term of each sub-step follows its own Householder factor, as
+ * in a delta-rule update (the reading of "two delta-rule updates per token").
+ * Layouts: q [B,H,T,dk]; k [B,H,T,2,dk]; v [B,H,T,2,dv]; beta [B,H,T,2];
+ * alpha [B,H,T] or NULL; h0/hT [B,H,dk,dv]; o [B,H,T,dv]. */
+
+/* H <- (I - b k k^T) H + b k v^T, with the Householder factor applied as
+ * H - b k (k^T H).  w: scratch of length dv. */
+static void householder_write(double* S, const double* kk, const double* vv, double b, double* w, int dk, int dv) {
+  for (int j = 0; j < dv; ++j) w[j] = 0.0;
+  for (int i = 0; i < dk; ++i)
+    for (int j = 0; j < dv; ++j) w[j] += kk[i] * S[(long)i * dv + j];
+  for (int i = 0; i < dk; ++i)
+    for (int j = 0; j < dv; ++j) S[(long)i * dv + j] += b * kk[i] * (vv[j] - w[j]);
+}
+
+static void dp2_token(double* S, const void* q, const void* k, const void* v, const void* alpha, const void* beta,
+                      int dtype, long long tok, int dk, int dv, double* buf, double* out) {
+  double *kk = buf, *qq = kk + dk, *vv = qq + dk, *w = vv + dv;
+  if (alpha) {
+    const double a = widen(alpha, tok, dtype);
+    for (long long e = 0; e < (long long)dk * dv; ++e) S[e] *= a;
+  }
+  for (int j = 0; j < 2; ++j) {
+    for (int i = 0; i < dk; ++i) kk[i] = widen(k, (tok * 2 + j) * dk + i, dtype);
+    for (int c = 0; c < dv; ++c) vv[c] = widen(v, (tok * 2 + j) * dv + c, dtype);
+    householder_write(S, kk, vv, widen(beta, tok * 2 + j, dtype), w, dk, dv);
+  }
+  if (out) {
+    for (int i = 0; i < dk; ++i) qq[i] = widen(q, tok * dk + i, dtype);
+    for (int c = 0; c < dv; ++c) out[c] = 0.0;
+    for (int i = 0; i < dk; ++i)
+      for (int c = 0; c < dv; ++c) out[c] += S[(long)i * dv + c] * qq[i];
+  }
+}
+
+int ckda_oracle_deltaproduct2(const void* q, const void* k, const void* v, const void* alpha, const void* beta,
+                              int dtype, const void* h0, int h0_dtype, double* o, double* hT, int B, int H, int T,
+                              int dk, int dv, int nthreads) {
+  if (!q || !k || !v || !beta) return 1;
+  if (B < 0 || H < 0 || T < 0 || dk <= 0 || dv <= 0) return 2;
+  if (!valid_dtype(dtype) || (h0 && !valid_dtype(h0_dtype))) return 3;
+  long long BH = (long long)B * H;
+  int failed = 0;
+#ifdef _OPENMP
+  int nt = nthreads > 0 ? nthreads : omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : failed) num_threads(nt)
+#else
+  (void)nthreads;
+#endif
+  for (long long bh = 0; bh < BH; ++bh) {
+    double* S = (double*)malloc(sizeof(double) * (size_t)dk * dv);
+    double* buf = (double*)malloc(sizeof(double) * (size_t)(2 * dk + 3 * dv));
+    if (!S || !buf) { free(S); free(buf); failed |= 1; continue; }
+    long long sbase = bh * (long long)dk * dv;
+    for (long long e = 0; e < (long long)dk * dv; ++e) S[e] = h0 ? widen(h0, sbase + e, h0_dtype) : 0.0;
+    for (int t = 0; t < T; ++t) {
+      const long long tok = bh * T + t;
+      dp2_token(S, q, k, v, alpha, beta, dtype, tok, dk, dv, buf, o ? o + tok * dv : NULL);
+    }
+    if (hT) memcpy(hT + sbase, S, sizeof(double) * (size_t)dk * dv);
+    free(S);
+    free(buf);
+  }
+  return failed ? 4 : 0;
+}
+
+/* One DeltaProduct_2 token for N sequences x H heads, fp64 state in place.
+ * q [N,H,dk]; k [N,H,2,dk]; v [N,H,2,dv]; beta [N,H,2]; alpha [N,H] or NULL. */
+int ckda_oracle_deltaproduct2_decode(const void* q, const void* k, const void* v, const void* alpha,
+                                     const void* beta, int dtype, double* S_inout, double* o, int N, int H, int dk,
+                                     int dv) {
+  if (!q || !k || !v || !beta || !S_inout) return 1;
+  if (N < 0 || H < 0 || dk <= 0 || dv <= 0) return 2;
+  if (!valid_dtype(dtype)) return 3;
+  double* buf = (double*)malloc(sizeof(double) * (size_t)(2 * dk + 3 * dv));
+  if (!buf) return 4;
+  for (long long nh = 0; nh < (long long)N * H; ++nh)
+    dp2_token(S_inout + nh * (long long)dk * dv, q, k, v, alpha, beta, dtype, nh, dk, dv, buf,
+              o ? o + nh * dv : NULL);
+  free(buf);
+  return 0;
+}

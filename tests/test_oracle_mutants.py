@@ -51,6 +51,15 @@ MUTANTS = {
     "norm_without_sqrt": [("      const double inv = 1.0 / sqrt(ss + 1e-6);", "      const double inv = 1.0 / (ss + 1e-6);")],
     "norm_flags_swapped": [("  unit_rows(k, dtype, ntok, dk, flags & PRO_NORM_K, kk);",
                             "  unit_rows(k, dtype, ntok, dk, flags & PRO_NORM_Q, kk);")],
+    # DeltaProduct_2
+    "dp2_gate_dropped": [("    for (long long e = 0; e < (long long)dk * dv; ++e) S[e] *= a;\n  }\n  for (int j = 0; j < 2; ++j) {",
+                          "    (void)a;\n  }\n  for (int j = 0; j < 2; ++j) {")],
+    "dp2_substep_keys_swapped": [("    for (int i = 0; i < dk; ++i) kk[i] = widen(k, (tok * 2 + j) * dk + i, dtype);",
+                                  "    for (int i = 0; i < dk; ++i) kk[i] = widen(k, (tok * 2 + 1 - j) * dk + i, dtype);")],
+    "dp2_one_beta": [("    householder_write(S, kk, vv, widen(beta, tok * 2 + j, dtype), w, dk, dv);",
+                      "    householder_write(S, kk, vv, widen(beta, tok * 2, dtype), w, dk, dv);")],
+    "dp2_value_not_corrected": [("    for (int j = 0; j < dv; ++j) S[(long)i * dv + j] += b * kk[i] * (vv[j] - w[j]);",
+                                 "    for (int j = 0; j < dv; ++j) S[(long)i * dv + j] += b * kk[i] * vv[j];")],
 }
 
 PIN_CALLS = [
@@ -73,6 +82,11 @@ PIN_CALLS = [
     lambda o: pins.test_practical_beta(o),
     lambda o: pins.test_unit_norm_keys_and_queries(o),
     lambda o: pins.test_fused_forward_is_the_recurrence_on_prepared_inputs(o),
+    lambda o: pins.test_deltaproduct2_tracks_permutations_with_transposition_keys(o),
+    lambda o: pins.test_deltaproduct2_transition_is_the_gated_householder_product(o),
+    lambda o: pins.test_deltaproduct2_with_one_inactive_substep_is_the_delta_rule(o, 0),
+    lambda o: pins.test_deltaproduct2_with_one_inactive_substep_is_the_delta_rule(o, 1),
+    lambda o: pins.test_deltaproduct2_decode_continues_the_forward(o),
 ]
 
 

@@ -525,3 +525,101 @@ def test_fused_forward_is_the_recurrence_on_prepared_inputs(oracle_lib):
     o_p, h_p = run(oracle_lib, qn, kn, v, al, be, h0)
     assert np.max(np.abs(o_f[0, 0] - o_p)) < 1e-5 * max(1.0, np.max(np.abs(o_p)))
     assert np.max(np.abs(h_f[0, 0] - h_p)) < 1e-5 * max(1.0, np.max(np.abs(h_p)))
+
+
+# ---------------------------------------------------------------- DeltaProduct_2
+
+def dp2(oracle_lib, q, k, v, a, b, h0=None):
+    """DeltaProduct_2 oracle on one head: q [T,dk], k [T,2,dk], v [T,2,dv], b [T,2], a [T] or None."""
+    e = lambda x: np.asarray(x, np.float64)[None, None]
+    h = None if h0 is None else e(h0)
+    o, hT = oracle_lib.deltaproduct2(e(q), e(k), e(v), None if a is None else e(a), e(b), h0=h)
+    return o[0, 0], hT[0, 0]
+
+
+def test_deltaproduct2_tracks_permutations_with_transposition_keys(oracle_lib):
+    """Paper App. C ("Consequences for CKDA and Gated DeltaProduct"): with
+    keys (e_i - e_j)/sqrt2, beta = 2, gate 1, no additive term and H_0 = I,
+    each Householder factor is the transposition (i j) and the state is the
+    permutation matrix of the running product -- two transpositions per token
+    here, so a token can apply a 3-cycle."""
+    n = 5
+    rng = np.random.default_rng(21)
+    T = 12
+    k = np.zeros((T, 2, n))
+    P = np.eye(n)
+    want = []
+    for t in range(T):
+        for j in range(2):
+            a, c = rng.choice(n, 2, replace=False)
+            k[t, j, a], k[t, j, c] = 1 / math.sqrt(2), -1 / math.sqrt(2)
+            Tr = np.eye(n)
+            Tr[[a, c]] = Tr[[c, a]]
+            P = Tr @ P                       # the first sub-step acts first
+        want.append(P.copy())
+    q = rng.standard_normal((T, n))
+    v = np.zeros((T, 2, n))            # no additive term; dv = n so that H_t is n x n
+    o, hT = dp2(oracle_lib, q, k, v, np.ones(T), np.full((T, 2), 2.0), np.eye(n))
+    assert np.max(np.abs(hT - want[-1])) < 1e-12
+    for t in range(T):
+        assert np.max(np.abs(o[t] - want[t].T @ q[t])) < 1e-12
+    # ungated (alpha = NULL) is the same as gate 1
+    o2, h2 = dp2(oracle_lib, q, k, v, None, np.full((T, 2), 2.0), np.eye(n))
+    assert np.array_equal(o, o2) and np.array_equal(hT, h2)
+
+
+def test_deltaproduct2_transition_is_the_gated_householder_product(oracle_lib):
+    """Gated DeltaProduct transition alpha_t (I - b2 k2 k2^T)(I - b1 k1 k1^T)
+    (paper App. C): with no additive term (v = 0) the state after T tokens is
+    the product of these dense matrices applied to H_0 (brute force)."""
+    rng = np.random.default_rng(22)
+    T, n, dv = 9, 4, 3
+    k = rng.standard_normal((T, 2, n))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    b = rng.uniform(0, 2, (T, 2))
+    a = rng.uniform(-1, 1, T)
+    h0 = rng.standard_normal((n, dv))
+    _, hT = dp2(oracle_lib, rng.standard_normal((T, n)), k, np.zeros((T, 2, dv)), a, b, h0)
+    H = h0.copy()
+    for t in range(T):
+        A = a[t] * (np.eye(n) - b[t, 1] * np.outer(k[t, 1], k[t, 1])) @ (np.eye(n) - b[t, 0] * np.outer(k[t, 0], k[t, 0]))
+        H = A @ H
+    assert np.max(np.abs(hT - H)) < 1e-12
+
+
+@pytest.mark.parametrize("which", [0, 1])
+def test_deltaproduct2_with_one_inactive_substep_is_the_delta_rule(oracle_lib, which):
+    """beta = 0 on one sub-step leaves a single delta-rule update per token:
+    the plain (pinned) recurrence with the scalar gate on every channel; with
+    the first sub-step inactive the gate still acts before the second."""
+    rng = np.random.default_rng(23 + which)
+    T, n, dv = 11, 5, 4
+    q = rng.standard_normal((T, n))
+    k = rng.standard_normal((T, 2, n))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((T, 2, dv))
+    b = rng.uniform(0, 2, (T, 2))
+    b[:, which] = 0.0
+    a = rng.uniform(-1, 1, T)
+    h0 = rng.standard_normal((n, dv))
+    o, hT = dp2(oracle_lib, q, k, v, a, b, h0)
+    act = 1 - which
+    o_p, h_p = run(oracle_lib, q, k[:, act], v[:, act], np.repeat(a[:, None], n, 1), b[:, act], h0)
+    assert np.max(np.abs(o - o_p)) < 1e-12 and np.max(np.abs(hT - h_p)) < 1e-12
+
+
+def test_deltaproduct2_decode_continues_the_forward(oracle_lib):
+    rng = np.random.default_rng(24)
+    T, n, dv = 6, 4, 3
+    q = rng.standard_normal((T, n))
+    k = rng.standard_normal((T, 2, n))
+    v = rng.standard_normal((T, 2, dv))
+    b = rng.uniform(0, 2, (T, 2))
+    a = rng.uniform(-1, 1, T)
+    o, hT = dp2(oracle_lib, q, k, v, a, b)
+    S = np.zeros((1, 1, n, dv))
+    for t in range(T):
+        ot = oracle_lib.deltaproduct2_decode(q[t][None, None], k[t][None, None], v[t][None, None],
+                                             np.asarray(a[t]).reshape(1, 1), b[t][None, None], S)
+        assert np.max(np.abs(ot[0, 0] - o[t])) < 1e-12
+    assert np.max(np.abs(S[0, 0] - hT)) < 1e-12
