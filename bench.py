@@ -7,8 +7,10 @@ and magnitude split, Gram matrices, triangular solve, state pass and output,
 plus the final state.  The decode step (256 sequences x 32 heads, d128, fp32
 state updated in place) is timed in the same run and reported under "decode",
 both again with the per-token prologue fused (gates from logits, unit-norm
-keys) under "fused_prologue", and the state-reduced workload (B2 H32 T32768,
-d_k 64 kept of 128 channels by an in-kernel gather) under "channel_gather".
+keys) under "fused_prologue", the state-reduced workload (B2 H32 T32768,
+d_k 64 kept of 128 channels by an in-kernel gather) under "channel_gather",
+and the comparators (scalar gate; DeltaProduct_2 forward and decode) under
+"comparators".
 
 Prints ONE JSON line.  `value` is tokens/s of the forward (a token is one
 (batch, position) across all heads), inputs resident in HBM: tokens per step
@@ -269,6 +271,31 @@ def main():
                                                 chunk=gw.chunk, workspace=gws, o=go, hT=ghT), gsteps)
     del pre, gd, gws, go
 
+    # ---- comparators on the bench shape: the scalar (Gated DeltaNet) gate and
+    # ungated DeltaProduct_2 (two delta-rule updates per token), and the
+    # DeltaProduct_2 decode step on the decode workload
+    log("[bench] comparators")
+    sg = {k: (None if v is None else v.to(dev)) for k, v in gen.make_scalar_gate_inputs(w).items()}
+    scalar_ms = timed(lambda: ck.chunk_fwd(sg["q"], sg["k"], sg["v"], sg["alpha"], sg["beta"], sg["h0"],
+                                           chunk=w.chunk, workspace=ws, o=o, hT=hT, fuse=ck.GATE_SCALAR), a.steps)
+    del sg
+    dp = {k: (None if v is None else v.to(dev)) for k, v in gen.make_dp2_inputs(w, gated=False).items()}
+    dws = torch.empty(ck.workspace_size(w.B, w.H, 2 * w.T, w.dk, w.dv, w.chunk, ck.DTYPE_BF16), dtype=torch.uint8,
+                      device=dev)
+    dp2_ms = timed(lambda: ck.deltaproduct2_fwd(dp["q"], dp["k"], dp["v"], dp["beta"], h0=dp["h0"], chunk=w.chunk,
+                                                workspace=dws, o=o, hT=hT), a.steps)
+    del dp, dws
+    dd = [{k: v.to(dev) for k, v in gen.dp2_decode_inputs(s, dec, gated=False).items() if v is not None}
+          for s in range(4)]
+    cnt = [0]
+
+    def dp2_dec():
+        x = dd[cnt[0] % 4]
+        cnt[0] += 1
+        ck.deltaproduct2_decode_step(x["q"], x["k"], x["v"], x["beta"], S, o=do)
+
+    dp2_dec_ms = timed(dp2_dec, a.decode_steps)
+
     # ---- reference device copy of the decode state's size (practical ceiling)
     src = torch.empty(dec.N * dec.H * dec.dk * dec.dv, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
@@ -326,6 +353,15 @@ def main():
             "total_GB_s": round(dec_gbs_total, 1),
             "frac_of_hbm_peak": round(dec_gbs_total / HBM_PEAK_GBS, 4),
             "device_copy_GB_s": round(copy_gbs, 1),
+        },
+        "comparators": {
+            "scalar_gate_forward_call_ms_mean": round(scalar_ms, 4),
+            "scalar_gate_tokens_per_s": round(tokens / (scalar_ms * 1e-3), 1),
+            "deltaproduct2_forward_call_ms_mean": round(dp2_ms, 4),
+            "deltaproduct2_tokens_per_s": round(tokens / (dp2_ms * 1e-3), 1),
+            "deltaproduct2_decode_ms_per_step": round(dp2_dec_ms, 4),
+            "deltaproduct2_decode_total_GB_s": round(
+                (state_bytes + dec.N * dec.H * (3 * dec.dk + 3 * dec.dv + 2) * 2) / (dp2_dec_ms * 1e-3) / 1e9, 1),
         },
         "channel_gather": {
             "workload": f"{gw.name} (d_k {gw.dk} kept of {dk_in})",

@@ -25,8 +25,10 @@ DTYPE_F32, DTYPE_BF16 = 0, 1
 STATUS = {0: "CKDA_OK", 1: "CKDA_ERR_NULL", 2: "CKDA_ERR_DIM", 3: "CKDA_ERR_UNSUPPORTED",
           4: "CKDA_ERR_ALIAS", 5: "CKDA_ERR_WORKSPACE", 6: "CKDA_ERR_HIP", 7: "CKDA_ERR_FLAGS"}
 FUSE_GATES, FUSE_NORM_K, FUSE_NORM_Q = 1, 2, 4       # CKDA_FUSE_*
+GATE_SCALAR = 8                                      # CKDA_GATE_SCALAR
 EXPORTS = ("ckda_chunk_fwd_workspace_size", "ckda_chunk_fwd", "ckda_chunk_fwd_timed", "ckda_chunk_fwd_ex",
            "ckda_chunk_fwd_gather", "ckda_decode_step", "ckda_decode_step_ex", "ckda_decode_step_gather",
+           "ckda_deltaproduct2_fwd", "ckda_deltaproduct2_decode_step",
            "ckda_status_string", "ckda_last_error", "ckda_abi_version")
 
 _lib = None
@@ -59,6 +61,10 @@ def lib() -> ctypes.CDLL:
         L.ckda_chunk_fwd_gather.restype = i
         L.ckda_decode_step_gather.argtypes = [vp] * 7 + [i] * 3 + [vp] + [i] * 4 + [vp]
         L.ckda_decode_step_gather.restype = i
+        L.ckda_deltaproduct2_fwd.argtypes = [vp] * 8 + [i] * 8 + [vp, sz, vp]
+        L.ckda_deltaproduct2_fwd.restype = i
+        L.ckda_deltaproduct2_decode_step.argtypes = [vp] * 7 + [i] * 6 + [vp]
+        L.ckda_deltaproduct2_decode_step.restype = i
         L.ckda_decode_step.argtypes = [vp] * 7 + [i] * 5 + [vp]
         L.ckda_decode_step.restype = i
         L.ckda_decode_step_ex.argtypes = [vp] * 7 + [i] * 6 + [vp]
@@ -191,4 +197,56 @@ def decode_step(q, k, v, alpha, beta, H, o=None, stream=None, fuse=0, idx=None):
         _check(lib().ckda_decode_step_ex(*ptrs, N, Hh, dk, dv, code, int(fuse), _stream(stream)))
     else:
         _check(lib().ckda_decode_step(*ptrs, N, Hh, dk, dv, code, _stream(stream)))
+    return o
+
+
+def deltaproduct2_fwd(q, k, v, beta, alpha=None, h0=None, chunk=64, workspace=None, o=None, hT=None,
+                      want_state=True, stream=None, fuse=0):
+    """DeltaProduct_2 forward (ckda_deltaproduct2_fwd): q [B,H,T,dk];
+    k [B,H,T,2,dk]; v [B,H,T,2,dv]; beta [B,H,T,2]; alpha [B,H,T] scalar
+    gates or None (ungated); h0 [B,H,dk,dv] fp32 or None.  Returns (o, hT)."""
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    ts = dict(q=q, k=k, v=v, beta=beta)
+    if alpha is not None:
+        ts["alpha"] = alpha
+    _require(ts, q.dtype)
+    if k.shape != (B, H, T, 2, dk) or v.shape != (B, H, T, 2, dv) or beta.shape != (B, H, T, 2) \
+            or (alpha is not None and alpha.shape != (B, H, T)):
+        raise ValueError("inconsistent DeltaProduct_2 shapes")
+    code = _dtype_code(q)
+    if h0 is not None:
+        _require(dict(h0=h0), torch.float32)
+    need = workspace_size(B, H, 2 * T, dk, dv, chunk, code)
+    if need == 0:
+        raise CkdaError(3, f"unsupported sizes dk={dk} dv={dv} chunk={chunk}")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if o is None:
+        o = torch.empty((B, H, T, dv), dtype=q.dtype, device=q.device)
+    if hT is None and want_state:
+        hT = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
+    _check(lib().ckda_deltaproduct2_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(h0), _ptr(o),
+                                        _ptr(hT), B, H, T, dk, dv, chunk, code, int(fuse), _ptr(workspace),
+                                        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return o, hT
+
+
+def deltaproduct2_decode_step(q, k, v, beta, H, alpha=None, o=None, stream=None, fuse=0):
+    """One DeltaProduct_2 decode step: q [N,Hh,dk]; k [N,Hh,2,dk];
+    v [N,Hh,2,dv]; beta [N,Hh,2]; alpha [N,Hh] or None; H fp32 in place."""
+    N, Hh, dk = q.shape
+    dv = v.shape[-1]
+    ts = dict(q=q, k=k, v=v, beta=beta)
+    if alpha is not None:
+        ts["alpha"] = alpha
+    _require(ts, q.dtype)
+    _require(dict(H=H), torch.float32)
+    if k.shape != (N, Hh, 2, dk) or v.shape != (N, Hh, 2, dv) or beta.shape != (N, Hh, 2):
+        raise ValueError("inconsistent DeltaProduct_2 shapes")
+    code = _dtype_code(q)
+    if o is None:
+        o = torch.empty((N, Hh, dv), dtype=q.dtype, device=q.device)
+    _check(lib().ckda_deltaproduct2_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(H), _ptr(o),
+                                                N, Hh, dk, dv, code, int(fuse), _stream(stream)))
     return o

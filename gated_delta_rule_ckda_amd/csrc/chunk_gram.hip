@@ -194,14 +194,14 @@ __global__ __launch_bounds__((GramCfg<T, DK, C>::NTH)) void chunk_gram_kernel(
 
   // ---- this thread's rows: signed gates (floored), keys, queries
   raw rl[16], rk[16], rq[16];   // gates (or, with the prologue, their logits) as loaded
-  // ld(x, i): this thread's channel pair of row 16 b + i of x
-  auto load_rows = [&](auto ld) __attribute__((always_inline)) {
+  // lda / ldk / ldq (i): this thread's channel pair of row 16 b + i
+  auto load_rows = [&](auto lda, auto ldk, auto ldq) __attribute__((always_inline)) {
     if (cv == C) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        rl[i] = ld(alpha, i);
-        rk[i] = ld(k, i);
-        rq[i] = ld(q, i);
+        rl[i] = lda(i);
+        rk[i] = ldk(i);
+        rq[i] = ldq(i);
       }
     } else {
       // ragged last chunk: rows past the end act as identity steps (gate 1, no key)
@@ -209,7 +209,7 @@ __global__ __launch_bounds__((GramCfg<T, DK, C>::NTH)) void chunk_gram_kernel(
       for (int i = 0; i < 16; ++i) {
         const int t = 16 * b + i;
         const int ii = min(t, cv - 1) - 16 * b;
-        const raw a = ld(alpha, ii), kk = ld(k, ii), qq = ld(q, ii);
+        const raw a = lda(ii), kk = ldk(ii), qq = ldq(ii);
         rl[i] = PR::ones();
         rk[i] = PR::zeros();
         rq[i] = PR::zeros();
@@ -221,20 +221,55 @@ __global__ __launch_bounds__((GramCfg<T, DK, C>::NTH)) void chunk_gram_kernel(
       }
     }
   };
+  const long long grow = row0 + 16 * b;   // global row of this thread's first row
+  auto pairs = [&](const T* x) __attribute__((always_inline)) {
+    const size_t base = (size_t)grow * DK + c0;
+    return [=](int i) __attribute__((always_inline)) { return PR::load(x + base + (size_t)i * DK); };
+  };
   if (act) {
-    if (PRO && gidx) {
-      // channel gather: rows of dk_in channels, this head's retained index
-      // set picks channels 2u and 2u + 1 (indices clamped into the row)
-      const int* hidx = gidx + (bh % nheads) * DK;
-      const int g0 = min(max(hidx[c0], 0), dk_in - 1), g1 = min(max(hidx[c0 + 1], 0), dk_in - 1);
-      const size_t rb = (size_t)(row0 + 16 * b) * dk_in;
-      load_rows([&](const T* x, int i) __attribute__((always_inline)) {
-        const T* r = x + rb + (size_t)i * dk_in;
-        return PR::pack(r[g0], r[g1]);
-      });
+    if constexpr (PRO) {
+      // one uniform branch per load mode, outside the row loops
+      if (gidx) {
+        // channel gather: rows of dk_in channels, this head's retained index
+        // set picks channels 2u and 2u + 1 (indices clamped into the row)
+        const int* hidx = gidx + (bh % nheads) * DK;
+        const int g0 = min(max(hidx[c0], 0), dk_in - 1), g1 = min(max(hidx[c0 + 1], 0), dk_in - 1);
+        const size_t rb = (size_t)grow * dk_in;
+        auto gat = [&](const T* x) __attribute__((always_inline)) {
+          return [=](int i) __attribute__((always_inline)) {
+            const T* r = x + rb + (size_t)i * dk_in;
+            return PR::pack(r[g0], r[g1]);
+          };
+        };
+        load_rows(gat(alpha), gat(k), gat(q));
+      } else if (flags & kProd2) {
+        // two sub-steps per token: rows 2 tau and 2 tau + 1 share query tau;
+        // the token's scalar gate (if any) acts on its first sub-step
+        const size_t qbase = (size_t)(grow >> 1) * DK + c0;
+        auto ldq = [=](int i) __attribute__((always_inline)) {
+          return PR::load(q + qbase + (size_t)(((grow & 1) + i) >> 1) * DK);
+        };
+        if (flags & kScalarGate) {
+          auto lda = [=](int i) __attribute__((always_inline)) {
+            const T g = alpha[(grow + i) >> 1];
+            return ((grow + i) & 1) ? PR::ones() : PR::pack(g, g);
+          };
+          load_rows(lda, pairs(k), ldq);
+        } else {
+          load_rows([](int) { return PR::ones(); }, pairs(k), ldq);
+        }
+      } else if (flags & kScalarGate) {
+        // one gate per token and head, the same on every channel
+        auto lda = [=](int i) __attribute__((always_inline)) {
+          const T g = alpha[grow + i];
+          return PR::pack(g, g);
+        };
+        load_rows(lda, pairs(k), pairs(q));
+      } else {
+        load_rows(pairs(alpha), pairs(k), pairs(q));
+      }
     } else {
-      const size_t base = (size_t)(row0 + 16 * b) * DK + c0;
-      load_rows([&](const T* x, int i) __attribute__((always_inline)) { return PR::load(x + base + (size_t)i * DK); });
+      load_rows(pairs(alpha), pairs(k), pairs(q));
     }
   }
   // Prologue gates: transformed after all loads are in flight, under one
@@ -245,9 +280,12 @@ __global__ __launch_bounds__((GramCfg<T, DK, C>::NTH)) void chunk_gram_kernel(
 #pragma unroll
     for (int i = 0; i < 16; ++i) ra[i] = graw{PR::lo(rl[i]), PR::hi(rl[i])};
     if (flags & kFuseGates) {
+      // rows that are identity steps keep gate 1: past a ragged end, and with
+      // two sub-steps per token the second one (or both, ungated)
+      const bool ones2 = (flags & kProd2) && !(flags & kScalarGate);
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const bool keep = 16 * b + i >= cv;
+        const bool keep = 16 * b + i >= cv || ((flags & kProd2) && (ones2 || ((grow + i) & 1)));
         ra[i] = graw{keep ? 1.f : practical_gate(ra[i][0]), keep ? 1.f : practical_gate(ra[i][1])};
       }
     }

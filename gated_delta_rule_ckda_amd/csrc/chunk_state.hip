@@ -63,7 +63,7 @@ struct StateCfg : ChunkGeom<T, DK, C> {
 template <typename T, int DK, int C, int NMW>
 __global__ __launch_bounds__((StateCfg<T, DK, C, NMW>::NTHREADS)) void chunk_state_kernel(
     const T* v, const float* __restrict__ h0, T* o, float* __restrict__ hT, const unsigned char* rec, int T_len,
-    int nchunks, int dv, int slices, int xcd_map) {
+    int nchunks, int dv, int slices, int xcd_map, int prod2) {
   using S = StateCfg<T, DK, C, NMW>;
   constexpr int RT = S::RT, RH = S::RH, KBN = S::KBN, KBC = S::KBC, NSET = S::NSET;
   constexpr int E = (int)sizeof(T);
@@ -95,8 +95,11 @@ __global__ __launch_bounds__((StateCfg<T, DK, C, NMW>::NTHREADS)) void chunk_sta
   if (matrix) {
     // ============================================================ matrix waves
     // This head's output rows as a range-checked buffer: stores to rows past
-    // the end of the sequence are dropped.
-    const __amdgpu_buffer_rsrc_t orsrc = make_rsrc(o + rowbase * dv, (uint32_t)((size_t)T_len * dv * E));
+    // the end of the sequence are dropped.  With two sub-steps per token
+    // (prod2 = 1) row r is sub-step r of the head and only odd rows are
+    // outputs, of token r / 2; even rows are dropped the same way.
+    const __amdgpu_buffer_rsrc_t orsrc =
+        make_rsrc(o + (rowbase >> prod2) * dv, (uint32_t)((size_t)(T_len >> prod2) * dv * E));
     const int col = slice * 16 * NMW + 16 * wave + r;       // this lane's value column
     const int ocol = slice * 16 * NMW + 16 * wave + 4 * g;  // first of its four output columns
     const long long sbase = (long long)bh * DK * dv;
@@ -211,7 +214,10 @@ __global__ __launch_bounds__((StateCfg<T, DK, C, NMW>::NTHREADS)) void chunk_sta
         for (int kb = 0; kb < KBC; ++kb) oacc[pt] = mma<T>(oacc[pt], ub[kb], mf[pt][kb]);   // + U^T M^T
         // lane (g, r) holds O^T rows 4 g .. 4 g + 3 of column r: four consecutive
         // value columns of output row 16 pt + r
-        store4<T>(orsrc, ((t0 + 16 * pt + r) * dv + ocol) * E, oacc[pt]);
+        const int orow = t0 + 16 * pt + r;
+        const int ooff = prod2 ? ((orow & 1) ? ((orow >> 1) * dv + ocol) * E : 0x7FFFFFF0)
+                               : (orow * dv + ocol) * E;
+        store4<T>(orsrc, ooff, oacc[pt]);
       }
       // H <- d . H + KR^T U
 #pragma unroll
@@ -341,7 +347,7 @@ hipError_t launch_state_nmw(const ChunkArgs& a, int nchunks) {
   const int xcd_map = (BH % 8 == 0) ? 1 : 0;
   hipLaunchKernelGGL((chunk_state_kernel<T, DK, C, NMW>), dim3((unsigned)wgs), dim3(S::NTHREADS), 0, a.stream,
                      (const T*)a.v, a.h0, (T*)a.o, a.hT, (const unsigned char*)a.workspace, a.T, nchunks, a.dv,
-                     slices, xcd_map);
+                     slices, xcd_map, (a.flags & kProd2) ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -54,6 +54,7 @@ bool overlap(const Range& a, const Range& b) {
 bool misaligned(const void* p) { return ((uintptr_t)p & 15u) != 0; }
 
 constexpr int kFuseAll = CKDA_FUSE_GATES | CKDA_FUSE_NORM_K | CKDA_FUSE_NORM_Q;
+constexpr int kFlagsAll = kFuseAll | CKDA_GATE_SCALAR;
 constexpr int kMaxDkIn = 65536;   // row width of gathered inputs
 
 }  // namespace
@@ -88,76 +89,87 @@ size_t ckda_chunk_fwd_workspace_size(int B, int H, int T, int dk, int dv, int ch
   return bytes == 0 ? 256 : bytes;  // never 0 for valid sizes: 0 means "invalid"
 }
 
-static int chunk_fwd_impl(const void* q, const void* k, const void* v, const void* alpha, const void* beta,
-                          const float* h0, void* o, float* hT, int B, int H, int T, int dk, int dv, int chunk,
-                          int dtype, int flags, void* workspace, size_t workspace_bytes, void* stream,
-                          void* const ev[3], const int* gidx = nullptr, int dk_in = 0) {
-  if ((flags & ~kFuseAll) != 0)
-    return fail(CKDA_ERR_FLAGS, "ckda_chunk_fwd: flags 0x%x has bits outside CKDA_FUSE_* (0x%x)", flags, kFuseAll);
+// Shared checks and dispatch of the chunked forward entry points.  `flags`
+// holds public bits only; prod2 selects DeltaProduct_2 (k, v, beta hold 2 T
+// sub-steps, q, o and a scalar alpha T tokens; alpha may be NULL for no
+// gate).  `fn` names the entry point in error messages.
+static int chunk_fwd_impl(const char* fn, const void* q, const void* k, const void* v, const void* alpha,
+                          const void* beta, const float* h0, void* o, float* hT, int B, int H, int T, int dk, int dv,
+                          int chunk, int dtype, int flags, void* workspace, size_t workspace_bytes, void* stream,
+                          void* const ev[3], const int* gidx = nullptr, int dk_in = 0, bool prod2 = false) {
+  if ((flags & ~kFlagsAll) != 0)
+    return fail(CKDA_ERR_FLAGS, "%s: flags 0x%x has bits outside CKDA_FUSE_* and CKDA_GATE_SCALAR (0x%x)", fn, flags,
+                kFlagsAll);
+  const bool scalar = (flags & CKDA_GATE_SCALAR) != 0;
+  if (gidx && scalar)
+    return fail(CKDA_ERR_UNSUPPORTED, "%s: CKDA_GATE_SCALAR does not combine with a channel gather", fn);
   if (!gidx) dk_in = dk;
   if (dk_in < 1 || dk_in > kMaxDkIn)
-    return fail(CKDA_ERR_DIM, "ckda_chunk_fwd: dk_in=%d outside 1..%d", dk_in, kMaxDkIn);
-  if (B < 0 || H < 0 || T < 0)
-    return fail(CKDA_ERR_DIM, "ckda_chunk_fwd: negative size (B=%d H=%d T=%d)", B, H, T);
+    return fail(CKDA_ERR_DIM, "%s: dk_in=%d outside 1..%d", fn, dk_in, kMaxDkIn);
+  if (B < 0 || H < 0 || T < 0 || (prod2 && T > INT32_MAX / 2))
+    return fail(CKDA_ERR_DIM, "%s: negative or too large size (B=%d H=%d T=%d)", fn, B, H, T);
   if (!supported_dtype(dtype))
-    return fail(CKDA_ERR_UNSUPPORTED, "ckda_chunk_fwd: dtype %d is not F32(0) or BF16(1)", dtype);
+    return fail(CKDA_ERR_UNSUPPORTED, "%s: dtype %d is not F32(0) or BF16(1)", fn, dtype);
   if (!supported_dim(dk) || !supported_dim(dv))
-    return fail(CKDA_ERR_UNSUPPORTED, "ckda_chunk_fwd: dk=%d dv=%d (supported: 16, 32, 64, 128)", dk, dv);
+    return fail(CKDA_ERR_UNSUPPORTED, "%s: dk=%d dv=%d (supported: 16, 32, 64, 128)", fn, dk, dv);
   if (!supported_chunk(chunk))
-    return fail(CKDA_ERR_UNSUPPORTED, "ckda_chunk_fwd: chunk=%d (supported: 16, 32, 64)", chunk);
+    return fail(CKDA_ERR_UNSUPPORTED, "%s: chunk=%d (supported: 16, 32, 64)", fn, chunk);
   const size_t BH = (size_t)B * H;
   const size_t es = dtype_bytes(dtype);
-  const size_t nk = BH * T * dk_in, nv = BH * T * dv, nb = BH * T, ns = BH * dk * dv;
+  const int rows = prod2 ? 2 * T : T;   // delta-rule steps per (batch, head)
+  const size_t nq = BH * T * dk_in, nk = BH * rows * dk_in, nv = BH * rows * dv, nb = BH * rows;
+  const size_t na = scalar ? BH * T : nk, no = BH * T * dv, ns = BH * dk * dv;
   if (BH == 0) return ok();
-  if (T > 0 && (!q || !k || !v || !alpha || !beta || !o))
-    return fail(CKDA_ERR_NULL, "ckda_chunk_fwd: q, k, v, alpha, beta and o are required");
+  if (T > 0 && (!q || !k || !v || !beta || !o || (!alpha && !prod2)))
+    return fail(CKDA_ERR_NULL, "%s: q, k, v, %sbeta and o are required", fn, prod2 ? "" : "alpha, ");
   if (T == 0 && !hT) return ok();
-  const size_t need = ckda_chunk_fwd_workspace_size(B, H, T, dk, dv, chunk, dtype);
-  const size_t nchunks = BH * (((size_t)T + chunk - 1) / chunk);
+  const size_t need = ckda_chunk_fwd_workspace_size(B, H, rows, dk, dv, chunk, dtype);
+  const size_t nchunks = BH * (((size_t)rows + chunk - 1) / chunk);
   if (nchunks > (size_t)INT32_MAX)
-    return fail(CKDA_ERR_DIM, "ckda_chunk_fwd: %zu chunks exceed the launch grid", nchunks);
+    return fail(CKDA_ERR_DIM, "%s: %zu chunks exceed the launch grid", fn, nchunks);
   if (BH * ((size_t)dv / 16) > (size_t)INT32_MAX)
-    return fail(CKDA_ERR_DIM, "ckda_chunk_fwd: B*H too large");
-  if (((size_t)T + 64) * dv * es > (size_t)INT32_MAX)
-    return fail(CKDA_ERR_DIM, "ckda_chunk_fwd: T=%d too long: one head's output must stay below 2 GiB", T);
-  const size_t head_records = (((size_t)T + chunk - 1) / chunk) * ckda::chunk_record_layout(dk, chunk, dtype).bytes;
+    return fail(CKDA_ERR_DIM, "%s: B*H too large", fn);
+  if (((size_t)rows + 64) * dv * es > (size_t)INT32_MAX)
+    return fail(CKDA_ERR_DIM, "%s: T=%d too long: one head's values and outputs must stay below 2 GiB", fn, T);
+  const size_t head_records = (((size_t)rows + chunk - 1) / chunk) * ckda::chunk_record_layout(dk, chunk, dtype).bytes;
   if (head_records > (size_t)INT32_MAX)
-    return fail(CKDA_ERR_DIM, "ckda_chunk_fwd: T=%d too long: one head's chunk records must stay below 2 GiB", T);
+    return fail(CKDA_ERR_DIM, "%s: T=%d too long: one head's chunk records must stay below 2 GiB", fn, T);
   if (T > 0) {
-    if (!workspace) return fail(CKDA_ERR_WORKSPACE, "ckda_chunk_fwd: workspace is NULL");
+    if (!workspace) return fail(CKDA_ERR_WORKSPACE, "%s: workspace is NULL", fn);
     if (workspace_bytes < need)
-      return fail(CKDA_ERR_WORKSPACE, "ckda_chunk_fwd: workspace of %zu bytes, need %zu", workspace_bytes, need);
+      return fail(CKDA_ERR_WORKSPACE, "%s: workspace of %zu bytes, need %zu", fn, workspace_bytes, need);
     if (((uintptr_t)workspace & 255u) != 0)
-      return fail(CKDA_ERR_WORKSPACE, "ckda_chunk_fwd: workspace not 256-byte aligned");
+      return fail(CKDA_ERR_WORKSPACE, "%s: workspace not 256-byte aligned", fn);
   }
   const void* ptrs[] = {q, k, v, alpha, beta, h0, o, hT, gidx};
   const char* names[] = {"q", "k", "v", "alpha", "beta", "h0", "o", "hT", "idx"};
   for (int i = 0; i < 9; ++i)
     if (ptrs[i] && misaligned(ptrs[i]))
-      return fail(CKDA_ERR_DIM, "ckda_chunk_fwd: %s is not 16-byte aligned", names[i]);
+      return fail(CKDA_ERR_DIM, "%s: %s is not 16-byte aligned", fn, names[i]);
 
-  const Range in[] = {range("q", q, T ? nk * es : 0),     range("k", k, T ? nk * es : 0),
-                      range("v", v, T ? nv * es : 0),     range("alpha", alpha, T ? nk * es : 0),
+  const Range in[] = {range("q", q, T ? nq * es : 0),     range("k", k, T ? nk * es : 0),
+                      range("v", v, T ? nv * es : 0),     range("alpha", alpha, T && alpha ? na * es : 0),
                       range("beta", beta, T ? nb * es : 0), range("h0", h0, h0 ? ns * 4 : 0),
                       range("idx", gidx, gidx ? (size_t)H * dk * 4 : 0)};
-  const Range ro = range("o", o, T ? nv * es : 0);
+  const Range ro = range("o", o, T ? no * es : 0);
   const Range rh = range("hT", hT, hT ? ns * 4 : 0);
   const Range rw = range("workspace", workspace, T ? need : 0);
   for (const Range& r : in) {
-    if (overlap(ro, r)) return fail(CKDA_ERR_ALIAS, "ckda_chunk_fwd: o overlaps %s", r.name);
-    if (overlap(rw, r)) return fail(CKDA_ERR_ALIAS, "ckda_chunk_fwd: workspace overlaps %s", r.name);
+    if (overlap(ro, r)) return fail(CKDA_ERR_ALIAS, "%s: o overlaps %s", fn, r.name);
+    if (overlap(rw, r)) return fail(CKDA_ERR_ALIAS, "%s: workspace overlaps %s", fn, r.name);
     const bool same_state = hT && h0 && (const void*)hT == (const void*)h0 && r.lo == (uintptr_t)h0;
-    if (!same_state && overlap(rh, r)) return fail(CKDA_ERR_ALIAS, "ckda_chunk_fwd: hT overlaps %s", r.name);
+    if (!same_state && overlap(rh, r)) return fail(CKDA_ERR_ALIAS, "%s: hT overlaps %s", fn, r.name);
   }
-  if (overlap(ro, rh)) return fail(CKDA_ERR_ALIAS, "ckda_chunk_fwd: o overlaps hT");
+  if (overlap(ro, rh)) return fail(CKDA_ERR_ALIAS, "%s: o overlaps hT", fn);
   if (overlap(rw, ro) || overlap(rw, rh))
-    return fail(CKDA_ERR_ALIAS, "ckda_chunk_fwd: workspace overlaps an output");
+    return fail(CKDA_ERR_ALIAS, "%s: workspace overlaps an output", fn);
 
-  ckda::ChunkArgs a{q, k, v, alpha, beta, h0, o, hT, B, H, T, dk, dv, chunk, dtype, flags, workspace,
+  ckda::ChunkArgs a{q, k, v, alpha, beta, h0, o, hT, B, H, rows, dk, dv, chunk, dtype,
+                    flags | (prod2 ? ckda::kProd2 : 0), workspace,
                     (hipStream_t)stream, {(hipEvent_t)ev[0], (hipEvent_t)ev[1], (hipEvent_t)ev[2]}, gidx, dk_in};
   hipError_t e = ckda::launch_chunk_fwd(a);
   if (e != hipSuccess)
-    return fail(CKDA_ERR_HIP, "ckda_chunk_fwd: launch failed: %s", hipGetErrorString(e));
+    return fail(CKDA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
   return ok();
 }
 
@@ -166,7 +178,7 @@ int ckda_chunk_fwd(const void* q, const void* k, const void* v, const void* alph
                    int B, int H, int T, int dk, int dv, int chunk, int dtype,
                    void* workspace, size_t workspace_bytes, void* stream) {
   void* const none[3] = {nullptr, nullptr, nullptr};
-  return chunk_fwd_impl(q, k, v, alpha, beta, h0, o, hT, B, H, T, dk, dv, chunk, dtype, 0, workspace,
+  return chunk_fwd_impl("ckda_chunk_fwd", q, k, v, alpha, beta, h0, o, hT, B, H, T, dk, dv, chunk, dtype, 0, workspace,
                         workspace_bytes, stream, none);
 }
 
@@ -175,7 +187,7 @@ int ckda_chunk_fwd_ex(const void* q, const void* k, const void* v, const void* a
                       int B, int H, int T, int dk, int dv, int chunk, int dtype, int flags,
                       void* workspace, size_t workspace_bytes, void* stream) {
   void* const none[3] = {nullptr, nullptr, nullptr};
-  return chunk_fwd_impl(q, k, v, alpha, beta, h0, o, hT, B, H, T, dk, dv, chunk, dtype, flags, workspace,
+  return chunk_fwd_impl("ckda_chunk_fwd", q, k, v, alpha, beta, h0, o, hT, B, H, T, dk, dv, chunk, dtype, flags, workspace,
                         workspace_bytes, stream, none);
 }
 
@@ -185,8 +197,21 @@ int ckda_chunk_fwd_gather(const void* q, const void* k, const void* v, const voi
                           int flags, void* workspace, size_t workspace_bytes, void* stream) {
   if (!idx && B > 0 && H > 0) return fail(CKDA_ERR_NULL, "ckda_chunk_fwd: idx is required");
   void* const none[3] = {nullptr, nullptr, nullptr};
-  return chunk_fwd_impl(q, k, v, alpha, beta, h0, o, hT, B, H, T, dk, dv, chunk, dtype, flags, workspace,
+  return chunk_fwd_impl("ckda_chunk_fwd", q, k, v, alpha, beta, h0, o, hT, B, H, T, dk, dv, chunk, dtype, flags, workspace,
                         workspace_bytes, stream, none, idx, dk_in);
+}
+
+int ckda_deltaproduct2_fwd(const void* q, const void* k, const void* v, const void* alpha,
+                           const void* beta, const float* h0, void* o, float* hT,
+                           int B, int H, int T, int dk, int dv, int chunk, int dtype, int flags,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  if ((flags & ~kFuseAll) != 0)
+    return fail(CKDA_ERR_FLAGS, "ckda_deltaproduct2_fwd: flags 0x%x has bits outside CKDA_FUSE_* (0x%x)", flags,
+                kFuseAll);
+  void* const none[3] = {nullptr, nullptr, nullptr};
+  const int f = flags | (alpha ? CKDA_GATE_SCALAR : 0);
+  return chunk_fwd_impl("ckda_deltaproduct2_fwd", q, k, v, alpha, beta, h0, o, hT, B, H, T, dk, dv, chunk, dtype, f,
+                        workspace, workspace_bytes, stream, none, nullptr, 0, true);
 }
 
 int ckda_chunk_fwd_timed(const void* q, const void* k, const void* v, const void* alpha,
@@ -195,56 +220,74 @@ int ckda_chunk_fwd_timed(const void* q, const void* k, const void* v, const void
                          void* workspace, size_t workspace_bytes, void* stream,
                          void* ev_start, void* ev_mid, void* ev_end) {
   void* const ev[3] = {ev_start, ev_mid, ev_end};
-  return chunk_fwd_impl(q, k, v, alpha, beta, h0, o, hT, B, H, T, dk, dv, chunk, dtype, 0, workspace,
+  return chunk_fwd_impl("ckda_chunk_fwd", q, k, v, alpha, beta, h0, o, hT, B, H, T, dk, dv, chunk, dtype, 0, workspace,
                         workspace_bytes, stream, ev);
 }
 
-static int decode_impl(const void* q, const void* k, const void* v, const void* alpha, const void* beta,
-                       float* H_inout, void* o, int N, int H, int dk, int dv, int dtype, int flags, void* stream,
-                       const int* gidx = nullptr, int dk_in = 0) {
-  if ((flags & ~kFuseAll) != 0)
-    return fail(CKDA_ERR_FLAGS, "ckda_decode_step: flags 0x%x has bits outside CKDA_FUSE_* (0x%x)", flags, kFuseAll);
+static int decode_impl(const char* fn, const void* q, const void* k, const void* v, const void* alpha,
+                       const void* beta, float* H_inout, void* o, int N, int H, int dk, int dv, int dtype, int flags,
+                       void* stream, const int* gidx = nullptr, int dk_in = 0, bool prod2 = false) {
+  if ((flags & ~kFlagsAll) != 0)
+    return fail(CKDA_ERR_FLAGS, "%s: flags 0x%x has bits outside CKDA_FUSE_* and CKDA_GATE_SCALAR (0x%x)", fn, flags,
+                kFlagsAll);
+  const bool scalar = (flags & CKDA_GATE_SCALAR) != 0;
+  if (gidx && scalar)
+    return fail(CKDA_ERR_UNSUPPORTED, "%s: CKDA_GATE_SCALAR does not combine with a channel gather", fn);
   if (!gidx) dk_in = dk;
   if (dk_in < 1 || dk_in > kMaxDkIn)
-    return fail(CKDA_ERR_DIM, "ckda_decode_step: dk_in=%d outside 1..%d", dk_in, kMaxDkIn);
-  if (N < 0 || H < 0) return fail(CKDA_ERR_DIM, "ckda_decode_step: negative size (N=%d H=%d)", N, H);
+    return fail(CKDA_ERR_DIM, "%s: dk_in=%d outside 1..%d", fn, dk_in, kMaxDkIn);
+  if (N < 0 || H < 0) return fail(CKDA_ERR_DIM, "%s: negative size (N=%d H=%d)", fn, N, H);
   if (!supported_dtype(dtype))
-    return fail(CKDA_ERR_UNSUPPORTED, "ckda_decode_step: dtype %d is not F32(0) or BF16(1)", dtype);
+    return fail(CKDA_ERR_UNSUPPORTED, "%s: dtype %d is not F32(0) or BF16(1)", fn, dtype);
   if (!supported_dim(dk) || !supported_dim(dv))
-    return fail(CKDA_ERR_UNSUPPORTED, "ckda_decode_step: dk=%d dv=%d (supported: 16, 32, 64, 128)", dk, dv);
+    return fail(CKDA_ERR_UNSUPPORTED, "%s: dk=%d dv=%d (supported: 16, 32, 64, 128)", fn, dk, dv);
   const size_t NH = (size_t)N * H;
   if (NH == 0) return ok();
-  if (NH > (size_t)INT32_MAX) return fail(CKDA_ERR_DIM, "ckda_decode_step: N*H exceeds the launch grid");
-  if (!q || !k || !v || !alpha || !beta || !H_inout || !o)
-    return fail(CKDA_ERR_NULL, "ckda_decode_step: every pointer is required");
+  if (NH > (size_t)INT32_MAX) return fail(CKDA_ERR_DIM, "%s: N*H exceeds the launch grid", fn);
+  if (!q || !k || !v || (!alpha && !prod2) || !beta || !H_inout || !o)
+    return fail(CKDA_ERR_NULL, "%s: every pointer%s is required", fn, prod2 ? " but alpha" : "");
   const void* ptrs[] = {q, k, v, alpha, beta, H_inout, o, gidx};
   const char* names[] = {"q", "k", "v", "alpha", "beta", "H_inout", "o", "idx"};
   for (int i = 0; i < 8; ++i)
     if (ptrs[i] && misaligned(ptrs[i]))
-      return fail(CKDA_ERR_DIM, "ckda_decode_step: %s is not 16-byte aligned", names[i]);
+      return fail(CKDA_ERR_DIM, "%s: %s is not 16-byte aligned", fn, names[i]);
   const size_t es = dtype_bytes(dtype);
-  const Range in[] = {range("q", q, NH * dk_in * es), range("k", k, NH * dk_in * es), range("v", v, NH * dv * es),
-                      range("alpha", alpha, NH * dk_in * es), range("beta", beta, NH * es),
+  const size_t sub = prod2 ? 2 : 1;   // delta sub-steps per token
+  const Range in[] = {range("q", q, NH * dk_in * es), range("k", k, sub * NH * dk_in * es),
+                      range("v", v, sub * NH * dv * es),
+                      range("alpha", alpha, alpha ? (scalar ? NH : NH * dk_in) * es : 0), range("beta", beta, sub * NH * es),
                       range("idx", gidx, gidx ? (size_t)H * dk * 4 : 0)};
   const Range rs = range("H_inout", H_inout, NH * dk * dv * 4);
   const Range ro = range("o", o, NH * dv * es);
   for (const Range& r : in) {
-    if (overlap(ro, r)) return fail(CKDA_ERR_ALIAS, "ckda_decode_step: o overlaps %s", r.name);
-    if (overlap(rs, r)) return fail(CKDA_ERR_ALIAS, "ckda_decode_step: H_inout overlaps %s", r.name);
+    if (overlap(ro, r)) return fail(CKDA_ERR_ALIAS, "%s: o overlaps %s", fn, r.name);
+    if (overlap(rs, r)) return fail(CKDA_ERR_ALIAS, "%s: H_inout overlaps %s", fn, r.name);
   }
-  if (overlap(ro, rs)) return fail(CKDA_ERR_ALIAS, "ckda_decode_step: o overlaps H_inout");
+  if (overlap(ro, rs)) return fail(CKDA_ERR_ALIAS, "%s: o overlaps H_inout", fn);
 
-  ckda::DecodeArgs a{q, k, v, alpha, beta, H_inout, o, N, H, dk, dv, dtype, flags, (hipStream_t)stream, gidx, dk_in};
+  ckda::DecodeArgs a{q, k, v, alpha, beta, H_inout, o, N, H, dk, dv, dtype, flags | (prod2 ? ckda::kProd2 : 0),
+                     (hipStream_t)stream, gidx, dk_in};
   hipError_t e = ckda::launch_decode(a);
   if (e != hipSuccess)
-    return fail(CKDA_ERR_HIP, "ckda_decode_step: launch failed: %s", hipGetErrorString(e));
+    return fail(CKDA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
   return ok();
 }
 
 int ckda_decode_step(const void* q, const void* k, const void* v, const void* alpha,
                      const void* beta, float* H_inout, void* o,
                      int N, int H, int dk, int dv, int dtype, void* stream) {
-  return decode_impl(q, k, v, alpha, beta, H_inout, o, N, H, dk, dv, dtype, 0, stream);
+  return decode_impl("ckda_decode_step", q, k, v, alpha, beta, H_inout, o, N, H, dk, dv, dtype, 0, stream);
+}
+
+int ckda_deltaproduct2_decode_step(const void* q, const void* k, const void* v, const void* alpha,
+                                   const void* beta, float* H_inout, void* o,
+                                   int N, int H, int dk, int dv, int dtype, int flags, void* stream) {
+  if ((flags & ~kFuseAll) != 0)
+    return fail(CKDA_ERR_FLAGS, "ckda_deltaproduct2_decode_step: flags 0x%x has bits outside CKDA_FUSE_* (0x%x)",
+                flags, kFuseAll);
+  const int f = flags | (alpha ? CKDA_GATE_SCALAR : 0);
+  return decode_impl("ckda_deltaproduct2_decode_step", q, k, v, alpha, beta, H_inout, o, N, H, dk, dv, dtype, f,
+                     stream, nullptr, 0, true);
 }
 
 int ckda_decode_step_gather(const void* q, const void* k, const void* v, const void* alpha,
@@ -252,13 +295,13 @@ int ckda_decode_step_gather(const void* q, const void* k, const void* v, const v
                             int N, int H, int dk_in, const int* idx, int dk, int dv, int dtype, int flags,
                             void* stream) {
   if (!idx && N > 0 && H > 0) return fail(CKDA_ERR_NULL, "ckda_decode_step: idx is required");
-  return decode_impl(q, k, v, alpha, beta, H_inout, o, N, H, dk, dv, dtype, flags, stream, idx, dk_in);
+  return decode_impl("ckda_decode_step", q, k, v, alpha, beta, H_inout, o, N, H, dk, dv, dtype, flags, stream, idx, dk_in);
 }
 
 int ckda_decode_step_ex(const void* q, const void* k, const void* v, const void* alpha,
                         const void* beta, float* H_inout, void* o,
                         int N, int H, int dk, int dv, int dtype, int flags, void* stream) {
-  return decode_impl(q, k, v, alpha, beta, H_inout, o, N, H, dk, dv, dtype, flags, stream);
+  return decode_impl("ckda_decode_step", q, k, v, alpha, beta, H_inout, o, N, H, dk, dv, dtype, flags, stream);
 }
 
 }  // extern "C"

@@ -55,6 +55,7 @@ template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) {
 // (frame "Backup: practical gates differ from exact theoretical endpoints")
 // and unit-norm keys and queries.
 constexpr int kFuseGates = 1, kFuseNormK = 2, kFuseNormQ = 4;   // as CKDA_FUSE_GATES, _NORM_K, _NORM_Q
+constexpr int kScalarGate = 8;   // as CKDA_GATE_SCALAR: one gate per token and head
 constexpr float kUnitGuard = 1e-6f;                 // x / sqrt(sum x^2 + guard)
 constexpr float kGateFloor = 0.006737946999085467f;  // e^-5: log|alpha| >= -5
 
@@ -255,7 +256,6 @@ template <> __device__ __forceinline__ void store4<bf16_t>(__amdgpu_buffer_rsrc_
   __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])}, r, byte_off, 0, 0);
 }
 
-// Wave-wide sum (wave64) via cross-lane shuffles.
 // Sum over aligned groups of N lanes (N = 2 .. 64), every lane of a group
 // receiving its group's sum; all lanes of the wave must be active.  Within a
 // 16-lane row the steps are DPP moves (swap neighbours, swap pairs, mirror
@@ -287,6 +287,7 @@ template <int N> __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
+// Wave-wide sum (wave64) via cross-lane shuffles.
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);

@@ -9,6 +9,11 @@
 
 namespace ckda {
 
+// Launch flag beside the public CKDA_FUSE_* / CKDA_GATE_SCALAR bits: two
+// delta-rule sub-steps per token (DeltaProduct_2; rows of k, v, beta are
+// sub-steps, rows of q, o and of a scalar alpha are tokens).
+constexpr int kProd2 = 1 << 16;
+
 struct DecodeArgs {
   const void *q, *k, *v, *alpha, *beta;
   float* H_inout;

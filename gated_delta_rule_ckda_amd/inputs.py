@@ -18,7 +18,9 @@ beta in [0,2], "Complex KDA" Sec. 3):
                        alpha~U[-1,1], beta~U[0,2], fp32 state ~N(0,0.1)
 
 The fused prologue's inputs (make_logit_inputs, decode_logit_inputs) are
-logits and unnormalised vectors of the same shapes.
+logits and unnormalised vectors of the same shapes; the comparators' inputs
+(make_scalar_gate_inputs: one gate per token and head; make_dp2_inputs and
+dp2_decode_inputs: two keys, values and betas per token) follow the same laws.
 
 N(mu, s) means standard deviation s.  Draw order per workload: q, k, v, alpha,
 beta, h0, each as a full C-order float32 array from numpy's PCG64 stream
@@ -232,6 +234,59 @@ def gather_channels(x: torch.Tensor, idx: torch.Tensor) -> torch.Tensor:
     """x[b, h, ..., idx[h]] for x [B, H, ..., dk_in] (CPU; for the oracle side)."""
     out = [x[:, h][..., idx[h].long()] for h in range(x.shape[1])]
     return torch.stack(out, dim=1).contiguous()
+
+
+def make_scalar_gate_inputs(w: Workload):
+    """Inputs with one gate per token and head (Gated DeltaNet's scalar gate):
+    dict(q, k, v, alpha [B,H,T], beta, h0); laws as make_inputs with the gate
+    law applied to the [B,H,T] scalars.  Draw order: q, k, v, alpha, beta, h0."""
+    rng = np.random.default_rng(w.seed)
+    B, H, T, dk, dv = w.B, w.H, w.T, w.dk, w.dv
+    q = rng.standard_normal((B, H, T, dk), dtype=np.float32)
+    k = _normalise(rng.standard_normal((B, H, T, dk), dtype=np.float32))
+    v = rng.standard_normal((B, H, T, dv), dtype=np.float32)
+    a, b = _gates(rng, w.gates, (B, H, T), (B, H, T))
+    h0 = _h0(rng, w)
+    return dict(q=_to(q, w.dtype), k=_to(k, w.dtype), v=_to(v, w.dtype),
+                alpha=_to(a, w.dtype), beta=_to(b, w.dtype), h0=h0)
+
+
+def make_dp2_inputs(w: Workload, gated: bool = True):
+    """DeltaProduct_2 inputs: dict(q [B,H,T,dk], k [B,H,T,2,dk] unit rows,
+    v [B,H,T,2,dv], alpha [B,H,T] scalar gates (None when not gated),
+    beta [B,H,T,2], h0).  Gate law w.gates on the scalars and on beta.
+    Draw order: q, k, v, alpha, beta, h0."""
+    rng = np.random.default_rng(w.seed)
+    B, H, T, dk, dv = w.B, w.H, w.T, w.dk, w.dv
+    q = rng.standard_normal((B, H, T, dk), dtype=np.float32)
+    k = _normalise(rng.standard_normal((B, H, T, 2, dk), dtype=np.float32))
+    v = rng.standard_normal((B, H, T, 2, dv), dtype=np.float32)
+    a, b = _gates(rng, w.gates, (B, H, T), (B, H, T, 2))
+    h0 = _h0(rng, w)
+    return dict(q=_to(q, w.dtype), k=_to(k, w.dtype), v=_to(v, w.dtype),
+                alpha=_to(a, w.dtype) if gated else None, beta=_to(b, w.dtype), h0=h0)
+
+
+def _h0(rng, w: Workload):
+    if w.h0 == "normal":
+        return torch.from_numpy(np.float32(0.1) * rng.standard_normal((w.B, w.H, w.dk, w.dv), dtype=np.float32))
+    if w.h0 == "zero":
+        return torch.zeros((w.B, w.H, w.dk, w.dv), dtype=torch.float32)
+    return None
+
+
+def dp2_decode_inputs(step: int, d: DecodeWorkload = DECODE, N=None, H=None, gated: bool = True):
+    """DeltaProduct_2 decode-step inputs: q [N,H,dk], k [N,H,2,dk] unit rows,
+    v [N,H,2,dv], beta [N,H,2] ~ U[0,2], alpha [N,H] ~ U[-1,1] (or None)."""
+    N = d.N if N is None else N
+    H = d.H if H is None else H
+    rng = np.random.default_rng(d.step_seed + step)
+    q = rng.standard_normal((N, H, d.dk), dtype=np.float32)
+    k = _normalise(rng.standard_normal((N, H, 2, d.dk), dtype=np.float32))
+    v = rng.standard_normal((N, H, 2, d.dv), dtype=np.float32)
+    a, b = _gates(rng, "ckda_uniform", (N, H), (N, H, 2))
+    return dict(q=_to(q, d.dtype), k=_to(k, d.dtype), v=_to(v, d.dtype),
+                alpha=_to(a, d.dtype) if gated else None, beta=_to(b, d.dtype))
 
 
 def decode_state(d: DecodeWorkload = DECODE, N=None, H=None):

@@ -63,7 +63,7 @@ typedef enum {
   CKDA_ERR_ALIAS = 4,       /* an output overlaps an input it may not overlap */
   CKDA_ERR_WORKSPACE = 5,   /* workspace missing, too small or misaligned */
   CKDA_ERR_HIP = 6,         /* the HIP runtime reported an error at launch */
-  CKDA_ERR_FLAGS = 7        /* prologue flags hold bits outside CKDA_FUSE_* */
+  CKDA_ERR_FLAGS = 7        /* flags hold bits outside CKDA_FUSE_* / CKDA_GATE_SCALAR */
 } ckda_status_t;
 
 /* Per-token prologue steps of the *_ex entry points (bitwise OR; 0 = none,
@@ -89,6 +89,14 @@ typedef enum {
 #define CKDA_FUSE_GATES 1
 #define CKDA_FUSE_NORM_K 2
 #define CKDA_FUSE_NORM_Q 4
+
+/* Gate shape flag of ckda_chunk_fwd_ex and ckda_decode_step_ex: alpha holds
+ * ONE gate per token and head ([B, H, T] / [N, H]) applied to every key
+ * channel -- the scalar gate of Gated DeltaNet, a comparator of the "Complex
+ * KDA" paper (Sec. 2, scalar gates commute with every matrix and leave the
+ * transition symmetric).  Combines with CKDA_FUSE_GATES (the scalar is then a
+ * logit) and the norm flags; not with a channel gather. */
+#define CKDA_GATE_SCALAR 8
 
 /* Bytes of device workspace ckda_chunk_fwd needs for these sizes, or 0 when
  * the sizes are invalid or unsupported (ckda_chunk_fwd then reports why).
@@ -150,8 +158,8 @@ int ckda_chunk_fwd_timed(const void* q, const void* k, const void* v, const void
  * to the inputs first: alpha and beta may be logits, k and q are normalised
  * per token.  The prologue's results are not written anywhere.  Same
  * arguments, layouts, aliasing rules and workspace as ckda_chunk_fwd; flags
- * = 0 gives ckda_chunk_fwd's results exactly.  Returns CKDA_ERR_FLAGS for
- * bits outside CKDA_FUSE_*. */
+ * = 0 gives ckda_chunk_fwd's results exactly.  With CKDA_GATE_SCALAR alpha
+ * is [B, H, T].  Returns CKDA_ERR_FLAGS for unknown bits. */
 int ckda_chunk_fwd_ex(const void* q, const void* k, const void* v, const void* alpha,
                       const void* beta, const float* h0, void* o, float* hT,
                       int B, int H, int T, int dk, int dv, int chunk, int dtype, int flags,
@@ -179,6 +187,34 @@ int ckda_chunk_fwd_gather(const void* q, const void* k, const void* v, const voi
                           int B, int H, int T, int dk_in, const int* idx, int dk, int dv, int chunk, int dtype,
                           int flags, void* workspace, size_t workspace_bytes, void* stream);
 
+/* DeltaProduct_2 forward: two delta-rule sub-steps per token, each with its
+ * own key, value and beta, and one read-out per token after both (the
+ * DeltaProduct_2 comparator of the "Complex KDA" paper, Fig. 5 and Sec. 6,
+ * where it runs ungated; App. C's Gated DeltaProduct scales the product of
+ * the sub-steps' Householder factors by one scalar gate per token):
+ *
+ *   Hb = alpha_t H_{t-1}            (alpha_t = 1 when alpha is NULL)
+ *   H' = Hb + beta_t1 k_t1 (v_t1 - Hb^T k_t1)^T
+ *   H_t = H' + beta_t2 k_t2 (v_t2 - H'^T k_t2)^T,   o_t = H_t^T q_t
+ *
+ *   q           : [B, H, T, dk]      dtype
+ *   k           : [B, H, T, 2, dk]   dtype (sub-step keys k_t1, k_t2)
+ *   v           : [B, H, T, 2, dv]   dtype
+ *   beta        : [B, H, T, 2]       dtype
+ *   alpha       : [B, H, T] dtype scalar gates, or NULL (ungated)
+ *   h0, hT      : [B, H, dk, dv] fp32 as ckda_chunk_fwd;  o : [B, H, T, dv]
+ *   workspace   : ckda_chunk_fwd_workspace_size(B, H, 2 * T, dk, dv, chunk, dtype) bytes
+ *
+ * The 2 T sub-steps run through the chunked forward's kernels as one
+ * sequence (k, v and beta above are that sequence in memory order); only the
+ * second sub-step of each token is read out.  flags: CKDA_FUSE_* (the norm
+ * flags normalise every sub-step key and the query; CKDA_FUSE_GATES makes
+ * beta, and alpha if given, logits).  Other rules as ckda_chunk_fwd. */
+int ckda_deltaproduct2_fwd(const void* q, const void* k, const void* v, const void* alpha,
+                           const void* beta, const float* h0, void* o, float* hT,
+                           int B, int H, int T, int dk, int dv, int chunk, int dtype, int flags,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
 /* One recurrent decode step for N sequences x H heads, state in place.
  *
  *   q, k, alpha : [N, H, dk]     dtype
@@ -205,11 +241,20 @@ int ckda_decode_step(const void* q, const void* k, const void* v, const void* al
 
 /* ckda_decode_step with the per-token prologue `flags` (CKDA_FUSE_*) applied
  * to the token first (fp32 throughout).  Same arguments and rules as
- * ckda_decode_step; flags = 0 gives its results exactly.  Returns
- * CKDA_ERR_FLAGS for bits outside CKDA_FUSE_*. */
+ * ckda_decode_step; flags = 0 gives its results exactly.  With
+ * CKDA_GATE_SCALAR alpha is [N, H].  Returns CKDA_ERR_FLAGS for unknown bits. */
 int ckda_decode_step_ex(const void* q, const void* k, const void* v, const void* alpha,
                         const void* beta, float* H_inout, void* o,
                         int N, int H, int dk, int dv, int dtype, int flags, void* stream);
+
+/* One DeltaProduct_2 decode step (the recurrence of ckda_deltaproduct2_fwd)
+ * for N sequences x H heads, state in place, in one read and one write of
+ * the state:  q [N, H, dk], k [N, H, 2, dk], v [N, H, 2, dv], beta [N, H, 2],
+ * alpha [N, H] scalar gates or NULL, H_inout [N, H, dk, dv] fp32, o [N, H, dv].
+ * flags: CKDA_FUSE_*.  All arithmetic fp32. */
+int ckda_deltaproduct2_decode_step(const void* q, const void* k, const void* v, const void* alpha,
+                                   const void* beta, float* H_inout, void* o,
+                                   int N, int H, int dk, int dv, int dtype, int flags, void* stream);
 
 /* ckda_decode_step_ex on a retained subset of key channels gathered inside
  * the kernel: q, k, alpha are [N, H, dk_in] full-width rows, idx [H, dk]

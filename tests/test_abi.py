@@ -106,7 +106,7 @@ def test_chunk_fwd_rejects(kw, status):
     assert msg.startswith("ckda_chunk_fwd")
 
 
-@pytest.mark.parametrize("flags", [8, 16, -1, 1 << 30])
+@pytest.mark.parametrize("flags", [16, 32, -1, 1 << 16, 1 << 30])
 def test_fused_entry_points_reject_unknown_flags(flags):
     rc, msg = call_fwd(flags=flags)
     assert rc == 7 and msg.startswith("ckda_chunk_fwd"), (rc, msg)
@@ -151,7 +151,7 @@ def call_dec_gather(**kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(idx=None), 1), (dict(dk_in=0), 2), (dict(dk_in=1 << 20), 2), (dict(idx=BASE + 80 * MB + 4), 2),
     (dict(o=BASE + 80 * MB), 4),                       # o overlaps idx
-    (dict(flags=8), 7), (dict(dk=48), 3),
+    (dict(flags=16), 7), (dict(dk=48), 3),
     (dict(o=BASE + 20000), 4),                       # o inside q's full-width rows (past its kept width)
 ])
 def test_gather_entry_points_reject(kw, status):
@@ -165,6 +165,48 @@ def test_gather_entry_points_reject(kw, status):
 def test_gather_entry_points_accept_valid_empty_calls():
     assert call_fwd_gather(B=0, idx=None)[0] == 0
     assert call_fwd_gather(H=0, idx=None)[0] == 0
+
+
+def call_dp2(**kw):
+    L = ck.lib()
+    B, H, T, dk, dv = 1, 2, kw.get("T", 64), 64, 64
+    p = dict(q=BASE, k=BASE + 1 * MB, v=BASE + 2 * MB, alpha=BASE + 3 * MB, beta=BASE + 4 * MB,
+             h0=BASE + 5 * MB, o=BASE + 6 * MB, hT=BASE + 7 * MB, ws=BASE + 8 * MB)
+    p.update({k: v for k, v in kw.items() if k in p})
+    rc = L.ckda_deltaproduct2_fwd(p["q"], p["k"], p["v"], p["alpha"], p["beta"], p["h0"], p["o"], p["hT"], B, H, T,
+                                  dk, dv, 64, 1, kw.get("flags", 0), p["ws"], kw.get("wsb", 64 * MB), None)
+    return rc, L.ckda_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(beta=None), 1), (dict(flags=8), 7), (dict(flags=1 << 16), 7),
+    (dict(o=BASE + 1 * MB + 20000), 4),                # o inside k: 2 T sub-step rows of k (32 KB)
+    (dict(wsb=ck.lib().ckda_chunk_fwd_workspace_size(1, 2, 64, 64, 64, 64, 1)), 5),   # sized for T, not 2 T
+])
+def test_deltaproduct2_rejects(kw, status):
+    rc, msg = call_dp2(**kw)
+    assert rc == status, (rc, msg)
+    assert msg.startswith("ckda_deltaproduct2_fwd")
+
+
+def test_deltaproduct2_decode_rejects():
+    L = ck.lib()
+    args = [BASE, BASE + MB, BASE + 2 * MB, None, BASE + 4 * MB, BASE + 5 * MB, BASE + 6 * MB, 2, 2, 64, 64, 1]
+    assert L.ckda_deltaproduct2_decode_step(*args, 8, None) == 7
+    bad = list(args)
+    bad[6] = BASE + 5 * MB + 64                              # o overlaps the state
+    assert L.ckda_deltaproduct2_decode_step(*bad, 0, None) == 4
+    bad = list(args)
+    bad[0] = None
+    assert L.ckda_deltaproduct2_decode_step(*bad, 0, None) == 1
+
+
+def test_scalar_gate_flag_checks():
+    # scalar gate: alpha is [B, H, T]; it does not combine with a gather
+    assert call_fwd(flags=8, o=BASE + 3 * MB + 128)[0] == 4      # o inside the 256-byte scalar alpha
+    assert call_fwd(flags=8, o=BASE + 3 * MB + 512)[0] == 6      # past it: checks pass (no device here)
+    assert call_fwd(flags=0, o=BASE + 3 * MB + 512)[0] == 4      # per-channel alpha is larger
+    assert call_fwd_gather(flags=8)[0] == 3
 
 
 def test_prologue_flag_values_agree():
