@@ -54,6 +54,8 @@ def _declare(lib):
     lib.ckda_oracle_deltaproduct2.restype = i
     lib.ckda_oracle_deltaproduct2_decode.argtypes = [vp, vp, vp, vp, vp, i, vp, vp, i, i, i, i]
     lib.ckda_oracle_deltaproduct2_decode.restype = i
+    lib.ckda_oracle_bwd.argtypes = [vp] * 5 + [i, vp, i, vp, vp, i] + [vp] * 6 + [i] * 6
+    lib.ckda_oracle_bwd.restype = i
     return lib
 
 
@@ -194,6 +196,40 @@ def decode_fused(q, k, v, a, b, S, flags=GATES | NORM_K, nthreads=0):
     return decode(qq, kk, _widen(v), alpha, beta, S, nthreads=nthreads)
 
 
+def bwd(q, k, v, alpha, beta, do, dhT=None, h0=None, nthreads=0):
+    """Reverse-mode gradients of fwd() (ckda_oracle_bwd): given do = dL/do
+    [B,H,T,dv] and dhT = dL/dH_T [B,H,dk,dv] (None: zero), returns fp64
+    (dq, dk, dv, dalpha [B,H,T,dk or dv], dbeta [B,H,T], dh0 [B,H,dk,dv]).
+    Inputs as fwd(); do and dhT float32 or float64 (one dtype)."""
+    q, k, v, alpha, beta = (np.ascontiguousarray(x) for x in (q, k, v, alpha, beta))
+    code = _code(q)
+    for x in (k, v, alpha, beta):
+        if _code(x) != code:
+            raise TypeError("q, k, v, alpha, beta must share one dtype")
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    do = np.ascontiguousarray(do)
+    gcode = _code(do)
+    if do.shape != (B, H, T, dv) or gcode == BF16:
+        raise ValueError("do must be float32/float64 [B,H,T,dv]")
+    dhTc = None
+    if dhT is not None:
+        dhTc = np.ascontiguousarray(dhT)
+        if dhTc.shape != (B, H, dk, dv) or _code(dhTc) != gcode:
+            raise ValueError("dhT must be [B,H,dk,dv] in do's dtype")
+    h0c, h0code = None, F32
+    if h0 is not None:
+        h0c = np.ascontiguousarray(h0)
+        h0code = _code(h0c)
+    out = [np.empty((B, H, T, dk)), np.empty((B, H, T, dk)), np.empty((B, H, T, dv)), np.empty((B, H, T, dk)),
+           np.empty((B, H, T)), np.empty((B, H, dk, dv))]
+    rc = _load().ckda_oracle_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), code, _ptr(h0c), h0code,
+                                 _ptr(do), _ptr(dhTc), gcode, *(_ptr(x) for x in out), B, H, T, dk, dv, int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"ckda_oracle_bwd failed with code {rc}")
+    return tuple(out)
+
+
 def deltaproduct2(q, k, v, alpha, beta, h0=None, nthreads=0):
     """DeltaProduct_2 forward in fp64 (ckda_oracle_deltaproduct2).
 
@@ -279,6 +315,9 @@ class Variant:
 
     def deltaproduct2_decode(self, *a, **kw):
         return self._swap(deltaproduct2_decode, *a, **kw)
+
+    def bwd(self, *a, **kw):
+        return self._swap(bwd, *a, **kw)
 
 
 def build_variant(source_text: str, out_path: str) -> "Variant":

@@ -329,3 +329,142 @@ int ckda_oracle_deltaproduct2_decode(const void* q, const void* k, const void* v
   free(buf);
   return 0;
 }
+
+/* ---------------------------------------------------------------- backward
+ *
+ * Reverse-mode derivative of the forward above for a loss L whose gradients
+ * with respect to the outputs are do = dL/do_t and dhT = dL/dH_T: returns
+ * dq, dk, dv, dalpha, dbeta (all per token, like their inputs) and dh0.
+ * Written from the step itself (paper Eq. (1), in the course's order:
+ * Hbar = Diag(alpha) H_{t-1}, s = Hbar^T k, u = beta (v - s),
+ * H_t = Hbar + k u^T, o_t = H_t^T q), differentiated line by line in
+ * reverse, with G = dL/dH_t carried from the end of the sequence:
+ *
+ *   G    += q do^T          dq = H_t do
+ *   dk    = G u             du = G^T k
+ *   dbeta = du . (v - s)    dv = beta du       ds = -beta du
+ *   dHbar = G + k ds^T      dk += Hbar ds
+ *   dalpha_i = sum_j dHbar_ij H_{t-1,ij}       G <- Diag(alpha) dHbar
+ *
+ * and dh0 = G after the first token.  The gate enters as the signed number
+ * it is: dalpha is the plain partial derivative (no log space, no sign
+ * convention, exact at zero gates).  States are kept at checkpoints every
+ * `seg` tokens and recomputed one segment at a time in reverse.
+ * Layouts as ckda_oracle_fwd; do [B,H,T,dv] (may be NULL: zero), dhT
+ * [B,H,dk,dv] (may be NULL: zero); all outputs fp64. */
+int ckda_oracle_bwd(const void* q, const void* k, const void* v, const void* alpha, const void* beta, int dtype,
+                    const void* h0, int h0_dtype, const void* dout, const void* dhT, int g_dtype, double* dq,
+                    double* dk, double* dv_, double* dalpha, double* dbeta, double* dh0, int B, int H, int T, int dk_,
+                    int dv, int nthreads) {
+  if (!q || !k || !v || !alpha || !beta || !dq || !dk || !dv_ || !dalpha || !dbeta || !dh0) return 1;
+  if (B < 0 || H < 0 || T < 0 || dk_ <= 0 || dv <= 0) return 2;
+  if (!valid_dtype(dtype) || (h0 && !valid_dtype(h0_dtype)) || !valid_dtype(g_dtype)) return 3;
+  const int n = dk_, seg = 64;
+  const long long NS = (long long)n * dv;
+  long long BH = (long long)B * H;
+  int failed = 0;
+#ifdef _OPENMP
+  int nt = nthreads > 0 ? nthreads : omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : failed) num_threads(nt)
+#else
+  (void)nthreads;
+#endif
+  for (long long bh = 0; bh < BH; ++bh) {
+    const int nseg = (T + seg - 1) / seg;
+    double* ck = (double*)malloc(sizeof(double) * (size_t)NS * (nseg + 1));   /* state at each segment start */
+    double* st = (double*)malloc(sizeof(double) * (size_t)NS * (seg + 1));    /* states inside one segment */
+    double* G = (double*)malloc(sizeof(double) * (size_t)NS);
+    double* Hb = (double*)malloc(sizeof(double) * (size_t)NS);
+    double* buf = (double*)malloc(sizeof(double) * (size_t)(3 * n + 6 * dv));
+    if (!ck || !st || !G || !Hb || !buf) {
+      free(ck); free(st); free(G); free(Hb); free(buf);
+      failed |= 1;
+      continue;
+    }
+    double *a = buf, *kk = a + n, *qq = kk + n, *vv = qq + n, *s = vv + dv, *u = s + dv, *gd = u + dv, *du = gd + dv,
+           *ds = du + dv;
+    const long long sbase = bh * NS;
+    /* forward: checkpoints */
+    for (long long e = 0; e < NS; ++e) ck[e] = h0 ? widen(h0, sbase + e, h0_dtype) : 0.0;
+    for (int g = 0; g < nseg; ++g) {
+      double* S = ck + (long long)(g + 1) * NS;
+      memcpy(S, ck + (long long)g * NS, sizeof(double) * NS);
+      for (int t = g * seg; t < T && t < (g + 1) * seg; ++t) {
+        const long long tk = (bh * T + t) * (long long)n, tv = (bh * T + t) * (long long)dv;
+        for (int i = 0; i < n; ++i) { a[i] = widen(alpha, tk + i, dtype); kk[i] = widen(k, tk + i, dtype); }
+        for (int j = 0; j < dv; ++j) vv[j] = widen(v, tv + j, dtype);
+        step(S, a, kk, kk, vv, widen(beta, bh * T + t, dtype), s, NULL, n, dv);
+      }
+    }
+    /* reverse */
+    for (long long e = 0; e < NS; ++e) G[e] = dhT ? widen(dhT, sbase + e, g_dtype) : 0.0;
+    for (int g = nseg - 1; g >= 0; --g) {
+      const int t0 = g * seg, t1 = (t0 + seg < T) ? t0 + seg : T;
+      memcpy(st, ck + (long long)g * NS, sizeof(double) * NS);   /* st[0] = H_{t0-1} */
+      for (int t = t0; t < t1; ++t) {
+        const long long tk = (bh * T + t) * (long long)n, tv = (bh * T + t) * (long long)dv;
+        double* S = st + (long long)(t - t0 + 1) * NS;
+        memcpy(S, S - NS, sizeof(double) * NS);
+        for (int i = 0; i < n; ++i) { a[i] = widen(alpha, tk + i, dtype); kk[i] = widen(k, tk + i, dtype); }
+        for (int j = 0; j < dv; ++j) vv[j] = widen(v, tv + j, dtype);
+        step(S, a, kk, kk, vv, widen(beta, bh * T + t, dtype), s, NULL, n, dv);
+      }
+      for (int t = t1 - 1; t >= t0; --t) {
+        const long long tk = (bh * T + t) * (long long)n, tv = (bh * T + t) * (long long)dv;
+        const double* Hp = st + (long long)(t - t0) * NS;       /* H_{t-1} */
+        const double* Ht = Hp + NS;                             /* H_t */
+        for (int i = 0; i < n; ++i) {
+          a[i] = widen(alpha, tk + i, dtype);
+          kk[i] = widen(k, tk + i, dtype);
+          qq[i] = widen(q, tk + i, dtype);
+        }
+        for (int j = 0; j < dv; ++j) { vv[j] = widen(v, tv + j, dtype); gd[j] = dout ? widen(dout, tv + j, g_dtype) : 0.0; }
+        const double b = widen(beta, bh * T + t, dtype);
+        /* recompute Hbar, s, u */
+        for (int i = 0; i < n; ++i)
+          for (int j = 0; j < dv; ++j) Hb[(long)i * dv + j] = a[i] * Hp[(long)i * dv + j];
+        for (int j = 0; j < dv; ++j) s[j] = 0.0;
+        for (int i = 0; i < n; ++i)
+          for (int j = 0; j < dv; ++j) s[j] += Hb[(long)i * dv + j] * kk[i];
+        for (int j = 0; j < dv; ++j) u[j] = b * (vv[j] - s[j]);
+        /* o_t = H_t^T q */
+        for (int i = 0; i < n; ++i) {
+          double acc = 0.0;
+          for (int j = 0; j < dv; ++j) acc += Ht[(long)i * dv + j] * gd[j];
+          dq[tk + i] = acc;
+          for (int j = 0; j < dv; ++j) G[(long)i * dv + j] += qq[i] * gd[j];
+        }
+        /* H_t = Hbar + k u^T */
+        for (int j = 0; j < dv; ++j) du[j] = 0.0;
+        for (int i = 0; i < n; ++i) {
+          double acc = 0.0;
+          for (int j = 0; j < dv; ++j) { acc += G[(long)i * dv + j] * u[j]; du[j] += G[(long)i * dv + j] * kk[i]; }
+          dk[tk + i] = acc;
+        }
+        /* u = beta (v - s) */
+        double db = 0.0;
+        for (int j = 0; j < dv; ++j) {
+          db += du[j] * (vv[j] - s[j]);
+          dv_[tv + j] = b * du[j];
+          ds[j] = -b * du[j];
+        }
+        dbeta[bh * T + t] = db;
+        /* s = Hbar^T k;  Hbar = Diag(alpha) H_{t-1} */
+        for (int i = 0; i < n; ++i) {
+          double acc = 0.0, ga = 0.0;
+          for (int j = 0; j < dv; ++j) {
+            acc += Hb[(long)i * dv + j] * ds[j];
+            const double dhb = G[(long)i * dv + j] + kk[i] * ds[j];
+            ga += dhb * Hp[(long)i * dv + j];
+            G[(long)i * dv + j] = a[i] * dhb;
+          }
+          dk[tk + i] += acc;
+          dalpha[tk + i] = ga;
+        }
+      }
+    }
+    memcpy(dh0 + sbase, G, sizeof(double) * NS);
+    free(ck); free(st); free(G); free(Hb); free(buf);
+  }
+  return failed ? 4 : 0;
+}

@@ -6,6 +6,7 @@ the row/column role of the gate, the signed gates, and the per-token prologue
 import pytest
 
 import oracle
+import test_oracle_bwd as bwdpins
 import test_oracle_pins as pins
 
 ORIG_GATE = "S[(long)i * dv + j] *= a[i];"
@@ -58,6 +59,12 @@ MUTANTS = {
                                   "    for (int i = 0; i < dk; ++i) kk[i] = widen(k, (tok * 2 + 1 - j) * dk + i, dtype);")],
     "dp2_one_beta": [("    householder_write(S, kk, vv, widen(beta, tok * 2 + j, dtype), w, dk, dv);",
                       "    householder_write(S, kk, vv, widen(beta, tok * 2, dtype), w, dk, dv);")],
+    # backward
+    "bwd_gate_not_carried": [("            G[(long)i * dv + j] = a[i] * dhb;", "            G[(long)i * dv + j] = dhb;")],
+    "bwd_dq_from_previous_state": [("          for (int j = 0; j < dv; ++j) acc += Ht[(long)i * dv + j] * gd[j];",
+                                    "          for (int j = 0; j < dv; ++j) acc += Hp[(long)i * dv + j] * gd[j];")],
+    "bwd_ds_sign": [("          ds[j] = -b * du[j];", "          ds[j] = b * du[j];")],
+    "bwd_dalpha_on_gated_state": [("            ga += dhb * Hp[(long)i * dv + j];", "            ga += dhb * Hb[(long)i * dv + j];")],
     "dp2_value_not_corrected": [("    for (int j = 0; j < dv; ++j) S[(long)i * dv + j] += b * kk[i] * (vv[j] - w[j]);",
                                  "    for (int j = 0; j < dv; ++j) S[(long)i * dv + j] += b * kk[i] * vv[j];")],
 }
@@ -87,6 +94,8 @@ PIN_CALLS = [
     lambda o: pins.test_deltaproduct2_with_one_inactive_substep_is_the_delta_rule(o, 0),
     lambda o: pins.test_deltaproduct2_with_one_inactive_substep_is_the_delta_rule(o, 1),
     lambda o: pins.test_deltaproduct2_decode_continues_the_forward(o),
+    lambda o: bwdpins.test_backward_matches_finite_differences(o, "uniform"),
+    lambda o: bwdpins.test_backward_of_pure_decay_is_closed_form(o),
 ]
 
 
