@@ -28,7 +28,8 @@ FUSE_GATES, FUSE_NORM_K, FUSE_NORM_Q = 1, 2, 4       # CKDA_FUSE_*
 GATE_SCALAR = 8                                      # CKDA_GATE_SCALAR
 EXPORTS = ("ckda_chunk_fwd_workspace_size", "ckda_chunk_fwd", "ckda_chunk_fwd_timed", "ckda_chunk_fwd_ex",
            "ckda_chunk_fwd_gather", "ckda_decode_step", "ckda_decode_step_ex", "ckda_decode_step_gather",
-           "ckda_deltaproduct2_fwd", "ckda_deltaproduct2_decode_step",
+           "ckda_deltaproduct2_fwd", "ckda_deltaproduct2_decode_step", "ckda_chunk_bwd",
+           "ckda_chunk_bwd_workspace_size",
            "ckda_status_string", "ckda_last_error", "ckda_abi_version")
 
 _lib = None
@@ -65,6 +66,10 @@ def lib() -> ctypes.CDLL:
         L.ckda_deltaproduct2_fwd.restype = i
         L.ckda_deltaproduct2_decode_step.argtypes = [vp] * 7 + [i] * 6 + [vp]
         L.ckda_deltaproduct2_decode_step.restype = i
+        L.ckda_chunk_bwd_workspace_size.argtypes = [i] * 6
+        L.ckda_chunk_bwd_workspace_size.restype = sz
+        L.ckda_chunk_bwd.argtypes = [vp] * 14 + [i] * 6 + [vp, sz, vp]
+        L.ckda_chunk_bwd.restype = i
         L.ckda_decode_step.argtypes = [vp] * 7 + [i] * 5 + [vp]
         L.ckda_decode_step.restype = i
         L.ckda_decode_step_ex.argtypes = [vp] * 7 + [i] * 6 + [vp]
@@ -250,3 +255,37 @@ def deltaproduct2_decode_step(q, k, v, beta, H, alpha=None, o=None, stream=None,
     _check(lib().ckda_deltaproduct2_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(H), _ptr(o),
                                                 N, Hh, dk, dv, code, int(fuse), _stream(stream)))
     return o
+
+
+def bwd_workspace_size(B, H, T, dk, dv, dtype) -> int:
+    code = dtype if isinstance(dtype, int) else _dtype_code(torch.empty(0, dtype=dtype))
+    return int(lib().ckda_chunk_bwd_workspace_size(B, H, T, dk, dv, code))
+
+
+def chunk_bwd(q, k, v, alpha, beta, do, h0=None, dhT=None, want_dh0=True, workspace=None, stream=None):
+    """Backward of chunk_fwd (ckda_chunk_bwd): given do = dL/do [B,H,T,dv]
+    (input dtype) and dhT = dL/dH_T [B,H,dk,dv] fp32 or None, returns fp32
+    (dq, dk, dv, dalpha, dbeta, dh0 or None)."""
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    _require(dict(q=q, k=k, v=v, alpha=alpha, beta=beta, do=do), q.dtype)
+    code = _dtype_code(q)
+    if h0 is not None:
+        _require(dict(h0=h0), torch.float32)
+    if dhT is not None:
+        _require(dict(dhT=dhT), torch.float32)
+    need = bwd_workspace_size(B, H, T, dk, dv, code)
+    if need == 0:
+        raise CkdaError(3, f"unsupported sizes dk={dk} dv={dv}")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    f32 = dict(dtype=torch.float32, device=q.device)
+    gq, gk, galpha = (torch.empty((B, H, T, dk), **f32) for _ in range(3))
+    gv = torch.empty((B, H, T, dv), **f32)
+    gbeta = torch.empty((B, H, T), **f32)
+    gh0 = torch.empty((B, H, dk, dv), **f32) if want_dh0 else None
+    _check(lib().ckda_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(h0), _ptr(do), _ptr(dhT),
+                                _ptr(gq), _ptr(gk), _ptr(gv), _ptr(galpha), _ptr(gbeta), _ptr(gh0),
+                                B, H, T, dk, dv, code, _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                _stream(stream)))
+    return gq, gk, gv, galpha, gbeta, gh0

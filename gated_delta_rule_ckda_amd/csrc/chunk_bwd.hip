@@ -1,0 +1,660 @@
+// chunk_bwd.hip -- chunkwise backward of the CKDA / KDA recurrence: given
+// dL/do and dL/dH_T, the gradients of q, k, v, alpha, beta and h0.
+//
+// The recurrence (paper Eq. (1)) per chunk of C positions with incoming
+// state H, signed gate products G(t, j) = alpha_{j+1} ... alpha_t per channel,
+// Gamma_t = G(t, -1):
+//   KG = K . Gamma, QG = Q . Gamma, KR_j = k_j . G(C-1, j),
+//   S[t, j] = sum_c k_tc k_jc G_c(t, j) (j < t), M[t, j] = sum_c q_tc k_jc G_c(t, j) (j <= t),
+//   T = (I + Diag(beta) S)^-1, TB = T Diag(beta),
+//   X = V - KG H, U = TB X, O = QG H + M U, H' = Gamma_C . H + KR^T U,
+// and its reverse-mode derivative
+//   dU = M^T dO + KR dH',  dX = TB^T dU (= dV),  dH = Gamma_C . dH' + QG^T dO - KG^T dX,
+//   dQG = dO H^T, dKG = -dX H^T, dKR = U dH'^T, dGamma_C = rowsum(H . dH'),
+//   dM = tril(dO U^T), dTB = tril(dU X^T), dbeta = colsum(T . dTB) + rowsum(dA . S),
+//   dA = -T^T dTB Diag(beta) T^T (strictly lower), dS = Diag(beta) dA,
+// followed by the decayed-Gram derivatives and every gate derivative.
+//
+// Four kernels, fp32 throughout:
+//   prep    (one workgroup per chunk)   S, M by recursive halving, T by forward
+//           substitution, TB, KG, KR, QG, Gamma_C -> a per-chunk fp32 record;
+//   states  (sequential, per head and 16-column value slice) chunk-start states;
+//   dstates (sequential, reverse)       the state gradient entering each chunk
+//           from its end, and dh0;
+//   grad    (one workgroup per chunk)   all per-token gradients.
+//
+// No gate is ever divided by.  Recursive halving: for a block of positions
+// split into halves L (keys, j) and R (queries, t) at m = last of L,
+// G(t, j) = G(t, m) G(m, j), both factors products of gates (modulus <= 1),
+// so the cross terms are plain products of operands rescaled by them, and the
+// derivative for the gate at s collects the pairs j < s <= t with its own
+// factor left out, G(t, s) G(s - 1, j), by scans inside the halves.  Exact
+// zero gates need no special case.
+#include <type_traits>
+
+#include "ckda_device.hpp"
+#include "ckda_internal.hpp"
+
+namespace ckda {
+
+constexpr int kBC = 32;          // positions per backward chunk
+constexpr int kBThreads = 256;
+constexpr int kBDS = 16;         // value columns per slice
+
+// per-chunk fp32 record of the prep kernel (offsets in floats)
+template <int DK>
+struct BwdRec {
+  static constexpr int C = kBC;
+  static constexpr int M_OFF = 0, TB_OFF = C * C, T_OFF = 2 * C * C, S_OFF = 3 * C * C;
+  static constexpr int KG_OFF = 4 * C * C, KR_OFF = KG_OFF + C * DK, QG_OFF = KR_OFF + C * DK;
+  static constexpr int GC_OFF = QG_OFF + C * DK;
+  static constexpr int FLOATS = (GC_OFF + DK + 63) / 64 * 64;
+};
+
+// ---------------------------------------------------------------- fp32 MFMA on LDS operands
+// v_mfma_f32_16x16x4_f32: lane (g, r) supplies A(r, g) and B(g, r) of one
+// 4-wide K step and holds D(4 g + v, r), v = 0..3, of the 16 x 16 result.
+// Operands are read from LDS through strides, so a transposed operand is only
+// a different pair of strides:  A(i, k) = a[i * ai + k * ak],
+// B(k, j) = b[k * bk + j * bj].
+__device__ __forceinline__ f32x4 mfma_lds(f32x4 acc, const float* a, int ai, int ak, const float* b, int bk, int bj,
+                                          int K) {
+  const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
+  for (int k0 = 0; k0 < K; k0 += 4)
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[r * ai + (k0 + g) * ak], b[(k0 + g) * bk + r * bj], acc, 0, 0, 0);
+  return acc;
+}
+
+// D (Mr x Nc, multiples of 16) = scale * A B  (ACC: D += scale * A B), the
+// 16 x 16 tiles spread over the waves; D(i, j) = d[i * di + j].
+template <bool ACC>
+__device__ __forceinline__ void gemm_lds(float* d, int di, const float* a, int ai, int ak, const float* b, int bk,
+                                         int bj, int Mr, int Nc, int K, float scale) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
+  constexpr int NW = kBThreads / 64;
+  const int tn = Nc / 16, tiles = (Mr / 16) * tn;
+  for (int ti = wave; ti < tiles; ti += NW) {
+    const int i0 = (ti / tn) * 16, j0 = (ti % tn) * 16;
+    const f32x4 acc = mfma_lds(zero4(), a + i0 * ai, ai, ak, b + j0 * bj, bk, bj, K);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      float* p = d + (i0 + 4 * g + v) * di + j0 + r;
+      *p = ACC ? *p + scale * acc[v] : scale * acc[v];
+    }
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ float ld_or(const T* p, size_t i, bool ok, float other) {
+  return ok ? to_f32(p[i]) : other;
+}
+
+// ============================================================ prep
+template <typename T, int DK>
+__global__ __launch_bounds__(kBThreads) void chunk_bwd_prep_kernel(const T* q, const T* k, const T* alpha,
+                                                                   const T* beta, float* __restrict__ rec, int T_len,
+                                                                   int nchunks) {
+  constexpr int C = kBC, DKP = DK + 1, CP = C + 1;
+  using R = BwdRec<DK>;
+  __shared__ float sq[C * DKP], sk[C * DKP], sa[C * DKP];
+  __shared__ float sx[C * DKP], sxq[C * DKP], sy[C * DKP];   // rescaled operands of one halving level
+  __shared__ float sS[C * CP], sM[C * CP], sT[C * CP], sb[C];
+
+  const int tid = threadIdx.x;
+  const long long chunk = blockIdx.x;
+  const long long bh = chunk / nchunks;
+  const int c = (int)(chunk % nchunks);
+  const int t0 = c * C, cv = min(C, T_len - t0);
+  const long long row0 = bh * (long long)T_len + t0;
+  // rows past a ragged end are identity steps: gate 1, no key, query or beta
+  for (int e = tid; e < C * DK; e += kBThreads) {
+    const int t = e / DK, ch = e % DK;
+    const bool ok = t < cv;
+    const size_t gi = ok ? (size_t)(row0 + t) * DK + ch : 0;
+    sq[t * DKP + ch] = ld_or(q, gi, ok, 0.f);
+    sk[t * DKP + ch] = ld_or(k, gi, ok, 0.f);
+    sa[t * DKP + ch] = ld_or(alpha, gi, ok, 1.f);
+  }
+  if (tid < C) sb[tid] = tid < cv ? to_f32(beta[row0 + tid]) : 0.f;
+  for (int e = tid; e < C * CP; e += kBThreads) {
+    sS[e] = 0.f;
+    sM[e] = 0.f;
+  }
+  __syncthreads();
+
+  float* rc = rec + (size_t)chunk * R::FLOATS;
+  if (tid < DK) {   // per channel: Gamma, KG, QG, Gamma_C; G(C-1, j), KR
+    const int ch = tid;
+    float gm = 1.f;
+    for (int t = 0; t < C; ++t) {
+      gm *= sa[t * DKP + ch];
+      rc[R::KG_OFF + t * DK + ch] = sk[t * DKP + ch] * gm;
+      rc[R::QG_OFF + t * DK + ch] = sq[t * DKP + ch] * gm;
+    }
+    rc[R::GC_OFF + ch] = gm;
+    float ge = 1.f;
+    for (int t = C - 1; t >= 0; --t) {
+      rc[R::KR_OFF + t * DK + ch] = sk[t * DKP + ch] * ge;
+      ge *= sa[t * DKP + ch];
+    }
+  }
+  if (tid < C) {   // diagonal of M (G = 1)
+    float d = 0.f;
+    for (int ch = 0; ch < DK; ++ch) d += sq[tid * DKP + ch] * sk[tid * DKP + ch];
+    sM[tid * CP + tid] = d;
+  }
+  // S and M below the diagonal by recursive halving
+  for (int h = C / 2; h >= 1; h >>= 1) {
+    if (tid < DK) {
+      const int ch = tid;
+      for (int lo = 0; lo < C; lo += 2 * h) {
+        const int m = lo + h - 1;
+        float f = 1.f;
+        for (int t = m + 1; t <= m + h; ++t) {   // x_t G(t, m)
+          f *= sa[t * DKP + ch];
+          sx[t * DKP + ch] = sk[t * DKP + ch] * f;
+          sxq[t * DKP + ch] = sq[t * DKP + ch] * f;
+        }
+        float e = 1.f;
+        for (int j = m; j >= lo; --j) {          // y_j G(m, j)
+          sy[j * DKP + ch] = sk[j * DKP + ch] * e;
+          e *= sa[j * DKP + ch];
+        }
+      }
+    }
+    __syncthreads();
+    const int nent = C * h / 2;   // (C / 2h) blocks of h x h entries
+    for (int e = tid; e < nent; e += kBThreads) {
+      const int blk = e / (h * h), w = e % (h * h);
+      const int lo = blk * 2 * h, t = lo + h + w / h, j = lo + w % h;
+      float s = 0.f, mm = 0.f;
+      for (int ch = 0; ch < DK; ++ch) {
+        const float y = sy[j * DKP + ch];
+        s += sx[t * DKP + ch] * y;
+        mm += sxq[t * DKP + ch] * y;
+      }
+      sS[t * CP + j] = s;
+      sM[t * CP + j] = mm;
+    }
+    __syncthreads();
+  }
+  // T = (I + Diag(beta) S)^-1, unit lower triangular, one column per thread
+  if (tid < C) {
+    const int j = tid;
+    for (int i = 0; i < C; ++i) sT[i * CP + j] = i == j ? 1.f : 0.f;
+    for (int i = j + 1; i < C; ++i) {
+      float acc = 0.f;
+      for (int l = j; l < i; ++l) acc += sS[i * CP + l] * sT[l * CP + j];
+      sT[i * CP + j] = -sb[i] * acc;
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < C * C; e += kBThreads) {
+    const int i = e / C, j = e % C;
+    rc[R::M_OFF + e] = sM[i * CP + j];
+    rc[R::T_OFF + e] = sT[i * CP + j];
+    rc[R::TB_OFF + e] = sT[i * CP + j] * sb[j];
+    rc[R::S_OFF + e] = sS[i * CP + j];
+  }
+}
+
+// ============================================================ states (forward, sequential)
+template <typename T, int DK>
+__global__ __launch_bounds__(kBThreads) void chunk_bwd_states_kernel(const T* v, const float* __restrict__ h0,
+                                                                     const float* __restrict__ rec,
+                                                                     float* __restrict__ hc, int T_len, int nchunks,
+                                                                     int dv) {
+  constexpr int C = kBC, DS = kBDS, DKP = DK + 1, CP = C + 1, DSP = DS + 1;
+  using R = BwdRec<DK>;
+  __shared__ float sH[DK * DSP], sKG[C * DKP], sKR[C * DKP], sTB[C * CP], sV[C * DSP], sX[C * DSP], sU[C * DSP],
+      sGC[DK];
+  const int tid = threadIdx.x;
+  const int nsl = dv / DS;
+  const long long bh = blockIdx.x / nsl;
+  const int col0 = (blockIdx.x % nsl) * DS;
+  for (int e = tid; e < DK * DS; e += kBThreads) {
+    const int i = e / DS, j = e % DS;
+    sH[i * DSP + j] = h0 ? h0[(bh * DK + i) * (long long)dv + col0 + j] : 0.f;
+  }
+  __syncthreads();
+  for (int c = 0; c < nchunks; ++c) {
+    const long long chunk = bh * nchunks + c;
+    const float* rc = rec + (size_t)chunk * R::FLOATS;
+    const int t0 = c * C, cv = min(C, T_len - t0);
+    for (int e = tid; e < DK * DS; e += kBThreads) {
+      const int i = e / DS, j = e % DS;
+      hc[(size_t)chunk * DK * dv + (size_t)i * dv + col0 + j] = sH[i * DSP + j];
+    }
+    for (int e = tid; e < C * DK; e += kBThreads) {
+      const int t = e / DK, ch = e % DK;
+      sKG[t * DKP + ch] = rc[R::KG_OFF + e];
+      sKR[t * DKP + ch] = rc[R::KR_OFF + e];
+    }
+    for (int e = tid; e < C * C; e += kBThreads) sTB[(e / C) * CP + e % C] = rc[R::TB_OFF + e];
+    for (int e = tid; e < C * DS; e += kBThreads) {
+      const int t = e / DS, j = e % DS;
+      const bool ok = t < cv;
+      sV[t * DSP + j] = ld_or(v, ok ? (size_t)(bh * T_len + t0 + t) * dv + col0 + j : 0, ok, 0.f);
+    }
+    if (tid < DK) sGC[tid] = rc[R::GC_OFF + tid];
+    __syncthreads();
+    for (int e = tid; e < C * DS; e += kBThreads) sX[(e / DS) * DSP + e % DS] = sV[(e / DS) * DSP + e % DS];
+    __syncthreads();
+    gemm_lds<true>(sX, DSP, sKG, DKP, 1, sH, DSP, 1, C, DS, DK, -1.f);      // X = V - KG H
+    __syncthreads();
+    gemm_lds<false>(sU, DSP, sTB, CP, 1, sX, DSP, 1, C, DS, C, 1.f);        // U = TB X
+    __syncthreads();
+    for (int e = tid; e < DK * DS; e += kBThreads) sH[(e / DS) * DSP + e % DS] *= sGC[e / DS];
+    __syncthreads();
+    gemm_lds<true>(sH, DSP, sKR, 1, DKP, sU, DSP, 1, DK, DS, C, 1.f);       // H = Gamma_C . H + KR^T U
+    __syncthreads();
+  }
+}
+
+// ============================================================ dstates (reverse, sequential)
+template <typename T, int DK>
+__global__ __launch_bounds__(kBThreads) void chunk_bwd_dstates_kernel(const T* dout, const float* __restrict__ dhT,
+                                                                      const float* __restrict__ rec,
+                                                                      float* __restrict__ dhn, float* __restrict__ dh0,
+                                                                      int T_len, int nchunks, int dv) {
+  constexpr int C = kBC, DS = kBDS, DKP = DK + 1, CP = C + 1, DSP = DS + 1;
+  using R = BwdRec<DK>;
+  __shared__ float sdH[DK * DSP], sKG[C * DKP], sKR[C * DKP], sQG[C * DKP], sM[C * CP], sTB[C * CP], sdO[C * DSP],
+      sdU[C * DSP], sdX[C * DSP], sGC[DK];
+  const int tid = threadIdx.x;
+  const int nsl = dv / DS;
+  const long long bh = blockIdx.x / nsl;
+  const int col0 = (blockIdx.x % nsl) * DS;
+  for (int e = tid; e < DK * DS; e += kBThreads) {
+    const int i = e / DS, j = e % DS;
+    sdH[i * DSP + j] = dhT ? dhT[(bh * DK + i) * (long long)dv + col0 + j] : 0.f;
+  }
+  __syncthreads();
+  for (int c = nchunks - 1; c >= 0; --c) {
+    const long long chunk = bh * nchunks + c;
+    const float* rc = rec + (size_t)chunk * R::FLOATS;
+    const int t0 = c * C, cv = min(C, T_len - t0);
+    for (int e = tid; e < DK * DS; e += kBThreads) {
+      const int i = e / DS, j = e % DS;
+      dhn[(size_t)chunk * DK * dv + (size_t)i * dv + col0 + j] = sdH[i * DSP + j];
+    }
+    for (int e = tid; e < C * DK; e += kBThreads) {
+      const int t = e / DK, ch = e % DK;
+      sKG[t * DKP + ch] = rc[R::KG_OFF + e];
+      sKR[t * DKP + ch] = rc[R::KR_OFF + e];
+      sQG[t * DKP + ch] = rc[R::QG_OFF + e];
+    }
+    for (int e = tid; e < C * C; e += kBThreads) {
+      sM[(e / C) * CP + e % C] = rc[R::M_OFF + e];
+      sTB[(e / C) * CP + e % C] = rc[R::TB_OFF + e];
+    }
+    for (int e = tid; e < C * DS; e += kBThreads) {
+      const int t = e / DS, j = e % DS;
+      const bool ok = t < cv;
+      sdO[t * DSP + j] = ld_or(dout, ok ? (size_t)(bh * T_len + t0 + t) * dv + col0 + j : 0, ok, 0.f);
+    }
+    if (tid < DK) sGC[tid] = rc[R::GC_OFF + tid];
+    __syncthreads();
+    gemm_lds<false>(sdU, DSP, sM, 1, CP, sdO, DSP, 1, C, DS, C, 1.f);       // dU = M^T dO
+    gemm_lds<true>(sdU, DSP, sKR, DKP, 1, sdH, DSP, 1, C, DS, DK, 1.f);     //    + KR dH'  (same tiles, same wave)
+    __syncthreads();
+    gemm_lds<false>(sdX, DSP, sTB, 1, CP, sdU, DSP, 1, C, DS, C, 1.f);      // dX = TB^T dU
+    __syncthreads();
+    for (int e = tid; e < DK * DS; e += kBThreads) sdH[(e / DS) * DSP + e % DS] *= sGC[e / DS];
+    __syncthreads();
+    gemm_lds<true>(sdH, DSP, sQG, 1, DKP, sdO, DSP, 1, DK, DS, C, 1.f);     // + QG^T dO
+    gemm_lds<true>(sdH, DSP, sKG, 1, DKP, sdX, DSP, 1, DK, DS, C, -1.f);    // - KG^T dX
+    __syncthreads();
+  }
+  if (dh0)
+    for (int e = tid; e < DK * DS; e += kBThreads) {
+      const int i = e / DS, j = e % DS;
+      dh0[(bh * DK + i) * (long long)dv + col0 + j] = sdH[i * DSP + j];
+    }
+}
+
+// ============================================================ grad (per chunk)
+template <typename T, int DK>
+__global__ __launch_bounds__(kBThreads) void chunk_bwd_grad_kernel(
+    const T* q, const T* k, const T* v, const T* alpha, const T* beta, const T* dout, const float* __restrict__ rec,
+    const float* __restrict__ hc, const float* __restrict__ dhn, float* __restrict__ dq, float* __restrict__ dk,
+    float* __restrict__ dvo, float* __restrict__ dal, float* __restrict__ dbe, int T_len, int nchunks, int dv) {
+  constexpr int C = kBC, DS = kBDS, DKP = DK + 1, CP = C + 1, DSP = DS + 1;
+  constexpr int NW = kBThreads / 64;
+  using R = BwdRec<DK>;
+  // big area: KG, KR and the slice buffers during the value-slice loop; the
+  // accumulated dQG, dKG, dKR afterwards
+  constexpr int SLICE = 2 * DK * DSP + 6 * C * DSP;
+  constexpr int BIG = (2 * C * DKP + SLICE) > 3 * C * DKP ? (2 * C * DKP + SLICE) : 3 * C * DKP;
+  __shared__ float sq[C * DKP], sk[C * DKP], sa[C * DKP];
+  __shared__ float big[BIG];
+  __shared__ float sM[C * CP], sTB[C * CP], sT[C * CP], sS[C * CP], sdM[C * CP], sdTB[C * CP], sP[C * CP];
+  __shared__ float sb[C], sdb[C], sGC[DK];
+  __shared__ float sG[C * DK];   // per-channel scratch columns
+  float* sKG = big;
+  float* sKR = big + C * DKP;
+  float* sH = big + 2 * C * DKP;
+  float* sdH = sH + DK * DSP;
+  float* sV = sdH + DK * DSP;
+  float* sdO = sV + C * DSP;
+  float* sX = sdO + C * DSP;
+  float* sU = sX + C * DSP;
+  float* sdU = sU + C * DSP;
+  float* sdX = sdU + C * DSP;
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 15, g = lane >> 4;
+  const long long chunk = blockIdx.x;
+  const long long bh = chunk / nchunks;
+  const int c = (int)(chunk % nchunks);
+  const int t0 = c * C, cv = min(C, T_len - t0);
+  const long long row0 = bh * (long long)T_len + t0;
+  const float* rc = rec + (size_t)chunk * R::FLOATS;
+
+  for (int e = tid; e < C * DK; e += kBThreads) {
+    const int t = e / DK, ch = e % DK;
+    const bool ok = t < cv;
+    const size_t gi = ok ? (size_t)(row0 + t) * DK + ch : 0;
+    sq[t * DKP + ch] = ld_or(q, gi, ok, 0.f);
+    sk[t * DKP + ch] = ld_or(k, gi, ok, 0.f);
+    sa[t * DKP + ch] = ld_or(alpha, gi, ok, 1.f);
+    sKG[t * DKP + ch] = rc[R::KG_OFF + e];
+    sKR[t * DKP + ch] = rc[R::KR_OFF + e];
+  }
+  for (int e = tid; e < C * C; e += kBThreads) {
+    const int i = e / C, j = e % C;
+    sM[i * CP + j] = rc[R::M_OFF + e];
+    sTB[i * CP + j] = rc[R::TB_OFF + e];
+    sT[i * CP + j] = rc[R::T_OFF + e];
+    sS[i * CP + j] = rc[R::S_OFF + e];
+  }
+  if (tid < C) sb[tid] = tid < cv ? to_f32(beta[row0 + tid]) : 0.f;
+  if (tid < DK) sGC[tid] = 0.f;
+
+  // ---- value slices: dV, and the dv contractions accumulated on the matrix cores
+  constexpr int TQ = (C / 16) * (DK / 16);          // tiles of a C x DK matrix
+  constexpr int TPW = (TQ + NW - 1) / NW;           // per wave
+  constexpr int TM = (C / 16) * (C / 16);           // tiles of a C x C matrix
+  constexpr int TMW = (TM + NW - 1) / NW;
+  f32x4 aqg[TPW], akg[TPW], akr[TPW], am[TMW], atb[TMW];
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) aqg[i] = akg[i] = akr[i] = zero4();
+#pragma unroll
+  for (int i = 0; i < TMW; ++i) am[i] = atb[i] = zero4();
+  const float* hcc = hc + (size_t)chunk * DK * dv;
+  const float* dhc = dhn + (size_t)chunk * DK * dv;
+  for (int col0 = 0; col0 < dv; col0 += DS) {
+    __syncthreads();   // previous slice fully consumed (and, first time, the loads above)
+    for (int e = tid; e < DK * DS; e += kBThreads) {
+      const int i = e / DS, j = e % DS;
+      sH[i * DSP + j] = hcc[(size_t)i * dv + col0 + j];
+      sdH[i * DSP + j] = dhc[(size_t)i * dv + col0 + j];
+    }
+    for (int e = tid; e < C * DS; e += kBThreads) {
+      const int t = e / DS, j = e % DS;
+      const bool ok = t < cv;
+      const size_t gi = ok ? (size_t)(row0 + t) * dv + col0 + j : 0;
+      sV[t * DSP + j] = ld_or(v, gi, ok, 0.f);
+      sdO[t * DSP + j] = ld_or(dout, gi, ok, 0.f);
+      sX[t * DSP + j] = ld_or(v, gi, ok, 0.f);
+    }
+    __syncthreads();
+    gemm_lds<true>(sX, DSP, sKG, DKP, 1, sH, DSP, 1, C, DS, DK, -1.f);      // X = V - KG H
+    gemm_lds<false>(sdU, DSP, sM, 1, CP, sdO, DSP, 1, C, DS, C, 1.f);       // dU = M^T dO + KR dH'
+    gemm_lds<true>(sdU, DSP, sKR, DKP, 1, sdH, DSP, 1, C, DS, DK, 1.f);
+    __syncthreads();
+    gemm_lds<false>(sU, DSP, sTB, CP, 1, sX, DSP, 1, C, DS, C, 1.f);        // U = TB X
+    gemm_lds<false>(sdX, DSP, sTB, 1, CP, sdU, DSP, 1, C, DS, C, 1.f);      // dX = TB^T dU
+    if (tid < DK) {
+      float acc = 0.f;
+      for (int j = 0; j < DS; ++j) acc += sH[tid * DSP + j] * sdH[tid * DSP + j];
+      sGC[tid] += acc;
+    }
+    __syncthreads();
+    for (int e = tid; e < C * DS; e += kBThreads) {
+      const int t = e / DS, j = e % DS;
+      if (t < cv) dvo[(size_t)(row0 + t) * dv + col0 + j] = sdX[t * DSP + j];
+    }
+    // dQG += dO H^T, dKG -= dX H^T, dKR += U dH'^T   (C x DK, K = DS)
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      const int ti = wave + NW * i;
+      if (ti < TQ) {
+        const int i0 = (ti / (DK / 16)) * 16, j0 = (ti % (DK / 16)) * 16;
+        aqg[i] = mfma_lds(aqg[i], sdO + i0 * DSP, DSP, 1, sH + j0 * DSP, 1, DSP, DS);
+        akg[i] = mfma_lds(akg[i], sdX + i0 * DSP, DSP, 1, sH + j0 * DSP, 1, DSP, DS);
+        akr[i] = mfma_lds(akr[i], sU + i0 * DSP, DSP, 1, sdH + j0 * DSP, 1, DSP, DS);
+      }
+    }
+    // dM += dO U^T, dTB += dU X^T   (C x C, K = DS)
+#pragma unroll
+    for (int i = 0; i < TMW; ++i) {
+      const int ti = wave + NW * i;
+      if (ti < TM) {
+        const int i0 = (ti / (C / 16)) * 16, j0 = (ti % (C / 16)) * 16;
+        am[i] = mfma_lds(am[i], sdO + i0 * DSP, DSP, 1, sU + j0 * DSP, 1, DSP, DS);
+        atb[i] = mfma_lds(atb[i], sdU + i0 * DSP, DSP, 1, sX + j0 * DSP, 1, DSP, DS);
+      }
+    }
+  }
+  __syncthreads();
+  // accumulators to LDS (the big area is free now); dKG is stored negated
+  float* sdQG = big;
+  float* sdKG = big + C * DKP;
+  float* sdKR = big + 2 * C * DKP;
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    const int ti = wave + NW * i;
+    if (ti < TQ) {
+      const int i0 = (ti / (DK / 16)) * 16, j0 = (ti % (DK / 16)) * 16;
+#pragma unroll
+      for (int vv = 0; vv < 4; ++vv) {
+        const int o = (i0 + 4 * g + vv) * DKP + j0 + r;
+        sdQG[o] = aqg[i][vv];
+        sdKG[o] = -akg[i][vv];
+        sdKR[o] = akr[i][vv];
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < TMW; ++i) {
+    const int ti = wave + NW * i;
+    if (ti < TM) {
+      const int i0 = (ti / (C / 16)) * 16, j0 = (ti % (C / 16)) * 16;
+#pragma unroll
+      for (int vv = 0; vv < 4; ++vv) {
+        const int row = i0 + 4 * g + vv, col = j0 + r;
+        sdM[row * CP + col] = col <= row ? am[i][vv] : 0.f;
+        sdTB[row * CP + col] = col <= row ? atb[i][vv] : 0.f;
+      }
+    }
+  }
+  __syncthreads();
+  // ---- through the solve: TB = T Diag(beta), T = (I + A)^-1, A = Diag(beta) S
+  if (tid < C) {
+    float acc = 0.f;
+    for (int i = 0; i < C; ++i) acc += sT[i * CP + tid] * sdTB[i * CP + tid];
+    sdb[tid] = acc;
+  }
+  __syncthreads();
+  for (int e = tid; e < C * C; e += kBThreads) sdTB[(e / C) * CP + e % C] *= sb[e % C];   // dT = dTB Diag(beta)
+  __syncthreads();
+  gemm_lds<false>(sP, CP, sdTB, CP, 1, sT, 1, CP, C, C, C, 1.f);                         // P = dT T^T
+  __syncthreads();
+  gemm_lds<false>(sdTB, CP, sT, 1, CP, sP, CP, 1, C, C, C, -1.f);                        // dA = -T^T P
+  __syncthreads();
+  if (tid < C) {   // strictly lower part: dbeta += rowsum(dA . S), dS = Diag(beta) dA
+    const int t = tid;
+    float acc = 0.f;
+    for (int j = 0; j < C; ++j) {
+      const float da = j < t ? sdTB[t * CP + j] : 0.f;
+      acc += da * sS[t * CP + j];
+      sdTB[t * CP + j] = sb[t] * da;
+    }
+    sdb[t] += acc;
+  }
+  __syncthreads();
+  float* sdS = sdTB;
+
+  // ---- per channel: direct terms, gate scans, recursive halving of S and M.
+  // The accumulators live in this channel's column of the (now consumed)
+  // dQG / dKG / dKR arrays: gq, gk, ga; sG is a per-channel scratch column.
+  if (tid < DK) {
+    const int ch = tid;
+    auto Q = [&](int t) { return sq[t * DKP + ch]; };
+    auto K = [&](int t) { return sk[t * DKP + ch]; };
+    auto A = [&](int t) { return sa[t * DKP + ch]; };
+    float* gq = sdQG + ch;   // element t at gq[t * DKP]
+    float* gk = sdKG + ch;
+    float* ga = sdKR + ch;
+    float* sg = sG + ch;     // element t at sg[t * DK]
+    // sg[t] = G(C-1, t) = alpha_{t+1} ... alpha_{C-1}
+    {
+      float e = 1.f;
+      for (int t = C - 1; t >= 0; --t) {
+        sg[t * DK] = e;
+        e *= A(t);
+      }
+    }
+    // forward: direct terms, the KR scan (pairs with the chunk end) and the
+    // Gamma_C term; pre[t] = Gamma_{t-1}
+    float pre[C + 1];
+    pre[0] = 1.f;
+    {
+      float f = 0.f;
+      const float gc = sGC[ch];
+#pragma unroll
+      for (int t = 0; t < C; ++t) {
+        pre[t + 1] = pre[t] * A(t);
+        const float dqg = gq[t * DKP], dkg = gk[t * DKP], dkr = ga[t * DKP], se = sg[t * DK];
+        const float dmd = sdM[t * CP + t];
+        gq[t * DKP] = dmd * K(t) + dqg * pre[t + 1];
+        gk[t * DKP] = dmd * Q(t) + dkg * pre[t + 1] + dkr * se;
+        ga[t * DKP] = se * f + gc * pre[t] * se;
+        f = A(t) * f + dkr * K(t);
+        sg[t * DK] = dqg * Q(t) + dkg * K(t);   // R_t of the Gamma_t scan
+      }
+    }
+    {   // Gamma_t terms (pairs with the chunk start): reverse scan of R_t
+      float bs = 0.f;
+#pragma unroll
+      for (int s = C - 1; s >= 0; --s) {
+        bs = sg[s * DK] + (s + 1 < C ? A(s + 1) * bs : 0.f);
+        ga[s * DKP] += pre[s] * bs;
+      }
+    }
+    // recursive halving: blocks [lo, lo + 2h), L = [lo, m], R = [m + 1, lo + 2h - 1];
+    // sg holds G(m, j) on L and G(t, m) on R
+    for (int h = C / 2; h >= 1; h >>= 1) {
+      for (int lo = 0; lo < C; lo += 2 * h) {
+        const int m = lo + h - 1;
+        {
+          float f = 1.f;
+          for (int i = 0; i < h; ++i) {
+            f *= A(m + 1 + i);
+            sg[(m + 1 + i) * DK] = f;
+          }
+          float e = 1.f;
+          for (int i = h - 1; i >= 0; --i) {
+            sg[(lo + i) * DK] = e;
+            e *= A(lo + i);
+          }
+        }
+        // rows t in R, last to first: cross terms with L, and the scan for
+        // the gates s in R, G(s - 1, m) sum_{t >= s} (q_t zm_t + k_t zs_t) G(t, s)
+        float bs = 0.f;
+        for (int i = h - 1; i >= 0; --i) {
+          const int t = m + 1 + i;
+          float zm = 0.f, zs = 0.f;
+          for (int jj = 0; jj < h; ++jj) {
+            const float ky = K(lo + jj) * sg[(lo + jj) * DK];
+            zm += sdM[t * CP + lo + jj] * ky;
+            zs += sdS[t * CP + lo + jj] * ky;
+          }
+          const float gr = sg[t * DK];
+          gq[t * DKP] += gr * zm;
+          gk[t * DKP] += gr * zs;
+          bs = Q(t) * zm + K(t) * zs + (i + 1 < h ? A(t + 1) * bs : 0.f);
+          ga[t * DKP] += (i > 0 ? sg[(t - 1) * DK] : 1.f) * bs;
+        }
+        // rows j in L, first to last: cross terms with R, and the scan for
+        // the gates s in L, G(m, s) sum_{j < s} k_j zl_j G(s - 1, j)
+        float f = 0.f;
+        for (int jj = 0; jj < h; ++jj) {
+          const int j = lo + jj;
+          float zl = 0.f;
+          for (int i = 0; i < h; ++i) {
+            const int t = m + 1 + i;
+            zl += (sdM[t * CP + j] * Q(t) + sdS[t * CP + j] * K(t)) * sg[t * DK];
+          }
+          const float gl = sg[j * DK];
+          gk[j * DKP] += gl * zl;
+          ga[j * DKP] += gl * f;
+          f = A(j) * f + K(j) * zl;
+        }
+      }
+    }
+    for (int t = 0; t < cv; ++t) {
+      const size_t o = (size_t)(row0 + t) * DK + ch;
+      dq[o] = gq[t * DKP];
+      dk[o] = gk[t * DKP];
+      dal[o] = ga[t * DKP];
+    }
+  }
+  if (tid < cv) dbe[row0 + tid] = sdb[tid];
+}
+
+// ============================================================ launch
+template <typename T, int DK>
+static hipError_t launch_bwd_t(const BwdArgs& a) {
+  using R = BwdRec<DK>;
+  const int nch = (a.T + kBC - 1) / kBC;
+  const long long BH = (long long)a.B * a.H, total = BH * nch;
+  float* rec = (float*)a.workspace;
+  float* hc = rec + (size_t)total * R::FLOATS;
+  float* dhn = hc + (size_t)total * DK * a.dv;
+  const unsigned nsl = (unsigned)(a.dv / kBDS);
+  if (total > 0) {
+    hipLaunchKernelGGL((chunk_bwd_prep_kernel<T, DK>), dim3((unsigned)total), dim3(kBThreads), 0, a.stream,
+                       (const T*)a.q, (const T*)a.k, (const T*)a.alpha, (const T*)a.beta, rec, a.T, nch);
+    hipLaunchKernelGGL((chunk_bwd_states_kernel<T, DK>), dim3((unsigned)(BH * nsl)), dim3(kBThreads), 0, a.stream,
+                       (const T*)a.v, a.h0, rec, hc, a.T, nch, a.dv);
+  }
+  hipLaunchKernelGGL((chunk_bwd_dstates_kernel<T, DK>), dim3((unsigned)(BH * nsl)), dim3(kBThreads), 0, a.stream,
+                     (const T*)a.dout, a.dhT, rec, dhn, a.gh0, a.T, nch, a.dv);
+  if (total > 0)
+    hipLaunchKernelGGL((chunk_bwd_grad_kernel<T, DK>), dim3((unsigned)total), dim3(kBThreads), 0, a.stream,
+                       (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.alpha, (const T*)a.beta,
+                       (const T*)a.dout, rec, hc, dhn, a.gq, a.gk, a.gv, a.galpha, a.gbeta, a.T, nch, a.dv);
+  return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t bwd_dk_dispatch(const BwdArgs& a) {
+  switch (a.dk) {
+    case 16: return launch_bwd_t<T, 16>(a);
+    case 32: return launch_bwd_t<T, 32>(a);
+    case 64: return launch_bwd_t<T, 64>(a);
+    case 128: return launch_bwd_t<T, 128>(a);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_chunk_bwd(const BwdArgs& a) {
+  if ((long long)a.B * a.H == 0) return hipSuccess;
+  return a.dtype == 1 ? bwd_dk_dispatch<bf16_t>(a) : bwd_dk_dispatch<float>(a);
+}
+
+size_t chunk_bwd_workspace_floats(int B, int H, int T, int dk, int dv) {
+  size_t per = 0;
+  switch (dk) {
+    case 16: per = BwdRec<16>::FLOATS; break;
+    case 32: per = BwdRec<32>::FLOATS; break;
+    case 64: per = BwdRec<64>::FLOATS; break;
+    case 128: per = BwdRec<128>::FLOATS; break;
+    default: return 0;
+  }
+  const size_t total = (size_t)B * H * (((size_t)T + kBC - 1) / kBC);
+  return total * (per + 2 * (size_t)dk * dv);
+}
+
+}  // namespace ckda

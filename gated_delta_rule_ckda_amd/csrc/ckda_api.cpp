@@ -214,6 +214,61 @@ int ckda_deltaproduct2_fwd(const void* q, const void* k, const void* v, const vo
                         workspace, workspace_bytes, stream, none, nullptr, 0, true);
 }
 
+size_t ckda_chunk_bwd_workspace_size(int B, int H, int T, int dk, int dv, int dtype) {
+  if (B < 0 || H < 0 || T < 0) return 0;
+  if (!supported_dim(dk) || !supported_dim(dv) || !supported_dtype(dtype)) return 0;
+  const size_t bytes = ckda::chunk_bwd_workspace_floats(B, H, T, dk, dv) * 4;
+  return bytes == 0 ? 256 : bytes;
+}
+
+int ckda_chunk_bwd(const void* q, const void* k, const void* v, const void* alpha, const void* beta,
+                   const float* h0, const void* dout, const float* dhT, float* dq, float* dk_out, float* dv_out,
+                   float* dalpha, float* dbeta, float* dh0, int B, int H, int T, int dk, int dv, int dtype,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "ckda_chunk_bwd";
+  if (B < 0 || H < 0 || T < 0) return fail(CKDA_ERR_DIM, "%s: negative size (B=%d H=%d T=%d)", fn, B, H, T);
+  if (!supported_dtype(dtype)) return fail(CKDA_ERR_UNSUPPORTED, "%s: dtype %d is not F32(0) or BF16(1)", fn, dtype);
+  if (!supported_dim(dk) || !supported_dim(dv))
+    return fail(CKDA_ERR_UNSUPPORTED, "%s: dk=%d dv=%d (supported: 16, 32, 64, 128)", fn, dk, dv);
+  const size_t BH = (size_t)B * H;
+  if (BH == 0) return ok();
+  const size_t es = dtype_bytes(dtype);
+  const size_t nk = BH * T * dk, nv = BH * T * dv, nb = BH * T, ns = BH * dk * dv;
+  if (T > 0 && (!q || !k || !v || !alpha || !beta || !dout || !dq || !dk_out || !dv_out || !dalpha || !dbeta))
+    return fail(CKDA_ERR_NULL, "%s: inputs, do and every per-token gradient are required", fn);
+  const size_t nch = BH * (((size_t)T + 31) / 32);
+  if (nch > (size_t)INT32_MAX || BH * (size_t)(dv / 16) > (size_t)INT32_MAX)
+    return fail(CKDA_ERR_DIM, "%s: sizes exceed the launch grid", fn);
+  const size_t need = ckda_chunk_bwd_workspace_size(B, H, T, dk, dv, dtype);
+  if (!workspace) return fail(CKDA_ERR_WORKSPACE, "%s: workspace is NULL", fn);
+  if (workspace_bytes < need)
+    return fail(CKDA_ERR_WORKSPACE, "%s: workspace of %zu bytes, need %zu", fn, workspace_bytes, need);
+  if (((uintptr_t)workspace & 255u) != 0) return fail(CKDA_ERR_WORKSPACE, "%s: workspace not 256-byte aligned", fn);
+  const void* ptrs[] = {q, k, v, alpha, beta, h0, dout, dhT, dq, dk_out, dv_out, dalpha, dbeta, dh0};
+  const char* names[] = {"q", "k", "v", "alpha", "beta", "h0", "do", "dhT", "dq", "dk", "dv", "dalpha", "dbeta", "dh0"};
+  for (int i = 0; i < 14; ++i)
+    if (ptrs[i] && misaligned(ptrs[i])) return fail(CKDA_ERR_DIM, "%s: %s is not 16-byte aligned", fn, names[i]);
+  const Range in[] = {range("q", q, T ? nk * es : 0),       range("k", k, T ? nk * es : 0),
+                      range("v", v, T ? nv * es : 0),       range("alpha", alpha, T ? nk * es : 0),
+                      range("beta", beta, T ? nb * es : 0), range("h0", h0, h0 ? ns * 4 : 0),
+                      range("do", dout, T ? nv * es : 0),   range("dhT", dhT, dhT ? ns * 4 : 0),
+                      range("workspace", workspace, need)};
+  const Range out[] = {range("dq", dq, T ? nk * 4 : 0),         range("dk", dk_out, T ? nk * 4 : 0),
+                       range("dv", dv_out, T ? nv * 4 : 0),     range("dalpha", dalpha, T ? nk * 4 : 0),
+                       range("dbeta", dbeta, T ? nb * 4 : 0),   range("dh0", dh0, dh0 ? ns * 4 : 0)};
+  for (const Range& o : out) {
+    for (const Range& r : in)
+      if (overlap(o, r)) return fail(CKDA_ERR_ALIAS, "%s: %s overlaps %s", fn, o.name, r.name);
+    for (const Range& o2 : out)
+      if (&o2 != &o && overlap(o, o2)) return fail(CKDA_ERR_ALIAS, "%s: %s overlaps %s", fn, o.name, o2.name);
+  }
+  ckda::BwdArgs a{q, k, v, alpha, beta, h0, dout, dhT, dq, dk_out, dv_out, dalpha, dbeta, dh0,
+                  B, H, T, dk, dv, dtype, workspace, (hipStream_t)stream};
+  hipError_t e = ckda::launch_chunk_bwd(a);
+  if (e != hipSuccess) return fail(CKDA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  return ok();
+}
+
 int ckda_chunk_fwd_timed(const void* q, const void* k, const void* v, const void* alpha,
                          const void* beta, const float* h0, void* o, float* hT,
                          int B, int H, int T, int dk, int dv, int chunk, int dtype,

@@ -46,6 +46,21 @@ struct ChunkRecord {
 };
 ChunkRecord chunk_record_layout(int dk, int chunk, int dtype);
 
+struct BwdArgs {
+  const void *q, *k, *v, *alpha, *beta;
+  const float* h0;
+  const void* dout;
+  const float* dhT;
+  float *gq, *gk, *gv, *galpha, *gbeta, *gh0;   // gradients of q, k, v, alpha, beta, h0
+  int B, H, T, dk, dv, dtype;
+  void* workspace;
+  hipStream_t stream;
+};
+// floats of backward workspace (per-chunk records, chunk-start states and
+// state gradients), 0 for an unsupported dk
+size_t chunk_bwd_workspace_floats(int B, int H, int T, int dk, int dv);
+hipError_t launch_chunk_bwd(const BwdArgs& a);
+
 hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_chunk_fwd(const ChunkArgs& a);
 

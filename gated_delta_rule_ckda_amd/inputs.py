@@ -289,6 +289,15 @@ def dp2_decode_inputs(step: int, d: DecodeWorkload = DECODE, N=None, H=None, gat
                 alpha=_to(a, d.dtype) if gated else None, beta=_to(b, d.dtype))
 
 
+def make_output_grads(w: Workload, seed: int):
+    """Upstream gradients for the backward: do ~ N(0, 1) [B,H,T,dv] in w.dtype
+    and dhT ~ N(0, 0.1) [B,H,dk,dv] fp32 (draw order: do, dhT)."""
+    rng = np.random.default_rng(seed)
+    do = rng.standard_normal((w.B, w.H, w.T, w.dv), dtype=np.float32)
+    dhT = np.float32(0.1) * rng.standard_normal((w.B, w.H, w.dk, w.dv), dtype=np.float32)
+    return _to(do, w.dtype), torch.from_numpy(dhT)
+
+
 def decode_state(d: DecodeWorkload = DECODE, N=None, H=None):
     """Initial fp32 decode state [N,H,dk,dv] ~ N(0, 0.1)."""
     N = d.N if N is None else N

@@ -215,6 +215,43 @@ int ckda_deltaproduct2_fwd(const void* q, const void* k, const void* v, const vo
                            int B, int H, int T, int dk, int dv, int chunk, int dtype, int flags,
                            void* workspace, size_t workspace_bytes, void* stream);
 
+/* Bytes of device workspace ckda_chunk_bwd needs, or 0 for invalid or
+ * unsupported sizes: per 32-position chunk of every (batch, head) an fp32
+ * record (4 * 32 * 32 + 3 * 32 * dk + dk floats, rounded up to 64 floats)
+ * plus the chunk-start state and its gradient (2 * dk * dv floats). */
+size_t ckda_chunk_bwd_workspace_size(int B, int H, int T, int dk, int dv, int dtype);
+
+/* Backward of the chunked forward: the gradients of a loss L with respect to
+ * every input, given do = dL/do and dhT = dL/dH_T.
+ *
+ *   q, k, v, alpha, beta, h0 : the forward's inputs (layouts, dtype and h0 as
+ *                 ckda_chunk_fwd; h0 NULL = zero initial state)
+ *   dout        : [B, H, T, dv] dtype, dL/do
+ *   dhT         : [B, H, dk, dv] fp32 dL/dH_T, or NULL for zero
+ *   dq, dk, dalpha : [B, H, T, dk] fp32;  dv : [B, H, T, dv] fp32
+ *   dbeta       : [B, H, T] fp32;  dh0 : [B, H, dk, dv] fp32, or NULL to skip
+ *   workspace   : at least ckda_chunk_bwd_workspace_size() bytes, 256-byte
+ *                 aligned, contents ignored on entry and unspecified on return
+ *
+ * The reverse-mode derivative of the recurrence of ckda_chunk_fwd (paper
+ * Eq. (1)) with the gates as the signed numbers they are: dalpha is the plain
+ * partial derivative, exact at zero gates, and no gate is floored or divided
+ * by (a gate derivative collects every pair of positions across it with the
+ * gate's own factor left out).  Computed in fp32 from the inputs (the forward's
+ * workspace is not needed): a chunk-parallel pass forms each 32-position
+ * chunk's solve and decayed Gram matrices, two sequential passes carry the
+ * state forward and its gradient backward from chunk to chunk, and a
+ * chunk-parallel pass forms every per-token gradient.  The CKDA_FUSE_*
+ * prologue is not differentiated here (the gradients are with respect to the
+ * gates, beta and vectors the recurrence consumes).
+ *
+ * Supported: dtype F32 or BF16; dk, dv in {16, 32, 64, 128}; any T >= 0.
+ * Outputs must not overlap each other, any input or the workspace. */
+int ckda_chunk_bwd(const void* q, const void* k, const void* v, const void* alpha, const void* beta,
+                   const float* h0, const void* dout, const float* dhT, float* dq, float* dk, float* dv,
+                   float* dalpha, float* dbeta, float* dh0, int B, int H, int T, int dk_, int dv_, int dtype,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
 /* One recurrent decode step for N sequences x H heads, state in place.
  *
  *   q, k, alpha : [N, H, dk]     dtype

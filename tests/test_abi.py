@@ -209,6 +209,45 @@ def test_scalar_gate_flag_checks():
     assert call_fwd_gather(flags=8)[0] == 3
 
 
+def call_bwd(**kw):
+    L = ck.lib()
+    B, H, T, dk, dv = 1, 2, kw.get("T", 64), kw.get("dk", 64), 64
+    p = dict(q=BASE, k=BASE + 1 * MB, v=BASE + 2 * MB, alpha=BASE + 3 * MB, beta=BASE + 4 * MB, h0=BASE + 5 * MB,
+             do=BASE + 6 * MB, dhT=BASE + 7 * MB, dq=BASE + 8 * MB, dk=BASE + 9 * MB, dv=BASE + 10 * MB,
+             da=BASE + 11 * MB, db=BASE + 12 * MB, dh0=BASE + 13 * MB, ws=BASE + 16 * MB)
+    p.update({k: v for k, v in kw.items() if k in p})
+    rc = L.ckda_chunk_bwd(*(p[n] for n in ("q", "k", "v", "alpha", "beta", "h0", "do", "dhT", "dq", "dk", "dv", "da",
+                                           "db", "dh0")), B, H, T, dk, dv, kw.get("dtype", 1), p["ws"],
+                          kw.get("wsb", 64 * MB), None)
+    return rc, L.ckda_last_error().decode()
+
+
+def test_bwd_workspace_size():
+    L = ck.lib()
+    # per 32-position chunk: (4*32*32 + 3*32*dk + dk) floats rounded to 64, plus 2 dk dv floats
+    per = ((4 * 32 * 32 + 3 * 32 * 128 + 128 + 63) // 64 * 64 + 2 * 128 * 128) * 4
+    assert L.ckda_chunk_bwd_workspace_size(1, 1, 32, 128, 128, 1) == per
+    assert L.ckda_chunk_bwd_workspace_size(4, 16, 4096, 128, 128, 1) == 64 * 128 * per
+    assert L.ckda_chunk_bwd_workspace_size(1, 1, 33, 128, 128, 1) == 2 * per
+    assert L.ckda_chunk_bwd_workspace_size(1, 1, 32, 96, 128, 1) == 0
+    assert L.ckda_chunk_bwd_workspace_size(1, 1, 32, 128, 128, 5) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(do=None), 1), (dict(dq=None), 1), (dict(da=None), 1),
+    (dict(T=-1), 2), (dict(dk=48), 3), (dict(dtype=3), 3),
+    (dict(ws=None), 5), (dict(wsb=1024), 5),
+    (dict(dq=BASE + 2), 2),
+    (dict(dq=BASE + 1 * MB), 4),                 # dq overlaps k
+    (dict(dv=BASE + 8 * MB + 64), 4),            # dv overlaps dq
+    (dict(dh0=BASE + 16 * MB + 256), 4),         # dh0 inside the workspace
+])
+def test_bwd_rejects(kw, status):
+    rc, msg = call_bwd(**kw)
+    assert rc == status, (rc, msg)
+    assert msg.startswith("ckda_chunk_bwd")
+
+
 def test_prologue_flag_values_agree():
     text = open(HEADER).read()
     defs = dict(re.findall(r"#define (CKDA_FUSE_\w+) (\d+)", text))
