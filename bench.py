@@ -9,8 +9,9 @@ state updated in place) is timed in the same run and reported under "decode",
 both again with the per-token prologue fused (gates from logits, unit-norm
 keys) under "fused_prologue", the state-reduced workload (B2 H32 T32768,
 d_k 64 kept of 128 channels by an in-kernel gather) under "channel_gather",
-and the comparators (scalar gate; DeltaProduct_2 forward and decode) under
-"comparators".
+the comparators (scalar gate; DeltaProduct_2 forward and decode) under
+"comparators", and the backward (all gradients) with the forward + backward
+throughput under "backward".
 
 Prints ONE JSON line.  `value` is tokens/s of the forward (a token is one
 (batch, position) across all heads), inputs resident in HBM: tokens per step
@@ -271,6 +272,15 @@ def main():
                                                 chunk=gw.chunk, workspace=gws, o=go, hT=ghT), gsteps)
     del pre, gd, gws, go
 
+    # ---- backward on the bench workload (ckda_chunk_bwd, fp32 gradients)
+    log("[bench] backward")
+    bdo, bdhT = gen.make_output_grads(w, 99)
+    bdo, bdhT = bdo.to(dev), bdhT.to(dev)
+    bws = torch.empty(ck.bwd_workspace_size(w.B, w.H, w.T, w.dk, w.dv, ck.DTYPE_BF16), dtype=torch.uint8, device=dev)
+    bwd_ms = timed(lambda: ck.chunk_bwd(d["q"], d["k"], d["v"], d["alpha"], d["beta"], bdo, h0=d["h0"], dhT=bdhT,
+                                        workspace=bws), max(3, a.steps // 3))
+    del bws
+
     # ---- comparators on the bench shape: the scalar (Gated DeltaNet) gate and
     # ungated DeltaProduct_2 (two delta-rule updates per token), and the
     # DeltaProduct_2 decode step on the decode workload
@@ -353,6 +363,13 @@ def main():
             "total_GB_s": round(dec_gbs_total, 1),
             "frac_of_hbm_peak": round(dec_gbs_total / HBM_PEAK_GBS, 4),
             "device_copy_GB_s": round(copy_gbs, 1),
+        },
+        "backward": {
+            "workload": w.name,
+            "call_ms_mean": round(bwd_ms, 4),
+            "tokens_per_s": round(tokens / (bwd_ms * 1e-3), 1),
+            "forward_plus_backward_tokens_per_s": round(tokens / ((bwd_ms + call_ms) * 1e-3), 1),
+            "gradients": "fp32 dq, dk, dv, dalpha, dbeta, dh0",
         },
         "comparators": {
             "scalar_gate_forward_call_ms_mean": round(scalar_ms, 4),
