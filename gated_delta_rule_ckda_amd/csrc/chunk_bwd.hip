@@ -57,25 +57,35 @@ struct BwdRec {
 // Operands are read from LDS through strides, so a transposed operand is only
 // a different pair of strides:  A(i, k) = a[i * ai + k * ak],
 // B(k, j) = b[k * bk + j * bj].
-__device__ __forceinline__ f32x4 mfma_lds(f32x4 acc, const float* a, int ai, int ak, const float* b, int bk, int bj,
-                                          int K) {
+// (K is a compile-time constant so that every operand load of the product
+// is issued before the chain of matrix-core steps.)
+template <int K>
+__device__ __forceinline__ f32x4 mfma_lds(f32x4 acc, const float* a, int ai, int ak, const float* b, int bk, int bj) {
   const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
-  for (int k0 = 0; k0 < K; k0 += 4)
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[r * ai + (k0 + g) * ak], b[(k0 + g) * bk + r * bj], acc, 0, 0, 0);
+  float av[K / 4], bv[K / 4];
+#pragma unroll
+  for (int s = 0; s < K / 4; ++s) {
+    av[s] = a[r * ai + (4 * s + g) * ak];
+    bv[s] = b[(4 * s + g) * bk + r * bj];
+  }
+#pragma unroll
+  for (int s = 0; s < K / 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[s], bv[s], acc, 0, 0, 0);
   return acc;
 }
 
 // D (Mr x Nc, multiples of 16) = scale * A B  (ACC: D += scale * A B), the
 // 16 x 16 tiles spread over the waves; D(i, j) = d[i * di + j].
-template <bool ACC>
+// W0: the wave that takes the first tile (two products of one phase can so
+// run on different waves).
+template <bool ACC, int K, int W0 = 0>
 __device__ __forceinline__ void gemm_lds(float* d, int di, const float* a, int ai, int ak, const float* b, int bk,
-                                         int bj, int Mr, int Nc, int K, float scale) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
+                                         int bj, int Mr, int Nc, float scale) {
   constexpr int NW = kBThreads / 64;
+  const int wave = ((threadIdx.x >> 6) + NW - W0) % NW, lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
   const int tn = Nc / 16, tiles = (Mr / 16) * tn;
   for (int ti = wave; ti < tiles; ti += NW) {
     const int i0 = (ti / tn) * 16, j0 = (ti % tn) * 16;
-    const f32x4 acc = mfma_lds(zero4(), a + i0 * ai, ai, ak, b + j0 * bj, bk, bj, K);
+    const f32x4 acc = mfma_lds<K>(zero4(), a + i0 * ai, ai, ak, b + j0 * bj, bk, bj);
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       float* p = d + (i0 + 4 * g + v) * di + j0 + r;
@@ -179,14 +189,20 @@ __global__ __launch_bounds__(kBThreads) void chunk_bwd_prep_kernel(const T* q, c
     __syncthreads();
   }
   // T = (I + Diag(beta) S)^-1, unit lower triangular, one column per thread
+  // held in registers: T[i][j] = -beta_i sum_{l < i} S[i][l] T[l][j] for i > j
+  // (the rows of S are read by every lane at once)
   if (tid < C) {
     const int j = tid;
-    for (int i = 0; i < C; ++i) sT[i * CP + j] = i == j ? 1.f : 0.f;
-    for (int i = j + 1; i < C; ++i) {
+    float tc[C];
+#pragma unroll
+    for (int i = 0; i < C; ++i) {
       float acc = 0.f;
-      for (int l = j; l < i; ++l) acc += sS[i * CP + l] * sT[l * CP + j];
-      sT[i * CP + j] = -sb[i] * acc;
+#pragma unroll
+      for (int l = 0; l < i; ++l) acc += sS[i * CP + l] * tc[l];
+      tc[i] = i > j ? -sb[i] * acc : (i == j ? 1.f : 0.f);
     }
+#pragma unroll
+    for (int i = 0; i < C; ++i) sT[i * CP + j] = tc[i];
   }
   __syncthreads();
   for (int e = tid; e < C * C; e += kBThreads) {
@@ -199,54 +215,86 @@ __global__ __launch_bounds__(kBThreads) void chunk_bwd_prep_kernel(const T* q, c
 }
 
 // ============================================================ states (forward, sequential)
+// The next chunk's operands are fetched into registers while the current one
+// is computed, and placed into LDS at the top of the next iteration.
 template <typename T, int DK>
 __global__ __launch_bounds__(kBThreads) void chunk_bwd_states_kernel(const T* v, const float* __restrict__ h0,
                                                                      const float* __restrict__ rec,
                                                                      float* __restrict__ hc, int T_len, int nchunks,
                                                                      int dv) {
   constexpr int C = kBC, DS = kBDS, DKP = DK + 1, CP = C + 1, DSP = DS + 1;
+  constexpr int NK = (C * DK + kBThreads - 1) / kBThreads, NT = (C * C + kBThreads - 1) / kBThreads;
+  constexpr int NV = (C * DS + kBThreads - 1) / kBThreads;
   using R = BwdRec<DK>;
-  __shared__ float sH[DK * DSP], sKG[C * DKP], sKR[C * DKP], sTB[C * CP], sV[C * DSP], sX[C * DSP], sU[C * DSP],
-      sGC[DK];
+  __shared__ float sH[DK * DSP], sKG[C * DKP], sKR[C * DKP], sTB[C * CP], sX[C * DSP], sU[C * DSP], sGC[DK];
   const int tid = threadIdx.x;
   const int nsl = dv / DS;
   const long long bh = blockIdx.x / nsl;
   const int col0 = (blockIdx.x % nsl) * DS;
+  float rKG[NK], rKR[NK], rTB[NT], rV[NV], rGC = 0.f;
+  auto fetch = [&](int c) __attribute__((always_inline)) {
+    const float* rc = rec + (size_t)(bh * nchunks + c) * R::FLOATS;
+    const int t0 = c * C, cv = min(C, T_len - t0);
+#pragma unroll
+    for (int i = 0; i < NK; ++i) {
+      const int e = tid + i * kBThreads;
+      if (e < C * DK) {
+        rKG[i] = rc[R::KG_OFF + e];
+        rKR[i] = rc[R::KR_OFF + e];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      const int e = tid + i * kBThreads;
+      if (e < C * C) rTB[i] = rc[R::TB_OFF + e];
+    }
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int e = tid + i * kBThreads, t = e / DS, j = e % DS;
+      const bool ok = e < C * DS && t < cv;
+      rV[i] = ld_or(v, ok ? (size_t)(bh * T_len + t0 + t) * dv + col0 + j : 0, ok, 0.f);
+    }
+    if (tid < DK) rGC = rc[R::GC_OFF + tid];
+  };
   for (int e = tid; e < DK * DS; e += kBThreads) {
     const int i = e / DS, j = e % DS;
     sH[i * DSP + j] = h0 ? h0[(bh * DK + i) * (long long)dv + col0 + j] : 0.f;
   }
-  __syncthreads();
+  if (nchunks > 0) fetch(0);
   for (int c = 0; c < nchunks; ++c) {
     const long long chunk = bh * nchunks + c;
-    const float* rc = rec + (size_t)chunk * R::FLOATS;
-    const int t0 = c * C, cv = min(C, T_len - t0);
+#pragma unroll
+    for (int i = 0; i < NK; ++i) {
+      const int e = tid + i * kBThreads;
+      if (e < C * DK) {
+        sKG[(e / DK) * DKP + e % DK] = rKG[i];
+        sKR[(e / DK) * DKP + e % DK] = rKR[i];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      const int e = tid + i * kBThreads;
+      if (e < C * C) sTB[(e / C) * CP + e % C] = rTB[i];
+    }
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int e = tid + i * kBThreads;
+      if (e < C * DS) sX[(e / DS) * DSP + e % DS] = rV[i];   // X starts as V
+    }
+    if (tid < DK) sGC[tid] = rGC;
+    __syncthreads();
+    if (c + 1 < nchunks) fetch(c + 1);
     for (int e = tid; e < DK * DS; e += kBThreads) {
       const int i = e / DS, j = e % DS;
       hc[(size_t)chunk * DK * dv + (size_t)i * dv + col0 + j] = sH[i * DSP + j];
     }
-    for (int e = tid; e < C * DK; e += kBThreads) {
-      const int t = e / DK, ch = e % DK;
-      sKG[t * DKP + ch] = rc[R::KG_OFF + e];
-      sKR[t * DKP + ch] = rc[R::KR_OFF + e];
-    }
-    for (int e = tid; e < C * C; e += kBThreads) sTB[(e / C) * CP + e % C] = rc[R::TB_OFF + e];
-    for (int e = tid; e < C * DS; e += kBThreads) {
-      const int t = e / DS, j = e % DS;
-      const bool ok = t < cv;
-      sV[t * DSP + j] = ld_or(v, ok ? (size_t)(bh * T_len + t0 + t) * dv + col0 + j : 0, ok, 0.f);
-    }
-    if (tid < DK) sGC[tid] = rc[R::GC_OFF + tid];
+    gemm_lds<true, DK>(sX, DSP, sKG, DKP, 1, sH, DSP, 1, C, DS, -1.f);      // X = V - KG H
     __syncthreads();
-    for (int e = tid; e < C * DS; e += kBThreads) sX[(e / DS) * DSP + e % DS] = sV[(e / DS) * DSP + e % DS];
-    __syncthreads();
-    gemm_lds<true>(sX, DSP, sKG, DKP, 1, sH, DSP, 1, C, DS, DK, -1.f);      // X = V - KG H
-    __syncthreads();
-    gemm_lds<false>(sU, DSP, sTB, CP, 1, sX, DSP, 1, C, DS, C, 1.f);        // U = TB X
+    gemm_lds<false, C>(sU, DSP, sTB, CP, 1, sX, DSP, 1, C, DS, 1.f);        // U = TB X
     __syncthreads();
     for (int e = tid; e < DK * DS; e += kBThreads) sH[(e / DS) * DSP + e % DS] *= sGC[e / DS];
     __syncthreads();
-    gemm_lds<true>(sH, DSP, sKR, 1, DKP, sU, DSP, 1, DK, DS, C, 1.f);       // H = Gamma_C . H + KR^T U
+    gemm_lds<true, C>(sH, DSP, sKR, 1, DKP, sU, DSP, 1, DK, DS, 1.f);       // H = Gamma_C . H + KR^T U
     __syncthreads();
   }
 }
@@ -258,6 +306,8 @@ __global__ __launch_bounds__(kBThreads) void chunk_bwd_dstates_kernel(const T* d
                                                                       float* __restrict__ dhn, float* __restrict__ dh0,
                                                                       int T_len, int nchunks, int dv) {
   constexpr int C = kBC, DS = kBDS, DKP = DK + 1, CP = C + 1, DSP = DS + 1;
+  constexpr int NK = (C * DK + kBThreads - 1) / kBThreads, NT = (C * C + kBThreads - 1) / kBThreads;
+  constexpr int NV = (C * DS + kBThreads - 1) / kBThreads;
   using R = BwdRec<DK>;
   __shared__ float sdH[DK * DSP], sKG[C * DKP], sKR[C * DKP], sQG[C * DKP], sM[C * CP], sTB[C * CP], sdO[C * DSP],
       sdU[C * DSP], sdX[C * DSP], sGC[DK];
@@ -265,45 +315,81 @@ __global__ __launch_bounds__(kBThreads) void chunk_bwd_dstates_kernel(const T* d
   const int nsl = dv / DS;
   const long long bh = blockIdx.x / nsl;
   const int col0 = (blockIdx.x % nsl) * DS;
+  float rKG[NK], rKR[NK], rQG[NK], rM[NT], rTB[NT], rO[NV], rGC = 0.f;
+  auto fetch = [&](int c) __attribute__((always_inline)) {
+    const float* rc = rec + (size_t)(bh * nchunks + c) * R::FLOATS;
+    const int t0 = c * C, cv = min(C, T_len - t0);
+#pragma unroll
+    for (int i = 0; i < NK; ++i) {
+      const int e = tid + i * kBThreads;
+      if (e < C * DK) {
+        rKG[i] = rc[R::KG_OFF + e];
+        rKR[i] = rc[R::KR_OFF + e];
+        rQG[i] = rc[R::QG_OFF + e];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      const int e = tid + i * kBThreads;
+      if (e < C * C) {
+        rM[i] = rc[R::M_OFF + e];
+        rTB[i] = rc[R::TB_OFF + e];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int e = tid + i * kBThreads, t = e / DS, j = e % DS;
+      const bool ok = e < C * DS && t < cv;
+      rO[i] = ld_or(dout, ok ? (size_t)(bh * T_len + t0 + t) * dv + col0 + j : 0, ok, 0.f);
+    }
+    if (tid < DK) rGC = rc[R::GC_OFF + tid];
+  };
   for (int e = tid; e < DK * DS; e += kBThreads) {
     const int i = e / DS, j = e % DS;
     sdH[i * DSP + j] = dhT ? dhT[(bh * DK + i) * (long long)dv + col0 + j] : 0.f;
   }
-  __syncthreads();
+  if (nchunks > 0) fetch(nchunks - 1);
   for (int c = nchunks - 1; c >= 0; --c) {
     const long long chunk = bh * nchunks + c;
-    const float* rc = rec + (size_t)chunk * R::FLOATS;
-    const int t0 = c * C, cv = min(C, T_len - t0);
+#pragma unroll
+    for (int i = 0; i < NK; ++i) {
+      const int e = tid + i * kBThreads;
+      if (e < C * DK) {
+        const int o = (e / DK) * DKP + e % DK;
+        sKG[o] = rKG[i];
+        sKR[o] = rKR[i];
+        sQG[o] = rQG[i];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      const int e = tid + i * kBThreads;
+      if (e < C * C) {
+        sM[(e / C) * CP + e % C] = rM[i];
+        sTB[(e / C) * CP + e % C] = rTB[i];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int e = tid + i * kBThreads;
+      if (e < C * DS) sdO[(e / DS) * DSP + e % DS] = rO[i];
+    }
+    if (tid < DK) sGC[tid] = rGC;
+    __syncthreads();
+    if (c > 0) fetch(c - 1);
     for (int e = tid; e < DK * DS; e += kBThreads) {
       const int i = e / DS, j = e % DS;
       dhn[(size_t)chunk * DK * dv + (size_t)i * dv + col0 + j] = sdH[i * DSP + j];
     }
-    for (int e = tid; e < C * DK; e += kBThreads) {
-      const int t = e / DK, ch = e % DK;
-      sKG[t * DKP + ch] = rc[R::KG_OFF + e];
-      sKR[t * DKP + ch] = rc[R::KR_OFF + e];
-      sQG[t * DKP + ch] = rc[R::QG_OFF + e];
-    }
-    for (int e = tid; e < C * C; e += kBThreads) {
-      sM[(e / C) * CP + e % C] = rc[R::M_OFF + e];
-      sTB[(e / C) * CP + e % C] = rc[R::TB_OFF + e];
-    }
-    for (int e = tid; e < C * DS; e += kBThreads) {
-      const int t = e / DS, j = e % DS;
-      const bool ok = t < cv;
-      sdO[t * DSP + j] = ld_or(dout, ok ? (size_t)(bh * T_len + t0 + t) * dv + col0 + j : 0, ok, 0.f);
-    }
-    if (tid < DK) sGC[tid] = rc[R::GC_OFF + tid];
+    gemm_lds<false, C>(sdU, DSP, sM, 1, CP, sdO, DSP, 1, C, DS, 1.f);       // dU = M^T dO
+    gemm_lds<true, DK>(sdU, DSP, sKR, DKP, 1, sdH, DSP, 1, C, DS, 1.f);     //    + KR dH'  (same tiles, same wave)
     __syncthreads();
-    gemm_lds<false>(sdU, DSP, sM, 1, CP, sdO, DSP, 1, C, DS, C, 1.f);       // dU = M^T dO
-    gemm_lds<true>(sdU, DSP, sKR, DKP, 1, sdH, DSP, 1, C, DS, DK, 1.f);     //    + KR dH'  (same tiles, same wave)
-    __syncthreads();
-    gemm_lds<false>(sdX, DSP, sTB, 1, CP, sdU, DSP, 1, C, DS, C, 1.f);      // dX = TB^T dU
+    gemm_lds<false, C>(sdX, DSP, sTB, 1, CP, sdU, DSP, 1, C, DS, 1.f);      // dX = TB^T dU
     __syncthreads();
     for (int e = tid; e < DK * DS; e += kBThreads) sdH[(e / DS) * DSP + e % DS] *= sGC[e / DS];
     __syncthreads();
-    gemm_lds<true>(sdH, DSP, sQG, 1, DKP, sdO, DSP, 1, DK, DS, C, 1.f);     // + QG^T dO
-    gemm_lds<true>(sdH, DSP, sKG, 1, DKP, sdX, DSP, 1, DK, DS, C, -1.f);    // - KG^T dX
+    gemm_lds<true, C>(sdH, DSP, sQG, 1, DKP, sdO, DSP, 1, DK, DS, 1.f);     // + QG^T dO
+    gemm_lds<true, C>(sdH, DSP, sKG, 1, DKP, sdX, DSP, 1, DK, DS, -1.f);    // - KG^T dX
     __syncthreads();
   }
   if (dh0)
@@ -382,28 +468,57 @@ __global__ __launch_bounds__(kBThreads) void chunk_bwd_grad_kernel(
   for (int i = 0; i < TMW; ++i) am[i] = atb[i] = zero4();
   const float* hcc = hc + (size_t)chunk * DK * dv;
   const float* dhc = dhn + (size_t)chunk * DK * dv;
+  // one value slice's operands, fetched into registers a slice ahead
+  constexpr int NH = (DK * DS + kBThreads - 1) / kBThreads, NV = (C * DS + kBThreads - 1) / kBThreads;
+  float rH[NH], rdH[NH], rV[NV], rO[NV];
+  auto fetch = [&](int col0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NH; ++i) {
+      const int e = tid + i * kBThreads, ii = e / DS, j = e % DS;
+      if (e < DK * DS) {
+        rH[i] = hcc[(size_t)ii * dv + col0 + j];
+        rdH[i] = dhc[(size_t)ii * dv + col0 + j];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int e = tid + i * kBThreads, t = e / DS, j = e % DS;
+      const bool ok = e < C * DS && t < cv;
+      const size_t gi = ok ? (size_t)(row0 + t) * dv + col0 + j : 0;
+      rV[i] = ld_or(v, gi, ok, 0.f);
+      rO[i] = ld_or(dout, gi, ok, 0.f);
+    }
+  };
+  fetch(0);
   for (int col0 = 0; col0 < dv; col0 += DS) {
     __syncthreads();   // previous slice fully consumed (and, first time, the loads above)
-    for (int e = tid; e < DK * DS; e += kBThreads) {
-      const int i = e / DS, j = e % DS;
-      sH[i * DSP + j] = hcc[(size_t)i * dv + col0 + j];
-      sdH[i * DSP + j] = dhc[(size_t)i * dv + col0 + j];
+#pragma unroll
+    for (int i = 0; i < NH; ++i) {
+      const int e = tid + i * kBThreads;
+      if (e < DK * DS) {
+        sH[(e / DS) * DSP + e % DS] = rH[i];
+        sdH[(e / DS) * DSP + e % DS] = rdH[i];
+      }
     }
-    for (int e = tid; e < C * DS; e += kBThreads) {
-      const int t = e / DS, j = e % DS;
-      const bool ok = t < cv;
-      const size_t gi = ok ? (size_t)(row0 + t) * dv + col0 + j : 0;
-      sV[t * DSP + j] = ld_or(v, gi, ok, 0.f);
-      sdO[t * DSP + j] = ld_or(dout, gi, ok, 0.f);
-      sX[t * DSP + j] = ld_or(v, gi, ok, 0.f);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int e = tid + i * kBThreads;
+      if (e < C * DS) {
+        const int o = (e / DS) * DSP + e % DS;
+        sV[o] = rV[i];
+        sX[o] = rV[i];
+        sdO[o] = rO[i];
+      }
     }
     __syncthreads();
-    gemm_lds<true>(sX, DSP, sKG, DKP, 1, sH, DSP, 1, C, DS, DK, -1.f);      // X = V - KG H
-    gemm_lds<false>(sdU, DSP, sM, 1, CP, sdO, DSP, 1, C, DS, C, 1.f);       // dU = M^T dO + KR dH'
-    gemm_lds<true>(sdU, DSP, sKR, DKP, 1, sdH, DSP, 1, C, DS, DK, 1.f);
+    if (col0 + DS < dv) fetch(col0 + DS);
+    // X and dU on different waves
+    gemm_lds<true, DK>(sX, DSP, sKG, DKP, 1, sH, DSP, 1, C, DS, -1.f);           // X = V - KG H
+    gemm_lds<false, C, 2>(sdU, DSP, sM, 1, CP, sdO, DSP, 1, C, DS, 1.f);         // dU = M^T dO + KR dH'
+    gemm_lds<true, DK, 2>(sdU, DSP, sKR, DKP, 1, sdH, DSP, 1, C, DS, 1.f);
     __syncthreads();
-    gemm_lds<false>(sU, DSP, sTB, CP, 1, sX, DSP, 1, C, DS, C, 1.f);        // U = TB X
-    gemm_lds<false>(sdX, DSP, sTB, 1, CP, sdU, DSP, 1, C, DS, C, 1.f);      // dX = TB^T dU
+    gemm_lds<false, C>(sU, DSP, sTB, CP, 1, sX, DSP, 1, C, DS, 1.f);             // U = TB X
+    gemm_lds<false, C, 2>(sdX, DSP, sTB, 1, CP, sdU, DSP, 1, C, DS, 1.f);        // dX = TB^T dU
     if (tid < DK) {
       float acc = 0.f;
       for (int j = 0; j < DS; ++j) acc += sH[tid * DSP + j] * sdH[tid * DSP + j];
@@ -420,9 +535,9 @@ __global__ __launch_bounds__(kBThreads) void chunk_bwd_grad_kernel(
       const int ti = wave + NW * i;
       if (ti < TQ) {
         const int i0 = (ti / (DK / 16)) * 16, j0 = (ti % (DK / 16)) * 16;
-        aqg[i] = mfma_lds(aqg[i], sdO + i0 * DSP, DSP, 1, sH + j0 * DSP, 1, DSP, DS);
-        akg[i] = mfma_lds(akg[i], sdX + i0 * DSP, DSP, 1, sH + j0 * DSP, 1, DSP, DS);
-        akr[i] = mfma_lds(akr[i], sU + i0 * DSP, DSP, 1, sdH + j0 * DSP, 1, DSP, DS);
+        aqg[i] = mfma_lds<DS>(aqg[i], sdO + i0 * DSP, DSP, 1, sH + j0 * DSP, 1, DSP);
+        akg[i] = mfma_lds<DS>(akg[i], sdX + i0 * DSP, DSP, 1, sH + j0 * DSP, 1, DSP);
+        akr[i] = mfma_lds<DS>(akr[i], sU + i0 * DSP, DSP, 1, sdH + j0 * DSP, 1, DSP);
       }
     }
     // dM += dO U^T, dTB += dU X^T   (C x C, K = DS)
@@ -431,8 +546,8 @@ __global__ __launch_bounds__(kBThreads) void chunk_bwd_grad_kernel(
       const int ti = wave + NW * i;
       if (ti < TM) {
         const int i0 = (ti / (C / 16)) * 16, j0 = (ti % (C / 16)) * 16;
-        am[i] = mfma_lds(am[i], sdO + i0 * DSP, DSP, 1, sU + j0 * DSP, 1, DSP, DS);
-        atb[i] = mfma_lds(atb[i], sdU + i0 * DSP, DSP, 1, sX + j0 * DSP, 1, DSP, DS);
+        am[i] = mfma_lds<DS>(am[i], sdO + i0 * DSP, DSP, 1, sU + j0 * DSP, 1, DSP);
+        atb[i] = mfma_lds<DS>(atb[i], sdU + i0 * DSP, DSP, 1, sX + j0 * DSP, 1, DSP);
       }
     }
   }
@@ -478,9 +593,9 @@ __global__ __launch_bounds__(kBThreads) void chunk_bwd_grad_kernel(
   __syncthreads();
   for (int e = tid; e < C * C; e += kBThreads) sdTB[(e / C) * CP + e % C] *= sb[e % C];   // dT = dTB Diag(beta)
   __syncthreads();
-  gemm_lds<false>(sP, CP, sdTB, CP, 1, sT, 1, CP, C, C, C, 1.f);                         // P = dT T^T
+  gemm_lds<false, C>(sP, CP, sdTB, CP, 1, sT, 1, CP, C, C, 1.f);                         // P = dT T^T
   __syncthreads();
-  gemm_lds<false>(sdTB, CP, sT, 1, CP, sP, CP, 1, C, C, C, -1.f);                        // dA = -T^T P
+  gemm_lds<false, C>(sdTB, CP, sT, 1, CP, sP, CP, 1, C, C, -1.f);                        // dA = -T^T P
   __syncthreads();
   if (tid < C) {   // strictly lower part: dbeta += rowsum(dA . S), dS = Diag(beta) dA
     const int t = tid;
@@ -496,10 +611,10 @@ __global__ __launch_bounds__(kBThreads) void chunk_bwd_grad_kernel(
   float* sdS = sdTB;
 
   // ---- per channel: direct terms, gate scans, recursive halving of S and M.
-  // The accumulators live in this channel's column of the (now consumed)
+  // The accumulators live in each channel's column of the (now consumed)
   // dQG / dKG / dKR arrays: gq, gk, ga; sG is a per-channel scratch column.
-  if (tid < DK) {
-    const int ch = tid;
+  {
+    const int ch = tid % DK, part = tid / DK;   // two threads per channel in the halving
     auto Q = [&](int t) { return sq[t * DKP + ch]; };
     auto K = [&](int t) { return sk[t * DKP + ch]; };
     auto A = [&](int t) { return sa[t * DKP + ch]; };
@@ -507,98 +622,156 @@ __global__ __launch_bounds__(kBThreads) void chunk_bwd_grad_kernel(
     float* gk = sdKG + ch;
     float* ga = sdKR + ch;
     float* sg = sG + ch;     // element t at sg[t * DK]
-    // sg[t] = G(C-1, t) = alpha_{t+1} ... alpha_{C-1}
-    {
-      float e = 1.f;
-      for (int t = C - 1; t >= 0; --t) {
-        sg[t * DK] = e;
-        e *= A(t);
-      }
-    }
-    // forward: direct terms, the KR scan (pairs with the chunk end) and the
-    // Gamma_C term; pre[t] = Gamma_{t-1}
-    float pre[C + 1];
-    pre[0] = 1.f;
-    {
-      float f = 0.f;
-      const float gc = sGC[ch];
-#pragma unroll
-      for (int t = 0; t < C; ++t) {
-        pre[t + 1] = pre[t] * A(t);
-        const float dqg = gq[t * DKP], dkg = gk[t * DKP], dkr = ga[t * DKP], se = sg[t * DK];
-        const float dmd = sdM[t * CP + t];
-        gq[t * DKP] = dmd * K(t) + dqg * pre[t + 1];
-        gk[t * DKP] = dmd * Q(t) + dkg * pre[t + 1] + dkr * se;
-        ga[t * DKP] = se * f + gc * pre[t] * se;
-        f = A(t) * f + dkr * K(t);
-        sg[t * DK] = dqg * Q(t) + dkg * K(t);   // R_t of the Gamma_t scan
-      }
-    }
-    {   // Gamma_t terms (pairs with the chunk start): reverse scan of R_t
-      float bs = 0.f;
-#pragma unroll
-      for (int s = C - 1; s >= 0; --s) {
-        bs = sg[s * DK] + (s + 1 < C ? A(s + 1) * bs : 0.f);
-        ga[s * DKP] += pre[s] * bs;
-      }
-    }
-    // recursive halving: blocks [lo, lo + 2h), L = [lo, m], R = [m + 1, lo + 2h - 1];
-    // sg holds G(m, j) on L and G(t, m) on R
-    for (int h = C / 2; h >= 1; h >>= 1) {
-      for (int lo = 0; lo < C; lo += 2 * h) {
-        const int m = lo + h - 1;
-        {
-          float f = 1.f;
-          for (int i = 0; i < h; ++i) {
-            f *= A(m + 1 + i);
-            sg[(m + 1 + i) * DK] = f;
-          }
-          float e = 1.f;
-          for (int i = h - 1; i >= 0; --i) {
-            sg[(lo + i) * DK] = e;
-            e *= A(lo + i);
-          }
+    if (tid < DK) {
+      // sg[t] = G(C-1, t) = alpha_{t+1} ... alpha_{C-1}
+      {
+        float e = 1.f;
+        for (int t = C - 1; t >= 0; --t) {
+          sg[t * DK] = e;
+          e *= A(t);
         }
-        // rows t in R, last to first: cross terms with L, and the scan for
-        // the gates s in R, G(s - 1, m) sum_{t >= s} (q_t zm_t + k_t zs_t) G(t, s)
-        float bs = 0.f;
-        for (int i = h - 1; i >= 0; --i) {
-          const int t = m + 1 + i;
-          float zm = 0.f, zs = 0.f;
-          for (int jj = 0; jj < h; ++jj) {
-            const float ky = K(lo + jj) * sg[(lo + jj) * DK];
-            zm += sdM[t * CP + lo + jj] * ky;
-            zs += sdS[t * CP + lo + jj] * ky;
-          }
-          const float gr = sg[t * DK];
-          gq[t * DKP] += gr * zm;
-          gk[t * DKP] += gr * zs;
-          bs = Q(t) * zm + K(t) * zs + (i + 1 < h ? A(t + 1) * bs : 0.f);
-          ga[t * DKP] += (i > 0 ? sg[(t - 1) * DK] : 1.f) * bs;
-        }
-        // rows j in L, first to last: cross terms with R, and the scan for
-        // the gates s in L, G(m, s) sum_{j < s} k_j zl_j G(s - 1, j)
+      }
+      // forward: direct terms, the KR scan (pairs with the chunk end) and the
+      // Gamma_C term; pre[t] = Gamma_{t-1}
+      float pre[C + 1];
+      pre[0] = 1.f;
+      {
         float f = 0.f;
-        for (int jj = 0; jj < h; ++jj) {
-          const int j = lo + jj;
-          float zl = 0.f;
-          for (int i = 0; i < h; ++i) {
-            const int t = m + 1 + i;
-            zl += (sdM[t * CP + j] * Q(t) + sdS[t * CP + j] * K(t)) * sg[t * DK];
-          }
-          const float gl = sg[j * DK];
-          gk[j * DKP] += gl * zl;
-          ga[j * DKP] += gl * f;
-          f = A(j) * f + K(j) * zl;
+        const float gc = sGC[ch];
+#pragma unroll
+        for (int t = 0; t < C; ++t) {
+          pre[t + 1] = pre[t] * A(t);
+          const float dqg = gq[t * DKP], dkg = gk[t * DKP], dkr = ga[t * DKP], se = sg[t * DK];
+          const float dmd = sdM[t * CP + t];
+          gq[t * DKP] = dmd * K(t) + dqg * pre[t + 1];
+          gk[t * DKP] = dmd * Q(t) + dkg * pre[t + 1] + dkr * se;
+          ga[t * DKP] = se * f + gc * pre[t] * se;
+          f = A(t) * f + dkr * K(t);
+          sg[t * DK] = dqg * Q(t) + dkg * K(t);   // R_t of the Gamma_t scan
+        }
+      }
+      {   // Gamma_t terms (pairs with the chunk start): reverse scan of R_t
+        float bs = 0.f;
+#pragma unroll
+        for (int s = C - 1; s >= 0; --s) {
+          bs = sg[s * DK] + (s + 1 < C ? A(s + 1) * bs : 0.f);
+          ga[s * DKP] += pre[s] * bs;
         }
       }
     }
-    for (int t = 0; t < cv; ++t) {
-      const size_t o = (size_t)(row0 + t) * DK + ch;
-      dq[o] = gq[t * DKP];
-      dk[o] = gk[t * DKP];
-      dal[o] = ga[t * DKP];
-    }
+    __syncthreads();
+    // recursive halving: blocks [lo, lo + 2h), L = [lo, m], R = [m + 1, lo + 2h - 1];
+    // sg holds G(m, j) on L and G(t, m) on R.  With several blocks the two
+    // threads of a channel take alternate blocks; with one block, one takes
+    // the R rows and the other the L rows (they update disjoint positions).
+    // h is a compile-time constant per level so that the inner loops unroll.
+    const bool on = tid < 2 * DK;
+    auto factors_R = [&](int lo, int h) __attribute__((always_inline)) {
+      float f = 1.f;
+      for (int i = 0; i < h; ++i) {
+        f *= A(lo + h + i);
+        sg[(lo + h + i) * DK] = f;
+      }
+    };
+    auto factors_L = [&](int lo, int h) __attribute__((always_inline)) {
+      float e = 1.f;
+      for (int i = h - 1; i >= 0; --i) {
+        sg[(lo + i) * DK] = e;
+        e *= A(lo + i);
+      }
+    };
+    auto rows_R = [&](int lo, auto hh) __attribute__((always_inline)) {
+      // rows t in R, last to first: cross terms with L, and the scan for the
+      // gates s in R, G(s - 1, m) sum_{t >= s} (q_t zm_t + k_t zs_t) G(t, s)
+      constexpr int h = decltype(hh)::value;
+      const int m = lo + h - 1;
+      float ky[h];
+#pragma unroll
+      for (int jj = 0; jj < h; ++jj) ky[jj] = K(lo + jj) * sg[(lo + jj) * DK];
+      float bs = 0.f;
+#pragma unroll 1
+      for (int i = h - 1; i >= 0; --i) {
+        const int t = m + 1 + i;
+        float zm = 0.f, zs = 0.f;
+#pragma unroll
+        for (int jj = 0; jj < h; ++jj) {
+          zm += sdM[t * CP + lo + jj] * ky[jj];
+          zs += sdS[t * CP + lo + jj] * ky[jj];
+        }
+        const float gr = sg[t * DK];
+        gq[t * DKP] += gr * zm;
+        gk[t * DKP] += gr * zs;
+        bs = Q(t) * zm + K(t) * zs + (i + 1 < h ? A(t + 1) * bs : 0.f);
+        ga[t * DKP] += (i > 0 ? sg[(t - 1) * DK] : 1.f) * bs;
+      }
+    };
+    auto rows_L = [&](int lo, auto hh) __attribute__((always_inline)) {
+      // rows j in L, first to last: cross terms with R, and the scan for the
+      // gates s in L, G(m, s) sum_{j < s} k_j zl_j G(s - 1, j)
+      constexpr int h = decltype(hh)::value;
+      const int m = lo + h - 1;
+      float qr[h], kr[h];
+#pragma unroll
+      for (int i = 0; i < h; ++i) {
+        const float gr = sg[(m + 1 + i) * DK];
+        qr[i] = Q(m + 1 + i) * gr;
+        kr[i] = K(m + 1 + i) * gr;
+      }
+      float f = 0.f;
+#pragma unroll 1
+      for (int jj = 0; jj < h; ++jj) {
+        const int j = lo + jj;
+        float zl = 0.f;
+#pragma unroll
+        for (int i = 0; i < h; ++i) {
+          const int t = m + 1 + i;
+          zl += sdM[t * CP + j] * qr[i] + sdS[t * CP + j] * kr[i];
+        }
+        const float gl = sg[j * DK];
+        gk[j * DKP] += gl * zl;
+        ga[j * DKP] += gl * f;
+        f = A(j) * f + K(j) * zl;
+      }
+    };
+    auto level = [&](auto hh) __attribute__((always_inline)) {
+      constexpr int h = decltype(hh)::value;
+      constexpr int nb = C / (2 * h);
+      if (on) {
+        if (nb == 1) {
+          if (part == 0) factors_R(0, h); else factors_L(0, h);
+        } else {
+          for (int b = part; b < nb; b += 2) {
+            factors_R(b * 2 * h, h);
+            factors_L(b * 2 * h, h);
+          }
+        }
+      }
+      __syncthreads();
+      if (on) {
+        if (nb == 1) {
+          if (part == 0) rows_R(0, hh); else rows_L(0, hh);
+        } else {
+          for (int b = part; b < nb; b += 2) {
+            rows_R(b * 2 * h, hh);
+            rows_L(b * 2 * h, hh);
+          }
+        }
+      }
+      __syncthreads();
+    };
+    static_assert(C == 32, "halving levels below assume 32-position chunks");
+    level(std::integral_constant<int, 16>{});
+    level(std::integral_constant<int, 8>{});
+    level(std::integral_constant<int, 4>{});
+    level(std::integral_constant<int, 2>{});
+    level(std::integral_constant<int, 1>{});
+    if (tid < DK)
+      for (int t = 0; t < cv; ++t) {
+        const size_t o = (size_t)(row0 + t) * DK + ch;
+        dq[o] = gq[t * DKP];
+        dk[o] = gk[t * DKP];
+        dal[o] = ga[t * DKP];
+      }
   }
   if (tid < cv) dbe[row0 + tid] = sdb[tid];
 }
