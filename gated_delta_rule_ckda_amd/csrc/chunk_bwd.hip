@@ -94,9 +94,13 @@ __device__ __forceinline__ void gemm_lds(float* d, int di, const float* a, int a
   }
 }
 
+// p[i] if ok, else `other`; the load is always issued (at p[0] when not ok,
+// which every caller keeps valid) so that it needs no branch: a branch per
+// element would put each load in a block of its own, waited on by itself.
 template <typename T>
 __device__ __forceinline__ float ld_or(const T* p, size_t i, bool ok, float other) {
-  return ok ? to_f32(p[i]) : other;
+  const float x = to_f32(p[ok ? i : 0]);
+  return ok ? x : other;
 }
 
 // ============================================================ prep
@@ -117,13 +121,28 @@ __global__ __launch_bounds__(kBThreads) void chunk_bwd_prep_kernel(const T* q, c
   const int t0 = c * C, cv = min(C, T_len - t0);
   const long long row0 = bh * (long long)T_len + t0;
   // rows past a ragged end are identity steps: gate 1, no key, query or beta
-  for (int e = tid; e < C * DK; e += kBThreads) {
-    const int t = e / DK, ch = e % DK;
-    const bool ok = t < cv;
-    const size_t gi = ok ? (size_t)(row0 + t) * DK + ch : 0;
-    sq[t * DKP + ch] = ld_or(q, gi, ok, 0.f);
-    sk[t * DKP + ch] = ld_or(k, gi, ok, 0.f);
-    sa[t * DKP + ch] = ld_or(alpha, gi, ok, 1.f);
+  {   // all loads issued before any is stored
+    constexpr int NK = (C * DK + kBThreads - 1) / kBThreads;
+    float r0[NK], r1[NK], r2[NK];
+#pragma unroll
+    for (int i = 0; i < NK; ++i) {
+      const int e = tid + i * kBThreads, t = e / DK, ch = e % DK;
+      const bool ok = e < C * DK && t < cv;
+      const size_t gi = ok ? (size_t)(row0 + t) * DK + ch : 0;
+      r0[i] = ld_or(q, gi, ok, 0.f);
+      r1[i] = ld_or(k, gi, ok, 0.f);
+      r2[i] = ld_or(alpha, gi, ok, 1.f);
+    }
+#pragma unroll
+    for (int i = 0; i < NK; ++i) {
+      const int e = tid + i * kBThreads;
+      if (e < C * DK) {
+        const int o = (e / DK) * DKP + e % DK;
+        sq[o] = r0[i];
+        sk[o] = r1[i];
+        sa[o] = r2[i];
+      }
+    }
   }
   if (tid < C) sb[tid] = tid < cv ? to_f32(beta[row0 + tid]) : 0.f;
   for (int e = tid; e < C * CP; e += kBThreads) {
@@ -238,15 +257,14 @@ __global__ __launch_bounds__(kBThreads) void chunk_bwd_states_kernel(const T* v,
 #pragma unroll
     for (int i = 0; i < NK; ++i) {
       const int e = tid + i * kBThreads;
-      if (e < C * DK) {
-        rKG[i] = rc[R::KG_OFF + e];
-        rKR[i] = rc[R::KR_OFF + e];
-      }
+      const int ee = e < C * DK ? e : 0;   // (always in range for these shapes; clamped, not branched)
+      rKG[i] = rc[R::KG_OFF + ee];
+      rKR[i] = rc[R::KR_OFF + ee];
     }
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
       const int e = tid + i * kBThreads;
-      if (e < C * C) rTB[i] = rc[R::TB_OFF + e];
+      rTB[i] = rc[R::TB_OFF + (e < C * C ? e : 0)];
     }
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
@@ -322,19 +340,16 @@ __global__ __launch_bounds__(kBThreads) void chunk_bwd_dstates_kernel(const T* d
 #pragma unroll
     for (int i = 0; i < NK; ++i) {
       const int e = tid + i * kBThreads;
-      if (e < C * DK) {
-        rKG[i] = rc[R::KG_OFF + e];
-        rKR[i] = rc[R::KR_OFF + e];
-        rQG[i] = rc[R::QG_OFF + e];
-      }
+      const int ee = e < C * DK ? e : 0;
+      rKG[i] = rc[R::KG_OFF + ee];
+      rKR[i] = rc[R::KR_OFF + ee];
+      rQG[i] = rc[R::QG_OFF + ee];
     }
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
-      const int e = tid + i * kBThreads;
-      if (e < C * C) {
-        rM[i] = rc[R::M_OFF + e];
-        rTB[i] = rc[R::TB_OFF + e];
-      }
+      const int e = tid + i * kBThreads, ee = e < C * C ? e : 0;
+      rM[i] = rc[R::M_OFF + ee];
+      rTB[i] = rc[R::TB_OFF + ee];
     }
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
@@ -436,22 +451,52 @@ __global__ __launch_bounds__(kBThreads) void chunk_bwd_grad_kernel(
   const long long row0 = bh * (long long)T_len + t0;
   const float* rc = rec + (size_t)chunk * R::FLOATS;
 
-  for (int e = tid; e < C * DK; e += kBThreads) {
-    const int t = e / DK, ch = e % DK;
-    const bool ok = t < cv;
-    const size_t gi = ok ? (size_t)(row0 + t) * DK + ch : 0;
-    sq[t * DKP + ch] = ld_or(q, gi, ok, 0.f);
-    sk[t * DKP + ch] = ld_or(k, gi, ok, 0.f);
-    sa[t * DKP + ch] = ld_or(alpha, gi, ok, 1.f);
-    sKG[t * DKP + ch] = rc[R::KG_OFF + e];
-    sKR[t * DKP + ch] = rc[R::KR_OFF + e];
-  }
-  for (int e = tid; e < C * C; e += kBThreads) {
-    const int i = e / C, j = e % C;
-    sM[i * CP + j] = rc[R::M_OFF + e];
-    sTB[i * CP + j] = rc[R::TB_OFF + e];
-    sT[i * CP + j] = rc[R::T_OFF + e];
-    sS[i * CP + j] = rc[R::S_OFF + e];
+  {   // all of the chunk's operand loads issued before any is stored
+    constexpr int NK = (C * DK + kBThreads - 1) / kBThreads, NC = (C * C + kBThreads - 1) / kBThreads;
+    float r0[NK], r1[NK], r2[NK], r3[NK], r4[NK], m0[NC], m1[NC], m2[NC], m3[NC];
+#pragma unroll
+    for (int i = 0; i < NK; ++i) {
+      const int e = tid + i * kBThreads, t = e / DK, ch = e % DK;
+      const bool in = e < C * DK, ok = in && t < cv;
+      const size_t gi = ok ? (size_t)(row0 + t) * DK + ch : 0;
+      r0[i] = ld_or(q, gi, ok, 0.f);
+      r1[i] = ld_or(k, gi, ok, 0.f);
+      r2[i] = ld_or(alpha, gi, ok, 1.f);
+      r3[i] = rc[R::KG_OFF + (in ? e : 0)];
+      r4[i] = rc[R::KR_OFF + (in ? e : 0)];
+    }
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const int e = tid + i * kBThreads;
+      const bool in = e < C * C;
+      m0[i] = rc[R::M_OFF + (in ? e : 0)];
+      m1[i] = rc[R::TB_OFF + (in ? e : 0)];
+      m2[i] = rc[R::T_OFF + (in ? e : 0)];
+      m3[i] = rc[R::S_OFF + (in ? e : 0)];
+    }
+#pragma unroll
+    for (int i = 0; i < NK; ++i) {
+      const int e = tid + i * kBThreads;
+      if (e < C * DK) {
+        const int o = (e / DK) * DKP + e % DK;
+        sq[o] = r0[i];
+        sk[o] = r1[i];
+        sa[o] = r2[i];
+        sKG[o] = r3[i];
+        sKR[o] = r4[i];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const int e = tid + i * kBThreads;
+      if (e < C * C) {
+        const int o = (e / C) * CP + e % C;
+        sM[o] = m0[i];
+        sTB[o] = m1[i];
+        sT[o] = m2[i];
+        sS[o] = m3[i];
+      }
+    }
   }
   if (tid < C) sb[tid] = tid < cv ? to_f32(beta[row0 + tid]) : 0.f;
   if (tid < DK) sGC[tid] = 0.f;
@@ -474,11 +519,9 @@ __global__ __launch_bounds__(kBThreads) void chunk_bwd_grad_kernel(
   auto fetch = [&](int col0) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < NH; ++i) {
-      const int e = tid + i * kBThreads, ii = e / DS, j = e % DS;
-      if (e < DK * DS) {
-        rH[i] = hcc[(size_t)ii * dv + col0 + j];
-        rdH[i] = dhc[(size_t)ii * dv + col0 + j];
-      }
+      const int e = tid + i * kBThreads, ee = e < DK * DS ? e : 0, ii = ee / DS, j = ee % DS;
+      rH[i] = hcc[(size_t)ii * dv + col0 + j];
+      rdH[i] = dhc[(size_t)ii * dv + col0 + j];
     }
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
