@@ -44,6 +44,8 @@ def parse():
     p.add_argument("--workload", default="ckda_bf16",
                    help="forward workload name (default: the headline ckda_bf16)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--skip-extras", action="store_true",
+                   help="headline forward and decode only (for counter runs)")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="about this much oracle work for the CPU baseline (whole-workload passes)")
     return p.parse_args()
@@ -203,108 +205,147 @@ def main():
     dec_gbs_state = state_bytes / (dec_ms * 1e-3) / 1e9
     dec_gbs_total = (state_bytes + io_bytes) / (dec_ms * 1e-3) / 1e9
 
-    # ---- the same forward and decode step with the per-token prologue fused
-    # (gates and beta from logits, unit-norm keys): ckda_chunk_fwd_ex and
-    # ckda_decode_step_ex, per-call HIP events on the same stream
-    fuse = ck.FUSE_GATES | ck.FUSE_NORM_K
-    log(f"[bench] fused prologue, flags {fuse}")
-    lg = {k: (None if v is None else v.to(dev)) for k, v in gen.make_logit_inputs(w).items()}
+    def extras():
+        """The variants beside the headline: fused prologue, channel gather,
+        backward, comparators (each timed with HIP events on the stream)."""
+        # ---- the same forward and decode step with the per-token prologue fused
+        # (gates and beta from logits, unit-norm keys): ckda_chunk_fwd_ex and
+        # ckda_decode_step_ex, per-call HIP events on the same stream
+        fuse = ck.FUSE_GATES | ck.FUSE_NORM_K
+        log(f"[bench] fused prologue, flags {fuse}")
+        lg = {k: (None if v is None else v.to(dev)) for k, v in gen.make_logit_inputs(w).items()}
 
-    def fstep():
-        ck.chunk_fwd(lg["q"], lg["k"], lg["v"], lg["alpha"], lg["beta"], lg["h0"], chunk=w.chunk,
-                     workspace=ws, o=o, hT=hT, fuse=fuse)
+        def fstep():
+            ck.chunk_fwd(lg["q"], lg["k"], lg["v"], lg["alpha"], lg["beta"], lg["h0"], chunk=w.chunk,
+                         workspace=ws, o=o, hT=hT, fuse=fuse)
 
-    for _ in range(a.warmup):
-        fstep()
-    torch.cuda.synchronize()
-    fev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(a.steps)]
-    for s in range(a.steps):
-        fev[s][0].record(stream)
-        fstep()
-        fev[s][1].record(stream)
-    torch.cuda.synchronize()
-    fused_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in fev]))
-    dlg = [{k: v.to(dev) for k, v in gen.decode_logit_inputs(s, dec).items()} for s in range(8)]
-    for s in range(a.warmup):
-        x = dlg[s % 8]
-        ck.decode_step(x["q"], x["k"], x["v"], x["alpha"], x["beta"], S, o=do, fuse=fuse)
-    torch.cuda.synchronize()
-    for s in range(a.decode_steps):
-        x = dlg[s % 8]
-        dev_ev[s][0].record(stream)
-        ck.decode_step(x["q"], x["k"], x["v"], x["alpha"], x["beta"], S, o=do, fuse=fuse)
-        dev_ev[s][1].record(stream)
-    torch.cuda.synchronize()
-    fdec_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in dev_ev]))
-
-    # ---- state-reduced workload (B2 H32 T32768, d_k 64 kept of 128 channels,
-    # d_v 128) with the channel gather inside the kernels, beside the plain
-    # forward on inputs gathered beforehand
-    gw, dk_in = gen.WORKLOADS["ckda_long_dk64"], 128
-    log(f"[bench] channel gather {gw} from {dk_in} channels")
-    gidx = gen.retained_channels(gw.H, dk_in, gw.dk, 4242)
-    gin = gen.make_gather_inputs(gw, dk_in, gidx)
-    gd = {k: (None if v is None else v.to(dev)) for k, v in gin.items()}
-    gidx_d = gidx.to(dev)
-    pre = {n: torch.stack([gd[n][:, h].index_select(-1, gidx_d[h].long()) for h in range(gw.H)], 1).contiguous()
-           for n in ("q", "k", "alpha")}
-    gws = torch.empty(ck.workspace_size(gw.B, gw.H, gw.T, gw.dk, gw.dv, gw.chunk, ck.DTYPE_BF16), dtype=torch.uint8,
-                      device=dev)
-    go = torch.empty((gw.B, gw.H, gw.T, gw.dv), dtype=torch.bfloat16, device=dev)
-    ghT = torch.empty((gw.B, gw.H, gw.dk, gw.dv), dtype=torch.float32, device=dev)
-
-    def timed(fn, n):
-        for _ in range(max(1, a.warmup)):
-            fn()
+        for _ in range(a.warmup):
+            fstep()
         torch.cuda.synchronize()
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
-        for e0, e1 in evs:
-            e0.record(stream)
-            fn()
-            e1.record(stream)
+        fev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(a.steps)]
+        for s in range(a.steps):
+            fev[s][0].record(stream)
+            fstep()
+            fev[s][1].record(stream)
         torch.cuda.synchronize()
-        return float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+        fused_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in fev]))
+        dlg = [{k: v.to(dev) for k, v in gen.decode_logit_inputs(s, dec).items()} for s in range(8)]
+        for s in range(a.warmup):
+            x = dlg[s % 8]
+            ck.decode_step(x["q"], x["k"], x["v"], x["alpha"], x["beta"], S, o=do, fuse=fuse)
+        torch.cuda.synchronize()
+        for s in range(a.decode_steps):
+            x = dlg[s % 8]
+            dev_ev[s][0].record(stream)
+            ck.decode_step(x["q"], x["k"], x["v"], x["alpha"], x["beta"], S, o=do, fuse=fuse)
+            dev_ev[s][1].record(stream)
+        torch.cuda.synchronize()
+        fdec_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in dev_ev]))
 
-    gsteps = max(3, a.steps // 3)
-    gather_ms = timed(lambda: ck.chunk_fwd(gd["q"], gd["k"], gd["v"], gd["alpha"], gd["beta"], gd["h0"],
-                                           chunk=gw.chunk, workspace=gws, o=go, hT=ghT, idx=gidx_d), gsteps)
-    pregathered_ms = timed(lambda: ck.chunk_fwd(pre["q"], pre["k"], gd["v"], pre["alpha"], gd["beta"], gd["h0"],
-                                                chunk=gw.chunk, workspace=gws, o=go, hT=ghT), gsteps)
-    del pre, gd, gws, go
+        # ---- state-reduced workload (B2 H32 T32768, d_k 64 kept of 128 channels,
+        # d_v 128) with the channel gather inside the kernels, beside the plain
+        # forward on inputs gathered beforehand
+        gw, dk_in = gen.WORKLOADS["ckda_long_dk64"], 128
+        log(f"[bench] channel gather {gw} from {dk_in} channels")
+        gidx = gen.retained_channels(gw.H, dk_in, gw.dk, 4242)
+        gin = gen.make_gather_inputs(gw, dk_in, gidx)
+        gd = {k: (None if v is None else v.to(dev)) for k, v in gin.items()}
+        gidx_d = gidx.to(dev)
+        pre = {n: torch.stack([gd[n][:, h].index_select(-1, gidx_d[h].long()) for h in range(gw.H)], 1).contiguous()
+               for n in ("q", "k", "alpha")}
+        gws = torch.empty(ck.workspace_size(gw.B, gw.H, gw.T, gw.dk, gw.dv, gw.chunk, ck.DTYPE_BF16), dtype=torch.uint8,
+                          device=dev)
+        go = torch.empty((gw.B, gw.H, gw.T, gw.dv), dtype=torch.bfloat16, device=dev)
+        ghT = torch.empty((gw.B, gw.H, gw.dk, gw.dv), dtype=torch.float32, device=dev)
 
-    # ---- backward on the bench workload (ckda_chunk_bwd, fp32 gradients)
-    log("[bench] backward")
-    bdo, bdhT = gen.make_output_grads(w, 99)
-    bdo, bdhT = bdo.to(dev), bdhT.to(dev)
-    bws = torch.empty(ck.bwd_workspace_size(w.B, w.H, w.T, w.dk, w.dv, ck.DTYPE_BF16), dtype=torch.uint8, device=dev)
-    bwd_ms = timed(lambda: ck.chunk_bwd(d["q"], d["k"], d["v"], d["alpha"], d["beta"], bdo, h0=d["h0"], dhT=bdhT,
-                                        workspace=bws), max(3, a.steps // 3))
-    del bws
+        def timed(fn, n):
+            for _ in range(max(1, a.warmup)):
+                fn()
+            torch.cuda.synchronize()
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+            for e0, e1 in evs:
+                e0.record(stream)
+                fn()
+                e1.record(stream)
+            torch.cuda.synchronize()
+            return float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
 
-    # ---- comparators on the bench shape: the scalar (Gated DeltaNet) gate and
-    # ungated DeltaProduct_2 (two delta-rule updates per token), and the
-    # DeltaProduct_2 decode step on the decode workload
-    log("[bench] comparators")
-    sg = {k: (None if v is None else v.to(dev)) for k, v in gen.make_scalar_gate_inputs(w).items()}
-    scalar_ms = timed(lambda: ck.chunk_fwd(sg["q"], sg["k"], sg["v"], sg["alpha"], sg["beta"], sg["h0"],
-                                           chunk=w.chunk, workspace=ws, o=o, hT=hT, fuse=ck.GATE_SCALAR), a.steps)
-    del sg
-    dp = {k: (None if v is None else v.to(dev)) for k, v in gen.make_dp2_inputs(w, gated=False).items()}
-    dws = torch.empty(ck.workspace_size(w.B, w.H, 2 * w.T, w.dk, w.dv, w.chunk, ck.DTYPE_BF16), dtype=torch.uint8,
-                      device=dev)
-    dp2_ms = timed(lambda: ck.deltaproduct2_fwd(dp["q"], dp["k"], dp["v"], dp["beta"], h0=dp["h0"], chunk=w.chunk,
-                                                workspace=dws, o=o, hT=hT), a.steps)
-    del dp, dws
-    dd = [{k: v.to(dev) for k, v in gen.dp2_decode_inputs(s, dec, gated=False).items() if v is not None}
-          for s in range(4)]
-    cnt = [0]
+        gsteps = max(3, a.steps // 3)
+        gather_ms = timed(lambda: ck.chunk_fwd(gd["q"], gd["k"], gd["v"], gd["alpha"], gd["beta"], gd["h0"],
+                                               chunk=gw.chunk, workspace=gws, o=go, hT=ghT, idx=gidx_d), gsteps)
+        pregathered_ms = timed(lambda: ck.chunk_fwd(pre["q"], pre["k"], gd["v"], pre["alpha"], gd["beta"], gd["h0"],
+                                                    chunk=gw.chunk, workspace=gws, o=go, hT=ghT), gsteps)
+        del pre, gd, gws, go
 
-    def dp2_dec():
-        x = dd[cnt[0] % 4]
-        cnt[0] += 1
-        ck.deltaproduct2_decode_step(x["q"], x["k"], x["v"], x["beta"], S, o=do)
+        # ---- backward on the bench workload (ckda_chunk_bwd, fp32 gradients)
+        log("[bench] backward")
+        bdo, bdhT = gen.make_output_grads(w, 99)
+        bdo, bdhT = bdo.to(dev), bdhT.to(dev)
+        bws = torch.empty(ck.bwd_workspace_size(w.B, w.H, w.T, w.dk, w.dv, ck.DTYPE_BF16), dtype=torch.uint8, device=dev)
+        bwd_ms = timed(lambda: ck.chunk_bwd(d["q"], d["k"], d["v"], d["alpha"], d["beta"], bdo, h0=d["h0"], dhT=bdhT,
+                                            workspace=bws), max(3, a.steps // 3))
+        del bws
 
-    dp2_dec_ms = timed(dp2_dec, a.decode_steps)
+        # ---- comparators on the bench shape: the scalar (Gated DeltaNet) gate and
+        # ungated DeltaProduct_2 (two delta-rule updates per token), and the
+        # DeltaProduct_2 decode step on the decode workload
+        log("[bench] comparators")
+        sg = {k: (None if v is None else v.to(dev)) for k, v in gen.make_scalar_gate_inputs(w).items()}
+        scalar_ms = timed(lambda: ck.chunk_fwd(sg["q"], sg["k"], sg["v"], sg["alpha"], sg["beta"], sg["h0"],
+                                               chunk=w.chunk, workspace=ws, o=o, hT=hT, fuse=ck.GATE_SCALAR), a.steps)
+        del sg
+        dp = {k: (None if v is None else v.to(dev)) for k, v in gen.make_dp2_inputs(w, gated=False).items()}
+        dws = torch.empty(ck.workspace_size(w.B, w.H, 2 * w.T, w.dk, w.dv, w.chunk, ck.DTYPE_BF16), dtype=torch.uint8,
+                          device=dev)
+        dp2_ms = timed(lambda: ck.deltaproduct2_fwd(dp["q"], dp["k"], dp["v"], dp["beta"], h0=dp["h0"], chunk=w.chunk,
+                                                    workspace=dws, o=o, hT=hT), a.steps)
+        del dp, dws
+        dd = [{k: v.to(dev) for k, v in gen.dp2_decode_inputs(s, dec, gated=False).items() if v is not None}
+              for s in range(4)]
+        cnt = [0]
+
+        def dp2_dec():
+            x = dd[cnt[0] % 4]
+            cnt[0] += 1
+            ck.deltaproduct2_decode_step(x["q"], x["k"], x["v"], x["beta"], S, o=do)
+
+        dp2_dec_ms = timed(dp2_dec, a.decode_steps)
+        return {
+            "backward": {
+                "workload": w.name,
+                "call_ms_mean": round(bwd_ms, 4),
+                "tokens_per_s": round(tokens / (bwd_ms * 1e-3), 1),
+                "forward_plus_backward_tokens_per_s": round(tokens / ((bwd_ms + call_ms) * 1e-3), 1),
+                "gradients": "fp32 dq, dk, dv, dalpha, dbeta, dh0",
+            },
+            "comparators": {
+                "scalar_gate_forward_call_ms_mean": round(scalar_ms, 4),
+                "scalar_gate_tokens_per_s": round(tokens / (scalar_ms * 1e-3), 1),
+                "deltaproduct2_forward_call_ms_mean": round(dp2_ms, 4),
+                "deltaproduct2_tokens_per_s": round(tokens / (dp2_ms * 1e-3), 1),
+                "deltaproduct2_decode_ms_per_step": round(dp2_dec_ms, 4),
+                "deltaproduct2_decode_total_GB_s": round(
+                    (state_bytes + dec.N * dec.H * (3 * dec.dk + 3 * dec.dv + 2) * 2) / (dp2_dec_ms * 1e-3) / 1e9, 1),
+            },
+            "channel_gather": {
+                "workload": f"{gw.name} (d_k {gw.dk} kept of {dk_in})",
+                "forward_call_ms_mean": round(gather_ms, 4),
+                "forward_tokens_per_s": round(gw.B * gw.T / (gather_ms * 1e-3), 1),
+                "pregathered_plain_call_ms_mean": round(pregathered_ms, 4),
+                "gather_overhead_vs_pregathered": round(gather_ms / pregathered_ms - 1.0, 4),
+            },
+            "fused_prologue": {
+                "flags": "CKDA_FUSE_GATES | CKDA_FUSE_NORM_K",
+                "inputs": "gate and beta logits, unnormalised keys (same shapes)",
+                "forward_call_ms_mean": round(fused_ms, 4),
+                "forward_tokens_per_s": round(tokens / (fused_ms * 1e-3), 1),
+                "forward_overhead_vs_plain": round(fused_ms / call_ms - 1.0, 4),
+                "decode_ms_per_step_events": round(fdec_ms, 4),
+                "decode_total_GB_s": round((state_bytes + io_bytes) / (fdec_ms * 1e-3) / 1e9, 1),
+            },
+        }
+
+    sections = {} if a.skip_extras else extras()
 
     # ---- reference device copy of the decode state's size (practical ceiling)
     src = torch.empty(dec.N * dec.H * dec.dk * dec.dv, dtype=torch.float32, device=dev)
@@ -364,40 +405,9 @@ def main():
             "frac_of_hbm_peak": round(dec_gbs_total / HBM_PEAK_GBS, 4),
             "device_copy_GB_s": round(copy_gbs, 1),
         },
-        "backward": {
-            "workload": w.name,
-            "call_ms_mean": round(bwd_ms, 4),
-            "tokens_per_s": round(tokens / (bwd_ms * 1e-3), 1),
-            "forward_plus_backward_tokens_per_s": round(tokens / ((bwd_ms + call_ms) * 1e-3), 1),
-            "gradients": "fp32 dq, dk, dv, dalpha, dbeta, dh0",
-        },
-        "comparators": {
-            "scalar_gate_forward_call_ms_mean": round(scalar_ms, 4),
-            "scalar_gate_tokens_per_s": round(tokens / (scalar_ms * 1e-3), 1),
-            "deltaproduct2_forward_call_ms_mean": round(dp2_ms, 4),
-            "deltaproduct2_tokens_per_s": round(tokens / (dp2_ms * 1e-3), 1),
-            "deltaproduct2_decode_ms_per_step": round(dp2_dec_ms, 4),
-            "deltaproduct2_decode_total_GB_s": round(
-                (state_bytes + dec.N * dec.H * (3 * dec.dk + 3 * dec.dv + 2) * 2) / (dp2_dec_ms * 1e-3) / 1e9, 1),
-        },
-        "channel_gather": {
-            "workload": f"{gw.name} (d_k {gw.dk} kept of {dk_in})",
-            "forward_call_ms_mean": round(gather_ms, 4),
-            "forward_tokens_per_s": round(gw.B * gw.T / (gather_ms * 1e-3), 1),
-            "pregathered_plain_call_ms_mean": round(pregathered_ms, 4),
-            "gather_overhead_vs_pregathered": round(gather_ms / pregathered_ms - 1.0, 4),
-        },
-        "fused_prologue": {
-            "flags": "CKDA_FUSE_GATES | CKDA_FUSE_NORM_K",
-            "inputs": "gate and beta logits, unnormalised keys (same shapes)",
-            "forward_call_ms_mean": round(fused_ms, 4),
-            "forward_tokens_per_s": round(tokens / (fused_ms * 1e-3), 1),
-            "forward_overhead_vs_plain": round(fused_ms / call_ms - 1.0, 4),
-            "decode_ms_per_step_events": round(fdec_ms, 4),
-            "decode_total_GB_s": round((state_bytes + io_bytes) / (fdec_ms * 1e-3) / 1e9, 1),
-        },
     }
 
+    out.update(sections)
     if not a.no_cpu_baseline:
         import oracle
         from gated_delta_rule_ckda_amd.inputs import raw
