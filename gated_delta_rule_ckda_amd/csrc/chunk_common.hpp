@@ -39,7 +39,17 @@ struct ChunkGeom {
   static constexpr int KBN = (DK + KB - 1) / KB;    // K blocks over channels
   static constexpr int KBC = (C + KB - 1) / KB;     // K blocks over positions
   static constexpr size_t FRAG = 1024;
-  static constexpr int NF_T = RT * KBC;             // fragments of TB (and of M)
+  // TB and M are lower triangular (j <= t): of their (row tile, K block)
+  // fragments only those reaching the diagonal are stored, row tile by row
+  // tile; blocks entirely above it hold zeros and are neither stored nor read
+  static constexpr bool tri_live(int pt, int kb) { return kb * KB < 16 * (pt + 1); }
+  static constexpr int tri_index(int pt, int kb) {
+    int n = 0;
+    for (int p = 0; p < pt; ++p)
+      for (int b = 0; b < KBC; ++b) n += tri_live(p, b) ? 1 : 0;
+    return n + kb;
+  }
+  static constexpr int NF_T = tri_index(RT, 0);     // stored fragments of TB (and of M)
   static constexpr int NF_W = RT * KBN;             // fragments of W (and of Q)
   static constexpr int NF_KR = RH * KBC;            // fragments of KR
   static constexpr int NF_D = (DK * 4 + 1023) / 1024;

@@ -702,6 +702,7 @@ __global__ __launch_bounds__((GramCfg<T, DK, C>::NTH)) void chunk_gram_kernel(
     const bool isT = f < NF;
     const int ff = isT ? f : f - NF;
     const int rt = ff / KBC, kb = ff % KBC;
+    if (!P::tri_live(rt, kb)) continue;   // all zero, not stored
     const float* src = (isT ? Ts : Ms) + (16 * rt + r) * LD;
     float vals[8];
     // K order: elements 0-3 are 4 consecutive columns, so are 4-7 (bf16)
@@ -723,7 +724,7 @@ __global__ __launch_bounds__((GramCfg<T, DK, C>::NTH)) void chunk_gram_kernel(
     } else {
       out.w = __builtin_bit_cast(u32x4, f32x4{vals[0], vals[1], vals[2], vals[3]});
     }
-    store_frag_stream(rec + (isT ? P::T_OFF : P::M_OFF) + frag_slot(rt, kb, KBC, lane), out);
+    store_frag_stream(rec + (isT ? P::T_OFF : P::M_OFF) + ((size_t)P::tri_index(rt, kb) * 64 + lane) * 16, out);
   }
 }
 

@@ -40,14 +40,13 @@ struct StateCfg : ChunkGeom<T, DK, C> {
   using G = ChunkGeom<T, DK, C>;
   static constexpr int NCW = 4;                              // copy waves
   static constexpr int NTHREADS = (NMW + NCW) * 64;
-  // one operand set: the chunk's record as stored, then the slice's value
-  // rows (VRB bytes each) at a padded stride VS: the four rows 4 g + i that
-  // lane groups g = 0..3 of a matrix wave read together fall in four
-  // different 16-bank groups
+  // one operand set: the chunk's record as stored, then the slice's values in
+  // accumulator order: for matrix wave w and row tile pt, lane (g, r) finds
+  // rows 16 pt + 4 g .. + 3 of its column 16 w + r as four consecutive
+  // elements at ((w RT + pt) 64 + lane) 4 E, one 8- or 16-byte read
   static constexpr int V_OFF = (int)G::BYTES;
-  static constexpr int VRB = NMW * 16 * (int)sizeof(T);
-  static constexpr int VS = VRB + 16;
-  static constexpr int V_BYTES = C * VS;
+  static constexpr int VRB = NMW * 16 * (int)sizeof(T);   // bytes of one value row of the slice
+  static constexpr int V_BYTES = C * VRB;
   static constexpr int SET_BYTES = V_OFF + V_BYTES;
   static constexpr int NSET = 2 * SET_BYTES <= 160 * 1024 ? 2 : 1;
   static constexpr int LDS_BYTES = NSET * SET_BYTES;
@@ -137,11 +136,15 @@ __global__ __launch_bounds__((StateCfg<T, DK, C, NMW>::NTHREADS)) void chunk_sta
           qf[pt % DB][kb] = frag(S::Q_OFF, pt * KBN + kb);
         }
       };
+      // K blocks of TB and M entirely above the diagonal are zero: the record
+      // does not hold them and they are not multiplied
+      auto upper = [](int pt, int kb) constexpr { return !S::tri_live(pt, kb); };
       auto ld_tm = [&](Frag (*dst)[KBC], size_t off) __attribute__((always_inline)) {
 #pragma unroll
         for (int pt = 0; pt < RT; ++pt)
 #pragma unroll
-          for (int kb = 0; kb < KBC; ++kb) dst[pt][kb] = frag(off, pt * KBC + kb);
+          for (int kb = 0; kb < KBC; ++kb)
+            if (!upper(pt, kb)) dst[pt][kb] = frag(off, S::tri_index(pt, kb));
       };
       constexpr int RHG = RH < 2 ? RH : 2;   // state row tiles per group of reads
       constexpr int NG = RH / RHG;
@@ -157,11 +160,21 @@ __global__ __launch_bounds__((StateCfg<T, DK, C, NMW>::NTHREADS)) void chunk_sta
         }
       };
 
+      // this lane's value rows (X starts from V), read first with bf16 operands:
+      // reads complete in order, so the products then wait only for what they
+      // need (fp32 reads them per row tile, to stay within the register file)
+      f32x4 xacc[RT], oacc[RT];
+      auto ld_v = [&](int pt) __attribute__((always_inline)) {
+        xacc[pt] = load_vals4<T>(set + S::V_OFF + ((wave * RT + pt) * 64 + lane) * 4 * E);
+      };
+      if constexpr (DB == 2) {
+#pragma unroll
+        for (int pt = 0; pt < RT; ++pt) ld_v(pt);
+      }
       Frag hb[KBN];
 #pragma unroll
       for (int kb = 0; kb < KBN; ++kb) hb[kb] = bfrag(hacc, kb, RH);
       // X = V + W H, O = Q~ H
-      f32x4 xacc[RT], oacc[RT];
       if constexpr (DB == 2) ld_wq(0);
 #pragma unroll
       for (int pt = 0; pt < RT; ++pt) {
@@ -170,14 +183,9 @@ __global__ __launch_bounds__((StateCfg<T, DK, C, NMW>::NTHREADS)) void chunk_sta
           else ld_tm(tf, S::T_OFF);
         } else {
           ld_wq(pt);
+          ld_v(pt);
         }
         __builtin_amdgcn_sched_barrier(0);
-        {
-          // rows 16 pt + 4 g + i of this lane's column
-          const unsigned char* vp = set + S::V_OFF + (16 * pt + 4 * g) * S::VS + (16 * wave + r) * E;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) xacc[pt][i] = load_elem_lds<T>(vp + i * S::VS);
-        }
         oacc[pt] = zero4();
 #pragma unroll
         for (int kb = 0; kb < KBN; ++kb) {
@@ -198,7 +206,8 @@ __global__ __launch_bounds__((StateCfg<T, DK, C, NMW>::NTHREADS)) void chunk_sta
       for (int pt = 0; pt < RT; ++pt) {
         uacc[pt] = zero4();
 #pragma unroll
-        for (int kb = 0; kb < KBC; ++kb) uacc[pt] = mma<T>(uacc[pt], tf[pt][kb], xb[kb]);
+        for (int kb = 0; kb < KBC; ++kb)
+          if (!upper(pt, kb)) uacc[pt] = mma<T>(uacc[pt], tf[pt][kb], xb[kb]);
       }
       if constexpr (DB == 1) ld_tm(mf, S::M_OFF);
       ld_kr(0);
@@ -206,18 +215,23 @@ __global__ __launch_bounds__((StateCfg<T, DK, C, NMW>::NTHREADS)) void chunk_sta
       Frag ub[KBC];
 #pragma unroll
       for (int kb = 0; kb < KBC; ++kb) ub[kb] = bfrag(uacc, kb, RT);
+      // lane (g, r) holds O^T rows 4 g .. 4 g + 3 of column r: four consecutive
+      // value columns of output row 16 pt + r.  With bf16 operands the outputs
+      // are stored last, when their products have long completed (fp32 stores
+      // them at once, to stay within the register file).
+      auto store_o = [&](int pt) __attribute__((always_inline)) {
+        const int orow = c * C + 16 * pt + r;
+        const int prow = prod2 ? orow >> 1 : orow;
+        const bool keep = !prod2 || (orow & 1);
+        store4<T>(orsrc, keep ? (prow * dv + ocol) * E : 0x7FFFFFF0, oacc[pt]);
+      };
       // O += M U
-      const int t0 = c * C;
 #pragma unroll
       for (int pt = 0; pt < RT; ++pt) {
 #pragma unroll
-        for (int kb = 0; kb < KBC; ++kb) oacc[pt] = mma<T>(oacc[pt], ub[kb], mf[pt][kb]);   // + U^T M^T
-        // lane (g, r) holds O^T rows 4 g .. 4 g + 3 of column r: four consecutive
-        // value columns of output row 16 pt + r
-        const int orow = t0 + 16 * pt + r;
-        const int ooff = prod2 ? ((orow & 1) ? ((orow >> 1) * dv + ocol) * E : 0x7FFFFFF0)
-                               : (orow * dv + ocol) * E;
-        store4<T>(orsrc, ooff, oacc[pt]);
+        for (int kb = 0; kb < KBC; ++kb)
+          if (!upper(pt, kb)) oacc[pt] = mma<T>(oacc[pt], ub[kb], mf[pt][kb]);   // + U^T M^T
+        if constexpr (DB == 1) store_o(pt);
       }
       // H <- d . H + KR^T U
 #pragma unroll
@@ -233,6 +247,10 @@ __global__ __launch_bounds__((StateCfg<T, DK, C, NMW>::NTHREADS)) void chunk_sta
           hacc[rh] = hh;
         }
         __builtin_amdgcn_sched_barrier(0);
+      }
+      if constexpr (DB == 2) {
+#pragma unroll
+        for (int pt = 0; pt < RT; ++pt) store_o(pt);
       }
       lds_barrier();
       if constexpr (NSET == 1) {
@@ -255,8 +273,10 @@ __global__ __launch_bounds__((StateCfg<T, DK, C, NMW>::NTHREADS)) void chunk_sta
         make_rsrc(rec + (size_t)bh * nchunks * S::BYTES, (uint32_t)((size_t)nchunks * S::BYTES));
     const __amdgpu_buffer_rsrc_t vrsrc = make_rsrc(v + rowbase * dv, (uint32_t)((size_t)T_len * dv * E));
     // value pieces: piece it = row it / (VRB / 16), 16 bytes at (it % (VRB / 16)) 16
-    // of the slice's columns (rows past the end read as zero)
-    constexpr int PPR = S::VRB / 16;
+    // of the slice's columns (rows past the end read as zero); its element e
+    // (column 16 w + cr of the slice) goes to the accumulator-order slot of
+    // lane (g, cr) = ((row % 16) / 4, cr) at position row % 4
+    constexpr int PPR = S::VRB / 16, EPP = 16 / E;
     int v_goff[NVI], v_loff[NVI];
     bool v_act[NVI];
 #pragma unroll
@@ -264,9 +284,21 @@ __global__ __launch_bounds__((StateCfg<T, DK, C, NMW>::NTHREADS)) void chunk_sta
       const int it = ct + NCT * j;
       v_act[j] = it < S::NVP;
       const int row = min(it, S::NVP - 1) / PPR, piece = it % PPR;
+      const int col0 = piece * EPP, w = col0 / 16;
       v_goff[j] = (row * dv + slice * 16 * NMW) * E + piece * 16;
-      v_loff[j] = S::V_OFF + row * S::VS + piece * 16;
+      v_loff[j] = S::V_OFF + ((w * S::RT + row / 16) * 64 + ((row % 16) / 4) * 16 + col0 % 16) * 4 * E + (row % 4) * E;
     }
+    auto put_vals = [&](unsigned char* set, int j, const Frag& x) __attribute__((always_inline)) {
+      unsigned char* p = set + v_loff[j];
+#pragma unroll
+      for (int e = 0; e < EPP; ++e) {
+        if constexpr (E == 2) {
+          *reinterpret_cast<uint16_t*>(p + e * 4 * E) = (uint16_t)(x.w[e / 2] >> (16 * (e % 2)));
+        } else {
+          *reinterpret_cast<uint32_t*>(p + e * 4 * E) = x.w[e];
+        }
+      }
+    };
     struct Regs {
       Frag f[NFL];
       Frag v[NVI];
@@ -292,12 +324,14 @@ __global__ __launch_bounds__((StateCfg<T, DK, C, NMW>::NTHREADS)) void chunk_sta
 #pragma unroll
       for (int j = 0; j < NFL; ++j) {
         const int f = fr[j];
-        if (store && f >= 0) store_frag(set + (f * 64 + lane) * 16, d.f[j]);
+        // every copy wave has a real fragment in the first NFR / NCW registers
+        // (stated for bf16 only: the fp32 copy loop then runs out of registers)
+        if (store && ((BF && j < S::NFR / S::NCW) || f >= 0)) store_frag(set + (f * 64 + lane) * 16, d.f[j]);
         d.f[j].w = __builtin_amdgcn_raw_buffer_load_b128(rrsrc, cc * (int)S::BYTES + (max(f, 0) * 64 + lane) * 16, 0, 0);
       }
 #pragma unroll
       for (int j = 0; j < NVI; ++j) {
-        if (store && v_act[j]) store_frag(set + v_loff[j], d.v[j]);
+        if (store && (S::NVP % NCT == 0 || v_act[j])) put_vals(set, j, d.v[j]);
         d.v[j].w = __builtin_amdgcn_raw_buffer_load_b128(vrsrc, cc * C * dv * E + v_goff[j], 0, 0);
       }
     };

@@ -101,9 +101,10 @@ typedef enum {
 /* Bytes of device workspace ckda_chunk_fwd needs for these sizes, or 0 when
  * the sizes are invalid or unsupported (ckda_chunk_fwd then reports why).
  * The workspace holds, per chunk of every (batch, head), the operands the
- * state pass consumes (see ckda_chunk_fwd): 2*chunk*chunk + 3*chunk*d_k
- * elements of dtype and d_k floats, each part rounded up to whole 1 KB
- * blocks (bf16, chunk 64, d_k 128: 65 KB per chunk). */
+ * state pass consumes (see ckda_chunk_fwd): the blocks on or below the
+ * diagonal of two chunk x chunk lower-triangular matrices, 3*chunk*d_k
+ * elements of dtype and d_k floats, in whole 1 KB blocks (bf16, chunk 64,
+ * d_k 128: 61 KB per chunk). */
 size_t ckda_chunk_fwd_workspace_size(int B, int H, int T, int dk, int dv, int chunk, int dtype);
 
 /* Chunkwise-parallel forward over a whole sequence for every (batch, head).

@@ -42,13 +42,15 @@ def test_workspace_size():
     L = ck.lib()
     ws = L.ckda_chunk_fwd_workspace_size
     # bf16, chunk 64, d_k 128: the record is a sequence of 1 KB fragments --
-    # TB and M (4 row tiles x 2 K blocks each), W and Q~ (4 x 4 each), KR
-    # (8 x 2) and one block for the d_k fp32 chunk decays
+    # TB and M (4 row tiles x 2 K blocks, less the 2 blocks above the
+    # diagonal), W and Q~ (4 x 4 each), KR (8 x 2) and one block for the d_k
+    # fp32 chunk decays
     per_chunk = ws(1, 1, 64, 128, 128, 64, 1)
-    assert per_chunk == 1024 * (2 * 8 + 2 * 16 + 16 + 1)
-    assert ws(1, 1, 64, 64, 128, 64, 1) == 1024 * (2 * 8 + 2 * 8 + 8 + 1)
-    # fp32: K blocks of 16 elements
-    assert ws(1, 1, 64, 128, 128, 64, 0) == 1024 * (2 * 16 + 2 * 32 + 32 + 1)
+    assert per_chunk == 1024 * (2 * 6 + 2 * 16 + 16 + 1)
+    assert ws(1, 1, 64, 64, 128, 64, 1) == 1024 * (2 * 6 + 2 * 8 + 8 + 1)
+    assert ws(1, 1, 32, 128, 128, 32, 1) == 1024 * (2 * 2 + 2 * 8 + 8 + 1)
+    # fp32: K blocks of 16 elements (lower triangle of 4 x 4 blocks)
+    assert ws(1, 1, 64, 128, 128, 64, 0) == 1024 * (2 * 10 + 2 * 32 + 32 + 1)
     assert ws(4, 16, 4096, 128, 128, 64, 1) == 64 * 64 * per_chunk
     assert ws(1, 1, 65, 128, 128, 64, 1) == 2 * per_chunk       # ragged tail = one more chunk
     assert ws(1, 1, 64, 128, 128, 48, 1) == 0                  # unsupported chunk
