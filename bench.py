@@ -9,7 +9,8 @@ state updated in place) is timed in the same run and reported under "decode",
 both again with the per-token prologue fused (gates from logits, unit-norm
 keys) under "fused_prologue", the state-reduced workload (B2 H32 T32768,
 d_k 64 kept of 128 channels by an in-kernel gather) under "channel_gather",
-the comparators (scalar gate; DeltaProduct_2 forward and decode) under
+the KDA workload (B4 H16 T2048, positive gates) under "kda", the
+comparators (scalar gate; DeltaProduct_2 forward and decode) under
 "comparators", and the backward (all gradients) with the forward + backward
 throughput under "backward".
 
@@ -277,6 +278,19 @@ def main():
                                                     chunk=gw.chunk, workspace=gws, o=go, hT=ghT), gsteps)
         del pre, gd, gws, go
 
+        # ---- the KDA workload (B4 H16 T2048: positive gates, beta in (0, 1), h0 = 0)
+        kw = gen.WORKLOADS["kda_bf16"]
+        log(f"[bench] KDA workload {kw}")
+        kin = {k: (None if v is None else v.to(dev)) for k, v in gen.make_inputs(kw).items()}
+        kws = torch.empty(ck.workspace_size(kw.B, kw.H, kw.T, kw.dk, kw.dv, kw.chunk, ck.DTYPE_BF16), dtype=torch.uint8,
+                          device=dev)
+        ko = torch.empty((kw.B, kw.H, kw.T, kw.dv), dtype=torch.bfloat16, device=dev)
+        khT = torch.empty((kw.B, kw.H, kw.dk, kw.dv), dtype=torch.float32, device=dev)
+        kda_ms = timed(lambda: ck.chunk_fwd(kin["q"], kin["k"], kin["v"], kin["alpha"], kin["beta"], kin["h0"],
+                                            chunk=kw.chunk, workspace=kws, o=ko, hT=khT), a.steps)
+        kda_bytes, _ = fwd_algorithmic(kw)
+        del kin, kws, ko, khT
+
         # ---- backward on the bench workload (ckda_chunk_bwd, fp32 gradients)
         log("[bench] backward")
         bdo, bdhT = gen.make_output_grads(w, 99)
@@ -326,6 +340,12 @@ def main():
                 "deltaproduct2_decode_ms_per_step": round(dp2_dec_ms, 4),
                 "deltaproduct2_decode_total_GB_s": round(
                     (state_bytes + dec.N * dec.H * (3 * dec.dk + 3 * dec.dv + 2) * 2) / (dp2_dec_ms * 1e-3) / 1e9, 1),
+            },
+            "kda": {
+                "workload": kw.name,
+                "forward_call_ms_mean": round(kda_ms, 4),
+                "forward_tokens_per_s": round(kw.B * kw.T / (kda_ms * 1e-3), 1),
+                "algorithmic_GB_s": round(kda_bytes / (kda_ms * 1e-3) / 1e9, 1),
             },
             "channel_gather": {
                 "workload": f"{gw.name} (d_k {gw.dk} kept of {dk_in})",

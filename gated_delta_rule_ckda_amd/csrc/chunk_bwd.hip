@@ -103,6 +103,22 @@ __device__ __forceinline__ float ld_or(const T* p, size_t i, bool ok, float othe
   return ok ? x : other;
 }
 
+// Workgroup -> (batch-head, value slice) of the two sequential kernels.  With
+// xcd_map the nsl slices of one head get ids that are equal modulo 8, so they
+// run on one XCD (workgroups are dispatched to the 8 XCDs round-robin) and
+// share its L2: each chunk's record then comes from HBM once per head rather
+// than once per slice.
+__device__ __forceinline__ void head_slice(int id, int nsl, int xcd_map, long long& bh, int& slice) {
+  if (xcd_map) {
+    const int xcd = id % 8, k8 = id / 8;
+    bh = (long long)(k8 / nsl) * 8 + xcd;
+    slice = k8 % nsl;
+  } else {
+    bh = id / nsl;
+    slice = id % nsl;
+  }
+}
+
 // ============================================================ prep
 template <typename T, int DK>
 __global__ __launch_bounds__(kBThreads) void chunk_bwd_prep_kernel(const T* q, const T* k, const T* alpha,
@@ -240,7 +256,7 @@ template <typename T, int DK>
 __global__ __launch_bounds__(kBThreads) void chunk_bwd_states_kernel(const T* v, const float* __restrict__ h0,
                                                                      const float* __restrict__ rec,
                                                                      float* __restrict__ hc, int T_len, int nchunks,
-                                                                     int dv) {
+                                                                     int dv, int xcd_map) {
   constexpr int C = kBC, DS = kBDS, DKP = DK + 1, CP = C + 1, DSP = DS + 1;
   constexpr int NK = (C * DK + kBThreads - 1) / kBThreads, NT = (C * C + kBThreads - 1) / kBThreads;
   constexpr int NV = (C * DS + kBThreads - 1) / kBThreads;
@@ -248,8 +264,10 @@ __global__ __launch_bounds__(kBThreads) void chunk_bwd_states_kernel(const T* v,
   __shared__ float sH[DK * DSP], sKG[C * DKP], sKR[C * DKP], sTB[C * CP], sX[C * DSP], sU[C * DSP], sGC[DK];
   const int tid = threadIdx.x;
   const int nsl = dv / DS;
-  const long long bh = blockIdx.x / nsl;
-  const int col0 = (blockIdx.x % nsl) * DS;
+  long long bh;
+  int slice;
+  head_slice(blockIdx.x, nsl, xcd_map, bh, slice);
+  const int col0 = slice * DS;
   float rKG[NK], rKR[NK], rTB[NT], rV[NV], rGC = 0.f;
   auto fetch = [&](int c) __attribute__((always_inline)) {
     const float* rc = rec + (size_t)(bh * nchunks + c) * R::FLOATS;
@@ -322,7 +340,7 @@ template <typename T, int DK>
 __global__ __launch_bounds__(kBThreads) void chunk_bwd_dstates_kernel(const T* dout, const float* __restrict__ dhT,
                                                                       const float* __restrict__ rec,
                                                                       float* __restrict__ dhn, float* __restrict__ dh0,
-                                                                      int T_len, int nchunks, int dv) {
+                                                                      int T_len, int nchunks, int dv, int xcd_map) {
   constexpr int C = kBC, DS = kBDS, DKP = DK + 1, CP = C + 1, DSP = DS + 1;
   constexpr int NK = (C * DK + kBThreads - 1) / kBThreads, NT = (C * C + kBThreads - 1) / kBThreads;
   constexpr int NV = (C * DS + kBThreads - 1) / kBThreads;
@@ -331,8 +349,10 @@ __global__ __launch_bounds__(kBThreads) void chunk_bwd_dstates_kernel(const T* d
       sdU[C * DSP], sdX[C * DSP], sGC[DK];
   const int tid = threadIdx.x;
   const int nsl = dv / DS;
-  const long long bh = blockIdx.x / nsl;
-  const int col0 = (blockIdx.x % nsl) * DS;
+  long long bh;
+  int slice;
+  head_slice(blockIdx.x, nsl, xcd_map, bh, slice);
+  const int col0 = slice * DS;
   float rKG[NK], rKR[NK], rQG[NK], rM[NT], rTB[NT], rO[NV], rGC = 0.f;
   auto fetch = [&](int c) __attribute__((always_inline)) {
     const float* rc = rec + (size_t)(bh * nchunks + c) * R::FLOATS;
@@ -829,14 +849,15 @@ static hipError_t launch_bwd_t(const BwdArgs& a) {
   float* hc = rec + (size_t)total * R::FLOATS;
   float* dhn = hc + (size_t)total * DK * a.dv;
   const unsigned nsl = (unsigned)(a.dv / kBDS);
+  const int xcd_map = (BH % 8 == 0) ? 1 : 0;
   if (total > 0) {
     hipLaunchKernelGGL((chunk_bwd_prep_kernel<T, DK>), dim3((unsigned)total), dim3(kBThreads), 0, a.stream,
                        (const T*)a.q, (const T*)a.k, (const T*)a.alpha, (const T*)a.beta, rec, a.T, nch);
     hipLaunchKernelGGL((chunk_bwd_states_kernel<T, DK>), dim3((unsigned)(BH * nsl)), dim3(kBThreads), 0, a.stream,
-                       (const T*)a.v, a.h0, rec, hc, a.T, nch, a.dv);
+                       (const T*)a.v, a.h0, rec, hc, a.T, nch, a.dv, xcd_map);
   }
   hipLaunchKernelGGL((chunk_bwd_dstates_kernel<T, DK>), dim3((unsigned)(BH * nsl)), dim3(kBThreads), 0, a.stream,
-                     (const T*)a.dout, a.dhT, rec, dhn, a.gh0, a.T, nch, a.dv);
+                     (const T*)a.dout, a.dhT, rec, dhn, a.gh0, a.T, nch, a.dv, xcd_map);
   if (total > 0)
     hipLaunchKernelGGL((chunk_bwd_grad_kernel<T, DK>), dim3((unsigned)total), dim3(kBThreads), 0, a.stream,
                        (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.alpha, (const T*)a.beta,
