@@ -56,6 +56,8 @@ def _declare(lib):
     lib.ckda_oracle_deltaproduct2_decode.restype = i
     lib.ckda_oracle_bwd.argtypes = [vp] * 5 + [i, vp, i, vp, vp, i] + [vp] * 6 + [i] * 6
     lib.ckda_oracle_bwd.restype = i
+    lib.ckda_oracle_prologue_bwd.argtypes = [vp, vp, vp, vp, i, i, ctypes.c_longlong, i] + [vp] * 8
+    lib.ckda_oracle_prologue_bwd.restype = i
     return lib
 
 
@@ -230,6 +232,49 @@ def bwd(q, k, v, alpha, beta, do, dhT=None, h0=None, nthreads=0):
     return tuple(out)
 
 
+def prologue_bwd(a, b, k, q, flags, dalpha, dbeta, dk, dq):
+    """Reverse mode of prologue() (ckda_oracle_prologue_bwd): the gradients
+    with respect to a, b, k, q (the logits and raw vectors) from those with
+    respect to its outputs alpha, beta, k, q (fp64 arrays of the same shapes).
+    The sign of a gate is held constant and |tanh(a / 2)| takes the zero
+    subgradient at 0.  Returns fp64 (da, db, dk, dq)."""
+    a, b, k, q = (np.ascontiguousarray(x) for x in (a, b, k, q))
+    code = _code(a)
+    for x in (b, k, q):
+        if _code(x) != code:
+            raise TypeError("a, b, k, q must share one dtype")
+    if k.shape != a.shape or q.shape != a.shape or b.shape != a.shape[:-1]:
+        raise ValueError("inconsistent shapes")
+    g = [np.ascontiguousarray(x, dtype=np.float64) for x in (dalpha, dbeta, dk, dq)]
+    if g[0].shape != a.shape or g[1].shape != b.shape or g[2].shape != a.shape or g[3].shape != a.shape:
+        raise ValueError("gradient shapes must match the prologue's outputs")
+    dk_ = a.shape[-1]
+    ntok = int(np.prod(a.shape[:-1], dtype=np.int64))
+    da, dkr, dqr = (np.empty(a.shape, np.float64) for _ in range(3))
+    db = np.empty(b.shape, np.float64)
+    rc = _load().ckda_oracle_prologue_bwd(_ptr(a), _ptr(b), _ptr(k), _ptr(q), code, int(flags), ntok, dk_,
+                                          *(_ptr(x) for x in g), _ptr(da), _ptr(db), _ptr(dkr), _ptr(dqr))
+    if rc != 0:
+        raise RuntimeError(f"ckda_oracle_prologue_bwd failed with code {rc}")
+    return da, db, dkr, dqr
+
+
+def bwd_fused(q, k, v, a, b, do, dhT=None, h0=None, flags=GATES | NORM_K, scalar=False, nthreads=0):
+    """Gradients of fwd_fused() with respect to its raw inputs: prologue(),
+    bwd() on what it produced, prologue_bwd().  With scalar, a is [B,H,T]
+    (one gate logit per token and head, the same on every channel): its
+    gradient sums the per-channel ones.  Returns fp64 (dq, dk, dv, da, db,
+    dh0) for the raw q, k, v, a, b and h0."""
+    a = np.ascontiguousarray(a)
+    af = np.ascontiguousarray(np.broadcast_to(a[..., None], np.shape(k))) if scalar else a
+    alpha, beta, kk, qq = prologue(af, b, k, q, flags)
+    dq_, dk_, dv, dalpha, dbeta, dh0 = bwd(qq, kk, _widen(v), alpha, beta, do, dhT=dhT, h0=h0, nthreads=nthreads)
+    da, db, dkr, dqr = prologue_bwd(af, b, k, q, flags, dalpha, dbeta, dk_, dq_)
+    if scalar:
+        da = da.sum(axis=-1)
+    return dqr, dkr, dv, da, db, dh0
+
+
 def deltaproduct2(q, k, v, alpha, beta, h0=None, nthreads=0):
     """DeltaProduct_2 forward in fp64 (ckda_oracle_deltaproduct2).
 
@@ -318,6 +363,12 @@ class Variant:
 
     def bwd(self, *a, **kw):
         return self._swap(bwd, *a, **kw)
+
+    def prologue_bwd(self, *a, **kw):
+        return self._swap(prologue_bwd, *a, **kw)
+
+    def bwd_fused(self, *a, **kw):
+        return self._swap(bwd_fused, *a, **kw)
 
 
 def build_variant(source_text: str, out_path: str) -> "Variant":

@@ -235,6 +235,62 @@ int ckda_oracle_prologue(const void* a, const void* b, const void* k, const void
   return 0;
 }
 
+/* Reverse mode of the prologue: given the gradients of a loss with respect
+ * to its outputs (dalpha, dkk, dqq [ntok, dk] and dbeta [ntok], fp64), the
+ * gradients with respect to its inputs (da, dk_raw, dq_raw [ntok, dk] and
+ * db [ntok], fp64).  The gate follows the backward convention of the same
+ * slide frame ("Backup: practical gates differ from exact theoretical
+ * endpoints"): the sign s is held constant and |r| takes the zero subgradient
+ * at r = 0, so
+ *   d alpha / d a = s (1 - eps) d|r|/da,   d|r|/da = sign(r) (1 - r^2) / 2 for r != 0, 0 at r = 0;
+ *   d beta / d b = 2 sigma(b) (1 - sigma(b));
+ * a normalised row y = x n, n = (sum x^2 + 1e-6)^-1/2, passes back
+ *   dx = n dy - n^3 x (x . dy)
+ * (the Jacobian of y is n I - n^3 x x^T).  A step whose flag is off passes its
+ * gradient through.  Returns 0, or 1 for invalid arguments. */
+static double practical_alpha_slope(double a) {
+  const double eps = exp(-5.0);
+  const double r = tanh(0.5 * a);
+  const double s = r >= 0.0 ? 1.0 : -1.0;   /* held constant */
+  const double dabs = r > 0.0 ? 0.5 * (1.0 - r * r) : r < 0.0 ? -0.5 * (1.0 - r * r) : 0.0;
+  return s * (1.0 - eps) * dabs;
+}
+
+static double practical_beta_slope(double b) {
+  const double sg = 1.0 / (1.0 + exp(-b));
+  return 2.0 * sg * (1.0 - sg);
+}
+
+static void unit_rows_bwd(const void* x, int dtype, long long ntok, int dk, int on, const double* dy, double* dx) {
+  for (long long t = 0; t < ntok; ++t) {
+    if (!on) {
+      for (int i = 0; i < dk; ++i) dx[t * dk + i] = dy[t * dk + i];
+      continue;
+    }
+    double ss = 0.0, xdy = 0.0;
+    for (int i = 0; i < dk; ++i) {
+      const double e = widen(x, t * dk + i, dtype);
+      ss += e * e;
+      xdy += e * dy[t * dk + i];
+    }
+    const double n = 1.0 / sqrt(ss + 1e-6);
+    for (int i = 0; i < dk; ++i) dx[t * dk + i] = n * dy[t * dk + i] - n * n * n * widen(x, t * dk + i, dtype) * xdy;
+  }
+}
+
+int ckda_oracle_prologue_bwd(const void* a, const void* b, const void* k, const void* q, int dtype, int flags,
+                             long long ntok, int dk, const double* dalpha, const double* dbeta, const double* dkk,
+                             const double* dqq, double* da, double* db, double* dk_raw, double* dq_raw) {
+  if (!valid_dtype(dtype) || ntok < 0 || dk <= 0 || (flags & ~7) != 0) return 1;
+  for (long long i = 0; i < ntok * dk; ++i)
+    da[i] = (flags & PRO_GATES) ? dalpha[i] * practical_alpha_slope(widen(a, i, dtype)) : dalpha[i];
+  for (long long t = 0; t < ntok; ++t)
+    db[t] = (flags & PRO_GATES) ? dbeta[t] * practical_beta_slope(widen(b, t, dtype)) : dbeta[t];
+  unit_rows_bwd(k, dtype, ntok, dk, flags & PRO_NORM_K, dkk, dk_raw);
+  unit_rows_bwd(q, dtype, ntok, dk, flags & PRO_NORM_Q, dqq, dq_raw);
+  return 0;
+}
+
 /* ---------------------------------------------------------------- DeltaProduct_2
  *
  * The DeltaProduct_2 comparator of the "Complex KDA" paper (Fig. 5 and the

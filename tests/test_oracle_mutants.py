@@ -1,13 +1,14 @@
 """Each plausible slip planted in a copy of the oracle (on the CPU) must fail at
 least one pin.  This shows the pins constrain every part of the step: the
 order gate -> read -> correct -> query, the sign and weight of the correction,
-the row/column role of the gate, the signed gates, and the per-token prologue
-(practical gates from logits, unit-norm keys and queries)."""
+the row/column role of the gate, the signed gates, the per-token prologue
+(practical gates from logits, unit-norm keys and queries) and its backward."""
 import pytest
 
 import oracle
 import test_oracle_bwd as bwdpins
 import test_oracle_pins as pins
+import test_oracle_prologue_bwd as ppins
 
 ORIG_GATE = "S[(long)i * dv + j] *= a[i];"
 ORIG_READ = "s[j] += S[(long)i * dv + j] * kk[i];"
@@ -65,6 +66,17 @@ MUTANTS = {
                                     "          for (int j = 0; j < dv; ++j) acc += Hp[(long)i * dv + j] * gd[j];")],
     "bwd_ds_sign": [("          ds[j] = -b * du[j];", "          ds[j] = b * du[j];")],
     "bwd_dalpha_on_gated_state": [("            ga += dhb * Hp[(long)i * dv + j];", "            ga += dhb * Hb[(long)i * dv + j];")],
+    # prologue backward (gate slope with the sign held constant, beta slope, normalisation)
+    "pbwd_slope_without_one_minus_r2": [("r > 0.0 ? 0.5 * (1.0 - r * r) : r < 0.0 ? -0.5 * (1.0 - r * r) : 0.0",
+                                         "r > 0.0 ? 0.5 : r < 0.0 ? -0.5 : 0.0")],
+    "pbwd_sign_not_held": [("  return s * (1.0 - eps) * dabs;", "  return (1.0 - eps) * dabs;")],
+    "pbwd_slope_at_kink": [("r > 0.0 ? 0.5 * (1.0 - r * r) : r < 0.0 ? -0.5 * (1.0 - r * r) : 0.0",
+                            "r > 0.0 ? 0.5 * (1.0 - r * r) : r < 0.0 ? -0.5 * (1.0 - r * r) : 0.5")],
+    "pbwd_beta_slope_halved": [("  return 2.0 * sg * (1.0 - sg);", "  return sg * (1.0 - sg);")],
+    "pbwd_norm_radial_term_dropped": [("n * dy[t * dk + i] - n * n * n * widen(x, t * dk + i, dtype) * xdy",
+                                       "n * dy[t * dk + i]")],
+    "pbwd_norm_radial_power": [("n * dy[t * dk + i] - n * n * n * widen(x, t * dk + i, dtype) * xdy",
+                                "n * dy[t * dk + i] - n * widen(x, t * dk + i, dtype) * xdy")],
     "dp2_value_not_corrected": [("    for (int j = 0; j < dv; ++j) S[(long)i * dv + j] += b * kk[i] * (vv[j] - w[j]);",
                                  "    for (int j = 0; j < dv; ++j) S[(long)i * dv + j] += b * kk[i] * vv[j];")],
 }
@@ -96,6 +108,10 @@ PIN_CALLS = [
     lambda o: pins.test_deltaproduct2_decode_continues_the_forward(o),
     lambda o: bwdpins.test_backward_matches_finite_differences(o, "uniform"),
     lambda o: bwdpins.test_backward_of_pure_decay_is_closed_form(o),
+    lambda o: ppins.test_prologue_backward_matches_finite_differences(o, 7),
+    lambda o: ppins.test_gate_slope_closed_form_and_zero_subgradient(o),
+    lambda o: ppins.test_normalisation_backward_is_tangent(o),
+    lambda o: ppins.test_fused_backward_matches_finite_differences(o, False),
 ]
 
 

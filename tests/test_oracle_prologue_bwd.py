@@ -1,0 +1,144 @@
+"""Pins of the oracle's prologue backward (ckda_oracle_prologue_bwd) and of
+the fused backward built from it (oracle.bwd_fused), on the CPU.
+
+The prologue of the "Complex KDA" discussion slides (frame "Backup: practical
+gates differ from exact theoretical endpoints") makes the gate from a logit,
+alpha = s [eps + (1 - eps) |tanh(a / 2)|], s the sign, and beta = 2 sigma(b);
+the same frame fixes the backward convention: s is held constant and |r| takes
+the zero subgradient at r = 0.  Away from a = 0 the gate is smooth, so central
+finite differences of the pinned forward prologue decide the derivative; at
+a = 0 the convention decides it (zero), and on either side of 0 the slope is
+the one-sided slope of the smooth branch, not the jump of 2 eps."""
+import math
+
+import numpy as np
+import pytest
+
+RNG = np.random.default_rng
+EPS5 = math.exp(-5.0)
+
+
+def _problem(seed, ntok=5, dk=4, margin=0.05):
+    r = RNG(seed)
+    a = r.normal(0.0, 2.0, (ntok, dk))
+    a = np.where(np.abs(a) < margin, np.sign(a + 1e-300) * margin, a)   # away from the kink at 0
+    b = r.normal(0.0, 1.5, ntok)
+    k = r.standard_normal((ntok, dk))
+    q = r.standard_normal((ntok, dk))
+    g = [r.standard_normal((ntok, dk)), r.standard_normal(ntok), r.standard_normal((ntok, dk)),
+         r.standard_normal((ntok, dk))]
+    return a, b, k, q, g
+
+
+def _lin(o, a, b, k, q, flags, g):
+    al, be, kk, qq = o.prologue(a, b, k, q, flags)
+    return float(np.sum(al * g[0]) + np.sum(be * g[1]) + np.sum(kk * g[2]) + np.sum(qq * g[3]))
+
+
+@pytest.mark.parametrize("flags", [7, 1, 2, 4, 0])
+def test_prologue_backward_matches_finite_differences(oracle_lib, flags, seed=3):
+    """L = sum(dalpha alpha) + sum(dbeta beta) + sum(dk k^) + sum(dq q^):
+    the backward's gradients equal central differences of L in fp64."""
+    o = oracle_lib
+    a, b, k, q, g = _problem(seed)
+    da, db, dk, dq = o.prologue_bwd(a, b, k, q, flags, *g)
+    h = 1e-6
+    for name, x, grad in (("a", a, da), ("b", b, db), ("k", k, dk), ("q", q, dq)):
+        for ix in np.ndindex(x.shape):
+            old = x[ix]
+            x[ix] = old + h
+            lp = _lin(o, a, b, k, q, flags, g)
+            x[ix] = old - h
+            lm = _lin(o, a, b, k, q, flags, g)
+            x[ix] = old
+            fd = (lp - lm) / (2 * h)
+            assert abs(fd - grad[ix]) <= 1e-7 * max(1.0, abs(fd)), (flags, name, ix, fd, grad[ix])
+
+
+def test_gate_slope_closed_form_and_zero_subgradient(oracle_lib):
+    """d alpha / d a = (1 - eps) (1 - r^2) / 2 on both sides of zero (the sign
+    held constant), exactly 0 at a = 0; beta' = 2 sigma (1 - sigma)."""
+    o = oracle_lib
+    a0 = 2.0 * math.atanh(0.5)                       # r = 1/2
+    a = np.array([[0.0, a0, -a0, 1e-9, -1e-9, 30.0]])
+    b = np.array([0.0])
+    one = np.ones_like(a)
+    da, db, _, _ = o.prologue_bwd(a, b, np.ones_like(a), np.ones_like(a), 1, one, np.ones(1), one, one)
+    assert da[0, 0] == 0.0                            # zero subgradient of |r| at r = 0
+    assert abs(da[0, 1] - (1 - EPS5) * 0.375) < 1e-15
+    assert da[0, 2] == da[0, 1]                        # same slope below zero: the sign is detached
+    assert abs(da[0, 3] - (1 - EPS5) * 0.5) < 1e-12    # one-sided slope, not the 2 eps jump
+    assert abs(da[0, 4] - (1 - EPS5) * 0.5) < 1e-12
+    assert 0.0 < da[0, 5] < 1e-12                      # saturated gate
+    assert db[0] == 0.5                                # 2 sigma(0) (1 - sigma(0))
+
+
+def test_detached_sign_differs_from_differencing_across_zero(oracle_lib):
+    """A central difference across a = 0 sees the jump 2 eps of the gate; the
+    backward does not (its slope near 0 is (1 - eps) / 2)."""
+    o = oracle_lib
+    h = 1e-8
+    al_p, _, _, _ = o.prologue(np.array([[h]]), np.zeros(1), np.ones((1, 1)), np.ones((1, 1)), 1)
+    al_m, _, _, _ = o.prologue(np.array([[-h]]), np.zeros(1), np.ones((1, 1)), np.ones((1, 1)), 1)
+    across = (al_p[0, 0] - al_m[0, 0]) / (2 * h)
+    assert across > 1e5                                # dominated by 2 eps / (2 h)
+    da, _, _, _ = o.prologue_bwd(np.array([[h]]), np.zeros(1), np.ones((1, 1)), np.ones((1, 1)), 1,
+                                 np.ones((1, 1)), np.ones(1), np.ones((1, 1)), np.ones((1, 1)))
+    assert abs(da[0, 0] - (1 - EPS5) / 2) < 1e-12
+
+
+def test_normalisation_backward_is_tangent(oracle_lib):
+    """The gradient through a unit-norm row is orthogonal to the row (the
+    normalisation cannot change with the row's length), and an upstream
+    gradient along the row itself maps to ~0."""
+    o = oracle_lib
+    r = RNG(11)
+    k = r.standard_normal((6, 8)) * 3.0
+    z = np.zeros((6, 8))
+    dy = r.standard_normal((6, 8))
+    _, _, dk, _ = o.prologue_bwd(z, np.zeros(6), k, k, 2, z, np.zeros(6), dy, z)
+    assert np.max(np.abs(np.sum(dk * k, axis=1))) < 1e-7 * np.max(np.abs(dk))
+    _, _, dk2, _ = o.prologue_bwd(z, np.zeros(6), k, k, 2, z, np.zeros(6), k.copy(), z)
+    assert np.max(np.abs(dk2)) < 1e-6
+
+
+def _fused_problem(seed, scalar):
+    r = RNG(seed)
+    B, H, T, dk, dv = 1, 2, 7, 3, 2
+    q = r.standard_normal((B, H, T, dk))
+    k = r.standard_normal((B, H, T, dk))
+    v = r.standard_normal((B, H, T, dv))
+    a = r.normal(0.0, 2.0, (B, H, T) if scalar else (B, H, T, dk))
+    a = np.where(np.abs(a) < 0.05, 0.05, a)
+    b = r.normal(0.0, 1.0, (B, H, T))
+    h0 = 0.3 * r.standard_normal((B, H, dk, dv))
+    do = r.standard_normal((B, H, T, dv))
+    dhT = r.standard_normal((B, H, dk, dv))
+    return q, k, v, a, b, h0, do, dhT
+
+
+@pytest.mark.parametrize("scalar", [False, True])
+def test_fused_backward_matches_finite_differences(oracle_lib, scalar, flags=7):
+    """bwd_fused (prologue, recurrence backward, prologue backward) against
+    central differences of fwd_fused for L = sum(o do) + sum(hT dhT), with
+    respect to every raw input: logits, raw keys and queries, values, h0."""
+    o = oracle_lib
+    q, k, v, a, b, h0, do, dhT = _fused_problem(5, scalar)
+    grads = o.bwd_fused(q, k, v, a, b, do, dhT=dhT, h0=h0, flags=flags, scalar=scalar)
+
+    def loss():
+        af = np.broadcast_to(a[..., None], k.shape).copy() if scalar else a
+        out, hT = o.fwd_fused(q, k, v, af, b, h0=h0, flags=flags)
+        return float(np.sum(out * do) + np.sum(hT * dhT))
+
+    h = 1e-6
+    for name, x, g in zip(("q", "k", "v", "a", "b", "h0"), (q, k, v, a, b, h0), grads):
+        for ix in np.ndindex(x.shape):
+            old = x[ix]
+            x[ix] = old + h
+            lp = loss()
+            x[ix] = old - h
+            lm = loss()
+            x[ix] = old
+            fd = (lp - lm) / (2 * h)
+            assert abs(fd - g[ix]) <= 1e-6 * max(1.0, abs(fd)), (scalar, name, ix, fd, g[ix])
