@@ -299,6 +299,13 @@ def main():
         bwd_ms = timed(lambda: ck.chunk_bwd(d["q"], d["k"], d["v"], d["alpha"], d["beta"], bdo, h0=d["h0"], dhT=bdhT,
                                             workspace=bws), max(3, a.steps // 3))
         del bws
+        # the same through the prologue (ckda_chunk_bwd_ex): gradients with respect to
+        # the gate and beta logits and the raw keys, on the fused prologue's inputs
+        bws = torch.empty(ck.bwd_ex_workspace_size(w.B, w.H, w.T, w.dk, w.dv, ck.DTYPE_BF16, fuse), dtype=torch.uint8,
+                          device=dev)
+        bwdx_ms = timed(lambda: ck.chunk_bwd(lg["q"], lg["k"], lg["v"], lg["alpha"], lg["beta"], bdo, h0=lg["h0"],
+                                             dhT=bdhT, workspace=bws, fuse=fuse), max(3, a.steps // 3))
+        del bws, lg
 
         # ---- comparators on the bench shape: the scalar (Gated DeltaNet) gate and
         # ungated DeltaProduct_2 (two delta-rule updates per token), and the
@@ -331,6 +338,9 @@ def main():
                 "tokens_per_s": round(tokens / (bwd_ms * 1e-3), 1),
                 "forward_plus_backward_tokens_per_s": round(tokens / ((bwd_ms + call_ms) * 1e-3), 1),
                 "gradients": "fp32 dq, dk, dv, dalpha, dbeta, dh0",
+                "fused_prologue_call_ms_mean": round(bwdx_ms, 4),
+                "fused_prologue_gradients": "with respect to the gate and beta logits and the raw keys "
+                                            "(CKDA_FUSE_GATES | CKDA_FUSE_NORM_K)",
             },
             "comparators": {
                 "scalar_gate_forward_call_ms_mean": round(scalar_ms, 4),

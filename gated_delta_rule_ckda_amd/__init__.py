@@ -29,7 +29,7 @@ GATE_SCALAR = 8                                      # CKDA_GATE_SCALAR
 EXPORTS = ("ckda_chunk_fwd_workspace_size", "ckda_chunk_fwd", "ckda_chunk_fwd_timed", "ckda_chunk_fwd_ex",
            "ckda_chunk_fwd_gather", "ckda_decode_step", "ckda_decode_step_ex", "ckda_decode_step_gather",
            "ckda_deltaproduct2_fwd", "ckda_deltaproduct2_decode_step", "ckda_chunk_bwd",
-           "ckda_chunk_bwd_workspace_size",
+           "ckda_chunk_bwd_workspace_size", "ckda_chunk_bwd_ex", "ckda_chunk_bwd_ex_workspace_size",
            "ckda_status_string", "ckda_last_error", "ckda_abi_version")
 
 _lib = None
@@ -70,6 +70,10 @@ def lib() -> ctypes.CDLL:
         L.ckda_chunk_bwd_workspace_size.restype = sz
         L.ckda_chunk_bwd.argtypes = [vp] * 14 + [i] * 6 + [vp, sz, vp]
         L.ckda_chunk_bwd.restype = i
+        L.ckda_chunk_bwd_ex_workspace_size.argtypes = [i] * 7
+        L.ckda_chunk_bwd_ex_workspace_size.restype = sz
+        L.ckda_chunk_bwd_ex.argtypes = [vp] * 14 + [i] * 7 + [vp, sz, vp]
+        L.ckda_chunk_bwd_ex.restype = i
         L.ckda_decode_step.argtypes = [vp] * 7 + [i] * 5 + [vp]
         L.ckda_decode_step.restype = i
         L.ckda_decode_step_ex.argtypes = [vp] * 7 + [i] * 6 + [vp]
@@ -262,10 +266,18 @@ def bwd_workspace_size(B, H, T, dk, dv, dtype) -> int:
     return int(lib().ckda_chunk_bwd_workspace_size(B, H, T, dk, dv, code))
 
 
-def chunk_bwd(q, k, v, alpha, beta, do, h0=None, dhT=None, want_dh0=True, workspace=None, stream=None):
+def bwd_ex_workspace_size(B, H, T, dk, dv, dtype, flags) -> int:
+    code = dtype if isinstance(dtype, int) else _dtype_code(torch.empty(0, dtype=dtype))
+    return int(lib().ckda_chunk_bwd_ex_workspace_size(B, H, T, dk, dv, code, int(flags)))
+
+
+def chunk_bwd(q, k, v, alpha, beta, do, h0=None, dhT=None, want_dh0=True, workspace=None, stream=None, fuse=0):
     """Backward of chunk_fwd (ckda_chunk_bwd): given do = dL/do [B,H,T,dv]
     (input dtype) and dhT = dL/dH_T [B,H,dk,dv] fp32 or None, returns fp32
-    (dq, dk, dv, dalpha, dbeta, dh0 or None)."""
+    (dq, dk, dv, dalpha, dbeta, dh0 or None).  With `fuse` (FUSE_* and
+    GATE_SCALAR bits, ckda_chunk_bwd_ex) the inputs are those of the fused
+    forward and the gradients are with respect to them: logits, raw keys
+    and queries; with GATE_SCALAR alpha and dalpha are [B,H,T]."""
     B, H, T, dk = q.shape
     dv = v.shape[-1]
     _require(dict(q=q, k=k, v=v, alpha=alpha, beta=beta, do=do), q.dtype)
@@ -274,18 +286,22 @@ def chunk_bwd(q, k, v, alpha, beta, do, h0=None, dhT=None, want_dh0=True, worksp
         _require(dict(h0=h0), torch.float32)
     if dhT is not None:
         _require(dict(dhT=dhT), torch.float32)
-    need = bwd_workspace_size(B, H, T, dk, dv, code)
+    need = bwd_ex_workspace_size(B, H, T, dk, dv, code, fuse) if fuse else bwd_workspace_size(B, H, T, dk, dv, code)
     if need == 0:
-        raise CkdaError(3, f"unsupported sizes dk={dk} dv={dv}")
+        raise CkdaError(3, f"unsupported sizes dk={dk} dv={dv} or flags {fuse}")
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     f32 = dict(dtype=torch.float32, device=q.device)
-    gq, gk, galpha = (torch.empty((B, H, T, dk), **f32) for _ in range(3))
+    gq, gk = (torch.empty((B, H, T, dk), **f32) for _ in range(2))
+    galpha = torch.empty((B, H, T) if fuse & GATE_SCALAR else (B, H, T, dk), **f32)
     gv = torch.empty((B, H, T, dv), **f32)
     gbeta = torch.empty((B, H, T), **f32)
     gh0 = torch.empty((B, H, dk, dv), **f32) if want_dh0 else None
-    _check(lib().ckda_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(h0), _ptr(do), _ptr(dhT),
-                                _ptr(gq), _ptr(gk), _ptr(gv), _ptr(galpha), _ptr(gbeta), _ptr(gh0),
-                                B, H, T, dk, dv, code, _ptr(workspace), workspace.numel() * workspace.element_size(),
-                                _stream(stream)))
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(h0), _ptr(do), _ptr(dhT),
+            _ptr(gq), _ptr(gk), _ptr(gv), _ptr(galpha), _ptr(gbeta), _ptr(gh0), B, H, T, dk, dv, code)
+    tail = (_ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    if fuse:
+        _check(lib().ckda_chunk_bwd_ex(*args, int(fuse), *tail))
+    else:
+        _check(lib().ckda_chunk_bwd(*args, *tail))
     return gq, gk, gv, galpha, gbeta, gh0

@@ -221,25 +221,41 @@ size_t ckda_chunk_bwd_workspace_size(int B, int H, int T, int dk, int dv, int dt
   return bytes == 0 ? 256 : bytes;
 }
 
-int ckda_chunk_bwd(const void* q, const void* k, const void* v, const void* alpha, const void* beta,
-                   const float* h0, const void* dout, const float* dhT, float* dq, float* dk_out, float* dv_out,
-                   float* dalpha, float* dbeta, float* dh0, int B, int H, int T, int dk, int dv, int dtype,
-                   void* workspace, size_t workspace_bytes, void* stream) {
-  const char* fn = "ckda_chunk_bwd";
+size_t ckda_chunk_bwd_ex_workspace_size(int B, int H, int T, int dk, int dv, int dtype, int flags) {
+  if ((flags & ~kFlagsAll) != 0) return 0;
+  if (flags == 0) return ckda_chunk_bwd_workspace_size(B, H, T, dk, dv, dtype);
+  if (B < 0 || H < 0 || T < 0) return 0;
+  if (!supported_dim(dk) || !supported_dim(dv) || !supported_dtype(dtype)) return 0;
+  const size_t bytes = ckda::prologue_bwd_workspace_floats(B, H, T, dk, dv, flags) * 4;
+  return bytes == 0 ? 256 : bytes;
+}
+
+// Shared checks and dispatch of the backward entry points; flags as
+// ckda_chunk_bwd_ex (0 for ckda_chunk_bwd).
+static int chunk_bwd_impl(const char* fn, const void* q, const void* k, const void* v, const void* alpha,
+                          const void* beta, const float* h0, const void* dout, const float* dhT, float* dq,
+                          float* dk_out, float* dv_out, float* dalpha, float* dbeta, float* dh0, int B, int H, int T,
+                          int dk, int dv, int dtype, int flags, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  if ((flags & ~kFlagsAll) != 0)
+    return fail(CKDA_ERR_FLAGS, "%s: flags 0x%x has bits outside CKDA_FUSE_* and CKDA_GATE_SCALAR (0x%x)", fn, flags,
+                kFlagsAll);
   if (B < 0 || H < 0 || T < 0) return fail(CKDA_ERR_DIM, "%s: negative size (B=%d H=%d T=%d)", fn, B, H, T);
   if (!supported_dtype(dtype)) return fail(CKDA_ERR_UNSUPPORTED, "%s: dtype %d is not F32(0) or BF16(1)", fn, dtype);
   if (!supported_dim(dk) || !supported_dim(dv))
     return fail(CKDA_ERR_UNSUPPORTED, "%s: dk=%d dv=%d (supported: 16, 32, 64, 128)", fn, dk, dv);
   const size_t BH = (size_t)B * H;
   if (BH == 0) return ok();
+  const bool scalar = (flags & CKDA_GATE_SCALAR) != 0;
   const size_t es = dtype_bytes(dtype);
   const size_t nk = BH * T * dk, nv = BH * T * dv, nb = BH * T, ns = BH * dk * dv;
+  const size_t na = scalar ? nb : nk;   // gates (and their gradient)
   if (T > 0 && (!q || !k || !v || !alpha || !beta || !dout || !dq || !dk_out || !dv_out || !dalpha || !dbeta))
     return fail(CKDA_ERR_NULL, "%s: inputs, do and every per-token gradient are required", fn);
   const size_t nch = BH * (((size_t)T + 31) / 32);
-  if (nch > (size_t)INT32_MAX || BH * (size_t)(dv / 16) > (size_t)INT32_MAX)
+  if (nch > (size_t)INT32_MAX || BH * (size_t)(dv / 16) > (size_t)INT32_MAX || (flags && (nb + 3) / 4 > INT32_MAX))
     return fail(CKDA_ERR_DIM, "%s: sizes exceed the launch grid", fn);
-  const size_t need = ckda_chunk_bwd_workspace_size(B, H, T, dk, dv, dtype);
+  const size_t need = ckda_chunk_bwd_ex_workspace_size(B, H, T, dk, dv, dtype, flags);
   if (!workspace) return fail(CKDA_ERR_WORKSPACE, "%s: workspace is NULL", fn);
   if (workspace_bytes < need)
     return fail(CKDA_ERR_WORKSPACE, "%s: workspace of %zu bytes, need %zu", fn, workspace_bytes, need);
@@ -249,12 +265,12 @@ int ckda_chunk_bwd(const void* q, const void* k, const void* v, const void* alph
   for (int i = 0; i < 14; ++i)
     if (ptrs[i] && misaligned(ptrs[i])) return fail(CKDA_ERR_DIM, "%s: %s is not 16-byte aligned", fn, names[i]);
   const Range in[] = {range("q", q, T ? nk * es : 0),       range("k", k, T ? nk * es : 0),
-                      range("v", v, T ? nv * es : 0),       range("alpha", alpha, T ? nk * es : 0),
+                      range("v", v, T ? nv * es : 0),       range("alpha", alpha, T ? na * es : 0),
                       range("beta", beta, T ? nb * es : 0), range("h0", h0, h0 ? ns * 4 : 0),
                       range("do", dout, T ? nv * es : 0),   range("dhT", dhT, dhT ? ns * 4 : 0),
                       range("workspace", workspace, need)};
   const Range out[] = {range("dq", dq, T ? nk * 4 : 0),         range("dk", dk_out, T ? nk * 4 : 0),
-                       range("dv", dv_out, T ? nv * 4 : 0),     range("dalpha", dalpha, T ? nk * 4 : 0),
+                       range("dv", dv_out, T ? nv * 4 : 0),     range("dalpha", dalpha, T ? na * 4 : 0),
                        range("dbeta", dbeta, T ? nb * 4 : 0),   range("dh0", dh0, dh0 ? ns * 4 : 0)};
   for (const Range& o : out) {
     for (const Range& r : in)
@@ -264,9 +280,25 @@ int ckda_chunk_bwd(const void* q, const void* k, const void* v, const void* alph
   }
   ckda::BwdArgs a{q, k, v, alpha, beta, h0, dout, dhT, dq, dk_out, dv_out, dalpha, dbeta, dh0,
                   B, H, T, dk, dv, dtype, workspace, (hipStream_t)stream};
-  hipError_t e = ckda::launch_chunk_bwd(a);
+  hipError_t e = flags ? ckda::launch_prologue_bwd(a, flags) : ckda::launch_chunk_bwd(a);
   if (e != hipSuccess) return fail(CKDA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
   return ok();
+}
+
+int ckda_chunk_bwd(const void* q, const void* k, const void* v, const void* alpha, const void* beta,
+                   const float* h0, const void* dout, const float* dhT, float* dq, float* dk_out, float* dv_out,
+                   float* dalpha, float* dbeta, float* dh0, int B, int H, int T, int dk, int dv, int dtype,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  return chunk_bwd_impl("ckda_chunk_bwd", q, k, v, alpha, beta, h0, dout, dhT, dq, dk_out, dv_out, dalpha, dbeta, dh0,
+                        B, H, T, dk, dv, dtype, 0, workspace, workspace_bytes, stream);
+}
+
+int ckda_chunk_bwd_ex(const void* q, const void* k, const void* v, const void* alpha, const void* beta,
+                      const float* h0, const void* dout, const float* dhT, float* dq, float* dk_out, float* dv_out,
+                      float* dalpha, float* dbeta, float* dh0, int B, int H, int T, int dk, int dv, int dtype,
+                      int flags, void* workspace, size_t workspace_bytes, void* stream) {
+  return chunk_bwd_impl("ckda_chunk_bwd_ex", q, k, v, alpha, beta, h0, dout, dhT, dq, dk_out, dv_out, dalpha, dbeta,
+                        dh0, B, H, T, dk, dv, dtype, flags, workspace, workspace_bytes, stream);
 }
 
 int ckda_chunk_fwd_timed(const void* q, const void* k, const void* v, const void* alpha,

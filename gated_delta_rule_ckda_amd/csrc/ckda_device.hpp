@@ -66,7 +66,7 @@ constexpr float kGateFloor = 0.006737946999085467f;  // e^-5: log|alpha| >= -5
 //   else:     (1 - e) / (1 + e), e = e^-2x by v_exp_f32 and v_rcp_f32
 //             (1 - e > 0.46, no cancellation).
 // Both branches are evaluated and selected (no divergence); a few ulp.
-__device__ __forceinline__ float practical_gate(float a) {
+__device__ __forceinline__ float tanh_half_abs(float a) {   // |tanh(a / 2)|
   const float x = 0.5f * fabsf(a);
   const float z = x * x;
   float p = -1382.f / 155925.f;
@@ -77,13 +77,26 @@ __device__ __forceinline__ float practical_gate(float a) {
   const float small = __builtin_fmaf(p * z, x, x);
   const float e = __builtin_amdgcn_exp2f(-2.8853900817779268f * x);   // 2 log2(e) = 2.88539...
   const float large = (1.f - e) * __builtin_amdgcn_rcpf(1.f + e);
-  const float r = x < 0.3125f ? small : large;
-  const float g = __builtin_fmaf(1.f - kGateFloor, r, kGateFloor);
+  return x < 0.3125f ? small : large;
+}
+__device__ __forceinline__ float practical_gate(float a) {
+  const float g = __builtin_fmaf(1.f - kGateFloor, tanh_half_abs(a), kGateFloor);
   return a >= 0.f ? g : -g;
+}
+// d alpha / d a with the sign held constant: s (1 - eps) d|r|/da = (1 - eps)
+// (1 - r^2) / 2, and the zero subgradient of |r| at r = 0 (a = 0).
+__device__ __forceinline__ float practical_gate_slope(float a) {
+  const float r = tanh_half_abs(a);
+  return a == 0.f ? 0.f : 0.5f * (1.f - kGateFloor) * __builtin_fmaf(-r, r, 1.f);
 }
 
 // beta = 2 sigma(b) in [0, 2].
 __device__ __forceinline__ float practical_beta(float b) { return 2.f / (1.f + expf(-b)); }
+// d beta / d b = 2 sigma(b) (1 - sigma(b)).
+__device__ __forceinline__ float practical_beta_slope(float b) {
+  const float sg = 1.f / (1.f + expf(-b));
+  return 2.f * sg * (1.f - sg);
+}
 
 // Two floats -> packed bf16 pair (low = a).
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {

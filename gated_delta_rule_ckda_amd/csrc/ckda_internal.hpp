@@ -60,6 +60,10 @@ struct BwdArgs {
 // state gradients), 0 for an unsupported dk
 size_t chunk_bwd_workspace_floats(int B, int H, int T, int dk, int dv);
 hipError_t launch_chunk_bwd(const BwdArgs& a);
+// the backward through the per-token prologue (prologue_bwd.hip); flags as
+// CKDA_FUSE_* | CKDA_GATE_SCALAR, nonzero
+size_t prologue_bwd_workspace_floats(int B, int H, int T, int dk, int dv, int flags);
+hipError_t launch_prologue_bwd(const BwdArgs& a, int flags);
 
 hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_chunk_fwd(const ChunkArgs& a);

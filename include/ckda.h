@@ -253,6 +253,39 @@ int ckda_chunk_bwd(const void* q, const void* k, const void* v, const void* alph
                    float* dalpha, float* dbeta, float* dh0, int B, int H, int T, int dk_, int dv_, int dtype,
                    void* workspace, size_t workspace_bytes, void* stream);
 
+/* Bytes of device workspace ckda_chunk_bwd_ex needs for these sizes and
+ * flags, or 0 when they are invalid or unsupported.  With flags 0 it equals
+ * ckda_chunk_bwd_workspace_size; otherwise it also holds the prologue's
+ * outputs, v and do in fp32 (3 dk + 2 dv + 1 floats per token and head, plus
+ * dk more with CKDA_GATE_SCALAR). */
+size_t ckda_chunk_bwd_ex_workspace_size(int B, int H, int T, int dk, int dv, int dtype, int flags);
+
+/* Backward of ckda_chunk_fwd_ex: the gradients with respect to the raw
+ * inputs the fused forward takes.  `flags` as ckda_chunk_fwd_ex
+ * (CKDA_FUSE_GATES, CKDA_FUSE_NORM_K, CKDA_FUSE_NORM_Q, CKDA_GATE_SCALAR):
+ *   CKDA_FUSE_GATES  dalpha, dbeta are the gradients with respect to the
+ *                    logits a, b.  The gate's backward follows the "Complex
+ *                    KDA" discussion slides (frame "Backup: practical gates
+ *                    differ from exact theoretical endpoints"): the sign s is
+ *                    held constant and |tanh(a/2)| takes the zero subgradient
+ *                    at 0, so d alpha/d a = (1 - e^-5)(1 - tanh(a/2)^2)/2 for
+ *                    a != 0 and 0 at a = 0 (the jump of the gate at 0 passes
+ *                    no gradient); d beta/d b = 2 sigma(b)(1 - sigma(b)).
+ *   CKDA_FUSE_NORM_K / _NORM_Q  dk / dq are with respect to the raw rows:
+ *                    dx = n (dy - y (y . dy)), y = x n, n = (|x|^2 + 1e-6)^-1/2.
+ *   CKDA_GATE_SCALAR alpha (and dalpha) are [B, H, T]: one gate per token and
+ *                    head; its gradient sums those of the channels it gates.
+ * Other arguments, layouts and rules as ckda_chunk_bwd (dv and dh0 are
+ * unaffected by the prologue).  With flags 0 this is ckda_chunk_bwd.
+ * Otherwise the prologue's outputs (and v, do) are first written to the
+ * workspace in fp32, the fp32 backward runs on them, and a last pass maps the
+ * gradients back through the prologue, one token row per wave.
+ * Errors: CKDA_ERR_FLAGS for unknown flag bits; others as ckda_chunk_bwd. */
+int ckda_chunk_bwd_ex(const void* q, const void* k, const void* v, const void* alpha, const void* beta,
+                      const float* h0, const void* dout, const float* dhT, float* dq, float* dk, float* dv,
+                      float* dalpha, float* dbeta, float* dh0, int B, int H, int T, int dk_, int dv_, int dtype,
+                      int flags, void* workspace, size_t workspace_bytes, void* stream);
+
 /* One recurrent decode step for N sequences x H heads, state in place.
  *
  *   q, k, alpha : [N, H, dk]     dtype

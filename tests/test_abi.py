@@ -218,9 +218,12 @@ def call_bwd(**kw):
              do=BASE + 6 * MB, dhT=BASE + 7 * MB, dq=BASE + 8 * MB, dk=BASE + 9 * MB, dv=BASE + 10 * MB,
              da=BASE + 11 * MB, db=BASE + 12 * MB, dh0=BASE + 13 * MB, ws=BASE + 16 * MB)
     p.update({k: v for k, v in kw.items() if k in p})
-    rc = L.ckda_chunk_bwd(*(p[n] for n in ("q", "k", "v", "alpha", "beta", "h0", "do", "dhT", "dq", "dk", "dv", "da",
-                                           "db", "dh0")), B, H, T, dk, dv, kw.get("dtype", 1), p["ws"],
-                          kw.get("wsb", 64 * MB), None)
+    ptrs = (p[n] for n in ("q", "k", "v", "alpha", "beta", "h0", "do", "dhT", "dq", "dk", "dv", "da", "db", "dh0"))
+    if "flags" in kw:
+        rc = L.ckda_chunk_bwd_ex(*ptrs, B, H, T, dk, dv, kw.get("dtype", 1), kw["flags"], p["ws"],
+                                 kw.get("wsb", 64 * MB), None)
+    else:
+        rc = L.ckda_chunk_bwd(*ptrs, B, H, T, dk, dv, kw.get("dtype", 1), p["ws"], kw.get("wsb", 64 * MB), None)
     return rc, L.ckda_last_error().decode()
 
 
@@ -248,6 +251,41 @@ def test_bwd_rejects(kw, status):
     rc, msg = call_bwd(**kw)
     assert rc == status, (rc, msg)
     assert msg.startswith("ckda_chunk_bwd")
+
+
+def test_bwd_ex_workspace_size():
+    L = ck.lib()
+    B, H, T, dk, dv = 2, 3, 100, 64, 32
+    plain = L.ckda_chunk_bwd_workspace_size(B, H, T, dk, dv, 1)
+    assert L.ckda_chunk_bwd_ex_workspace_size(B, H, T, dk, dv, 1, 0) == plain
+    part = lambda n: (n + 63) // 64 * 64 * 4     # fp32 parts, 256-byte aligned
+    ntok = B * H * T
+    extra = 3 * part(ntok * dk) + 2 * part(ntok * dv) + part(ntok)
+    assert L.ckda_chunk_bwd_ex_workspace_size(B, H, T, dk, dv, 1, 7) == plain + extra
+    assert L.ckda_chunk_bwd_ex_workspace_size(B, H, T, dk, dv, 1, 8 | 1) == plain + extra + part(ntok * dk)
+    assert L.ckda_chunk_bwd_ex_workspace_size(B, H, T, dk, dv, 1, 16) == 0      # unknown flag bit
+    assert L.ckda_chunk_bwd_ex_workspace_size(B, H, T, 48, dv, 1, 7) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(flags=16), 7),                                   # unknown flag bit
+    (dict(flags=7, wsb=4096), 5),                          # too small for the prologue's fp32 copies
+    (dict(flags=7, q=None), 1),
+    (dict(flags=7, dq=BASE + 1 * MB), 4),                  # dq overlaps k
+    (dict(flags=1, da=BASE + 3 * MB + 512), 4),            # per-channel alpha (16 KB) overlaps dalpha ...
+])
+def test_bwd_ex_rejects(kw, status):
+    rc, msg = call_bwd(**kw)
+    assert rc == status, (rc, msg)
+    assert msg.startswith("ckda_chunk_bwd_ex")
+
+
+def test_bwd_ex_scalar_gate_sizes():
+    # with one gate per token alpha and dalpha are B*H*T long (256 bytes of
+    # bf16 here): a dalpha 128 bytes into alpha overlaps it
+    rc, msg = call_bwd(flags=9, da=BASE + 3 * MB + 128)
+    assert rc == 4, (rc, msg)
+    assert "dalpha overlaps alpha" in msg
 
 
 def test_prologue_flag_values_agree():
