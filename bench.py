@@ -314,12 +314,21 @@ def main():
         sg = {k: (None if v is None else v.to(dev)) for k, v in gen.make_scalar_gate_inputs(w).items()}
         scalar_ms = timed(lambda: ck.chunk_fwd(sg["q"], sg["k"], sg["v"], sg["alpha"], sg["beta"], sg["h0"],
                                                chunk=w.chunk, workspace=ws, o=o, hT=hT, fuse=ck.GATE_SCALAR), a.steps)
-        del sg
+        bws = torch.empty(ck.bwd_ex_workspace_size(w.B, w.H, w.T, w.dk, w.dv, ck.DTYPE_BF16, ck.GATE_SCALAR),
+                          dtype=torch.uint8, device=dev)
+        scalar_bwd_ms = timed(lambda: ck.chunk_bwd(sg["q"], sg["k"], sg["v"], sg["alpha"], sg["beta"], bdo, h0=sg["h0"],
+                                                   dhT=bdhT, workspace=bws, fuse=ck.GATE_SCALAR), max(3, a.steps // 3))
+        del sg, bws
         dp = {k: (None if v is None else v.to(dev)) for k, v in gen.make_dp2_inputs(w, gated=False).items()}
         dws = torch.empty(ck.workspace_size(w.B, w.H, 2 * w.T, w.dk, w.dv, w.chunk, ck.DTYPE_BF16), dtype=torch.uint8,
                           device=dev)
         dp2_ms = timed(lambda: ck.deltaproduct2_fwd(dp["q"], dp["k"], dp["v"], dp["beta"], h0=dp["h0"], chunk=w.chunk,
                                                     workspace=dws, o=o, hT=hT), a.steps)
+        del dws
+        dws = torch.empty(int(ck.lib().ckda_deltaproduct2_bwd_workspace_size(w.B, w.H, w.T, w.dk, w.dv, ck.DTYPE_BF16)),
+                          dtype=torch.uint8, device=dev)
+        dp2_bwd_ms = timed(lambda: ck.deltaproduct2_bwd(dp["q"], dp["k"], dp["v"], None, dp["beta"], bdo, h0=dp["h0"],
+                                                        dhT=bdhT, workspace=dws), max(3, a.steps // 3))
         del dp, dws
         dd = [{k: v.to(dev) for k, v in gen.dp2_decode_inputs(s, dec, gated=False).items() if v is not None}
               for s in range(4)]
@@ -345,8 +354,12 @@ def main():
             "comparators": {
                 "scalar_gate_forward_call_ms_mean": round(scalar_ms, 4),
                 "scalar_gate_tokens_per_s": round(tokens / (scalar_ms * 1e-3), 1),
+                "scalar_gate_backward_call_ms_mean": round(scalar_bwd_ms, 4),
+                "scalar_gate_forward_plus_backward_tokens_per_s": round(tokens / ((scalar_ms + scalar_bwd_ms) * 1e-3), 1),
                 "deltaproduct2_forward_call_ms_mean": round(dp2_ms, 4),
                 "deltaproduct2_tokens_per_s": round(tokens / (dp2_ms * 1e-3), 1),
+                "deltaproduct2_backward_call_ms_mean": round(dp2_bwd_ms, 4),
+                "deltaproduct2_forward_plus_backward_tokens_per_s": round(tokens / ((dp2_ms + dp2_bwd_ms) * 1e-3), 1),
                 "deltaproduct2_decode_ms_per_step": round(dp2_dec_ms, 4),
                 "deltaproduct2_decode_total_GB_s": round(
                     (state_bytes + dec.N * dec.H * (3 * dec.dk + 3 * dec.dv + 2) * 2) / (dp2_dec_ms * 1e-3) / 1e9, 1),

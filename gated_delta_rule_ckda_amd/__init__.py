@@ -30,6 +30,7 @@ EXPORTS = ("ckda_chunk_fwd_workspace_size", "ckda_chunk_fwd", "ckda_chunk_fwd_ti
            "ckda_chunk_fwd_gather", "ckda_decode_step", "ckda_decode_step_ex", "ckda_decode_step_gather",
            "ckda_deltaproduct2_fwd", "ckda_deltaproduct2_decode_step", "ckda_chunk_bwd",
            "ckda_chunk_bwd_workspace_size", "ckda_chunk_bwd_ex", "ckda_chunk_bwd_ex_workspace_size",
+           "ckda_deltaproduct2_bwd", "ckda_deltaproduct2_bwd_workspace_size",
            "ckda_status_string", "ckda_last_error", "ckda_abi_version")
 
 _lib = None
@@ -74,6 +75,10 @@ def lib() -> ctypes.CDLL:
         L.ckda_chunk_bwd_ex_workspace_size.restype = sz
         L.ckda_chunk_bwd_ex.argtypes = [vp] * 14 + [i] * 7 + [vp, sz, vp]
         L.ckda_chunk_bwd_ex.restype = i
+        L.ckda_deltaproduct2_bwd_workspace_size.argtypes = [i] * 6
+        L.ckda_deltaproduct2_bwd_workspace_size.restype = sz
+        L.ckda_deltaproduct2_bwd.argtypes = [vp] * 14 + [i] * 6 + [vp, sz, vp]
+        L.ckda_deltaproduct2_bwd.restype = i
         L.ckda_decode_step.argtypes = [vp] * 7 + [i] * 5 + [vp]
         L.ckda_decode_step.restype = i
         L.ckda_decode_step_ex.argtypes = [vp] * 7 + [i] * 6 + [vp]
@@ -304,4 +309,38 @@ def chunk_bwd(q, k, v, alpha, beta, do, h0=None, dhT=None, want_dh0=True, worksp
         _check(lib().ckda_chunk_bwd_ex(*args, int(fuse), *tail))
     else:
         _check(lib().ckda_chunk_bwd(*args, *tail))
+    return gq, gk, gv, galpha, gbeta, gh0
+
+
+def deltaproduct2_bwd(q, k, v, alpha, beta, do, h0=None, dhT=None, want_dh0=True, workspace=None, stream=None):
+    """Backward of deltaproduct2_fwd (ckda_deltaproduct2_bwd): q [B,H,T,dk],
+    k [B,H,T,2,dk], v [B,H,T,2,dv], beta [B,H,T,2], alpha [B,H,T] or None,
+    do [B,H,T,dv] (input dtype), dhT fp32 or None.  Returns fp32 (dq, dk, dv,
+    dalpha or None, dbeta, dh0 or None) in the inputs' shapes."""
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    ts = dict(q=q, k=k, v=v, beta=beta, do=do)
+    if alpha is not None:
+        ts["alpha"] = alpha
+    _require(ts, q.dtype)
+    code = _dtype_code(q)
+    for name, t in (("h0", h0), ("dhT", dhT)):
+        if t is not None:
+            _require({name: t}, torch.float32)
+    need = int(lib().ckda_deltaproduct2_bwd_workspace_size(B, H, T, dk, dv, code))
+    if need == 0:
+        raise CkdaError(3, f"unsupported sizes dk={dk} dv={dv}")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    f32 = dict(dtype=torch.float32, device=q.device)
+    gq = torch.empty((B, H, T, dk), **f32)
+    gk = torch.empty((B, H, T, 2, dk), **f32)
+    gv = torch.empty((B, H, T, 2, dv), **f32)
+    galpha = torch.empty((B, H, T), **f32) if alpha is not None else None
+    gbeta = torch.empty((B, H, T, 2), **f32)
+    gh0 = torch.empty((B, H, dk, dv), **f32) if want_dh0 else None
+    _check(lib().ckda_deltaproduct2_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(h0), _ptr(do),
+                                        _ptr(dhT), _ptr(gq), _ptr(gk), _ptr(gv), _ptr(galpha), _ptr(gbeta), _ptr(gh0),
+                                        B, H, T, dk, dv, code, _ptr(workspace),
+                                        workspace.numel() * workspace.element_size(), _stream(stream)))
     return gq, gk, gv, galpha, gbeta, gh0

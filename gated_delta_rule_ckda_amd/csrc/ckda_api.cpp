@@ -301,6 +301,63 @@ int ckda_chunk_bwd_ex(const void* q, const void* k, const void* v, const void* a
                         dh0, B, H, T, dk, dv, dtype, flags, workspace, workspace_bytes, stream);
 }
 
+size_t ckda_deltaproduct2_bwd_workspace_size(int B, int H, int T, int dk, int dv, int dtype) {
+  if (B < 0 || H < 0 || T < 0 || T > INT32_MAX / 2) return 0;
+  if (!supported_dim(dk) || !supported_dim(dv) || !supported_dtype(dtype)) return 0;
+  const size_t bytes = ckda::dp2_bwd_workspace_bytes(B, H, T, dk, dv, dtype);
+  return bytes == 0 ? 256 : bytes;
+}
+
+int ckda_deltaproduct2_bwd(const void* q, const void* k, const void* v, const void* alpha, const void* beta,
+                           const float* h0, const void* dout, const float* dhT, float* dq, float* dk_out,
+                           float* dv_out, float* dalpha, float* dbeta, float* dh0, int B, int H, int T, int dk,
+                           int dv, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "ckda_deltaproduct2_bwd";
+  if (B < 0 || H < 0 || T < 0 || T > INT32_MAX / 2)
+    return fail(CKDA_ERR_DIM, "%s: negative or too large size (B=%d H=%d T=%d)", fn, B, H, T);
+  if (!supported_dtype(dtype)) return fail(CKDA_ERR_UNSUPPORTED, "%s: dtype %d is not F32(0) or BF16(1)", fn, dtype);
+  if (!supported_dim(dk) || !supported_dim(dv))
+    return fail(CKDA_ERR_UNSUPPORTED, "%s: dk=%d dv=%d (supported: 16, 32, 64, 128)", fn, dk, dv);
+  const size_t BH = (size_t)B * H;
+  if (BH == 0) return ok();
+  const size_t es = dtype_bytes(dtype);
+  const size_t nq = BH * T * dk, nk = 2 * nq, nv = 2 * BH * T * dv, no = BH * T * dv, nt = BH * T, ns = BH * dk * dv;
+  if (T > 0 && (!q || !k || !v || !beta || !dout || !dq || !dk_out || !dv_out || !dbeta || (alpha && !dalpha)))
+    return fail(CKDA_ERR_NULL, "%s: inputs, do and every per-token gradient (dalpha with alpha) are required", fn);
+  const size_t nch = BH * ((2 * (size_t)T + 31) / 32);
+  if (nch > (size_t)INT32_MAX || BH * (size_t)(dv / 16) > (size_t)INT32_MAX || (2 * nt + 3) / 4 > INT32_MAX)
+    return fail(CKDA_ERR_DIM, "%s: sizes exceed the launch grid", fn);
+  const size_t need = ckda_deltaproduct2_bwd_workspace_size(B, H, T, dk, dv, dtype);
+  if (!workspace) return fail(CKDA_ERR_WORKSPACE, "%s: workspace is NULL", fn);
+  if (workspace_bytes < need)
+    return fail(CKDA_ERR_WORKSPACE, "%s: workspace of %zu bytes, need %zu", fn, workspace_bytes, need);
+  if (((uintptr_t)workspace & 255u) != 0) return fail(CKDA_ERR_WORKSPACE, "%s: workspace not 256-byte aligned", fn);
+  const void* ptrs[] = {q, k, v, alpha, beta, h0, dout, dhT, dq, dk_out, dv_out, dalpha, dbeta, dh0};
+  const char* names[] = {"q", "k", "v", "alpha", "beta", "h0", "do", "dhT", "dq", "dk", "dv", "dalpha", "dbeta", "dh0"};
+  for (int i = 0; i < 14; ++i)
+    if (ptrs[i] && misaligned(ptrs[i])) return fail(CKDA_ERR_DIM, "%s: %s is not 16-byte aligned", fn, names[i]);
+  const bool gated = alpha != nullptr;
+  const Range in[] = {range("q", q, T ? nq * es : 0),       range("k", k, T ? nk * es : 0),
+                      range("v", v, T ? nv * es : 0),       range("alpha", alpha, T && gated ? nt * es : 0),
+                      range("beta", beta, T ? 2 * nt * es : 0), range("h0", h0, h0 ? ns * 4 : 0),
+                      range("do", dout, T ? no * es : 0),   range("dhT", dhT, dhT ? ns * 4 : 0),
+                      range("workspace", workspace, need)};
+  const Range out[] = {range("dq", dq, T ? nq * 4 : 0),         range("dk", dk_out, T ? nk * 4 : 0),
+                       range("dv", dv_out, T ? nv * 4 : 0),     range("dalpha", dalpha, T && gated ? nt * 4 : 0),
+                       range("dbeta", dbeta, T ? 2 * nt * 4 : 0), range("dh0", dh0, dh0 ? ns * 4 : 0)};
+  for (const Range& o : out) {
+    for (const Range& r : in)
+      if (overlap(o, r)) return fail(CKDA_ERR_ALIAS, "%s: %s overlaps %s", fn, o.name, r.name);
+    for (const Range& o2 : out)
+      if (&o2 != &o && overlap(o, o2)) return fail(CKDA_ERR_ALIAS, "%s: %s overlaps %s", fn, o.name, o2.name);
+  }
+  ckda::BwdArgs a{q, k, v, alpha, beta, h0, dout, dhT, dq, dk_out, dv_out, gated ? dalpha : nullptr, dbeta, dh0,
+                  B, H, T, dk, dv, dtype, workspace, (hipStream_t)stream};
+  hipError_t e = ckda::launch_dp2_bwd(a);
+  if (e != hipSuccess) return fail(CKDA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  return ok();
+}
+
 int ckda_chunk_fwd_timed(const void* q, const void* k, const void* v, const void* alpha,
                          const void* beta, const float* h0, void* o, float* hT,
                          int B, int H, int T, int dk, int dv, int chunk, int dtype,

@@ -64,6 +64,10 @@ hipError_t launch_chunk_bwd(const BwdArgs& a);
 // CKDA_FUSE_* | CKDA_GATE_SCALAR, nonzero
 size_t prologue_bwd_workspace_floats(int B, int H, int T, int dk, int dv, int flags);
 hipError_t launch_prologue_bwd(const BwdArgs& a, int flags);
+// the DeltaProduct_2 backward (dp2_bwd.hip): k, v, beta, dk, dv, dbeta hold 2 T
+// sub-steps; alpha (or NULL: ungated) and dalpha are [B, H, T]
+size_t dp2_bwd_workspace_bytes(int B, int H, int T, int dk, int dv, int dtype);
+hipError_t launch_dp2_bwd(const BwdArgs& a);
 
 hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_chunk_fwd(const ChunkArgs& a);

@@ -286,6 +286,28 @@ int ckda_chunk_bwd_ex(const void* q, const void* k, const void* v, const void* a
                       float* dalpha, float* dbeta, float* dh0, int B, int H, int T, int dk_, int dv_, int dtype,
                       int flags, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Bytes of device workspace ckda_deltaproduct2_bwd needs, or 0 when the
+ * sizes are invalid or unsupported: the sub-step queries, gates and upstream
+ * gradients (2 T rows, dtype), two fp32 sub-step gradient arrays and the
+ * chunked backward's workspace for 2 T steps. */
+size_t ckda_deltaproduct2_bwd_workspace_size(int B, int H, int T, int dk, int dv, int dtype);
+
+/* Backward of ckda_deltaproduct2_fwd ("Complex KDA" paper, Fig. 5 and
+ * Sec. 6; gated form App. C): the gradients of a loss with respect to every
+ * input, given do = dL/do [B, H, T, dv] (dtype) and dhT = dL/dH_T (fp32 or
+ * NULL).  Layouts as the forward: k, dk [B, H, T, 2, dk]; v, dv
+ * [B, H, T, 2, dv]; beta, dbeta [B, H, T, 2]; q, dq [B, H, T, dk]; alpha and
+ * dalpha [B, H, T] (alpha NULL: ungated, dalpha ignored); gradients fp32.
+ * DeltaProduct_2 is the delta rule over the 2 T sub-steps (the gate on the
+ * first of each token's two, the query read after the second), so this runs
+ * the chunked backward of ckda_chunk_bwd on that sequence and folds each
+ * token's two sub-step query gradients and its gate sub-step's channel
+ * gradients.  Errors and rules as ckda_chunk_bwd. */
+int ckda_deltaproduct2_bwd(const void* q, const void* k, const void* v, const void* alpha, const void* beta,
+                           const float* h0, const void* dout, const float* dhT, float* dq, float* dk, float* dv,
+                           float* dalpha, float* dbeta, float* dh0, int B, int H, int T, int dk_, int dv_, int dtype,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
 /* One recurrent decode step for N sequences x H heads, state in place.
  *
  *   q, k, alpha : [N, H, dk]     dtype

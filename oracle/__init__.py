@@ -307,6 +307,35 @@ def deltaproduct2(q, k, v, alpha, beta, h0=None, nthreads=0):
     return o, hT
 
 
+def deltaproduct2_bwd(q, k, v, alpha, beta, do, dhT=None, h0=None, nthreads=0):
+    """Gradients of deltaproduct2() for L with dL/do = do [B,H,T,dv] and
+    dL/dH_T = dhT.  DeltaProduct_2 is two delta-rule updates per token (paper
+    Fig. 5 and Sec. 6; the gated form scales the state by the token's scalar
+    gate first, App. C): the delta rule over 2 T sub-steps, sub-step 2 t with
+    the gate alpha_t on every channel, sub-step 2 t + 1 ungated, and only the
+    odd sub-steps read out (with q_t).  So this is bwd() on that sequence:
+    queries repeated, gates [alpha_t, 1], upstream gradient [0, do_t]; then
+    dq_t sums its two sub-steps and dalpha_t the channels of its gate.
+    Returns fp64 (dq, dk [B,H,T,2,dk], dv [B,H,T,2,dv], dalpha [B,H,T] or
+    None, dbeta [B,H,T,2], dh0)."""
+    B, H, T, dk = np.shape(q)
+    dv = np.shape(v)[-1]
+    q2 = np.repeat(_widen(q), 2, axis=2)
+    a2 = np.ones((B, H, 2 * T, dk))
+    if alpha is not None:
+        a2[:, :, 0::2, :] = _widen(alpha)[..., None]
+    do2 = np.zeros((B, H, 2 * T, dv))
+    do2[:, :, 1::2, :] = np.asarray(do, np.float64)
+    k2 = _widen(k).reshape(B, H, 2 * T, dk)
+    v2 = _widen(v).reshape(B, H, 2 * T, dv)
+    b2 = _widen(beta).reshape(B, H, 2 * T)
+    dhT2 = None if dhT is None else np.asarray(dhT, np.float64)
+    dq2, dk2, dv2, da2, db2, dh0 = bwd(q2, k2, v2, a2, b2, do2, dhT=dhT2, h0=h0, nthreads=nthreads)
+    dq = dq2[:, :, 0::2, :] + dq2[:, :, 1::2, :]
+    da = None if alpha is None else da2[:, :, 0::2, :].sum(axis=-1)
+    return (dq, dk2.reshape(B, H, T, 2, dk), dv2.reshape(B, H, T, 2, dv), da, db2.reshape(B, H, T, 2), dh0)
+
+
 def deltaproduct2_decode(q, k, v, alpha, beta, S):
     """One DeltaProduct_2 token applied in place to the fp64 state S [N,H,dk,dv].
     q [N,H,dk]; k [N,H,2,dk]; v [N,H,2,dv]; beta [N,H,2]; alpha [N,H] or None."""
@@ -363,6 +392,9 @@ class Variant:
 
     def bwd(self, *a, **kw):
         return self._swap(bwd, *a, **kw)
+
+    def deltaproduct2_bwd(self, *a, **kw):
+        return self._swap(deltaproduct2_bwd, *a, **kw)
 
     def prologue_bwd(self, *a, **kw):
         return self._swap(prologue_bwd, *a, **kw)

@@ -288,6 +288,44 @@ def test_bwd_ex_scalar_gate_sizes():
     assert "dalpha overlaps alpha" in msg
 
 
+def test_dp2_bwd_workspace_size():
+    L = ck.lib()
+    B, H, T, dk, dv = 1, 2, 40, 64, 32
+    part = lambda n: (n + 255) // 256 * 256
+    nsub = 2 * B * H * T
+    want = 2 * part(nsub * dk * 2) + part(nsub * dv * 2) + 2 * part(nsub * dk * 4) + \
+        L.ckda_chunk_bwd_workspace_size(B, H, 2 * T, dk, dv, 1)
+    assert L.ckda_deltaproduct2_bwd_workspace_size(B, H, T, dk, dv, 1) == want
+    assert L.ckda_deltaproduct2_bwd_workspace_size(B, H, 1 << 30, dk, dv, 1) == 0
+    assert L.ckda_deltaproduct2_bwd_workspace_size(B, H, T, 24, dv, 1) == 0
+
+
+def _call_dp2_bwd(**kw):
+    L = ck.lib()
+    B, H, T, dk, dv = 1, 2, kw.get("T", 64), 64, 64
+    p = dict(q=BASE, k=BASE + 1 * MB, v=BASE + 2 * MB, alpha=BASE + 3 * MB, beta=BASE + 4 * MB, h0=BASE + 5 * MB,
+             do=BASE + 6 * MB, dhT=BASE + 7 * MB, dq=BASE + 8 * MB, dk=BASE + 9 * MB, dv=BASE + 10 * MB,
+             da=BASE + 11 * MB, db=BASE + 12 * MB, dh0=BASE + 13 * MB, ws=BASE + 16 * MB)
+    p.update({k: v for k, v in kw.items() if k in p})
+    rc = L.ckda_deltaproduct2_bwd(*(p[n] for n in ("q", "k", "v", "alpha", "beta", "h0", "do", "dhT", "dq", "dk",
+                                                   "dv", "da", "db", "dh0")), B, H, T, dk, dv, 1, p["ws"],
+                                  kw.get("wsb", 4096), None)
+    return rc, L.ckda_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(da=None), 1),                          # a gated call needs dalpha
+    (dict(T=-1), 2), (dict(T=1 << 30), 2),
+    (dict(wsb=4096), 5),                         # too small
+    (dict(dq=BASE + 1 * MB, wsb=64 * MB), 4),    # dq overlaps k (2 T sub-steps of keys)
+    (dict(dk=BASE + 9 * MB + 4, wsb=64 * MB), 2),
+])
+def test_dp2_bwd_rejects(kw, status):
+    rc, msg = _call_dp2_bwd(**kw)
+    assert rc == status, (rc, msg)
+    assert msg.startswith("ckda_deltaproduct2_bwd")
+
+
 def test_prologue_flag_values_agree():
     text = open(HEADER).read()
     defs = dict(re.findall(r"#define (CKDA_FUSE_\w+) (\d+)", text))

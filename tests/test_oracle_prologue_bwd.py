@@ -1,5 +1,6 @@
-"""Pins of the oracle's prologue backward (ckda_oracle_prologue_bwd) and of
-the fused backward built from it (oracle.bwd_fused), on the CPU.
+"""Pins of the oracle's prologue backward (ckda_oracle_prologue_bwd), of the
+fused backward built from it (oracle.bwd_fused) and of the DeltaProduct_2
+backward (oracle.deltaproduct2_bwd), on the CPU.
 
 The prologue of the "Complex KDA" discussion slides (frame "Backup: practical
 gates differ from exact theoretical endpoints") makes the gate from a logit,
@@ -142,3 +143,45 @@ def test_fused_backward_matches_finite_differences(oracle_lib, scalar, flags=7):
             x[ix] = old
             fd = (lp - lm) / (2 * h)
             assert abs(fd - g[ix]) <= 1e-6 * max(1.0, abs(fd)), (scalar, name, ix, fd, g[ix])
+
+
+@pytest.mark.parametrize("gated", [True, False])
+def test_deltaproduct2_backward_matches_finite_differences(oracle_lib, gated):
+    """deltaproduct2_bwd (the recurrence backward on the 2 T sub-steps) against
+    central differences of the separately written DeltaProduct_2 forward
+    (ckda_oracle_deltaproduct2: the gate, then two Householder writes per
+    token), for L = sum(o do) + sum(hT dhT), with respect to every input."""
+    o = oracle_lib
+    r = RNG(21 + gated)
+    B, H, T, dk, dv = 1, 2, 6, 3, 2
+    q = r.standard_normal((B, H, T, dk))
+    k = r.standard_normal((B, H, T, 2, dk))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = r.standard_normal((B, H, T, 2, dv))
+    a = r.uniform(-1, 1, (B, H, T)) if gated else None
+    b = r.uniform(0, 2, (B, H, T, 2))
+    h0 = 0.3 * r.standard_normal((B, H, dk, dv))
+    do = r.standard_normal((B, H, T, dv))
+    dhT = r.standard_normal((B, H, dk, dv))
+    grads = o.deltaproduct2_bwd(q, k, v, a, b, do, dhT=dhT, h0=h0)
+
+    def loss():
+        out, hT = o.deltaproduct2(q, k, v, a, b, h0=h0)
+        return float(np.sum(out * do) + np.sum(hT * dhT))
+
+    h = 1e-6
+    inputs = (("q", q, grads[0]), ("k", k, grads[1]), ("v", v, grads[2]), ("b", b, grads[4]), ("h0", h0, grads[5]))
+    if gated:
+        inputs += (("a", a, grads[3]),)
+    else:
+        assert grads[3] is None
+    for name, x, g in inputs:
+        for ix in np.ndindex(x.shape):
+            old = x[ix]
+            x[ix] = old + h
+            lp = loss()
+            x[ix] = old - h
+            lm = loss()
+            x[ix] = old
+            fd = (lp - lm) / (2 * h)
+            assert abs(fd - g[ix]) <= 1e-6 * max(1.0, abs(fd)), (gated, name, ix, fd, g[ix])
