@@ -33,7 +33,6 @@ struct ChunkGeom {
   static constexpr int KB = FragTraits<T>::KB;
   static constexpr int EPL = FragTraits<T>::EPL;
   static constexpr int E = sizeof(T);
-  static constexpr int HALVES = KB / 16;            // 16-row accumulator tiles per K block
   static constexpr int RT = C / 16;                 // row tiles of a chunk
   static constexpr int RH = DK / 16;                // row tiles of the state
   static constexpr int KBN = (DK + KB - 1) / KB;    // K blocks over channels
@@ -62,12 +61,6 @@ struct ChunkGeom {
   static constexpr size_t D_OFF = KR_OFF + NF_KR * FRAG;
   static constexpr size_t BYTES = NFR * FRAG;
 };
-
-// Byte offset of lane `lane`'s 16-byte slot in fragment (tile, kblock) of an
-// operand with `nkb` K blocks (unpadded layout, used in global memory).
-__host__ __device__ constexpr size_t frag_slot(int tile, int kblock, int nkb, int lane) {
-  return (((size_t)tile * nkb + kblock) * 64 + lane) * 16;
-}
 
 // Position of K index `kk` (0 <= kk < DK or C) in a padded fragment row:
 // byte offset of its element relative to the start of row 0 of the fragment
@@ -132,10 +125,6 @@ template <> struct Quad<bf16_t> {
     return __uint_as_float((j & 1) ? (x & 0xFFFF0000u) : (x << 16));
   }
   __device__ __forceinline__ void pin() { ckda::pin(w); }
-  // element j's bits to LDS unchanged
-  __device__ __forceinline__ void store_raw(unsigned char* p, int j) const {
-    *reinterpret_cast<uint16_t*>(p) = (uint16_t)((j & 1) ? (w[j >> 1] >> 16) : w[j >> 1]);
-  }
   static __device__ __forceinline__ Quad ones() { return Quad{u32x2{0x3F803F80u, 0x3F803F80u}}; }
   static __device__ __forceinline__ Quad zeros() { return Quad{u32x2{0u, 0u}}; }
   // store four values as consecutive elements
@@ -157,7 +146,6 @@ template <> struct Quad<float> {
   }
   __device__ __forceinline__ float get(int j) const { return w[j]; }
   __device__ __forceinline__ void pin() { ckda::pin(w); }
-  __device__ __forceinline__ void store_raw(unsigned char* p, int j) const { *reinterpret_cast<float*>(p) = w[j]; }
   static __device__ __forceinline__ Quad ones() { return Quad{f32x4{1.f, 1.f, 1.f, 1.f}}; }
   static __device__ __forceinline__ Quad zeros() { return Quad{f32x4{0.f, 0.f, 0.f, 0.f}}; }
   static __device__ __forceinline__ void put(unsigned char* p, const float* v) {

@@ -185,35 +185,13 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// Orders this wave's LDS writes before its later LDS reads (by any lane).
-__device__ __forceinline__ void lds_wave_fence() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
-
 // ---- register-level helpers
 // Ties a value to this point of the program: the compiler may not move its
 // uses above it, so a widening of prefetched bits cannot be hoisted into an
 // earlier phase (which would make that phase wait for the prefetch).
-// s_waitcnt operand that waits for every vector memory access of the wave
-// (vmcnt 0; expcnt and lgkmcnt at their maxima, i.e. not waited for)
-constexpr int kWaitVmcnt0 = 0x0F70;
-
 __device__ __forceinline__ void pin(uint32_t& x) { asm volatile("" : "+v"(x)); }
 __device__ __forceinline__ void pin(u32x2& x) { asm volatile("" : "+v"(x)); }
 __device__ __forceinline__ void pin(f32x4& x) { asm volatile("" : "+v"(x)); }
-
-__device__ __forceinline__ uint32_t elem_bits(bf16_t x) { return x.bits; }
-__device__ __forceinline__ uint32_t elem_bits(float x) { return __float_as_uint(x); }
-template <typename T> __device__ __forceinline__ float bits_to_f32(uint32_t u);
-template <> __device__ __forceinline__ float bits_to_f32<bf16_t>(uint32_t u) { return __uint_as_float(u << 16); }
-template <> __device__ __forceinline__ float bits_to_f32<float>(uint32_t u) { return __uint_as_float(u); }
-
-// DPP lane permutation inside groups of four lanes (quad_perm selector).
-enum : int {
-  kDppQuad1032 = 1 | (0 << 2) | (3 << 4) | (2 << 6),   // swap neighbouring lanes
-};
-template <int CTRL>
-__device__ __forceinline__ float dpp(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), CTRL, 0xF, 0xF, false));
-}
 
 // ---- range-checked buffer access
 // A raw buffer resource over `bytes` bytes from `base` (stride 0, so an access
@@ -221,28 +199,7 @@ __device__ __forceinline__ float dpp(float x) {
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
-template <typename T> __device__ __forceinline__ uint32_t load_elem_bits(__amdgpu_buffer_rsrc_t r, int byte_off);
-template <> __device__ __forceinline__ uint32_t load_elem_bits<float>(__amdgpu_buffer_rsrc_t r, int byte_off) {
-  return __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0);
-}
-template <> __device__ __forceinline__ uint32_t load_elem_bits<bf16_t>(__amdgpu_buffer_rsrc_t r, int byte_off) {
-  return __builtin_amdgcn_raw_buffer_load_b16(r, byte_off, 0, 0);
-}
-// one element to LDS in the storage type; four consecutive elements from LDS
-template <typename T> __device__ __forceinline__ void store_elem_lds(unsigned char* p, float x);
-template <> __device__ __forceinline__ void store_elem_lds<float>(unsigned char* p, float x) {
-  *reinterpret_cast<float*>(p) = x;
-}
-template <> __device__ __forceinline__ void store_elem_lds<bf16_t>(unsigned char* p, float x) {
-  *reinterpret_cast<uint16_t*>(p) = from_f32<bf16_t>(x).bits;
-}
-template <typename T> __device__ __forceinline__ float load_elem_lds(const unsigned char* p);
-template <> __device__ __forceinline__ float load_elem_lds<float>(const unsigned char* p) {
-  return *reinterpret_cast<const float*>(p);
-}
-template <> __device__ __forceinline__ float load_elem_lds<bf16_t>(const unsigned char* p) {
-  return __uint_as_float((uint32_t)*reinterpret_cast<const uint16_t*>(p) << 16);
-}
+// four consecutive elements from LDS, widened
 template <typename T> __device__ __forceinline__ f32x4 load_vals4(const unsigned char* p);
 template <> __device__ __forceinline__ f32x4 load_vals4<float>(const unsigned char* p) {
   return *reinterpret_cast<const f32x4*>(p);
@@ -251,13 +208,6 @@ template <> __device__ __forceinline__ f32x4 load_vals4<bf16_t>(const unsigned c
   const u32x2 w = *reinterpret_cast<const u32x2*>(p);
   return f32x4{__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xFFFF0000u), __uint_as_float(w[1] << 16),
                __uint_as_float(w[1] & 0xFFFF0000u)};
-}
-template <typename T> __device__ __forceinline__ void store_elem(__amdgpu_buffer_rsrc_t r, int byte_off, float x);
-template <> __device__ __forceinline__ void store_elem<float>(__amdgpu_buffer_rsrc_t r, int byte_off, float x) {
-  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, byte_off, 0, 0);
-}
-template <> __device__ __forceinline__ void store_elem<bf16_t>(__amdgpu_buffer_rsrc_t r, int byte_off, float x) {
-  __builtin_amdgcn_raw_buffer_store_b16(from_f32<bf16_t>(x).bits, r, byte_off, 0, 0);
 }
 
 // four consecutive elements to global memory in the storage type
