@@ -435,6 +435,13 @@ __global__ __launch_bounds__(kBThreads) void chunk_bwd_dstates_kernel(const T* d
 }
 
 // ============================================================ grad (per chunk)
+// Unrolling of the row loops of the grad kernel's recursive halving: full
+// with dk >= 64, so that the rows' LDS reads overlap (the LDS allows one
+// workgroup per CU there, one wave per SIMD, which hides no latency); rolled
+// below, which keeps the registers of two workgroups per CU.
+template <int DK>
+constexpr int kHalvUnroll = DK >= 64 ? 16 : 1;
+
 template <typename T, int DK>
 __global__ __launch_bounds__(kBThreads) void chunk_bwd_grad_kernel(
     const T* q, const T* k, const T* v, const T* alpha, const T* beta, const T* dout, const float* __restrict__ rec,
@@ -727,7 +734,8 @@ __global__ __launch_bounds__(kBThreads) void chunk_bwd_grad_kernel(
     // sg holds G(m, j) on L and G(t, m) on R.  With several blocks the two
     // threads of a channel take alternate blocks; with one block, one takes
     // the R rows and the other the L rows (they update disjoint positions).
-    // h is a compile-time constant per level so that the inner loops unroll.
+    // h is a compile-time constant per level so that the loops unroll, the
+    // row loops as kHalvUnroll says.
     const bool on = tid < 2 * DK;
     auto factors_R = [&](int lo, int h) __attribute__((always_inline)) {
       float f = 1.f;
@@ -752,7 +760,7 @@ __global__ __launch_bounds__(kBThreads) void chunk_bwd_grad_kernel(
 #pragma unroll
       for (int jj = 0; jj < h; ++jj) ky[jj] = K(lo + jj) * sg[(lo + jj) * DK];
       float bs = 0.f;
-#pragma unroll 1
+#pragma unroll kHalvUnroll<DK>
       for (int i = h - 1; i >= 0; --i) {
         const int t = m + 1 + i;
         float zm = 0.f, zs = 0.f;
@@ -781,7 +789,7 @@ __global__ __launch_bounds__(kBThreads) void chunk_bwd_grad_kernel(
         kr[i] = K(m + 1 + i) * gr;
       }
       float f = 0.f;
-#pragma unroll 1
+#pragma unroll kHalvUnroll<DK>
       for (int jj = 0; jj < h; ++jj) {
         const int j = lo + jj;
         float zl = 0.f;
