@@ -168,19 +168,33 @@ __global__ __launch_bounds__(kBThreads) void chunk_bwd_prep_kernel(const T* q, c
   __syncthreads();
 
   float* rc = rec + (size_t)chunk * R::FLOATS;
+  // this thread's channel (tid < DK): its gate, key and query columns in
+  // registers for the sequential products below (read from LDS once; the LDS
+  // allows one workgroup per CU, one wave per SIMD, which hides no latency)
+  float ca[C], ck[C], cq[C];
+  if (tid < DK) {
+#pragma unroll
+    for (int t = 0; t < C; ++t) {
+      ca[t] = sa[t * DKP + tid];
+      ck[t] = sk[t * DKP + tid];
+      cq[t] = sq[t * DKP + tid];
+    }
+  }
   if (tid < DK) {   // per channel: Gamma, KG, QG, Gamma_C; G(C-1, j), KR
     const int ch = tid;
     float gm = 1.f;
+#pragma unroll
     for (int t = 0; t < C; ++t) {
-      gm *= sa[t * DKP + ch];
-      rc[R::KG_OFF + t * DK + ch] = sk[t * DKP + ch] * gm;
-      rc[R::QG_OFF + t * DK + ch] = sq[t * DKP + ch] * gm;
+      gm *= ca[t];
+      rc[R::KG_OFF + t * DK + ch] = ck[t] * gm;
+      rc[R::QG_OFF + t * DK + ch] = cq[t] * gm;
     }
     rc[R::GC_OFF + ch] = gm;
     float ge = 1.f;
+#pragma unroll
     for (int t = C - 1; t >= 0; --t) {
-      rc[R::KR_OFF + t * DK + ch] = sk[t * DKP + ch] * ge;
-      ge *= sa[t * DKP + ch];
+      rc[R::KR_OFF + t * DK + ch] = ck[t] * ge;
+      ge *= ca[t];
     }
   }
   if (tid < C) {   // diagonal of M (G = 1)
@@ -188,27 +202,32 @@ __global__ __launch_bounds__(kBThreads) void chunk_bwd_prep_kernel(const T* q, c
     for (int ch = 0; ch < DK; ++ch) d += sq[tid * DKP + ch] * sk[tid * DKP + ch];
     sM[tid * CP + tid] = d;
   }
-  // S and M below the diagonal by recursive halving
-  for (int h = C / 2; h >= 1; h >>= 1) {
+  // S and M below the diagonal by recursive halving (h a compile-time
+  // constant per level, so that the channel's loops run on its registers)
+  auto level = [&](auto hh) __attribute__((always_inline)) {
+    constexpr int h = decltype(hh)::value;
     if (tid < DK) {
       const int ch = tid;
+#pragma unroll
       for (int lo = 0; lo < C; lo += 2 * h) {
         const int m = lo + h - 1;
         float f = 1.f;
+#pragma unroll
         for (int t = m + 1; t <= m + h; ++t) {   // x_t G(t, m)
-          f *= sa[t * DKP + ch];
-          sx[t * DKP + ch] = sk[t * DKP + ch] * f;
-          sxq[t * DKP + ch] = sq[t * DKP + ch] * f;
+          f *= ca[t];
+          sx[t * DKP + ch] = ck[t] * f;
+          sxq[t * DKP + ch] = cq[t] * f;
         }
         float e = 1.f;
+#pragma unroll
         for (int j = m; j >= lo; --j) {          // y_j G(m, j)
-          sy[j * DKP + ch] = sk[j * DKP + ch] * e;
-          e *= sa[j * DKP + ch];
+          sy[j * DKP + ch] = ck[j] * e;
+          e *= ca[j];
         }
       }
     }
     __syncthreads();
-    const int nent = C * h / 2;   // (C / 2h) blocks of h x h entries
+    constexpr int nent = C * h / 2;   // (C / 2h) blocks of h x h entries
     for (int e = tid; e < nent; e += kBThreads) {
       const int blk = e / (h * h), w = e % (h * h);
       const int lo = blk * 2 * h, t = lo + h + w / h, j = lo + w % h;
@@ -222,7 +241,13 @@ __global__ __launch_bounds__(kBThreads) void chunk_bwd_prep_kernel(const T* q, c
       sM[t * CP + j] = mm;
     }
     __syncthreads();
-  }
+  };
+  static_assert(C == 32, "halving levels below assume 32-position chunks");
+  level(std::integral_constant<int, 16>{});
+  level(std::integral_constant<int, 8>{});
+  level(std::integral_constant<int, 4>{});
+  level(std::integral_constant<int, 2>{});
+  level(std::integral_constant<int, 1>{});
   // T = (I + Diag(beta) S)^-1, unit lower triangular, one column per thread
   // held in registers: T[i][j] = -beta_i sum_{l < i} S[i][l] T[l][j] for i > j
   // (the rows of S are read by every lane at once)
