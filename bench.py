@@ -161,6 +161,25 @@ def main():
     torch.cuda.synchronize()
     gram_ms = [e[0].elapsed_time(e[1]) for e in kev]
     state_ms = [e[1].elapsed_time(e[2]) for e in kev]
+    # Timed region 3: the same call captured once in a HIP graph and replayed K
+    # times (events around each replay): the launch path without the host.
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(stream)
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(graph, stream=cap):
+            step()
+    stream.wait_stream(cap)
+    gev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(a.steps)]
+    graph.replay()
+    torch.cuda.synchronize()
+    for e0, e1 in gev:
+        e0.record(stream)
+        graph.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    graph_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in gev]))
+    del graph
     call_ms = float(np.mean(per_call_ms))
     call_ms_median = float(np.median(per_call_ms))
     kern_ms = {"chunk_gram_kernel": float(np.mean(gram_ms)), "chunk_state_kernel": float(np.mean(state_ms))}
@@ -434,6 +453,7 @@ def main():
                             "record_bytes": record_bytes,
                             "traffic": traffic_from_profile(k)} for k in kern_ms},
             "forward": {"call_ms_mean": round(call_ms, 4), "call_ms_median": round(call_ms_median, 4),
+                        "graph_replay_ms_mean": round(graph_ms, 4),
                         "algorithmic_bytes": nbytes, "algorithmic_GB_s": round(achieved_gbs, 1),
                         "frac_of_hbm_peak": round(achieved_gbs / HBM_PEAK_GBS, 4),
                         "mfma_algorithmic_tflops": round(achieved_tflops, 2),
