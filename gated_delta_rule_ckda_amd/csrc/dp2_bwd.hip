@@ -15,7 +15,7 @@
 //   3. dp2_fold_kernel sums each token's two sub-step query gradients and its
 //      gate sub-step's channel gate gradients.
 // One wave per sub-step row (expand) or token row (fold); lane l holds
-// channels l and l + 64 (d <= 128).
+// channels 4 l .. 4 l + 3 (d <= 128).
 #include "ckda_device.hpp"
 #include "ckda_internal.hpp"
 
@@ -23,10 +23,19 @@ namespace ckda {
 
 constexpr int kDp2Rows = 4;   // rows per workgroup, one wave each
 
-template <typename T>
-__device__ __forceinline__ T one_of() {
-  return from_f32<T>(1.f);
-}
+// four elements of the storage type, moved as one unit
+template <typename T> struct Four;
+template <> struct Four<float> {
+  typedef f32x4 raw;
+  static __device__ __forceinline__ raw splat(float x) { return raw{x, x, x, x}; }
+};
+template <> struct Four<bf16_t> {
+  typedef u32x2 raw;
+  static __device__ __forceinline__ raw splat(float x) {
+    const uint32_t h = (uint32_t)from_f32<bf16_t>(x).bits;
+    return raw{h | (h << 16), h | (h << 16)};
+  }
+};
 
 template <typename T>
 __global__ __launch_bounds__(64 * kDp2Rows) void dp2_expand_kernel(const T* q, const T* alpha, const T* dout, T* q2,
@@ -36,12 +45,15 @@ __global__ __launch_bounds__(64 * kDp2Rows) void dp2_expand_kernel(const T* q, c
   const int lane = threadIdx.x & 63;
   const long long t = s >> 1;   // its token
   const bool first = (s & 1) == 0;
-  const T g = (first && alpha) ? alpha[t] : one_of<T>();
-  for (int c = lane; c < dk; c += 64) {
-    q2[s * dk + c] = q[t * dk + c];
-    a2[s * dk + c] = g;
+  typedef typename Four<T>::raw R4;
+  const int c = 4 * lane;
+  if (c < dk) {
+    *reinterpret_cast<R4*>(q2 + s * dk + c) = *reinterpret_cast<const R4*>(q + t * dk + c);
+    *reinterpret_cast<R4*>(a2 + s * dk + c) = Four<T>::splat((first && alpha) ? to_f32(alpha[t]) : 1.f);
   }
-  for (int c = lane; c < dv; c += 64) do2[s * dv + c] = first ? from_f32<T>(0.f) : dout[t * dv + c];
+  if (c < dv)
+    *reinterpret_cast<R4*>(do2 + s * dv + c) =
+        first ? Four<T>::splat(0.f) : *reinterpret_cast<const R4*>(dout + t * dv + c);
 }
 
 __global__ __launch_bounds__(64 * kDp2Rows) void dp2_fold_kernel(const float* gq2, const float* ga2, float* dq,
@@ -50,9 +62,14 @@ __global__ __launch_bounds__(64 * kDp2Rows) void dp2_fold_kernel(const float* gq
   if (t >= ntok) return;   // the whole wave
   const int lane = threadIdx.x & 63;
   float gsum = 0.f;
-  for (int c = lane; c < dk; c += 64) {
-    dq[t * dk + c] = gq2[2 * t * dk + c] + gq2[(2 * t + 1) * dk + c];
-    if (dalpha) gsum += ga2[2 * t * dk + c];
+  const int c = 4 * lane;
+  if (c < dk) {
+    *reinterpret_cast<f32x4*>(dq + t * dk + c) = *reinterpret_cast<const f32x4*>(gq2 + 2 * t * dk + c) +
+                                                 *reinterpret_cast<const f32x4*>(gq2 + (2 * t + 1) * dk + c);
+    if (dalpha) {
+      const f32x4 g = *reinterpret_cast<const f32x4*>(ga2 + 2 * t * dk + c);
+      gsum = (g[0] + g[1]) + (g[2] + g[3]);
+    }
   }
   if (dalpha) {
     gsum = wave_sum(gsum);

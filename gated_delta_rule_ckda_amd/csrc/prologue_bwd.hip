@@ -18,7 +18,8 @@
 //        db = dbeta 2 sigma(b)(1 - sigma(b)),
 //        dx = n (dy - y (y . dy)),  y = x n   (normalised rows),
 //      and with one gate per token the per-channel gate gradients summed.
-// One wave per token row: lane l holds channels l and l + 64 (d <= 128).
+// One wave per token row: lane l holds channels 4 l .. 4 l + 3 (d <= 128,
+// 16-byte fp32 and 8-byte bf16 accesses).
 #include "ckda_device.hpp"
 #include "ckda_internal.hpp"
 
@@ -26,15 +27,26 @@ namespace ckda {
 
 constexpr int kRowsPerBlock = 4;   // one wave per row, four waves per workgroup
 
+// this lane's four channels of row `row` (rows of d elements), widened; zero
+// past the row's end
 template <typename T>
-__device__ __forceinline__ void row_pair(const T* x, long long row, int d, int lane, float& e0, float& e1) {
-  e0 = lane < d ? to_f32(x[row * d + lane]) : 0.f;
-  e1 = lane + 64 < d ? to_f32(x[row * d + lane + 64]) : 0.f;
+__device__ __forceinline__ f32x4 row_quad(const T* x, long long row, int d, int lane) {
+  if (4 * lane >= d) return zero4();
+  if constexpr (sizeof(T) == 2) {
+    const u32x2 w = *reinterpret_cast<const u32x2*>(x + row * d + 4 * lane);
+    return f32x4{__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xFFFF0000u), __uint_as_float(w[1] << 16),
+                 __uint_as_float(w[1] & 0xFFFF0000u)};
+  } else {
+    return *reinterpret_cast<const f32x4*>(x + row * d + 4 * lane);
+  }
 }
 
-__device__ __forceinline__ void put_pair(float* y, long long row, int d, int lane, float e0, float e1) {
-  if (lane < d) y[row * d + lane] = e0;
-  if (lane + 64 < d) y[row * d + lane + 64] = e1;
+__device__ __forceinline__ void put_quad(float* y, long long row, int d, int lane, f32x4 v) {
+  if (4 * lane < d) *reinterpret_cast<f32x4*>(y + row * d + 4 * lane) = v;
+}
+
+__device__ __forceinline__ float dot4(f32x4 a, f32x4 b) {
+  return __builtin_fmaf(a[0], b[0], __builtin_fmaf(a[1], b[1], __builtin_fmaf(a[2], b[2], a[3] * b[3])));
 }
 
 template <typename T>
@@ -45,14 +57,9 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void prologue_fwd_kernel(
   if (row >= ntok) return;   // the whole wave
   const int lane = threadIdx.x & 63;
   auto unit = [&](const T* x, float* y, bool on) __attribute__((always_inline)) {
-    float e0, e1;
-    row_pair(x, row, dk, lane, e0, e1);
-    if (on) {
-      const float n = __builtin_amdgcn_rsqf(wave_sum(__builtin_fmaf(e0, e0, e1 * e1)) + kUnitGuard);
-      e0 *= n;
-      e1 *= n;
-    }
-    put_pair(y, row, dk, lane, e0, e1);
+    f32x4 e = row_quad(x, row, dk, lane);
+    if (on) e *= __builtin_amdgcn_rsqf(wave_sum(dot4(e, e)) + kUnitGuard);
+    put_quad(y, row, dk, lane, e);
   };
   unit(k, kf, flags & kFuseNormK);
   unit(q, qf, flags & kFuseNormQ);
@@ -60,21 +67,21 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void prologue_fwd_kernel(
   if (flags & kScalarGate) {
     const float a = to_f32(alpha[row]);
     const float g = gates ? practical_gate(a) : a;
-    put_pair(af, row, dk, lane, g, g);
+    put_quad(af, row, dk, lane, f32x4{g, g, g, g});
   } else {
-    float a0, a1;
-    row_pair(alpha, row, dk, lane, a0, a1);
-    put_pair(af, row, dk, lane, gates ? practical_gate(a0) : a0, gates ? practical_gate(a1) : a1);
+    f32x4 a = row_quad(alpha, row, dk, lane);
+    if (gates) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) a[e] = practical_gate(a[e]);
+    }
+    put_quad(af, row, dk, lane, a);
   }
   if (lane == 0) {
     const float b = to_f32(beta[row]);
     bf[row] = gates ? practical_beta(b) : b;
   }
-  float v0, v1;
-  row_pair(v, row, dv, lane, v0, v1);
-  put_pair(vf, row, dv, lane, v0, v1);
-  row_pair(dout, row, dv, lane, v0, v1);
-  put_pair(of, row, dv, lane, v0, v1);
+  put_quad(vf, row, dv, lane, row_quad(v, row, dv, lane));
+  put_quad(of, row, dv, lane, row_quad(dout, row, dv, lane));
 }
 
 // dq, dk hold the gradients with respect to q^, k^ on entry and those with
@@ -89,28 +96,26 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void prologue_bwd_kernel(
   if (row >= ntok) return;   // the whole wave
   const int lane = threadIdx.x & 63;
   auto unit_bwd = [&](const T* x, float* g) __attribute__((always_inline)) {
-    float e0, e1, g0, g1;
-    row_pair(x, row, d, lane, e0, e1);
-    g0 = lane < d ? g[row * d + lane] : 0.f;
-    g1 = lane + 64 < d ? g[row * d + lane + 64] : 0.f;
-    const float n = __builtin_amdgcn_rsqf(wave_sum(__builtin_fmaf(e0, e0, e1 * e1)) + kUnitGuard);
-    const float y0 = e0 * n, y1 = e1 * n;
-    const float ydy = wave_sum(__builtin_fmaf(y0, g0, y1 * g1));
-    put_pair(g, row, d, lane, n * __builtin_fmaf(-y0, ydy, g0), n * __builtin_fmaf(-y1, ydy, g1));
+    const f32x4 e = row_quad(x, row, d, lane);
+    const f32x4 dy = row_quad(g, row, d, lane);
+    const float n = __builtin_amdgcn_rsqf(wave_sum(dot4(e, e)) + kUnitGuard);
+    const f32x4 y = e * n;
+    const float ydy = wave_sum(dot4(y, dy));
+    put_quad(g, row, d, lane, (dy - y * ydy) * n);
   };
   if (flags & kFuseNormK) unit_bwd(k, dk);
   if (flags & kFuseNormQ) unit_bwd(q, dq);
   const bool gates = flags & kFuseGates;
   if (flags & kScalarGate) {
-    float g0 = lane < d ? galpha_ch[row * d + lane] : 0.f;
-    float g1 = lane + 64 < d ? galpha_ch[row * d + lane + 64] : 0.f;
-    const float sum = wave_sum(g0 + g1);
+    const f32x4 gch = row_quad(galpha_ch, row, d, lane);
+    const float sum = wave_sum((gch[0] + gch[1]) + (gch[2] + gch[3]));
     if (lane == 0) dalpha[row] = gates ? sum * practical_gate_slope(to_f32(alpha[row])) : sum;
   } else if (gates) {
-    float a0, a1;
-    row_pair(alpha, row, d, lane, a0, a1);
-    if (lane < d) dalpha[row * d + lane] *= practical_gate_slope(a0);
-    if (lane + 64 < d) dalpha[row * d + lane + 64] *= practical_gate_slope(a1);
+    const f32x4 a = row_quad(alpha, row, d, lane);
+    f32x4 ga = row_quad(dalpha, row, d, lane);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ga[e] *= practical_gate_slope(a[e]);
+    put_quad(dalpha, row, d, lane, ga);
   }
   if (gates && lane == 0) dbeta[row] *= practical_beta_slope(to_f32(beta[row]));
 }
