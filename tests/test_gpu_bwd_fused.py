@@ -139,3 +139,15 @@ def test_full_size_sampled_heads():
     unit-norm keys; the oracle follows one of the 64 heads."""
     w = gen.variant(gen.WORKLOADS["ckda_bf16"], name="bwdx_full")
     run(w, 3, heads=[37])
+
+
+def test_deterministic():
+    """Two calls give the same bytes (no atomics, fixed reduction orders)."""
+    w = gen.Workload("bwdx", 1, 2, 77, 64, 64, 64, "bf16", "ckda_tanh", "normal", 7990)
+    d = to_dev(_inputs(w, 7))
+    do, gT = (x.cuda() for x in gen.make_output_grads(w, 5))
+    a = ck.chunk_bwd(d["q"], d["k"], d["v"], d["alpha"], d["beta"], do, h0=d["h0"], dhT=gT, fuse=7)
+    b = ck.chunk_bwd(d["q"], d["k"], d["v"], d["alpha"], d["beta"], do, h0=d["h0"], dhT=gT, fuse=7)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)

@@ -78,3 +78,14 @@ def test_full_size_sampled_heads():
     """The bench shape (B4 H16 T4096 d128 bf16, 8192 sub-steps per head),
     ungated as the pages' comparator; the oracle follows one head."""
     run(gen.variant(gen.WORKLOADS["ckda_bf16"], name="dp2b_full"), False, heads=[22])
+
+
+def test_deterministic():
+    w = gen.Workload("dp2b", 1, 2, 60, 64, 64, 64, "bf16", "ckda_tanh", "normal", 8500)
+    d = to_dev(gen.make_dp2_inputs(w, gated=True))
+    do, gT = (x.cuda() for x in gen.make_output_grads(w, 5))
+    a = ck.deltaproduct2_bwd(d["q"], d["k"], d["v"], d["alpha"], d["beta"], do, h0=d["h0"], dhT=gT)
+    b = ck.deltaproduct2_bwd(d["q"], d["k"], d["v"], d["alpha"], d["beta"], do, h0=d["h0"], dhT=gT)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
