@@ -41,7 +41,8 @@ constexpr int kBC = 32;          // positions per backward chunk
 constexpr int kBThreads = 256;
 constexpr int kBDS = 16;         // value columns per slice
 
-// per-chunk fp32 record of the prep kernel (offsets in floats)
+// per-chunk fp32 record of the prep kernel (offsets in floats): M, TB, T, S
+// (C x C), KG (C x DK), KR^T (DK x C), QG (C x DK), Gamma_C (DK), row-major
 template <int DK>
 struct BwdRec {
   static constexpr int C = kBC;
@@ -190,12 +191,15 @@ __global__ __launch_bounds__(kBThreads) void chunk_bwd_prep_kernel(const T* q, c
       rc[R::QG_OFF + t * DK + ch] = cq[t] * gm;
     }
     rc[R::GC_OFF + ch] = gm;
-    float ge = 1.f;
+    float ge = 1.f, kr[C];
 #pragma unroll
     for (int t = C - 1; t >= 0; --t) {
-      rc[R::KR_OFF + t * DK + ch] = ck[t] * ge;
+      kr[t] = ck[t] * ge;
       ge *= ca[t];
     }
+#pragma unroll
+    for (int t = 0; t < C; t += 4)   // KR^T: this channel's row
+      *reinterpret_cast<f32x4*>(rc + R::KR_OFF + ch * C + t) = f32x4{kr[t], kr[t + 1], kr[t + 2], kr[t + 3]};
   }
   if (tid < C) {   // diagonal of M (G = 1)
     float d = 0.f;
@@ -275,88 +279,143 @@ __global__ __launch_bounds__(kBThreads) void chunk_bwd_prep_kernel(const T* q, c
 }
 
 // ============================================================ states (forward, sequential)
-// The next chunk's operands are fetched into registers while the current one
-// is computed, and placed into LDS at the top of the next iteration.
+// float offset, within a chunk's dk x dv state block, of element (i, j) as the
+// states kernel writes it (value slices of 16 columns, each in accumulator
+// order)
+template <int DK>
+__device__ __forceinline__ int hc_slot(int i, int j) {
+  return (j / 16) * (DK * 16) + ((i / 16) * 64 + ((i % 16) / 4) * 16 + j % 16) * 4 + i % 4;
+}
+
+// One wave per head and 16-column value slice, the state slice (dk x 16) in
+// its accumulator registers, as the forward's state pass keeps it: per chunk
+//   X = V - KG H,  U = TB X,  H <- Gamma_C . H + KR^T U
+// on fp32 matrix cores, the accumulator tiles of one product being (with the
+// K order 4 g + e of an fp32 fragment) the B operand of the next.  The A
+// operands come straight from the chunk record (the slices of a head share it
+// through their XCD's L2), every fragment one 16-byte load of a KG, TB or
+// KR^T row.  Each operand is loaded for the next chunk as soon as the current
+// chunk has used it (KR^T and Gamma_C, used last, at the top of their own
+// chunk), so the loads run under the matrix-core work without a second
+// register set; the next chunk's loads are unconditional (the last chunk
+// reloads itself), which keeps them in one basic block.  About 60 memory
+// instructions per chunk, within what the in-order vector memory counter
+// can track, so no wait covers more than the loads it needs.  No LDS and no
+// barrier.
+//
+// The chunk-start states go out in accumulator order: per chunk and slice a
+// dk x 16 block, the f32x4 of lane l of row tile rh at float (64 rh + l) 4,
+// holding rows 16 rh + 4 (l / 16) + i, column l % 16 (hc_slot).
 template <typename T, int DK>
-__global__ __launch_bounds__(kBThreads) void chunk_bwd_states_kernel(const T* v, const float* __restrict__ h0,
-                                                                     const float* __restrict__ rec,
-                                                                     float* __restrict__ hc, int T_len, int nchunks,
-                                                                     int dv, int xcd_map) {
-  constexpr int C = kBC, DS = kBDS, DKP = DK + 1, CP = C + 1, DSP = DS + 1;
-  constexpr int NK = (C * DK + kBThreads - 1) / kBThreads, NT = (C * C + kBThreads - 1) / kBThreads;
-  constexpr int NV = (C * DS + kBThreads - 1) / kBThreads;
+__global__ __launch_bounds__(64) void chunk_bwd_states_kernel(const T* v, const float* __restrict__ h0,
+                                                              const float* __restrict__ rec, float* __restrict__ hc,
+                                                              int T_len, int nchunks, int dv, int xcd_map) {
+  constexpr int C = kBC, RH = DK / 16, RT = C / 16;
   using R = BwdRec<DK>;
-  __shared__ float sH[DK * DSP], sKG[C * DKP], sKR[C * DKP], sTB[C * CP], sX[C * DSP], sU[C * DSP], sGC[DK];
-  const int tid = threadIdx.x;
-  const int nsl = dv / DS;
+  const int lane = threadIdx.x, g = lane >> 4, r = lane & 15;
+  const int nsl = dv / 16;
   long long bh;
   int slice;
   head_slice(blockIdx.x, nsl, xcd_map, bh, slice);
-  const int col0 = slice * DS;
-  float rKG[NK], rKR[NK], rTB[NT], rV[NV], rGC = 0.f;
-  auto fetch = [&](int c) __attribute__((always_inline)) {
-    const float* rc = rec + (size_t)(bh * nchunks + c) * R::FLOATS;
+  const int col = slice * 16 + r;   // this lane's value column
+  f32x4 hacc[RH];   // H rows 16 rh + 4 g + i, column col
+#pragma unroll
+  for (int rh = 0; rh < RH; ++rh)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      hacc[rh][i] = h0 ? h0[(bh * DK + 16 * rh + 4 * g + i) * (long long)dv + col] : 0.f;
+  f32x4 kg[RT][RH];   // KG rows 16 rt + r, channels 16 kb + 4 g .. + 3
+  f32x4 kr[RH][RT];   // KR^T rows 16 rh + r (channels), positions 16 kb + 4 g .. + 3
+  f32x4 tb[RT][RT];   // TB rows 16 rt + r, positions 16 kb + 4 g .. + 3 (kb <= rt)
+  f32x4 gc[RH];       // Gamma_C at channels 16 rh + 4 g .. + 3
+  T vv[RT][4];        // V rows 16 rt + 4 g .. + 3, column col, as stored (rows past the end: any row)
+  auto recp = [&](int c) { return rec + (size_t)(bh * nchunks + c) * R::FLOATS; };
+  auto load_kg = [&](int c) __attribute__((always_inline)) {
+    const float* rc = recp(c);
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int kb = 0; kb < RH; ++kb)
+        kg[rt][kb] = *reinterpret_cast<const f32x4*>(rc + R::KG_OFF + (16 * rt + r) * DK + 16 * kb + 4 * g);
+  };
+  auto load_tb_v = [&](int c) __attribute__((always_inline)) {
+    const float* rc = recp(c);
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int kb = 0; kb <= rt; ++kb)
+        tb[rt][kb] = *reinterpret_cast<const f32x4*>(rc + R::TB_OFF + (16 * rt + r) * C + 16 * kb + 4 * g);
+    // unconditional loads (a row past the end reads the chunk's first row and
+    // is masked where it is used), kept as stored so that nothing waits for
+    // them before the next chunk
     const int t0 = c * C, cv = min(C, T_len - t0);
 #pragma unroll
-    for (int i = 0; i < NK; ++i) {
-      const int e = tid + i * kBThreads;
-      const int ee = e < C * DK ? e : 0;   // (always in range for these shapes; clamped, not branched)
-      rKG[i] = rc[R::KG_OFF + ee];
-      rKR[i] = rc[R::KR_OFF + ee];
-    }
+    for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-    for (int i = 0; i < NT; ++i) {
-      const int e = tid + i * kBThreads;
-      rTB[i] = rc[R::TB_OFF + (e < C * C ? e : 0)];
-    }
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int e = tid + i * kBThreads, t = e / DS, j = e % DS;
-      const bool ok = e < C * DS && t < cv;
-      rV[i] = ld_or(v, ok ? (size_t)(bh * T_len + t0 + t) * dv + col0 + j : 0, ok, 0.f);
-    }
-    if (tid < DK) rGC = rc[R::GC_OFF + tid];
+      for (int i = 0; i < 4; ++i) {
+        const int t = 16 * rt + 4 * g + i;
+        vv[rt][i] = v[(size_t)(bh * T_len + t0 + (t < cv ? t : 0)) * dv + col];
+      }
   };
-  for (int e = tid; e < DK * DS; e += kBThreads) {
-    const int i = e / DS, j = e % DS;
-    sH[i * DSP + j] = h0 ? h0[(bh * DK + i) * (long long)dv + col0 + j] : 0.f;
+  auto load_kr_gc = [&](int c) __attribute__((always_inline)) {
+    const float* rc = recp(c);
+#pragma unroll
+    for (int rh = 0; rh < RH; ++rh)
+#pragma unroll
+      for (int kb = 0; kb < RT; ++kb)
+        kr[rh][kb] = *reinterpret_cast<const f32x4*>(rc + R::KR_OFF + (16 * rh + r) * C + 16 * kb + 4 * g);
+#pragma unroll
+    for (int rh = 0; rh < RH; ++rh) gc[rh] = *reinterpret_cast<const f32x4*>(rc + R::GC_OFF + 16 * rh + 4 * g);
+  };
+  if (nchunks > 0) {
+    load_kg(0);
+    load_tb_v(0);
   }
-  if (nchunks > 0) fetch(0);
   for (int c = 0; c < nchunks; ++c) {
     const long long chunk = bh * nchunks + c;
+    const int cn = min(c + 1, nchunks - 1);
+    // the chunk-start state
 #pragma unroll
-    for (int i = 0; i < NK; ++i) {
-      const int e = tid + i * kBThreads;
-      if (e < C * DK) {
-        sKG[(e / DK) * DKP + e % DK] = rKG[i];
-        sKR[(e / DK) * DKP + e % DK] = rKR[i];
-      }
-    }
+    for (int rh = 0; rh < RH; ++rh)
+      *reinterpret_cast<f32x4*>(hc + (size_t)chunk * DK * dv + hc_slot<DK>(16 * rh + 4 * g, col)) = hacc[rh];
+    load_kr_gc(c);
+    // (scheduling barriers keep each group of loads where it is written: the
+    // scheduler would otherwise sink them toward their uses)
+    __builtin_amdgcn_sched_barrier(0);
+    // X = V - KG H
+    f32x4 xacc[RT];
 #pragma unroll
-    for (int i = 0; i < NT; ++i) {
-      const int e = tid + i * kBThreads;
-      if (e < C * C) sTB[(e / C) * CP + e % C] = rTB[i];
-    }
+    for (int rt = 0; rt < RT; ++rt) {
+      f32x4 p = zero4();
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int e = tid + i * kBThreads;
-      if (e < C * DS) sX[(e / DS) * DSP + e % DS] = rV[i];   // X starts as V
+      for (int kb = 0; kb < RH; ++kb) p = mma<float>(p, Frag{__builtin_bit_cast(u32x4, kg[rt][kb])}, frag_from_acc_f32(hacc[kb]));
+      const int cv = min(C, T_len - c * C);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xacc[rt][i] = (16 * rt + 4 * g + i < cv ? to_f32(vv[rt][i]) : 0.f) - p[i];
     }
-    if (tid < DK) sGC[tid] = rGC;
-    __syncthreads();
-    if (c + 1 < nchunks) fetch(c + 1);
-    for (int e = tid; e < DK * DS; e += kBThreads) {
-      const int i = e / DS, j = e % DS;
-      hc[(size_t)chunk * DK * dv + (size_t)i * dv + col0 + j] = sH[i * DSP + j];
+    __builtin_amdgcn_sched_barrier(0);
+    load_kg(cn);
+    __builtin_amdgcn_sched_barrier(0);
+    // U = TB X
+    f32x4 uacc[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      uacc[rt] = zero4();
+#pragma unroll
+      for (int kb = 0; kb <= rt; ++kb)
+        uacc[rt] = mma<float>(uacc[rt], Frag{__builtin_bit_cast(u32x4, tb[rt][kb])}, frag_from_acc_f32(xacc[kb]));
     }
-    gemm_lds<true, DK>(sX, DSP, sKG, DKP, 1, sH, DSP, 1, C, DS, -1.f);      // X = V - KG H
-    __syncthreads();
-    gemm_lds<false, C>(sU, DSP, sTB, CP, 1, sX, DSP, 1, C, DS, 1.f);        // U = TB X
-    __syncthreads();
-    for (int e = tid; e < DK * DS; e += kBThreads) sH[(e / DS) * DSP + e % DS] *= sGC[e / DS];
-    __syncthreads();
-    gemm_lds<true, C>(sH, DSP, sKR, 1, DKP, sU, DSP, 1, DK, DS, 1.f);       // H = Gamma_C . H + KR^T U
-    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    load_tb_v(cn);
+    __builtin_amdgcn_sched_barrier(0);
+    // H <- Gamma_C . H + KR^T U
+#pragma unroll
+    for (int rh = 0; rh < RH; ++rh) {
+      f32x4 hh = gc[rh] * hacc[rh];
+#pragma unroll
+      for (int kb = 0; kb < RT; ++kb) hh = mma<float>(hh, Frag{__builtin_bit_cast(u32x4, kr[rh][kb])}, frag_from_acc_f32(uacc[kb]));
+      hacc[rh] = hh;
+    }
   }
 }
 
@@ -417,7 +476,7 @@ __global__ __launch_bounds__(kBThreads) void chunk_bwd_dstates_kernel(const T* d
       if (e < C * DK) {
         const int o = (e / DK) * DKP + e % DK;
         sKG[o] = rKG[i];
-        sKR[o] = rKR[i];
+        sKR[(e % C) * DKP + e / C] = rKR[i];   // the record holds KR^T
         sQG[o] = rQG[i];
       }
     }
@@ -535,7 +594,7 @@ __global__ __launch_bounds__(kBThreads) void chunk_bwd_grad_kernel(
         sk[o] = r1[i];
         sa[o] = r2[i];
         sKG[o] = r3[i];
-        sKR[o] = r4[i];
+        sKR[(e % C) * DKP + e / C] = r4[i];   // the record holds KR^T
       }
     }
 #pragma unroll
@@ -572,7 +631,7 @@ __global__ __launch_bounds__(kBThreads) void chunk_bwd_grad_kernel(
 #pragma unroll
     for (int i = 0; i < NH; ++i) {
       const int e = tid + i * kBThreads, ee = e < DK * DS ? e : 0, ii = ee / DS, j = ee % DS;
-      rH[i] = hcc[(size_t)ii * dv + col0 + j];
+      rH[i] = hcc[(size_t)col0 * DK + ee];   // the slice's block, in slot order (hc_slot)
       rdH[i] = dhc[(size_t)ii * dv + col0 + j];
     }
 #pragma unroll
@@ -591,7 +650,8 @@ __global__ __launch_bounds__(kBThreads) void chunk_bwd_grad_kernel(
     for (int i = 0; i < NH; ++i) {
       const int e = tid + i * kBThreads;
       if (e < DK * DS) {
-        sH[(e / DS) * DSP + e % DS] = rH[i];
+        // slot e holds row 16 (e / 256) + 4 ((e / 64) % 4) + e % 4, column (e / 4) % 16
+        sH[(16 * (e / 256) + 4 * ((e / 64) % 4) + e % 4) * DSP + (e / 4) % 16] = rH[i];
         sdH[(e / DS) * DSP + e % DS] = rdH[i];
       }
     }
@@ -886,7 +946,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a) {
   if (total > 0) {
     hipLaunchKernelGGL((chunk_bwd_prep_kernel<T, DK>), dim3((unsigned)total), dim3(kBThreads), 0, a.stream,
                        (const T*)a.q, (const T*)a.k, (const T*)a.alpha, (const T*)a.beta, rec, a.T, nch);
-    hipLaunchKernelGGL((chunk_bwd_states_kernel<T, DK>), dim3((unsigned)(BH * nsl)), dim3(kBThreads), 0, a.stream,
+    hipLaunchKernelGGL((chunk_bwd_states_kernel<T, DK>), dim3((unsigned)(BH * nsl)), dim3(64), 0, a.stream,
                        (const T*)a.v, a.h0, rec, hc, a.T, nch, a.dv, xcd_map);
   }
   hipLaunchKernelGGL((chunk_bwd_dstates_kernel<T, DK>), dim3((unsigned)(BH * nsl)), dim3(kBThreads), 0, a.stream,
