@@ -17,7 +17,8 @@
 //
 // Four kernels, fp32 throughout:
 //   prep    (one workgroup per chunk)   S, M by recursive halving, T by forward
-//           substitution, TB, KG, KR, QG, Gamma_C -> a per-chunk fp32 record;
+//           substitution, TB, KG, KR, QG, Gamma_C -> a per-chunk fp32 record
+//           (with the transposes the sequential kernels contract along);
 //   states  (sequential, per head and 16-column value slice) chunk-start states;
 //   dstates (sequential, reverse)       the state gradient entering each chunk
 //           from its end, and dh0;
@@ -41,14 +42,18 @@ constexpr int kBC = 32;          // positions per backward chunk
 constexpr int kBThreads = 256;
 constexpr int kBDS = 16;         // value columns per slice
 
-// per-chunk fp32 record of the prep kernel (offsets in floats): M, TB, T, S
-// (C x C), KG (C x DK), KR^T (DK x C), QG (C x DK), Gamma_C (DK), row-major
+// per-chunk fp32 record of the prep kernel (offsets in floats), row-major:
+// M^T, TB, TB^T, T, S (C x C); KG, KG^T, KR, KR^T, QG^T (C x DK or DK x C);
+// Gamma_C (DK).  The sequential kernels read matrix-core A fragments straight
+// from it, 16 bytes of a row along the contraction each: the states kernel
+// KG, TB, KR^T; the dstates kernel M^T, KR, TB^T, QG^T, KG^T.
 template <int DK>
 struct BwdRec {
   static constexpr int C = kBC;
-  static constexpr int M_OFF = 0, TB_OFF = C * C, T_OFF = 2 * C * C, S_OFF = 3 * C * C;
-  static constexpr int KG_OFF = 4 * C * C, KR_OFF = KG_OFF + C * DK, QG_OFF = KR_OFF + C * DK;
-  static constexpr int GC_OFF = QG_OFF + C * DK;
+  static constexpr int MT_OFF = 0, TB_OFF = C * C, TBT_OFF = 2 * C * C, T_OFF = 3 * C * C, S_OFF = 4 * C * C;
+  static constexpr int KG_OFF = 5 * C * C, KGT_OFF = KG_OFF + C * DK, KR_OFF = KGT_OFF + C * DK;
+  static constexpr int KRT_OFF = KR_OFF + C * DK, QGT_OFF = KRT_OFF + C * DK;
+  static constexpr int GC_OFF = QGT_OFF + C * DK;
   static constexpr int FLOATS = (GC_OFF + DK + 63) / 64 * 64;
 };
 
@@ -183,23 +188,28 @@ __global__ __launch_bounds__(kBThreads) void chunk_bwd_prep_kernel(const T* q, c
   }
   if (tid < DK) {   // per channel: Gamma, KG, QG, Gamma_C; G(C-1, j), KR
     const int ch = tid;
-    float gm = 1.f;
+    float gm = 1.f, kg[4], qg[4];
 #pragma unroll
     for (int t = 0; t < C; ++t) {
       gm *= ca[t];
-      rc[R::KG_OFF + t * DK + ch] = ck[t] * gm;
-      rc[R::QG_OFF + t * DK + ch] = cq[t] * gm;
+      kg[t % 4] = ck[t] * gm;
+      qg[t % 4] = cq[t] * gm;
+      rc[R::KG_OFF + t * DK + ch] = kg[t % 4];
+      if (t % 4 == 3) {   // KG^T, QG^T: this channel's rows, 16 bytes at a time
+        *reinterpret_cast<f32x4*>(rc + R::KGT_OFF + ch * C + t - 3) = f32x4{kg[0], kg[1], kg[2], kg[3]};
+        *reinterpret_cast<f32x4*>(rc + R::QGT_OFF + ch * C + t - 3) = f32x4{qg[0], qg[1], qg[2], qg[3]};
+      }
     }
     rc[R::GC_OFF + ch] = gm;
-    float ge = 1.f, kr[C];
+    float ge = 1.f, kr[4];
 #pragma unroll
     for (int t = C - 1; t >= 0; --t) {
-      kr[t] = ck[t] * ge;
+      kr[t % 4] = ck[t] * ge;
       ge *= ca[t];
+      rc[R::KR_OFF + t * DK + ch] = kr[t % 4];
+      if (t % 4 == 0)   // KR^T: this channel's row
+        *reinterpret_cast<f32x4*>(rc + R::KRT_OFF + ch * C + t) = f32x4{kr[0], kr[1], kr[2], kr[3]};
     }
-#pragma unroll
-    for (int t = 0; t < C; t += 4)   // KR^T: this channel's row
-      *reinterpret_cast<f32x4*>(rc + R::KR_OFF + ch * C + t) = f32x4{kr[t], kr[t + 1], kr[t + 2], kr[t + 3]};
   }
   if (tid < C) {   // diagonal of M (G = 1)
     float d = 0.f;
@@ -271,9 +281,10 @@ __global__ __launch_bounds__(kBThreads) void chunk_bwd_prep_kernel(const T* q, c
   __syncthreads();
   for (int e = tid; e < C * C; e += kBThreads) {
     const int i = e / C, j = e % C;
-    rc[R::M_OFF + e] = sM[i * CP + j];
+    rc[R::MT_OFF + e] = sM[j * CP + i];
     rc[R::T_OFF + e] = sT[i * CP + j];
     rc[R::TB_OFF + e] = sT[i * CP + j] * sb[j];
+    rc[R::TBT_OFF + e] = sT[j * CP + i] * sb[i];
     rc[R::S_OFF + e] = sS[i * CP + j];
   }
 }
@@ -363,7 +374,7 @@ __global__ __launch_bounds__(64) void chunk_bwd_states_kernel(const T* v, const 
     for (int rh = 0; rh < RH; ++rh)
 #pragma unroll
       for (int kb = 0; kb < RT; ++kb)
-        kr[rh][kb] = *reinterpret_cast<const f32x4*>(rc + R::KR_OFF + (16 * rh + r) * C + 16 * kb + 4 * g);
+        kr[rh][kb] = *reinterpret_cast<const f32x4*>(rc + R::KRT_OFF + (16 * rh + r) * C + 16 * kb + 4 * g);
 #pragma unroll
     for (int rh = 0; rh < RH; ++rh) gc[rh] = *reinterpret_cast<const f32x4*>(rc + R::GC_OFF + 16 * rh + 4 * g);
   };
@@ -420,102 +431,185 @@ __global__ __launch_bounds__(64) void chunk_bwd_states_kernel(const T* v, const 
 }
 
 // ============================================================ dstates (reverse, sequential)
+// One workgroup per head and 16-column value slice, its waves splitting the
+// key channels: each holds dk / waves rows of the state gradient (x 16
+// columns) in accumulator registers.  Per chunk, from the last:
+//   dU = M^T dO + KR dH',  dX = TB^T dU,  dH = Gamma_C . dH' + QG^T dO - KG^T dX
+// on fp32 matrix cores, accumulator tiles feeding the next product as B
+// operands.  Each wave's KR dH' covers its own channels; the waves' partial
+// dU are summed through LDS (one barrier per chunk, the exchange buffer
+// alternating between chunks; a + b = b + a, so both waves hold the same dU).
+// Every A fragment is one 16-byte load of a record row; dO's fragments are
+// four loads of the input each, kept as stored until used.  Operands are
+// reloaded for the next chunk as soon as the current one has used them (KR,
+// M^T and dO, needed first, into the other of two sets).  The state gradient entering
+// each chunk from its end (dH') is stored in accumulator order (hc_slot),
+// dh0 at the end.
+template <int DK>
+constexpr int kDsWaves = DK >= 32 ? 2 : 1;
+
 template <typename T, int DK>
-__global__ __launch_bounds__(kBThreads) void chunk_bwd_dstates_kernel(const T* dout, const float* __restrict__ dhT,
-                                                                      const float* __restrict__ rec,
-                                                                      float* __restrict__ dhn, float* __restrict__ dh0,
-                                                                      int T_len, int nchunks, int dv, int xcd_map) {
-  constexpr int C = kBC, DS = kBDS, DKP = DK + 1, CP = C + 1, DSP = DS + 1;
-  constexpr int NK = (C * DK + kBThreads - 1) / kBThreads, NT = (C * C + kBThreads - 1) / kBThreads;
-  constexpr int NV = (C * DS + kBThreads - 1) / kBThreads;
+__global__ __launch_bounds__(128) void chunk_bwd_dstates_kernel(const T* dout, const float* __restrict__ dhT,
+                                                               const float* __restrict__ rec,
+                                                               float* __restrict__ dhn, float* __restrict__ dh0,
+                                                               int T_len, int nchunks, int dv, int xcd_map) {
+  constexpr int C = kBC, NW = kDsWaves<DK>, RHW = DK / 16 / NW, RT = C / 16;
   using R = BwdRec<DK>;
-  __shared__ float sdH[DK * DSP], sKG[C * DKP], sKR[C * DKP], sQG[C * DKP], sM[C * CP], sTB[C * CP], sdO[C * DSP],
-      sdU[C * DSP], sdX[C * DSP], sGC[DK];
-  const int tid = threadIdx.x;
-  const int nsl = dv / DS;
+  __shared__ f32x4 xb[2][NW][RT][64];   // partial dU of each wave, by chunk parity
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, r = lane & 15;
+  const int nsl = dv / 16;
   long long bh;
   int slice;
   head_slice(blockIdx.x, nsl, xcd_map, bh, slice);
-  const int col0 = slice * DS;
-  float rKG[NK], rKR[NK], rQG[NK], rM[NT], rTB[NT], rO[NV], rGC = 0.f;
-  auto fetch = [&](int c) __attribute__((always_inline)) {
-    const float* rc = rec + (size_t)(bh * nchunks + c) * R::FLOATS;
+  const int col = slice * 16 + r;   // this lane's value column
+  const int rb = wave * RHW;        // the wave's first row tile
+  f32x4 dacc[RHW];                  // dH rows 16 (rb + rh) + 4 g + i, column col
+#pragma unroll
+  for (int rh = 0; rh < RHW; ++rh)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      dacc[rh][i] = dhT ? dhT[(bh * DK + 16 * (rb + rh) + 4 * g + i) * (long long)dv + col] : 0.f;
+  struct First {        // needed first in a chunk
+    f32x4 kr[RT][RHW];  // KR rows 16 rt + r, channels 16 (rb + kb) + 4 g .. + 3
+    f32x4 mt[RT][RT];   // M^T rows 16 rt + r, positions 16 kb + 4 g .. + 3 (kb >= rt)
+    T dov[RT][4];       // dO rows 16 kb + 4 g + e, column col, as stored (rows past the end: any row)
+  };
+  f32x4 tbt[RT][RT];    // TB^T rows 16 rt + r, positions 16 kb + 4 g .. + 3 (kb >= rt)
+  f32x4 qgt[RHW][RT];   // QG^T rows 16 (rb + rh) + r, positions 16 kb + 4 g .. + 3
+  f32x4 kgt[RHW][RT];   // KG^T likewise
+  f32x4 gc[RHW];        // Gamma_C at channels 16 (rb + rh) + 4 g .. + 3
+  auto recp = [&](int c) { return rec + (size_t)(bh * nchunks + c) * R::FLOATS; };
+  auto load_first = [&](First& o, int c) __attribute__((always_inline)) {
+    const float* rc = recp(c);
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int kb = 0; kb < RHW; ++kb)
+        o.kr[rt][kb] = *reinterpret_cast<const f32x4*>(rc + R::KR_OFF + (16 * rt + r) * DK + 16 * (rb + kb) + 4 * g);
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int kb = rt; kb < RT; ++kb)
+        o.mt[rt][kb] = *reinterpret_cast<const f32x4*>(rc + R::MT_OFF + (16 * rt + r) * C + 16 * kb + 4 * g);
     const int t0 = c * C, cv = min(C, T_len - t0);
 #pragma unroll
-    for (int i = 0; i < NK; ++i) {
-      const int e = tid + i * kBThreads;
-      const int ee = e < C * DK ? e : 0;
-      rKG[i] = rc[R::KG_OFF + ee];
-      rKR[i] = rc[R::KR_OFF + ee];
-      rQG[i] = rc[R::QG_OFF + ee];
-    }
+    for (int kb = 0; kb < RT; ++kb)
 #pragma unroll
-    for (int i = 0; i < NT; ++i) {
-      const int e = tid + i * kBThreads, ee = e < C * C ? e : 0;
-      rM[i] = rc[R::M_OFF + ee];
-      rTB[i] = rc[R::TB_OFF + ee];
-    }
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int e = tid + i * kBThreads, t = e / DS, j = e % DS;
-      const bool ok = e < C * DS && t < cv;
-      rO[i] = ld_or(dout, ok ? (size_t)(bh * T_len + t0 + t) * dv + col0 + j : 0, ok, 0.f);
-    }
-    if (tid < DK) rGC = rc[R::GC_OFF + tid];
+      for (int e = 0; e < 4; ++e) {
+        const int t = 16 * kb + 4 * g + e;
+        o.dov[kb][e] = dout[(size_t)(bh * T_len + t0 + (t < cv ? t : 0)) * dv + col];
+      }
   };
-  for (int e = tid; e < DK * DS; e += kBThreads) {
-    const int i = e / DS, j = e % DS;
-    sdH[i * DSP + j] = dhT ? dhT[(bh * DK + i) * (long long)dv + col0 + j] : 0.f;
-  }
-  if (nchunks > 0) fetch(nchunks - 1);
-  for (int c = nchunks - 1; c >= 0; --c) {
+  auto load_tbt = [&](int c) __attribute__((always_inline)) {
+    const float* rc = recp(c);
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int kb = rt; kb < RT; ++kb)
+        tbt[rt][kb] = *reinterpret_cast<const f32x4*>(rc + R::TBT_OFF + (16 * rt + r) * C + 16 * kb + 4 * g);
+  };
+  auto load_last = [&](int c) __attribute__((always_inline)) {
+    const float* rc = recp(c);
+#pragma unroll
+    for (int rh = 0; rh < RHW; ++rh)
+#pragma unroll
+      for (int kb = 0; kb < RT; ++kb) {
+        qgt[rh][kb] = *reinterpret_cast<const f32x4*>(rc + R::QGT_OFF + (16 * (rb + rh) + r) * C + 16 * kb + 4 * g);
+        kgt[rh][kb] = *reinterpret_cast<const f32x4*>(rc + R::KGT_OFF + (16 * (rb + rh) + r) * C + 16 * kb + 4 * g);
+      }
+#pragma unroll
+    for (int rh = 0; rh < RHW; ++rh)
+      gc[rh] = *reinterpret_cast<const f32x4*>(rc + R::GC_OFF + 16 * (rb + rh) + 4 * g);
+  };
+  // chunk c with the first-needed operands in `cur`, loading chunk c - 1's
+  // into `nxt`; a step with live == false (past the first chunk) computes on
+  // chunk 0 again and changes nothing
+  auto step = [&](First& cur, First& nxt, int c, bool live) __attribute__((always_inline)) {
+    c = max(c, 0);
     const long long chunk = bh * nchunks + c;
+    const int cn = max(c - 1, 0);   // the next chunk processed (the first reloads itself)
+    if (live)
 #pragma unroll
-    for (int i = 0; i < NK; ++i) {
-      const int e = tid + i * kBThreads;
-      if (e < C * DK) {
-        const int o = (e / DK) * DKP + e % DK;
-        sKG[o] = rKG[i];
-        sKR[(e % C) * DKP + e / C] = rKR[i];   // the record holds KR^T
-        sQG[o] = rQG[i];
-      }
-    }
+      for (int rh = 0; rh < RHW; ++rh)   // dH'
+        *reinterpret_cast<f32x4*>(dhn + (size_t)chunk * DK * dv + hc_slot<DK>(16 * (rb + rh) + 4 * g, col)) = dacc[rh];
+    // (scheduling barriers keep each group of loads where it is written: the
+    // scheduler would otherwise sink them toward their uses)
+    __builtin_amdgcn_sched_barrier(0);
+    load_first(nxt, cn);
+    __builtin_amdgcn_sched_barrier(0);
+    const int cv = min(C, T_len - c * C);
+    f32x4 dof[RT];
 #pragma unroll
-    for (int i = 0; i < NT; ++i) {
-      const int e = tid + i * kBThreads;
-      if (e < C * C) {
-        sM[(e / C) * CP + e % C] = rM[i];
-        sTB[(e / C) * CP + e % C] = rTB[i];
-      }
-    }
+    for (int kb = 0; kb < RT; ++kb)
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int e = tid + i * kBThreads;
-      if (e < C * DS) sdO[(e / DS) * DSP + e % DS] = rO[i];
+      for (int e = 0; e < 4; ++e) dof[kb][e] = 16 * kb + 4 * g + e < cv ? to_f32(cur.dov[kb][e]) : 0.f;
+    // dU = M^T dO (first wave) + KR dH' (each wave its channels), summed over the waves
+    f32x4 du[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      f32x4 m = zero4();
+#pragma unroll
+      for (int kb = rt; kb < RT; ++kb)
+        m = mma<float>(m, Frag{__builtin_bit_cast(u32x4, cur.mt[rt][kb])}, frag_from_acc_f32(dof[kb]));
+      du[rt] = wave == 0 ? m : zero4();
+#pragma unroll
+      for (int kb = 0; kb < RHW; ++kb)
+        du[rt] = mma<float>(du[rt], Frag{__builtin_bit_cast(u32x4, cur.kr[rt][kb])}, frag_from_acc_f32(dacc[kb]));
     }
-    if (tid < DK) sGC[tid] = rGC;
-    __syncthreads();
-    if (c > 0) fetch(c - 1);
-    for (int e = tid; e < DK * DS; e += kBThreads) {
-      const int i = e / DS, j = e % DS;
-      dhn[(size_t)chunk * DK * dv + (size_t)i * dv + col0 + j] = sdH[i * DSP + j];
+    if constexpr (NW == 2) {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) xb[c & 1][wave][rt][lane] = du[rt];
+      __syncthreads();
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) du[rt] += xb[c & 1][1 - wave][rt][lane];
     }
-    gemm_lds<false, C>(sdU, DSP, sM, 1, CP, sdO, DSP, 1, C, DS, 1.f);       // dU = M^T dO
-    gemm_lds<true, DK>(sdU, DSP, sKR, DKP, 1, sdH, DSP, 1, C, DS, 1.f);     //    + KR dH'  (same tiles, same wave)
-    __syncthreads();
-    gemm_lds<false, C>(sdX, DSP, sTB, 1, CP, sdU, DSP, 1, C, DS, 1.f);      // dX = TB^T dU
-    __syncthreads();
-    for (int e = tid; e < DK * DS; e += kBThreads) sdH[(e / DS) * DSP + e % DS] *= sGC[e / DS];
-    __syncthreads();
-    gemm_lds<true, C>(sdH, DSP, sQG, 1, DKP, sdO, DSP, 1, DK, DS, 1.f);     // + QG^T dO
-    gemm_lds<true, C>(sdH, DSP, sKG, 1, DKP, sdX, DSP, 1, DK, DS, -1.f);    // - KG^T dX
-    __syncthreads();
+    // dX = TB^T dU, negated for the update below
+    f32x4 ndx[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      f32x4 x = zero4();
+#pragma unroll
+      for (int kb = rt; kb < RT; ++kb)
+        x = mma<float>(x, Frag{__builtin_bit_cast(u32x4, tbt[rt][kb])}, frag_from_acc_f32(du[kb]));
+      ndx[rt] = -x;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    load_tbt(cn);
+    __builtin_amdgcn_sched_barrier(0);
+    // dH = Gamma_C . dH' + QG^T dO - KG^T dX
+#pragma unroll
+    for (int rh = 0; rh < RHW; ++rh) {
+      f32x4 h = gc[rh] * dacc[rh];
+#pragma unroll
+      for (int kb = 0; kb < RT; ++kb)
+        h = mma<float>(h, Frag{__builtin_bit_cast(u32x4, qgt[rh][kb])}, frag_from_acc_f32(dof[kb]));
+#pragma unroll
+      for (int kb = 0; kb < RT; ++kb)
+        h = mma<float>(h, Frag{__builtin_bit_cast(u32x4, kgt[rh][kb])}, frag_from_acc_f32(ndx[kb]));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dacc[rh][i] = live ? h[i] : dacc[rh][i];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    load_last(cn);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // two first-needed sets trading roles, so that no register copy waits for
+  // loads just issued
+  First s0, s1;
+  if (nchunks > 0) {
+    load_first(s0, nchunks - 1);
+    load_tbt(nchunks - 1);
+    load_last(nchunks - 1);
+  }
+  for (int c = nchunks - 1; c >= 0; c -= 2) {
+    step(s0, s1, c, true);
+    step(s1, s0, c - 1, c >= 1);
   }
   if (dh0)
-    for (int e = tid; e < DK * DS; e += kBThreads) {
-      const int i = e / DS, j = e % DS;
-      dh0[(bh * DK + i) * (long long)dv + col0 + j] = sdH[i * DSP + j];
-    }
+#pragma unroll
+    for (int rh = 0; rh < RHW; ++rh)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dh0[(bh * DK + 16 * (rb + rh) + 4 * g + i) * (long long)dv + col] = dacc[rh][i];
 }
 
 // ============================================================ grad (per chunk)
@@ -580,7 +674,7 @@ __global__ __launch_bounds__(kBThreads) void chunk_bwd_grad_kernel(
     for (int i = 0; i < NC; ++i) {
       const int e = tid + i * kBThreads;
       const bool in = e < C * C;
-      m0[i] = rc[R::M_OFF + (in ? e : 0)];
+      m0[i] = rc[R::MT_OFF + (in ? e : 0)];
       m1[i] = rc[R::TB_OFF + (in ? e : 0)];
       m2[i] = rc[R::T_OFF + (in ? e : 0)];
       m3[i] = rc[R::S_OFF + (in ? e : 0)];
@@ -594,7 +688,7 @@ __global__ __launch_bounds__(kBThreads) void chunk_bwd_grad_kernel(
         sk[o] = r1[i];
         sa[o] = r2[i];
         sKG[o] = r3[i];
-        sKR[(e % C) * DKP + e / C] = r4[i];   // the record holds KR^T
+        sKR[o] = r4[i];
       }
     }
 #pragma unroll
@@ -602,7 +696,7 @@ __global__ __launch_bounds__(kBThreads) void chunk_bwd_grad_kernel(
       const int e = tid + i * kBThreads;
       if (e < C * C) {
         const int o = (e / C) * CP + e % C;
-        sM[o] = m0[i];
+        sM[(e % C) * CP + e / C] = m0[i];   // the record holds M^T
         sTB[o] = m1[i];
         sT[o] = m2[i];
         sS[o] = m3[i];
@@ -631,8 +725,8 @@ __global__ __launch_bounds__(kBThreads) void chunk_bwd_grad_kernel(
 #pragma unroll
     for (int i = 0; i < NH; ++i) {
       const int e = tid + i * kBThreads, ee = e < DK * DS ? e : 0, ii = ee / DS, j = ee % DS;
-      rH[i] = hcc[(size_t)col0 * DK + ee];   // the slice's block, in slot order (hc_slot)
-      rdH[i] = dhc[(size_t)ii * dv + col0 + j];
+      rH[i] = hcc[(size_t)col0 * DK + ee];   // the slice's blocks, in slot order (hc_slot)
+      rdH[i] = dhc[(size_t)col0 * DK + ee];
     }
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
@@ -651,8 +745,9 @@ __global__ __launch_bounds__(kBThreads) void chunk_bwd_grad_kernel(
       const int e = tid + i * kBThreads;
       if (e < DK * DS) {
         // slot e holds row 16 (e / 256) + 4 ((e / 64) % 4) + e % 4, column (e / 4) % 16
-        sH[(16 * (e / 256) + 4 * ((e / 64) % 4) + e % 4) * DSP + (e / 4) % 16] = rH[i];
-        sdH[(e / DS) * DSP + e % DS] = rdH[i];
+        const int o = (16 * (e / 256) + 4 * ((e / 64) % 4) + e % 4) * DSP + (e / 4) % 16;
+        sH[o] = rH[i];
+        sdH[o] = rdH[i];
       }
     }
 #pragma unroll
@@ -949,8 +1044,8 @@ static hipError_t launch_bwd_t(const BwdArgs& a) {
     hipLaunchKernelGGL((chunk_bwd_states_kernel<T, DK>), dim3((unsigned)(BH * nsl)), dim3(64), 0, a.stream,
                        (const T*)a.v, a.h0, rec, hc, a.T, nch, a.dv, xcd_map);
   }
-  hipLaunchKernelGGL((chunk_bwd_dstates_kernel<T, DK>), dim3((unsigned)(BH * nsl)), dim3(kBThreads), 0, a.stream,
-                     (const T*)a.dout, a.dhT, rec, dhn, a.gh0, a.T, nch, a.dv, xcd_map);
+  hipLaunchKernelGGL((chunk_bwd_dstates_kernel<T, DK>), dim3((unsigned)(BH * nsl)), dim3(64 * kDsWaves<DK>), 0,
+                     a.stream, (const T*)a.dout, a.dhT, rec, dhn, a.gh0, a.T, nch, a.dv, xcd_map);
   if (total > 0)
     hipLaunchKernelGGL((chunk_bwd_grad_kernel<T, DK>), dim3((unsigned)total), dim3(kBThreads), 0, a.stream,
                        (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.alpha, (const T*)a.beta,

@@ -218,7 +218,7 @@ int ckda_deltaproduct2_fwd(const void* q, const void* k, const void* v, const vo
 
 /* Bytes of device workspace ckda_chunk_bwd needs, or 0 for invalid or
  * unsupported sizes: per 32-position chunk of every (batch, head) an fp32
- * record (4 * 32 * 32 + 3 * 32 * dk + dk floats, rounded up to 64 floats)
+ * record (5 * 32 * 32 + 5 * 32 * dk + dk floats, rounded up to 64 floats)
  * plus the chunk-start state and its gradient (2 * dk * dv floats). */
 size_t ckda_chunk_bwd_workspace_size(int B, int H, int T, int dk, int dv, int dtype);
 

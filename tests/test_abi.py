@@ -229,8 +229,8 @@ def call_bwd(**kw):
 
 def test_bwd_workspace_size():
     L = ck.lib()
-    # per 32-position chunk: (4*32*32 + 3*32*dk + dk) floats rounded to 64, plus 2 dk dv floats
-    per = ((4 * 32 * 32 + 3 * 32 * 128 + 128 + 63) // 64 * 64 + 2 * 128 * 128) * 4
+    # per 32-position chunk: (5*32*32 + 5*32*dk + dk) floats rounded to 64, plus 2 dk dv floats
+    per = ((5 * 32 * 32 + 5 * 32 * 128 + 128 + 63) // 64 * 64 + 2 * 128 * 128) * 4
     assert L.ckda_chunk_bwd_workspace_size(1, 1, 32, 128, 128, 1) == per
     assert L.ckda_chunk_bwd_workspace_size(4, 16, 4096, 128, 128, 1) == 64 * 128 * per
     assert L.ckda_chunk_bwd_workspace_size(1, 1, 33, 128, 128, 1) == 2 * per
