@@ -63,6 +63,16 @@ def test_shapes(dtype, dk, dv):
     run(w)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dk,T", [(16, 89), (128, 89), (128, 160), (16, 1)])
+def test_odd_chunk_counts(dtype, dk, T):
+    """The reverse state pass takes two chunks per loop iteration; an odd
+    number of 32-position chunks ends with a step that must change nothing
+    (one wave per slice at dk 16, two at dk 128)."""
+    w = gen.Workload("bwd", 1, 2, T, dk, 32, 64, dtype, "ckda_tanh", "normal", 7250 + dk + T)
+    run(w)
+
+
 @pytest.mark.parametrize("law", ["zero_and_unit", "small_gates", "orthogonal", "kda"])
 def test_stress_gates(law):
     """Exact zero and +-1 gates, gates down to 1e-12, orthogonal steps: the
