@@ -525,6 +525,11 @@ __global__ __launch_bounds__(128) void chunk_bwd_dstates_kernel(const T* dout, c
   // into `nxt`; a step with live == false (past the first chunk) computes on
   // chunk 0 again and changes nothing
   auto step = [&](First& cur, First& nxt, int c, bool live) __attribute__((always_inline)) {
+    // exchange buffer by the parity of the UNCLAMPED chunk index: the dead
+    // step (c = -1) then writes buffer 1, last read before the live chunk-0
+    // step's barrier, never buffer 0, which the other wave may still be
+    // reading for chunk 0
+    const int par = c & 1;
     c = max(c, 0);
     const long long chunk = bh * nchunks + c;
     const int cn = max(c - 1, 0);   // the next chunk processed (the first reloads itself)
@@ -558,10 +563,10 @@ __global__ __launch_bounds__(128) void chunk_bwd_dstates_kernel(const T* dout, c
     }
     if constexpr (NW == 2) {
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) xb[c & 1][wave][rt][lane] = du[rt];
+      for (int rt = 0; rt < RT; ++rt) xb[par][wave][rt][lane] = du[rt];
       __syncthreads();
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) du[rt] += xb[c & 1][1 - wave][rt][lane];
+      for (int rt = 0; rt < RT; ++rt) du[rt] += xb[par][1 - wave][rt][lane];
     }
     // dX = TB^T dU, negated for the update below
     f32x4 ndx[RT];

@@ -64,11 +64,14 @@ def test_shapes(dtype, dk, dv):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("dk,T", [(16, 89), (128, 89), (128, 160), (16, 1)])
+@pytest.mark.parametrize("dk,T", [(16, 89), (32, 89), (64, 89), (64, 33), (128, 89), (128, 160), (16, 1)])
 def test_odd_chunk_counts(dtype, dk, T):
     """The reverse state pass takes two chunks per loop iteration; an odd
     number of 32-position chunks ends with a step that must change nothing
-    (one wave per slice at dk 16, two at dk 128)."""
+    (one wave per slice at dk 16; two waves at dk 32, 64 and 128, which sum
+    their partial dU through an LDS buffer chosen by the chunk's parity, so
+    the dead step must not write the buffer the last live step exchanged
+    through)."""
     w = gen.Workload("bwd", 1, 2, T, dk, 32, 64, dtype, "ckda_tanh", "normal", 7250 + dk + T)
     run(w)
 
