@@ -23,7 +23,8 @@ LIB_PATH = os.path.join(_HERE, "libckda.so")
 
 DTYPE_F32, DTYPE_BF16 = 0, 1
 STATUS = {0: "CKDA_OK", 1: "CKDA_ERR_NULL", 2: "CKDA_ERR_DIM", 3: "CKDA_ERR_UNSUPPORTED",
-          4: "CKDA_ERR_ALIAS", 5: "CKDA_ERR_WORKSPACE", 6: "CKDA_ERR_HIP", 7: "CKDA_ERR_FLAGS"}
+          4: "CKDA_ERR_ALIAS", 5: "CKDA_ERR_HIP", 6: "CKDA_ERR_WORKSPACE", 7: "CKDA_ERR_FLAGS"}
+(ERR_NULL, ERR_DIM, ERR_UNSUPPORTED, ERR_ALIAS, ERR_HIP, ERR_WORKSPACE, ERR_FLAGS) = range(1, 8)
 FUSE_GATES, FUSE_NORM_K, FUSE_NORM_Q = 1, 2, 4       # CKDA_FUSE_*
 GATE_SCALAR = 8                                      # CKDA_GATE_SCALAR
 EXPORTS = ("ckda_chunk_fwd_workspace_size", "ckda_chunk_fwd", "ckda_chunk_fwd_timed", "ckda_chunk_fwd_ex",
@@ -125,6 +126,34 @@ def _require(ts, dtype):
             raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
 
 
+def _shapes(expect):
+    """Raise ValueError unless every given tensor has exactly its expected
+    shape.  The C ABI receives bare pointers and cannot see shapes, so this is
+    the only guard against a wrong-shaped tensor turning into out-of-bounds
+    device reads or writes; it runs before anything else touches the
+    tensors.  `expect` maps a name to (tensor or None, shape tuple)."""
+    for name, (t, shape) in expect.items():
+        if t is not None and tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _dims(t, n, name):
+    if t.dim() != n:
+        raise ValueError(f"{name} must have {n} dimensions, got shape {tuple(t.shape)}")
+    return tuple(t.shape)
+
+
+def _scratch(nbytes, device, stream):
+    """A temporary uint8 workspace for one call.  It is allocated from torch's
+    caching allocator; when the kernels run on another stream than the
+    current one, the allocation is tied to that stream too, so that it is not
+    handed out again before those kernels are done with it."""
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    if stream is not None and stream != torch.cuda.current_stream(device):
+        ws.record_stream(stream)
+    return ws
+
+
 def workspace_size(B, H, T, dk, dv, chunk, dtype) -> int:
     code = dtype if isinstance(dtype, int) else _dtype_code(torch.empty(0, dtype=dtype))
     return int(lib().ckda_chunk_fwd_workspace_size(B, H, T, dk, dv, chunk, code))
@@ -144,23 +173,32 @@ def chunk_fwd(q, k, v, alpha, beta, h0=None, chunk=64, workspace=None, o=None, h
     `events`.  `idx` ([H, dk] int32 GPU tensor) gathers each head's retained
     key channels from full-width q, k, alpha rows [B,H,T,dk_in] inside the
     kernels (ckda_chunk_fwd_gather); states then have dk rows."""
-    B, H, T, dk = q.shape
+    B, H, T, dk = _dims(q, 4, "q")
     dk_in = dk
     if idx is not None:
-        _require(dict(idx=idx), torch.int32)
         if idx.dim() != 2 or idx.shape[0] != H:
             raise ValueError(f"idx must be [H, dk], got {tuple(idx.shape)}")
         dk = idx.shape[1]
-    dv = v.shape[-1]
+    dv = _dims(v, 4, "v")[-1]
+    scalar = bool(fuse & GATE_SCALAR)
+    _shapes(dict(k=(k, (B, H, T, dk_in)), v=(v, (B, H, T, dv)),
+                 alpha=(alpha, (B, H, T) if scalar else (B, H, T, dk_in)), beta=(beta, (B, H, T)),
+                 h0=(h0, (B, H, dk, dv)), o=(o, (B, H, T, dv)), hT=(hT, (B, H, dk, dv))))
     _require(dict(q=q, k=k, v=v, alpha=alpha, beta=beta), q.dtype)
+    if idx is not None:
+        _require(dict(idx=idx), torch.int32)
     code = _dtype_code(q)
     if h0 is not None:
         _require(dict(h0=h0), torch.float32)
+    if o is not None:
+        _require(dict(o=o), q.dtype)
+    if hT is not None:
+        _require(dict(hT=hT), torch.float32)
     need = workspace_size(B, H, T, dk, dv, chunk, code)
     if need == 0:
-        raise CkdaError(3, f"unsupported sizes dk={dk} dv={dv} chunk={chunk}")
+        raise CkdaError(ERR_UNSUPPORTED, f"unsupported sizes dk={dk} dv={dv} chunk={chunk}")
     if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = _scratch(need, q.device, stream)
     if o is None:
         o = torch.empty((B, H, T, dv), dtype=q.dtype, device=q.device)
     if hT is None and want_state:
@@ -191,16 +229,22 @@ def decode_step(q, k, v, alpha, beta, H, o=None, stream=None, fuse=0, idx=None):
     (FUSE_* bits) applies the per-token prologue first (ckda_decode_step_ex).
     `idx` ([Hh, dk] int32) gathers retained key channels from rows of dk_in
     (ckda_decode_step_gather)."""
-    N, Hh, dk = q.shape
+    N, Hh, dk = _dims(q, 3, "q")
     dk_in = dk
     if idx is not None:
-        _require(dict(idx=idx), torch.int32)
         if idx.dim() != 2 or idx.shape[0] != Hh:
             raise ValueError(f"idx must be [H, dk], got {tuple(idx.shape)}")
         dk = idx.shape[1]
-    dv = v.shape[-1]
+    dv = _dims(v, 3, "v")[-1]
+    scalar = bool(fuse & GATE_SCALAR)
+    _shapes(dict(k=(k, (N, Hh, dk_in)), v=(v, (N, Hh, dv)), alpha=(alpha, (N, Hh) if scalar else (N, Hh, dk_in)),
+                 beta=(beta, (N, Hh)), H=(H, (N, Hh, dk, dv)), o=(o, (N, Hh, dv))))
     _require(dict(q=q, k=k, v=v, alpha=alpha, beta=beta), q.dtype)
     _require(dict(H=H), torch.float32)
+    if idx is not None:
+        _require(dict(idx=idx), torch.int32)
+    if o is not None:
+        _require(dict(o=o), q.dtype)
     code = _dtype_code(q)
     if o is None:
         o = torch.empty((N, Hh, dv), dtype=q.dtype, device=q.device)
@@ -219,23 +263,25 @@ def deltaproduct2_fwd(q, k, v, beta, alpha=None, h0=None, chunk=64, workspace=No
     """DeltaProduct_2 forward (ckda_deltaproduct2_fwd): q [B,H,T,dk];
     k [B,H,T,2,dk]; v [B,H,T,2,dv]; beta [B,H,T,2]; alpha [B,H,T] scalar
     gates or None (ungated); h0 [B,H,dk,dv] fp32 or None.  Returns (o, hT)."""
-    B, H, T, dk = q.shape
-    dv = v.shape[-1]
+    B, H, T, dk = _dims(q, 4, "q")
+    dv = _dims(v, 5, "v")[-1]
+    _shapes(dict(k=(k, (B, H, T, 2, dk)), v=(v, (B, H, T, 2, dv)), beta=(beta, (B, H, T, 2)),
+                 alpha=(alpha, (B, H, T)), h0=(h0, (B, H, dk, dv)), o=(o, (B, H, T, dv)), hT=(hT, (B, H, dk, dv))))
     ts = dict(q=q, k=k, v=v, beta=beta)
     if alpha is not None:
         ts["alpha"] = alpha
+    if o is not None:
+        ts["o"] = o
     _require(ts, q.dtype)
-    if k.shape != (B, H, T, 2, dk) or v.shape != (B, H, T, 2, dv) or beta.shape != (B, H, T, 2) \
-            or (alpha is not None and alpha.shape != (B, H, T)):
-        raise ValueError("inconsistent DeltaProduct_2 shapes")
     code = _dtype_code(q)
-    if h0 is not None:
-        _require(dict(h0=h0), torch.float32)
+    for name, t in (("h0", h0), ("hT", hT)):
+        if t is not None:
+            _require({name: t}, torch.float32)
     need = workspace_size(B, H, 2 * T, dk, dv, chunk, code)
     if need == 0:
-        raise CkdaError(3, f"unsupported sizes dk={dk} dv={dv} chunk={chunk}")
+        raise CkdaError(ERR_UNSUPPORTED, f"unsupported sizes dk={dk} dv={dv} chunk={chunk}")
     if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = _scratch(need, q.device, stream)
     if o is None:
         o = torch.empty((B, H, T, dv), dtype=q.dtype, device=q.device)
     if hT is None and want_state:
@@ -249,15 +295,17 @@ def deltaproduct2_fwd(q, k, v, beta, alpha=None, h0=None, chunk=64, workspace=No
 def deltaproduct2_decode_step(q, k, v, beta, H, alpha=None, o=None, stream=None, fuse=0):
     """One DeltaProduct_2 decode step: q [N,Hh,dk]; k [N,Hh,2,dk];
     v [N,Hh,2,dv]; beta [N,Hh,2]; alpha [N,Hh] or None; H fp32 in place."""
-    N, Hh, dk = q.shape
-    dv = v.shape[-1]
+    N, Hh, dk = _dims(q, 3, "q")
+    dv = _dims(v, 4, "v")[-1]
+    _shapes(dict(k=(k, (N, Hh, 2, dk)), v=(v, (N, Hh, 2, dv)), beta=(beta, (N, Hh, 2)), alpha=(alpha, (N, Hh)),
+                 H=(H, (N, Hh, dk, dv)), o=(o, (N, Hh, dv))))
     ts = dict(q=q, k=k, v=v, beta=beta)
     if alpha is not None:
         ts["alpha"] = alpha
+    if o is not None:
+        ts["o"] = o
     _require(ts, q.dtype)
     _require(dict(H=H), torch.float32)
-    if k.shape != (N, Hh, 2, dk) or v.shape != (N, Hh, 2, dv) or beta.shape != (N, Hh, 2):
-        raise ValueError("inconsistent DeltaProduct_2 shapes")
     code = _dtype_code(q)
     if o is None:
         o = torch.empty((N, Hh, dv), dtype=q.dtype, device=q.device)
@@ -283,8 +331,10 @@ def chunk_bwd(q, k, v, alpha, beta, do, h0=None, dhT=None, want_dh0=True, worksp
     GATE_SCALAR bits, ckda_chunk_bwd_ex) the inputs are those of the fused
     forward and the gradients are with respect to them: logits, raw keys
     and queries; with GATE_SCALAR alpha and dalpha are [B,H,T]."""
-    B, H, T, dk = q.shape
-    dv = v.shape[-1]
+    B, H, T, dk = _dims(q, 4, "q")
+    dv = _dims(v, 4, "v")[-1]
+    _shapes(dict(k=(k, (B, H, T, dk)), alpha=(alpha, (B, H, T) if fuse & GATE_SCALAR else (B, H, T, dk)),
+                 beta=(beta, (B, H, T)), do=(do, (B, H, T, dv)), h0=(h0, (B, H, dk, dv)), dhT=(dhT, (B, H, dk, dv))))
     _require(dict(q=q, k=k, v=v, alpha=alpha, beta=beta, do=do), q.dtype)
     code = _dtype_code(q)
     if h0 is not None:
@@ -293,9 +343,9 @@ def chunk_bwd(q, k, v, alpha, beta, do, h0=None, dhT=None, want_dh0=True, worksp
         _require(dict(dhT=dhT), torch.float32)
     need = bwd_ex_workspace_size(B, H, T, dk, dv, code, fuse) if fuse else bwd_workspace_size(B, H, T, dk, dv, code)
     if need == 0:
-        raise CkdaError(3, f"unsupported sizes dk={dk} dv={dv} or flags {fuse}")
+        raise CkdaError(ERR_UNSUPPORTED, f"unsupported sizes dk={dk} dv={dv} or flags {fuse}")
     if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = _scratch(need, q.device, stream)
     f32 = dict(dtype=torch.float32, device=q.device)
     gq, gk = (torch.empty((B, H, T, dk), **f32) for _ in range(2))
     galpha = torch.empty((B, H, T) if fuse & GATE_SCALAR else (B, H, T, dk), **f32)
@@ -317,8 +367,11 @@ def deltaproduct2_bwd(q, k, v, alpha, beta, do, h0=None, dhT=None, want_dh0=True
     k [B,H,T,2,dk], v [B,H,T,2,dv], beta [B,H,T,2], alpha [B,H,T] or None,
     do [B,H,T,dv] (input dtype), dhT fp32 or None.  Returns fp32 (dq, dk, dv,
     dalpha or None, dbeta, dh0 or None) in the inputs' shapes."""
-    B, H, T, dk = q.shape
-    dv = v.shape[-1]
+    B, H, T, dk = _dims(q, 4, "q")
+    dv = _dims(v, 5, "v")[-1]
+    _shapes(dict(k=(k, (B, H, T, 2, dk)), v=(v, (B, H, T, 2, dv)), beta=(beta, (B, H, T, 2)),
+                 alpha=(alpha, (B, H, T)), do=(do, (B, H, T, dv)), h0=(h0, (B, H, dk, dv)),
+                 dhT=(dhT, (B, H, dk, dv))))
     ts = dict(q=q, k=k, v=v, beta=beta, do=do)
     if alpha is not None:
         ts["alpha"] = alpha
@@ -329,9 +382,9 @@ def deltaproduct2_bwd(q, k, v, alpha, beta, do, h0=None, dhT=None, want_dh0=True
             _require({name: t}, torch.float32)
     need = int(lib().ckda_deltaproduct2_bwd_workspace_size(B, H, T, dk, dv, code))
     if need == 0:
-        raise CkdaError(3, f"unsupported sizes dk={dk} dv={dv}")
+        raise CkdaError(ERR_UNSUPPORTED, f"unsupported sizes dk={dk} dv={dv}")
     if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = _scratch(need, q.device, stream)
     f32 = dict(dtype=torch.float32, device=q.device)
     gq = torch.empty((B, H, T, dk), **f32)
     gk = torch.empty((B, H, T, 2, dk), **f32)

@@ -28,8 +28,8 @@
  * which is the same matrix as the first form: (I - b k k^T) Hbar + b k v^T
  * = Hbar + b k (v - Hbar^T k)^T.  The state is n x d_v with row i = key
  * channel i.  No log-space, no sign handling, no chunking: alpha is applied
- * as the signed real number it is (negative and zero gates included, App. B.2
- * "These theoretical ranges include their endpoints and zero gates").  No
+ * as the signed real number it is (negative and zero gates included: App. B.2
+ * admits the closed ranges, their endpoints and zero gates among them).  No
  * query scaling and no key normalisation are applied; inputs are used exactly
  * as given (bf16 and fp32 inputs are widened exactly to fp64).
  *

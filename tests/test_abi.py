@@ -14,6 +14,7 @@ HEADER = os.path.join(ROOT, "include", "ckda.h")
 
 BASE = 0x7F0000000000   # fake, never-dereferenced device addresses
 MB = 1 << 20
+HIP, WS = ck.ERR_HIP, ck.ERR_WORKSPACE   # 5 and 6
 
 
 def declared_functions():
@@ -31,6 +32,19 @@ def test_library_exports_every_declared_function():
     assert L.ckda_abi_version() == 1
 
 
+def test_status_numbering():
+    """Codes 0-5 keep the boundary's original numbering (CKDA_ERR_HIP = 5);
+    the workspace and flag codes were added after it."""
+    text = open(HEADER).read()
+    vals = dict((n, int(v)) for n, v in re.findall(r"\b(CKDA_(?:OK|ERR_\w+))\s*=\s*(\d+)", text))
+    assert vals == {"CKDA_OK": 0, "CKDA_ERR_NULL": 1, "CKDA_ERR_DIM": 2, "CKDA_ERR_UNSUPPORTED": 3,
+                    "CKDA_ERR_ALIAS": 4, "CKDA_ERR_HIP": 5, "CKDA_ERR_WORKSPACE": 6, "CKDA_ERR_FLAGS": 7}
+    assert {v: "CKDA_" + k for v, k in ((v, n[5:]) for n, v in vals.items())} == ck.STATUS
+    L = ck.lib()
+    assert L.ckda_status_string(5) == b"HIP runtime error"
+    assert b"workspace" in L.ckda_status_string(6)
+
+
 def test_status_strings():
     L = ck.lib()
     for s in range(8):
@@ -42,13 +56,13 @@ def test_workspace_size():
     L = ck.lib()
     ws = L.ckda_chunk_fwd_workspace_size
     # bf16, chunk 64, d_k 128: the record is a sequence of 1 KB fragments --
-    # TB and M (4 row tiles x 2 K blocks, less the 2 blocks above the
-    # diagonal), W and Q~ (4 x 4 each), KR (8 x 2) and one block for the d_k
-    # fp32 chunk decays
+    # TB, its lo part and M (4 row tiles x 2 K blocks, less the 2 blocks
+    # above the diagonal), W and Q~ (4 x 4 each), KR (8 x 2) and one block for
+    # the d_k fp32 chunk decays
     per_chunk = ws(1, 1, 64, 128, 128, 64, 1)
-    assert per_chunk == 1024 * (2 * 6 + 2 * 16 + 16 + 1)
-    assert ws(1, 1, 64, 64, 128, 64, 1) == 1024 * (2 * 6 + 2 * 8 + 8 + 1)
-    assert ws(1, 1, 32, 128, 128, 32, 1) == 1024 * (2 * 2 + 2 * 8 + 8 + 1)
+    assert per_chunk == 1024 * (3 * 6 + 2 * 16 + 16 + 1)
+    assert ws(1, 1, 64, 64, 128, 64, 1) == 1024 * (3 * 6 + 2 * 8 + 8 + 1)
+    assert ws(1, 1, 32, 128, 128, 32, 1) == 1024 * (3 * 2 + 2 * 8 + 8 + 1)
     # fp32: K blocks of 16 elements (lower triangle of 4 x 4 blocks)
     assert ws(1, 1, 64, 128, 128, 64, 0) == 1024 * (2 * 10 + 2 * 32 + 32 + 1)
     assert ws(4, 16, 4096, 128, 128, 64, 1) == 64 * 64 * per_chunk
@@ -100,7 +114,7 @@ def call_dec(**kw):
     (dict(hT=BASE + 16), 4),                                      # hT overlaps q
     (dict(hT=BASE + 5 * MB + 16), 4),                             # hT partially overlaps h0
     (dict(ws=BASE + 6 * MB), 4),                                  # workspace overlaps o
-    (dict(ws=None), 5), (dict(wsb=1024), 5), (dict(ws=BASE + 8 * MB + 16), 5),
+    (dict(ws=None), WS), (dict(wsb=1024), WS), (dict(ws=BASE + 8 * MB + 16), WS),
 ])
 def test_chunk_fwd_rejects(kw, status):
     rc, msg = call_fwd(**kw)
@@ -122,7 +136,7 @@ def test_fused_entry_points_check_arguments_like_the_plain_ones(flags):
     assert call_fwd(flags=flags, q=None)[0] == 1
     assert call_fwd(flags=flags, dk=48)[0] == 3
     assert call_fwd(flags=flags, o=BASE + 2 * MB + 64)[0] == 4
-    assert call_fwd(flags=flags, wsb=1024)[0] == 5
+    assert call_fwd(flags=flags, wsb=1024)[0] == WS
     assert call_fwd(flags=flags, B=0)[0] == 0
     assert call_dec(flags=flags, S=None)[0] == 1
     assert call_dec(flags=flags, o=BASE + 5 * MB)[0] == 4
@@ -183,7 +197,7 @@ def call_dp2(**kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(q=None), 1), (dict(beta=None), 1), (dict(flags=8), 7), (dict(flags=1 << 16), 7),
     (dict(o=BASE + 1 * MB + 20000), 4),                # o inside k: 2 T sub-step rows of k (32 KB)
-    (dict(wsb=ck.lib().ckda_chunk_fwd_workspace_size(1, 2, 64, 64, 64, 64, 1)), 5),   # sized for T, not 2 T
+    (dict(wsb=ck.lib().ckda_chunk_fwd_workspace_size(1, 2, 64, 64, 64, 64, 1)), WS),   # sized for T, not 2 T
 ])
 def test_deltaproduct2_rejects(kw, status):
     rc, msg = call_dp2(**kw)
@@ -206,7 +220,7 @@ def test_deltaproduct2_decode_rejects():
 def test_scalar_gate_flag_checks():
     # scalar gate: alpha is [B, H, T]; it does not combine with a gather
     assert call_fwd(flags=8, o=BASE + 3 * MB + 128)[0] == 4      # o inside the 256-byte scalar alpha
-    assert call_fwd(flags=8, o=BASE + 3 * MB + 512)[0] == 6      # past it: checks pass (no device here)
+    assert call_fwd(flags=8, o=BASE + 3 * MB + 512)[0] == HIP     # past it: checks pass (no device here)
     assert call_fwd(flags=0, o=BASE + 3 * MB + 512)[0] == 4      # per-channel alpha is larger
     assert call_fwd_gather(flags=8)[0] == 3
 
@@ -241,7 +255,7 @@ def test_bwd_workspace_size():
 @pytest.mark.parametrize("kw,status", [
     (dict(q=None), 1), (dict(do=None), 1), (dict(dq=None), 1), (dict(da=None), 1),
     (dict(T=-1), 2), (dict(dk=48), 3), (dict(dtype=3), 3),
-    (dict(ws=None), 5), (dict(wsb=1024), 5),
+    (dict(ws=None), WS), (dict(wsb=1024), WS),
     (dict(dq=BASE + 2), 2),
     (dict(dq=BASE + 1 * MB), 4),                 # dq overlaps k
     (dict(dv=BASE + 8 * MB + 64), 4),            # dv overlaps dq
@@ -269,7 +283,7 @@ def test_bwd_ex_workspace_size():
 
 @pytest.mark.parametrize("kw,status", [
     (dict(flags=16), 7),                                   # unknown flag bit
-    (dict(flags=7, wsb=4096), 5),                          # too small for the prologue's fp32 copies
+    (dict(flags=7, wsb=4096), WS),                         # too small for the prologue's fp32 copies
     (dict(flags=7, q=None), 1),
     (dict(flags=7, dq=BASE + 1 * MB), 4),                  # dq overlaps k
     (dict(flags=1, da=BASE + 3 * MB + 512), 4),            # per-channel alpha (16 KB) overlaps dalpha ...
@@ -316,7 +330,7 @@ def _call_dp2_bwd(**kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(da=None), 1),                          # a gated call needs dalpha
     (dict(T=-1), 2), (dict(T=1 << 30), 2),
-    (dict(wsb=4096), 5),                         # too small
+    (dict(wsb=4096), WS),                       # too small
     (dict(dq=BASE + 1 * MB, wsb=64 * MB), 4),    # dq overlaps k (2 T sub-steps of keys)
     (dict(dk=BASE + 9 * MB + 4, wsb=64 * MB), 2),
 ])
