@@ -6,6 +6,9 @@
 // matrix-core A operands of the state pass as 1 KB fragments (64 lanes x 16
 // bytes, K order of ckda_device.hpp), each operand indexed [row tile][K block]:
 //   TB  [C x C]  = (I + Diag(beta) A)^-1 Diag(beta)    the UT/WY triangular solve
+//   TBL [C x C]  = TB - bf16(TB), rounded to bf16      (bf16 records only: TB as
+//                  a hi + lo pair, about 16 significant bits, for the state pass's
+//                  U = TB X, which sits on the state's chunk-to-chunk chain)
 //   M   [C x C]  = causal (incl. diagonal) decayed query-key products
 //   W   [C x DK] = -(K . gamma)      gamma_t: signed gate product from the chunk start to t
 //   Q   [C x DK] =   Q . gamma
@@ -49,12 +52,15 @@ struct ChunkGeom {
     return n + kb;
   }
   static constexpr int NF_T = tri_index(RT, 0);     // stored fragments of TB (and of M)
+  static constexpr bool SPLIT = sizeof(T) == 2;     // TB kept as hi + lo (bf16 records)
+  static constexpr int NF_TL = SPLIT ? NF_T : 0;    // fragments of TBL
   static constexpr int NF_W = RT * KBN;             // fragments of W (and of Q)
   static constexpr int NF_KR = RH * KBC;            // fragments of KR
   static constexpr int NF_D = (DK * 4 + 1023) / 1024;
-  static constexpr int NFR = 2 * NF_T + 2 * NF_W + NF_KR + NF_D;
+  static constexpr int NFR = 2 * NF_T + NF_TL + 2 * NF_W + NF_KR + NF_D;
   static constexpr size_t T_OFF = 0;
-  static constexpr size_t M_OFF = T_OFF + NF_T * FRAG;
+  static constexpr size_t TL_OFF = T_OFF + NF_T * FRAG;
+  static constexpr size_t M_OFF = TL_OFF + NF_TL * FRAG;
   static constexpr size_t W_OFF = M_OFF + NF_T * FRAG;
   static constexpr size_t Q_OFF = W_OFF + NF_W * FRAG;
   static constexpr size_t KR_OFF = Q_OFF + NF_W * FRAG;

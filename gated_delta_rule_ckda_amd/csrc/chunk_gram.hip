@@ -692,15 +692,17 @@ __global__ __launch_bounds__((GramCfg<T, DK, C>::NTH)) void chunk_gram_kernel(
     lds_barrier();
   }
 
-  // ---- record: T Diag(beta) and M fragments
+  // ---- record: T Diag(beta) (bf16: as hi and lo parts) and M fragments
   constexpr int NF = RT * KBC;
-  constexpr int NEW = (2 * NF + NW - 1) / NW;   // fragments per wave, unrolled
+  constexpr int NSETS = P::SPLIT ? 3 : 2;       // TB, M (, TBL)
+  constexpr int NEW = (NSETS * NF + NW - 1) / NW;   // fragments per wave, unrolled
 #pragma unroll
   for (int j = 0; j < NEW; ++j) {
     const int f = wave + NW * j;
-    if (f >= 2 * NF) break;
-    const bool isT = f < NF;
-    const int ff = isT ? f : f - NF;
+    if (f >= NSETS * NF) break;
+    const int set = f / NF;                     // 0: TB, 1: M, 2: TBL
+    const bool isT = set != 1;
+    const int ff = f - set * NF;
     const int rt = ff / KBC, kb = ff % KBC;
     if (!P::tri_live(rt, kb)) continue;   // all zero, not stored
     const float* src = (isT ? Ts : Ms) + (16 * rt + r) * LD;
@@ -721,10 +723,12 @@ __global__ __launch_bounds__((GramCfg<T, DK, C>::NTH)) void chunk_gram_kernel(
     if constexpr (sizeof(T) == 2) {
       out.w = u32x4{pack_bf16x2(vals[0], vals[1]), pack_bf16x2(vals[2], vals[3]), pack_bf16x2(vals[4], vals[5]),
                     pack_bf16x2(vals[6], vals[7])};
+      if (set == 2) out = frag_residual_bf16(vals, out);   // TB - bf16(TB), rounded
     } else {
       out.w = __builtin_bit_cast(u32x4, f32x4{vals[0], vals[1], vals[2], vals[3]});
     }
-    store_frag_stream(rec + (isT ? P::T_OFF : P::M_OFF) + ((size_t)P::tri_index(rt, kb) * 64 + lane) * 16, out);
+    const size_t off = set == 0 ? P::T_OFF : set == 1 ? P::M_OFF : P::TL_OFF;
+    store_frag_stream(rec + off + ((size_t)P::tri_index(rt, kb) * 64 + lane) * 16, out);
   }
 }
 

@@ -16,7 +16,11 @@
 // the K order of ckda_device.hpp the accumulator tiles of one product are,
 // converted element-wise, the B operand of the next (H for X and O, X for U,
 // U for O and H), so the matrix waves exchange nothing.  The decay of H is
-// applied element-wise in fp32; the state itself is never rounded.
+// applied element-wise in fp32; the state itself is never rounded.  With bf16
+// operands the products that carry the state from chunk to chunk (W H, TB X,
+// KR^T U) multiply split bf16 pairs for H, X, U and TB (hi + lo, about 16
+// significant bits), so that the state keeps close to fp32 accuracy over long
+// runs of undamped steps; the read-out products take the hi parts only.
 //
 // Every operand of a chunk but the values is state-independent and sits in
 // the chunk's record (chunk_gram.hip).  Four "copy waves" move the records and
@@ -129,6 +133,7 @@ __global__ __launch_bounds__((StateCfg<T, DK, C, NMW>::NTHREADS)) void chunk_sta
       // as many: no read-ahead there, to stay within the register file.)
       constexpr int DB = BF ? 2 : 1;
       Frag wf[DB][KBN], qf[DB][KBN], tf[RT][KBC], mf[RT][KBC];
+      Frag tl[BF ? RT : 1][KBC];   // TB lo parts (bf16)
       auto ld_wq = [&](int pt) __attribute__((always_inline)) {
 #pragma unroll
         for (int kb = 0; kb < KBN; ++kb) {
@@ -171,16 +176,28 @@ __global__ __launch_bounds__((StateCfg<T, DK, C, NMW>::NTHREADS)) void chunk_sta
 #pragma unroll
         for (int pt = 0; pt < RT; ++pt) ld_v(pt);
       }
-      Frag hb[KBN];
+      // The products on the state's chain from chunk to chunk (W H, TB X and
+      // KR^T U) take their state-dependent B operands H, X and U, and TB, as
+      // split bf16 pairs (hi + lo, ckda_device.hpp): with plain bf16 operands
+      // each of these roundings alone left errors near 2e-2 after 64 chunks of
+      // orthogonal steps (beta = 2, alpha = +-1), where nothing damps them.
+      // W, KR and the read-out operands Q~ and M stay single bf16.
+      Frag hb[KBN], hl[BF ? KBN : 1];
 #pragma unroll
-      for (int kb = 0; kb < KBN; ++kb) hb[kb] = bfrag(hacc, kb, RH);
+      for (int kb = 0; kb < KBN; ++kb) {
+        if constexpr (BF) frags_from_acc_bf16_split(hacc[2 * kb], 2 * kb + 1 < RH ? hacc[2 * kb + 1] : zero4(), hb[kb], hl[kb]);
+        else hb[kb] = bfrag(hacc, kb, RH);
+      }
       // X = V + W H, O = Q~ H
       if constexpr (DB == 2) ld_wq(0);
 #pragma unroll
       for (int pt = 0; pt < RT; ++pt) {
         if constexpr (DB == 2) {
           if (pt + 1 < RT) ld_wq(pt + 1);
-          else ld_tm(tf, S::T_OFF);
+          else {
+            ld_tm(tf, S::T_OFF);
+            if constexpr (BF) ld_tm(tl, S::TL_OFF);
+          }
         } else {
           ld_wq(pt);
           ld_v(pt);
@@ -190,6 +207,7 @@ __global__ __launch_bounds__((StateCfg<T, DK, C, NMW>::NTHREADS)) void chunk_sta
 #pragma unroll
         for (int kb = 0; kb < KBN; ++kb) {
           xacc[pt] = mma<T>(xacc[pt], wf[pt % DB][kb], hb[kb]);
+          if constexpr (BF) xacc[pt] = mma<T>(xacc[pt], wf[pt % DB][kb], hl[kb]);
           oacc[pt] = mma<T>(oacc[pt], hb[kb], qf[pt % DB][kb]);   // O^T: H^T Q~^T
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -198,23 +216,35 @@ __global__ __launch_bounds__((StateCfg<T, DK, C, NMW>::NTHREADS)) void chunk_sta
       if constexpr (DB == 2) ld_tm(mf, S::M_OFF);
       __builtin_amdgcn_sched_barrier(0);
       // U = TB X
-      Frag xb[KBC];
+      Frag xb[KBC], xl[BF ? KBC : 1];
 #pragma unroll
-      for (int kb = 0; kb < KBC; ++kb) xb[kb] = bfrag(xacc, kb, RT);
+      for (int kb = 0; kb < KBC; ++kb) {
+        if constexpr (BF) frags_from_acc_bf16_split(xacc[2 * kb], 2 * kb + 1 < RT ? xacc[2 * kb + 1] : zero4(), xb[kb], xl[kb]);
+        else xb[kb] = bfrag(xacc, kb, RT);
+      }
       f32x4 uacc[RT];
 #pragma unroll
       for (int pt = 0; pt < RT; ++pt) {
         uacc[pt] = zero4();
 #pragma unroll
         for (int kb = 0; kb < KBC; ++kb)
-          if (!upper(pt, kb)) uacc[pt] = mma<T>(uacc[pt], tf[pt][kb], xb[kb]);
+          if (!upper(pt, kb)) {
+            uacc[pt] = mma<T>(uacc[pt], tf[pt][kb], xb[kb]);
+            if constexpr (BF) {
+              uacc[pt] = mma<T>(uacc[pt], tf[pt][kb], xl[kb]);
+              uacc[pt] = mma<T>(uacc[pt], tl[pt][kb], xb[kb]);
+            }
+          }
       }
       if constexpr (DB == 1) ld_tm(mf, S::M_OFF);
       ld_kr(0);
       __builtin_amdgcn_sched_barrier(0);
-      Frag ub[KBC];
+      Frag ub[KBC], ul[BF ? KBC : 1];
 #pragma unroll
-      for (int kb = 0; kb < KBC; ++kb) ub[kb] = bfrag(uacc, kb, RT);
+      for (int kb = 0; kb < KBC; ++kb) {
+        if constexpr (BF) frags_from_acc_bf16_split(uacc[2 * kb], 2 * kb + 1 < RT ? uacc[2 * kb + 1] : zero4(), ub[kb], ul[kb]);
+        else ub[kb] = bfrag(uacc, kb, RT);
+      }
       // lane (g, r) holds O^T rows 4 g .. 4 g + 3 of column r: four consecutive
       // value columns of output row 16 pt + r.  With bf16 operands the outputs
       // are stored last, when their products have long completed (fp32 stores
@@ -243,7 +273,10 @@ __global__ __launch_bounds__((StateCfg<T, DK, C, NMW>::NTHREADS)) void chunk_sta
           const int rh = grp * RHG + j;
           f32x4 hh = dd[grp & 1][j] * hacc[rh];
 #pragma unroll
-          for (int kb = 0; kb < KBC; ++kb) hh = mma<T>(hh, kf[grp & 1][j][kb], ub[kb]);
+          for (int kb = 0; kb < KBC; ++kb) {
+            hh = mma<T>(hh, kf[grp & 1][j][kb], ub[kb]);
+            if constexpr (BF) hh = mma<T>(hh, kf[grp & 1][j][kb], ul[kb]);
+          }
           hacc[rh] = hh;
         }
         __builtin_amdgcn_sched_barrier(0);

@@ -159,6 +159,26 @@ __device__ __forceinline__ Frag frag_from_acc_bf16(f32x4 lo, f32x4 hi) {
   f.w[3] = pack_bf16x2(hi[2], hi[3]);
   return f;
 }
+// Split bf16 operands.  A value x is carried as hi = bf16(x) and
+// lo = bf16(x - hi) (x - hi is exact in fp32), about 16 significant bits in
+// all; a product then takes the partial products hi.hi, hi.lo and lo.hi,
+// whose sum differs from the fp32 product by about 2^-16 relative.
+__device__ __forceinline__ float bf16_lo_half(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi_half(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+// The lo fragment of 8 values v whose hi fragment (same K order) is `hi`.
+__device__ __forceinline__ Frag frag_residual_bf16(const float* v, Frag hi) {
+  Frag f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    f.w[i] = pack_bf16x2(v[2 * i] - bf16_lo_half(hi.w[i]), v[2 * i + 1] - bf16_hi_half(hi.w[i]));
+  return f;
+}
+// hi and lo B fragments of the K block covered by accumulator tiles lo, hi.
+__device__ __forceinline__ void frags_from_acc_bf16_split(f32x4 lo, f32x4 hi, Frag& fh, Frag& fl) {
+  fh = frag_from_acc_bf16(lo, hi);
+  const float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  fl = frag_residual_bf16(v, fh);
+}
 __device__ __forceinline__ Frag frag_from_acc_f32(f32x4 t) {
   Frag f;
   f.w = __builtin_bit_cast(u32x4, t);

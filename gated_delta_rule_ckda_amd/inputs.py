@@ -105,6 +105,10 @@ def _gates(rng, law: str, shape_a, shape_b):
         # beta = 2 and alpha in {-1, +1}: every transition is orthogonal.
         a = np.where(rng.integers(0, 2, size=shape_a) == 0, -1.0, 1.0).astype(np.float32)
         b = np.full(shape_b, 2.0, np.float32)
+    elif law == "mild_overrange":
+        # Range violation: |alpha| up to 1.25 (outside the CKDA range), beta ~ U[0, 2].
+        a = rng.uniform(-1.25, 1.25, size=shape_a).astype(np.float32)
+        b = rng.uniform(0.0, 2.0, size=shape_b).astype(np.float32)
     elif law == "small_gates":
         # Stress law: |alpha| spread log-uniformly down to 1e-12 with random signs.
         mag = np.exp(rng.uniform(np.log(1e-12), 0.0, size=shape_a)).astype(np.float32)
@@ -127,21 +131,35 @@ def _to(x: np.ndarray, dtype: str) -> torch.Tensor:
     return t.to(torch_dtype(dtype)).contiguous()
 
 
-def make_inputs(w: Workload, repeated_keys: bool = False):
+def make_inputs(w: Workload, repeated_keys: bool = False, keys: str = "normal", values: str = "normal"):
     """Return dict(q, k, v, alpha, beta, h0) of CPU torch tensors for workload w.
 
     q, k, v, alpha, beta are in w.dtype; h0 is float32 [B,H,dk,dv] or None.
-    repeated_keys: stress option, every token of a head reuses one key
-    (worst conditioning of the intra-chunk triangular system).
+    Stress options (the same random draws, transformed):
+      repeated_keys / keys="repeated": every token of a head reuses one key
+        (worst conditioning of the intra-chunk triangular system);
+      keys="near_parallel": token t's key is normalise(k_0 + 1e-3 k_t) with
+        the head's first draw k_0 and its own draw k_t (distinct, nearly
+        parallel unit keys);
+      values="zero": v = 0 (with beta = 2 and alpha = +-1 every step is then
+        an orthogonal map of the state, which keeps its Frobenius norm).
     """
     rng = np.random.default_rng(w.seed)
     B, H, T, dk, dv = w.B, w.H, w.T, w.dk, w.dv
     q = rng.standard_normal((B, H, T, dk), dtype=np.float32)
     k = rng.standard_normal((B, H, T, dk), dtype=np.float32)
-    if repeated_keys:
+    if repeated_keys or keys == "repeated":
         k = np.broadcast_to(k[:, :, :1, :], k.shape).copy()
+    elif keys == "near_parallel":
+        k = k[:, :, :1, :] + np.float32(1e-3) * k
+    elif keys != "normal":
+        raise ValueError(f"unknown key law {keys!r}")
     k = _normalise(k)
     v = rng.standard_normal((B, H, T, dv), dtype=np.float32)
+    if values == "zero":
+        v = np.zeros_like(v)
+    elif values != "normal":
+        raise ValueError(f"unknown value law {values!r}")
     a, b = _gates(rng, w.gates, (B, H, T, dk), (B, H, T))
     if w.h0 == "normal":
         h0 = torch.from_numpy(np.float32(0.1) * rng.standard_normal((B, H, dk, dv), dtype=np.float32))

@@ -55,14 +55,15 @@ extern "C" {
 
 typedef enum { CKDA_DTYPE_F32 = 0, CKDA_DTYPE_BF16 = 1 } ckda_dtype_t;
 
+/* Codes 0-5 are the boundary's original set; codes added later follow them. */
 typedef enum {
   CKDA_OK = 0,
   CKDA_ERR_NULL = 1,        /* a required pointer is NULL */
   CKDA_ERR_DIM = 2,         /* a size is negative or inconsistent */
   CKDA_ERR_UNSUPPORTED = 3, /* valid but not supported (dtype, d_k, d_v, chunk) */
   CKDA_ERR_ALIAS = 4,       /* an output overlaps an input it may not overlap */
-  CKDA_ERR_WORKSPACE = 5,   /* workspace missing, too small or misaligned */
-  CKDA_ERR_HIP = 6,         /* the HIP runtime reported an error at launch */
+  CKDA_ERR_HIP = 5,         /* the HIP runtime reported an error at launch */
+  CKDA_ERR_WORKSPACE = 6,   /* workspace missing, too small or misaligned */
   CKDA_ERR_FLAGS = 7        /* flags hold bits outside CKDA_FUSE_* / CKDA_GATE_SCALAR */
 } ckda_status_t;
 
@@ -102,9 +103,9 @@ typedef enum {
  * the sizes are invalid or unsupported (ckda_chunk_fwd then reports why).
  * The workspace holds, per chunk of every (batch, head), the operands the
  * state pass consumes (see ckda_chunk_fwd): the blocks on or below the
- * diagonal of two chunk x chunk lower-triangular matrices, 3*chunk*d_k
- * elements of dtype and d_k floats, in whole 1 KB blocks (bf16, chunk 64,
- * d_k 128: 61 KB per chunk). */
+ * diagonal of two chunk x chunk lower-triangular matrices (for bf16 one of
+ * them twice, as a hi and a lo part), 3*chunk*d_k elements of dtype and d_k
+ * floats, in whole 1 KB blocks (bf16, chunk 64, d_k 128: 67 KB per chunk). */
 size_t ckda_chunk_fwd_workspace_size(int B, int H, int T, int dk, int dv, int chunk, int dtype);
 
 /* Chunkwise-parallel forward over a whole sequence for every (batch, head).

@@ -4,6 +4,9 @@ the exact bytes handed to the GPU, and case logging.
 Metric (per output tensor): for every (batch, head) slice, max |x - y| divided
 by max |y| of that slice; the reported error is the maximum over slices.
 Tolerances: 1e-4 for fp32 inputs, 2e-2 for bf16 inputs (fp32 states).
+Logged beside it, for information: the elementwise relative error
+|x - y| / max(|y|, 1e-3 max|y|), the floor taken per slice, maximised over
+all elements.
 """
 from __future__ import annotations
 
@@ -37,6 +40,33 @@ def slice_rel_err(x, y) -> float:
     if not np.all(np.isfinite(num)):
         return float("inf")
     return float(np.max(num / den))
+
+
+def elem_rel_err(x, y, floor=1e-3) -> float:
+    """max over all elements of |x - y| / max(|y|, floor * max|y| of the
+    element's (batch, head) slice)."""
+    x = np.asarray(x, np.float64)
+    y = np.asarray(y, np.float64)
+    assert x.shape == y.shape, (x.shape, y.shape)
+    lead = x.shape[:2]
+    xs = x.reshape(int(np.prod(lead)), -1)
+    ys = y.reshape(int(np.prod(lead)), -1)
+    fl = floor * np.max(np.abs(ys), axis=1, keepdims=True)
+    den = np.maximum(np.abs(ys), fl)
+    den = np.where(den == 0, 1.0, den)
+    e = np.abs(xs - ys) / den
+    if not np.all(np.isfinite(e)):
+        return float("inf")
+    return float(np.max(e)) if e.size else 0.0
+
+
+def errs(x, y) -> tuple:
+    """(slice_rel_err, elem_rel_err) of x against y."""
+    return slice_rel_err(x, y), elem_rel_err(x, y)
+
+
+def fmt(name, e) -> str:
+    return f"{name}={e[0]:.3e} (elem {e[1]:.3e})"
 
 
 def oracle_fwd(inp, heads=None):
