@@ -27,7 +27,8 @@ STATUS = {0: "CKDA_OK", 1: "CKDA_ERR_NULL", 2: "CKDA_ERR_DIM", 3: "CKDA_ERR_UNSU
 (ERR_NULL, ERR_DIM, ERR_UNSUPPORTED, ERR_ALIAS, ERR_HIP, ERR_WORKSPACE, ERR_FLAGS) = range(1, 8)
 FUSE_GATES, FUSE_NORM_K, FUSE_NORM_Q = 1, 2, 4       # CKDA_FUSE_*
 GATE_SCALAR = 8                                      # CKDA_GATE_SCALAR
-EXPORTS = ("ckda_chunk_fwd_workspace_size", "ckda_chunk_fwd", "ckda_chunk_fwd_timed", "ckda_chunk_fwd_ex",
+EXPORTS = ("ckda_chunk_fwd_workspace_size", "ckda_chunk_fwd", "ckda_chunk_fwd_noalloc", "ckda_chunk_fwd_timed",
+           "ckda_chunk_fwd_ex",
            "ckda_chunk_fwd_gather", "ckda_decode_step", "ckda_decode_step_ex", "ckda_decode_step_gather",
            "ckda_deltaproduct2_fwd", "ckda_deltaproduct2_decode_step", "ckda_chunk_bwd",
            "ckda_chunk_bwd_workspace_size", "ckda_chunk_bwd_ex", "ckda_chunk_bwd_ex_workspace_size",
@@ -56,6 +57,8 @@ def lib() -> ctypes.CDLL:
         L.ckda_chunk_fwd_workspace_size.restype = sz
         L.ckda_chunk_fwd.argtypes = [vp] * 8 + [i] * 7 + [vp, sz, vp]
         L.ckda_chunk_fwd.restype = i
+        L.ckda_chunk_fwd_noalloc.argtypes = [vp] * 8 + [i] * 7 + [vp]
+        L.ckda_chunk_fwd_noalloc.restype = i
         L.ckda_chunk_fwd_timed.argtypes = [vp] * 8 + [i] * 7 + [vp, sz, vp, vp, vp, vp]
         L.ckda_chunk_fwd_timed.restype = i
         L.ckda_chunk_fwd_ex.argtypes = [vp] * 8 + [i] * 8 + [vp, sz, vp]
@@ -220,6 +223,27 @@ def chunk_fwd(q, k, v, alpha, beta, h0=None, chunk=64, workspace=None, o=None, h
     else:
         handles = [None if e is None else ctypes.c_void_p(e.cuda_event) for e in events]
         _check(lib().ckda_chunk_fwd_timed(*args, *handles))
+    return o, hT
+
+
+def chunk_fwd_noalloc(q, k, v, alpha, beta, h0, o, hT=None, chunk=64, stream=None):
+    """ckda_chunk_fwd_noalloc: the chunkwise forward with no workspace and no
+    allocation (for callers that cannot allocate, e.g. under graph capture).
+    The caller passes the outputs o [B,H,T,dv] and hT [B,H,dk,dv] fp32 (or
+    None).  Calls that overlap in time on one GPU share its fixed scratch and
+    race; calls on one stream are safe.  Returns (o, hT)."""
+    B, H, T, dk = _dims(q, 4, "q")
+    dv = _dims(v, 4, "v")[-1]
+    if o is None:
+        raise ValueError("o is required (this entry point allocates nothing)")
+    _shapes(dict(k=(k, (B, H, T, dk)), v=(v, (B, H, T, dv)), alpha=(alpha, (B, H, T, dk)), beta=(beta, (B, H, T)),
+                 h0=(h0, (B, H, dk, dv)), o=(o, (B, H, T, dv)), hT=(hT, (B, H, dk, dv))))
+    _require(dict(q=q, k=k, v=v, alpha=alpha, beta=beta, o=o), q.dtype)
+    for name, t in (("h0", h0), ("hT", hT)):
+        if t is not None:
+            _require({name: t}, torch.float32)
+    _check(lib().ckda_chunk_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(h0), _ptr(o),
+                                        _ptr(hT), B, H, T, dk, dv, chunk, _dtype_code(q), _stream(stream)))
     return o, hT
 
 

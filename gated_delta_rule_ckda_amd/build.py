@@ -17,7 +17,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libckda.so")
-SOURCES = ["ckda_api.cpp", "decode.hip", "chunk_gram.hip", "chunk_state.hip", "chunk_bwd.hip", "prologue_bwd.hip", "dp2_bwd.hip"]
+SOURCES = ["ckda_api.cpp", "decode.hip", "chunk_gram.hip", "chunk_state.hip", "chunk_bwd.hip", "prologue_bwd.hip", "dp2_bwd.hip",
+           "noalloc.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",

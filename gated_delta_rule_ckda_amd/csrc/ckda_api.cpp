@@ -96,7 +96,8 @@ size_t ckda_chunk_fwd_workspace_size(int B, int H, int T, int dk, int dv, int ch
 static int chunk_fwd_impl(const char* fn, const void* q, const void* k, const void* v, const void* alpha,
                           const void* beta, const float* h0, void* o, float* hT, int B, int H, int T, int dk, int dv,
                           int chunk, int dtype, int flags, void* workspace, size_t workspace_bytes, void* stream,
-                          void* const ev[3], const int* gidx = nullptr, int dk_in = 0, bool prod2 = false) {
+                          void* const ev[3], const int* gidx = nullptr, int dk_in = 0, bool prod2 = false,
+                          bool check_only = false) {
   if ((flags & ~kFlagsAll) != 0)
     return fail(CKDA_ERR_FLAGS, "%s: flags 0x%x has bits outside CKDA_FUSE_* and CKDA_GATE_SCALAR (0x%x)", fn, flags,
                 kFlagsAll);
@@ -134,7 +135,7 @@ static int chunk_fwd_impl(const char* fn, const void* q, const void* k, const vo
   const size_t head_records = (((size_t)rows + chunk - 1) / chunk) * ckda::chunk_record_layout(dk, chunk, dtype).bytes;
   if (head_records > (size_t)INT32_MAX)
     return fail(CKDA_ERR_DIM, "%s: T=%d too long: one head's chunk records must stay below 2 GiB", fn, T);
-  if (T > 0) {
+  if (T > 0 && !check_only) {
     if (!workspace) return fail(CKDA_ERR_WORKSPACE, "%s: workspace is NULL", fn);
     if (workspace_bytes < need)
       return fail(CKDA_ERR_WORKSPACE, "%s: workspace of %zu bytes, need %zu", fn, workspace_bytes, need);
@@ -153,7 +154,7 @@ static int chunk_fwd_impl(const char* fn, const void* q, const void* k, const vo
                       range("idx", gidx, gidx ? (size_t)H * dk * 4 : 0)};
   const Range ro = range("o", o, T ? no * es : 0);
   const Range rh = range("hT", hT, hT ? ns * 4 : 0);
-  const Range rw = range("workspace", workspace, T ? need : 0);
+  const Range rw = range("workspace", workspace, T && !check_only ? need : 0);
   for (const Range& r : in) {
     if (overlap(ro, r)) return fail(CKDA_ERR_ALIAS, "%s: o overlaps %s", fn, r.name);
     if (overlap(rw, r)) return fail(CKDA_ERR_ALIAS, "%s: workspace overlaps %s", fn, r.name);
@@ -163,6 +164,8 @@ static int chunk_fwd_impl(const char* fn, const void* q, const void* k, const vo
   if (overlap(ro, rh)) return fail(CKDA_ERR_ALIAS, "%s: o overlaps hT", fn);
   if (overlap(rw, ro) || overlap(rw, rh))
     return fail(CKDA_ERR_ALIAS, "%s: workspace overlaps an output", fn);
+
+  if (check_only) return ok();
 
   ckda::ChunkArgs a{q, k, v, alpha, beta, h0, o, hT, B, H, rows, dk, dv, chunk, dtype,
                     flags | (prod2 ? ckda::kProd2 : 0), workspace,
@@ -180,6 +183,46 @@ int ckda_chunk_fwd(const void* q, const void* k, const void* v, const void* alph
   void* const none[3] = {nullptr, nullptr, nullptr};
   return chunk_fwd_impl("ckda_chunk_fwd", q, k, v, alpha, beta, h0, o, hT, B, H, T, dk, dv, chunk, dtype, 0, workspace,
                         workspace_bytes, stream, none);
+}
+
+int ckda_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const void* alpha,
+                           const void* beta, const float* h0, void* o, float* hT,
+                           int B, int H, int T, int dk, int dv, int chunk, int dtype, void* stream) {
+  const char* fn = "ckda_chunk_fwd_noalloc";
+  void* const none[3] = {nullptr, nullptr, nullptr};
+  // every argument check of ckda_chunk_fwd, on the whole problem
+  const int st = chunk_fwd_impl(fn, q, k, v, alpha, beta, h0, o, hT, B, H, T, dk, dv, chunk, dtype, 0, nullptr, 0,
+                                stream, none, nullptr, 0, false, true);
+  if (st != CKDA_OK) return st;
+  const size_t BH = (size_t)B * H;
+  if (BH == 0 || (T == 0 && !hT)) return ok();
+  // one head's chunk records must fit the scratch; heads then run in batches
+  // that fill it, one Gram + state-pass launch pair per batch, in order on
+  // `stream` (records of one batch are consumed before the next overwrites them)
+  const size_t per_head = ckda_chunk_fwd_workspace_size(1, 1, T, dk, dv, chunk, dtype);
+  if (per_head > ckda::kNoallocScratchBytes)
+    return fail(CKDA_ERR_WORKSPACE,
+                "%s: T=%d needs %zu bytes of chunk records per head, more than the %zu-byte built-in scratch", fn, T,
+                per_head, ckda::kNoallocScratchBytes);
+  void* scr = nullptr;
+  hipError_t e = ckda::noalloc_scratch(&scr);
+  if (e != hipSuccess) return fail(CKDA_ERR_HIP, "%s: scratch lookup failed: %s", fn, hipGetErrorString(e));
+  const size_t batch = ckda::kNoallocScratchBytes / per_head;
+  const size_t es = dtype_bytes(dtype);
+  const unsigned char *qb = (const unsigned char*)q, *kb = (const unsigned char*)k, *vb = (const unsigned char*)v,
+                      *ab = (const unsigned char*)alpha, *bb = (const unsigned char*)beta;
+  for (size_t f0 = 0; f0 < BH; f0 += batch) {
+    const size_t nb = BH - f0 < batch ? BH - f0 : batch;
+    const size_t rows = f0 * (size_t)T;   // first token row of the batch
+    ckda::ChunkArgs a{T ? qb + rows * dk * es : nullptr, T ? kb + rows * dk * es : nullptr,
+                      T ? vb + rows * dv * es : nullptr, T ? ab + rows * dk * es : nullptr,
+                      T ? bb + rows * es : nullptr, h0 ? h0 + f0 * dk * dv : nullptr,
+                      T ? (unsigned char*)o + rows * dv * es : nullptr, hT ? hT + f0 * dk * dv : nullptr,
+                      1, (int)nb, T, dk, dv, chunk, dtype, 0, scr, (hipStream_t)stream, {nullptr, nullptr, nullptr}};
+    e = ckda::launch_chunk_fwd(a);
+    if (e != hipSuccess) return fail(CKDA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  }
+  return ok();
 }
 
 int ckda_chunk_fwd_ex(const void* q, const void* k, const void* v, const void* alpha,

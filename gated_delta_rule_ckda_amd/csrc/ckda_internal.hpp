@@ -72,4 +72,9 @@ hipError_t launch_dp2_bwd(const BwdArgs& a);
 hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_chunk_fwd(const ChunkArgs& a);
 
+// Size of the fixed device scratch of ckda_chunk_fwd_noalloc (noalloc.hip),
+// and its device address on the current device (looked up on first use).
+constexpr size_t kNoallocScratchBytes = (size_t)64 << 20;
+hipError_t noalloc_scratch(void** ptr);
+
 }  // namespace ckda

@@ -143,6 +143,26 @@ int ckda_chunk_fwd(const void* q, const void* k, const void* v, const void* alph
                    int B, int H, int T, int dk, int dv, int chunk, int dtype,
                    void* workspace, size_t workspace_bytes, void* stream);
 
+/* ckda_chunk_fwd for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same arguments without the workspace, the same checks and results.
+ * The chunk records live in the library's one fixed device buffer, 64 MiB
+ * per GPU, held from the first call on that GPU until the process ends; the
+ * call itself allocates nothing.  Heads run in batches that fill the buffer
+ * (one Gram and one state-pass launch per batch, in order on `stream`).
+ *
+ * Limit: one head's records (ckda_chunk_fwd_workspace_size(1, 1, T, dk, dv,
+ * chunk, dtype) bytes; bf16, chunk 64, d_k 128: about 1.05 KB per position,
+ * T <= 62,000) must fit the buffer, else CKDA_ERR_WORKSPACE.
+ *
+ * All calls on one GPU share its buffer: calls that overlap in time on one
+ * GPU (different streams, or different host threads) race and corrupt each
+ * other's results; calls on one stream are ordered and safe.  Errors as
+ * ckda_chunk_fwd (CKDA_ERR_HIP if the buffer's address cannot be found). */
+int ckda_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const void* alpha,
+                           const void* beta, const float* h0, void* o, float* hT,
+                           int B, int H, int T, int dk, int dv, int chunk, int dtype, void* stream);
+
 /* ckda_chunk_fwd with timing marks, for measurement: identical arguments,
  * checks and results, and in addition each non-NULL event (a hipEvent_t the
  * caller created on the current device) is recorded on `stream` -- ev_start
