@@ -39,7 +39,7 @@ METRIC = "CKDA chunkwise fwd tokens/s (B4 H16 T4096 d128, %MFMA) + decode state 
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--steps", type=int, default=100)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--decode-steps", type=int, default=128)
     p.add_argument("--workload", default="ckda_bf16",
@@ -47,6 +47,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--skip-extras", action="store_true",
                    help="headline forward and decode only (for counter runs)")
+    p.add_argument("--protocol-trials", type=int, default=3,
+                   help="trials of 100 calls for the median-of-medians timing (0: skip, for counter runs)")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="about this much oracle work for the CPU baseline (whole-workload passes)")
     return p.parse_args()
@@ -83,6 +85,63 @@ def traffic_from_profile(kernel):
     if not m_sha or not m_b or m_sha.group(1) != sha:
         return None
     return int(m_b.group(1))
+
+
+def counters_from_profile(name, kernels):
+    """Executed matrix-core figures per kernel from a committed counter summary
+    (profiles/<name>.md: lines `kernel <name> mfma_busy_frac <x>`), or None
+    when any listed kernel's source changed after the counters were taken."""
+    import hashlib
+    import re
+    path = os.path.join(ROOT, "profiles", f"{name}.md")
+    try:
+        text = open(path).read()
+    except OSError:
+        return None
+    out = {}
+    for k in kernels:
+        src = os.path.join(ROOT, "gated_delta_rule_ckda_amd", "csrc",
+                           {"chunk_gram_kernel": "chunk_gram.hip", "chunk_state_kernel": "chunk_state.hip"}[k])
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        m_sha = re.search(rf"{k} source sha256: `([0-9a-f]{{64}})`", text)
+        m_v = re.search(rf"kernel {k} mfma_busy_frac ([0-9.]+)", text)
+        if not m_sha or not m_v or m_sha.group(1) != sha:
+            return None
+        out[k] = float(m_v.group(1))
+    return out
+
+
+def trial_medians(fn, stream, trials=3, calls=100, warmup=10):
+    """The pages' timing protocol (the state-reduction slides: 10 warm-ups,
+    100 measured steps, median of 3 trials): HIP events on `stream` around
+    each call, the median per trial, then the median of the trial medians (ms)."""
+    import numpy as np
+    import torch
+    if trials <= 0:
+        return None, []
+    for _ in range(warmup):
+        fn()
+    meds = []
+    for _ in range(trials):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
+        torch.cuda.synchronize()
+        for e0, e1 in evs:
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        meds.append(float(np.median([e0.elapsed_time(e1) for e0, e1 in evs])))
+    return float(np.median(meds)), meds
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def fwd_algorithmic(w):
@@ -180,6 +239,17 @@ def main():
     torch.cuda.synchronize()
     graph_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in gev]))
     del graph
+    # Timed region 4: the pages' protocol (3 trials of 100 calls after 10
+    # warm-ups, median of the trial medians), per-call events
+    log("[bench] protocol timing: 3 trials x 100 calls")
+    proto_ms, proto_trials = trial_medians(step, stream, trials=a.protocol_trials)
+    # This very output on two sampled heads (the heads are independent
+    # recurrences), kept for the comparison with the oracle in the CPU leg
+    step()
+    torch.cuda.synchronize()
+    heads = [0, w.B * w.H - 1]
+    sel = lambda t: t.reshape(w.B * w.H, *t.shape[2:])[heads].unsqueeze(1).contiguous()
+    gpu_sample = (sel(o.float().cpu()).numpy(), sel(hT.cpu()).numpy())
     call_ms = float(np.mean(per_call_ms))
     call_ms_median = float(np.median(per_call_ms))
     kern_ms = {"chunk_gram_kernel": float(np.mean(gram_ms)), "chunk_state_kernel": float(np.mean(state_ms))}
@@ -206,6 +276,16 @@ def main():
         x = dsteps[s % 8]
         ck.decode_step(x["q"], x["k"], x["v"], x["alpha"], x["beta"], S, o=do)
 
+    # one step on sampled states: the states before and after and the output,
+    # kept for the comparison with the oracle in the CPU leg
+    ds_idx = [0, 4099, dec.N * dec.H - 1]
+    S_flat = S.view(dec.N * dec.H, dec.dk, dec.dv)
+    dsel = lambda t: t.reshape(dec.N * dec.H, *t.shape[2:])[ds_idx].unsqueeze(1).contiguous()
+    S_before = S_flat[ds_idx].double().cpu().numpy()[:, None].copy()
+    dstep(0)
+    torch.cuda.synchronize()
+    dec_sample = (S_before, {n: dsel(dsteps[0][n]).cpu() for n in ("q", "k", "v", "alpha", "beta")},
+                  dsel(do.float()).cpu().numpy(), S_flat[ds_idx].unsqueeze(1).cpu().numpy())
     for s in range(a.warmup):
         dstep(s)
     torch.cuda.synchronize()
@@ -220,6 +300,7 @@ def main():
     dwall = time.perf_counter() - t1
     dms = [e0.elapsed_time(e1) for e0, e1 in dev_ev]
     dec_ms = float(np.mean(dms))
+    dec_proto_ms, dec_proto_trials = trial_medians(lambda: dstep(0), stream, trials=a.protocol_trials)
     state_bytes = dec.N * dec.H * dec.dk * dec.dv * 4 * 2
     io_bytes = dec.N * dec.H * (3 * dec.dk + 2 * dec.dv + 1) * 2
     dec_gbs_state = state_bytes / (dec_ms * 1e-3) / 1e9
@@ -452,7 +533,11 @@ def main():
                             "algorithmic_GB_s": round(kbytes[k] / (kern_ms[k] * 1e-3) / 1e9, 1),
                             "record_bytes": record_bytes,
                             "traffic": traffic_from_profile(k)} for k in kern_ms},
+            "mfma_executed_busy_frac": counters_from_profile("chunk_fwd_ckda_bf16_mfma_counters",
+                                                             ["chunk_gram_kernel", "chunk_state_kernel"]),
             "forward": {"call_ms_mean": round(call_ms, 4), "call_ms_median": round(call_ms_median, 4),
+                        "protocol_ms_median_of_3x100": None if proto_ms is None else round(proto_ms, 4),
+                        "protocol_trial_medians_ms": [round(x, 4) for x in proto_trials],
                         "graph_replay_ms_mean": round(graph_ms, 4),
                         "algorithmic_bytes": nbytes, "algorithmic_GB_s": round(achieved_gbs, 1),
                         "frac_of_hbm_peak": round(achieved_gbs / HBM_PEAK_GBS, 4),
@@ -462,6 +547,7 @@ def main():
         "decode": {
             "workload": dec.name, "steps": a.decode_steps,
             "ms_per_step_events": round(dec_ms, 4),
+            "protocol_ms_median_of_3x100": None if dec_proto_ms is None else round(dec_proto_ms, 4),
             "ms_per_step_wall": round(dwall * 1e3 / a.decode_steps, 4),
             "state_GB_s": round(dec_gbs_state, 1),
             "total_GB_s": round(dec_gbs_total, 1),
@@ -487,10 +573,40 @@ def main():
             oracle.fwd(*args, h0=h0)
         passes += more
         csec = time.perf_counter() - c0
+        # one thread on one (batch, head), extrapolated to the B*H heads; the
+        # sampled heads' results also check the GPU output measured above
+        one = [raw(sel(inp[n])[:1]) for n in ("q", "k", "v", "alpha", "beta")]
+        h01 = None if inp["h0"] is None else raw(sel(inp["h0"])[:1])
+        c1 = time.perf_counter()
+        oracle.fwd(*one, h0=h01, nthreads=1)
+        one_s = time.perf_counter() - c1
+        ro, rh = oracle.fwd(*[raw(sel(inp[n])) for n in ("q", "k", "v", "alpha", "beta")],
+                            h0=None if inp["h0"] is None else raw(sel(inp["h0"])))
+
+        def rel(x, y):
+            x = np.asarray(x, np.float64).reshape(x.shape[0], -1)
+            y = np.asarray(y, np.float64).reshape(y.shape[0], -1)
+            return float(np.max(np.max(np.abs(x - y), 1) / np.maximum(np.max(np.abs(y), 1), 1e-300)))
+
+        S_ref = dec_sample[0].copy()
+        d_ref = oracle.decode(*[raw(dec_sample[1][n]) for n in ("q", "k", "v", "alpha", "beta")], S_ref)
+        parity = {"metric": "per sampled head: max|gpu - oracle| / max|oracle|, the maximum over the heads",
+                  "forward": {"workload": w.name, "heads": heads, "o_rel_err": rel(gpu_sample[0], ro),
+                              "hT_rel_err": rel(gpu_sample[1], rh),
+                              "tolerance": 2e-2 if w.dtype == "bf16" else 1e-4},
+                  "decode": {"workload": dec.name, "states": ds_idx, "steps": 1,
+                             "o_rel_err": rel(dec_sample[2], d_ref), "state_rel_err": rel(dec_sample[3], S_ref),
+                             "tolerance": 2e-2}}
         out["cpu_baseline"] = {"value": round(passes * w.B * w.T / csec, 1), "unit": "tokens/s", "cores": nt,
                                "kind": "oracle",
                                "sample": f"the whole {w.name} forward ({w.B * w.H} heads x {w.T} positions) "
-                                         f"{passes} times, {csec:.1f} s"}
+                                         f"{passes} times, {csec:.1f} s",
+                               "cpu_model": cpu_model(), "nproc": os.cpu_count(),
+                               "one_thread": {"seconds_one_head": round(one_s, 4),
+                                              "extrapolated_tokens_per_s": round(w.B * w.T / (one_s * w.B * w.H), 1),
+                                              "sample": f"one head x {w.T} positions, 1 thread, "
+                                                        f"extrapolated x{w.B * w.H} heads"},
+                               "parity_of_this_run": parity}
     print(json.dumps(out), flush=True)
     return 0
 
