@@ -58,6 +58,8 @@ def _declare(lib):
     lib.ckda_oracle_bwd.restype = i
     lib.ckda_oracle_prologue_bwd.argtypes = [vp, vp, vp, vp, i, i, ctypes.c_longlong, i] + [vp] * 8
     lib.ckda_oracle_prologue_bwd.restype = i
+    lib.ckda_oracle_deltaproduct2_bwd.argtypes = [vp] * 5 + [i, vp, i, vp, vp, i] + [vp] * 6 + [i] * 6
+    lib.ckda_oracle_deltaproduct2_bwd.restype = i
     return lib
 
 
@@ -309,15 +311,53 @@ def deltaproduct2(q, k, v, alpha, beta, h0=None, nthreads=0):
 
 def deltaproduct2_bwd(q, k, v, alpha, beta, do, dhT=None, h0=None, nthreads=0):
     """Gradients of deltaproduct2() for L with dL/do = do [B,H,T,dv] and
-    dL/dH_T = dhT.  DeltaProduct_2 is two delta-rule updates per token (paper
-    Fig. 5 and Sec. 6; the gated form scales the state by the token's scalar
-    gate first, App. C): the delta rule over 2 T sub-steps, sub-step 2 t with
-    the gate alpha_t on every channel, sub-step 2 t + 1 ungated, and only the
-    odd sub-steps read out (with q_t).  So this is bwd() on that sequence:
-    queries repeated, gates [alpha_t, 1], upstream gradient [0, do_t]; then
-    dq_t sums its two sub-steps and dalpha_t the channels of its gate.
-    Returns fp64 (dq, dk [B,H,T,2,dk], dv [B,H,T,2,dv], dalpha [B,H,T] or
-    None, dbeta [B,H,T,2], dh0)."""
+    dL/dH_T = dhT (ckda_oracle_deltaproduct2_bwd: the adjoint of the token
+    step, two Householder writes after the scalar gate, differentiated line
+    by line in reverse).  Inputs as deltaproduct2(); do and dhT float32 or
+    float64 (one dtype).  Returns fp64 (dq, dk [B,H,T,2,dk], dv [B,H,T,2,dv],
+    dalpha [B,H,T] or None, dbeta [B,H,T,2], dh0)."""
+    q, k, v, beta = (np.ascontiguousarray(x) for x in (q, k, v, beta))
+    alpha = None if alpha is None else np.ascontiguousarray(alpha)
+    code = _code(q)
+    for x in (k, v, beta) + (() if alpha is None else (alpha,)):
+        if _code(x) != code:
+            raise TypeError("inputs must share one dtype")
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    if k.shape != (B, H, T, 2, dk) or v.shape != (B, H, T, 2, dv) or beta.shape != (B, H, T, 2) \
+            or (alpha is not None and alpha.shape != (B, H, T)):
+        raise ValueError("inconsistent shapes")
+    do = np.ascontiguousarray(do)
+    gcode = _code(do)
+    if do.shape != (B, H, T, dv) or gcode == BF16:
+        raise ValueError("do must be float32/float64 [B,H,T,dv]")
+    dhTc = None
+    if dhT is not None:
+        dhTc = np.ascontiguousarray(dhT)
+        if dhTc.shape != (B, H, dk, dv) or _code(dhTc) != gcode:
+            raise ValueError("dhT must be [B,H,dk,dv] in do's dtype")
+    h0c, h0code = None, F32
+    if h0 is not None:
+        h0c = np.ascontiguousarray(h0)
+        h0code = _code(h0c)
+    out = [np.empty((B, H, T, dk)), np.empty((B, H, T, 2, dk)), np.empty((B, H, T, 2, dv)),
+           np.empty((B, H, T)) if alpha is not None else None, np.empty((B, H, T, 2)), np.empty((B, H, dk, dv))]
+    rc = _load().ckda_oracle_deltaproduct2_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), code, _ptr(h0c),
+                                               h0code, _ptr(do), _ptr(dhTc), gcode, *(_ptr(x) for x in out), B, H, T,
+                                               dk, dv, int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"ckda_oracle_deltaproduct2_bwd failed with code {rc}")
+    return tuple(out)
+
+
+def deltaproduct2_bwd_substeps(q, k, v, alpha, beta, do, dhT=None, h0=None, nthreads=0):
+    """The same gradients by a second route, kept as a cross-check of
+    deltaproduct2_bwd(): DeltaProduct_2 is the delta rule over 2 T sub-steps
+    (sub-step 2 t with the gate alpha_t on every channel, sub-step 2 t + 1
+    ungated, only the odd sub-steps read out, with q_t), so bwd() on that
+    sequence (queries repeated, gates [alpha_t, 1], upstream gradient
+    [0, do_t]), then dq_t sums its two sub-steps and dalpha_t the channels of
+    its gate.  Returns what deltaproduct2_bwd() returns."""
     B, H, T, dk = np.shape(q)
     dv = np.shape(v)[-1]
     q2 = np.repeat(_widen(q), 2, axis=2)

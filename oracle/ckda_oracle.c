@@ -524,3 +524,166 @@ int ckda_oracle_bwd(const void* q, const void* k, const void* v, const void* alp
   }
   return failed ? 4 : 0;
 }
+
+/* ---------------------------------------------------------------- DeltaProduct_2 backward
+ *
+ * Reverse-mode derivative of ckda_oracle_deltaproduct2 for a loss L with
+ * dL/do_t = do and dL/dH_T = dhT, written from the token step itself (not by
+ * way of the delta-rule backward above).  Per token, forward:
+ *
+ *   Hb = alpha_t H_{t-1}                        (Hb = H_{t-1} when ungated)
+ *   e1 = v_t1 - Hb^T k_t1,   Hm = Hb + beta_t1 k_t1 e1^T
+ *   e2 = v_t2 - Hm^T k_t2,   H_t = Hm + beta_t2 k_t2 e2^T
+ *   o_t = H_t^T q_t
+ *
+ * and in reverse, with G = dL/dH_t carried from the end of the sequence:
+ *
+ *   dq = H_t do                    G += q do^T
+ *   de2 = beta2 G^T k2             dbeta2 = k2^T G e2      dv2 = de2
+ *   dk2 = beta2 G e2 - Hm de2      dHm = G - k2 de2^T
+ *   de1 = beta1 dHm^T k1           dbeta1 = k1^T dHm e1    dv1 = de1
+ *   dk1 = beta1 dHm e1 - Hb de1    dHb = dHm - k1 de1^T
+ *   dalpha = <dHb, H_{t-1}>        G <- alpha dHb
+ *
+ * States are kept at checkpoints every 64 tokens and recomputed one segment
+ * at a time.  Layouts as the forward: q, dq [B,H,T,dk]; k, dk [B,H,T,2,dk];
+ * v, dv [B,H,T,2,dv]; beta, dbeta [B,H,T,2]; alpha, dalpha [B,H,T] (alpha
+ * NULL: ungated, dalpha not written); do [B,H,T,dv] and dhT [B,H,dk,dv] in
+ * g_dtype (either may be NULL: zero); dh0 [B,H,dk,dv]. */
+int ckda_oracle_deltaproduct2_bwd(const void* q, const void* k, const void* v, const void* alpha, const void* beta,
+                                  int dtype, const void* h0, int h0_dtype, const void* dout, const void* dhT,
+                                  int g_dtype, double* dq, double* dk, double* dv_, double* dalpha, double* dbeta,
+                                  double* dh0, int B, int H, int T, int dk_, int dv, int nthreads) {
+  if (!q || !k || !v || !beta || !dq || !dk || !dv_ || !dbeta || !dh0 || (alpha && !dalpha)) return 1;
+  if (B < 0 || H < 0 || T < 0 || dk_ <= 0 || dv <= 0) return 2;
+  if (!valid_dtype(dtype) || (h0 && !valid_dtype(h0_dtype)) || !valid_dtype(g_dtype)) return 3;
+  const int n = dk_, seg = 64;
+  const long long NS = (long long)n * dv;
+  const long long BH = (long long)B * H;
+  int failed = 0;
+#ifdef _OPENMP
+  int nt = nthreads > 0 ? nthreads : omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : failed) num_threads(nt)
+#else
+  (void)nthreads;
+#endif
+  for (long long bh = 0; bh < BH; ++bh) {
+    const int nseg = (T + seg - 1) / seg;
+    double* ck = (double*)malloc(sizeof(double) * (size_t)NS * (nseg + 1));   /* state at each segment start */
+    double* st = (double*)malloc(sizeof(double) * (size_t)NS * (seg + 1));    /* states inside one segment */
+    double* work = (double*)malloc(sizeof(double) * (size_t)NS * 4);          /* G, Hb, Hm, Ht */
+    /* k1, k2, q, (3 n spare), v1, v2, e1, e2, do, de1, de2, then the forward step's scratch (2 n + 3 dv) */
+    double* buf = (double*)malloc(sizeof(double) * (size_t)(8 * n + 12 * dv));
+    if (!ck || !st || !work || !buf) {
+      free(ck); free(st); free(work); free(buf);
+      failed |= 1;
+      continue;
+    }
+    double *G = work, *Hb = G + NS, *Hm = Hb + NS, *Ht = Hm + NS;
+    double *k1 = buf, *k2 = k1 + n, *qq = k2 + n, *tmp = qq + n;
+    double *v1 = tmp + 3 * n, *v2 = v1 + dv, *e1 = v2 + dv, *e2 = e1 + dv, *gd = e2 + dv, *de1 = gd + dv,
+           *de2 = de1 + dv, *w = de2 + dv;
+    const long long sbase = bh * NS;
+    /* forward: checkpoints */
+    for (long long e = 0; e < NS; ++e) ck[e] = h0 ? widen(h0, sbase + e, h0_dtype) : 0.0;
+    for (int g = 0; g < nseg; ++g) {
+      double* S = ck + (long long)(g + 1) * NS;
+      memcpy(S, ck + (long long)g * NS, sizeof(double) * NS);
+      for (int t = g * seg; t < T && t < (g + 1) * seg; ++t) dp2_token(S, q, k, v, alpha, beta, dtype, bh * T + t, n, dv, w, NULL);
+    }
+    /* reverse */
+    for (long long e = 0; e < NS; ++e) G[e] = dhT ? widen(dhT, sbase + e, g_dtype) : 0.0;
+    for (int g = nseg - 1; g >= 0; --g) {
+      const int t0 = g * seg, t1 = (t0 + seg < T) ? t0 + seg : T;
+      memcpy(st, ck + (long long)g * NS, sizeof(double) * NS);
+      for (int t = t0; t < t1; ++t) {
+        double* S = st + (long long)(t - t0 + 1) * NS;
+        memcpy(S, S - NS, sizeof(double) * NS);
+        dp2_token(S, q, k, v, alpha, beta, dtype, bh * T + t, n, dv, w, NULL);
+      }
+      for (int t = t1 - 1; t >= t0; --t) {
+        const long long tok = bh * T + t;
+        const double* Hp = st + (long long)(t - t0) * NS;   /* H_{t-1} */
+        const double a = alpha ? widen(alpha, tok, dtype) : 1.0;
+        const double b1 = widen(beta, tok * 2, dtype), b2 = widen(beta, tok * 2 + 1, dtype);
+        for (int i = 0; i < n; ++i) {
+          k1[i] = widen(k, (tok * 2) * n + i, dtype);
+          k2[i] = widen(k, (tok * 2 + 1) * n + i, dtype);
+          qq[i] = widen(q, tok * n + i, dtype);
+        }
+        for (int j = 0; j < dv; ++j) {
+          v1[j] = widen(v, (tok * 2) * dv + j, dtype);
+          v2[j] = widen(v, (tok * 2 + 1) * dv + j, dtype);
+          gd[j] = dout ? widen(dout, tok * dv + j, g_dtype) : 0.0;
+        }
+        /* recompute Hb, e1, Hm, e2, H_t */
+        for (long long e = 0; e < NS; ++e) Hb[e] = a * Hp[e];
+        for (int j = 0; j < dv; ++j) {
+          double s = 0.0;
+          for (int i = 0; i < n; ++i) s += Hb[(long)i * dv + j] * k1[i];
+          e1[j] = v1[j] - s;
+        }
+        for (int i = 0; i < n; ++i)
+          for (int j = 0; j < dv; ++j) Hm[(long)i * dv + j] = Hb[(long)i * dv + j] + b1 * k1[i] * e1[j];
+        for (int j = 0; j < dv; ++j) {
+          double s = 0.0;
+          for (int i = 0; i < n; ++i) s += Hm[(long)i * dv + j] * k2[i];
+          e2[j] = v2[j] - s;
+        }
+        for (int i = 0; i < n; ++i)
+          for (int j = 0; j < dv; ++j) Ht[(long)i * dv + j] = Hm[(long)i * dv + j] + b2 * k2[i] * e2[j];
+        /* o_t = H_t^T q */
+        for (int i = 0; i < n; ++i) {
+          double acc = 0.0;
+          for (int j = 0; j < dv; ++j) acc += Ht[(long)i * dv + j] * gd[j];
+          dq[tok * n + i] = acc;
+          for (int j = 0; j < dv; ++j) G[(long)i * dv + j] += qq[i] * gd[j];
+        }
+        /* second write: H_t = Hm + beta2 k2 e2^T */
+        double db2 = 0.0;
+        for (int j = 0; j < dv; ++j) {
+          double acc = 0.0;
+          for (int i = 0; i < n; ++i) acc += G[(long)i * dv + j] * k2[i];
+          de2[j] = b2 * acc;
+          db2 += acc * e2[j];
+          dv_[(tok * 2 + 1) * dv + j] = de2[j];
+        }
+        for (int i = 0; i < n; ++i) {
+          double acc = 0.0;
+          for (int j = 0; j < dv; ++j) acc += b2 * G[(long)i * dv + j] * e2[j] - Hm[(long)i * dv + j] * de2[j];
+          dk[(tok * 2 + 1) * n + i] = acc;
+        }
+        for (int i = 0; i < n; ++i)
+          for (int j = 0; j < dv; ++j) G[(long)i * dv + j] -= k2[i] * de2[j];   /* now dHm */
+        /* first write: Hm = Hb + beta1 k1 e1^T */
+        double db1 = 0.0;
+        for (int j = 0; j < dv; ++j) {
+          double acc = 0.0;
+          for (int i = 0; i < n; ++i) acc += G[(long)i * dv + j] * k1[i];
+          de1[j] = b1 * acc;
+          db1 += acc * e1[j];
+          dv_[(tok * 2) * dv + j] = de1[j];
+        }
+        for (int i = 0; i < n; ++i) {
+          double acc = 0.0;
+          for (int j = 0; j < dv; ++j) acc += b1 * G[(long)i * dv + j] * e1[j] - Hb[(long)i * dv + j] * de1[j];
+          dk[(tok * 2) * n + i] = acc;
+        }
+        dbeta[tok * 2] = db1;
+        dbeta[tok * 2 + 1] = db2;
+        for (int i = 0; i < n; ++i)
+          for (int j = 0; j < dv; ++j) G[(long)i * dv + j] -= k1[i] * de1[j];   /* now dHb */
+        /* gate: Hb = alpha H_{t-1} */
+        double ga = 0.0;
+        for (long long e = 0; e < NS; ++e) {
+          ga += G[e] * Hp[e];
+          G[e] *= a;
+        }
+        if (alpha) dalpha[tok] = ga;
+      }
+    }
+    memcpy(dh0 + sbase, G, sizeof(double) * NS);
+    free(ck); free(st); free(work); free(buf);
+  }
+  return failed ? 4 : 0;
+}

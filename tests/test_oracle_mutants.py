@@ -77,6 +77,18 @@ MUTANTS = {
                                        "n * dy[t * dk + i]")],
     "pbwd_norm_radial_power": [("n * dy[t * dk + i] - n * n * n * widen(x, t * dk + i, dtype) * xdy",
                                 "n * dy[t * dk + i] - n * widen(x, t * dk + i, dtype) * xdy")],
+    # DeltaProduct_2 backward (the adjoint of the token step)
+    "dp2bwd_dk2_without_state_term": [
+        ("          for (int j = 0; j < dv; ++j) acc += b2 * G[(long)i * dv + j] * e2[j] - Hm[(long)i * dv + j] * de2[j];",
+         "          for (int j = 0; j < dv; ++j) acc += b2 * G[(long)i * dv + j] * e2[j];")],
+    "dp2bwd_dk1_with_first_write_state": [
+        ("          for (int j = 0; j < dv; ++j) acc += b1 * G[(long)i * dv + j] * e1[j] - Hb[(long)i * dv + j] * de1[j];",
+         "          for (int j = 0; j < dv; ++j) acc += b1 * G[(long)i * dv + j] * e1[j] - Hm[(long)i * dv + j] * de1[j];")],
+    "dp2bwd_dhm_sign": [("          for (int j = 0; j < dv; ++j) G[(long)i * dv + j] -= k2[i] * de2[j];   /* now dHm */",
+                         "          for (int j = 0; j < dv; ++j) G[(long)i * dv + j] += k2[i] * de2[j];   /* now dHm */")],
+    "dp2bwd_gate_not_carried": [("          G[e] *= a;\n        }\n        if (alpha) dalpha[tok] = ga;",
+                                 "        }\n        if (alpha) dalpha[tok] = ga;")],
+    "dp2bwd_dalpha_on_gated_state": [("          ga += G[e] * Hp[e];", "          ga += G[e] * Hb[e];")],
     "dp2_value_not_corrected": [("    for (int j = 0; j < dv; ++j) S[(long)i * dv + j] += b * kk[i] * (vv[j] - w[j]);",
                                  "    for (int j = 0; j < dv; ++j) S[(long)i * dv + j] += b * kk[i] * vv[j];")],
 }
@@ -112,6 +124,8 @@ PIN_CALLS = [
     lambda o: ppins.test_gate_slope_closed_form_and_zero_subgradient(o),
     lambda o: ppins.test_normalisation_backward_is_tangent(o),
     lambda o: ppins.test_fused_backward_matches_finite_differences(o, False),
+    lambda o: ppins.test_deltaproduct2_backward_matches_finite_differences(o, True),
+    lambda o: ppins.test_deltaproduct2_backward_matches_finite_differences(o, False),
 ]
 
 

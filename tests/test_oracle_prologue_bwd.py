@@ -145,10 +145,69 @@ def test_fused_backward_matches_finite_differences(oracle_lib, scalar, flags=7):
             assert abs(fd - g[ix]) <= 1e-6 * max(1.0, abs(fd)), (scalar, name, ix, fd, g[ix])
 
 
+def dp2_problem(seed, gated, B=1, H=2, T=6, dk=3, dv=2):
+    r = RNG(seed)
+    q = r.standard_normal((B, H, T, dk))
+    k = r.standard_normal((B, H, T, 2, dk))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = r.standard_normal((B, H, T, 2, dv))
+    a = r.uniform(-1, 1, (B, H, T)) if gated else None
+    b = r.uniform(0, 2, (B, H, T, 2))
+    h0 = 0.3 * r.standard_normal((B, H, dk, dv))
+    do = r.standard_normal((B, H, T, dv))
+    dhT = r.standard_normal((B, H, dk, dv))
+    return q, k, v, a, b, h0, do, dhT
+
+
+@pytest.mark.parametrize("gated", [True, False])
+@pytest.mark.parametrize("T,dk,dv", [(6, 3, 2), (5, 2, 4)])
+def test_deltaproduct2_backward_agrees_with_the_substep_route(oracle_lib, gated, T, dk, dv):
+    """The adjoint of the token step (deltaproduct2_bwd) and the delta-rule
+    backward over the 2 T sub-steps (deltaproduct2_bwd_substeps, through the
+    pinned bwd()) are two separate constructions of the same gradients."""
+    q, k, v, a, b, h0, do, dhT = dp2_problem(40 + T + gated, gated, T=T, dk=dk, dv=dv)
+    g1 = oracle_lib.deltaproduct2_bwd(q, k, v, a, b, do, dhT=dhT, h0=h0)
+    import oracle as orc
+    g2 = orc.deltaproduct2_bwd_substeps(q, k, v, a, b, do, dhT=dhT, h0=h0)
+    for x, y in zip(g1, g2):
+        if x is None:
+            assert y is None
+        else:
+            np.testing.assert_allclose(x, y, rtol=1e-11, atol=1e-11)
+
+
+def test_deltaproduct2_backward_across_checkpoints_and_without_optional_terms(oracle_lib):
+    """70 tokens (two checkpoint segments), no h0 and no dhT, dk > dv."""
+    q, k, v, a, b, _, do, _ = dp2_problem(77, True, T=70, dk=5, dv=2)
+    g = oracle_lib.deltaproduct2_bwd(q, k, v, a, b, do)
+    import oracle as orc
+    g2 = orc.deltaproduct2_bwd_substeps(q, k, v, a, b, do)
+    for x, y in zip(g, g2):
+        np.testing.assert_allclose(x, y, rtol=1e-10, atol=1e-10)
+    # a few central differences across the segment boundary
+    o = oracle_lib
+
+    def loss():
+        out, _ = o.deltaproduct2(q, k, v, a, b)
+        return float(np.sum(out * do))
+
+    h = 1e-6
+    for name, x, gx, ix in (("a", a, g[3], (0, 1, 63)), ("k", k, g[1], (0, 0, 64, 1, 2)),
+                            ("v", v, g[2], (0, 1, 65, 0, 1)), ("b", b, g[4], (0, 0, 62, 1))):
+        old = x[ix]
+        x[ix] = old + h
+        lp = loss()
+        x[ix] = old - h
+        lm = loss()
+        x[ix] = old
+        fd = (lp - lm) / (2 * h)
+        assert abs(fd - gx[ix]) <= 1e-6 * max(1.0, abs(fd)), (name, ix, fd, gx[ix])
+
+
 @pytest.mark.parametrize("gated", [True, False])
 def test_deltaproduct2_backward_matches_finite_differences(oracle_lib, gated):
-    """deltaproduct2_bwd (the recurrence backward on the 2 T sub-steps) against
-    central differences of the separately written DeltaProduct_2 forward
+    """deltaproduct2_bwd (the adjoint of the token step) against central
+    differences of the separately written DeltaProduct_2 forward
     (ckda_oracle_deltaproduct2: the gate, then two Householder writes per
     token), for L = sum(o do) + sum(hT dhT), with respect to every input."""
     o = oracle_lib
