@@ -37,7 +37,7 @@ def run(w, gated, heads=None, h0=True, dhT=True):
         q, k, v, a, b, dot, h0t, gT = (pick(t) for t in (q, k, v, a, b, dot, h0t, gT))
         got = [pick(g) for g in got]
     want = oracle.deltaproduct2_bwd(raw(q), raw(k), raw(v), None if a is None else raw(a), raw(b),
-                                    oracle._widen(raw(dot)), dhT=None if gT is None else gT.numpy(),
+                                    oracle._widen(raw(dot)), dhT=None if gT is None else gT.double().numpy(),
                                     h0=None if h0t is None else raw(h0t))
     errs = {}
     for n, g, wv in zip(NAMES, got, want):
