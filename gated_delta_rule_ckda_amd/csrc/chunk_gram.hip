@@ -95,8 +95,11 @@ struct GramCfg : ChunkGeom<T, DK, C> {
   // row stride of the fp32 scratch: 272 bytes like a padded-fragment group,
   // so that every layout of the area leaves bytes 256..271 of each 272-byte
   // group unused (see pad_float)
-  static constexpr int LD = kFragGroupBytes / 4;
-  static constexpr int SCR_BYTES = 3 * C * LD * 4;      // A, M, T in fp32
+  // A, M (then T in M's place) in fp32: only the 16x16 blocks on and below
+  // the diagonal, each in a padded fragment slot (four 272-byte groups of four
+  // 64-byte rows), which leaves bytes 256..271 of every group unused
+  static constexpr int NBT = RT * (RT + 1) / 2;
+  static constexpr int SCR_BYTES = 2 * NBT * kFragPadBytes;
   // phase 0: padded fragments of W, Q~ and KR, in record order
   static constexpr int NF3 = 2 * G::NF_W + G::NF_KR;
   static constexpr int KR_AREA = 2 * G::NF_W * kFragPadBytes;
@@ -598,19 +601,21 @@ __global__ __launch_bounds__((GramCfg<T, DK, C>::NTH)) void chunk_gram_kernel(
 #undef QL
 #undef QH
 
-  // ---- A (rows scaled by beta, strictly lower) and M (lower incl.) to LDS, fp32
-  float* As = reinterpret_cast<float*>(area);
-  constexpr int LD = P::LD;
-  float* Ms = As + C * LD;
-  float* Ts = Ms + C * LD;
-  // Only the blocks on and below the diagonal are written and read; the
-  // record's blocks above the diagonal are emitted as zeros.
+  // ---- A (rows scaled by beta, strictly lower) and M (lower incl.) to LDS,
+  // fp32, blocks on and below the diagonal only (GramCfg::SCR_BYTES); M goes
+  // to the record before the solve, which then keeps T in M's blocks
+  constexpr int NBT = P::NBT, MA = 0, MM = 1, MT = 1;
+  auto sc = [&](int m, int row, int col) __attribute__((always_inline)) {
+    const int I = row >> 4, J = col >> 4;
+    return reinterpret_cast<float*>(area + (m * NBT + I * (I + 1) / 2 + J) * kFragPadBytes +
+                                    ((row & 15) >> 2) * kFragGroupBytes + (row & 3) * 64 + (col & 15) * 4);
+  };
   auto put_tile = [&](int I, int J, int kind, f32x4 acc) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = 16 * I + 4 * g + i, col = 16 * J + r;
-      if (kind == 0) As[row * LD + col] = acc[i] * *s_beta(row);
-      else Ms[row * LD + col] = acc[i];
+      if (kind == 0) *sc(MA, row, col) = acc[i] * *s_beta(row);
+      else *sc(MM, row, col) = acc[i];
     }
   };
   if constexpr (P::NPP > 0) {
@@ -636,76 +641,23 @@ __global__ __launch_bounds__((GramCfg<T, DK, C>::NTH)) void chunk_gram_kernel(
         const bool ll = lr >= 8 && r < 8;
         if (kind == 0) {
           const float a = diagq ? (r < lr ? accC[j][i] : 0.f) : (ll ? accD[j][i] : 0.f);
-          As[row * LD + col] = a * *s_beta(row);
+          *sc(MA, row, col) = a * *s_beta(row);
         } else {
-          Ms[row * LD + col] = diagq ? (r <= lr ? accC[j][i] : 0.f) : (ll ? accD[j][i] : 0.f);
+          *sc(MM, row, col) = diagq ? (r <= lr ? accC[j][i] : 0.f) : (ll ? accD[j][i] : 0.f);
         }
       }
     }
   }
   lds_barrier();
 
-  // ---- T = (I + A)^-1: diagonal 16x16 blocks by forward substitution
-  if (tid < 16 * RT) {
-    const int blk = tid >> 4, jc = tid & 15, o = 16 * blk;
-    float tcol[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      float s = (i == jc) ? 1.f : 0.f;
-      const float* arow = As + (o + i) * LD + o;
-#pragma unroll
-      for (int k4 = 0; k4 < i; k4 += 4) {
-        const f32x4 av = *reinterpret_cast<const f32x4*>(arow + k4);
-#pragma unroll
-        for (int uu = 0; uu < 4; ++uu)
-          if (k4 + uu < i) s -= av[uu] * tcol[k4 + uu];
-      }
-      tcol[i] = s;
-    }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) Ts[(o + i) * LD + o + jc] = tcol[i];
-  }
-  lds_barrier();
-
-  // ---- off-diagonal blocks by distance on fp32 matrix cores:
-  //      T_IJ = -T_II sum_{K=J}^{I-1} A_IK T_KJ
-  for (int d = 1; d < RT; ++d) {
-    for (int J = wave; J + d < RT; J += NW) {
-      const int I = J + d;
-      f32x4 s = zero4();
-      for (int K = J; K < I; ++K) {
-        const float* arow = As + (16 * I + r) * LD + 16 * K;
-        const float* tb = Ts + (16 * K) * LD + 16 * J + r;
-        Frag fa, fb;
-        fa.w = __builtin_bit_cast(u32x4, *reinterpret_cast<const f32x4*>(arow + 4 * g));
-        fb.w = __builtin_bit_cast(u32x4, f32x4{tb[(4 * g + 0) * LD], tb[(4 * g + 1) * LD], tb[(4 * g + 2) * LD],
-                                               tb[(4 * g + 3) * LD]});
-        s = mma<float>(s, fa, fb);
-      }
-      const float* trow = Ts + (16 * I + r) * LD + 16 * I;
-      Frag fa;
-      fa.w = __builtin_bit_cast(u32x4, *reinterpret_cast<const f32x4*>(trow + 4 * g));
-      const f32x4 tij = mma<float>(zero4(), fa, frag_from_acc_f32(s));
-#pragma unroll
-      for (int i = 0; i < 4; ++i) Ts[(16 * I + 4 * g + i) * LD + 16 * J + r] = -tij[i];
-    }
-    lds_barrier();
-  }
-
-  // ---- record: T Diag(beta) (bf16: as hi and lo parts) and M fragments
+  // ---- record fragments of a C x C lower-triangular matrix (set 0: T Diag(beta),
+  // 1: M, 2: the lo part of T Diag(beta), bf16 only); blocks above the diagonal
+  // are all zero and not stored
   constexpr int NF = RT * KBC;
-  constexpr int NSETS = P::SPLIT ? 3 : 2;       // TB, M (, TBL)
-  constexpr int NEW = (NSETS * NF + NW - 1) / NW;   // fragments per wave, unrolled
-#pragma unroll
-  for (int j = 0; j < NEW; ++j) {
-    const int f = wave + NW * j;
-    if (f >= NSETS * NF) break;
-    const int set = f / NF;                     // 0: TB, 1: M, 2: TBL
+  auto emit = [&](int set, int ff) __attribute__((always_inline)) {
     const bool isT = set != 1;
-    const int ff = f - set * NF;
     const int rt = ff / KBC, kb = ff % KBC;
-    if (!P::tri_live(rt, kb)) continue;   // all zero, not stored
-    const float* src = (isT ? Ts : Ms) + (16 * rt + r) * LD;
+    if (!P::tri_live(rt, kb)) return;
     float vals[8];
     // K order: elements 0-3 are 4 consecutive columns, so are 4-7 (bf16)
 #pragma unroll
@@ -713,7 +665,7 @@ __global__ __launch_bounds__((GramCfg<T, DK, C>::NTH)) void chunk_gram_kernel(
       const int col = kb * KB + kappa<T>(g, 4 * hh);
       f32x4 x = zero4();
       if (col < C && col / 16 <= rt) {
-        x = *reinterpret_cast<const f32x4*>(src + col);
+        x = *reinterpret_cast<const f32x4*>(sc(isT ? MT : MM, 16 * rt + r, col));
         if (isT) x *= *reinterpret_cast<const f32x4*>(s_beta(col));
       }
 #pragma unroll
@@ -729,6 +681,64 @@ __global__ __launch_bounds__((GramCfg<T, DK, C>::NTH)) void chunk_gram_kernel(
     }
     const size_t off = set == 0 ? P::T_OFF : set == 1 ? P::M_OFF : P::TL_OFF;
     store_frag_stream(rec + off + ((size_t)P::tri_index(rt, kb) * 64 + lane) * 16, out);
+  };
+  // M first: T takes its blocks
+#pragma unroll
+  for (int j = 0; j < (NF + NW - 1) / NW; ++j) {
+    const int f = wave + NW * j;
+    if (f < NF) emit(1, f);
+  }
+  lds_barrier();
+
+  // ---- T = (I + A)^-1: diagonal 16x16 blocks by forward substitution
+  if (tid < 16 * RT) {
+    const int blk = tid >> 4, jc = tid & 15, o = 16 * blk;
+    float tcol[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float s = (i == jc) ? 1.f : 0.f;
+#pragma unroll
+      for (int k4 = 0; k4 < i; k4 += 4) {
+        const f32x4 av = *reinterpret_cast<const f32x4*>(sc(MA, o + i, o + k4));
+#pragma unroll
+        for (int uu = 0; uu < 4; ++uu)
+          if (k4 + uu < i) s -= av[uu] * tcol[k4 + uu];
+      }
+      tcol[i] = s;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) *sc(MT, o + i, o + jc) = tcol[i];
+  }
+  lds_barrier();
+
+  // ---- off-diagonal blocks by distance on fp32 matrix cores:
+  //      T_IJ = -T_II sum_{K=J}^{I-1} A_IK T_KJ
+  for (int d = 1; d < RT; ++d) {
+    for (int J = wave; J + d < RT; J += NW) {
+      const int I = J + d;
+      f32x4 s = zero4();
+      for (int K = J; K < I; ++K) {
+        Frag fa, fb;
+        fa.w = __builtin_bit_cast(u32x4, *reinterpret_cast<const f32x4*>(sc(MA, 16 * I + r, 16 * K + 4 * g)));
+        fb.w = __builtin_bit_cast(u32x4, f32x4{*sc(MT, 16 * K + 4 * g + 0, 16 * J + r), *sc(MT, 16 * K + 4 * g + 1, 16 * J + r),
+                                               *sc(MT, 16 * K + 4 * g + 2, 16 * J + r), *sc(MT, 16 * K + 4 * g + 3, 16 * J + r)});
+        s = mma<float>(s, fa, fb);
+      }
+      Frag fa;
+      fa.w = __builtin_bit_cast(u32x4, *reinterpret_cast<const f32x4*>(sc(MT, 16 * I + r, 16 * I + 4 * g)));
+      const f32x4 tij = mma<float>(zero4(), fa, frag_from_acc_f32(s));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) *sc(MT, 16 * I + 4 * g + i, 16 * J + r) = -tij[i];
+    }
+    lds_barrier();
+  }
+
+  // ---- record: T Diag(beta) (bf16: as hi and lo parts)
+  constexpr int NTS = P::SPLIT ? 2 : 1;
+#pragma unroll
+  for (int j = 0; j < (NTS * NF + NW - 1) / NW; ++j) {
+    const int f = wave + NW * j;
+    if (f < NTS * NF) emit(f < NF ? 0 : 2, f < NF ? f : f - NF);
   }
 }
 
