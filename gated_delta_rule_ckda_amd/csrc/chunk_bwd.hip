@@ -83,10 +83,9 @@ __device__ __forceinline__ f32x4 mfma_lds(f32x4 acc, const float* a, int ai, int
 // 16 x 16 tiles spread over the waves; D(i, j) = d[i * di + j].
 // W0: the wave that takes the first tile (two products of one phase can so
 // run on different waves).
-template <bool ACC, int K, int W0 = 0>
+template <bool ACC, int K, int W0 = 0, int NW = kBThreads / 64>
 __device__ __forceinline__ void gemm_lds(float* d, int di, const float* a, int ai, int ak, const float* b, int bk,
                                          int bj, int Mr, int Nc, float scale) {
-  constexpr int NW = kBThreads / 64;
   const int wave = ((threadIdx.x >> 6) + NW - W0) % NW, lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
   const int tn = Nc / 16, tiles = (Mr / 16) * tn;
   for (int ti = wave; ti < tiles; ti += NW) {
@@ -619,35 +618,48 @@ __global__ __launch_bounds__(128) void chunk_bwd_dstates_kernel(const T* dout, c
 
 // ============================================================ grad (per chunk)
 // Unrolling of the row loops of the grad kernel's recursive halving: full
-// with dk >= 64, so that the rows' LDS reads overlap (the LDS allows one
-// workgroup per CU there, one wave per SIMD, which hides no latency); rolled
-// below, which keeps the registers of two workgroups per CU.
+// with dk >= 64, so that the rows' LDS reads overlap; rolled below, which
+// keeps the registers low.
 template <int DK>
 constexpr int kHalvUnroll = DK >= 64 ? 16 : 1;
 
-template <typename T, int DK>
-__global__ __launch_bounds__(kBThreads) void chunk_bwd_grad_kernel(
+// threads of the grad kernel: two waves per SIMD, so that one wave's LDS and
+// matrix-core latencies overlap the other's (its LDS keeps one workgroup per
+// CU at dk = 128)
+constexpr int kGThreads = 512;
+
+template <typename T, int DK, int DS>
+__global__ __launch_bounds__(kGThreads) void chunk_bwd_grad_kernel(
     const T* q, const T* k, const T* v, const T* alpha, const T* beta, const T* dout, const float* __restrict__ rec,
     const float* __restrict__ hc, const float* __restrict__ dhn, float* __restrict__ dq, float* __restrict__ dk,
     float* __restrict__ dvo, float* __restrict__ dal, float* __restrict__ dbe, int T_len, int nchunks, int dv) {
-  constexpr int C = kBC, DS = kBDS, DKP = DK + 1, CP = C + 1, DSP = DS + 1;
-  constexpr int NW = kBThreads / 64;
+  constexpr int C = kBC, DKP = DK + 1, CP = C + 1, DSP = DS + 1;
+  constexpr int NW = kGThreads / 64;
+  static_assert(DS == 16 || DS == 32, "value slices are one or two 16-column blocks");
   using R = BwdRec<DK>;
   // big area: KG, KR and the slice buffers during the value-slice loop; the
-  // accumulated dQG, dKG, dKR afterwards
-  constexpr int SLICE = 2 * DK * DSP + 6 * C * DSP;
-  constexpr int BIG = (2 * C * DKP + SLICE) > 3 * C * DKP ? (2 * C * DKP + SLICE) : 3 * C * DKP;
-  __shared__ float sq[C * DKP], sk[C * DKP], sa[C * DKP];
+  // accumulated dQG, dKG, dKR and the per-channel scratch columns afterwards
+  constexpr int SLICE = 2 * DK * DSP + 5 * C * DSP;
+  constexpr int BIG = (2 * C * DKP + SLICE) > 3 * C * DKP + C * DK ? (2 * C * DKP + SLICE) : 3 * C * DKP + C * DK;
+  // q, k and alpha in their input type (bf16 inputs are kept exactly)
+  __shared__ T sq[C * DKP], sk[C * DKP], sa[C * DKP];
   __shared__ float big[BIG];
-  __shared__ float sM[C * CP], sTB[C * CP], sT[C * CP], sS[C * CP], sdM[C * CP], sdTB[C * CP], sP[C * CP];
+  // C x C matrices; TB, T, S and P (the last four) are consumed before the
+  // halving, which keeps its scan inputs there
+  __shared__ float sCC[7 * C * CP];
+  float* sM = sCC;
+  float* sdM = sCC + C * CP;
+  float* sdTB = sCC + 2 * C * CP;
+  float* sTB = sCC + 3 * C * CP;
+  float* sT = sCC + 4 * C * CP;
+  float* sS = sCC + 5 * C * CP;
+  float* sP = sCC + 6 * C * CP;
   __shared__ float sb[C], sdb[C], sGC[DK];
-  __shared__ float sG[C * DK];   // per-channel scratch columns
   float* sKG = big;
   float* sKR = big + C * DKP;
   float* sH = big + 2 * C * DKP;
   float* sdH = sH + DK * DSP;
-  float* sV = sdH + DK * DSP;
-  float* sdO = sV + C * DSP;
+  float* sdO = sdH + DK * DSP;
   float* sX = sdO + C * DSP;
   float* sU = sX + C * DSP;
   float* sdU = sU + C * DSP;
@@ -662,11 +674,11 @@ __global__ __launch_bounds__(kBThreads) void chunk_bwd_grad_kernel(
   const float* rc = rec + (size_t)chunk * R::FLOATS;
 
   {   // all of the chunk's operand loads issued before any is stored
-    constexpr int NK = (C * DK + kBThreads - 1) / kBThreads, NC = (C * C + kBThreads - 1) / kBThreads;
+    constexpr int NK = (C * DK + kGThreads - 1) / kGThreads, NC = (C * C + kGThreads - 1) / kGThreads;
     float r0[NK], r1[NK], r2[NK], r3[NK], r4[NK], m0[NC], m1[NC], m2[NC], m3[NC];
 #pragma unroll
     for (int i = 0; i < NK; ++i) {
-      const int e = tid + i * kBThreads, t = e / DK, ch = e % DK;
+      const int e = tid + i * kGThreads, t = e / DK, ch = e % DK;
       const bool in = e < C * DK, ok = in && t < cv;
       const size_t gi = ok ? (size_t)(row0 + t) * DK + ch : 0;
       r0[i] = ld_or(q, gi, ok, 0.f);
@@ -677,7 +689,7 @@ __global__ __launch_bounds__(kBThreads) void chunk_bwd_grad_kernel(
     }
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
-      const int e = tid + i * kBThreads;
+      const int e = tid + i * kGThreads;
       const bool in = e < C * C;
       m0[i] = rc[R::MT_OFF + (in ? e : 0)];
       m1[i] = rc[R::TB_OFF + (in ? e : 0)];
@@ -686,19 +698,19 @@ __global__ __launch_bounds__(kBThreads) void chunk_bwd_grad_kernel(
     }
 #pragma unroll
     for (int i = 0; i < NK; ++i) {
-      const int e = tid + i * kBThreads;
+      const int e = tid + i * kGThreads;
       if (e < C * DK) {
         const int o = (e / DK) * DKP + e % DK;
-        sq[o] = r0[i];
-        sk[o] = r1[i];
-        sa[o] = r2[i];
+        sq[o] = from_f32<T>(r0[i]);
+        sk[o] = from_f32<T>(r1[i]);
+        sa[o] = from_f32<T>(r2[i]);
         sKG[o] = r3[i];
         sKR[o] = r4[i];
       }
     }
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
-      const int e = tid + i * kBThreads;
+      const int e = tid + i * kGThreads;
       if (e < C * C) {
         const int o = (e / C) * CP + e % C;
         sM[(e % C) * CP + e / C] = m0[i];   // the record holds M^T
@@ -724,18 +736,18 @@ __global__ __launch_bounds__(kBThreads) void chunk_bwd_grad_kernel(
   const float* hcc = hc + (size_t)chunk * DK * dv;
   const float* dhc = dhn + (size_t)chunk * DK * dv;
   // one value slice's operands, fetched into registers a slice ahead
-  constexpr int NH = (DK * DS + kBThreads - 1) / kBThreads, NV = (C * DS + kBThreads - 1) / kBThreads;
+  constexpr int NH = (DK * DS + kGThreads - 1) / kGThreads, NV = (C * DS + kGThreads - 1) / kGThreads;
   float rH[NH], rdH[NH], rV[NV], rO[NV];
   auto fetch = [&](int col0) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < NH; ++i) {
-      const int e = tid + i * kBThreads, ee = e < DK * DS ? e : 0, ii = ee / DS, j = ee % DS;
+      const int e = tid + i * kGThreads, ee = e < DK * DS ? e : 0, ii = ee / DS, j = ee % DS;
       rH[i] = hcc[(size_t)col0 * DK + ee];   // the slice's blocks, in slot order (hc_slot)
       rdH[i] = dhc[(size_t)col0 * DK + ee];
     }
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-      const int e = tid + i * kBThreads, t = e / DS, j = e % DS;
+      const int e = tid + i * kGThreads, t = e / DS, j = e % DS;
       const bool ok = e < C * DS && t < cv;
       const size_t gi = ok ? (size_t)(row0 + t) * dv + col0 + j : 0;
       rV[i] = ld_or(v, gi, ok, 0.f);
@@ -747,20 +759,21 @@ __global__ __launch_bounds__(kBThreads) void chunk_bwd_grad_kernel(
     __syncthreads();   // previous slice fully consumed (and, first time, the loads above)
 #pragma unroll
     for (int i = 0; i < NH; ++i) {
-      const int e = tid + i * kBThreads;
+      const int e = tid + i * kGThreads;
       if (e < DK * DS) {
-        // slot e holds row 16 (e / 256) + 4 ((e / 64) % 4) + e % 4, column (e / 4) % 16
-        const int o = (16 * (e / 256) + 4 * ((e / 64) % 4) + e % 4) * DSP + (e / 4) % 16;
+        // slot e of 16-column block b = e / (16 dk) holds, with l = e % (16 dk),
+        // row 16 (l / 256) + 4 ((l / 64) % 4) + l % 4, column 16 b + (l / 4) % 16
+        const int b = e / (16 * DK), l = e % (16 * DK);
+        const int o = (16 * (l / 256) + 4 * ((l / 64) % 4) + l % 4) * DSP + 16 * b + (l / 4) % 16;
         sH[o] = rH[i];
         sdH[o] = rdH[i];
       }
     }
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-      const int e = tid + i * kBThreads;
+      const int e = tid + i * kGThreads;
       if (e < C * DS) {
         const int o = (e / DS) * DSP + e % DS;
-        sV[o] = rV[i];
         sX[o] = rV[i];
         sdO[o] = rO[i];
       }
@@ -768,19 +781,19 @@ __global__ __launch_bounds__(kBThreads) void chunk_bwd_grad_kernel(
     __syncthreads();
     if (col0 + DS < dv) fetch(col0 + DS);
     // X and dU on different waves
-    gemm_lds<true, DK>(sX, DSP, sKG, DKP, 1, sH, DSP, 1, C, DS, -1.f);           // X = V - KG H
-    gemm_lds<false, C, 2>(sdU, DSP, sM, 1, CP, sdO, DSP, 1, C, DS, 1.f);         // dU = M^T dO + KR dH'
-    gemm_lds<true, DK, 2>(sdU, DSP, sKR, DKP, 1, sdH, DSP, 1, C, DS, 1.f);
+    gemm_lds<true, DK, 0, NW>(sX, DSP, sKG, DKP, 1, sH, DSP, 1, C, DS, -1.f);           // X = V - KG H
+    gemm_lds<false, C, NW / 2, NW>(sdU, DSP, sM, 1, CP, sdO, DSP, 1, C, DS, 1.f);         // dU = M^T dO + KR dH'
+    gemm_lds<true, DK, NW / 2, NW>(sdU, DSP, sKR, DKP, 1, sdH, DSP, 1, C, DS, 1.f);
     __syncthreads();
-    gemm_lds<false, C>(sU, DSP, sTB, CP, 1, sX, DSP, 1, C, DS, 1.f);             // U = TB X
-    gemm_lds<false, C, 2>(sdX, DSP, sTB, 1, CP, sdU, DSP, 1, C, DS, 1.f);        // dX = TB^T dU
+    gemm_lds<false, C, 0, NW>(sU, DSP, sTB, CP, 1, sX, DSP, 1, C, DS, 1.f);             // U = TB X
+    gemm_lds<false, C, NW / 2, NW>(sdX, DSP, sTB, 1, CP, sdU, DSP, 1, C, DS, 1.f);        // dX = TB^T dU
     if (tid < DK) {
       float acc = 0.f;
       for (int j = 0; j < DS; ++j) acc += sH[tid * DSP + j] * sdH[tid * DSP + j];
       sGC[tid] += acc;
     }
     __syncthreads();
-    for (int e = tid; e < C * DS; e += kBThreads) {
+    for (int e = tid; e < C * DS; e += kGThreads) {
       const int t = e / DS, j = e % DS;
       if (t < cv) dvo[(size_t)(row0 + t) * dv + col0 + j] = sdX[t * DSP + j];
     }
@@ -846,11 +859,11 @@ __global__ __launch_bounds__(kBThreads) void chunk_bwd_grad_kernel(
     sdb[tid] = acc;
   }
   __syncthreads();
-  for (int e = tid; e < C * C; e += kBThreads) sdTB[(e / C) * CP + e % C] *= sb[e % C];   // dT = dTB Diag(beta)
+  for (int e = tid; e < C * C; e += kGThreads) sdTB[(e / C) * CP + e % C] *= sb[e % C];   // dT = dTB Diag(beta)
   __syncthreads();
-  gemm_lds<false, C>(sP, CP, sdTB, CP, 1, sT, 1, CP, C, C, 1.f);                         // P = dT T^T
+  gemm_lds<false, C, 0, NW>(sP, CP, sdTB, CP, 1, sT, 1, CP, C, C, 1.f);                         // P = dT T^T
   __syncthreads();
-  gemm_lds<false, C>(sdTB, CP, sT, 1, CP, sP, CP, 1, C, C, -1.f);                        // dA = -T^T P
+  gemm_lds<false, C, 0, NW>(sdTB, CP, sT, 1, CP, sP, CP, 1, C, C, -1.f);                        // dA = -T^T P
   __syncthreads();
   if (tid < C) {   // strictly lower part: dbeta += rowsum(dA . S), dS = Diag(beta) dA
     const int t = tid;
@@ -867,16 +880,16 @@ __global__ __launch_bounds__(kBThreads) void chunk_bwd_grad_kernel(
 
   // ---- per channel: direct terms, gate scans, recursive halving of S and M.
   // The accumulators live in each channel's column of the (now consumed)
-  // dQG / dKG / dKR arrays: gq, gk, ga; sG is a per-channel scratch column.
+  // dQG / dKG / dKR arrays: gq, gk, ga; sg is a per-channel scratch column.
   {
-    const int ch = tid % DK, part = tid / DK;   // two threads per channel in the halving
-    auto Q = [&](int t) { return sq[t * DKP + ch]; };
-    auto K = [&](int t) { return sk[t * DKP + ch]; };
-    auto A = [&](int t) { return sa[t * DKP + ch]; };
+    const int ch = tid % DK, part = tid / DK;   // P threads per channel in the halving's scalar passes
+    auto Q = [&](int t) { return to_f32(sq[t * DKP + ch]); };
+    auto K = [&](int t) { return to_f32(sk[t * DKP + ch]); };
+    auto A = [&](int t) { return to_f32(sa[t * DKP + ch]); };
     float* gq = sdQG + ch;   // element t at gq[t * DKP]
     float* gk = sdKG + ch;
     float* ga = sdKR + ch;
-    float* sg = sG + ch;     // element t at sg[t * DK]
+    float* sg = big + 3 * C * DKP + ch;   // element t at sg[t * DK]
     if (tid < DK) {
       // sg[t] = G(C-1, t) = alpha_{t+1} ... alpha_{C-1}
       {
@@ -916,24 +929,27 @@ __global__ __launch_bounds__(kBThreads) void chunk_bwd_grad_kernel(
     }
     __syncthreads();
     // recursive halving: blocks [lo, lo + 2h), L = [lo, m], R = [m + 1, lo + 2h - 1];
-    // sg holds G(m, j) on L and G(t, m) on R.  With several blocks the two
-    // threads of a channel take alternate blocks; with one block, one takes
-    // the R rows and the other the L rows (they update disjoint positions).
-    // h is a compile-time constant per level so that the loops unroll, the
-    // row loops as kHalvUnroll says.
-    const bool on = tid < 2 * DK;
-    auto factors_R = [&](int lo, int h) __attribute__((always_inline)) {
-      float f = 1.f;
-      for (int i = 0; i < h; ++i) {
-        f *= A(lo + h + i);
-        sg[(lo + h + i) * DK] = f;
-      }
-    };
-    auto factors_L = [&](int lo, int h) __attribute__((always_inline)) {
-      float e = 1.f;
-      for (int i = h - 1; i >= 0; --i) {
-        sg[(lo + i) * DK] = e;
-        e *= A(lo + i);
+    // sg holds G(m, j) on L and G(t, m) on R.  The work items of a level are
+    // (block, side); the P threads of a channel take them in turn (R and L rows
+    // are disjoint positions).  h is a compile-time constant per level so that
+    // the loops unroll, the row loops as kHalvUnroll says.
+    constexpr int P = kGThreads / DK;
+    auto factors = [&](int lo, auto hh, bool left) __attribute__((always_inline)) {
+      constexpr int h = decltype(hh)::value;
+      if (left) {
+        float e = 1.f;
+#pragma unroll
+        for (int i = h - 1; i >= 0; --i) {
+          sg[(lo + i) * DK] = e;
+          e *= A(lo + i);
+        }
+      } else {
+        float f = 1.f;
+#pragma unroll
+        for (int i = 0; i < h; ++i) {
+          f *= A(lo + h + i);
+          sg[(lo + h + i) * DK] = f;
+        }
       }
     };
     auto rows_R = [&](int lo, auto hh) __attribute__((always_inline)) {
@@ -992,42 +1008,100 @@ __global__ __launch_bounds__(kBThreads) void chunk_bwd_grad_kernel(
     auto level = [&](auto hh) __attribute__((always_inline)) {
       constexpr int h = decltype(hh)::value;
       constexpr int nb = C / (2 * h);
-      if (on) {
-        if (nb == 1) {
-          if (part == 0) factors_R(0, h); else factors_L(0, h);
-        } else {
-          for (int b = part; b < nb; b += 2) {
-            factors_R(b * 2 * h, h);
-            factors_L(b * 2 * h, h);
+      for (int it = part; it < 2 * nb; it += P) factors((it >> 1) * 2 * h, hh, it & 1);
+      __syncthreads();
+      for (int it = part; it < 2 * nb; it += P) {
+        if (it & 1) rows_L((it >> 1) * 2 * h, hh);
+        else rows_R((it >> 1) * 2 * h, hh);
+      }
+      __syncthreads();
+    };
+    // The first level (one block: L = 0..15, R = 16..31, all 16 x 16 pairs)
+    // has its cross terms on the matrix cores for all channels at once: with
+    // k~_j = k_j G(15, j) on L and q~_t = q_t G(t, 15), k~_t = k_t G(t, 15) on R,
+    //   zm = dM[R, L] k~_L,  zs = dS[R, L] k~_L  (rows of R),
+    //   zl = dM[R, L]^T q~_R + dS[R, L]^T k~_R    (rows of L);
+    // then dq_t += G(t, 15) zm_t, dk_t += G(t, 15) zs_t, dk_j += G(15, j) zl_j,
+    // and the scans take Z_t = q_t zm_t + k_t zs_t on R and Z_j = k_j zl_j on L:
+    // on R, s from last to first, b_s = Z_s + alpha_{s+1} b_{s+1} and dalpha_s
+    // += G(s - 1, 15) b_s (1 at s = 16); on L, j from first to last, dalpha_j +=
+    // G(15, j) f and f = alpha_j f + Z_j.
+    float* Z = sCC + 3 * C * CP;   // [t][channel]: TB, T, S and P are consumed
+    static_assert(3 * C * CP + C * DK <= 7 * C * CP, "scan inputs fit in the consumed C x C arrays");
+    const float* sgall = big + 3 * C * DKP;
+    auto level16 = [&]() __attribute__((always_inline)) {
+      constexpr int h = C / 2;
+      const auto hh = std::integral_constant<int, h>{};
+      if (part < 2) factors(0, hh, part == 1);
+      __syncthreads();
+      constexpr int TJ = DK / 16;
+      for (int ti = wave; ti < 2 * TJ; ti += NW) {   // ti / TJ is uniform in a wave
+        const int J = ti % TJ, c = 16 * J + r;
+        f32x4 z0 = zero4(), z1 = zero4();
+        if (ti >= TJ) {   // rows t = 16 + r of R, contraction over L
+#pragma unroll
+          for (int st = 0; st < 4; ++st) {
+            const int t = h + r, j = 4 * st + g;
+            const float kt = to_f32(sk[j * DKP + c]) * sgall[j * DK + c];
+            z0 = __builtin_amdgcn_mfma_f32_16x16x4f32(sdM[t * CP + j], kt, z0, 0, 0, 0);
+            z1 = __builtin_amdgcn_mfma_f32_16x16x4f32(sdS[t * CP + j], kt, z1, 0, 0, 0);
+          }
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int tr = h + 4 * g + v;
+            const float fac = sgall[tr * DK + c];
+            sdQG[tr * DKP + c] += fac * z0[v];
+            sdKG[tr * DKP + c] += fac * z1[v];
+            Z[tr * DK + c] = to_f32(sq[tr * DKP + c]) * z0[v] + to_f32(sk[tr * DKP + c]) * z1[v];
+          }
+        } else {   // rows j = r of L, contraction over R
+#pragma unroll
+          for (int st = 0; st < 4; ++st) {
+            const int j = r, t = h + 4 * st + g;
+            const float fac = sgall[t * DK + c];
+            const float qt = to_f32(sq[t * DKP + c]) * fac, kt = to_f32(sk[t * DKP + c]) * fac;
+            z0 = __builtin_amdgcn_mfma_f32_16x16x4f32(sdM[t * CP + j], qt, z0, 0, 0, 0);
+            z0 = __builtin_amdgcn_mfma_f32_16x16x4f32(sdS[t * CP + j], kt, z0, 0, 0, 0);
+          }
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int jr = 4 * g + v;
+            sdKG[jr * DKP + c] += sgall[jr * DK + c] * z0[v];
+            Z[jr * DK + c] = to_f32(sk[jr * DKP + c]) * z0[v];
           }
         }
       }
       __syncthreads();
-      if (on) {
-        if (nb == 1) {
-          if (part == 0) rows_R(0, hh); else rows_L(0, hh);
-        } else {
-          for (int b = part; b < nb; b += 2) {
-            rows_R(b * 2 * h, hh);
-            rows_L(b * 2 * h, hh);
-          }
+      if (part == 1) {
+        float f = 0.f;
+#pragma unroll
+        for (int j = 0; j < h; ++j) {
+          ga[j * DKP] += sg[j * DK] * f;
+          f = A(j) * f + Z[j * DK + ch];
+        }
+      } else if (part == 0) {
+        float bsum = 0.f;
+#pragma unroll
+        for (int t = C - 1; t >= h; --t) {
+          bsum = Z[t * DK + ch] + (t + 1 < C ? A(t + 1) * bsum : 0.f);
+          ga[t * DKP] += (t > h ? sg[(t - 1) * DK] : 1.f) * bsum;
         }
       }
       __syncthreads();
     };
     static_assert(C == 32, "halving levels below assume 32-position chunks");
-    level(std::integral_constant<int, 16>{});
+    level16();
     level(std::integral_constant<int, 8>{});
     level(std::integral_constant<int, 4>{});
     level(std::integral_constant<int, 2>{});
     level(std::integral_constant<int, 1>{});
-    if (tid < DK)
-      for (int t = 0; t < cv; ++t) {
-        const size_t o = (size_t)(row0 + t) * DK + ch;
-        dq[o] = gq[t * DKP];
-        dk[o] = gk[t * DKP];
-        dal[o] = ga[t * DKP];
-      }
+    for (int e = tid; e < cv * DK; e += kGThreads) {
+      const int t = e / DK, cc = e % DK;
+      const size_t o = (size_t)(row0 + t) * DK + cc;
+      dq[o] = sdQG[t * DKP + cc];
+      dk[o] = sdKG[t * DKP + cc];
+      dal[o] = sdKR[t * DKP + cc];
+    }
   }
   if (tid < cv) dbe[row0 + tid] = sdb[tid];
 }
@@ -1051,10 +1125,16 @@ static hipError_t launch_bwd_t(const BwdArgs& a) {
   }
   hipLaunchKernelGGL((chunk_bwd_dstates_kernel<T, DK>), dim3((unsigned)(BH * nsl)), dim3(64 * kDsWaves<DK>), 0,
                      a.stream, (const T*)a.dout, a.dhT, rec, dhn, a.gh0, a.T, nch, a.dv, xcd_map);
-  if (total > 0)
-    hipLaunchKernelGGL((chunk_bwd_grad_kernel<T, DK>), dim3((unsigned)total), dim3(kBThreads), 0, a.stream,
-                       (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.alpha, (const T*)a.beta,
-                       (const T*)a.dout, rec, hc, dhn, a.gq, a.gk, a.gv, a.galpha, a.gbeta, a.T, nch, a.dv);
+  if (total > 0) {
+    // bf16 inputs free enough LDS for 32-column value slices (half the slice
+    // steps); fp32 inputs, and dv = 16, take 16 columns
+    auto grad = chunk_bwd_grad_kernel<T, DK, 16>;
+    if constexpr (std::is_same<T, bf16_t>::value)
+      if (a.dv % 32 == 0) grad = chunk_bwd_grad_kernel<T, DK, 32>;
+    hipLaunchKernelGGL(grad, dim3((unsigned)total), dim3(kGThreads), 0, a.stream, (const T*)a.q, (const T*)a.k,
+                       (const T*)a.v, (const T*)a.alpha, (const T*)a.beta, (const T*)a.dout, rec, hc, dhn, a.gq, a.gk,
+                       a.gv, a.galpha, a.gbeta, a.T, nch, a.dv);
+  }
   return hipGetLastError();
 }
 
