@@ -125,8 +125,12 @@ __device__ __forceinline__ void head_slice(int id, int nsl, int xcd_map, long lo
 }
 
 // ============================================================ prep
+// threads of the prep kernel (its LDS keeps one workgroup per CU at dk = 128;
+// two waves per SIMD hide part of each one's latencies)
+constexpr int kPThreads = 512;
+
 template <typename T, int DK>
-__global__ __launch_bounds__(kBThreads) void chunk_bwd_prep_kernel(const T* q, const T* k, const T* alpha,
+__global__ __launch_bounds__(kPThreads) void chunk_bwd_prep_kernel(const T* q, const T* k, const T* alpha,
                                                                    const T* beta, float* __restrict__ rec, int T_len,
                                                                    int nchunks) {
   constexpr int C = kBC, DKP = DK + 1, CP = C + 1;
@@ -143,11 +147,11 @@ __global__ __launch_bounds__(kBThreads) void chunk_bwd_prep_kernel(const T* q, c
   const long long row0 = bh * (long long)T_len + t0;
   // rows past a ragged end are identity steps: gate 1, no key, query or beta
   {   // all loads issued before any is stored
-    constexpr int NK = (C * DK + kBThreads - 1) / kBThreads;
+    constexpr int NK = (C * DK + kPThreads - 1) / kPThreads;
     float r0[NK], r1[NK], r2[NK];
 #pragma unroll
     for (int i = 0; i < NK; ++i) {
-      const int e = tid + i * kBThreads, t = e / DK, ch = e % DK;
+      const int e = tid + i * kPThreads, t = e / DK, ch = e % DK;
       const bool ok = e < C * DK && t < cv;
       const size_t gi = ok ? (size_t)(row0 + t) * DK + ch : 0;
       r0[i] = ld_or(q, gi, ok, 0.f);
@@ -156,7 +160,7 @@ __global__ __launch_bounds__(kBThreads) void chunk_bwd_prep_kernel(const T* q, c
     }
 #pragma unroll
     for (int i = 0; i < NK; ++i) {
-      const int e = tid + i * kBThreads;
+      const int e = tid + i * kPThreads;
       if (e < C * DK) {
         const int o = (e / DK) * DKP + e % DK;
         sq[o] = r0[i];
@@ -166,7 +170,7 @@ __global__ __launch_bounds__(kBThreads) void chunk_bwd_prep_kernel(const T* q, c
     }
   }
   if (tid < C) sb[tid] = tid < cv ? to_f32(beta[row0 + tid]) : 0.f;
-  for (int e = tid; e < C * CP; e += kBThreads) {
+  for (int e = tid; e < C * CP; e += kPThreads) {
     sS[e] = 0.f;
     sM[e] = 0.f;
   }
@@ -210,10 +214,15 @@ __global__ __launch_bounds__(kBThreads) void chunk_bwd_prep_kernel(const T* q, c
         *reinterpret_cast<f32x4*>(rc + R::KRT_OFF + ch * C + t) = f32x4{kr[0], kr[1], kr[2], kr[3]};
     }
   }
-  if (tid < C) {   // diagonal of M (G = 1)
+  {   // diagonal of M (G = 1): kPThreads / C threads per row
+    constexpr int TPE = kPThreads / C;
+    static_assert(TPE <= 64 && DK % TPE == 0, "row groups within a wave");
+    const int t = tid / TPE, sub = tid % TPE;
     float d = 0.f;
-    for (int ch = 0; ch < DK; ++ch) d += sq[tid * DKP + ch] * sk[tid * DKP + ch];
-    sM[tid * CP + tid] = d;
+#pragma unroll
+    for (int ch = sub; ch < DK; ch += TPE) d += sq[t * DKP + ch] * sk[t * DKP + ch];
+    d = group_sum<TPE>(d);
+    if (sub == 0) sM[t * CP + t] = d;
   }
   // S and M below the diagonal by recursive halving (h a compile-time
   // constant per level, so that the channel's loops run on its registers)
@@ -240,18 +249,31 @@ __global__ __launch_bounds__(kBThreads) void chunk_bwd_prep_kernel(const T* q, c
       }
     }
     __syncthreads();
-    constexpr int nent = C * h / 2;   // (C / 2h) blocks of h x h entries
-    for (int e = tid; e < nent; e += kBThreads) {
-      const int blk = e / (h * h), w = e % (h * h);
+    // (C / 2h) blocks of h x h entries, TPE threads per entry (consecutive
+    // lanes, strided channels), partial sums reduced across the group
+    constexpr int nent = C * h / 2;
+    constexpr int TPE0 = kPThreads / nent < 1 ? 1 : kPThreads / nent;
+    constexpr int TPE = TPE0 > DK ? DK : (TPE0 > 64 ? 64 : TPE0);
+    for (int base = 0; base < nent * TPE; base += kPThreads) {
+      const int e = (base + tid) / TPE, sub = (base + tid) % TPE;
+      const bool ok = e < nent;
+      const int blk = ok ? e / (h * h) : 0, w = ok ? e % (h * h) : 0;
       const int lo = blk * 2 * h, t = lo + h + w / h, j = lo + w % h;
       float s = 0.f, mm = 0.f;
-      for (int ch = 0; ch < DK; ++ch) {
-        const float y = sy[j * DKP + ch];
-        s += sx[t * DKP + ch] * y;
-        mm += sxq[t * DKP + ch] * y;
+      if (ok) {
+#pragma unroll
+        for (int ch = sub; ch < DK; ch += TPE) {
+          const float y = sy[j * DKP + ch];
+          s += sx[t * DKP + ch] * y;
+          mm += sxq[t * DKP + ch] * y;
+        }
       }
-      sS[t * CP + j] = s;
-      sM[t * CP + j] = mm;
+      s = group_sum<TPE>(s);
+      mm = group_sum<TPE>(mm);
+      if (ok && sub == 0) {
+        sS[t * CP + j] = s;
+        sM[t * CP + j] = mm;
+      }
     }
     __syncthreads();
   };
@@ -278,7 +300,7 @@ __global__ __launch_bounds__(kBThreads) void chunk_bwd_prep_kernel(const T* q, c
     for (int i = 0; i < C; ++i) sT[i * CP + j] = tc[i];
   }
   __syncthreads();
-  for (int e = tid; e < C * C; e += kBThreads) {
+  for (int e = tid; e < C * C; e += kPThreads) {
     const int i = e / C, j = e % C;
     rc[R::MT_OFF + e] = sM[j * CP + i];
     rc[R::T_OFF + e] = sT[i * CP + j];
@@ -1118,7 +1140,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a) {
   const unsigned nsl = (unsigned)(a.dv / kBDS);
   const int xcd_map = (BH % 8 == 0) ? 1 : 0;
   if (total > 0) {
-    hipLaunchKernelGGL((chunk_bwd_prep_kernel<T, DK>), dim3((unsigned)total), dim3(kBThreads), 0, a.stream,
+    hipLaunchKernelGGL((chunk_bwd_prep_kernel<T, DK>), dim3((unsigned)total), dim3(kPThreads), 0, a.stream,
                        (const T*)a.q, (const T*)a.k, (const T*)a.alpha, (const T*)a.beta, rec, a.T, nch);
     hipLaunchKernelGGL((chunk_bwd_states_kernel<T, DK>), dim3((unsigned)(BH * nsl)), dim3(64), 0, a.stream,
                        (const T*)a.v, a.h0, rec, hc, a.T, nch, a.dv, xcd_map);
