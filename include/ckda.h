@@ -136,8 +136,19 @@ size_t ckda_chunk_fwd_workspace_size(int B, int H, int T, int dk, int dv, int ch
  * and the unit lower-triangular (UT/WY) solve, and writes the chunk's state-
  * independent operands to the workspace.  A state-pass kernel carries the
  * fp32 state from chunk to chunk and emits the outputs.  bf16 inputs are
- * multiplied on bf16 matrix cores with fp32 accumulation; fp32 inputs on fp32
- * matrix cores. */
+ * multiplied on bf16 matrix cores with fp32 accumulation (the state's chain
+ * from chunk to chunk with split hi + lo bf16 operands); fp32 inputs on fp32
+ * matrix cores.  The workspace argument is this entry point's one departure
+ * from a plain (inputs, outputs, sizes, stream) call: the two kernels hand
+ * the per-chunk operands over through it, and the library allocates nothing
+ * (ckda_chunk_fwd_noalloc takes the plain signature and a fixed buffer).
+ *
+ * Gate range: the paper's CKDA range is |alpha| <= 1 (App. B.2).  Gates of
+ * larger modulus are computed as given (no clamp, no error); the chunk
+ * kernels rescale by products of a chunk's gates, so results stay accurate
+ * while those products stay far from the fp32 limits (tested with |alpha| up
+ * to 1.25).  Gate magnitudes below 2^-31 enter the Gram factors as 2^-31
+ * (sign kept); the products that reach the outputs use the gates as given. */
 int ckda_chunk_fwd(const void* q, const void* k, const void* v, const void* alpha,
                    const void* beta, const float* h0, void* o, float* hT,
                    int B, int H, int T, int dk, int dv, int chunk, int dtype,
