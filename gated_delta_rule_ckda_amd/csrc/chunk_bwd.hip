@@ -124,6 +124,35 @@ __device__ __forceinline__ void head_slice(int id, int nsl, int xcd_map, long lo
   }
 }
 
+// Split bf16 products for the sequential passes with bf16 inputs and
+// dk >= 64: each operand x (fp32) enters as hi = bf16(x), lo = bf16(x - hi),
+// and acc + A B takes lo.hi + hi.lo + hi.hi on bf16 matrix cores (about
+// 2^-16 relative per product, against 2^-24 for fp32 matrix cores, at 3 bf16
+// steps of 32 K each instead of 8 fp32 steps of 4).  The operands are given
+// as two f32x4 in the K order of an fp32 fragment (K 0-15 and 16-31 of the
+// block), which is the bf16 fragment's K order (kappa) once packed.
+template <typename T, int DK>
+constexpr bool kSplitSeq = std::is_same<T, bf16_t>::value && DK >= 64;
+
+struct SplitFrag {
+  Frag h, l;
+};
+__device__ __forceinline__ SplitFrag split_frag(f32x4 k0, f32x4 k1) {
+  SplitFrag f;
+  frags_from_acc_bf16_split(k0, k1, f.h, f.l);
+  return f;
+}
+__device__ __forceinline__ f32x4 mma_split(f32x4 acc, SplitFrag a, SplitFrag b) {
+  acc = mma<bf16_t>(acc, a.l, b.h);
+  acc = mma<bf16_t>(acc, a.h, b.l);
+  return mma<bf16_t>(acc, a.h, b.h);
+}
+// B exact in bf16 (an input): lo.B + hi.B
+__device__ __forceinline__ f32x4 mma_split_exact(f32x4 acc, SplitFrag a, Frag b) {
+  acc = mma<bf16_t>(acc, a.l, b);
+  return mma<bf16_t>(acc, a.h, b);
+}
+
 // ============================================================ prep
 // threads of the prep kernel (its LDS keeps one workgroup per CU at dk = 128;
 // two waves per SIMD hide part of each one's latencies)
@@ -343,6 +372,8 @@ __global__ __launch_bounds__(64) void chunk_bwd_states_kernel(const T* v, const 
                                                               const float* __restrict__ rec, float* __restrict__ hc,
                                                               int T_len, int nchunks, int dv, int xcd_map) {
   constexpr int C = kBC, RH = DK / 16, RT = C / 16;
+  constexpr bool SPLIT = kSplitSeq<T, DK>;
+  static_assert(RT == 2, "one 32-position K block per chunk");
   using R = BwdRec<DK>;
   const int lane = threadIdx.x, g = lane >> 4, r = lane & 15;
   const int nsl = dv / 16;
@@ -416,11 +447,21 @@ __global__ __launch_bounds__(64) void chunk_bwd_states_kernel(const T* v, const 
     __builtin_amdgcn_sched_barrier(0);
     // X = V - KG H
     f32x4 xacc[RT];
+    SplitFrag hs[SPLIT ? RH / 2 : 1];
+    if constexpr (SPLIT)
+#pragma unroll
+      for (int j = 0; j < RH / 2; ++j) hs[j] = split_frag(hacc[2 * j], hacc[2 * j + 1]);
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
       f32x4 p = zero4();
+      if constexpr (SPLIT) {
 #pragma unroll
-      for (int kb = 0; kb < RH; ++kb) p = mma<float>(p, Frag{__builtin_bit_cast(u32x4, kg[rt][kb])}, frag_from_acc_f32(hacc[kb]));
+        for (int j = 0; j < RH / 2; ++j) p = mma_split(p, split_frag(kg[rt][2 * j], kg[rt][2 * j + 1]), hs[j]);
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < RH; ++kb)
+          p = mma<float>(p, Frag{__builtin_bit_cast(u32x4, kg[rt][kb])}, frag_from_acc_f32(hacc[kb]));
+      }
       const int cv = min(C, T_len - c * C);
 #pragma unroll
       for (int i = 0; i < 4; ++i) xacc[rt][i] = (16 * rt + 4 * g + i < cv ? to_f32(vv[rt][i]) : 0.f) - p[i];
@@ -430,22 +471,35 @@ __global__ __launch_bounds__(64) void chunk_bwd_states_kernel(const T* v, const 
     __builtin_amdgcn_sched_barrier(0);
     // U = TB X
     f32x4 uacc[RT];
+    if constexpr (SPLIT) {
+      const SplitFrag xs = split_frag(xacc[0], xacc[1]);
+      uacc[0] = mma_split(zero4(), split_frag(tb[0][0], zero4()), xs);   // TB is lower triangular
+      uacc[1] = mma_split(zero4(), split_frag(tb[1][0], tb[1][1]), xs);
+    } else {
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      uacc[rt] = zero4();
+      for (int rt = 0; rt < RT; ++rt) {
+        uacc[rt] = zero4();
 #pragma unroll
-      for (int kb = 0; kb <= rt; ++kb)
-        uacc[rt] = mma<float>(uacc[rt], Frag{__builtin_bit_cast(u32x4, tb[rt][kb])}, frag_from_acc_f32(xacc[kb]));
+        for (int kb = 0; kb <= rt; ++kb)
+          uacc[rt] = mma<float>(uacc[rt], Frag{__builtin_bit_cast(u32x4, tb[rt][kb])}, frag_from_acc_f32(xacc[kb]));
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
     load_tb_v(cn);
     __builtin_amdgcn_sched_barrier(0);
     // H <- Gamma_C . H + KR^T U
+    SplitFrag us;
+    if constexpr (SPLIT) us = split_frag(uacc[0], uacc[1]);
 #pragma unroll
     for (int rh = 0; rh < RH; ++rh) {
       f32x4 hh = gc[rh] * hacc[rh];
+      if constexpr (SPLIT) {
+        hh = mma_split(hh, split_frag(kr[rh][0], kr[rh][1]), us);
+      } else {
 #pragma unroll
-      for (int kb = 0; kb < RT; ++kb) hh = mma<float>(hh, Frag{__builtin_bit_cast(u32x4, kr[rh][kb])}, frag_from_acc_f32(uacc[kb]));
+        for (int kb = 0; kb < RT; ++kb)
+          hh = mma<float>(hh, Frag{__builtin_bit_cast(u32x4, kr[rh][kb])}, frag_from_acc_f32(uacc[kb]));
+      }
       hacc[rh] = hh;
     }
   }
@@ -475,6 +529,8 @@ __global__ __launch_bounds__(128) void chunk_bwd_dstates_kernel(const T* dout, c
                                                                float* __restrict__ dhn, float* __restrict__ dh0,
                                                                int T_len, int nchunks, int dv, int xcd_map) {
   constexpr int C = kBC, NW = kDsWaves<DK>, RHW = DK / 16 / NW, RT = C / 16;
+  constexpr bool SPLIT = kSplitSeq<T, DK>;
+  static_assert(RT == 2 && (!SPLIT || RHW % 2 == 0), "32-position K blocks; whole 32-channel blocks per wave");
   using R = BwdRec<DK>;
   __shared__ f32x4 xb[2][NW][RT][64];   // partial dU of each wave, by chunk parity
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, r = lane & 15;
@@ -571,16 +627,33 @@ __global__ __launch_bounds__(128) void chunk_bwd_dstates_kernel(const T* dout, c
       for (int e = 0; e < 4; ++e) dof[kb][e] = 16 * kb + 4 * g + e < cv ? to_f32(cur.dov[kb][e]) : 0.f;
     // dU = M^T dO (first wave) + KR dH' (each wave its channels), summed over the waves
     f32x4 du[RT];
+    Frag dob;   // dO as bf16 (exact: the input)
+    SplitFrag dhs[SPLIT ? RHW / 2 : 1];
+    if constexpr (SPLIT) {
+      dob = frag_from_acc_bf16(dof[0], dof[1]);
+#pragma unroll
+      for (int j = 0; j < RHW / 2; ++j) dhs[j] = split_frag(dacc[2 * j], dacc[2 * j + 1]);
+    }
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
       f32x4 m = zero4();
+      if constexpr (SPLIT) {   // M^T is upper triangular
+        m = mma_split_exact(m, split_frag(rt == 0 ? cur.mt[0][0] : zero4(), cur.mt[rt][1]), dob);
+      } else {
 #pragma unroll
-      for (int kb = rt; kb < RT; ++kb)
-        m = mma<float>(m, Frag{__builtin_bit_cast(u32x4, cur.mt[rt][kb])}, frag_from_acc_f32(dof[kb]));
+        for (int kb = rt; kb < RT; ++kb)
+          m = mma<float>(m, Frag{__builtin_bit_cast(u32x4, cur.mt[rt][kb])}, frag_from_acc_f32(dof[kb]));
+      }
       du[rt] = wave == 0 ? m : zero4();
+      if constexpr (SPLIT) {
 #pragma unroll
-      for (int kb = 0; kb < RHW; ++kb)
-        du[rt] = mma<float>(du[rt], Frag{__builtin_bit_cast(u32x4, cur.kr[rt][kb])}, frag_from_acc_f32(dacc[kb]));
+        for (int j = 0; j < RHW / 2; ++j)
+          du[rt] = mma_split(du[rt], split_frag(cur.kr[rt][2 * j], cur.kr[rt][2 * j + 1]), dhs[j]);
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < RHW; ++kb)
+          du[rt] = mma<float>(du[rt], Frag{__builtin_bit_cast(u32x4, cur.kr[rt][kb])}, frag_from_acc_f32(dacc[kb]));
+      }
     }
     if constexpr (NW == 2) {
 #pragma unroll
@@ -591,27 +664,40 @@ __global__ __launch_bounds__(128) void chunk_bwd_dstates_kernel(const T* dout, c
     }
     // dX = TB^T dU, negated for the update below
     f32x4 ndx[RT];
+    if constexpr (SPLIT) {   // TB^T is upper triangular
+      const SplitFrag dus = split_frag(du[0], du[1]);
+      ndx[0] = -mma_split(zero4(), split_frag(tbt[0][0], tbt[0][1]), dus);
+      ndx[1] = -mma_split(zero4(), split_frag(zero4(), tbt[1][1]), dus);
+    } else {
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      f32x4 x = zero4();
+      for (int rt = 0; rt < RT; ++rt) {
+        f32x4 x = zero4();
 #pragma unroll
-      for (int kb = rt; kb < RT; ++kb)
-        x = mma<float>(x, Frag{__builtin_bit_cast(u32x4, tbt[rt][kb])}, frag_from_acc_f32(du[kb]));
-      ndx[rt] = -x;
+        for (int kb = rt; kb < RT; ++kb)
+          x = mma<float>(x, Frag{__builtin_bit_cast(u32x4, tbt[rt][kb])}, frag_from_acc_f32(du[kb]));
+        ndx[rt] = -x;
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
     load_tbt(cn);
     __builtin_amdgcn_sched_barrier(0);
     // dH = Gamma_C . dH' + QG^T dO - KG^T dX
+    SplitFrag ndxs;
+    if constexpr (SPLIT) ndxs = split_frag(ndx[0], ndx[1]);
 #pragma unroll
     for (int rh = 0; rh < RHW; ++rh) {
       f32x4 h = gc[rh] * dacc[rh];
+      if constexpr (SPLIT) {
+        h = mma_split_exact(h, split_frag(qgt[rh][0], qgt[rh][1]), dob);
+        h = mma_split(h, split_frag(kgt[rh][0], kgt[rh][1]), ndxs);
+      } else {
 #pragma unroll
-      for (int kb = 0; kb < RT; ++kb)
-        h = mma<float>(h, Frag{__builtin_bit_cast(u32x4, qgt[rh][kb])}, frag_from_acc_f32(dof[kb]));
+        for (int kb = 0; kb < RT; ++kb)
+          h = mma<float>(h, Frag{__builtin_bit_cast(u32x4, qgt[rh][kb])}, frag_from_acc_f32(dof[kb]));
 #pragma unroll
-      for (int kb = 0; kb < RT; ++kb)
-        h = mma<float>(h, Frag{__builtin_bit_cast(u32x4, kgt[rh][kb])}, frag_from_acc_f32(ndx[kb]));
+        for (int kb = 0; kb < RT; ++kb)
+          h = mma<float>(h, Frag{__builtin_bit_cast(u32x4, kgt[rh][kb])}, frag_from_acc_f32(ndx[kb]));
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) dacc[rh][i] = live ? h[i] : dacc[rh][i];
     }
