@@ -1,7 +1,8 @@
 """GPU parity of ckda_chunk_bwd (through the C ABI) against the oracle's
 sequential fp64 backward, gradient by gradient: dq, dk, dv, dalpha, dbeta,
 dh0.  The kernels compute in fp32 from the exact input bytes (bf16 inputs
-included), so both dtypes are held to fp32-level tolerances."""
+included; with bf16 inputs at dk >= 64 the sequential passes multiply split
+bf16 pairs, about 16 bits), so both dtypes are held to fp32-level tolerances."""
 import numpy as np
 import pytest
 import torch
@@ -82,6 +83,25 @@ def test_stress_gates(law):
     gate derivatives divide by no gate, so none of these is a special case."""
     w = gen.Workload("bwd", 1, 2, 77, 32, 32, 64, "f32", law, "normal", 7100)
     run(w)
+
+
+@pytest.mark.parametrize("law", ["zero_and_unit", "small_gates", "orthogonal", "kda"])
+def test_stress_gates_split_path(law):
+    """bf16 inputs at dk >= 64: the sequential passes multiply split bf16
+    pairs (hi + lo, about 16 bits) instead of fp32; the same stress laws, an
+    odd number of chunks, held to the same bar."""
+    w = gen.Workload("bwd", 1, 2, 333, 128, 64, 64, "bf16", law, "normal", 7150)
+    run(w)
+
+
+def test_isometric_full_shape_sampled_heads():
+    """The bench shape with orthogonal steps (beta = 2, alpha = +-1): no step
+    damps a rounding error, over 128 chunks forward (chunk-start states) and
+    128 back (state gradients), so errors of the split products add up here
+    if anywhere; the oracle follows 2 of the 64 heads."""
+    b = gen.WORKLOADS["ckda_bf16"]
+    w = gen.Workload("bwd_isometric", b.B, b.H, b.T, b.dk, b.dv, b.chunk, "bf16", "orthogonal", "normal", 7160)
+    run(w, heads=[0, 63])
 
 
 @pytest.mark.parametrize("T", [1, 31, 32, 33, 64, 200])
