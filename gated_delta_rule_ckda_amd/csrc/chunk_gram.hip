@@ -150,8 +150,14 @@ __device__ __forceinline__ void tile_pair(int n, int& I, int& J, int& xk, int& x
 // over the chunk's products).  The same instantiation gathers each head's
 // retained key channels when gidx is set (q, k, alpha rows of dk_in channels;
 // gidx [nheads][DK] channel indices).
+// Waves per SIMD the compiler is asked to leave room for: three for bf16 at
+// dk 64, chunk 64 (two-wave workgroups, 26 KB of LDS: the registers, at 190,
+// would otherwise hold them to two), one (no bound) elsewhere.
+template <typename T, int DK, int C>
+constexpr int kGramMinWaves = (std::is_same<T, bf16_t>::value && DK == 64 && C == 64) ? 3 : 1;
+
 template <typename T, int DK, int C, bool PRO>
-__global__ __launch_bounds__((GramCfg<T, DK, C>::NTH)) void chunk_gram_kernel(
+__global__ __launch_bounds__((GramCfg<T, DK, C>::NTH), (kGramMinWaves<T, DK, C>)) void chunk_gram_kernel(
     const T* q, const T* k, const T* alpha, const T* beta, unsigned char* __restrict__ ws, int T_len,
     int nchunks, int flags, const int* __restrict__ gidx, int dk_in, int nheads) {
   using P = GramCfg<T, DK, C>;
