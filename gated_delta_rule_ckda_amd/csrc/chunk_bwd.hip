@@ -960,11 +960,17 @@ __global__ __launch_bounds__(kGThreads) void chunk_bwd_grad_kernel(
     }
   }
   __syncthreads();
-  // ---- through the solve: TB = T Diag(beta), T = (I + A)^-1, A = Diag(beta) S
-  if (tid < C) {
+  // ---- through the solve: TB = T Diag(beta), T = (I + A)^-1, A = Diag(beta) S.
+  // Row and column sums below take TPC threads per row (column), summed by DPP.
+  constexpr int TPC = kGThreads / C;
+  static_assert(TPC <= 64 && C % TPC == 0, "row groups within a wave");
+  {   // dbeta from TB = T Diag(beta): colsum(T . dTB)
+    const int col = tid / TPC, sub = tid % TPC;
     float acc = 0.f;
-    for (int i = 0; i < C; ++i) acc += sT[i * CP + tid] * sdTB[i * CP + tid];
-    sdb[tid] = acc;
+#pragma unroll
+    for (int i = sub; i < C; i += TPC) acc += sT[i * CP + col] * sdTB[i * CP + col];
+    acc = group_sum<TPC>(acc);
+    if (sub == 0) sdb[col] = acc;
   }
   __syncthreads();
   for (int e = tid; e < C * C; e += kGThreads) sdTB[(e / C) * CP + e % C] *= sb[e % C];   // dT = dTB Diag(beta)
@@ -973,15 +979,17 @@ __global__ __launch_bounds__(kGThreads) void chunk_bwd_grad_kernel(
   __syncthreads();
   gemm_lds<false, C, 0, NW>(sdTB, CP, sT, 1, CP, sP, CP, 1, C, C, -1.f);                        // dA = -T^T P
   __syncthreads();
-  if (tid < C) {   // strictly lower part: dbeta += rowsum(dA . S), dS = Diag(beta) dA
-    const int t = tid;
+  {   // strictly lower part: dbeta += rowsum(dA . S), dS = Diag(beta) dA
+    const int t = tid / TPC, sub = tid % TPC;
     float acc = 0.f;
-    for (int j = 0; j < C; ++j) {
+#pragma unroll
+    for (int j = sub; j < C; j += TPC) {
       const float da = j < t ? sdTB[t * CP + j] : 0.f;
       acc += da * sS[t * CP + j];
       sdTB[t * CP + j] = sb[t] * da;
     }
-    sdb[t] += acc;
+    acc = group_sum<TPC>(acc);
+    if (sub == 0) sdb[t] += acc;
   }
   __syncthreads();
   float* sdS = sdTB;
@@ -998,41 +1006,93 @@ __global__ __launch_bounds__(kGThreads) void chunk_bwd_grad_kernel(
     float* gk = sdKG + ch;
     float* ga = sdKR + ch;
     float* sg = big + 3 * C * DKP + ch;   // element t at sg[t * DK]
-    if (tid < DK) {
-      // sg[t] = G(C-1, t) = alpha_{t+1} ... alpha_{C-1}
-      {
-        float e = 1.f;
-        for (int t = C - 1; t >= 0; --t) {
-          sg[t * DK] = e;
-          e *= A(t);
-        }
-      }
-      // forward: direct terms, the KR scan (pairs with the chunk end) and the
-      // Gamma_C term; pre[t] = Gamma_{t-1}
-      float pre[C + 1];
-      pre[0] = 1.f;
-      {
-        float f = 0.f;
-        const float gc = sGC[ch];
+    constexpr int P = kGThreads / DK;
+    // Direct terms, the KR scan (pairs with the chunk end), the Gamma_C term
+    // and the Gamma_t terms (pairs with the chunk start), per channel:
+    //   dq_t = dM_tt k_t + dQG_t pre_{t+1},  dk_t = dM_tt q_t + dKG_t pre_{t+1} + dKR_t se_t,
+    //   dalpha_t = se_t f_t + gc pre_t se_t + pre_t b_t,
+    // with pre_t = Gamma_{t-1} (alpha_0 ... alpha_{t-1}), se_t = G(C-1, t),
+    // f_0 = 0, f_{t+1} = alpha_t f_t + dKR_t k_t, and b_t = R_t + alpha_{t+1} b_{t+1}
+    // (b_{C-1} = R_{C-1}), R_t = dQG_t q_t + dKG_t k_t, gc = rowsum(H . dH').
+    // NS threads per channel take NS segments of SL positions: each forms its
+    // segment's part of every product and scan with nothing carried in, the
+    // carries (segment products, f at the segment end, b at its start and its
+    // gate product) go through LDS, and each then completes its positions.
+    constexpr int NS = 4, SL = C / NS;
+    static_assert(P >= NS, "a thread per channel and segment");
+    float* xs = sCC + 3 * C * CP;   // [4][NS][DK] carries: TB, T, S and P are consumed
+    static_assert(3 * C * CP + 4 * NS * DK <= 7 * C * CP, "carries fit in the consumed C x C arrays");
+    const bool segon = part < NS;
+    const int t0s = part * SL;
+    float av[SL], pl[SL + 1], sl[SL], fl[SL], bl[SL], ml[SL];
+    if (segon) {
+      pl[0] = 1.f;
 #pragma unroll
-        for (int t = 0; t < C; ++t) {
-          pre[t + 1] = pre[t] * A(t);
-          const float dqg = gq[t * DKP], dkg = gk[t * DKP], dkr = ga[t * DKP], se = sg[t * DK];
-          const float dmd = sdM[t * CP + t];
-          gq[t * DKP] = dmd * K(t) + dqg * pre[t + 1];
-          gk[t * DKP] = dmd * Q(t) + dkg * pre[t + 1] + dkr * se;
-          ga[t * DKP] = se * f + gc * pre[t] * se;
-          f = A(t) * f + dkr * K(t);
-          sg[t * DK] = dqg * Q(t) + dkg * K(t);   // R_t of the Gamma_t scan
-        }
+      for (int i = 0; i < SL; ++i) {
+        av[i] = A(t0s + i);
+        pl[i + 1] = pl[i] * av[i];
       }
-      {   // Gamma_t terms (pairs with the chunk start): reverse scan of R_t
-        float bs = 0.f;
+      xs[(0 * NS + part) * DK + ch] = pl[SL];
+    }
+    __syncthreads();
+    float pre_in = 1.f;
+    if (segon) {
+      float suf_in = 1.f;
 #pragma unroll
-        for (int s = C - 1; s >= 0; --s) {
-          bs = sg[s * DK] + (s + 1 < C ? A(s + 1) * bs : 0.f);
-          ga[s * DKP] += pre[s] * bs;
-        }
+      for (int p = 0; p < NS; ++p) {
+        const float lp = xs[(0 * NS + p) * DK + ch];
+        if (p < part) pre_in *= lp;
+        if (p > part) suf_in *= lp;
+      }
+      float e = suf_in;   // se of the segment's positions
+#pragma unroll
+      for (int i = SL - 1; i >= 0; --i) {
+        sl[i] = e;
+        e *= av[i];
+      }
+      float f = 0.f, rv[SL];
+#pragma unroll
+      for (int i = 0; i < SL; ++i) {
+        const int t = t0s + i;
+        const float dqg = gq[t * DKP], dkg = gk[t * DKP], dkr = ga[t * DKP], dmd = sdM[t * CP + t];
+        const float pr1 = pre_in * pl[i + 1];
+        gq[t * DKP] = dmd * K(t) + dqg * pr1;
+        gk[t * DKP] = dmd * Q(t) + dkg * pr1 + dkr * sl[i];
+        fl[i] = f;
+        f = av[i] * f + dkr * K(t);
+        rv[i] = dqg * Q(t) + dkg * K(t);
+      }
+      xs[(1 * NS + part) * DK + ch] = f;
+      // b inside the segment with nothing from the right, and the gate product
+      // ml_t = alpha_{t+1} ... alpha_{t0s+SL} that carries the right part in
+      const float anext = part + 1 < NS ? A(t0s + SL) : 0.f;
+      float bb = 0.f, mm = 1.f;
+#pragma unroll
+      for (int i = SL - 1; i >= 0; --i) {
+        const float a1 = i + 1 < SL ? av[i + 1] : anext;
+        bb = rv[i] + a1 * bb;
+        mm = a1 * mm;
+        bl[i] = bb;
+        ml[i] = mm;
+      }
+      xs[(2 * NS + part) * DK + ch] = bl[0];
+      xs[(3 * NS + part) * DK + ch] = ml[0];
+    }
+    __syncthreads();
+    if (segon) {
+      float fin = 0.f, bin = 0.f;   // f at the segment's start, b at the next segment's start
+#pragma unroll
+      for (int p = 0; p < NS; ++p)
+        if (p < part) fin = xs[(0 * NS + p) * DK + ch] * fin + xs[(1 * NS + p) * DK + ch];
+#pragma unroll
+      for (int p = NS - 1; p >= 0; --p)
+        if (p > part) bin = xs[(2 * NS + p) * DK + ch] + xs[(3 * NS + p) * DK + ch] * bin;
+      const float gc = sGC[ch];
+#pragma unroll
+      for (int i = 0; i < SL; ++i) {
+        const int t = t0s + i;
+        const float pr = pre_in * pl[i];
+        ga[t * DKP] = sl[i] * (fl[i] + pl[i] * fin) + gc * pr * sl[i] + pr * (bl[i] + ml[i] * bin);
       }
     }
     __syncthreads();
@@ -1041,7 +1101,6 @@ __global__ __launch_bounds__(kGThreads) void chunk_bwd_grad_kernel(
     // (block, side); the P threads of a channel take them in turn (R and L rows
     // are disjoint positions).  h is a compile-time constant per level so that
     // the loops unroll, the row loops as kHalvUnroll says.
-    constexpr int P = kGThreads / DK;
     auto factors = [&](int lo, auto hh, bool left) __attribute__((always_inline)) {
       constexpr int h = decltype(hh)::value;
       if (left) {
