@@ -165,7 +165,9 @@ __global__ __launch_bounds__(kPThreads) void chunk_bwd_prep_kernel(const T* q, c
   constexpr int C = kBC, DKP = DK + 1, CP = C + 1;
   using R = BwdRec<DK>;
   __shared__ float sq[C * DKP], sk[C * DKP], sa[C * DKP];
-  __shared__ float sx[C * DKP], sxq[C * DKP], sy[C * DKP];   // rescaled operands of one halving level
+  // rescaled operands of one halving level, rows 16-byte aligned for 4-channel reads
+  constexpr int XP = DK + 4;
+  __shared__ __align__(16) float sx[C * XP], sxq[C * XP], sy[C * XP];
   __shared__ float sS[C * CP], sM[C * CP], sT[C * CP], sb[C];
 
   const int tid = threadIdx.x;
@@ -266,23 +268,25 @@ __global__ __launch_bounds__(kPThreads) void chunk_bwd_prep_kernel(const T* q, c
 #pragma unroll
         for (int t = m + 1; t <= m + h; ++t) {   // x_t G(t, m)
           f *= ca[t];
-          sx[t * DKP + ch] = ck[t] * f;
-          sxq[t * DKP + ch] = cq[t] * f;
+          sx[t * XP + ch] = ck[t] * f;
+          sxq[t * XP + ch] = cq[t] * f;
         }
         float e = 1.f;
 #pragma unroll
         for (int j = m; j >= lo; --j) {          // y_j G(m, j)
-          sy[j * DKP + ch] = ck[j] * e;
+          sy[j * XP + ch] = ck[j] * e;
           e *= ca[j];
         }
       }
     }
     __syncthreads();
     // (C / 2h) blocks of h x h entries, TPE threads per entry (consecutive
-    // lanes, strided channels), partial sums reduced across the group
+    // lanes, strided groups of 4 channels), partial sums reduced across the group
     constexpr int nent = C * h / 2;
     constexpr int TPE0 = kPThreads / nent < 1 ? 1 : kPThreads / nent;
-    constexpr int TPE = TPE0 > DK ? DK : (TPE0 > 64 ? 64 : TPE0);
+    constexpr int TPE1 = TPE0 > DK / 4 ? DK / 4 : TPE0;
+    constexpr int TPE = TPE1 > 64 ? 64 : TPE1;
+    static_assert(TPE >= 2, "lane groups of two or more");
     for (int base = 0; base < nent * TPE; base += kPThreads) {
       const int e = (base + tid) / TPE, sub = (base + tid) % TPE;
       const bool ok = e < nent;
@@ -291,10 +295,15 @@ __global__ __launch_bounds__(kPThreads) void chunk_bwd_prep_kernel(const T* q, c
       float s = 0.f, mm = 0.f;
       if (ok) {
 #pragma unroll
-        for (int ch = sub; ch < DK; ch += TPE) {
-          const float y = sy[j * DKP + ch];
-          s += sx[t * DKP + ch] * y;
-          mm += sxq[t * DKP + ch] * y;
+        for (int c4 = sub; c4 < DK / 4; c4 += TPE) {
+          const f32x4 y = *reinterpret_cast<const f32x4*>(sy + j * XP + 4 * c4);
+          const f32x4 x = *reinterpret_cast<const f32x4*>(sx + t * XP + 4 * c4);
+          const f32x4 xq = *reinterpret_cast<const f32x4*>(sxq + t * XP + 4 * c4);
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            s += x[v] * y[v];
+            mm += xq[v] * y[v];
+          }
         }
       }
       s = group_sum<TPE>(s);
@@ -312,21 +321,45 @@ __global__ __launch_bounds__(kPThreads) void chunk_bwd_prep_kernel(const T* q, c
   level(std::integral_constant<int, 4>{});
   level(std::integral_constant<int, 2>{});
   level(std::integral_constant<int, 1>{});
-  // T = (I + Diag(beta) S)^-1, unit lower triangular, one column per thread
-  // held in registers: T[i][j] = -beta_i sum_{l < i} S[i][l] T[l][j] for i > j
-  // (the rows of S are read by every lane at once)
+  // T = (I + B)^-1, B = Diag(beta) S strictly lower, unit lower triangular,
+  // by 16 x 16 blocks: the diagonal blocks T11 = (I + B11)^-1 and
+  // T22 = (I + B22)^-1 by forward substitution, one column per thread held in
+  // registers (T[i][j] = -beta_i sum_{l < i} S[i][l] T[l][j] for i > j; the
+  // rows of S are read by every lane at once), then T21 = -T22 (B21 T11) as
+  // two 16 x 16 products, one entry per thread.
+  constexpr int HB = C / 2;
   if (tid < C) {
-    const int j = tid;
-    float tc[C];
+    const int o = (tid / HB) * HB, j = tid % HB;   // the block's first row, the column in it
+    float tc[HB];
 #pragma unroll
-    for (int i = 0; i < C; ++i) {
+    for (int i = 0; i < HB; ++i) {
       float acc = 0.f;
 #pragma unroll
-      for (int l = 0; l < i; ++l) acc += sS[i * CP + l] * tc[l];
-      tc[i] = i > j ? -sb[i] * acc : (i == j ? 1.f : 0.f);
+      for (int l = 0; l < i; ++l) acc += sS[(o + i) * CP + o + l] * tc[l];
+      tc[i] = i > j ? -sb[o + i] * acc : (i == j ? 1.f : 0.f);
     }
 #pragma unroll
-    for (int i = 0; i < C; ++i) sT[i * CP + j] = tc[i];
+    for (int i = 0; i < HB; ++i) sT[(o + i) * CP + o + j] = tc[i];
+    if (o == 0)
+#pragma unroll
+      for (int i = 0; i < HB; ++i) sT[i * CP + HB + j] = 0.f;   // T12
+  }
+  __syncthreads();
+  float* sW = sx;   // B21 T11 (the rescaled operands are consumed)
+  if (tid < HB * HB) {
+    const int i = tid / HB, j = tid % HB;
+    float acc = 0.f;
+#pragma unroll
+    for (int l = 0; l < HB; ++l) acc += sS[(HB + i) * CP + l] * sT[l * CP + j];
+    sW[i * HB + j] = sb[HB + i] * acc;
+  }
+  __syncthreads();
+  if (tid < HB * HB) {
+    const int i = tid / HB, j = tid % HB;
+    float acc = 0.f;
+#pragma unroll
+    for (int l = 0; l < HB; ++l) acc += sT[(HB + i) * CP + HB + l] * sW[l * HB + j];
+    sT[(HB + i) * CP + j] = -acc;
   }
   __syncthreads();
   for (int e = tid; e < C * C; e += kPThreads) {
