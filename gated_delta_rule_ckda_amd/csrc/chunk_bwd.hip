@@ -758,12 +758,6 @@ __global__ __launch_bounds__(128) void chunk_bwd_dstates_kernel(const T* dout, c
 }
 
 // ============================================================ grad (per chunk)
-// Unrolling of the row loops of the grad kernel's recursive halving: full
-// with dk >= 64, so that the rows' LDS reads overlap; rolled below, which
-// keeps the registers low.
-template <int DK>
-constexpr int kHalvUnroll = DK >= 64 ? 16 : 1;
-
 // threads of the grad kernel: two waves per SIMD, so that one wave's LDS and
 // matrix-core latencies overlap the other's (its LDS keeps one workgroup per
 // CU at dk = 128)
@@ -1130,10 +1124,8 @@ __global__ __launch_bounds__(kGThreads) void chunk_bwd_grad_kernel(
     }
     __syncthreads();
     // recursive halving: blocks [lo, lo + 2h), L = [lo, m], R = [m + 1, lo + 2h - 1];
-    // sg holds G(m, j) on L and G(t, m) on R.  The work items of a level are
-    // (block, side); the P threads of a channel take them in turn (R and L rows
-    // are disjoint positions).  h is a compile-time constant per level so that
-    // the loops unroll, the row loops as kHalvUnroll says.
+    // sg holds G(m, j) on L and G(t, m) on R.  h is a compile-time constant per
+    // level so that the loops unroll.
     auto factors = [&](int lo, auto hh, bool left) __attribute__((always_inline)) {
       constexpr int h = decltype(hh)::value;
       if (left) {
@@ -1151,70 +1143,6 @@ __global__ __launch_bounds__(kGThreads) void chunk_bwd_grad_kernel(
           sg[(lo + h + i) * DK] = f;
         }
       }
-    };
-    auto rows_R = [&](int lo, auto hh) __attribute__((always_inline)) {
-      // rows t in R, last to first: cross terms with L, and the scan for the
-      // gates s in R, G(s - 1, m) sum_{t >= s} (q_t zm_t + k_t zs_t) G(t, s)
-      constexpr int h = decltype(hh)::value;
-      const int m = lo + h - 1;
-      float ky[h];
-#pragma unroll
-      for (int jj = 0; jj < h; ++jj) ky[jj] = K(lo + jj) * sg[(lo + jj) * DK];
-      float bs = 0.f;
-#pragma unroll kHalvUnroll<DK>
-      for (int i = h - 1; i >= 0; --i) {
-        const int t = m + 1 + i;
-        float zm = 0.f, zs = 0.f;
-#pragma unroll
-        for (int jj = 0; jj < h; ++jj) {
-          zm += sdM[t * CP + lo + jj] * ky[jj];
-          zs += sdS[t * CP + lo + jj] * ky[jj];
-        }
-        const float gr = sg[t * DK];
-        gq[t * DKP] += gr * zm;
-        gk[t * DKP] += gr * zs;
-        bs = Q(t) * zm + K(t) * zs + (i + 1 < h ? A(t + 1) * bs : 0.f);
-        ga[t * DKP] += (i > 0 ? sg[(t - 1) * DK] : 1.f) * bs;
-      }
-    };
-    auto rows_L = [&](int lo, auto hh) __attribute__((always_inline)) {
-      // rows j in L, first to last: cross terms with R, and the scan for the
-      // gates s in L, G(m, s) sum_{j < s} k_j zl_j G(s - 1, j)
-      constexpr int h = decltype(hh)::value;
-      const int m = lo + h - 1;
-      float qr[h], kr[h];
-#pragma unroll
-      for (int i = 0; i < h; ++i) {
-        const float gr = sg[(m + 1 + i) * DK];
-        qr[i] = Q(m + 1 + i) * gr;
-        kr[i] = K(m + 1 + i) * gr;
-      }
-      float f = 0.f;
-#pragma unroll kHalvUnroll<DK>
-      for (int jj = 0; jj < h; ++jj) {
-        const int j = lo + jj;
-        float zl = 0.f;
-#pragma unroll
-        for (int i = 0; i < h; ++i) {
-          const int t = m + 1 + i;
-          zl += sdM[t * CP + j] * qr[i] + sdS[t * CP + j] * kr[i];
-        }
-        const float gl = sg[j * DK];
-        gk[j * DKP] += gl * zl;
-        ga[j * DKP] += gl * f;
-        f = A(j) * f + K(j) * zl;
-      }
-    };
-    auto level = [&](auto hh) __attribute__((always_inline)) {
-      constexpr int h = decltype(hh)::value;
-      constexpr int nb = C / (2 * h);
-      for (int it = part; it < 2 * nb; it += P) factors((it >> 1) * 2 * h, hh, it & 1);
-      __syncthreads();
-      for (int it = part; it < 2 * nb; it += P) {
-        if (it & 1) rows_L((it >> 1) * 2 * h, hh);
-        else rows_R((it >> 1) * 2 * h, hh);
-      }
-      __syncthreads();
     };
     // The first level (one block: L = 0..15, R = 16..31, all 16 x 16 pairs)
     // has its cross terms on the matrix cores for all channels at once: with
@@ -1291,17 +1219,154 @@ __global__ __launch_bounds__(kGThreads) void chunk_bwd_grad_kernel(
     };
     static_assert(C == 32, "halving levels below assume 32-position chunks");
     level16();
-    level(std::integral_constant<int, 8>{});
-    level(std::integral_constant<int, 4>{});
-    level(std::integral_constant<int, 2>{});
-    level(std::integral_constant<int, 1>{});
-    for (int e = tid; e < cv * DK; e += kGThreads) {
-      const int t = e / DK, cc = e % DK;
-      const size_t o = (size_t)(row0 + t) * DK + cc;
-      dq[o] = sdQG[t * DKP + cc];
-      dk[o] = sdKG[t * DKP + cc];
-      dal[o] = sdKR[t * DKP + cc];
+    // The levels below the first (h = 8, 4, 2, 1) by position segments: the
+    // thread of segment p (positions 8p .. 8p + 7 of its channel) keeps their
+    // q, k, alpha and the three accumulators in registers and takes every
+    // (block, side) of a level whose positions lie in its segment: at h = 8
+    // one side of a 16-position block (the other side's operands come from
+    // LDS), below it both sides of every block of the segment.  Right-side
+    // rows t, last to first: the cross terms with L (zm = sum_j dM[t, j] k~_j,
+    // zs likewise with dS; dq_t += G(t, m) zm, dk_t += G(t, m) zs) and the
+    // scan for the gates s in R, G(s - 1, m) sum_{t >= s} (q_t zm_t + k_t zs_t)
+    // G(t, s).  Left-side rows j, first to last: the cross terms with R
+    // (zl = sum_t dM[t, j] q~_t + dS[t, j] k~_t; dk_j += G(m, j) zl) and the
+    // scan for the gates s in L, G(m, s) sum_{j < s} k_j zl_j G(s - 1, j).
+    static_assert(SL == 8 && NS == 4, "8-position segments");
+    float rq[SL], rk[SL], ra[SL], aq[SL], ak[SL], aa[SL], sgv[SL];
+    if (segon) {
+#pragma unroll
+      for (int i = 0; i < SL; ++i) {
+        const int t = t0s + i;
+        rq[i] = Q(t);
+        rk[i] = K(t);
+        ra[i] = av[i];
+        aq[i] = gq[t * DKP];
+        ak[i] = gk[t * DKP];
+        aa[i] = ga[t * DKP];
+      }
     }
+    // factors of one side, positions o .. o + h - 1 of the segment: G(t, m) on
+    // the right side (m = o - 1), G(m, j) on the left (m = o + h - 1)
+    // (written to LDS too when another segment's thread reads them: h = 8)
+    auto seg_factors = [&](auto oo, auto hh, bool right) __attribute__((always_inline)) {
+      constexpr int o = decltype(oo)::value, h = decltype(hh)::value;
+      constexpr bool publish = h == SL;
+      if (right) {
+        float f = 1.f;
+#pragma unroll
+        for (int i = 0; i < h; ++i) {
+          f *= ra[o + i];
+          sgv[o + i] = f;
+          if (publish) sg[(t0s + o + i) * DK] = f;
+        }
+      } else {
+        float e = 1.f;
+#pragma unroll
+        for (int i = h - 1; i >= 0; --i) {
+          sgv[o + i] = e;
+          if (publish) sg[(t0s + o + i) * DK] = e;
+          e *= ra[o + i];
+        }
+      }
+    };
+    // right side at segment offset o (positions t0s + o ..), its left side at
+    // lo (absolute); the left side's k~ from registers (same segment) or LDS
+    auto seg_right = [&](auto oo, auto hh, int lo, bool left_here) __attribute__((always_inline)) {
+      constexpr int o = decltype(oo)::value, h = decltype(hh)::value;
+      float ky[h];
+#pragma unroll
+      for (int jj = 0; jj < h; ++jj)
+        ky[jj] = left_here ? rk[o - h + jj] * sgv[o - h + jj] : K(lo + jj) * sg[(lo + jj) * DK];
+      float bs = 0.f;
+#pragma unroll
+      for (int i = h - 1; i >= 0; --i) {
+        const int t = t0s + o + i;
+        float zm = 0.f, zs = 0.f;
+#pragma unroll
+        for (int jj = 0; jj < h; ++jj) {
+          zm += sdM[t * CP + lo + jj] * ky[jj];
+          zs += sdS[t * CP + lo + jj] * ky[jj];
+        }
+        const float gr = sgv[o + i];
+        aq[o + i] += gr * zm;
+        ak[o + i] += gr * zs;
+        bs = rq[o + i] * zm + rk[o + i] * zs + (i + 1 < h ? ra[o + i + 1] * bs : 0.f);
+        aa[o + i] += (i > 0 ? sgv[o + i - 1] : 1.f) * bs;
+      }
+    };
+    // left side at segment offset o, its right side starting at rlo (absolute)
+    auto seg_left = [&](auto oo, auto hh, int rlo, bool right_here) __attribute__((always_inline)) {
+      constexpr int o = decltype(oo)::value, h = decltype(hh)::value;
+      float qr[h], kr[h];
+#pragma unroll
+      for (int i = 0; i < h; ++i) {
+        if (right_here) {
+          qr[i] = rq[o + h + i] * sgv[o + h + i];
+          kr[i] = rk[o + h + i] * sgv[o + h + i];
+        } else {
+          const float gr = sg[(rlo + i) * DK];
+          qr[i] = Q(rlo + i) * gr;
+          kr[i] = K(rlo + i) * gr;
+        }
+      }
+      float f = 0.f;
+#pragma unroll
+      for (int jj = 0; jj < h; ++jj) {
+        const int j = t0s + o + jj;
+        float zl = 0.f;
+#pragma unroll
+        for (int i = 0; i < h; ++i) zl += sdM[(rlo + i) * CP + j] * qr[i] + sdS[(rlo + i) * CP + j] * kr[i];
+        const float gl = sgv[o + jj];
+        ak[o + jj] += gl * zl;
+        aa[o + jj] += gl * f;
+        f = ra[o + jj] * f + rk[o + jj] * zl;
+      }
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I8 = std::integral_constant<int, 8>;
+    // h = 8: blocks of 16 positions, segment 2b is the left side of block b, 2b + 1 its right
+    const bool odd = part & 1;
+    if (segon) seg_factors(I0{}, I8{}, odd);
+    __syncthreads();
+    if (segon) {
+      if (odd) seg_right(I0{}, I8{}, t0s - SL, false);
+      else seg_left(I0{}, I8{}, t0s + SL, false);
+    }
+    // h = 4, 2, 1: every block inside the segment, both sides, from this
+    // thread's registers only (no barrier)
+    auto seg_block = [&](auto bb, auto hh) __attribute__((always_inline)) {
+      constexpr int b = decltype(bb)::value, h = decltype(hh)::value;
+      using OL = std::integral_constant<int, 2 * h * b>;
+      using OR = std::integral_constant<int, 2 * h * b + h>;
+      seg_factors(OL{}, hh, false);
+      seg_factors(OR{}, hh, true);
+      seg_right(OR{}, hh, t0s + 2 * h * b, true);
+      seg_left(OL{}, hh, t0s + 2 * h * b + h, true);
+    };
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    using I4 = std::integral_constant<int, 4>;
+    if (segon) {
+      seg_block(I0{}, I4{});
+      seg_block(I0{}, I2{});
+      seg_block(I1{}, I2{});
+      seg_block(I0{}, I1{});
+      seg_block(I1{}, I1{});
+      seg_block(I2{}, I1{});
+      seg_block(I3{}, I1{});
+    }
+    if (segon)
+#pragma unroll
+      for (int i = 0; i < SL; ++i) {
+        const int t = t0s + i;
+        if (t < cv) {
+          const size_t o = (size_t)(row0 + t) * DK + ch;
+          dq[o] = aq[i];
+          dk[o] = ak[i];
+          dal[o] = aa[i];
+        }
+      }
   }
   if (tid < cv) dbe[row0 + tid] = sdb[tid];
 }
