@@ -758,6 +758,60 @@ __global__ __launch_bounds__(128) void chunk_bwd_dstates_kernel(const T* dout, c
 }
 
 // ============================================================ grad (per chunk)
+// Split bf16 operands of the grad kernel's value-slice loop, kept in LDS as
+// bf16 bit patterns (hi = bf16(x), lo = bf16(x - hi)).  Along the contracted
+// index K, each 32-wide block is stored in the K order of a bf16 fragment
+// (kappa), so that a lane's 8 values of a row are one 16-byte read; a
+// fragment along the other index ("column" fragment) is 8 two-byte reads.
+__device__ __forceinline__ int kperm(int k) {   // storage position of K index k within its 32-block
+  return (k & ~31) + ((k & 31) < 16 ? 8 * ((k & 15) >> 2) + (k & 3) : 8 * ((k & 15) >> 2) + 4 + (k & 3));
+}
+__device__ __forceinline__ void split_bits(float x, unsigned short& h, unsigned short& l) {
+  const uint32_t hw = pack_bf16x2(x, 0.f) & 0xFFFFu;
+  h = (unsigned short)hw;
+  l = (unsigned short)(pack_bf16x2(x - __uint_as_float(hw << 16), 0.f) & 0xFFFFu);
+}
+__device__ __forceinline__ float bits_f32(unsigned short b) { return __uint_as_float((uint32_t)b << 16); }
+// lane (r, g): row `row`, the 8 K values of block kb (16-byte read)
+__device__ __forceinline__ Frag row_frag(const unsigned short* m, int stride, int row, int kb, int g) {
+  return load_frag(m + row * stride + 32 * kb + 8 * g);
+}
+// lane (r, g): column position `cpos`, rows 32 kb + kappa(g, e)
+__device__ __forceinline__ Frag col_frag(const unsigned short* m, int stride, int cpos, int kb, int g) {
+  Frag f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t a = m[(32 * kb + kappa<bf16_t>(g, 2 * i)) * stride + cpos];
+    const uint32_t b = m[(32 * kb + kappa<bf16_t>(g, 2 * i + 1)) * stride + cpos];
+    f.w[i] = a | (b << 16);
+  }
+  return f;
+}
+struct SFrag {
+  Frag h, l;
+};
+__device__ __forceinline__ SFrag srow(const unsigned short* mh, const unsigned short* ml, int stride, int row, int kb,
+                                      int g) {
+  return SFrag{row_frag(mh, stride, row, kb, g), row_frag(ml, stride, row, kb, g)};
+}
+__device__ __forceinline__ SFrag scol(const unsigned short* mh, const unsigned short* ml, int stride, int cpos, int kb,
+                                      int g) {
+  return SFrag{col_frag(mh, stride, cpos, kb, g), col_frag(ml, stride, cpos, kb, g)};
+}
+__device__ __forceinline__ f32x4 mma3(f32x4 acc, SFrag a, SFrag b) {
+  acc = mma<bf16_t>(acc, a.l, b.h);
+  acc = mma<bf16_t>(acc, a.h, b.l);
+  return mma<bf16_t>(acc, a.h, b.h);
+}
+__device__ __forceinline__ f32x4 mma2a(f32x4 acc, Frag a, SFrag b) {   // A exact in bf16
+  acc = mma<bf16_t>(acc, a, b.l);
+  return mma<bf16_t>(acc, a, b.h);
+}
+__device__ __forceinline__ f32x4 mma2b(f32x4 acc, SFrag a, Frag b) {   // B exact in bf16
+  acc = mma<bf16_t>(acc, a.l, b);
+  return mma<bf16_t>(acc, a.h, b);
+}
+
 // threads of the grad kernel: two waves per SIMD, so that one wave's LDS and
 // matrix-core latencies overlap the other's (its LDS keeps one workgroup per
 // CU at dk = 128)
@@ -772,23 +826,61 @@ __global__ __launch_bounds__(kGThreads) void chunk_bwd_grad_kernel(
   constexpr int NW = kGThreads / 64;
   static_assert(DS == 16 || DS == 32, "value slices are one or two 16-column blocks");
   using R = BwdRec<DK>;
-  // big area: KG, KR and the slice buffers during the value-slice loop; the
-  // accumulated dQG, dKG, dKR and the per-channel scratch columns afterwards
+  // SG: bf16 inputs with 32-column slices: the value-slice loop on split bf16
+  // operands (bf16 matrix cores, 3 steps of 32 K where fp32 takes 8 of 4)
+  constexpr bool SG = std::is_same<T, bf16_t>::value && DS == 32 && DK >= 32;
+  // split-bf16 areas (in 2-byte units): per chunk KG, KR (hi, lo; rows of
+  // KP), M^T, TB (hi, lo; rows of CP2); per slice H, dH' (hi, lo; DK rows of
+  // SP), dO (bf16, C rows of SP), V (as stored, C x DS), X, U, dU, dX (hi, lo;
+  // C rows of SP).  Row strides are multiples of 16 bytes.
+  constexpr int KP = DK + 8, SP = DS + 8, CP2 = C + 8;
+  constexpr int SG_U16 = 4 * C * KP + 4 * C * CP2 + 4 * DK * SP + C * SP + C * DS + 8 * C * SP;
+  // after the loop: dQG, dKG, dKR, the per-channel scratch, (SG) the halving's
+  // scan inputs and the slots' H . dH' partial sums
+  constexpr int POST = 3 * C * DKP + C * DK + (SG ? C * DK + DK * DS : 0);
+  // big area: KG, KR and the slice buffers during the value-slice loop (SG:
+  // the split areas), the accumulated dQG, dKG, dKR and the per-channel
+  // scratch columns afterwards
   constexpr int SLICE = 2 * DK * DSP + 5 * C * DSP;
-  constexpr int BIG = (2 * C * DKP + SLICE) > 3 * C * DKP + C * DK ? (2 * C * DKP + SLICE) : 3 * C * DKP + C * DK;
+  constexpr int LOOP = SG ? (SG_U16 + 1) / 2 : 2 * C * DKP + SLICE;
+  constexpr int BIG = LOOP > POST ? LOOP : POST;
   // q, k and alpha in their input type (bf16 inputs are kept exactly)
   __shared__ T sq[C * DKP], sk[C * DKP], sa[C * DKP];
-  __shared__ float big[BIG];
-  // C x C matrices; TB, T, S and P (the last four) are consumed before the
-  // halving, which keeps its scan inputs there
-  __shared__ float sCC[7 * C * CP];
-  float* sM = sCC;
-  float* sdM = sCC + C * CP;
-  float* sdTB = sCC + 2 * C * CP;
-  float* sTB = sCC + 3 * C * CP;
-  float* sT = sCC + 4 * C * CP;
-  float* sS = sCC + 5 * C * CP;
-  float* sP = sCC + 6 * C * CP;
+  __shared__ __align__(16) float big[BIG];
+  // C x C matrices: (not SG) M and TB for the loop; dM, dTB; T, S and P, which
+  // are consumed before the halving's scalar passes keep data there
+  constexpr int NCC = SG ? 5 : 7;
+  __shared__ float sCC[NCC * C * CP];
+  float* sM = SG ? nullptr : sCC;
+  float* sdM = sCC + (SG ? 0 : 1) * C * CP;
+  float* sdTB = sCC + (SG ? 1 : 2) * C * CP;
+  float* sTB = SG ? nullptr : sCC + 3 * C * CP;
+  float* sT = sCC + (SG ? 2 : 4) * C * CP;
+  float* sS = sCC + (SG ? 3 : 5) * C * CP;
+  float* sP = sCC + (SG ? 4 : 6) * C * CP;
+  using u16 = unsigned short;
+  u16* KGh = reinterpret_cast<u16*>(big);
+  u16* KGl = KGh + C * KP;
+  u16* KRh = KGl + C * KP;
+  u16* KRl = KRh + C * KP;
+  u16* MTh = KRl + C * KP;
+  u16* MTl = MTh + C * CP2;
+  u16* TBh = MTl + C * CP2;
+  u16* TBl = TBh + C * CP2;
+  u16* Hh = TBl + C * CP2;
+  u16* Hl = Hh + DK * SP;
+  u16* dHh = Hl + DK * SP;
+  u16* dHl = dHh + DK * SP;
+  u16* dOb = dHl + DK * SP;
+  u16* Vb = dOb + C * SP;
+  u16* Xh = Vb + C * DS;
+  u16* Xl = Xh + C * SP;
+  u16* Uh = Xl + C * SP;
+  u16* Ul = Uh + C * SP;
+  u16* dUh = Ul + C * SP;
+  u16* dUl = dUh + C * SP;
+  u16* dXh = dUl + C * SP;
+  u16* dXl = dXh + C * SP;
   __shared__ float sb[C], sdb[C], sGC[DK];
   float* sKG = big;
   float* sKR = big + C * DKP;
@@ -839,8 +931,14 @@ __global__ __launch_bounds__(kGThreads) void chunk_bwd_grad_kernel(
         sq[o] = from_f32<T>(r0[i]);
         sk[o] = from_f32<T>(r1[i]);
         sa[o] = from_f32<T>(r2[i]);
-        sKG[o] = r3[i];
-        sKR[o] = r4[i];
+        if constexpr (SG) {
+          const int os = (e / DK) * KP + kperm(e % DK);
+          split_bits(r3[i], KGh[os], KGl[os]);
+          split_bits(r4[i], KRh[os], KRl[os]);
+        } else {
+          sKG[o] = r3[i];
+          sKR[o] = r4[i];
+        }
       }
     }
 #pragma unroll
@@ -848,8 +946,14 @@ __global__ __launch_bounds__(kGThreads) void chunk_bwd_grad_kernel(
       const int e = tid + i * kGThreads;
       if (e < C * C) {
         const int o = (e / C) * CP + e % C;
-        sM[(e % C) * CP + e / C] = m0[i];   // the record holds M^T
-        sTB[o] = m1[i];
+        if constexpr (SG) {   // the record holds M^T, the A operand of M^T dO
+          const int os = (e / C) * CP2 + kperm(e % C);
+          split_bits(m0[i], MTh[os], MTl[os]);
+          split_bits(m1[i], TBh[os], TBl[os]);
+        } else {
+          sM[(e % C) * CP + e / C] = m0[i];   // the record holds M^T
+          sTB[o] = m1[i];
+        }
         sT[o] = m2[i];
         sS[o] = m3[i];
       }
@@ -890,6 +994,119 @@ __global__ __launch_bounds__(kGThreads) void chunk_bwd_grad_kernel(
     }
   };
   fetch(0);
+  if constexpr (SG) {
+    // per slot, H . dH' summed over the slices (the slot's row is the same in
+    // every slice), reduced per channel after the loop in a fixed order
+    float gcp[NH];
+#pragma unroll
+    for (int i = 0; i < NH; ++i) gcp[i] = 0.f;
+    const int tq = wave & 3, prt = tq >> 1, pct = tq & 1;   // a wave's tile of the C x DS products
+    const int cpos = kperm(16 * pct + r);                     // its column's storage position
+    for (int col0 = 0; col0 < dv; col0 += DS) {
+      __syncthreads();   // previous slice fully consumed (and, first time, the loads above)
+#pragma unroll
+      for (int i = 0; i < NH; ++i) {
+        const int e = tid + i * kGThreads;
+        if (e < DK * DS) {
+          // slot e of 16-column block b = e / (16 dk) holds, with l = e % (16 dk),
+          // row 16 (l / 256) + 4 ((l / 64) % 4) + l % 4, column 16 b + (l / 4) % 16
+          const int b = e / (16 * DK), l = e % (16 * DK);
+          const int o = (16 * (l / 256) + 4 * ((l / 64) % 4) + l % 4) * SP + kperm(16 * b + (l / 4) % 16);
+          split_bits(rH[i], Hh[o], Hl[o]);
+          split_bits(rdH[i], dHh[o], dHl[o]);
+          gcp[i] += rH[i] * rdH[i];
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const int e = tid + i * kGThreads;
+        if (e < C * DS) {   // exact in bf16 (the inputs)
+          Vb[e] = (u16)(__float_as_uint(rV[i]) >> 16);
+          dOb[(e / DS) * SP + kperm(e % DS)] = (u16)(__float_as_uint(rO[i]) >> 16);
+        }
+      }
+      __syncthreads();
+      if (col0 + DS < dv) fetch(col0 + DS);
+      // waves 0-3: X = V - KG H; waves 4-7: dU = M^T dO + KR dH'  (tile prt, pct)
+      {
+        f32x4 acc = zero4();
+        if (wave < 4) {
+#pragma unroll
+          for (int kb = 0; kb < DK / 32; ++kb)
+            acc = mma3(acc, srow(KGh, KGl, KP, 16 * prt + r, kb, g), scol(Hh, Hl, SP, cpos, kb, g));
+#pragma unroll
+          for (int vv = 0; vv < 4; ++vv) {
+            const int t = 16 * prt + 4 * g + vv;
+            split_bits(bits_f32(Vb[t * DS + 16 * pct + r]) - acc[vv], Xh[t * SP + cpos], Xl[t * SP + cpos]);
+          }
+        } else {
+          acc = mma2b(acc, srow(MTh, MTl, CP2, 16 * prt + r, 0, g), col_frag(dOb, SP, cpos, 0, g));
+#pragma unroll
+          for (int kb = 0; kb < DK / 32; ++kb)
+            acc = mma3(acc, srow(KRh, KRl, KP, 16 * prt + r, kb, g), scol(dHh, dHl, SP, cpos, kb, g));
+#pragma unroll
+          for (int vv = 0; vv < 4; ++vv) {
+            const int t = 16 * prt + 4 * g + vv;
+            split_bits(acc[vv], dUh[t * SP + cpos], dUl[t * SP + cpos]);
+          }
+        }
+      }
+      __syncthreads();
+      // waves 0-3: U = TB X; waves 4-7: dX = TB^T dU (= dv, stored)
+      {
+        f32x4 acc = zero4();
+        if (wave < 4) {
+          acc = mma3(acc, srow(TBh, TBl, CP2, 16 * prt + r, 0, g), scol(Xh, Xl, SP, cpos, 0, g));
+#pragma unroll
+          for (int vv = 0; vv < 4; ++vv) {
+            const int t = 16 * prt + 4 * g + vv;
+            split_bits(acc[vv], Uh[t * SP + cpos], Ul[t * SP + cpos]);
+          }
+        } else {
+          // TB^T's row t is TB's column t: a column fragment of TB
+          acc = mma3(acc, scol(TBh, TBl, CP2, kperm(16 * prt + r), 0, g), scol(dUh, dUl, SP, cpos, 0, g));
+#pragma unroll
+          for (int vv = 0; vv < 4; ++vv) {
+            const int t = 16 * prt + 4 * g + vv;
+            split_bits(acc[vv], dXh[t * SP + cpos], dXl[t * SP + cpos]);
+            if (t < cv) dvo[(size_t)(row0 + t) * dv + col0 + 16 * pct + r] = acc[vv];
+          }
+        }
+      }
+      __syncthreads();
+      // dQG += dO H^T, dKG += dX H^T (negated when stored), dKR += U dH'^T  (C x DK, K = DS)
+#pragma unroll
+      for (int i = 0; i < TPW; ++i) {
+        const int ti = wave + NW * i;
+        if (ti < TQ) {
+          const int i0 = (ti / (DK / 16)) * 16, j0 = (ti % (DK / 16)) * 16;
+          const SFrag bh = srow(Hh, Hl, SP, j0 + r, 0, g);
+          aqg[i] = mma2a(aqg[i], row_frag(dOb, SP, i0 + r, 0, g), bh);
+          akg[i] = mma3(akg[i], srow(dXh, dXl, SP, i0 + r, 0, g), bh);
+          akr[i] = mma3(akr[i], srow(Uh, Ul, SP, i0 + r, 0, g), srow(dHh, dHl, SP, j0 + r, 0, g));
+        }
+      }
+      // waves 0-3: dM += dO U^T; waves 4-7: dTB += dU X^T  (C x C, K = DS)
+      if (wave < 4) am[0] = mma2a(am[0], row_frag(dOb, SP, 16 * prt + r, 0, g), srow(Uh, Ul, SP, 16 * pct + r, 0, g));
+      else atb[0] = mma3(atb[0], srow(dUh, dUl, SP, 16 * prt + r, 0, g), srow(Xh, Xl, SP, 16 * pct + r, 0, g));
+    }
+    __syncthreads();
+    // H . dH' per channel: the channel's 16 DS / 16 slots, in a fixed order
+    float* gpart = big + 3 * C * DKP + 2 * C * DK;   // [slot]
+#pragma unroll
+    for (int i = 0; i < NH; ++i) {
+      const int e = tid + i * kGThreads;
+      if (e < DK * DS) gpart[e] = gcp[i];
+    }
+    __syncthreads();
+    if (tid < DK) {
+      const int ch = tid;
+      float acc = 0.f;
+      for (int b = 0; b < DS / 16; ++b)
+        for (int m = 0; m < 16; ++m) acc += gpart[b * 16 * DK + 256 * (ch / 16) + 64 * ((ch % 16) / 4) + 4 * m + ch % 4];
+      sGC[ch] = acc;
+    }
+  } else
   for (int col0 = 0; col0 < dv; col0 += DS) {
     __syncthreads();   // previous slice fully consumed (and, first time, the loads above)
 #pragma unroll
@@ -973,16 +1190,27 @@ __global__ __launch_bounds__(kGThreads) void chunk_bwd_grad_kernel(
       }
     }
   }
+  if constexpr (SG) {   // dM on waves 0-3, dTB on waves 4-7, tile wave % 4
+    const int tq = wave & 3, i0 = (tq >> 1) * 16, j0 = (tq & 1) * 16;
+    float* dst = wave < 4 ? sdM : sdTB;
+    const f32x4 a = wave < 4 ? am[0] : atb[0];
 #pragma unroll
-  for (int i = 0; i < TMW; ++i) {
-    const int ti = wave + NW * i;
-    if (ti < TM) {
-      const int i0 = (ti / (C / 16)) * 16, j0 = (ti % (C / 16)) * 16;
+    for (int vv = 0; vv < 4; ++vv) {
+      const int row = i0 + 4 * g + vv, col = j0 + r;
+      dst[row * CP + col] = col <= row ? a[vv] : 0.f;
+    }
+  } else {
 #pragma unroll
-      for (int vv = 0; vv < 4; ++vv) {
-        const int row = i0 + 4 * g + vv, col = j0 + r;
-        sdM[row * CP + col] = col <= row ? am[i][vv] : 0.f;
-        sdTB[row * CP + col] = col <= row ? atb[i][vv] : 0.f;
+    for (int i = 0; i < TMW; ++i) {
+      const int ti = wave + NW * i;
+      if (ti < TM) {
+        const int i0 = (ti / (C / 16)) * 16, j0 = (ti % (C / 16)) * 16;
+#pragma unroll
+        for (int vv = 0; vv < 4; ++vv) {
+          const int row = i0 + 4 * g + vv, col = j0 + r;
+          sdM[row * CP + col] = col <= row ? am[i][vv] : 0.f;
+          sdTB[row * CP + col] = col <= row ? atb[i][vv] : 0.f;
+        }
       }
     }
   }
@@ -1047,8 +1275,9 @@ __global__ __launch_bounds__(kGThreads) void chunk_bwd_grad_kernel(
     // gate product) go through LDS, and each then completes its positions.
     constexpr int NS = 4, SL = C / NS;
     static_assert(P >= NS, "a thread per channel and segment");
-    float* xs = sCC + 3 * C * CP;   // [4][NS][DK] carries: TB, T, S and P are consumed
-    static_assert(3 * C * CP + 4 * NS * DK <= 7 * C * CP, "carries fit in the consumed C x C arrays");
+    // [4][NS][DK] carries, in C x C arrays consumed by now (T, S, P and, not SG, TB)
+    float* xs = SG ? sT : sCC + 3 * C * CP;
+    static_assert(4 * NS * DK <= 3 * C * CP, "carries fit in the consumed C x C arrays");
     const bool segon = part < NS;
     const int t0s = part * SL;
     float av[SL], pl[SL + 1], sl[SL], fl[SL], bl[SL], ml[SL];
@@ -1154,8 +1383,10 @@ __global__ __launch_bounds__(kGThreads) void chunk_bwd_grad_kernel(
     // on R, s from last to first, b_s = Z_s + alpha_{s+1} b_{s+1} and dalpha_s
     // += G(s - 1, 15) b_s (1 at s = 16); on L, j from first to last, dalpha_j +=
     // G(15, j) f and f = alpha_j f + Z_j.
-    float* Z = sCC + 3 * C * CP;   // [t][channel]: TB, T, S and P are consumed
-    static_assert(3 * C * CP + C * DK <= 7 * C * CP, "scan inputs fit in the consumed C x C arrays");
+    // [t][channel]: (not SG) in TB, T, S and P, consumed by now; (SG) after the
+    // scratch columns in the big area
+    float* Z = SG ? big + 3 * C * DKP + C * DK : sCC + 3 * C * CP;
+    static_assert(SG || C * DK <= 4 * C * CP, "scan inputs fit in the consumed C x C arrays");
     const float* sgall = big + 3 * C * DKP;
     auto level16 = [&]() __attribute__((always_inline)) {
       constexpr int h = C / 2;
