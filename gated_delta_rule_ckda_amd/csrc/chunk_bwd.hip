@@ -42,11 +42,25 @@ constexpr int kBC = 32;          // positions per backward chunk
 constexpr int kBThreads = 256;
 constexpr int kBDS = 16;         // value columns per slice
 
-// per-chunk fp32 record of the prep kernel (offsets in floats), row-major:
-// M^T, TB, TB^T, T, S (C x C); KG, KG^T, KR, KR^T, QG^T (C x DK or DK x C);
-// Gamma_C (DK).  The sequential kernels read matrix-core A fragments straight
-// from it, 16 bytes of a row along the contraction each: the states kernel
-// KG, TB, KR^T; the dstates kernel M^T, KR, TB^T, QG^T, KG^T.
+// per-chunk fp32 record of the prep kernel (offsets in floats): M^T, TB,
+// TB^T, T, S (C x C); KG, KG^T, KR, KR^T, QG^T (C x DK or DK x C); Gamma_C
+// (DK).  T and S are row-major; the others, the matrix-core A operands of the
+// sequential kernels (the states kernel KG, TB, KR^T; the dstates kernel
+// M^T, KR, TB^T, QG^T, KG^T), are in fragment order (frag_off), so that a
+// wave reads one operand fragment as 1 KB in one piece.
+// Fragment order of an fp32 A operand with R rows and KD columns (K, the
+// contraction): 16 x 16 tiles (row tile, K tile) in row-major order, 256
+// floats each, lane 16 g + r holding row r, columns 4 g .. 4 g + 3 of its tile.
+__host__ __device__ constexpr int frag_off(int row, int k, int KD) {
+  return ((row / 16) * (KD / 16) + k / 16) * 256 + ((((k % 16) / 4) * 16 + row % 16) * 4) + k % 4;
+}
+// the inverse: row and column of the element at offset e
+__device__ __forceinline__ void frag_pos(int e, int KD, int& row, int& k) {
+  const int f = e / 256, w = e % 256, ln = w / 4;
+  row = 16 * (f / (KD / 16)) + ln % 16;
+  k = 16 * (f % (KD / 16)) + 4 * (ln / 16) + w % 4;
+}
+
 template <int DK>
 struct BwdRec {
   static constexpr int C = kBC;
@@ -228,10 +242,10 @@ __global__ __launch_bounds__(kPThreads) void chunk_bwd_prep_kernel(const T* q, c
       gm *= ca[t];
       kg[t % 4] = ck[t] * gm;
       qg[t % 4] = cq[t] * gm;
-      rc[R::KG_OFF + t * DK + ch] = kg[t % 4];
+      rc[R::KG_OFF + frag_off(t, ch, DK)] = kg[t % 4];
       if (t % 4 == 3) {   // KG^T, QG^T: this channel's rows, 16 bytes at a time
-        *reinterpret_cast<f32x4*>(rc + R::KGT_OFF + ch * C + t - 3) = f32x4{kg[0], kg[1], kg[2], kg[3]};
-        *reinterpret_cast<f32x4*>(rc + R::QGT_OFF + ch * C + t - 3) = f32x4{qg[0], qg[1], qg[2], qg[3]};
+        *reinterpret_cast<f32x4*>(rc + R::KGT_OFF + frag_off(ch, t - 3, C)) = f32x4{kg[0], kg[1], kg[2], kg[3]};
+        *reinterpret_cast<f32x4*>(rc + R::QGT_OFF + frag_off(ch, t - 3, C)) = f32x4{qg[0], qg[1], qg[2], qg[3]};
       }
     }
     rc[R::GC_OFF + ch] = gm;
@@ -240,9 +254,9 @@ __global__ __launch_bounds__(kPThreads) void chunk_bwd_prep_kernel(const T* q, c
     for (int t = C - 1; t >= 0; --t) {
       kr[t % 4] = ck[t] * ge;
       ge *= ca[t];
-      rc[R::KR_OFF + t * DK + ch] = kr[t % 4];
+      rc[R::KR_OFF + frag_off(t, ch, DK)] = kr[t % 4];
       if (t % 4 == 0)   // KR^T: this channel's row
-        *reinterpret_cast<f32x4*>(rc + R::KRT_OFF + ch * C + t) = f32x4{kr[0], kr[1], kr[2], kr[3]};
+        *reinterpret_cast<f32x4*>(rc + R::KRT_OFF + frag_off(ch, t, C)) = f32x4{kr[0], kr[1], kr[2], kr[3]};
     }
   }
   {   // diagonal of M (G = 1): kPThreads / C threads per row
@@ -364,10 +378,11 @@ __global__ __launch_bounds__(kPThreads) void chunk_bwd_prep_kernel(const T* q, c
   __syncthreads();
   for (int e = tid; e < C * C; e += kPThreads) {
     const int i = e / C, j = e % C;
-    rc[R::MT_OFF + e] = sM[j * CP + i];
+    const int fo = frag_off(i, j, C);
+    rc[R::MT_OFF + fo] = sM[j * CP + i];
     rc[R::T_OFF + e] = sT[i * CP + j];
-    rc[R::TB_OFF + e] = sT[i * CP + j] * sb[j];
-    rc[R::TBT_OFF + e] = sT[j * CP + i] * sb[i];
+    rc[R::TB_OFF + fo] = sT[i * CP + j] * sb[j];
+    rc[R::TBT_OFF + fo] = sT[j * CP + i] * sb[i];
     rc[R::S_OFF + e] = sS[i * CP + j];
   }
 }
@@ -432,7 +447,7 @@ __global__ __launch_bounds__(64) void chunk_bwd_states_kernel(const T* v, const 
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
       for (int kb = 0; kb < RH; ++kb)
-        kg[rt][kb] = *reinterpret_cast<const f32x4*>(rc + R::KG_OFF + (16 * rt + r) * DK + 16 * kb + 4 * g);
+        kg[rt][kb] = *reinterpret_cast<const f32x4*>(rc + R::KG_OFF + (rt * (DK / 16) + kb) * 256 + 4 * lane);
   };
   auto load_tb_v = [&](int c) __attribute__((always_inline)) {
     const float* rc = recp(c);
@@ -440,7 +455,7 @@ __global__ __launch_bounds__(64) void chunk_bwd_states_kernel(const T* v, const 
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
       for (int kb = 0; kb <= rt; ++kb)
-        tb[rt][kb] = *reinterpret_cast<const f32x4*>(rc + R::TB_OFF + (16 * rt + r) * C + 16 * kb + 4 * g);
+        tb[rt][kb] = *reinterpret_cast<const f32x4*>(rc + R::TB_OFF + (rt * RT + kb) * 256 + 4 * lane);
     // unconditional loads (a row past the end reads the chunk's first row and
     // is masked where it is used), kept as stored so that nothing waits for
     // them before the next chunk
@@ -459,7 +474,7 @@ __global__ __launch_bounds__(64) void chunk_bwd_states_kernel(const T* v, const 
     for (int rh = 0; rh < RH; ++rh)
 #pragma unroll
       for (int kb = 0; kb < RT; ++kb)
-        kr[rh][kb] = *reinterpret_cast<const f32x4*>(rc + R::KRT_OFF + (16 * rh + r) * C + 16 * kb + 4 * g);
+        kr[rh][kb] = *reinterpret_cast<const f32x4*>(rc + R::KRT_OFF + (rh * RT + kb) * 256 + 4 * lane);
 #pragma unroll
     for (int rh = 0; rh < RH; ++rh) gc[rh] = *reinterpret_cast<const f32x4*>(rc + R::GC_OFF + 16 * rh + 4 * g);
   };
@@ -595,12 +610,12 @@ __global__ __launch_bounds__(128) void chunk_bwd_dstates_kernel(const T* dout, c
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
       for (int kb = 0; kb < RHW; ++kb)
-        o.kr[rt][kb] = *reinterpret_cast<const f32x4*>(rc + R::KR_OFF + (16 * rt + r) * DK + 16 * (rb + kb) + 4 * g);
+        o.kr[rt][kb] = *reinterpret_cast<const f32x4*>(rc + R::KR_OFF + (rt * (DK / 16) + rb + kb) * 256 + 4 * lane);
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
       for (int kb = rt; kb < RT; ++kb)
-        o.mt[rt][kb] = *reinterpret_cast<const f32x4*>(rc + R::MT_OFF + (16 * rt + r) * C + 16 * kb + 4 * g);
+        o.mt[rt][kb] = *reinterpret_cast<const f32x4*>(rc + R::MT_OFF + (rt * RT + kb) * 256 + 4 * lane);
     const int t0 = c * C, cv = min(C, T_len - t0);
 #pragma unroll
     for (int kb = 0; kb < RT; ++kb)
@@ -616,7 +631,7 @@ __global__ __launch_bounds__(128) void chunk_bwd_dstates_kernel(const T* dout, c
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
       for (int kb = rt; kb < RT; ++kb)
-        tbt[rt][kb] = *reinterpret_cast<const f32x4*>(rc + R::TBT_OFF + (16 * rt + r) * C + 16 * kb + 4 * g);
+        tbt[rt][kb] = *reinterpret_cast<const f32x4*>(rc + R::TBT_OFF + (rt * RT + kb) * 256 + 4 * lane);
   };
   auto load_last = [&](int c) __attribute__((always_inline)) {
     const float* rc = recp(c);
@@ -624,8 +639,8 @@ __global__ __launch_bounds__(128) void chunk_bwd_dstates_kernel(const T* dout, c
     for (int rh = 0; rh < RHW; ++rh)
 #pragma unroll
       for (int kb = 0; kb < RT; ++kb) {
-        qgt[rh][kb] = *reinterpret_cast<const f32x4*>(rc + R::QGT_OFF + (16 * (rb + rh) + r) * C + 16 * kb + 4 * g);
-        kgt[rh][kb] = *reinterpret_cast<const f32x4*>(rc + R::KGT_OFF + (16 * (rb + rh) + r) * C + 16 * kb + 4 * g);
+        qgt[rh][kb] = *reinterpret_cast<const f32x4*>(rc + R::QGT_OFF + ((rb + rh) * RT + kb) * 256 + 4 * lane);
+        kgt[rh][kb] = *reinterpret_cast<const f32x4*>(rc + R::KGT_OFF + ((rb + rh) * RT + kb) * 256 + 4 * lane);
       }
 #pragma unroll
     for (int rh = 0; rh < RHW; ++rh)
@@ -931,13 +946,15 @@ __global__ __launch_bounds__(kGThreads) void chunk_bwd_grad_kernel(
         sq[o] = from_f32<T>(r0[i]);
         sk[o] = from_f32<T>(r1[i]);
         sa[o] = from_f32<T>(r2[i]);
+        int tt, cc;   // KG and KR are in fragment order
+        frag_pos(e, DK, tt, cc);
         if constexpr (SG) {
-          const int os = (e / DK) * KP + kperm(e % DK);
+          const int os = tt * KP + kperm(cc);
           split_bits(r3[i], KGh[os], KGl[os]);
           split_bits(r4[i], KRh[os], KRl[os]);
         } else {
-          sKG[o] = r3[i];
-          sKR[o] = r4[i];
+          sKG[tt * DKP + cc] = r3[i];
+          sKR[tt * DKP + cc] = r4[i];
         }
       }
     }
@@ -946,13 +963,15 @@ __global__ __launch_bounds__(kGThreads) void chunk_bwd_grad_kernel(
       const int e = tid + i * kGThreads;
       if (e < C * C) {
         const int o = (e / C) * CP + e % C;
+        int ii, jj;   // M^T and TB are in fragment order, T and S row-major
+        frag_pos(e, C, ii, jj);
         if constexpr (SG) {   // the record holds M^T, the A operand of M^T dO
-          const int os = (e / C) * CP2 + kperm(e % C);
+          const int os = ii * CP2 + kperm(jj);
           split_bits(m0[i], MTh[os], MTl[os]);
           split_bits(m1[i], TBh[os], TBl[os]);
         } else {
-          sM[(e % C) * CP + e / C] = m0[i];   // the record holds M^T
-          sTB[o] = m1[i];
+          sM[jj * CP + ii] = m0[i];   // the record holds M^T
+          sTB[ii * CP + jj] = m1[i];
         }
         sT[o] = m2[i];
         sS[o] = m3[i];
