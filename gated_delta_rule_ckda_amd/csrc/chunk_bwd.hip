@@ -703,6 +703,20 @@ __global__ __launch_bounds__(128) void chunk_bwd_dstates_kernel(const T* dout, c
           du[rt] = mma<float>(du[rt], Frag{__builtin_bit_cast(u32x4, cur.kr[rt][kb])}, frag_from_acc_f32(dacc[kb]));
       }
     }
+    // the part of dH that does not wait for dX: Gamma_C . dH' + QG^T dO, issued
+    // before the exchange so that it runs while the waves meet
+    f32x4 hp[RHW];
+#pragma unroll
+    for (int rh = 0; rh < RHW; ++rh) {
+      hp[rh] = gc[rh] * dacc[rh];
+      if constexpr (SPLIT) {
+        hp[rh] = mma_split_exact(hp[rh], split_frag(qgt[rh][0], qgt[rh][1]), dob);
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < RT; ++kb)
+          hp[rh] = mma<float>(hp[rh], Frag{__builtin_bit_cast(u32x4, qgt[rh][kb])}, frag_from_acc_f32(dof[kb]));
+      }
+    }
     if constexpr (NW == 2) {
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) xb[par][wave][rt][lane] = du[rt];
@@ -734,14 +748,10 @@ __global__ __launch_bounds__(128) void chunk_bwd_dstates_kernel(const T* dout, c
     if constexpr (SPLIT) ndxs = split_frag(ndx[0], ndx[1]);
 #pragma unroll
     for (int rh = 0; rh < RHW; ++rh) {
-      f32x4 h = gc[rh] * dacc[rh];
+      f32x4 h = hp[rh];
       if constexpr (SPLIT) {
-        h = mma_split_exact(h, split_frag(qgt[rh][0], qgt[rh][1]), dob);
         h = mma_split(h, split_frag(kgt[rh][0], kgt[rh][1]), ndxs);
       } else {
-#pragma unroll
-        for (int kb = 0; kb < RT; ++kb)
-          h = mma<float>(h, Frag{__builtin_bit_cast(u32x4, qgt[rh][kb])}, frag_from_acc_f32(dof[kb]));
 #pragma unroll
         for (int kb = 0; kb < RT; ++kb)
           h = mma<float>(h, Frag{__builtin_bit_cast(u32x4, kgt[rh][kb])}, frag_from_acc_f32(ndx[kb]));
