@@ -801,15 +801,23 @@ __device__ __forceinline__ float bits_f32(unsigned short b) { return __uint_as_f
 __device__ __forceinline__ Frag row_frag(const unsigned short* m, int stride, int row, int kb, int g) {
   return load_frag(m + row * stride + 32 * kb + 8 * g);
 }
-// lane (r, g): column position `cpos`, rows 32 kb + kappa(g, e)
+// lane (r, g): column position `cpos` = kperm(16 b + r) of a 16-column block
+// b (the same b for the whole wave), rows 32 kb + kappa(g, e), as two
+// transposing LDS reads (ds_read_b64_tr_b16).  Within each 16-lane group, that
+// read gives lane i, as its element j, element i % 4 of the 8 bytes that lane
+// 4 j + i / 4 of the group addresses; so lane (g, s) addresses row 4 g + s / 4
+// (16 rows further for the second read) at column position 8 (s % 4) + 4 b,
+// the first of the 4 consecutive positions kperm gives lanes 4 (s % 4) .. + 3.
 __device__ __forceinline__ Frag col_frag(const unsigned short* m, int stride, int cpos, int kb, int g) {
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) v4s lds_v4s;
+  const int s = threadIdx.x & 15;
+  const unsigned short* p = m + (32 * kb + 4 * g + (s >> 2)) * stride + 8 * (s & 3) + (cpos & 4);
+  const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)p);
+  const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p + 16 * stride));
+  const u32x2 a = __builtin_bit_cast(u32x2, lo), b = __builtin_bit_cast(u32x2, hi);
   Frag f;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t a = m[(32 * kb + kappa<bf16_t>(g, 2 * i)) * stride + cpos];
-    const uint32_t b = m[(32 * kb + kappa<bf16_t>(g, 2 * i + 1)) * stride + cpos];
-    f.w[i] = a | (b << 16);
-  }
+  f.w = u32x4{a[0], a[1], b[0], b[1]};
   return f;
 }
 struct SFrag {
