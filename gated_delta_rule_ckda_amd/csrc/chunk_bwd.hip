@@ -61,6 +61,14 @@ __device__ __forceinline__ void frag_pos(int e, int KD, int& row, int& k) {
   k = 16 * (f % (KD / 16)) + 4 * (ln / 16) + w % 4;
 }
 
+// Split record (bf16 inputs, dk >= 64, d_v a multiple of 32: every consumer
+// multiplies split bf16 pairs).  The matrix-core A operands (KG, KG^T, KR,
+// KR^T, QG^T, M^T, TB, TB^T) are stored as the pairs themselves, in the same
+// bytes: the two fp32 tiles (row tile, 2 kb) and (row tile, 2 kb + 1) of K
+// block kb (32 wide) hold the hi and the lo bf16 fragments of that block,
+// lane 16 g + r's 16 bytes being row r, K = 32 kb + kappa(g, e), e = 0..7
+// (hi = bf16(x), lo = bf16(x - hi), as split_frag forms them from fp32).
+// T, S and Gamma_C stay fp32.
 template <int DK>
 struct BwdRec {
   static constexpr int C = kBC;
@@ -167,12 +175,28 @@ __device__ __forceinline__ f32x4 mma_split_exact(f32x4 acc, SplitFrag a, Frag b)
   return mma<bf16_t>(acc, a.h, b);
 }
 
+// hi and lo of 8 values as two bf16 fragments, the values in the fragment's
+// element order (hi = bf16(x), lo = bf16(x - hi), as split_frag forms them)
+__device__ __forceinline__ void split8(const float* x, u32x4& h, u32x4& l) {
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const uint32_t w = pack_bf16x2(x[2 * p], x[2 * p + 1]);
+    h[p] = w;
+    l[p] = pack_bf16x2(x[2 * p] - bf16_lo_half(w), x[2 * p + 1] - bf16_hi_half(w));
+  }
+}
+// A operand `a` as a split pair read from a split record: the two tiles' 16
+// bytes are the hi and lo fragments
+__device__ __forceinline__ SplitFrag rec_pair(f32x4 hi, f32x4 lo) {
+  return SplitFrag{Frag{__builtin_bit_cast(u32x4, hi)}, Frag{__builtin_bit_cast(u32x4, lo)}};
+}
+
 // ============================================================ prep
 // threads of the prep kernel (its LDS keeps one workgroup per CU at dk = 128;
 // two waves per SIMD hide part of each one's latencies)
 constexpr int kPThreads = 512;
 
-template <typename T, int DK>
+template <typename T, int DK, bool RS>
 __global__ __launch_bounds__(kPThreads) void chunk_bwd_prep_kernel(const T* q, const T* k, const T* alpha,
                                                                    const T* beta, float* __restrict__ rec, int T_len,
                                                                    int nchunks) {
@@ -242,10 +266,15 @@ __global__ __launch_bounds__(kPThreads) void chunk_bwd_prep_kernel(const T* q, c
       gm *= ca[t];
       kg[t % 4] = ck[t] * gm;
       qg[t % 4] = cq[t] * gm;
-      rc[R::KG_OFF + frag_off(t, ch, DK)] = kg[t % 4];
-      if (t % 4 == 3) {   // KG^T, QG^T: this channel's rows, 16 bytes at a time
-        *reinterpret_cast<f32x4*>(rc + R::KGT_OFF + frag_off(ch, t - 3, C)) = f32x4{kg[0], kg[1], kg[2], kg[3]};
-        *reinterpret_cast<f32x4*>(rc + R::QGT_OFF + frag_off(ch, t - 3, C)) = f32x4{qg[0], qg[1], qg[2], qg[3]};
+      if constexpr (RS) {   // to LDS; all threads write the split record below
+        sx[t * XP + ch] = kg[t % 4];
+        sxq[t * XP + ch] = qg[t % 4];
+      } else {
+        rc[R::KG_OFF + frag_off(t, ch, DK)] = kg[t % 4];
+        if (t % 4 == 3) {   // KG^T, QG^T: this channel's rows, 16 bytes at a time
+          *reinterpret_cast<f32x4*>(rc + R::KGT_OFF + frag_off(ch, t - 3, C)) = f32x4{kg[0], kg[1], kg[2], kg[3]};
+          *reinterpret_cast<f32x4*>(rc + R::QGT_OFF + frag_off(ch, t - 3, C)) = f32x4{qg[0], qg[1], qg[2], qg[3]};
+        }
       }
     }
     rc[R::GC_OFF + ch] = gm;
@@ -254,10 +283,67 @@ __global__ __launch_bounds__(kPThreads) void chunk_bwd_prep_kernel(const T* q, c
     for (int t = C - 1; t >= 0; --t) {
       kr[t % 4] = ck[t] * ge;
       ge *= ca[t];
-      rc[R::KR_OFF + frag_off(t, ch, DK)] = kr[t % 4];
-      if (t % 4 == 0)   // KR^T: this channel's row
-        *reinterpret_cast<f32x4*>(rc + R::KRT_OFF + frag_off(ch, t, C)) = f32x4{kr[0], kr[1], kr[2], kr[3]};
+      if constexpr (RS) {
+        sy[t * XP + ch] = kr[t % 4];
+      } else {
+        rc[R::KR_OFF + frag_off(t, ch, DK)] = kr[t % 4];
+        if (t % 4 == 0)   // KR^T: this channel's row
+          *reinterpret_cast<f32x4*>(rc + R::KRT_OFF + frag_off(ch, t, C)) = f32x4{kr[0], kr[1], kr[2], kr[3]};
+      }
     }
+  }
+  if constexpr (RS) {
+    // KG, KR (C x DK) and KG^T, QG^T, KR^T (DK x C) as split fragment pairs,
+    // every thread writing whole 16-byte hi and lo fragments: a task is one
+    // lane of one pair (row tile rt, K block kb) of one field.  (Barriers
+    // for the LDS data only: the record stores drain meanwhile.)
+    lds_barrier();
+    constexpr int NT = 4 * DK;   // tasks per field: 64 lanes x (2 (DK / 32) pairs, or DK / 16)
+    static_assert(NT % 64 == 0, "whole waves per field");
+#pragma unroll
+    for (int i = 0; i < (5 * NT + kPThreads - 1) / kPThreads; ++i) {
+      const int task = tid + i * kPThreads, field = task / NT, pair = (task % NT) / 64, ln = task % 64;
+      if (task >= 5 * NT) break;
+      const int gg = ln >> 4, rr = ln & 15;
+      float v8[8];
+      int off, kd, rt, kb;
+      // (one LDS array per call: a pointer chosen at run time would be a flat access)
+      auto rows = [&](const float* src) __attribute__((always_inline)) {   // row t, K = channels
+        const float* row = src + (16 * rt + rr) * XP + 32 * kb;
+        const f32x4 a = *reinterpret_cast<const f32x4*>(row + 4 * gg), b = *reinterpret_cast<const f32x4*>(row + 16 + 4 * gg);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v8[e] = a[e];
+          v8[4 + e] = b[e];
+        }
+      };
+      auto cols = [&](const float* src) __attribute__((always_inline)) {   // row = channel, K = positions
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v8[e] = src[kappa<bf16_t>(gg, e) * XP + 16 * rt + rr];
+      };
+      if (field < 2) {   // KG, KR
+        rt = pair / (DK / 32);
+        kb = pair % (DK / 32);
+        off = field == 0 ? R::KG_OFF : R::KR_OFF;
+        kd = DK;
+        if (field == 0) rows(sx);
+        else rows(sy);
+      } else {           // KG^T, QG^T, KR^T
+        rt = pair;
+        kb = 0;
+        off = field == 2 ? R::KGT_OFF : field == 3 ? R::QGT_OFF : R::KRT_OFF;
+        kd = C;
+        if (field == 2) cols(sx);
+        else if (field == 3) cols(sxq);
+        else cols(sy);
+      }
+      u32x4 h, l;
+      split8(v8, h, l);
+      float* tile = rc + off + (rt * (kd / 16) + 2 * kb) * 256 + 4 * ln;
+      *reinterpret_cast<u32x4*>(tile) = h;
+      *reinterpret_cast<u32x4*>(tile + 256) = l;
+    }
+    lds_barrier();   // the halving below rewrites sx, sxq and sy
   }
   {   // diagonal of M (G = 1): kPThreads / C threads per row
     constexpr int TPE = kPThreads / C;
@@ -379,11 +465,30 @@ __global__ __launch_bounds__(kPThreads) void chunk_bwd_prep_kernel(const T* q, c
   for (int e = tid; e < C * C; e += kPThreads) {
     const int i = e / C, j = e % C;
     const int fo = frag_off(i, j, C);
-    rc[R::MT_OFF + fo] = sM[j * CP + i];
+    if constexpr (!RS) {
+      rc[R::MT_OFF + fo] = sM[j * CP + i];
+      rc[R::TB_OFF + fo] = sT[i * CP + j] * sb[j];
+      rc[R::TBT_OFF + fo] = sT[j * CP + i] * sb[i];
+    }
     rc[R::T_OFF + e] = sT[i * CP + j];
-    rc[R::TB_OFF + fo] = sT[i * CP + j] * sb[j];
-    rc[R::TBT_OFF + fo] = sT[j * CP + i] * sb[i];
     rc[R::S_OFF + e] = sS[i * CP + j];
+  }
+  if constexpr (RS) {   // M^T, TB, TB^T as split pairs: 2 row tiles, one K block, 64 lanes each
+    static_assert(3 * 2 * 64 <= kPThreads, "one task per thread");
+    if (tid < 3 * 2 * 64) {
+      const int field = tid / 128, rt = (tid / 64) % 2, ln = tid % 64, gg = ln >> 4, i = 16 * rt + (ln & 15);
+      float v8[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int j = kappa<bf16_t>(gg, e);
+        v8[e] = field == 0 ? sM[j * CP + i] : field == 1 ? sT[i * CP + j] * sb[j] : sT[j * CP + i] * sb[i];
+      }
+      u32x4 h, l;
+      split8(v8, h, l);
+      float* tile = rc + (field == 0 ? R::MT_OFF : field == 1 ? R::TB_OFF : R::TBT_OFF) + (rt * (C / 16)) * 256 + 4 * ln;
+      *reinterpret_cast<u32x4*>(tile) = h;
+      *reinterpret_cast<u32x4*>(tile + 256) = l;
+    }
   }
 }
 
@@ -415,7 +520,7 @@ __device__ __forceinline__ int hc_slot(int i, int j) {
 // The chunk-start states go out in accumulator order: per chunk and slice a
 // dk x 16 block, the f32x4 of lane l of row tile rh at float (64 rh + l) 4,
 // holding rows 16 rh + 4 (l / 16) + i, column l % 16 (hc_slot).
-template <typename T, int DK>
+template <typename T, int DK, bool RS>
 __global__ __launch_bounds__(64) void chunk_bwd_states_kernel(const T* v, const float* __restrict__ h0,
                                                               const float* __restrict__ rec, float* __restrict__ hc,
                                                               int T_len, int nchunks, int dv, int xcd_map) {
@@ -454,7 +559,7 @@ __global__ __launch_bounds__(64) void chunk_bwd_states_kernel(const T* v, const 
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-      for (int kb = 0; kb <= rt; ++kb)
+      for (int kb = 0; kb < (RS ? RT : rt + 1); ++kb)   // (a split record: both halves of every pair)
         tb[rt][kb] = *reinterpret_cast<const f32x4*>(rc + R::TB_OFF + (rt * RT + kb) * 256 + 4 * lane);
     // unconditional loads (a row past the end reads the chunk's first row and
     // is masked where it is used), kept as stored so that nothing waits for
@@ -504,7 +609,9 @@ __global__ __launch_bounds__(64) void chunk_bwd_states_kernel(const T* v, const 
       f32x4 p = zero4();
       if constexpr (SPLIT) {
 #pragma unroll
-        for (int j = 0; j < RH / 2; ++j) p = mma_split(p, split_frag(kg[rt][2 * j], kg[rt][2 * j + 1]), hs[j]);
+        for (int j = 0; j < RH / 2; ++j)
+          p = mma_split(p, RS ? rec_pair(kg[rt][2 * j], kg[rt][2 * j + 1]) : split_frag(kg[rt][2 * j], kg[rt][2 * j + 1]),
+                        hs[j]);
       } else {
 #pragma unroll
         for (int kb = 0; kb < RH; ++kb)
@@ -521,8 +628,9 @@ __global__ __launch_bounds__(64) void chunk_bwd_states_kernel(const T* v, const 
     f32x4 uacc[RT];
     if constexpr (SPLIT) {
       const SplitFrag xs = split_frag(xacc[0], xacc[1]);
-      uacc[0] = mma_split(zero4(), split_frag(tb[0][0], zero4()), xs);   // TB is lower triangular
-      uacc[1] = mma_split(zero4(), split_frag(tb[1][0], tb[1][1]), xs);
+      // TB is lower triangular
+      uacc[0] = mma_split(zero4(), RS ? rec_pair(tb[0][0], tb[0][1]) : split_frag(tb[0][0], zero4()), xs);
+      uacc[1] = mma_split(zero4(), RS ? rec_pair(tb[1][0], tb[1][1]) : split_frag(tb[1][0], tb[1][1]), xs);
     } else {
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
@@ -542,7 +650,7 @@ __global__ __launch_bounds__(64) void chunk_bwd_states_kernel(const T* v, const 
     for (int rh = 0; rh < RH; ++rh) {
       f32x4 hh = gc[rh] * hacc[rh];
       if constexpr (SPLIT) {
-        hh = mma_split(hh, split_frag(kr[rh][0], kr[rh][1]), us);
+        hh = mma_split(hh, RS ? rec_pair(kr[rh][0], kr[rh][1]) : split_frag(kr[rh][0], kr[rh][1]), us);
       } else {
 #pragma unroll
         for (int kb = 0; kb < RT; ++kb)
@@ -571,7 +679,7 @@ __global__ __launch_bounds__(64) void chunk_bwd_states_kernel(const T* v, const 
 template <int DK>
 constexpr int kDsWaves = DK >= 32 ? 2 : 1;
 
-template <typename T, int DK>
+template <typename T, int DK, bool RS>
 __global__ __launch_bounds__(128) void chunk_bwd_dstates_kernel(const T* dout, const float* __restrict__ dhT,
                                                                const float* __restrict__ rec,
                                                                float* __restrict__ dhn, float* __restrict__ dh0,
@@ -614,7 +722,7 @@ __global__ __launch_bounds__(128) void chunk_bwd_dstates_kernel(const T* dout, c
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-      for (int kb = rt; kb < RT; ++kb)
+      for (int kb = RS ? 0 : rt; kb < RT; ++kb)   // (a split record: both halves of every pair)
         o.mt[rt][kb] = *reinterpret_cast<const f32x4*>(rc + R::MT_OFF + (rt * RT + kb) * 256 + 4 * lane);
     const int t0 = c * C, cv = min(C, T_len - t0);
 #pragma unroll
@@ -630,7 +738,7 @@ __global__ __launch_bounds__(128) void chunk_bwd_dstates_kernel(const T* dout, c
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-      for (int kb = rt; kb < RT; ++kb)
+      for (int kb = RS ? 0 : rt; kb < RT; ++kb)
         tbt[rt][kb] = *reinterpret_cast<const f32x4*>(rc + R::TBT_OFF + (rt * RT + kb) * 256 + 4 * lane);
   };
   auto load_last = [&](int c) __attribute__((always_inline)) {
@@ -686,7 +794,8 @@ __global__ __launch_bounds__(128) void chunk_bwd_dstates_kernel(const T* dout, c
     for (int rt = 0; rt < RT; ++rt) {
       f32x4 m = zero4();
       if constexpr (SPLIT) {   // M^T is upper triangular
-        m = mma_split_exact(m, split_frag(rt == 0 ? cur.mt[0][0] : zero4(), cur.mt[rt][1]), dob);
+        m = mma_split_exact(m, RS ? rec_pair(cur.mt[rt][0], cur.mt[rt][1])
+                                  : split_frag(rt == 0 ? cur.mt[0][0] : zero4(), cur.mt[rt][1]), dob);
       } else {
 #pragma unroll
         for (int kb = rt; kb < RT; ++kb)
@@ -696,7 +805,8 @@ __global__ __launch_bounds__(128) void chunk_bwd_dstates_kernel(const T* dout, c
       if constexpr (SPLIT) {
 #pragma unroll
         for (int j = 0; j < RHW / 2; ++j)
-          du[rt] = mma_split(du[rt], split_frag(cur.kr[rt][2 * j], cur.kr[rt][2 * j + 1]), dhs[j]);
+          du[rt] = mma_split(du[rt], RS ? rec_pair(cur.kr[rt][2 * j], cur.kr[rt][2 * j + 1])
+                                        : split_frag(cur.kr[rt][2 * j], cur.kr[rt][2 * j + 1]), dhs[j]);
       } else {
 #pragma unroll
         for (int kb = 0; kb < RHW; ++kb)
@@ -710,7 +820,7 @@ __global__ __launch_bounds__(128) void chunk_bwd_dstates_kernel(const T* dout, c
     for (int rh = 0; rh < RHW; ++rh) {
       hp[rh] = gc[rh] * dacc[rh];
       if constexpr (SPLIT) {
-        hp[rh] = mma_split_exact(hp[rh], split_frag(qgt[rh][0], qgt[rh][1]), dob);
+        hp[rh] = mma_split_exact(hp[rh], RS ? rec_pair(qgt[rh][0], qgt[rh][1]) : split_frag(qgt[rh][0], qgt[rh][1]), dob);
       } else {
 #pragma unroll
         for (int kb = 0; kb < RT; ++kb)
@@ -728,8 +838,8 @@ __global__ __launch_bounds__(128) void chunk_bwd_dstates_kernel(const T* dout, c
     f32x4 ndx[RT];
     if constexpr (SPLIT) {   // TB^T is upper triangular
       const SplitFrag dus = split_frag(du[0], du[1]);
-      ndx[0] = -mma_split(zero4(), split_frag(tbt[0][0], tbt[0][1]), dus);
-      ndx[1] = -mma_split(zero4(), split_frag(zero4(), tbt[1][1]), dus);
+      ndx[0] = -mma_split(zero4(), RS ? rec_pair(tbt[0][0], tbt[0][1]) : split_frag(tbt[0][0], tbt[0][1]), dus);
+      ndx[1] = -mma_split(zero4(), RS ? rec_pair(tbt[1][0], tbt[1][1]) : split_frag(zero4(), tbt[1][1]), dus);
     } else {
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
@@ -750,7 +860,7 @@ __global__ __launch_bounds__(128) void chunk_bwd_dstates_kernel(const T* dout, c
     for (int rh = 0; rh < RHW; ++rh) {
       f32x4 h = hp[rh];
       if constexpr (SPLIT) {
-        h = mma_split(h, split_frag(kgt[rh][0], kgt[rh][1]), ndxs);
+        h = mma_split(h, RS ? rec_pair(kgt[rh][0], kgt[rh][1]) : split_frag(kgt[rh][0], kgt[rh][1]), ndxs);
       } else {
 #pragma unroll
         for (int kb = 0; kb < RT; ++kb)
@@ -850,7 +960,7 @@ __device__ __forceinline__ f32x4 mma2b(f32x4 acc, SFrag a, Frag b) {   // B exac
 // CU at dk = 128)
 constexpr int kGThreads = 512;
 
-template <typename T, int DK, int DS>
+template <typename T, int DK, int DS, bool RS>
 __global__ __launch_bounds__(kGThreads) void chunk_bwd_grad_kernel(
     const T* q, const T* k, const T* v, const T* alpha, const T* beta, const T* dout, const float* __restrict__ rec,
     const float* __restrict__ hc, const float* __restrict__ dhn, float* __restrict__ dq, float* __restrict__ dk,
@@ -862,6 +972,7 @@ __global__ __launch_bounds__(kGThreads) void chunk_bwd_grad_kernel(
   // SG: bf16 inputs with 32-column slices: the value-slice loop on split bf16
   // operands (bf16 matrix cores, 3 steps of 32 K where fp32 takes 8 of 4)
   constexpr bool SG = std::is_same<T, bf16_t>::value && DS == 32 && DK >= 32;
+  static_assert(!RS || SG, "a split record is read by the split-bf16 value-slice loop");
   // split-bf16 areas (in 2-byte units): per chunk KG, KR (hi, lo; rows of
   // KP), M^T, TB (hi, lo; rows of CP2); per slice H, dH' (hi, lo; DK rows of
   // SP), dO (bf16, C rows of SP), V (as stored, C x DS), X, U, dU, dX (hi, lo;
@@ -944,17 +1055,67 @@ __global__ __launch_bounds__(kGThreads) void chunk_bwd_grad_kernel(
       r0[i] = ld_or(q, gi, ok, 0.f);
       r1[i] = ld_or(k, gi, ok, 0.f);
       r2[i] = ld_or(alpha, gi, ok, 1.f);
-      r3[i] = rc[R::KG_OFF + (in ? e : 0)];
-      r4[i] = rc[R::KR_OFF + (in ? e : 0)];
+      if constexpr (!RS) {
+        r3[i] = rc[R::KG_OFF + (in ? e : 0)];
+        r4[i] = rc[R::KR_OFF + (in ? e : 0)];
+      }
+    }
+    // a split record: KG, KR, M^T and TB as hi and lo fragments, copied as
+    // they are (task = one lane of one pair: row tile rt, K block kb)
+    constexpr int NPK = 2 * (DK / 32) * 64, NPS = 2 * NPK + 2 * 2 * 64;
+    constexpr int NRS = RS ? (NPS + kGThreads - 1) / kGThreads : 0;
+    u32x4 ph[NRS > 0 ? NRS : 1], pl[NRS > 0 ? NRS : 1];
+    // (the LDS destinations as offsets from KGh, so that the stores stay LDS
+    // stores: KGh, KGl, KRh, KRl of C x KP, then MTh, MTl, TBh, TBl of C x CP2)
+    constexpr int KBS = DK >= 32 ? DK / 32 : 1;
+    auto rs_task = [&](int task, int& off, int& kd, int& rt, int& kb, int& stride, int& dh, int& dl)
+                       __attribute__((always_inline)) {
+      const int field = task < NPK ? 0 : task < 2 * NPK ? 1 : task < 2 * NPK + 128 ? 2 : 3;
+      const int pair = field < 2 ? (task - field * NPK) / 64 : (task - 2 * NPK - (field - 2) * 128) / 64;
+      kd = field < 2 ? DK : C;
+      rt = field < 2 ? pair / KBS : pair;
+      kb = field < 2 ? pair % KBS : 0;
+      off = field == 0 ? R::KG_OFF : field == 1 ? R::KR_OFF : field == 2 ? R::MT_OFF : R::TB_OFF;
+      stride = field < 2 ? KP : CP2;
+      dh = field < 2 ? 2 * field * C * KP : 4 * C * KP + 2 * (field - 2) * C * CP2;
+      dl = dh + (field < 2 ? C * KP : C * CP2);
+    };
+    if constexpr (RS) {
+#pragma unroll
+      for (int i = 0; i < NRS; ++i) {
+        const int task = tid + i * kGThreads;
+        if (task < NPS) {
+          int off, kd, rt, kb, stride, dh, dl;
+          rs_task(task, off, kd, rt, kb, stride, dh, dl);
+          const float* tile = rc + off + (rt * (kd / 16) + 2 * kb) * 256 + 4 * (task % 64);
+          ph[i] = *reinterpret_cast<const u32x4*>(tile);
+          pl[i] = *reinterpret_cast<const u32x4*>(tile + 256);
+        }
+      }
     }
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
       const int e = tid + i * kGThreads;
       const bool in = e < C * C;
-      m0[i] = rc[R::MT_OFF + (in ? e : 0)];
-      m1[i] = rc[R::TB_OFF + (in ? e : 0)];
+      if constexpr (!RS) {
+        m0[i] = rc[R::MT_OFF + (in ? e : 0)];
+        m1[i] = rc[R::TB_OFF + (in ? e : 0)];
+      }
       m2[i] = rc[R::T_OFF + (in ? e : 0)];
       m3[i] = rc[R::S_OFF + (in ? e : 0)];
+    }
+    if constexpr (RS) {
+#pragma unroll
+      for (int i = 0; i < NRS; ++i) {
+        const int task = tid + i * kGThreads;
+        if (task < NPS) {
+          int off, kd, rt, kb, stride, dh, dl;
+          rs_task(task, off, kd, rt, kb, stride, dh, dl);
+          const int ln = task % 64, o = (16 * rt + (ln & 15)) * stride + 32 * kb + 8 * (ln >> 4);
+          *reinterpret_cast<u32x4*>(KGh + dh + o) = ph[i];
+          *reinterpret_cast<u32x4*>(KGh + dl + o) = pl[i];
+        }
+      }
     }
 #pragma unroll
     for (int i = 0; i < NK; ++i) {
@@ -966,7 +1127,8 @@ __global__ __launch_bounds__(kGThreads) void chunk_bwd_grad_kernel(
         sa[o] = from_f32<T>(r2[i]);
         int tt, cc;   // KG and KR are in fragment order
         frag_pos(e, DK, tt, cc);
-        if constexpr (SG) {
+        if constexpr (RS) {
+        } else if constexpr (SG) {
           const int os = tt * KP + kperm(cc);
           split_bits(r3[i], KGh[os], KGl[os]);
           split_bits(r4[i], KRh[os], KRl[os]);
@@ -983,7 +1145,8 @@ __global__ __launch_bounds__(kGThreads) void chunk_bwd_grad_kernel(
         const int o = (e / C) * CP + e % C;
         int ii, jj;   // M^T and TB are in fragment order, T and S row-major
         frag_pos(e, C, ii, jj);
-        if constexpr (SG) {   // the record holds M^T, the A operand of M^T dO
+        if constexpr (RS) {
+        } else if constexpr (SG) {   // the record holds M^T, the A operand of M^T dO
           const int os = ii * CP2 + kperm(jj);
           split_bits(m0[i], MTh[os], MTl[os]);
           split_bits(m1[i], TBh[os], TBl[os]);
@@ -1650,24 +1813,37 @@ static hipError_t launch_bwd_t(const BwdArgs& a) {
   float* dhn = hc + (size_t)total * DK * a.dv;
   const unsigned nsl = (unsigned)(a.dv / kBDS);
   const int xcd_map = (BH % 8 == 0) ? 1 : 0;
-  if (total > 0) {
-    hipLaunchKernelGGL((chunk_bwd_prep_kernel<T, DK>), dim3((unsigned)total), dim3(kPThreads), 0, a.stream,
-                       (const T*)a.q, (const T*)a.k, (const T*)a.alpha, (const T*)a.beta, rec, a.T, nch);
-    hipLaunchKernelGGL((chunk_bwd_states_kernel<T, DK>), dim3((unsigned)(BH * nsl)), dim3(64), 0, a.stream,
-                       (const T*)a.v, a.h0, rec, hc, a.T, nch, a.dv, xcd_map);
+  // bf16 inputs free enough LDS for 32-column value slices (half the slice
+  // steps); fp32 inputs, and dv = 16, take 16 columns.  With bf16 inputs,
+  // dk >= 64 and 32-column slices every consumer of the record multiplies
+  // split pairs, and the record holds them (BwdRec).
+  auto prep = chunk_bwd_prep_kernel<T, DK, false>;
+  auto states = chunk_bwd_states_kernel<T, DK, false>;
+  auto dstates = chunk_bwd_dstates_kernel<T, DK, false>;
+  auto grad = chunk_bwd_grad_kernel<T, DK, 16, false>;
+  if constexpr (std::is_same<T, bf16_t>::value) {
+    if (a.dv % 32 == 0) grad = chunk_bwd_grad_kernel<T, DK, 32, false>;
+    if constexpr (kSplitSeq<T, DK>) {
+      if (a.dv % 32 == 0) {
+        prep = chunk_bwd_prep_kernel<T, DK, true>;
+        states = chunk_bwd_states_kernel<T, DK, true>;
+        dstates = chunk_bwd_dstates_kernel<T, DK, true>;
+        grad = chunk_bwd_grad_kernel<T, DK, 32, true>;
+      }
+    }
   }
-  hipLaunchKernelGGL((chunk_bwd_dstates_kernel<T, DK>), dim3((unsigned)(BH * nsl)), dim3(64 * kDsWaves<DK>), 0,
-                     a.stream, (const T*)a.dout, a.dhT, rec, dhn, a.gh0, a.T, nch, a.dv, xcd_map);
   if (total > 0) {
-    // bf16 inputs free enough LDS for 32-column value slices (half the slice
-    // steps); fp32 inputs, and dv = 16, take 16 columns
-    auto grad = chunk_bwd_grad_kernel<T, DK, 16>;
-    if constexpr (std::is_same<T, bf16_t>::value)
-      if (a.dv % 32 == 0) grad = chunk_bwd_grad_kernel<T, DK, 32>;
+    hipLaunchKernelGGL(prep, dim3((unsigned)total), dim3(kPThreads), 0, a.stream, (const T*)a.q, (const T*)a.k,
+                       (const T*)a.alpha, (const T*)a.beta, rec, a.T, nch);
+    hipLaunchKernelGGL(states, dim3((unsigned)(BH * nsl)), dim3(64), 0, a.stream, (const T*)a.v, a.h0, rec, hc, a.T,
+                       nch, a.dv, xcd_map);
+  }
+  hipLaunchKernelGGL(dstates, dim3((unsigned)(BH * nsl)), dim3(64 * kDsWaves<DK>), 0, a.stream, (const T*)a.dout,
+                     a.dhT, rec, dhn, a.gh0, a.T, nch, a.dv, xcd_map);
+  if (total > 0)
     hipLaunchKernelGGL(grad, dim3((unsigned)total), dim3(kGThreads), 0, a.stream, (const T*)a.q, (const T*)a.k,
                        (const T*)a.v, (const T*)a.alpha, (const T*)a.beta, (const T*)a.dout, rec, hc, dhn, a.gq, a.gk,
                        a.gv, a.galpha, a.gbeta, a.T, nch, a.dv);
-  }
   return hipGetLastError();
 }
 
