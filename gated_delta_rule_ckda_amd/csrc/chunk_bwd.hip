@@ -68,7 +68,11 @@ __device__ __forceinline__ void frag_pos(int e, int KD, int& row, int& k) {
 // block kb (32 wide) hold the hi and the lo bf16 fragments of that block,
 // lane 16 g + r's 16 bytes being row r, K = 32 kb + kappa(g, e), e = 0..7
 // (hi = bf16(x), lo = bf16(x - hi), as split_frag forms them from fp32).
-// T, S and Gamma_C stay fp32.
+// T, S and Gamma_C stay fp32.  In a split record the place of KG^T (which
+// only dstates reads) holds -K~G^T, K~G = TB KG, which takes one dependent
+// product off the dstates pass:  dH = Gamma_C . dH' + QG^T dO - K~G^T dU
+// (= ... - KG^T TB^T dU, without forming dX); TB^T, then unread, is not
+// written.
 template <int DK>
 struct BwdRec {
   static constexpr int C = kBC;
@@ -206,6 +210,8 @@ __global__ __launch_bounds__(kPThreads) void chunk_bwd_prep_kernel(const T* q, c
   // rescaled operands of one halving level, rows 16-byte aligned for 4-channel reads
   constexpr int XP = DK + 4;
   __shared__ __align__(16) float sx[C * XP], sxq[C * XP], sy[C * XP];
+  // (split record) KG, kept for K~G = TB KG after the halving has reused sx
+  __shared__ __align__(16) float skg[RS ? C * XP : 1];
   __shared__ float sS[C * CP], sM[C * CP], sT[C * CP], sb[C];
 
   const int tid = threadIdx.x;
@@ -267,7 +273,7 @@ __global__ __launch_bounds__(kPThreads) void chunk_bwd_prep_kernel(const T* q, c
       kg[t % 4] = ck[t] * gm;
       qg[t % 4] = cq[t] * gm;
       if constexpr (RS) {   // to LDS; all threads write the split record below
-        sx[t * XP + ch] = kg[t % 4];
+        skg[t * XP + ch] = kg[t % 4];
         sxq[t * XP + ch] = qg[t % 4];
       } else {
         rc[R::KG_OFF + frag_off(t, ch, DK)] = kg[t % 4];
@@ -293,7 +299,7 @@ __global__ __launch_bounds__(kPThreads) void chunk_bwd_prep_kernel(const T* q, c
     }
   }
   if constexpr (RS) {
-    // KG, KR (C x DK) and KG^T, QG^T, KR^T (DK x C) as split fragment pairs,
+    // KG, KR (C x DK) and QG^T, KR^T (DK x C) as split fragment pairs,
     // every thread writing whole 16-byte hi and lo fragments: a task is one
     // lane of one pair (row tile rt, K block kb) of one field.  (Barriers
     // for the LDS data only: the record stores drain meanwhile.)
@@ -301,9 +307,12 @@ __global__ __launch_bounds__(kPThreads) void chunk_bwd_prep_kernel(const T* q, c
     constexpr int NT = 4 * DK;   // tasks per field: 64 lanes x (2 (DK / 32) pairs, or DK / 16)
     static_assert(NT % 64 == 0, "whole waves per field");
 #pragma unroll
-    for (int i = 0; i < (5 * NT + kPThreads - 1) / kPThreads; ++i) {
-      const int task = tid + i * kPThreads, field = task / NT, pair = (task % NT) / 64, ln = task % 64;
-      if (task >= 5 * NT) break;
+    for (int i = 0; i < (4 * NT + kPThreads - 1) / kPThreads; ++i) {
+      const int task0 = tid + i * kPThreads, f0 = task0 / NT;
+      // fields 0 KG, 1 KR, 3 QG^T, 4 KR^T (2, KG^T, is replaced by -K~G^T below)
+      const int field = f0 < 2 ? f0 : f0 + 1, task = task0 + (f0 < 2 ? 0 : NT);
+      const int pair = (task % NT) / 64, ln = task % 64;
+      if (task0 >= 4 * NT) break;
       const int gg = ln >> 4, rr = ln & 15;
       float v8[8];
       int off, kd, rt, kb;
@@ -326,15 +335,14 @@ __global__ __launch_bounds__(kPThreads) void chunk_bwd_prep_kernel(const T* q, c
         kb = pair % (DK / 32);
         off = field == 0 ? R::KG_OFF : R::KR_OFF;
         kd = DK;
-        if (field == 0) rows(sx);
+        if (field == 0) rows(skg);
         else rows(sy);
       } else {           // KG^T, QG^T, KR^T
         rt = pair;
         kb = 0;
         off = field == 2 ? R::KGT_OFF : field == 3 ? R::QGT_OFF : R::KRT_OFF;
         kd = C;
-        if (field == 2) cols(sx);
-        else if (field == 3) cols(sxq);
+        if (field == 3) cols(sxq);
         else cols(sy);
       }
       u32x4 h, l;
@@ -462,6 +470,35 @@ __global__ __launch_bounds__(kPThreads) void chunk_bwd_prep_kernel(const T* q, c
     sT[(HB + i) * CP + j] = -acc;
   }
   __syncthreads();
+  if constexpr (RS) {
+    // -K~G^T, K~G = TB KG, on fp32 matrix cores straight from T, beta and KG
+    // in LDS: the accumulator tiles of positions 0-15 and 16-31 of channel
+    // tile ct are, element by element, the fragment of row tile ct of K~G^T
+    // (K = positions in kappa order), split and stored as a pair
+    const int wv = tid >> 6, ln = tid & 63, rr = ln & 15, gg = ln >> 4;
+    for (int ct = wv; ct < DK / 16; ct += kPThreads / 64) {
+      f32x4 acc[2] = {zero4(), zero4()};
+#pragma unroll
+      for (int st = 0; st < C / 4; ++st) {
+        const int kk = 4 * st + gg;   // lane (g, r) supplies A(r, k) and B(k, r) of K step k = 4 st + g
+        const float bk = skg[kk * XP + 16 * ct + rr], bt = sb[kk];
+#pragma unroll
+        for (int pt = 0; pt < 2; ++pt)
+          acc[pt] = __builtin_amdgcn_mfma_f32_16x16x4f32(sT[(16 * pt + rr) * CP + kk] * bt, bk, acc[pt], 0, 0, 0);
+      }
+      float v8[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v8[e] = -acc[0][e];
+        v8[4 + e] = -acc[1][e];
+      }
+      u32x4 h, l;
+      split8(v8, h, l);
+      float* tile = rc + R::KGT_OFF + (ct * (C / 16)) * 256 + 4 * ln;
+      *reinterpret_cast<u32x4*>(tile) = h;
+      *reinterpret_cast<u32x4*>(tile + 256) = l;
+    }
+  }
   for (int e = tid; e < C * C; e += kPThreads) {
     const int i = e / C, j = e % C;
     const int fo = frag_off(i, j, C);
@@ -473,9 +510,9 @@ __global__ __launch_bounds__(kPThreads) void chunk_bwd_prep_kernel(const T* q, c
     rc[R::T_OFF + e] = sT[i * CP + j];
     rc[R::S_OFF + e] = sS[i * CP + j];
   }
-  if constexpr (RS) {   // M^T, TB, TB^T as split pairs: 2 row tiles, one K block, 64 lanes each
-    static_assert(3 * 2 * 64 <= kPThreads, "one task per thread");
-    if (tid < 3 * 2 * 64) {
+  if constexpr (RS) {   // M^T, TB as split pairs: 2 row tiles, one K block, 64 lanes each
+    static_assert(2 * 2 * 64 <= kPThreads, "one task per thread");
+    if (tid < 2 * 2 * 64) {
       const int field = tid / 128, rt = (tid / 64) % 2, ln = tid % 64, gg = ln >> 4, i = 16 * rt + (ln & 15);
       float v8[8];
 #pragma unroll
@@ -590,11 +627,14 @@ __global__ __launch_bounds__(64) void chunk_bwd_states_kernel(const T* v, const 
   for (int c = 0; c < nchunks; ++c) {
     const long long chunk = bh * nchunks + c;
     const int cn = min(c + 1, nchunks - 1);
-    // the chunk-start state
+    // KR^T and Gamma_C, then the chunk-start state (the vector memory counter
+    // drains in issue order: loads issued after the stores would make the
+    // update's wait for them a wait for the stores too)
+    load_kr_gc(c);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int rh = 0; rh < RH; ++rh)
       *reinterpret_cast<f32x4*>(hc + (size_t)chunk * DK * dv + hc_slot<DK>(16 * rh + 4 * g, col)) = hacc[rh];
-    load_kr_gc(c);
     // (scheduling barriers keep each group of loads where it is written: the
     // scheduler would otherwise sink them toward their uses)
     __builtin_amdgcn_sched_barrier(0);
@@ -734,6 +774,7 @@ __global__ __launch_bounds__(128) void chunk_bwd_dstates_kernel(const T* dout, c
       }
   };
   auto load_tbt = [&](int c) __attribute__((always_inline)) {
+    if constexpr (RS) return;   // TB^T is not read (and not written) with a split record
     const float* rc = recp(c);
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
@@ -833,6 +874,20 @@ __global__ __launch_bounds__(128) void chunk_bwd_dstates_kernel(const T* dout, c
       __syncthreads();
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) du[rt] += xb[par][1 - wave][rt][lane];
+    }
+    if constexpr (RS) {
+      // dH = Gamma_C . dH' + QG^T dO + (-K~G^T) dU: no dX on the chain
+      const SplitFrag dus = split_frag(du[0], du[1]);
+#pragma unroll
+      for (int rh = 0; rh < RHW; ++rh) {
+        const f32x4 h = mma_split(hp[rh], rec_pair(kgt[rh][0], kgt[rh][1]), dus);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dacc[rh][i] = live ? h[i] : dacc[rh][i];
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      load_last(cn);
+      __builtin_amdgcn_sched_barrier(0);
+      return;
     }
     // dX = TB^T dU, negated for the update below
     f32x4 ndx[RT];
