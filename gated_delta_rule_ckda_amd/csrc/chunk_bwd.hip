@@ -31,6 +31,7 @@
 // derivative for the gate at s collects the pairs j < s <= t with its own
 // factor left out, G(t, s) G(s - 1, j), by scans inside the halves.  Exact
 // zero gates need no special case.
+#include <atomic>
 #include <type_traits>
 
 #include "ckda_device.hpp"
@@ -184,9 +185,10 @@ __device__ __forceinline__ f32x4 mma_split_exact(f32x4 acc, SplitFrag a, Frag b)
 __device__ __forceinline__ void split8(const float* x, u32x4& h, u32x4& l) {
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
-    const uint32_t w = pack_bf16x2(x[2 * p], x[2 * p + 1]);
-    h[p] = w;
-    l[p] = pack_bf16x2(x[2 * p] - bf16_lo_half(w), x[2 * p + 1] - bf16_hi_half(w));
+    uint32_t a, b;
+    split_pair_bf16(x[2 * p], x[2 * p + 1], a, b);
+    h[p] = a;
+    l[p] = b;
   }
 }
 // A operand `a` as a split pair read from a split record: the two tiles' 16
@@ -538,50 +540,67 @@ __device__ __forceinline__ int hc_slot(int i, int j) {
   return (j / 16) * (DK * 16) + ((i / 16) * 64 + ((i % 16) / 4) * 16 + j % 16) * 4 + i % 4;
 }
 
-// One wave per head and 16-column value slice, the state slice (dk x 16) in
-// its accumulator registers, as the forward's state pass keeps it: per chunk
+// 16 bytes at a wave-uniform float address plus a per-lane byte offset: the
+// address form with a scalar base and a 32-bit lane offset, so that no 64-bit
+// address arithmetic is done per lane
+__device__ __forceinline__ f32x4 ld16(const float* base, uint32_t boff) {
+  return *reinterpret_cast<const f32x4*>(reinterpret_cast<const char*>(base) + boff);
+}
+__device__ __forceinline__ void st16(float* base, uint32_t boff, f32x4 x) {
+  *reinterpret_cast<f32x4*>(reinterpret_cast<char*>(base) + boff) = x;
+}
+
+// One wave per head and NS 16-column value slices (NS = 1 or 2), each
+// slice's state (dk x 16) in its accumulator registers, as the forward's state
+// pass keeps it: per chunk
 //   X = V - KG H,  U = TB X,  H <- Gamma_C . H + KR^T U
-// on fp32 matrix cores, the accumulator tiles of one product being (with the
-// K order 4 g + e of an fp32 fragment) the B operand of the next.  The A
+// on matrix cores, the accumulator tiles of one product being (with the K
+// order 4 g + e of an fp32 fragment) the B operand of the next.  The A
 // operands come straight from the chunk record (the slices of a head share it
 // through their XCD's L2), every fragment one 16-byte load of a KG, TB or
-// KR^T row.  Each operand is loaded for the next chunk as soon as the current
-// chunk has used it (KR^T and Gamma_C, used last, at the top of their own
-// chunk), so the loads run under the matrix-core work without a second
-// register set; the next chunk's loads are unconditional (the last chunk
-// reloads itself), which keeps them in one basic block.  About 60 memory
-// instructions per chunk, within what the in-order vector memory counter
-// can track, so no wait covers more than the loads it needs.  No LDS and no
-// barrier.
+// KR^T row, and serve all NS slices: the kernel moves its record through each
+// CU's vector memory path, whose throughput for L2 hits bounds it once two
+// workgroups share a CU, so two slices per wave halve those bytes (and the
+// two slices' independent chains fill each other's latency).  Each operand is
+// loaded for the next chunk as soon as the current chunk has used it (KR^T and
+// Gamma_C, used last, at the top of their own chunk), so the loads run under
+// the matrix-core work without a second register set; the next chunk's loads
+// are unconditional (the last chunk reloads itself), which keeps them in one
+// basic block.  No LDS and no barrier.
 //
 // The chunk-start states go out in accumulator order: per chunk and slice a
 // dk x 16 block, the f32x4 of lane l of row tile rh at float (64 rh + l) 4,
 // holding rows 16 rh + 4 (l / 16) + i, column l % 16 (hc_slot).
-template <typename T, int DK, bool RS>
+template <typename T, int DK, bool RS, int NS>
 __global__ __launch_bounds__(64) void chunk_bwd_states_kernel(const T* v, const float* __restrict__ h0,
                                                               const float* __restrict__ rec, float* __restrict__ hc,
                                                               int T_len, int nchunks, int dv, int xcd_map) {
   constexpr int C = kBC, RH = DK / 16, RT = C / 16;
   constexpr bool SPLIT = kSplitSeq<T, DK>;
   static_assert(RT == 2, "one 32-position K block per chunk");
+  static_assert(NS == 1 || NS == 2, "one or two slices per wave");
   using R = BwdRec<DK>;
   const int lane = threadIdx.x, g = lane >> 4, r = lane & 15;
-  const int nsl = dv / 16;
   long long bh;
-  int slice;
-  head_slice(blockIdx.x, nsl, xcd_map, bh, slice);
-  const int col = slice * 16 + r;   // this lane's value column
-  f32x4 hacc[RH];   // H rows 16 rh + 4 g + i, column col
+  int sg;
+  head_slice(blockIdx.x, dv / (16 * NS), xcd_map, bh, sg);
+  const int slice0 = sg * NS;         // the wave's first slice
+  const int col0 = slice0 * 16 + r;   // this lane's value column in it (slice s: + 16 s)
+  f32x4 hacc[NS][RH];   // H rows 16 rh + 4 g + i, column col0 + 16 s
 #pragma unroll
-  for (int rh = 0; rh < RH; ++rh)
+  for (int s = 0; s < NS; ++s)
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      hacc[rh][i] = h0 ? h0[(bh * DK + 16 * rh + 4 * g + i) * (long long)dv + col] : 0.f;
+    for (int rh = 0; rh < RH; ++rh)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        hacc[s][rh][i] = h0 ? h0[(bh * DK + 16 * rh + 4 * g + i) * (long long)dv + col0 + 16 * s] : 0.f;
   f32x4 kg[RT][RH];   // KG rows 16 rt + r, channels 16 kb + 4 g .. + 3
   f32x4 kr[RH][RT];   // KR^T rows 16 rh + r (channels), positions 16 kb + 4 g .. + 3
   f32x4 tb[RT][RT];   // TB rows 16 rt + r, positions 16 kb + 4 g .. + 3 (kb <= rt)
   f32x4 gc[RH];       // Gamma_C at channels 16 rh + 4 g .. + 3
-  T vv[RT][4];        // V rows 16 rt + 4 g .. + 3, column col, as stored (rows past the end: any row)
+  T vv[NS][RT][4];    // V rows 16 rt + 4 g .. + 3, column col0 + 16 s, as stored (rows past the end: 0)
+  const uint32_t v_boff = (uint32_t)((4 * g * dv + col0) * sizeof(T));
+  const uint32_t lboff = 16u * lane;   // this lane's 16 bytes of a fragment tile
   auto recp = [&](int c) { return rec + (size_t)(bh * nchunks + c) * R::FLOATS; };
   auto load_kg = [&](int c) __attribute__((always_inline)) {
     const float* rc = recp(c);
@@ -589,7 +608,7 @@ __global__ __launch_bounds__(64) void chunk_bwd_states_kernel(const T* v, const 
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
       for (int kb = 0; kb < RH; ++kb)
-        kg[rt][kb] = *reinterpret_cast<const f32x4*>(rc + R::KG_OFF + (rt * (DK / 16) + kb) * 256 + 4 * lane);
+        kg[rt][kb] = ld16(rc + R::KG_OFF + (rt * (DK / 16) + kb) * 256, lboff);
   };
   auto load_tb_v = [&](int c) __attribute__((always_inline)) {
     const float* rc = recp(c);
@@ -597,18 +616,31 @@ __global__ __launch_bounds__(64) void chunk_bwd_states_kernel(const T* v, const 
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
       for (int kb = 0; kb < (RS ? RT : rt + 1); ++kb)   // (a split record: both halves of every pair)
-        tb[rt][kb] = *reinterpret_cast<const f32x4*>(rc + R::TB_OFF + (rt * RT + kb) * 256 + 4 * lane);
-    // unconditional loads (a row past the end reads the chunk's first row and
-    // is masked where it is used), kept as stored so that nothing waits for
-    // them before the next chunk
+        tb[rt][kb] = ld16(rc + R::TB_OFF + (rt * RT + kb) * 256, lboff);
+    // V rows kept as stored, so that nothing waits for them before the next
+    // chunk: row 16 rt + i of the chunk at a uniform base, plus this lane's
+    // byte offset (rows 4 g and its column); rows past the end (last chunk
+    // only) read as 0
     const int t0 = c * C, cv = min(C, T_len - t0);
+    const T* vc = v + ((size_t)bh * T_len + t0) * dv;
+    if (cv == C) {
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
+      for (int s = 0; s < NS; ++s)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = 16 * rt + 4 * g + i;
-        vv[rt][i] = v[(size_t)(bh * T_len + t0 + (t < cv ? t : 0)) * dv + col];
-      }
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            vv[s][rt][i] = *reinterpret_cast<const T*>(reinterpret_cast<const char*>(vc + (size_t)(16 * rt + i) * dv) +
+                                                       v_boff + 16 * s * sizeof(T));
+    } else {
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            vv[s][rt][i] = 16 * rt + 4 * g + i < cv ? vc[(size_t)(16 * rt + 4 * g + i) * dv + col0 + 16 * s] : T{};
+    }
   };
   auto load_kr_gc = [&](int c) __attribute__((always_inline)) {
     const float* rc = recp(c);
@@ -616,9 +648,9 @@ __global__ __launch_bounds__(64) void chunk_bwd_states_kernel(const T* v, const 
     for (int rh = 0; rh < RH; ++rh)
 #pragma unroll
       for (int kb = 0; kb < RT; ++kb)
-        kr[rh][kb] = *reinterpret_cast<const f32x4*>(rc + R::KRT_OFF + (rh * RT + kb) * 256 + 4 * lane);
+        kr[rh][kb] = ld16(rc + R::KRT_OFF + (rh * RT + kb) * 256, lboff);
 #pragma unroll
-    for (int rh = 0; rh < RH; ++rh) gc[rh] = *reinterpret_cast<const f32x4*>(rc + R::GC_OFF + 16 * rh + 4 * g);
+    for (int rh = 0; rh < RH; ++rh) gc[rh] = ld16(rc + R::GC_OFF + 16 * rh, 16u * g);
   };
   if (nchunks > 0) {
     load_kg(0);
@@ -633,70 +665,99 @@ __global__ __launch_bounds__(64) void chunk_bwd_states_kernel(const T* v, const 
     load_kr_gc(c);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int rh = 0; rh < RH; ++rh)
-      *reinterpret_cast<f32x4*>(hc + (size_t)chunk * DK * dv + hc_slot<DK>(16 * rh + 4 * g, col)) = hacc[rh];
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int rh = 0; rh < RH; ++rh)   // (hc_slot order)
+        st16(hc + (size_t)chunk * DK * dv + (slice0 + s) * (DK * 16) + rh * 256, lboff, hacc[s][rh]);
     // (scheduling barriers keep each group of loads where it is written: the
     // scheduler would otherwise sink them toward their uses)
     __builtin_amdgcn_sched_barrier(0);
     // X = V - KG H
-    f32x4 xacc[RT];
-    SplitFrag hs[SPLIT ? RH / 2 : 1];
+    f32x4 xacc[NS][RT];
+    SplitFrag hs[NS][SPLIT ? RH / 2 : 1];
     if constexpr (SPLIT)
 #pragma unroll
-      for (int j = 0; j < RH / 2; ++j) hs[j] = split_frag(hacc[2 * j], hacc[2 * j + 1]);
+      for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int j = 0; j < RH / 2; ++j) hs[s][j] = split_frag(hacc[s][2 * j], hacc[s][2 * j + 1]);
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-      f32x4 p = zero4();
+      f32x4 p[NS];
+#pragma unroll
+      for (int s = 0; s < NS; ++s) p[s] = zero4();
       if constexpr (SPLIT) {
 #pragma unroll
-        for (int j = 0; j < RH / 2; ++j)
-          p = mma_split(p, RS ? rec_pair(kg[rt][2 * j], kg[rt][2 * j + 1]) : split_frag(kg[rt][2 * j], kg[rt][2 * j + 1]),
-                        hs[j]);
+        for (int j = 0; j < RH / 2; ++j) {
+          const SplitFrag a = RS ? rec_pair(kg[rt][2 * j], kg[rt][2 * j + 1]) : split_frag(kg[rt][2 * j], kg[rt][2 * j + 1]);
+#pragma unroll
+          for (int s = 0; s < NS; ++s) p[s] = mma_split(p[s], a, hs[s][j]);
+        }
       } else {
 #pragma unroll
         for (int kb = 0; kb < RH; ++kb)
-          p = mma<float>(p, Frag{__builtin_bit_cast(u32x4, kg[rt][kb])}, frag_from_acc_f32(hacc[kb]));
-      }
-      const int cv = min(C, T_len - c * C);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) xacc[rt][i] = (16 * rt + 4 * g + i < cv ? to_f32(vv[rt][i]) : 0.f) - p[i];
+          for (int s = 0; s < NS; ++s)
+            p[s] = mma<float>(p[s], Frag{__builtin_bit_cast(u32x4, kg[rt][kb])}, frag_from_acc_f32(hacc[s][kb]));
+      }
+      // (rows past the end: V read as 0 and no key, so X is 0)
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) xacc[s][rt][i] = to_f32(vv[s][rt][i]) - p[s][i];
     }
     __builtin_amdgcn_sched_barrier(0);
     load_kg(cn);
     __builtin_amdgcn_sched_barrier(0);
     // U = TB X
-    f32x4 uacc[RT];
+    f32x4 uacc[NS][RT];
     if constexpr (SPLIT) {
-      const SplitFrag xs = split_frag(xacc[0], xacc[1]);
+      SplitFrag xs[NS];
+#pragma unroll
+      for (int s = 0; s < NS; ++s) xs[s] = split_frag(xacc[s][0], xacc[s][1]);
       // TB is lower triangular
-      uacc[0] = mma_split(zero4(), RS ? rec_pair(tb[0][0], tb[0][1]) : split_frag(tb[0][0], zero4()), xs);
-      uacc[1] = mma_split(zero4(), RS ? rec_pair(tb[1][0], tb[1][1]) : split_frag(tb[1][0], tb[1][1]), xs);
+      const SplitFrag t0 = RS ? rec_pair(tb[0][0], tb[0][1]) : split_frag(tb[0][0], zero4());
+      const SplitFrag t1 = RS ? rec_pair(tb[1][0], tb[1][1]) : split_frag(tb[1][0], tb[1][1]);
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        uacc[s][0] = mma_split(zero4(), t0, xs[s]);
+        uacc[s][1] = mma_split(zero4(), t1, xs[s]);
+      }
     } else {
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        uacc[rt] = zero4();
+      for (int s = 0; s < NS; ++s)
 #pragma unroll
-        for (int kb = 0; kb <= rt; ++kb)
-          uacc[rt] = mma<float>(uacc[rt], Frag{__builtin_bit_cast(u32x4, tb[rt][kb])}, frag_from_acc_f32(xacc[kb]));
-      }
+        for (int rt = 0; rt < RT; ++rt) {
+          uacc[s][rt] = zero4();
+#pragma unroll
+          for (int kb = 0; kb <= rt; ++kb)
+            uacc[s][rt] =
+                mma<float>(uacc[s][rt], Frag{__builtin_bit_cast(u32x4, tb[rt][kb])}, frag_from_acc_f32(xacc[s][kb]));
+        }
     }
     __builtin_amdgcn_sched_barrier(0);
     load_tb_v(cn);
     __builtin_amdgcn_sched_barrier(0);
     // H <- Gamma_C . H + KR^T U
-    SplitFrag us;
-    if constexpr (SPLIT) us = split_frag(uacc[0], uacc[1]);
+    SplitFrag us[NS];
+    if constexpr (SPLIT)
+#pragma unroll
+      for (int s = 0; s < NS; ++s) us[s] = split_frag(uacc[s][0], uacc[s][1]);
 #pragma unroll
     for (int rh = 0; rh < RH; ++rh) {
-      f32x4 hh = gc[rh] * hacc[rh];
       if constexpr (SPLIT) {
-        hh = mma_split(hh, RS ? rec_pair(kr[rh][0], kr[rh][1]) : split_frag(kr[rh][0], kr[rh][1]), us);
+        const SplitFrag a = RS ? rec_pair(kr[rh][0], kr[rh][1]) : split_frag(kr[rh][0], kr[rh][1]);
+#pragma unroll
+        for (int s = 0; s < NS; ++s) hacc[s][rh] = mma_split(gc[rh] * hacc[s][rh], a, us[s]);
       } else {
 #pragma unroll
-        for (int kb = 0; kb < RT; ++kb)
-          hh = mma<float>(hh, Frag{__builtin_bit_cast(u32x4, kr[rh][kb])}, frag_from_acc_f32(uacc[kb]));
+        for (int s = 0; s < NS; ++s) {
+          f32x4 hh = gc[rh] * hacc[s][rh];
+#pragma unroll
+          for (int kb = 0; kb < RT; ++kb)
+            hh = mma<float>(hh, Frag{__builtin_bit_cast(u32x4, kr[rh][kb])}, frag_from_acc_f32(uacc[s][kb]));
+          hacc[s][rh] = hh;
+        }
       }
-      hacc[rh] = hh;
     }
   }
 }
@@ -1858,6 +1919,19 @@ __global__ __launch_bounds__(kGThreads) void chunk_bwd_grad_kernel(
 }
 
 // ============================================================ launch
+// compute units of the current device, cached per device
+static int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 template <typename T, int DK>
 static hipError_t launch_bwd_t(const BwdArgs& a) {
   using R = BwdRec<DK>;
@@ -1873,7 +1947,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a) {
   // dk >= 64 and 32-column slices every consumer of the record multiplies
   // split pairs, and the record holds them (BwdRec).
   auto prep = chunk_bwd_prep_kernel<T, DK, false>;
-  auto states = chunk_bwd_states_kernel<T, DK, false>;
+  auto states = chunk_bwd_states_kernel<T, DK, false, 1>;
   auto dstates = chunk_bwd_dstates_kernel<T, DK, false>;
   auto grad = chunk_bwd_grad_kernel<T, DK, 16, false>;
   if constexpr (std::is_same<T, bf16_t>::value) {
@@ -1881,7 +1955,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a) {
     if constexpr (kSplitSeq<T, DK>) {
       if (a.dv % 32 == 0) {
         prep = chunk_bwd_prep_kernel<T, DK, true>;
-        states = chunk_bwd_states_kernel<T, DK, true>;
+        states = chunk_bwd_states_kernel<T, DK, true, 1>;
         dstates = chunk_bwd_dstates_kernel<T, DK, true>;
         grad = chunk_bwd_grad_kernel<T, DK, 32, true>;
       }
@@ -1890,8 +1964,17 @@ static hipError_t launch_bwd_t(const BwdArgs& a) {
   if (total > 0) {
     hipLaunchKernelGGL(prep, dim3((unsigned)total), dim3(kPThreads), 0, a.stream, (const T*)a.q, (const T*)a.k,
                        (const T*)a.alpha, (const T*)a.beta, rec, a.T, nch);
-    hipLaunchKernelGGL(states, dim3((unsigned)(BH * nsl)), dim3(64), 0, a.stream, (const T*)a.v, a.h0, rec, hc, a.T,
-                       nch, a.dv, xcd_map);
+    // two value slices per wave once one per wave would put two or more
+    // workgroups on every compute unit (they would share its memory path)
+    const bool two = a.dv % 32 == 0 && BH * nsl >= 2LL * device_cus();
+    if (two) {
+      auto states2 = chunk_bwd_states_kernel<T, DK, false, 2>;
+      if constexpr (kSplitSeq<T, DK>)
+        if (states == chunk_bwd_states_kernel<T, DK, true, 1>) states2 = chunk_bwd_states_kernel<T, DK, true, 2>;
+      states = states2;
+    }
+    hipLaunchKernelGGL(states, dim3((unsigned)(BH * nsl / (two ? 2 : 1))), dim3(64), 0, a.stream, (const T*)a.v, a.h0,
+                       rec, hc, a.T, nch, a.dv, xcd_map);
   }
   hipLaunchKernelGGL(dstates, dim3((unsigned)(BH * nsl)), dim3(64 * kDsWaves<DK>), 0, a.stream, (const T*)a.dout,
                      a.dhT, rec, dhn, a.gh0, a.T, nch, a.dv, xcd_map);

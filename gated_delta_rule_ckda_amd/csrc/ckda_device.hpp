@@ -173,11 +173,25 @@ __device__ __forceinline__ Frag frag_residual_bf16(const float* v, Frag hi) {
     f.w[i] = pack_bf16x2(v[2 * i] - bf16_lo_half(hi.w[i]), v[2 * i + 1] - bf16_hi_half(hi.w[i]));
   return f;
 }
+// hi and lo of the pair (a, b), packed.  The empty asm hides the packed hi
+// word from the optimiser, which would otherwise convert a again on its own
+// to get the low half back (one conversion more per pair).
+__device__ __forceinline__ void split_pair_bf16(float a, float b, uint32_t& h, uint32_t& l) {
+  uint32_t w = pack_bf16x2(a, b);
+  asm("" : "+v"(w));
+  h = w;
+  l = pack_bf16x2(a - bf16_lo_half(w), b - bf16_hi_half(w));
+}
 // hi and lo B fragments of the K block covered by accumulator tiles lo, hi.
 __device__ __forceinline__ void frags_from_acc_bf16_split(f32x4 lo, f32x4 hi, Frag& fh, Frag& fl) {
-  fh = frag_from_acc_bf16(lo, hi);
   const float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  fl = frag_residual_bf16(v, fh);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t a, b;
+    split_pair_bf16(v[2 * i], v[2 * i + 1], a, b);
+    fh.w[i] = a;
+    fl.w[i] = b;
+  }
 }
 __device__ __forceinline__ Frag frag_from_acc_f32(f32x4 t) {
   Frag f;
