@@ -31,6 +31,7 @@
 // derivative for the gate at s collects the pairs j < s <= t with its own
 // factor left out, G(t, s) G(s - 1, j), by scans inside the halves.  Exact
 // zero gates need no special case.
+#include <algorithm>
 #include <atomic>
 #include <type_traits>
 
@@ -205,7 +206,7 @@ constexpr int kPThreads = 512;
 template <typename T, int DK, bool RS>
 __global__ __launch_bounds__(kPThreads) void chunk_bwd_prep_kernel(const T* q, const T* k, const T* alpha,
                                                                    const T* beta, float* __restrict__ rec, int T_len,
-                                                                   int nchunks) {
+                                                                   int nchunks, long long total) {
   constexpr int C = kBC, DKP = DK + 1, CP = C + 1;
   using R = BwdRec<DK>;
   __shared__ float sq[C * DKP], sk[C * DKP], sa[C * DKP];
@@ -217,317 +218,331 @@ __global__ __launch_bounds__(kPThreads) void chunk_bwd_prep_kernel(const T* q, c
   __shared__ float sS[C * CP], sM[C * CP], sT[C * CP], sb[C];
 
   const int tid = threadIdx.x;
-  const long long chunk = blockIdx.x;
-  const long long bh = chunk / nchunks;
-  const int c = (int)(chunk % nchunks);
-  const int t0 = c * C, cv = min(C, T_len - t0);
-  const long long row0 = bh * (long long)T_len + t0;
-  // rows past a ragged end are identity steps: gate 1, no key, query or beta
-  {   // all loads issued before any is stored
-    constexpr int NK = (C * DK + kPThreads - 1) / kPThreads;
-    float r0[NK], r1[NK], r2[NK];
+  // A persistent loop over chunks blockIdx.x, + gridDim.x, ...: each chunk's
+  // inputs are fetched, as stored and at in-bounds addresses, while the
+  // previous chunk is computed, and the barriers wait for LDS traffic only
+  // (the kernel reads no global memory that it writes), so the fetch and the
+  // record stores stay in flight across them.
+  constexpr int NK = (C * DK + kPThreads - 1) / kPThreads;
+  T xq[NK], xk[NK], xa[NK], xb;   // the fetched chunk's q, k, alpha and beta
+  auto fetch = [&](long long chunk) __attribute__((always_inline)) {
+    const long long bh = chunk / nchunks;
+    const int c = (int)(chunk % nchunks), t0 = c * C, cv = min(C, T_len - t0);
+    const long long row0 = bh * (long long)T_len + t0;
 #pragma unroll
     for (int i = 0; i < NK; ++i) {
       const int e = tid + i * kPThreads, t = e / DK, ch = e % DK;
-      const bool ok = e < C * DK && t < cv;
-      const size_t gi = ok ? (size_t)(row0 + t) * DK + ch : 0;
-      r0[i] = ld_or(q, gi, ok, 0.f);
-      r1[i] = ld_or(k, gi, ok, 0.f);
-      r2[i] = ld_or(alpha, gi, ok, 1.f);
+      const size_t gi = e < C * DK && t < cv ? (size_t)(row0 + t) * DK + ch : 0;
+      xq[i] = q[gi];
+      xk[i] = k[gi];
+      xa[i] = alpha[gi];
     }
+    xb = beta[row0 + (tid < cv ? tid : 0)];
+  };
+  if (blockIdx.x < total) fetch(blockIdx.x);
+  for (long long chunk = blockIdx.x; chunk < total; chunk += gridDim.x) {
+    // (the thread index, hidden from the optimiser per chunk: its many derived
+    // offsets are recomputed in each chunk rather than held across the loop)
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int cv = min(C, T_len - (int)(chunk % nchunks) * C);
+    // rows past a ragged end are identity steps: gate 1, no key, query or beta
 #pragma unroll
     for (int i = 0; i < NK; ++i) {
-      const int e = tid + i * kPThreads;
+      const int e = tid + i * kPThreads, t = e / DK;
       if (e < C * DK) {
-        const int o = (e / DK) * DKP + e % DK;
-        sq[o] = r0[i];
-        sk[o] = r1[i];
-        sa[o] = r2[i];
+        const int o = t * DKP + e % DK;
+        const bool ok = t < cv;
+        sq[o] = ok ? to_f32(xq[i]) : 0.f;
+        sk[o] = ok ? to_f32(xk[i]) : 0.f;
+        sa[o] = ok ? to_f32(xa[i]) : 1.f;
       }
     }
-  }
-  if (tid < C) sb[tid] = tid < cv ? to_f32(beta[row0 + tid]) : 0.f;
-  for (int e = tid; e < C * CP; e += kPThreads) {
-    sS[e] = 0.f;
-    sM[e] = 0.f;
-  }
-  __syncthreads();
-
-  float* rc = rec + (size_t)chunk * R::FLOATS;
-  // this thread's channel (tid < DK): its gate, key and query columns in
-  // registers for the sequential products below (read from LDS once; the LDS
-  // allows one workgroup per CU, one wave per SIMD, which hides no latency)
-  float ca[C], ck[C], cq[C];
-  if (tid < DK) {
-#pragma unroll
-    for (int t = 0; t < C; ++t) {
-      ca[t] = sa[t * DKP + tid];
-      ck[t] = sk[t * DKP + tid];
-      cq[t] = sq[t * DKP + tid];
+    if (tid < C) sb[tid] = tid < cv ? to_f32(xb) : 0.f;
+    for (int e = tid; e < C * CP; e += kPThreads) {
+      sS[e] = 0.f;
+      sM[e] = 0.f;
     }
-  }
-  if (tid < DK) {   // per channel: Gamma, KG, QG, Gamma_C; G(C-1, j), KR
-    const int ch = tid;
-    float gm = 1.f, kg[4], qg[4];
-#pragma unroll
-    for (int t = 0; t < C; ++t) {
-      gm *= ca[t];
-      kg[t % 4] = ck[t] * gm;
-      qg[t % 4] = cq[t] * gm;
-      if constexpr (RS) {   // to LDS; all threads write the split record below
-        skg[t * XP + ch] = kg[t % 4];
-        sxq[t * XP + ch] = qg[t % 4];
-      } else {
-        rc[R::KG_OFF + frag_off(t, ch, DK)] = kg[t % 4];
-        if (t % 4 == 3) {   // KG^T, QG^T: this channel's rows, 16 bytes at a time
-          *reinterpret_cast<f32x4*>(rc + R::KGT_OFF + frag_off(ch, t - 3, C)) = f32x4{kg[0], kg[1], kg[2], kg[3]};
-          *reinterpret_cast<f32x4*>(rc + R::QGT_OFF + frag_off(ch, t - 3, C)) = f32x4{qg[0], qg[1], qg[2], qg[3]};
-        }
-      }
-    }
-    rc[R::GC_OFF + ch] = gm;
-    float ge = 1.f, kr[4];
-#pragma unroll
-    for (int t = C - 1; t >= 0; --t) {
-      kr[t % 4] = ck[t] * ge;
-      ge *= ca[t];
-      if constexpr (RS) {
-        sy[t * XP + ch] = kr[t % 4];
-      } else {
-        rc[R::KR_OFF + frag_off(t, ch, DK)] = kr[t % 4];
-        if (t % 4 == 0)   // KR^T: this channel's row
-          *reinterpret_cast<f32x4*>(rc + R::KRT_OFF + frag_off(ch, t, C)) = f32x4{kr[0], kr[1], kr[2], kr[3]};
-      }
-    }
-  }
-  if constexpr (RS) {
-    // KG, KR (C x DK) and QG^T, KR^T (DK x C) as split fragment pairs,
-    // every thread writing whole 16-byte hi and lo fragments: a task is one
-    // lane of one pair (row tile rt, K block kb) of one field.  (Barriers
-    // for the LDS data only: the record stores drain meanwhile.)
     lds_barrier();
-    constexpr int NT = 4 * DK;   // tasks per field: 64 lanes x (2 (DK / 32) pairs, or DK / 16)
-    static_assert(NT % 64 == 0, "whole waves per field");
-#pragma unroll
-    for (int i = 0; i < (4 * NT + kPThreads - 1) / kPThreads; ++i) {
-      const int task0 = tid + i * kPThreads, f0 = task0 / NT;
-      // fields 0 KG, 1 KR, 3 QG^T, 4 KR^T (2, KG^T, is replaced by -K~G^T below)
-      const int field = f0 < 2 ? f0 : f0 + 1, task = task0 + (f0 < 2 ? 0 : NT);
-      const int pair = (task % NT) / 64, ln = task % 64;
-      if (task0 >= 4 * NT) break;
-      const int gg = ln >> 4, rr = ln & 15;
-      float v8[8];
-      int off, kd, rt, kb;
-      // (one LDS array per call: a pointer chosen at run time would be a flat access)
-      auto rows = [&](const float* src) __attribute__((always_inline)) {   // row t, K = channels
-        const float* row = src + (16 * rt + rr) * XP + 32 * kb;
-        const f32x4 a = *reinterpret_cast<const f32x4*>(row + 4 * gg), b = *reinterpret_cast<const f32x4*>(row + 16 + 4 * gg);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          v8[e] = a[e];
-          v8[4 + e] = b[e];
-        }
-      };
-      auto cols = [&](const float* src) __attribute__((always_inline)) {   // row = channel, K = positions
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v8[e] = src[kappa<bf16_t>(gg, e) * XP + 16 * rt + rr];
-      };
-      if (field < 2) {   // KG, KR
-        rt = pair / (DK / 32);
-        kb = pair % (DK / 32);
-        off = field == 0 ? R::KG_OFF : R::KR_OFF;
-        kd = DK;
-        if (field == 0) rows(skg);
-        else rows(sy);
-      } else {           // KG^T, QG^T, KR^T
-        rt = pair;
-        kb = 0;
-        off = field == 2 ? R::KGT_OFF : field == 3 ? R::QGT_OFF : R::KRT_OFF;
-        kd = C;
-        if (field == 3) cols(sxq);
-        else cols(sy);
-      }
-      u32x4 h, l;
-      split8(v8, h, l);
-      float* tile = rc + off + (rt * (kd / 16) + 2 * kb) * 256 + 4 * ln;
-      *reinterpret_cast<u32x4*>(tile) = h;
-      *reinterpret_cast<u32x4*>(tile + 256) = l;
-    }
-    lds_barrier();   // the halving below rewrites sx, sxq and sy
-  }
-  {   // diagonal of M (G = 1): kPThreads / C threads per row
-    constexpr int TPE = kPThreads / C;
-    static_assert(TPE <= 64 && DK % TPE == 0, "row groups within a wave");
-    const int t = tid / TPE, sub = tid % TPE;
-    float d = 0.f;
-#pragma unroll
-    for (int ch = sub; ch < DK; ch += TPE) d += sq[t * DKP + ch] * sk[t * DKP + ch];
-    d = group_sum<TPE>(d);
-    if (sub == 0) sM[t * CP + t] = d;
-  }
-  // S and M below the diagonal by recursive halving (h a compile-time
-  // constant per level, so that the channel's loops run on its registers)
-  auto level = [&](auto hh) __attribute__((always_inline)) {
-    constexpr int h = decltype(hh)::value;
+    if (chunk + gridDim.x < total) fetch(chunk + gridDim.x);   // the next chunk's inputs, under this one's work
+
+    float* rc = rec + (size_t)chunk * R::FLOATS;
+    // this thread's channel (tid < DK): its gate, key and query columns in
+    // registers for the sequential products below (read from LDS once; the LDS
+    // allows one workgroup per CU, one wave per SIMD, which hides no latency)
+    float ca[C], ck[C], cq[C];
     if (tid < DK) {
-      const int ch = tid;
 #pragma unroll
-      for (int lo = 0; lo < C; lo += 2 * h) {
-        const int m = lo + h - 1;
-        float f = 1.f;
-#pragma unroll
-        for (int t = m + 1; t <= m + h; ++t) {   // x_t G(t, m)
-          f *= ca[t];
-          sx[t * XP + ch] = ck[t] * f;
-          sxq[t * XP + ch] = cq[t] * f;
-        }
-        float e = 1.f;
-#pragma unroll
-        for (int j = m; j >= lo; --j) {          // y_j G(m, j)
-          sy[j * XP + ch] = ck[j] * e;
-          e *= ca[j];
-        }
+      for (int t = 0; t < C; ++t) {
+        ca[t] = sa[t * DKP + tid];
+        ck[t] = sk[t * DKP + tid];
+        cq[t] = sq[t * DKP + tid];
       }
     }
-    __syncthreads();
-    // (C / 2h) blocks of h x h entries, TPE threads per entry (consecutive
-    // lanes, strided groups of 4 channels), partial sums reduced across the group
-    constexpr int nent = C * h / 2;
-    constexpr int TPE0 = kPThreads / nent < 1 ? 1 : kPThreads / nent;
-    constexpr int TPE1 = TPE0 > DK / 4 ? DK / 4 : TPE0;
-    constexpr int TPE = TPE1 > 64 ? 64 : TPE1;
-    static_assert(TPE >= 2, "lane groups of two or more");
-    for (int base = 0; base < nent * TPE; base += kPThreads) {
-      const int e = (base + tid) / TPE, sub = (base + tid) % TPE;
-      const bool ok = e < nent;
-      const int blk = ok ? e / (h * h) : 0, w = ok ? e % (h * h) : 0;
-      const int lo = blk * 2 * h, t = lo + h + w / h, j = lo + w % h;
-      float s = 0.f, mm = 0.f;
-      if (ok) {
+    if (tid < DK) {   // per channel: Gamma, KG, QG, Gamma_C; G(C-1, j), KR
+      const int ch = tid;
+      float gm = 1.f, kg[4], qg[4];
 #pragma unroll
-        for (int c4 = sub; c4 < DK / 4; c4 += TPE) {
-          const f32x4 y = *reinterpret_cast<const f32x4*>(sy + j * XP + 4 * c4);
-          const f32x4 x = *reinterpret_cast<const f32x4*>(sx + t * XP + 4 * c4);
-          const f32x4 xq = *reinterpret_cast<const f32x4*>(sxq + t * XP + 4 * c4);
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            s += x[v] * y[v];
-            mm += xq[v] * y[v];
+      for (int t = 0; t < C; ++t) {
+        gm *= ca[t];
+        kg[t % 4] = ck[t] * gm;
+        qg[t % 4] = cq[t] * gm;
+        if constexpr (RS) {   // to LDS; all threads write the split record below
+          skg[t * XP + ch] = kg[t % 4];
+          sxq[t * XP + ch] = qg[t % 4];
+        } else {
+          rc[R::KG_OFF + frag_off(t, ch, DK)] = kg[t % 4];
+          if (t % 4 == 3) {   // KG^T, QG^T: this channel's rows, 16 bytes at a time
+            *reinterpret_cast<f32x4*>(rc + R::KGT_OFF + frag_off(ch, t - 3, C)) = f32x4{kg[0], kg[1], kg[2], kg[3]};
+            *reinterpret_cast<f32x4*>(rc + R::QGT_OFF + frag_off(ch, t - 3, C)) = f32x4{qg[0], qg[1], qg[2], qg[3]};
           }
         }
       }
-      s = group_sum<TPE>(s);
-      mm = group_sum<TPE>(mm);
-      if (ok && sub == 0) {
-        sS[t * CP + j] = s;
-        sM[t * CP + j] = mm;
+      rc[R::GC_OFF + ch] = gm;
+      float ge = 1.f, kr[4];
+#pragma unroll
+      for (int t = C - 1; t >= 0; --t) {
+        kr[t % 4] = ck[t] * ge;
+        ge *= ca[t];
+        if constexpr (RS) {
+          sy[t * XP + ch] = kr[t % 4];
+        } else {
+          rc[R::KR_OFF + frag_off(t, ch, DK)] = kr[t % 4];
+          if (t % 4 == 0)   // KR^T: this channel's row
+            *reinterpret_cast<f32x4*>(rc + R::KRT_OFF + frag_off(ch, t, C)) = f32x4{kr[0], kr[1], kr[2], kr[3]};
+        }
       }
     }
-    __syncthreads();
-  };
-  static_assert(C == 32, "halving levels below assume 32-position chunks");
-  level(std::integral_constant<int, 16>{});
-  level(std::integral_constant<int, 8>{});
-  level(std::integral_constant<int, 4>{});
-  level(std::integral_constant<int, 2>{});
-  level(std::integral_constant<int, 1>{});
-  // T = (I + B)^-1, B = Diag(beta) S strictly lower, unit lower triangular,
-  // by 16 x 16 blocks: the diagonal blocks T11 = (I + B11)^-1 and
-  // T22 = (I + B22)^-1 by forward substitution, one column per thread held in
-  // registers (T[i][j] = -beta_i sum_{l < i} S[i][l] T[l][j] for i > j; the
-  // rows of S are read by every lane at once), then T21 = -T22 (B21 T11) as
-  // two 16 x 16 products, one entry per thread.
-  constexpr int HB = C / 2;
-  if (tid < C) {
-    const int o = (tid / HB) * HB, j = tid % HB;   // the block's first row, the column in it
-    float tc[HB];
+    if constexpr (RS) {
+      // KG, KR (C x DK) and QG^T, KR^T (DK x C) as split fragment pairs,
+      // every thread writing whole 16-byte hi and lo fragments: a task is one
+      // lane of one pair (row tile rt, K block kb) of one field.  (Barriers
+      // for the LDS data only: the record stores drain meanwhile.)
+      lds_barrier();
+      constexpr int NT = 4 * DK;   // tasks per field: 64 lanes x (2 (DK / 32) pairs, or DK / 16)
+      static_assert(NT % 64 == 0, "whole waves per field");
 #pragma unroll
-    for (int i = 0; i < HB; ++i) {
+      for (int i = 0; i < (4 * NT + kPThreads - 1) / kPThreads; ++i) {
+        const int task0 = tid + i * kPThreads, f0 = task0 / NT;
+        // fields 0 KG, 1 KR, 3 QG^T, 4 KR^T (2, KG^T, is replaced by -K~G^T below)
+        const int field = f0 < 2 ? f0 : f0 + 1, task = task0 + (f0 < 2 ? 0 : NT);
+        const int pair = (task % NT) / 64, ln = task % 64;
+        if (task0 >= 4 * NT) break;
+        const int gg = ln >> 4, rr = ln & 15;
+        float v8[8];
+        int off, kd, rt, kb;
+        // (one LDS array per call: a pointer chosen at run time would be a flat access)
+        auto rows = [&](const float* src) __attribute__((always_inline)) {   // row t, K = channels
+          const float* row = src + (16 * rt + rr) * XP + 32 * kb;
+          const f32x4 a = *reinterpret_cast<const f32x4*>(row + 4 * gg), b = *reinterpret_cast<const f32x4*>(row + 16 + 4 * gg);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            v8[e] = a[e];
+            v8[4 + e] = b[e];
+          }
+        };
+        auto cols = [&](const float* src) __attribute__((always_inline)) {   // row = channel, K = positions
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v8[e] = src[kappa<bf16_t>(gg, e) * XP + 16 * rt + rr];
+        };
+        if (field < 2) {   // KG, KR
+          rt = pair / (DK / 32);
+          kb = pair % (DK / 32);
+          off = field == 0 ? R::KG_OFF : R::KR_OFF;
+          kd = DK;
+          if (field == 0) rows(skg);
+          else rows(sy);
+        } else {           // KG^T, QG^T, KR^T
+          rt = pair;
+          kb = 0;
+          off = field == 2 ? R::KGT_OFF : field == 3 ? R::QGT_OFF : R::KRT_OFF;
+          kd = C;
+          if (field == 3) cols(sxq);
+          else cols(sy);
+        }
+        u32x4 h, l;
+        split8(v8, h, l);
+        float* tile = rc + off + (rt * (kd / 16) + 2 * kb) * 256 + 4 * ln;
+        *reinterpret_cast<u32x4*>(tile) = h;
+        *reinterpret_cast<u32x4*>(tile + 256) = l;
+      }
+      lds_barrier();   // the halving below rewrites sx, sxq and sy
+    }
+    {   // diagonal of M (G = 1): kPThreads / C threads per row
+      constexpr int TPE = kPThreads / C;
+      static_assert(TPE <= 64 && DK % TPE == 0, "row groups within a wave");
+      const int t = tid / TPE, sub = tid % TPE;
+      float d = 0.f;
+#pragma unroll
+      for (int ch = sub; ch < DK; ch += TPE) d += sq[t * DKP + ch] * sk[t * DKP + ch];
+      d = group_sum<TPE>(d);
+      if (sub == 0) sM[t * CP + t] = d;
+    }
+    // S and M below the diagonal by recursive halving (h a compile-time
+    // constant per level, so that the channel's loops run on its registers)
+    auto level = [&](auto hh) __attribute__((always_inline)) {
+      constexpr int h = decltype(hh)::value;
+      if (tid < DK) {
+        const int ch = tid;
+#pragma unroll
+        for (int lo = 0; lo < C; lo += 2 * h) {
+          const int m = lo + h - 1;
+          float f = 1.f;
+#pragma unroll
+          for (int t = m + 1; t <= m + h; ++t) {   // x_t G(t, m)
+            f *= ca[t];
+            sx[t * XP + ch] = ck[t] * f;
+            sxq[t * XP + ch] = cq[t] * f;
+          }
+          float e = 1.f;
+#pragma unroll
+          for (int j = m; j >= lo; --j) {          // y_j G(m, j)
+            sy[j * XP + ch] = ck[j] * e;
+            e *= ca[j];
+          }
+        }
+      }
+      lds_barrier();
+      // (C / 2h) blocks of h x h entries, TPE threads per entry (consecutive
+      // lanes, strided groups of 4 channels), partial sums reduced across the group
+      constexpr int nent = C * h / 2;
+      constexpr int TPE0 = kPThreads / nent < 1 ? 1 : kPThreads / nent;
+      constexpr int TPE1 = TPE0 > DK / 4 ? DK / 4 : TPE0;
+      constexpr int TPE = TPE1 > 64 ? 64 : TPE1;
+      static_assert(TPE >= 2, "lane groups of two or more");
+      for (int base = 0; base < nent * TPE; base += kPThreads) {
+        const int e = (base + tid) / TPE, sub = (base + tid) % TPE;
+        const bool ok = e < nent;
+        const int blk = ok ? e / (h * h) : 0, w = ok ? e % (h * h) : 0;
+        const int lo = blk * 2 * h, t = lo + h + w / h, j = lo + w % h;
+        float s = 0.f, mm = 0.f;
+        if (ok) {
+#pragma unroll
+          for (int c4 = sub; c4 < DK / 4; c4 += TPE) {
+            const f32x4 y = *reinterpret_cast<const f32x4*>(sy + j * XP + 4 * c4);
+            const f32x4 x = *reinterpret_cast<const f32x4*>(sx + t * XP + 4 * c4);
+            const f32x4 xq = *reinterpret_cast<const f32x4*>(sxq + t * XP + 4 * c4);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              s += x[v] * y[v];
+              mm += xq[v] * y[v];
+            }
+          }
+        }
+        s = group_sum<TPE>(s);
+        mm = group_sum<TPE>(mm);
+        if (ok && sub == 0) {
+          sS[t * CP + j] = s;
+          sM[t * CP + j] = mm;
+        }
+      }
+      lds_barrier();
+    };
+    static_assert(C == 32, "halving levels below assume 32-position chunks");
+    level(std::integral_constant<int, 16>{});
+    level(std::integral_constant<int, 8>{});
+    level(std::integral_constant<int, 4>{});
+    level(std::integral_constant<int, 2>{});
+    level(std::integral_constant<int, 1>{});
+    // T = (I + B)^-1, B = Diag(beta) S strictly lower, unit lower triangular,
+    // by 16 x 16 blocks: the diagonal blocks T11 = (I + B11)^-1 and
+    // T22 = (I + B22)^-1 by forward substitution, one column per thread held in
+    // registers (T[i][j] = -beta_i sum_{l < i} S[i][l] T[l][j] for i > j; the
+    // rows of S are read by every lane at once), then T21 = -T22 (B21 T11) as
+    // two 16 x 16 products, one entry per thread.
+    constexpr int HB = C / 2;
+    if (tid < C) {
+      const int o = (tid / HB) * HB, j = tid % HB;   // the block's first row, the column in it
+      float tc[HB];
+#pragma unroll
+      for (int i = 0; i < HB; ++i) {
+        float acc = 0.f;
+#pragma unroll
+        for (int l = 0; l < i; ++l) acc += sS[(o + i) * CP + o + l] * tc[l];
+        tc[i] = i > j ? -sb[o + i] * acc : (i == j ? 1.f : 0.f);
+      }
+#pragma unroll
+      for (int i = 0; i < HB; ++i) sT[(o + i) * CP + o + j] = tc[i];
+      if (o == 0)
+#pragma unroll
+        for (int i = 0; i < HB; ++i) sT[i * CP + HB + j] = 0.f;   // T12
+    }
+    lds_barrier();
+    float* sW = sx;   // B21 T11 (the rescaled operands are consumed)
+    if (tid < HB * HB) {
+      const int i = tid / HB, j = tid % HB;
       float acc = 0.f;
 #pragma unroll
-      for (int l = 0; l < i; ++l) acc += sS[(o + i) * CP + o + l] * tc[l];
-      tc[i] = i > j ? -sb[o + i] * acc : (i == j ? 1.f : 0.f);
+      for (int l = 0; l < HB; ++l) acc += sS[(HB + i) * CP + l] * sT[l * CP + j];
+      sW[i * HB + j] = sb[HB + i] * acc;
     }
+    lds_barrier();
+    if (tid < HB * HB) {
+      const int i = tid / HB, j = tid % HB;
+      float acc = 0.f;
 #pragma unroll
-    for (int i = 0; i < HB; ++i) sT[(o + i) * CP + o + j] = tc[i];
-    if (o == 0)
+      for (int l = 0; l < HB; ++l) acc += sT[(HB + i) * CP + HB + l] * sW[l * HB + j];
+      sT[(HB + i) * CP + j] = -acc;
+    }
+    lds_barrier();
+    if constexpr (RS) {
+      // -K~G^T, K~G = TB KG, on fp32 matrix cores straight from T, beta and KG
+      // in LDS: the accumulator tiles of positions 0-15 and 16-31 of channel
+      // tile ct are, element by element, the fragment of row tile ct of K~G^T
+      // (K = positions in kappa order), split and stored as a pair
+      const int wv = tid >> 6, ln = tid & 63, rr = ln & 15, gg = ln >> 4;
+      for (int ct = wv; ct < DK / 16; ct += kPThreads / 64) {
+        f32x4 acc[2] = {zero4(), zero4()};
 #pragma unroll
-      for (int i = 0; i < HB; ++i) sT[i * CP + HB + j] = 0.f;   // T12
-  }
-  __syncthreads();
-  float* sW = sx;   // B21 T11 (the rescaled operands are consumed)
-  if (tid < HB * HB) {
-    const int i = tid / HB, j = tid % HB;
-    float acc = 0.f;
+        for (int st = 0; st < C / 4; ++st) {
+          const int kk = 4 * st + gg;   // lane (g, r) supplies A(r, k) and B(k, r) of K step k = 4 st + g
+          const float bk = skg[kk * XP + 16 * ct + rr], bt = sb[kk];
 #pragma unroll
-    for (int l = 0; l < HB; ++l) acc += sS[(HB + i) * CP + l] * sT[l * CP + j];
-    sW[i * HB + j] = sb[HB + i] * acc;
-  }
-  __syncthreads();
-  if (tid < HB * HB) {
-    const int i = tid / HB, j = tid % HB;
-    float acc = 0.f;
+          for (int pt = 0; pt < 2; ++pt)
+            acc[pt] = __builtin_amdgcn_mfma_f32_16x16x4f32(sT[(16 * pt + rr) * CP + kk] * bt, bk, acc[pt], 0, 0, 0);
+        }
+        float v8[8];
 #pragma unroll
-    for (int l = 0; l < HB; ++l) acc += sT[(HB + i) * CP + HB + l] * sW[l * HB + j];
-    sT[(HB + i) * CP + j] = -acc;
-  }
-  __syncthreads();
-  if constexpr (RS) {
-    // -K~G^T, K~G = TB KG, on fp32 matrix cores straight from T, beta and KG
-    // in LDS: the accumulator tiles of positions 0-15 and 16-31 of channel
-    // tile ct are, element by element, the fragment of row tile ct of K~G^T
-    // (K = positions in kappa order), split and stored as a pair
-    const int wv = tid >> 6, ln = tid & 63, rr = ln & 15, gg = ln >> 4;
-    for (int ct = wv; ct < DK / 16; ct += kPThreads / 64) {
-      f32x4 acc[2] = {zero4(), zero4()};
-#pragma unroll
-      for (int st = 0; st < C / 4; ++st) {
-        const int kk = 4 * st + gg;   // lane (g, r) supplies A(r, k) and B(k, r) of K step k = 4 st + g
-        const float bk = skg[kk * XP + 16 * ct + rr], bt = sb[kk];
-#pragma unroll
-        for (int pt = 0; pt < 2; ++pt)
-          acc[pt] = __builtin_amdgcn_mfma_f32_16x16x4f32(sT[(16 * pt + rr) * CP + kk] * bt, bk, acc[pt], 0, 0, 0);
+        for (int e = 0; e < 4; ++e) {
+          v8[e] = -acc[0][e];
+          v8[4 + e] = -acc[1][e];
+        }
+        u32x4 h, l;
+        split8(v8, h, l);
+        float* tile = rc + R::KGT_OFF + (ct * (C / 16)) * 256 + 4 * ln;
+        *reinterpret_cast<u32x4*>(tile) = h;
+        *reinterpret_cast<u32x4*>(tile + 256) = l;
       }
-      float v8[8];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        v8[e] = -acc[0][e];
-        v8[4 + e] = -acc[1][e];
+    }
+    for (int e = tid; e < C * C; e += kPThreads) {
+      const int i = e / C, j = e % C;
+      const int fo = frag_off(i, j, C);
+      if constexpr (!RS) {
+        rc[R::MT_OFF + fo] = sM[j * CP + i];
+        rc[R::TB_OFF + fo] = sT[i * CP + j] * sb[j];
+        rc[R::TBT_OFF + fo] = sT[j * CP + i] * sb[i];
       }
-      u32x4 h, l;
-      split8(v8, h, l);
-      float* tile = rc + R::KGT_OFF + (ct * (C / 16)) * 256 + 4 * ln;
-      *reinterpret_cast<u32x4*>(tile) = h;
-      *reinterpret_cast<u32x4*>(tile + 256) = l;
+      rc[R::T_OFF + e] = sT[i * CP + j];
+      rc[R::S_OFF + e] = sS[i * CP + j];
     }
-  }
-  for (int e = tid; e < C * C; e += kPThreads) {
-    const int i = e / C, j = e % C;
-    const int fo = frag_off(i, j, C);
-    if constexpr (!RS) {
-      rc[R::MT_OFF + fo] = sM[j * CP + i];
-      rc[R::TB_OFF + fo] = sT[i * CP + j] * sb[j];
-      rc[R::TBT_OFF + fo] = sT[j * CP + i] * sb[i];
-    }
-    rc[R::T_OFF + e] = sT[i * CP + j];
-    rc[R::S_OFF + e] = sS[i * CP + j];
-  }
-  if constexpr (RS) {   // M^T, TB as split pairs: 2 row tiles, one K block, 64 lanes each
-    static_assert(2 * 2 * 64 <= kPThreads, "one task per thread");
-    if (tid < 2 * 2 * 64) {
-      const int field = tid / 128, rt = (tid / 64) % 2, ln = tid % 64, gg = ln >> 4, i = 16 * rt + (ln & 15);
-      float v8[8];
+    if constexpr (RS) {   // M^T, TB as split pairs: 2 row tiles, one K block, 64 lanes each
+      static_assert(2 * 2 * 64 <= kPThreads, "one task per thread");
+      if (tid < 2 * 2 * 64) {
+        const int field = tid / 128, rt = (tid / 64) % 2, ln = tid % 64, gg = ln >> 4, i = 16 * rt + (ln & 15);
+        float v8[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int j = kappa<bf16_t>(gg, e);
-        v8[e] = field == 0 ? sM[j * CP + i] : field == 1 ? sT[i * CP + j] * sb[j] : sT[j * CP + i] * sb[i];
+        for (int e = 0; e < 8; ++e) {
+          const int j = kappa<bf16_t>(gg, e);
+          v8[e] = field == 0 ? sM[j * CP + i] : field == 1 ? sT[i * CP + j] * sb[j] : sT[j * CP + i] * sb[i];
+        }
+        u32x4 h, l;
+        split8(v8, h, l);
+        float* tile = rc + (field == 0 ? R::MT_OFF : field == 1 ? R::TB_OFF : R::TBT_OFF) + (rt * (C / 16)) * 256 + 4 * ln;
+        *reinterpret_cast<u32x4*>(tile) = h;
+        *reinterpret_cast<u32x4*>(tile + 256) = l;
       }
-      u32x4 h, l;
-      split8(v8, h, l);
-      float* tile = rc + (field == 0 ? R::MT_OFF : field == 1 ? R::TB_OFF : R::TBT_OFF) + (rt * (C / 16)) * 256 + 4 * ln;
-      *reinterpret_cast<u32x4*>(tile) = h;
-      *reinterpret_cast<u32x4*>(tile + 256) = l;
     }
+    lds_barrier();   // the next chunk's staging rewrites the LDS operands
   }
 }
 
@@ -1962,8 +1977,13 @@ static hipError_t launch_bwd_t(const BwdArgs& a) {
     }
   }
   if (total > 0) {
-    hipLaunchKernelGGL(prep, dim3((unsigned)total), dim3(kPThreads), 0, a.stream, (const T*)a.q, (const T*)a.k,
-                       (const T*)a.alpha, (const T*)a.beta, rec, a.T, nch);
+    // prep loops over chunks: as many workgroups as are resident at once
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, prep, kPThreads, 0) != hipSuccess || per_cu < 1)
+      per_cu = 1;
+    const long long nprep = std::min<long long>(total, (long long)per_cu * device_cus());
+    hipLaunchKernelGGL(prep, dim3((unsigned)nprep), dim3(kPThreads), 0, a.stream, (const T*)a.q, (const T*)a.k,
+                       (const T*)a.alpha, (const T*)a.beta, rec, a.T, nch, total);
     // two value slices per wave once one per wave would put two or more
     // workgroups on every compute unit (they would share its memory path)
     const bool two = a.dv % 32 == 0 && BH * nsl >= 2LL * device_cus();

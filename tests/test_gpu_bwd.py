@@ -117,6 +117,19 @@ def test_two_slices_per_wave(dtype, dk, dv, B, H, T):
     run(w, heads=[0, B * H // 2 + 1, B * H - 1])
 
 
+@pytest.mark.parametrize("dtype,dk,dv,B,H,T", [
+    ("bf16", 128, 128, 8, 16, 77), ("f32", 128, 64, 8, 16, 77), ("bf16", 64, 64, 16, 16, 77),
+    ("f32", 32, 32, 16, 16, 50)])
+def test_prep_loops_over_chunks(dtype, dk, dv, B, H, T):
+    """The backward's prep kernel runs as many workgroups as fit on the GPU at
+    once and loops over the chunks, fetching the next chunk's inputs while it
+    computes the current one: with more chunks than resident workgroups (384
+    to 768 here, ragged last chunks) some workgroups handle two or three, and
+    the sampled heads lie on both sides of the first pass."""
+    w = gen.Workload("bwd_prep_loop", B, H, T, dk, dv, 64, dtype, "ckda_tanh", "normal", 7700 + dk + dv + T)
+    run(w, heads=[0, B * H * 2 // 3, B * H - 1])
+
+
 @pytest.mark.parametrize("T", [1, 31, 32, 33, 64, 200])
 def test_ragged_lengths(T):
     w = gen.Workload("bwd", 1, 1, T, 64, 64, 64, "f32", "ckda_tanh", "normal", 7200 + T)
