@@ -576,7 +576,8 @@ __device__ __forceinline__ void st16(float* base, uint32_t boff, f32x4 x) {
 // KR^T row, and serve all NS slices: the kernel moves its record through each
 // CU's vector memory path, whose throughput for L2 hits bounds it once two
 // workgroups share a CU, so two slices per wave halve those bytes (and the
-// two slices' independent chains fill each other's latency).  Each operand is
+// two slices' independent chains fill each other's latency; the launcher
+// takes two with split products only).  Each operand is
 // loaded for the next chunk as soon as the current chunk has used it (KR^T and
 // Gamma_C, used last, at the top of their own chunk), so the loads run under
 // the matrix-core work without a second register set; the next chunk's loads
@@ -1984,15 +1985,16 @@ static hipError_t launch_bwd_t(const BwdArgs& a) {
     const long long nprep = std::min<long long>(total, (long long)per_cu * device_cus());
     hipLaunchKernelGGL(prep, dim3((unsigned)nprep), dim3(kPThreads), 0, a.stream, (const T*)a.q, (const T*)a.k,
                        (const T*)a.alpha, (const T*)a.beta, rec, a.T, nch, total);
-    // two value slices per wave once one per wave would put two or more
-    // workgroups on every compute unit (they would share its memory path)
-    const bool two = a.dv % 32 == 0 && BH * nsl >= 2LL * device_cus();
-    if (two) {
-      auto states2 = chunk_bwd_states_kernel<T, DK, false, 2>;
-      if constexpr (kSplitSeq<T, DK>)
-        if (states == chunk_bwd_states_kernel<T, DK, true, 1>) states2 = chunk_bwd_states_kernel<T, DK, true, 2>;
-      states = states2;
-    }
+    // with split products, two value slices per wave once one per wave would
+    // put two or more workgroups on every compute unit (they would share its
+    // memory path); the fp32 matrix-core chain is bound by its own issue, and
+    // one slice per wave is faster there
+    bool two = false;
+    if constexpr (kSplitSeq<T, DK>)
+      if (states == chunk_bwd_states_kernel<T, DK, true, 1> && BH * nsl >= 2LL * device_cus()) {
+        two = true;
+        states = chunk_bwd_states_kernel<T, DK, true, 2>;
+      }
     hipLaunchKernelGGL(states, dim3((unsigned)(BH * nsl / (two ? 2 : 1))), dim3(64), 0, a.stream, (const T*)a.v, a.h0,
                        rec, hc, a.T, nch, a.dv, xcd_map);
   }

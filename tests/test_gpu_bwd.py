@@ -105,14 +105,16 @@ def test_isometric_full_shape_sampled_heads():
 
 
 @pytest.mark.parametrize("dtype,dk,dv,B,H,T", [
-    ("bf16", 128, 128, 4, 16, 77), ("f32", 128, 128, 4, 16, 77), ("bf16", 64, 64, 8, 16, 45),
-    ("f32", 32, 32, 16, 16, 40), ("bf16", 16, 128, 4, 16, 33), ("bf16", 128, 32, 16, 16, 3)])
+    ("bf16", 128, 128, 4, 16, 77), ("bf16", 64, 128, 4, 16, 77), ("bf16", 64, 64, 8, 16, 45),
+    ("bf16", 128, 32, 16, 16, 3), ("bf16", 64, 32, 16, 16, 40), ("f32", 128, 128, 4, 16, 77)])
 def test_two_slices_per_wave(dtype, dk, dv, B, H, T):
-    """Grids with B H dv / 16 of at least twice the compute units (512 on a
-    256-CU part) run the forward state pass of the backward with two 16-column
-    value slices per wave, both slices' products sharing each record fragment;
-    ragged lengths, every dk, dv 32 (one slice pair per head) to 128; the
-    oracle follows the first, a middle and the last head."""
+    """With split products (bf16 inputs, dk >= 64, dv a multiple of 32), grids
+    with B H dv / 16 of at least twice the compute units (512 on a 256-CU
+    part) run the forward state pass of the backward with two 16-column value
+    slices per wave, both slices' products sharing each record fragment;
+    ragged lengths, dv 32 (one slice pair per head) to 128, and an fp32 grid of
+    the same size (one slice per wave); the oracle follows the first, a middle
+    and the last head."""
     w = gen.Workload("bwd_two_slices", B, H, T, dk, dv, 64, dtype, "ckda_tanh", "normal", 7600 + dk + dv + T)
     run(w, heads=[0, B * H // 2 + 1, B * H - 1])
 
