@@ -67,17 +67,29 @@ def kernel_algorithmic(w):
             "chunk_state_kernel": th * 2 * w.dv * es + state}
 
 
+KERNEL_SOURCES = {"chunk_gram_kernel": "chunk_gram.hip", "chunk_state_kernel": "chunk_state.hip"}
+DEVICE_HEADERS = ("chunk_common.hpp", "ckda_device.hpp")
+
+
+def kernel_source_sha(kernel):
+    """sha256 of the kernel's source file followed by the device headers it
+    includes (the counters belong to the code all of them make)."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in (KERNEL_SOURCES[kernel],) + DEVICE_HEADERS:
+        with open(os.path.join(ROOT, "gated_delta_rule_ckda_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
 def traffic_from_profile(kernel):
     """HBM bytes per launch of `kernel` from the committed counter summary,
     or None when the kernel's source changed after the counters were taken."""
-    import hashlib
     import re
     path = os.path.join(ROOT, "profiles", f"{kernel}_ckda_bf16_hbm_counters.md")
-    src = os.path.join(ROOT, "gated_delta_rule_ckda_amd", "csrc",
-                       {"chunk_gram_kernel": "chunk_gram.hip", "chunk_state_kernel": "chunk_state.hip"}[kernel])
     try:
         text = open(path).read()
-        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        sha = kernel_source_sha(kernel)
     except OSError:
         return None
     m_sha = re.search(r"source sha256: `([0-9a-f]{64})`", text)
@@ -91,7 +103,6 @@ def counters_from_profile(name, kernels):
     """Executed matrix-core figures per kernel from a committed counter summary
     (profiles/<name>.md: lines `kernel <name> mfma_busy_frac <x>`), or None
     when any listed kernel's source changed after the counters were taken."""
-    import hashlib
     import re
     path = os.path.join(ROOT, "profiles", f"{name}.md")
     try:
@@ -100,9 +111,7 @@ def counters_from_profile(name, kernels):
         return None
     out = {}
     for k in kernels:
-        src = os.path.join(ROOT, "gated_delta_rule_ckda_amd", "csrc",
-                           {"chunk_gram_kernel": "chunk_gram.hip", "chunk_state_kernel": "chunk_state.hip"}[k])
-        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        sha = kernel_source_sha(k)
         m_sha = re.search(rf"{k} source sha256: `([0-9a-f]{{64}})`", text)
         m_v = re.search(rf"kernel {k} mfma_busy_frac ([0-9.]+)", text)
         if not m_sha or not m_v or m_sha.group(1) != sha:
