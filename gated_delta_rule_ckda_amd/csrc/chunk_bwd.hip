@@ -779,50 +779,58 @@ __global__ __launch_bounds__(64) void chunk_bwd_states_kernel(const T* v, const 
 }
 
 // ============================================================ dstates (reverse, sequential)
-// One workgroup per head and 16-column value slice, its waves splitting the
-// key channels: each holds dk / waves rows of the state gradient (x 16
-// columns) in accumulator registers.  Per chunk, from the last:
+// One workgroup per head and NS 16-column value slices (NS = 1 or 2), its NW
+// waves splitting the key channels: each holds dk / NW rows of the state
+// gradient (x 16 columns, per slice) in accumulator registers.  Per chunk,
+// from the last:
 //   dU = M^T dO + KR dH',  dX = TB^T dU,  dH = Gamma_C . dH' + QG^T dO - KG^T dX
-// on fp32 matrix cores, accumulator tiles feeding the next product as B
-// operands.  Each wave's KR dH' covers its own channels; the waves' partial
-// dU are summed through LDS (one barrier per chunk, the exchange buffer
-// alternating between chunks; a + b = b + a, so both waves hold the same dU).
-// Every A fragment is one 16-byte load of a record row; dO's fragments are
-// four loads of the input each, kept as stored until used.  Operands are
-// reloaded for the next chunk as soon as the current one has used them (KR,
-// M^T and dO, needed first, into the other of two sets).  The state gradient entering
-// each chunk from its end (dH') is stored in accumulator order (hc_slot),
-// dh0 at the end.
+// on matrix cores, accumulator tiles feeding the next product as B operands.
+// Each wave's KR dH' covers its own channels; the waves' partial dU are
+// summed through LDS (one barrier per chunk, the exchange buffer alternating
+// between chunks), in the same order in every wave, so all waves hold the
+// same dU (with two waves, a + b = b + a).  Every A fragment is one 16-byte
+// load of a record row and serves all NS slices; dO's fragments are four
+// loads of the input each, kept as stored until used.  Operands are reloaded
+// for the next chunk as soon as the current one has used them (KR, M^T and
+// dO, needed first, into the other of two sets).  The state gradient entering
+// each chunk from its end (dH') is stored in accumulator order (hc_slot), dh0
+// at the end.  The kernel moves its record through each CU's vector memory
+// path, which bounds it at two workgroups per CU; at the bench shape four
+// waves of two slices each make one workgroup per CU with each wave's work
+// unchanged.
 template <int DK>
 constexpr int kDsWaves = DK >= 32 ? 2 : 1;
 
-template <typename T, int DK, bool RS>
-__global__ __launch_bounds__(128) void chunk_bwd_dstates_kernel(const T* dout, const float* __restrict__ dhT,
-                                                               const float* __restrict__ rec,
-                                                               float* __restrict__ dhn, float* __restrict__ dh0,
-                                                               int T_len, int nchunks, int dv, int xcd_map) {
-  constexpr int C = kBC, NW = kDsWaves<DK>, RHW = DK / 16 / NW, RT = C / 16;
+template <typename T, int DK, bool RS, int NW, int NS>
+__global__ __launch_bounds__(64 * NW) void chunk_bwd_dstates_kernel(const T* dout, const float* __restrict__ dhT,
+                                                                   const float* __restrict__ rec,
+                                                                   float* __restrict__ dhn, float* __restrict__ dh0,
+                                                                   int T_len, int nchunks, int dv, int xcd_map) {
+  constexpr int C = kBC, RHW = DK / 16 / NW, RT = C / 16;
   constexpr bool SPLIT = kSplitSeq<T, DK>;
-  static_assert(RT == 2 && (!SPLIT || RHW % 2 == 0), "32-position K blocks; whole 32-channel blocks per wave");
+  static_assert(RT == 2 && RHW >= 1 && (!SPLIT || RHW % 2 == 0), "32-position K blocks; whole 32-channel blocks per wave");
+  static_assert(NS == 1 || NS == 2, "one or two slices per workgroup");
   using R = BwdRec<DK>;
-  __shared__ f32x4 xb[2][NW][RT][64];   // partial dU of each wave, by chunk parity
+  __shared__ f32x4 xb[2][NW][NS][RT][64];   // partial dU of each wave, by chunk parity
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, r = lane & 15;
-  const int nsl = dv / 16;
   long long bh;
-  int slice;
-  head_slice(blockIdx.x, nsl, xcd_map, bh, slice);
-  const int col = slice * 16 + r;   // this lane's value column
-  const int rb = wave * RHW;        // the wave's first row tile
-  f32x4 dacc[RHW];                  // dH rows 16 (rb + rh) + 4 g + i, column col
+  int sg;
+  head_slice(blockIdx.x, dv / (16 * NS), xcd_map, bh, sg);
+  const int slice0 = sg * NS;         // the first slice
+  const int col0 = slice0 * 16 + r;   // this lane's value column in it (slice s: + 16 s)
+  const int rb = wave * RHW;          // the wave's first row tile
+  f32x4 dacc[NS][RHW];                // dH rows 16 (rb + rh) + 4 g + i, column col0 + 16 s
 #pragma unroll
-  for (int rh = 0; rh < RHW; ++rh)
+  for (int s = 0; s < NS; ++s)
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      dacc[rh][i] = dhT ? dhT[(bh * DK + 16 * (rb + rh) + 4 * g + i) * (long long)dv + col] : 0.f;
-  struct First {        // needed first in a chunk
-    f32x4 kr[RT][RHW];  // KR rows 16 rt + r, channels 16 (rb + kb) + 4 g .. + 3
-    f32x4 mt[RT][RT];   // M^T rows 16 rt + r, positions 16 kb + 4 g .. + 3 (kb >= rt)
-    T dov[RT][4];       // dO rows 16 kb + 4 g + e, column col, as stored (rows past the end: any row)
+    for (int rh = 0; rh < RHW; ++rh)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        dacc[s][rh][i] = dhT ? dhT[(bh * DK + 16 * (rb + rh) + 4 * g + i) * (long long)dv + col0 + 16 * s] : 0.f;
+  struct First {          // needed first in a chunk
+    f32x4 kr[RT][RHW];    // KR rows 16 rt + r, channels 16 (rb + kb) + 4 g .. + 3
+    f32x4 mt[RT][RT];     // M^T rows 16 rt + r, positions 16 kb + 4 g .. + 3 (kb >= rt)
+    T dov[NS][RT][4];     // dO rows 16 kb + 4 g + e, column col0 + 16 s, as stored (rows past the end: any row)
   };
   f32x4 tbt[RT][RT];    // TB^T rows 16 rt + r, positions 16 kb + 4 g .. + 3 (kb >= rt)
   f32x4 qgt[RHW][RT];   // QG^T rows 16 (rb + rh) + r, positions 16 kb + 4 g .. + 3
@@ -843,12 +851,14 @@ __global__ __launch_bounds__(128) void chunk_bwd_dstates_kernel(const T* dout, c
         o.mt[rt][kb] = *reinterpret_cast<const f32x4*>(rc + R::MT_OFF + (rt * RT + kb) * 256 + 4 * lane);
     const int t0 = c * C, cv = min(C, T_len - t0);
 #pragma unroll
-    for (int kb = 0; kb < RT; ++kb)
+    for (int s = 0; s < NS; ++s)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int t = 16 * kb + 4 * g + e;
-        o.dov[kb][e] = dout[(size_t)(bh * T_len + t0 + (t < cv ? t : 0)) * dv + col];
-      }
+      for (int kb = 0; kb < RT; ++kb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int t = 16 * kb + 4 * g + e;
+          o.dov[s][kb][e] = dout[(size_t)(bh * T_len + t0 + (t < cv ? t : 0)) * dv + col0 + 16 * s];
+        }
   };
   auto load_tbt = [&](int c) __attribute__((always_inline)) {
     if constexpr (RS) return;   // TB^T is not read (and not written) with a split record
@@ -878,7 +888,7 @@ __global__ __launch_bounds__(128) void chunk_bwd_dstates_kernel(const T* dout, c
   auto step = [&](First& cur, First& nxt, int c, bool live) __attribute__((always_inline)) {
     // exchange buffer by the parity of the UNCLAMPED chunk index: the dead
     // step (c = -1) then writes buffer 1, last read before the live chunk-0
-    // step's barrier, never buffer 0, which the other wave may still be
+    // step's barrier, never buffer 0, which the other waves may still be
     // reading for chunk 0
     const int par = c & 1;
     c = max(c, 0);
@@ -886,80 +896,121 @@ __global__ __launch_bounds__(128) void chunk_bwd_dstates_kernel(const T* dout, c
     const int cn = max(c - 1, 0);   // the next chunk processed (the first reloads itself)
     if (live)
 #pragma unroll
-      for (int rh = 0; rh < RHW; ++rh)   // dH'
-        *reinterpret_cast<f32x4*>(dhn + (size_t)chunk * DK * dv + hc_slot<DK>(16 * (rb + rh) + 4 * g, col)) = dacc[rh];
+      for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int rh = 0; rh < RHW; ++rh)   // dH'
+          *reinterpret_cast<f32x4*>(dhn + (size_t)chunk * DK * dv +
+                                    hc_slot<DK>(16 * (rb + rh) + 4 * g, col0 + 16 * s)) = dacc[s][rh];
     // (scheduling barriers keep each group of loads where it is written: the
     // scheduler would otherwise sink them toward their uses)
     __builtin_amdgcn_sched_barrier(0);
     load_first(nxt, cn);
     __builtin_amdgcn_sched_barrier(0);
     const int cv = min(C, T_len - c * C);
-    f32x4 dof[RT];
+    f32x4 dof[NS][RT];
 #pragma unroll
-    for (int kb = 0; kb < RT; ++kb)
+    for (int s = 0; s < NS; ++s)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) dof[kb][e] = 16 * kb + 4 * g + e < cv ? to_f32(cur.dov[kb][e]) : 0.f;
+      for (int kb = 0; kb < RT; ++kb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dof[s][kb][e] = 16 * kb + 4 * g + e < cv ? to_f32(cur.dov[s][kb][e]) : 0.f;
     // dU = M^T dO (first wave) + KR dH' (each wave its channels), summed over the waves
-    f32x4 du[RT];
-    Frag dob;   // dO as bf16 (exact: the input)
-    SplitFrag dhs[SPLIT ? RHW / 2 : 1];
+    f32x4 du[NS][RT];
+    Frag dob[NS];   // dO as bf16 (exact: the input)
+    SplitFrag dhs[NS][SPLIT ? RHW / 2 : 1];
     if constexpr (SPLIT) {
-      dob = frag_from_acc_bf16(dof[0], dof[1]);
 #pragma unroll
-      for (int j = 0; j < RHW / 2; ++j) dhs[j] = split_frag(dacc[2 * j], dacc[2 * j + 1]);
+      for (int s = 0; s < NS; ++s) {
+        dob[s] = frag_from_acc_bf16(dof[s][0], dof[s][1]);
+#pragma unroll
+        for (int j = 0; j < RHW / 2; ++j) dhs[s][j] = split_frag(dacc[s][2 * j], dacc[s][2 * j + 1]);
+      }
     }
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-      f32x4 m = zero4();
       if constexpr (SPLIT) {   // M^T is upper triangular
-        m = mma_split_exact(m, RS ? rec_pair(cur.mt[rt][0], cur.mt[rt][1])
-                                  : split_frag(rt == 0 ? cur.mt[0][0] : zero4(), cur.mt[rt][1]), dob);
+        const SplitFrag am = RS ? rec_pair(cur.mt[rt][0], cur.mt[rt][1])
+                                : split_frag(rt == 0 ? cur.mt[0][0] : zero4(), cur.mt[rt][1]);
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          const f32x4 m = mma_split_exact(zero4(), am, dob[s]);
+          du[s][rt] = wave == 0 ? m : zero4();
+        }
+#pragma unroll
+        for (int j = 0; j < RHW / 2; ++j) {
+          const SplitFrag ak = RS ? rec_pair(cur.kr[rt][2 * j], cur.kr[rt][2 * j + 1])
+                                  : split_frag(cur.kr[rt][2 * j], cur.kr[rt][2 * j + 1]);
+#pragma unroll
+          for (int s = 0; s < NS; ++s) du[s][rt] = mma_split(du[s][rt], ak, dhs[s][j]);
+        }
       } else {
 #pragma unroll
-        for (int kb = rt; kb < RT; ++kb)
-          m = mma<float>(m, Frag{__builtin_bit_cast(u32x4, cur.mt[rt][kb])}, frag_from_acc_f32(dof[kb]));
-      }
-      du[rt] = wave == 0 ? m : zero4();
-      if constexpr (SPLIT) {
+        for (int s = 0; s < NS; ++s) {
+          f32x4 m = zero4();
 #pragma unroll
-        for (int j = 0; j < RHW / 2; ++j)
-          du[rt] = mma_split(du[rt], RS ? rec_pair(cur.kr[rt][2 * j], cur.kr[rt][2 * j + 1])
-                                        : split_frag(cur.kr[rt][2 * j], cur.kr[rt][2 * j + 1]), dhs[j]);
-      } else {
+          for (int kb = rt; kb < RT; ++kb)
+            m = mma<float>(m, Frag{__builtin_bit_cast(u32x4, cur.mt[rt][kb])}, frag_from_acc_f32(dof[s][kb]));
+          du[s][rt] = wave == 0 ? m : zero4();
 #pragma unroll
-        for (int kb = 0; kb < RHW; ++kb)
-          du[rt] = mma<float>(du[rt], Frag{__builtin_bit_cast(u32x4, cur.kr[rt][kb])}, frag_from_acc_f32(dacc[kb]));
+          for (int kb = 0; kb < RHW; ++kb)
+            du[s][rt] =
+                mma<float>(du[s][rt], Frag{__builtin_bit_cast(u32x4, cur.kr[rt][kb])}, frag_from_acc_f32(dacc[s][kb]));
+        }
       }
     }
     // the part of dH that does not wait for dX: Gamma_C . dH' + QG^T dO, issued
     // before the exchange so that it runs while the waves meet
-    f32x4 hp[RHW];
+    f32x4 hp[NS][RHW];
 #pragma unroll
     for (int rh = 0; rh < RHW; ++rh) {
-      hp[rh] = gc[rh] * dacc[rh];
       if constexpr (SPLIT) {
-        hp[rh] = mma_split_exact(hp[rh], RS ? rec_pair(qgt[rh][0], qgt[rh][1]) : split_frag(qgt[rh][0], qgt[rh][1]), dob);
+        const SplitFrag aq = RS ? rec_pair(qgt[rh][0], qgt[rh][1]) : split_frag(qgt[rh][0], qgt[rh][1]);
+#pragma unroll
+        for (int s = 0; s < NS; ++s) hp[s][rh] = mma_split_exact(gc[rh] * dacc[s][rh], aq, dob[s]);
       } else {
 #pragma unroll
-        for (int kb = 0; kb < RT; ++kb)
-          hp[rh] = mma<float>(hp[rh], Frag{__builtin_bit_cast(u32x4, qgt[rh][kb])}, frag_from_acc_f32(dof[kb]));
+        for (int s = 0; s < NS; ++s) {
+          hp[s][rh] = gc[rh] * dacc[s][rh];
+#pragma unroll
+          for (int kb = 0; kb < RT; ++kb)
+            hp[s][rh] = mma<float>(hp[s][rh], Frag{__builtin_bit_cast(u32x4, qgt[rh][kb])}, frag_from_acc_f32(dof[s][kb]));
+        }
       }
     }
-    if constexpr (NW == 2) {
+    if constexpr (NW > 1) {
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) xb[par][wave][rt][lane] = du[rt];
+      for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) xb[par][wave][s][rt][lane] = du[s][rt];
       __syncthreads();
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) du[rt] += xb[par][1 - wave][rt][lane];
+      for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          if constexpr (NW == 2) {
+            du[s][rt] += xb[par][1 - wave][s][rt][lane];
+          } else {   // the waves' parts in wave order, the same sum in every wave
+            f32x4 a = xb[par][0][s][rt][lane];
+#pragma unroll
+            for (int w = 1; w < NW; ++w) a += xb[par][w][s][rt][lane];
+            du[s][rt] = a;
+          }
+        }
     }
     if constexpr (RS) {
       // dH = Gamma_C . dH' + QG^T dO + (-K~G^T) dU: no dX on the chain
-      const SplitFrag dus = split_frag(du[0], du[1]);
+      SplitFrag dus[NS];
+#pragma unroll
+      for (int s = 0; s < NS; ++s) dus[s] = split_frag(du[s][0], du[s][1]);
 #pragma unroll
       for (int rh = 0; rh < RHW; ++rh) {
-        const f32x4 h = mma_split(hp[rh], rec_pair(kgt[rh][0], kgt[rh][1]), dus);
+        const SplitFrag ak = rec_pair(kgt[rh][0], kgt[rh][1]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dacc[rh][i] = live ? h[i] : dacc[rh][i];
+        for (int s = 0; s < NS; ++s) {
+          const f32x4 h = mma_split(hp[s][rh], ak, dus[s]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) dacc[s][rh][i] = live ? h[i] : dacc[s][rh][i];
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
       load_last(cn);
@@ -967,39 +1018,50 @@ __global__ __launch_bounds__(128) void chunk_bwd_dstates_kernel(const T* dout, c
       return;
     }
     // dX = TB^T dU, negated for the update below
-    f32x4 ndx[RT];
+    f32x4 ndx[NS][RT];
     if constexpr (SPLIT) {   // TB^T is upper triangular
-      const SplitFrag dus = split_frag(du[0], du[1]);
-      ndx[0] = -mma_split(zero4(), RS ? rec_pair(tbt[0][0], tbt[0][1]) : split_frag(tbt[0][0], tbt[0][1]), dus);
-      ndx[1] = -mma_split(zero4(), RS ? rec_pair(tbt[1][0], tbt[1][1]) : split_frag(zero4(), tbt[1][1]), dus);
+      const SplitFrag t0 = split_frag(tbt[0][0], tbt[0][1]), t1 = split_frag(zero4(), tbt[1][1]);
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const SplitFrag dus = split_frag(du[s][0], du[s][1]);
+        ndx[s][0] = -mma_split(zero4(), t0, dus);
+        ndx[s][1] = -mma_split(zero4(), t1, dus);
+      }
     } else {
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        f32x4 x = zero4();
+      for (int s = 0; s < NS; ++s)
 #pragma unroll
-        for (int kb = rt; kb < RT; ++kb)
-          x = mma<float>(x, Frag{__builtin_bit_cast(u32x4, tbt[rt][kb])}, frag_from_acc_f32(du[kb]));
-        ndx[rt] = -x;
-      }
+        for (int rt = 0; rt < RT; ++rt) {
+          f32x4 x = zero4();
+#pragma unroll
+          for (int kb = rt; kb < RT; ++kb)
+            x = mma<float>(x, Frag{__builtin_bit_cast(u32x4, tbt[rt][kb])}, frag_from_acc_f32(du[s][kb]));
+          ndx[s][rt] = -x;
+        }
     }
     __builtin_amdgcn_sched_barrier(0);
     load_tbt(cn);
     __builtin_amdgcn_sched_barrier(0);
     // dH = Gamma_C . dH' + QG^T dO - KG^T dX
-    SplitFrag ndxs;
-    if constexpr (SPLIT) ndxs = split_frag(ndx[0], ndx[1]);
+    SplitFrag ndxs[NS];
+    if constexpr (SPLIT)
+#pragma unroll
+      for (int s = 0; s < NS; ++s) ndxs[s] = split_frag(ndx[s][0], ndx[s][1]);
 #pragma unroll
     for (int rh = 0; rh < RHW; ++rh) {
-      f32x4 h = hp[rh];
-      if constexpr (SPLIT) {
-        h = mma_split(h, RS ? rec_pair(kgt[rh][0], kgt[rh][1]) : split_frag(kgt[rh][0], kgt[rh][1]), ndxs);
-      } else {
 #pragma unroll
-        for (int kb = 0; kb < RT; ++kb)
-          h = mma<float>(h, Frag{__builtin_bit_cast(u32x4, kgt[rh][kb])}, frag_from_acc_f32(ndx[kb]));
+      for (int s = 0; s < NS; ++s) {
+        f32x4 h = hp[s][rh];
+        if constexpr (SPLIT) {
+          h = mma_split(h, split_frag(kgt[rh][0], kgt[rh][1]), ndxs[s]);
+        } else {
+#pragma unroll
+          for (int kb = 0; kb < RT; ++kb)
+            h = mma<float>(h, Frag{__builtin_bit_cast(u32x4, kgt[rh][kb])}, frag_from_acc_f32(ndx[s][kb]));
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dacc[s][rh][i] = live ? h[i] : dacc[s][rh][i];
       }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) dacc[rh][i] = live ? h[i] : dacc[rh][i];
     }
     __builtin_amdgcn_sched_barrier(0);
     load_last(cn);
@@ -1019,9 +1081,12 @@ __global__ __launch_bounds__(128) void chunk_bwd_dstates_kernel(const T* dout, c
   }
   if (dh0)
 #pragma unroll
-    for (int rh = 0; rh < RHW; ++rh)
+    for (int s = 0; s < NS; ++s)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dh0[(bh * DK + 16 * (rb + rh) + 4 * g + i) * (long long)dv + col] = dacc[rh][i];
+      for (int rh = 0; rh < RHW; ++rh)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          dh0[(bh * DK + 16 * (rb + rh) + 4 * g + i) * (long long)dv + col0 + 16 * s] = dacc[s][rh][i];
 }
 
 // ============================================================ grad (per chunk)
@@ -1964,7 +2029,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a) {
   // split pairs, and the record holds them (BwdRec).
   auto prep = chunk_bwd_prep_kernel<T, DK, false>;
   auto states = chunk_bwd_states_kernel<T, DK, false, 1>;
-  auto dstates = chunk_bwd_dstates_kernel<T, DK, false>;
+  auto dstates = chunk_bwd_dstates_kernel<T, DK, false, kDsWaves<DK>, 1>;
   auto grad = chunk_bwd_grad_kernel<T, DK, 16, false>;
   if constexpr (std::is_same<T, bf16_t>::value) {
     if (a.dv % 32 == 0) grad = chunk_bwd_grad_kernel<T, DK, 32, false>;
@@ -1972,7 +2037,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a) {
       if (a.dv % 32 == 0) {
         prep = chunk_bwd_prep_kernel<T, DK, true>;
         states = chunk_bwd_states_kernel<T, DK, true, 1>;
-        dstates = chunk_bwd_dstates_kernel<T, DK, true>;
+        dstates = chunk_bwd_dstates_kernel<T, DK, true, kDsWaves<DK>, 1>;
         grad = chunk_bwd_grad_kernel<T, DK, 32, true>;
       }
     }
@@ -1998,8 +2063,18 @@ static hipError_t launch_bwd_t(const BwdArgs& a) {
     hipLaunchKernelGGL(states, dim3((unsigned)(BH * nsl / (two ? 2 : 1))), dim3(64), 0, a.stream, (const T*)a.v, a.h0,
                        rec, hc, a.T, nch, a.dv, xcd_map);
   }
-  hipLaunchKernelGGL(dstates, dim3((unsigned)(BH * nsl)), dim3(64 * kDsWaves<DK>), 0, a.stream, (const T*)a.dout,
-                     a.dhT, rec, dhn, a.gh0, a.T, nch, a.dv, xcd_map);
+  // the reverse pass likewise halves its workgroups (four waves of two slices
+  // each) once one slice per workgroup would put two or more on every CU
+  bool two_ds = false;
+  int ds_waves = kDsWaves<DK>;
+  if constexpr (kSplitSeq<T, DK> && DK == 128)
+    if (dstates == chunk_bwd_dstates_kernel<T, DK, true, kDsWaves<DK>, 1> && BH * nsl >= 2LL * device_cus()) {
+      two_ds = true;
+      ds_waves = 4;
+      dstates = chunk_bwd_dstates_kernel<T, DK, true, 4, 2>;
+    }
+  hipLaunchKernelGGL(dstates, dim3((unsigned)(BH * nsl / (two_ds ? 2 : 1))), dim3(64 * ds_waves), 0, a.stream,
+                     (const T*)a.dout, a.dhT, rec, dhn, a.gh0, a.T, nch, a.dv, xcd_map);
   if (total > 0)
     hipLaunchKernelGGL(grad, dim3((unsigned)total), dim3(kGThreads), 0, a.stream, (const T*)a.q, (const T*)a.k,
                        (const T*)a.v, (const T*)a.alpha, (const T*)a.beta, (const T*)a.dout, rec, hc, dhn, a.gq, a.gk,
