@@ -1240,8 +1240,34 @@ __global__ __launch_bounds__(kGThreads) void chunk_bwd_grad_kernel(
   const int t0 = c * C, cv = min(C, T_len - t0);
   const long long row0 = bh * (long long)T_len + t0;
   const float* rc = rec + (size_t)chunk * R::FLOATS;
+  const float* hcc = hc + (size_t)chunk * DK * dv;
+  const float* dhc = dhn + (size_t)chunk * DK * dv;
+  // one value slice's operands, fetched into registers a slice ahead (V and
+  // dO as stored, at in-bounds addresses: the mask for rows past the end is
+  // applied when they are staged, so that nothing waits for them early)
+  constexpr int NH = (DK * DS + kGThreads - 1) / kGThreads, NV = (C * DS + kGThreads - 1) / kGThreads;
+  float rH[NH], rdH[NH];
+  T rV[NV], rO[NV];
+  auto fetch = [&](int col0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NH; ++i) {
+      const int e = tid + i * kGThreads, ee = e < DK * DS ? e : 0;
+      rH[i] = hcc[(size_t)col0 * DK + ee];   // the slice's blocks, in slot order (hc_slot)
+      rdH[i] = dhc[(size_t)col0 * DK + ee];
+    }
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int e = tid + i * kGThreads, t = e / DS, j = e % DS;
+      const size_t gi = e < C * DS && t < cv ? (size_t)(row0 + t) * dv + col0 + j : 0;
+      rV[i] = v[gi];
+      rO[i] = dout[gi];
+    }
+  };
+  auto v_ok = [&](int e) { return e < C * DS && e / DS < cv; };   // a staged V / dO element inside the chunk
+  // beta as stored, fetched with the chunk's operands
+  const T braw = beta[row0 + (tid < C && tid < cv ? tid : 0)];
 
-  {   // all of the chunk's operand loads issued before any is stored
+  {   // all of the chunk's operand loads, and the first value slice's, issued before any is stored
     constexpr int NK = (C * DK + kGThreads - 1) / kGThreads, NC = (C * C + kGThreads - 1) / kGThreads;
     float r0[NK], r1[NK], r2[NK], r3[NK], r4[NK], m0[NC], m1[NC], m2[NC], m3[NC];
 #pragma unroll
@@ -1301,6 +1327,7 @@ __global__ __launch_bounds__(kGThreads) void chunk_bwd_grad_kernel(
       m2[i] = rc[R::T_OFF + (in ? e : 0)];
       m3[i] = rc[R::S_OFF + (in ? e : 0)];
     }
+    fetch(0);
     if constexpr (RS) {
 #pragma unroll
       for (int i = 0; i < NRS; ++i) {
@@ -1356,7 +1383,7 @@ __global__ __launch_bounds__(kGThreads) void chunk_bwd_grad_kernel(
       }
     }
   }
-  if (tid < C) sb[tid] = tid < cv ? to_f32(beta[row0 + tid]) : 0.f;
+  if (tid < C) sb[tid] = tid < cv ? to_f32(braw) : 0.f;
   if (tid < DK) sGC[tid] = 0.f;
 
   // ---- value slices: dV, and the dv contractions accumulated on the matrix cores
@@ -1369,28 +1396,6 @@ __global__ __launch_bounds__(kGThreads) void chunk_bwd_grad_kernel(
   for (int i = 0; i < TPW; ++i) aqg[i] = akg[i] = akr[i] = zero4();
 #pragma unroll
   for (int i = 0; i < TMW; ++i) am[i] = atb[i] = zero4();
-  const float* hcc = hc + (size_t)chunk * DK * dv;
-  const float* dhc = dhn + (size_t)chunk * DK * dv;
-  // one value slice's operands, fetched into registers a slice ahead
-  constexpr int NH = (DK * DS + kGThreads - 1) / kGThreads, NV = (C * DS + kGThreads - 1) / kGThreads;
-  float rH[NH], rdH[NH], rV[NV], rO[NV];
-  auto fetch = [&](int col0) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < NH; ++i) {
-      const int e = tid + i * kGThreads, ee = e < DK * DS ? e : 0, ii = ee / DS, j = ee % DS;
-      rH[i] = hcc[(size_t)col0 * DK + ee];   // the slice's blocks, in slot order (hc_slot)
-      rdH[i] = dhc[(size_t)col0 * DK + ee];
-    }
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int e = tid + i * kGThreads, t = e / DS, j = e % DS;
-      const bool ok = e < C * DS && t < cv;
-      const size_t gi = ok ? (size_t)(row0 + t) * dv + col0 + j : 0;
-      rV[i] = ld_or(v, gi, ok, 0.f);
-      rO[i] = ld_or(dout, gi, ok, 0.f);
-    }
-  };
-  fetch(0);
   if constexpr (SG) {
     // per slot, H . dH' summed over the slices (the slot's row is the same in
     // every slice), reduced per channel after the loop in a fixed order
@@ -1418,8 +1423,8 @@ __global__ __launch_bounds__(kGThreads) void chunk_bwd_grad_kernel(
       for (int i = 0; i < NV; ++i) {
         const int e = tid + i * kGThreads;
         if (e < C * DS) {   // exact in bf16 (the inputs)
-          Vb[e] = (u16)(__float_as_uint(rV[i]) >> 16);
-          dOb[(e / DS) * SP + kperm(e % DS)] = (u16)(__float_as_uint(rO[i]) >> 16);
+          Vb[e] = v_ok(e) ? rV[i].bits : (u16)0;
+          dOb[(e / DS) * SP + kperm(e % DS)] = v_ok(e) ? rO[i].bits : (u16)0;
         }
       }
       __syncthreads();
@@ -1523,8 +1528,8 @@ __global__ __launch_bounds__(kGThreads) void chunk_bwd_grad_kernel(
       const int e = tid + i * kGThreads;
       if (e < C * DS) {
         const int o = (e / DS) * DSP + e % DS;
-        sX[o] = rV[i];
-        sdO[o] = rO[i];
+        sX[o] = v_ok(e) ? to_f32(rV[i]) : 0.f;
+        sdO[o] = v_ok(e) ? to_f32(rO[i]) : 0.f;
       }
     }
     __syncthreads();
