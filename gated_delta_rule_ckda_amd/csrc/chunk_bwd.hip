@@ -127,14 +127,6 @@ __device__ __forceinline__ void gemm_lds(float* d, int di, const float* a, int a
   }
 }
 
-// p[i] if ok, else `other`; the load is always issued (at p[0] when not ok,
-// which every caller keeps valid) so that it needs no branch: a branch per
-// element would put each load in a block of its own, waited on by itself.
-template <typename T>
-__device__ __forceinline__ float ld_or(const T* p, size_t i, bool ok, float other) {
-  const float x = to_f32(p[ok ? i : 0]);
-  return ok ? x : other;
-}
 
 // Workgroup -> (batch-head, value slice) of the two sequential kernels.  With
 // xcd_map the nsl slices of one head get ids that are equal modulo 8, so they
@@ -1269,15 +1261,18 @@ __global__ __launch_bounds__(kGThreads) void chunk_bwd_grad_kernel(
 
   {   // all of the chunk's operand loads, and the first value slice's, issued before any is stored
     constexpr int NK = (C * DK + kGThreads - 1) / kGThreads, NC = (C * C + kGThreads - 1) / kGThreads;
-    float r0[NK], r1[NK], r2[NK], r3[NK], r4[NK], m0[NC], m1[NC], m2[NC], m3[NC];
+    // (q, k and alpha as stored, at in-bounds addresses: rows past the end
+    // are masked when staged, so that nothing waits for them early)
+    T r0[NK], r1[NK], r2[NK];
+    float r3[NK], r4[NK], m0[NC], m1[NC], m2[NC], m3[NC];
 #pragma unroll
     for (int i = 0; i < NK; ++i) {
       const int e = tid + i * kGThreads, t = e / DK, ch = e % DK;
       const bool in = e < C * DK, ok = in && t < cv;
       const size_t gi = ok ? (size_t)(row0 + t) * DK + ch : 0;
-      r0[i] = ld_or(q, gi, ok, 0.f);
-      r1[i] = ld_or(k, gi, ok, 0.f);
-      r2[i] = ld_or(alpha, gi, ok, 1.f);
+      r0[i] = q[gi];
+      r1[i] = k[gi];
+      r2[i] = alpha[gi];
       if constexpr (!RS) {
         r3[i] = rc[R::KG_OFF + (in ? e : 0)];
         r4[i] = rc[R::KR_OFF + (in ? e : 0)];
@@ -1346,9 +1341,10 @@ __global__ __launch_bounds__(kGThreads) void chunk_bwd_grad_kernel(
       const int e = tid + i * kGThreads;
       if (e < C * DK) {
         const int o = (e / DK) * DKP + e % DK;
-        sq[o] = from_f32<T>(r0[i]);
-        sk[o] = from_f32<T>(r1[i]);
-        sa[o] = from_f32<T>(r2[i]);
+        const bool ok = e / DK < cv;   // rows past a ragged end: no query or key, gate 1
+        sq[o] = ok ? r0[i] : T{};
+        sk[o] = ok ? r1[i] : T{};
+        sa[o] = ok ? r2[i] : from_f32<T>(1.f);
         int tt, cc;   // KG and KR are in fragment order
         frag_pos(e, DK, tt, cc);
         if constexpr (RS) {
