@@ -606,7 +606,7 @@ __global__ __launch_bounds__(64) void chunk_bwd_states_kernel(const T* v, const 
   f32x4 kr[RH][RT];   // KR^T rows 16 rh + r (channels), positions 16 kb + 4 g .. + 3
   f32x4 tb[RT][RT];   // TB rows 16 rt + r, positions 16 kb + 4 g .. + 3 (kb <= rt)
   f32x4 gc[RH];       // Gamma_C at channels 16 rh + 4 g .. + 3
-  T vv[NS][RT][4];    // V rows 16 rt + 4 g .. + 3, column col0 + 16 s, as stored (rows past the end: 0)
+  T vv[NS][RT][4];    // V rows 16 rt + 4 g .. + 3, column col0 + 16 s, as stored (rows past the end: 0 or any row)
   const uint32_t v_boff = (uint32_t)((4 * g * dv + col0) * sizeof(T));
   const uint32_t lboff = 16u * lane;   // this lane's 16 bytes of a fragment tile
   auto recp = [&](int c) { return rec + (size_t)(bh * nchunks + c) * R::FLOATS; };
@@ -626,12 +626,25 @@ __global__ __launch_bounds__(64) void chunk_bwd_states_kernel(const T* v, const 
       for (int kb = 0; kb < (RS ? RT : rt + 1); ++kb)   // (a split record: both halves of every pair)
         tb[rt][kb] = ld16(rc + R::TB_OFF + (rt * RT + kb) * 256, lboff);
     // V rows kept as stored, so that nothing waits for them before the next
-    // chunk: row 16 rt + i of the chunk at a uniform base, plus this lane's
-    // byte offset (rows 4 g and its column); rows past the end (last chunk
-    // only) read as 0
+    // chunk.  With split products: row 16 rt + i of the chunk at a uniform base
+    // plus this lane's byte offset (rows 4 g and its column), rows past the end
+    // (last chunk only) read as 0; with fp32 products that form came out slower
+    // (389 -> 474 us at the bench shape), and every row's address is formed
+    // per element, a row past the end reading the chunk's first row and masked
+    // where it is used.
     const int t0 = c * C, cv = min(C, T_len - t0);
     const T* vc = v + ((size_t)bh * T_len + t0) * dv;
-    if (cv == C) {
+    if constexpr (!SPLIT) {
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int t = 16 * rt + 4 * g + i;
+            vv[s][rt][i] = v[(size_t)(bh * T_len + t0 + (t < cv ? t : 0)) * dv + col0 + 16 * s];
+          }
+    } else if (cv == C) {
 #pragma unroll
       for (int s = 0; s < NS; ++s)
 #pragma unroll
@@ -707,11 +720,13 @@ __global__ __launch_bounds__(64) void chunk_bwd_states_kernel(const T* v, const 
           for (int s = 0; s < NS; ++s)
             p[s] = mma<float>(p[s], Frag{__builtin_bit_cast(u32x4, kg[rt][kb])}, frag_from_acc_f32(hacc[s][kb]));
       }
-      // (rows past the end: V read as 0 and no key, so X is 0)
+      // (rows past the end: V read as 0 or masked here, and no key, so X is 0)
+      const int cvx = min(C, T_len - c * C);
 #pragma unroll
       for (int s = 0; s < NS; ++s)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) xacc[s][rt][i] = to_f32(vv[s][rt][i]) - p[s][i];
+        for (int i = 0; i < 4; ++i)
+          xacc[s][rt][i] = (SPLIT || 16 * rt + 4 * g + i < cvx ? to_f32(vv[s][rt][i]) : 0.f) - p[s][i];
     }
     __builtin_amdgcn_sched_barrier(0);
     load_kg(cn);
