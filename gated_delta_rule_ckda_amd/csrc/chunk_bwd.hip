@@ -2029,6 +2029,34 @@ static int device_cus() {
   return n;
 }
 
+// workgroups of `kernel` resident per CU at `threads` threads (its LDS and
+// registers decide), cached per kernel and device (kernels past the cache's
+// slots are asked each time); at least 1
+template <typename K>
+static int resident_per_cu(K kernel, int threads) {
+  constexpr int kSlots = 16;
+  static std::atomic<int> cache[kSlots][64];   // [kernel slot][device]
+  static std::atomic<const void*> which[kSlots];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  const void* f = reinterpret_cast<const void*>(kernel);
+  int slot = -1;
+  for (int i = 0; i < kSlots && slot < 0; ++i) {
+    const void* w = which[i].load(std::memory_order_relaxed);
+    if (w == f) slot = i;
+    else if (w == nullptr) {
+      const void* expected = nullptr;
+      if (which[i].compare_exchange_strong(expected, f) || expected == f) slot = i;
+    }
+  }
+  int n = slot >= 0 ? cache[slot][dev].load(std::memory_order_relaxed) : 0;
+  if (n == 0) {
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, 0) != hipSuccess || n < 1) n = 1;
+    if (slot >= 0) cache[slot][dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 template <typename T, int DK>
 static hipError_t launch_bwd_t(const BwdArgs& a) {
   using R = BwdRec<DK>;
@@ -2060,10 +2088,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a) {
   }
   if (total > 0) {
     // prep loops over chunks: as many workgroups as are resident at once
-    int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, prep, kPThreads, 0) != hipSuccess || per_cu < 1)
-      per_cu = 1;
-    const long long nprep = std::min<long long>(total, (long long)per_cu * device_cus());
+    const long long nprep = std::min<long long>(total, (long long)resident_per_cu(prep, kPThreads) * device_cus());
     hipLaunchKernelGGL(prep, dim3((unsigned)nprep), dim3(kPThreads), 0, a.stream, (const T*)a.q, (const T*)a.k,
                        (const T*)a.alpha, (const T*)a.beta, rec, a.T, nch, total);
     // with split products, two value slices per wave once one per wave would

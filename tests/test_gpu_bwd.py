@@ -119,6 +119,14 @@ def test_two_slices_per_wave(dtype, dk, dv, B, H, T):
     run(w, heads=[0, B * H // 2 + 1, B * H - 1])
 
 
+def test_two_slices_without_initial_or_final_state():
+    """The two-slice forward pass and the four-wave reverse pass (bench-sized
+    grid, bf16, dk 128) with neither h0 nor dhT, an odd number of 32-position
+    chunks (the reverse pass ends with a step that must change nothing)."""
+    w = gen.Workload("bwd_two_slices", 4, 16, 99, 128, 128, 64, "bf16", "ckda_tanh", "normal", 7690)
+    run(w, heads=[0, 33, 63], h0=False, dhT=False)
+
+
 @pytest.mark.parametrize("dtype,dk,dv,B,H,T", [
     ("bf16", 128, 128, 8, 16, 77), ("f32", 128, 64, 8, 16, 77), ("bf16", 64, 64, 16, 16, 77),
     ("f32", 32, 32, 16, 16, 50)])
