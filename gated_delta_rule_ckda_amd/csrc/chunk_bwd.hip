@@ -15,13 +15,19 @@
 //   dA = -T^T dTB Diag(beta) T^T (strictly lower), dS = Diag(beta) dA,
 // followed by the decayed-Gram derivatives and every gate derivative.
 //
-// Four kernels, fp32 throughout:
-//   prep    (one workgroup per chunk)   S, M by recursive halving, T by forward
-//           substitution, TB, KG, KR, QG, Gamma_C -> a per-chunk fp32 record
-//           (with the transposes the sequential kernels contract along);
-//   states  (sequential, per head and 16-column value slice) chunk-start states;
-//   dstates (sequential, reverse)       the state gradient entering each chunk
-//           from its end, and dh0;
+// Four kernels, fp32 arithmetic (with bf16 inputs at dk >= 64 the products of
+// the sequential passes and of grad's value-slice loop take split bf16 pairs,
+// about 16 bits, on bf16 matrix cores):
+//   prep    (resident workgroups looping over chunks) S, M by recursive
+//           halving, T by forward substitution, TB, KG, KR, QG, Gamma_C -> a
+//           per-chunk record (with the transposes the sequential kernels
+//           contract along);
+//   states  (sequential, per head and 16-column value slice; two slices per
+//           wave with split products once one per wave would put two
+//           workgroups on every CU) chunk-start states;
+//   dstates (sequential, reverse; at dk 128 with split products and such
+//           grids, four waves of two slices per workgroup) the state gradient
+//           entering each chunk from its end, and dh0;
 //   grad    (one workgroup per chunk)   all per-token gradients.
 //
 // No gate is ever divided by.  Recursive halving: for a block of positions
