@@ -197,7 +197,7 @@ __device__ __forceinline__ SplitFrag rec_pair(f32x4 hi, f32x4 lo) {
 }
 
 // ============================================================ prep
-// threads of the prep kernel (its LDS keeps one workgroup per CU at dk = 128;
+// threads of the prep kernel (its LDS keeps one workgroup per CU at dk = 128:
 // two waves per SIMD hide part of each one's latencies)
 constexpr int kPThreads = 512;
 
@@ -207,13 +207,27 @@ __global__ __launch_bounds__(kPThreads) void chunk_bwd_prep_kernel(const T* q, c
                                                                    int nchunks, long long total) {
   constexpr int C = kBC, DKP = DK + 1, CP = C + 1;
   using R = BwdRec<DK>;
-  __shared__ float sq[C * DKP], sk[C * DKP], sa[C * DKP];
-  // rescaled operands of one halving level, rows 16-byte aligned for 4-channel reads
+  // One buffer holds, in turn, the staged q, k and alpha (rows of DKP
+  // floats), then (split record) QG and KR, then the rescaled rows of the five
+  // halving levels (per level 16 x, 16 query and 16 y rows of XP floats,
+  // 16-byte aligned for 4-channel reads), then B21 T11: the staged rows are
+  // read once, into the channel threads' registers and the diagonal of M,
+  // before anything else is written there.
   constexpr int XP = DK + 4;
-  __shared__ __align__(16) float sx[C * XP], sxq[C * XP], sy[C * XP];
-  // (split record) KG, kept for K~G = TB KG after the halving has reused sx
+  static_assert(C == 32, "five halving levels of 16-row tiles");
+  static_assert(DKP <= XP && 3 * C <= 5 * 3 * 16, "the staged rows fit the level rows' buffer");
+  __shared__ __align__(16) float slev[5 * 3 * 16 * XP];
+  float* const sq = slev;
+  float* const sk = slev + C * XP;
+  float* const sa = slev + 2 * C * XP;
+  float* const sqg = slev;
+  float* const skr = slev + C * XP;
+  // (split record) KG, kept for K~G = TB KG
   __shared__ __align__(16) float skg[RS ? C * XP : 1];
-  __shared__ float sS[C * CP], sM[C * CP], sT[C * CP], sb[C];
+  // S in 16-byte aligned rows (the block solve reads them four at a time)
+  constexpr int SP = C + 4;
+  __shared__ __align__(16) float sS[C * SP], sb[C];
+  __shared__ float sM[C * CP], sT[C * CP];
 
   const int tid = threadIdx.x;
   // A persistent loop over chunks blockIdx.x, + gridDim.x, ...: each chunk's
@@ -257,17 +271,17 @@ __global__ __launch_bounds__(kPThreads) void chunk_bwd_prep_kernel(const T* q, c
       }
     }
     if (tid < C) sb[tid] = tid < cv ? to_f32(xb) : 0.f;
-    for (int e = tid; e < C * CP; e += kPThreads) {
+    for (int e = tid; e < C * SP; e += kPThreads) {
       sS[e] = 0.f;
-      sM[e] = 0.f;
+      if (e < C * CP) sM[e] = 0.f;
     }
     lds_barrier();
     if (chunk + gridDim.x < total) fetch(chunk + gridDim.x);   // the next chunk's inputs, under this one's work
 
     float* rc = rec + (size_t)chunk * R::FLOATS;
     // this thread's channel (tid < DK): its gate, key and query columns in
-    // registers for the sequential products below (read from LDS once; the LDS
-    // allows one workgroup per CU, one wave per SIMD, which hides no latency)
+    // registers for the sequential products below (the staged rows' only read
+    // besides the diagonal of M)
     float ca[C], ck[C], cq[C];
     if (tid < DK) {
 #pragma unroll
@@ -277,6 +291,17 @@ __global__ __launch_bounds__(kPThreads) void chunk_bwd_prep_kernel(const T* q, c
         cq[t] = sq[t * DKP + tid];
       }
     }
+    {   // diagonal of M (G = 1): kPThreads / C threads per row
+      constexpr int TPE = kPThreads / C;
+      static_assert(TPE <= 64 && DK % TPE == 0, "row groups within a wave");
+      const int t = tid / TPE, sub = tid % TPE;
+      float d = 0.f;
+#pragma unroll
+      for (int i = 0; i < DK / TPE; ++i) d += sq[t * DKP + sub + i * TPE] * sk[t * DKP + sub + i * TPE];
+      d = group_sum<TPE>(d);
+      if (sub == 0) sM[t * CP + t] = d;
+    }
+    lds_barrier();   // the staged rows are read: their buffer is rewritten below
     if (tid < DK) {   // per channel: Gamma, KG, QG, Gamma_C; G(C-1, j), KR
       const int ch = tid;
       float gm = 1.f, kg[4], qg[4];
@@ -287,7 +312,7 @@ __global__ __launch_bounds__(kPThreads) void chunk_bwd_prep_kernel(const T* q, c
         qg[t % 4] = cq[t] * gm;
         if constexpr (RS) {   // to LDS; all threads write the split record below
           skg[t * XP + ch] = kg[t % 4];
-          sxq[t * XP + ch] = qg[t % 4];
+          sqg[t * XP + ch] = qg[t % 4];
         } else {
           rc[R::KG_OFF + frag_off(t, ch, DK)] = kg[t % 4];
           if (t % 4 == 3) {   // KG^T, QG^T: this channel's rows, 16 bytes at a time
@@ -303,7 +328,7 @@ __global__ __launch_bounds__(kPThreads) void chunk_bwd_prep_kernel(const T* q, c
         kr[t % 4] = ck[t] * ge;
         ge *= ca[t];
         if constexpr (RS) {
-          sy[t * XP + ch] = kr[t % 4];
+          skr[t * XP + ch] = kr[t % 4];
         } else {
           rc[R::KR_OFF + frag_off(t, ch, DK)] = kr[t % 4];
           if (t % 4 == 0)   // KR^T: this channel's row
@@ -349,14 +374,14 @@ __global__ __launch_bounds__(kPThreads) void chunk_bwd_prep_kernel(const T* q, c
           off = field == 0 ? R::KG_OFF : R::KR_OFF;
           kd = DK;
           if (field == 0) rows(skg);
-          else rows(sy);
+          else rows(skr);
         } else {           // KG^T, QG^T, KR^T
           rt = pair;
           kb = 0;
           off = field == 2 ? R::KGT_OFF : field == 3 ? R::QGT_OFF : R::KRT_OFF;
           kd = C;
-          if (field == 3) cols(sxq);
-          else cols(sy);
+          if (field == 3) cols(sqg);
+          else cols(skr);
         }
         u32x4 h, l;
         split8(v8, h, l);
@@ -364,100 +389,101 @@ __global__ __launch_bounds__(kPThreads) void chunk_bwd_prep_kernel(const T* q, c
         *reinterpret_cast<u32x4*>(tile) = h;
         *reinterpret_cast<u32x4*>(tile + 256) = l;
       }
-      lds_barrier();   // the halving below rewrites sx, sxq and sy
+      lds_barrier();   // the level rows below overwrite QG and KR
     }
-    {   // diagonal of M (G = 1): kPThreads / C threads per row
-      constexpr int TPE = kPThreads / C;
-      static_assert(TPE <= 64 && DK % TPE == 0, "row groups within a wave");
-      const int t = tid / TPE, sub = tid % TPE;
-      float d = 0.f;
-#pragma unroll
-      for (int ch = sub; ch < DK; ch += TPE) d += sq[t * DKP + ch] * sk[t * DKP + ch];
-      d = group_sum<TPE>(d);
-      if (sub == 0) sM[t * CP + t] = d;
-    }
-    // S and M below the diagonal by recursive halving (h a compile-time
-    // constant per level, so that the channel's loops run on its registers)
-    auto level = [&](auto hh) __attribute__((always_inline)) {
-      constexpr int h = decltype(hh)::value;
-      if (tid < DK) {
-        const int ch = tid;
+    // S and M below the diagonal by recursive halving.  Level h (16, 8, 4, 2,
+    // 1) splits the chunk into blocks of 2h positions around their midpoints
+    // m: entry (t, j) with t in the upper and j in the lower half of one block
+    // is sum over channels of (x_t G(t, m)) (y_j G(m, j)), every factor a
+    // product of at most h gates.  The channel threads write all five levels'
+    // rescaled rows at once; then each level is two 16 x 16 products over the
+    // channels (rows u = block * h + offset in the half: S from the x rows,
+    // M from the query rows, both against the y rows), on fp32 matrix cores,
+    // of which the blocks' h x h diagonal quadrants are the level's entries.
+    if (tid < DK) {
+      const int ch = tid;
+      auto rescale = [&](auto ll) __attribute__((always_inline)) {
+        constexpr int L = decltype(ll)::value, h = (C / 2) >> L;
+        float* X = slev + L * 3 * 16 * XP;
 #pragma unroll
         for (int lo = 0; lo < C; lo += 2 * h) {
-          const int m = lo + h - 1;
+          const int m = lo + h - 1, u0 = lo / 2;
           float f = 1.f;
 #pragma unroll
           for (int t = m + 1; t <= m + h; ++t) {   // x_t G(t, m)
             f *= ca[t];
-            sx[t * XP + ch] = ck[t] * f;
-            sxq[t * XP + ch] = cq[t] * f;
+            X[(u0 + t - m - 1) * XP + ch] = ck[t] * f;
+            X[(16 + u0 + t - m - 1) * XP + ch] = cq[t] * f;
           }
           float e = 1.f;
 #pragma unroll
           for (int j = m; j >= lo; --j) {          // y_j G(m, j)
-            sy[j * XP + ch] = ck[j] * e;
+            X[(32 + u0 + j - lo) * XP + ch] = ck[j] * e;
             e *= ca[j];
           }
         }
-      }
-      lds_barrier();
-      // (C / 2h) blocks of h x h entries, TPE threads per entry (consecutive
-      // lanes, strided groups of 4 channels), partial sums reduced across the group
-      constexpr int nent = C * h / 2;
-      constexpr int TPE0 = kPThreads / nent < 1 ? 1 : kPThreads / nent;
-      constexpr int TPE1 = TPE0 > DK / 4 ? DK / 4 : TPE0;
-      constexpr int TPE = TPE1 > 64 ? 64 : TPE1;
-      static_assert(TPE >= 2, "lane groups of two or more");
-      for (int base = 0; base < nent * TPE; base += kPThreads) {
-        const int e = (base + tid) / TPE, sub = (base + tid) % TPE;
-        const bool ok = e < nent;
-        const int blk = ok ? e / (h * h) : 0, w = ok ? e % (h * h) : 0;
-        const int lo = blk * 2 * h, t = lo + h + w / h, j = lo + w % h;
-        float s = 0.f, mm = 0.f;
-        if (ok) {
+      };
+      rescale(std::integral_constant<int, 0>{});
+      rescale(std::integral_constant<int, 1>{});
+      rescale(std::integral_constant<int, 2>{});
+      rescale(std::integral_constant<int, 3>{});
+      rescale(std::integral_constant<int, 4>{});
+    }
+    lds_barrier();
+    {
+      // tile w of the ten (level w / 2, S or M), and tile 8 + w for waves 0
+      // and 1; lane (g, r) takes the 16-byte channel groups 16 s + 4 g of row
+      // r of both operands, K step e of group s being channel 16 s + 4 g + e
+      const int wv = tid >> 6, ln = tid & 63, rr = ln & 15, gg = ln >> 4;
+      for (int tt = wv; tt < 10; tt += kPThreads / 64) {
+        const int L = tt >> 1, h = (C / 2) >> L;
+        const float* A = slev + (L * 3 + (tt & 1)) * 16 * XP + rr * XP + 4 * gg;
+        const float* B = slev + (L * 3 + 2) * 16 * XP + rr * XP + 4 * gg;
+        f32x4 acc = zero4();
 #pragma unroll
-          for (int c4 = sub; c4 < DK / 4; c4 += TPE) {
-            const f32x4 y = *reinterpret_cast<const f32x4*>(sy + j * XP + 4 * c4);
-            const f32x4 x = *reinterpret_cast<const f32x4*>(sx + t * XP + 4 * c4);
-            const f32x4 xq = *reinterpret_cast<const f32x4*>(sxq + t * XP + 4 * c4);
+        for (int s = 0; s < DK / 16; ++s) {
+          const f32x4 a = *reinterpret_cast<const f32x4*>(A + 16 * s);
+          const f32x4 b = *reinterpret_cast<const f32x4*>(B + 16 * s);
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-              s += x[v] * y[v];
-              mm += xq[v] * y[v];
-            }
+          for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], b[e], acc, 0, 0, 0);
+        }
+        // lane (g, r) holds entries (4 g + e, r): x row 4 g + e against y row r
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int ut = 4 * gg + e, blk = ut / h;
+          if (blk == rr / h) {
+            const int lo = 2 * h * blk, t = lo + h + ut % h, j = lo + rr % h;
+            if (tt & 1) sM[t * CP + j] = acc[e];
+            else sS[t * SP + j] = acc[e];
           }
         }
-        s = group_sum<TPE>(s);
-        mm = group_sum<TPE>(mm);
-        if (ok && sub == 0) {
-          sS[t * CP + j] = s;
-          sM[t * CP + j] = mm;
-        }
       }
-      lds_barrier();
-    };
-    static_assert(C == 32, "halving levels below assume 32-position chunks");
-    level(std::integral_constant<int, 16>{});
-    level(std::integral_constant<int, 8>{});
-    level(std::integral_constant<int, 4>{});
-    level(std::integral_constant<int, 2>{});
-    level(std::integral_constant<int, 1>{});
+    }
+    lds_barrier();
     // T = (I + B)^-1, B = Diag(beta) S strictly lower, unit lower triangular,
     // by 16 x 16 blocks: the diagonal blocks T11 = (I + B11)^-1 and
     // T22 = (I + B22)^-1 by forward substitution, one column per thread held in
     // registers (T[i][j] = -beta_i sum_{l < i} S[i][l] T[l][j] for i > j; the
-    // rows of S are read by every lane at once), then T21 = -T22 (B21 T11) as
-    // two 16 x 16 products, one entry per thread.
+    // block's rows of S and its betas are read into registers first, 16 bytes
+    // at a time and the same by every lane), then T21 = -T22 (B21 T11) as two
+    // 16 x 16 products, one entry per thread.
     constexpr int HB = C / 2;
+    static_assert(HB % 4 == 0, "whole 16-byte groups per block row");
     if (tid < C) {
       const int o = (tid / HB) * HB, j = tid % HB;   // the block's first row, the column in it
+      f32x4 bq[HB / 4];
+#pragma unroll
+      for (int v = 0; v < HB / 4; ++v) bq[v] = *reinterpret_cast<const f32x4*>(sb + o + 4 * v);
       float tc[HB];
 #pragma unroll
       for (int i = 0; i < HB; ++i) {
+        f32x4 srow[HB / 4];   // S(o + i, o + 4 v ...), v <= (i - 1) / 4
+#pragma unroll
+        for (int v = 0; v < (i + 3) / 4; ++v) srow[v] = *reinterpret_cast<const f32x4*>(sS + (o + i) * SP + o + 4 * v);
         float acc = 0.f;
 #pragma unroll
-        for (int l = 0; l < i; ++l) acc += sS[(o + i) * CP + o + l] * tc[l];
-        tc[i] = i > j ? -sb[o + i] * acc : (i == j ? 1.f : 0.f);
+        for (int l = 0; l < i; ++l) acc += srow[l / 4][l % 4] * tc[l];
+        tc[i] = i > j ? -bq[i / 4][i % 4] * acc : (i == j ? 1.f : 0.f);
       }
 #pragma unroll
       for (int i = 0; i < HB; ++i) sT[(o + i) * CP + o + j] = tc[i];
@@ -466,12 +492,12 @@ __global__ __launch_bounds__(kPThreads) void chunk_bwd_prep_kernel(const T* q, c
         for (int i = 0; i < HB; ++i) sT[i * CP + HB + j] = 0.f;   // T12
     }
     lds_barrier();
-    float* sW = sx;   // B21 T11 (the rescaled operands are consumed)
+    float* sW = slev;   // B21 T11 (the level rows are consumed)
     if (tid < HB * HB) {
       const int i = tid / HB, j = tid % HB;
       float acc = 0.f;
 #pragma unroll
-      for (int l = 0; l < HB; ++l) acc += sS[(HB + i) * CP + l] * sT[l * CP + j];
+      for (int l = 0; l < HB; ++l) acc += sS[(HB + i) * SP + l] * sT[l * CP + j];
       sW[i * HB + j] = sb[HB + i] * acc;
     }
     lds_barrier();
@@ -521,7 +547,7 @@ __global__ __launch_bounds__(kPThreads) void chunk_bwd_prep_kernel(const T* q, c
         rc[R::TBT_OFF + fo] = sT[j * CP + i] * sb[i];
       }
       rc[R::T_OFF + e] = sT[i * CP + j];
-      rc[R::S_OFF + e] = sS[i * CP + j];
+      rc[R::S_OFF + e] = sS[i * SP + j];
     }
     if constexpr (RS) {   // M^T, TB as split pairs: 2 row tiles, one K block, 64 lanes each
       static_assert(2 * 2 * 64 <= kPThreads, "one task per thread");
