@@ -205,17 +205,17 @@ template <typename T, int DK, bool RS>
 __global__ __launch_bounds__(kPThreads) void chunk_bwd_prep_kernel(const T* q, const T* k, const T* alpha,
                                                                    const T* beta, float* __restrict__ rec, int T_len,
                                                                    int nchunks, long long total) {
-  constexpr int C = kBC, DKP = DK + 1, CP = C + 1;
+  constexpr int C = kBC, CP = C + 1;
   using R = BwdRec<DK>;
-  // One buffer holds, in turn, the staged q, k and alpha (rows of DKP
-  // floats), then (split record) QG and KR, then the rescaled rows of the five
-  // halving levels (per level 16 x, 16 query and 16 y rows of XP floats,
-  // 16-byte aligned for 4-channel reads), then B21 T11: the staged rows are
-  // read once, into the channel threads' registers and the diagonal of M,
-  // before anything else is written there.
+  // One buffer holds, in turn, the staged q, k and alpha, then (split record)
+  // QG and KR, then the rescaled rows of the five halving levels (per level
+  // 16 x, 16 query and 16 y rows), then B21 T11, all in rows of XP floats,
+  // 16-byte aligned for 4-channel accesses: the staged rows are read once,
+  // into the channel threads' registers and the diagonal of M, before
+  // anything else is written there.
   constexpr int XP = DK + 4;
   static_assert(C == 32, "five halving levels of 16-row tiles");
-  static_assert(DKP <= XP && 3 * C <= 5 * 3 * 16, "the staged rows fit the level rows' buffer");
+  static_assert(3 * C <= 5 * 3 * 16, "the staged rows fit the level rows' buffer");
   __shared__ __align__(16) float slev[5 * 3 * 16 * XP];
   float* const sq = slev;
   float* const sk = slev + C * XP;
@@ -235,20 +235,23 @@ __global__ __launch_bounds__(kPThreads) void chunk_bwd_prep_kernel(const T* q, c
   // previous chunk is computed, and the barriers wait for LDS traffic only
   // (the kernel reads no global memory that it writes), so the fetch and the
   // record stores stay in flight across them.
-  constexpr int NK = (C * DK + kPThreads - 1) / kPThreads;
-  T xq[NK], xk[NK], xa[NK], xb;   // the fetched chunk's q, k, alpha and beta
+  // Thread tid fetches the 8 consecutive channels 8 tid ... of row 8 tid / DK
+  // of q, k and alpha (16 bytes each in bf16) and beta of row tid.
+  static_assert(C * DK <= 8 * kPThreads && DK % 8 == 0, "one group of 8 channels per thread");
+  struct alignas(16) G8 {
+    T v[8];
+  };
+  G8 xq, xk, xa;   // the fetched chunk's q, k and alpha
+  T xb;            // and beta
   auto fetch = [&](long long chunk) __attribute__((always_inline)) {
     const long long bh = chunk / nchunks;
     const int c = (int)(chunk % nchunks), t0 = c * C, cv = min(C, T_len - t0);
     const long long row0 = bh * (long long)T_len + t0;
-#pragma unroll
-    for (int i = 0; i < NK; ++i) {
-      const int e = tid + i * kPThreads, t = e / DK, ch = e % DK;
-      const size_t gi = e < C * DK && t < cv ? (size_t)(row0 + t) * DK + ch : 0;
-      xq[i] = q[gi];
-      xk[i] = k[gi];
-      xa[i] = alpha[gi];
-    }
+    const int t = 8 * tid / DK, ch = 8 * tid % DK;
+    const size_t gi = 8 * tid < C * DK && t < cv ? (size_t)(row0 + t) * DK + ch : 0;
+    xq = *reinterpret_cast<const G8*>(q + gi);
+    xk = *reinterpret_cast<const G8*>(k + gi);
+    xa = *reinterpret_cast<const G8*>(alpha + gi);
     xb = beta[row0 + (tid < cv ? tid : 0)];
   };
   if (blockIdx.x < total) fetch(blockIdx.x);
@@ -259,15 +262,21 @@ __global__ __launch_bounds__(kPThreads) void chunk_bwd_prep_kernel(const T* q, c
     asm volatile("" : "+v"(tid));
     const int cv = min(C, T_len - (int)(chunk % nchunks) * C);
     // rows past a ragged end are identity steps: gate 1, no key, query or beta
+    if (8 * tid < C * DK) {
+      const int t = 8 * tid / DK, o = t * XP + 8 * tid % DK;
+      const bool ok = t < cv;
 #pragma unroll
-    for (int i = 0; i < NK; ++i) {
-      const int e = tid + i * kPThreads, t = e / DK;
-      if (e < C * DK) {
-        const int o = t * DKP + e % DK;
-        const bool ok = t < cv;
-        sq[o] = ok ? to_f32(xq[i]) : 0.f;
-        sk[o] = ok ? to_f32(xk[i]) : 0.f;
-        sa[o] = ok ? to_f32(xa[i]) : 1.f;
+      for (int hf = 0; hf < 2; ++hf) {
+        f32x4 vq, vk, va;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          vq[e] = ok ? to_f32(xq.v[4 * hf + e]) : 0.f;
+          vk[e] = ok ? to_f32(xk.v[4 * hf + e]) : 0.f;
+          va[e] = ok ? to_f32(xa.v[4 * hf + e]) : 1.f;
+        }
+        *reinterpret_cast<f32x4*>(sq + o + 4 * hf) = vq;
+        *reinterpret_cast<f32x4*>(sk + o + 4 * hf) = vk;
+        *reinterpret_cast<f32x4*>(sa + o + 4 * hf) = va;
       }
     }
     if (tid < C) sb[tid] = tid < cv ? to_f32(xb) : 0.f;
@@ -286,9 +295,9 @@ __global__ __launch_bounds__(kPThreads) void chunk_bwd_prep_kernel(const T* q, c
     if (tid < DK) {
 #pragma unroll
       for (int t = 0; t < C; ++t) {
-        ca[t] = sa[t * DKP + tid];
-        ck[t] = sk[t * DKP + tid];
-        cq[t] = sq[t * DKP + tid];
+        ca[t] = sa[t * XP + tid];
+        ck[t] = sk[t * XP + tid];
+        cq[t] = sq[t * XP + tid];
       }
     }
     {   // diagonal of M (G = 1): kPThreads / C threads per row
@@ -297,7 +306,7 @@ __global__ __launch_bounds__(kPThreads) void chunk_bwd_prep_kernel(const T* q, c
       const int t = tid / TPE, sub = tid % TPE;
       float d = 0.f;
 #pragma unroll
-      for (int i = 0; i < DK / TPE; ++i) d += sq[t * DKP + sub + i * TPE] * sk[t * DKP + sub + i * TPE];
+      for (int i = 0; i < DK / TPE; ++i) d += sq[t * XP + sub + i * TPE] * sk[t * XP + sub + i * TPE];
       d = group_sum<TPE>(d);
       if (sub == 0) sM[t * CP + t] = d;
     }
@@ -336,74 +345,25 @@ __global__ __launch_bounds__(kPThreads) void chunk_bwd_prep_kernel(const T* q, c
         }
       }
     }
-    if constexpr (RS) {
-      // KG, KR (C x DK) and QG^T, KR^T (DK x C) as split fragment pairs,
-      // every thread writing whole 16-byte hi and lo fragments: a task is one
-      // lane of one pair (row tile rt, K block kb) of one field.  (Barriers
-      // for the LDS data only: the record stores drain meanwhile.)
-      lds_barrier();
-      constexpr int NT = 4 * DK;   // tasks per field: 64 lanes x (2 (DK / 32) pairs, or DK / 16)
-      static_assert(NT % 64 == 0, "whole waves per field");
-#pragma unroll
-      for (int i = 0; i < (4 * NT + kPThreads - 1) / kPThreads; ++i) {
-        const int task0 = tid + i * kPThreads, f0 = task0 / NT;
-        // fields 0 KG, 1 KR, 3 QG^T, 4 KR^T (2, KG^T, is replaced by -K~G^T below)
-        const int field = f0 < 2 ? f0 : f0 + 1, task = task0 + (f0 < 2 ? 0 : NT);
-        const int pair = (task % NT) / 64, ln = task % 64;
-        if (task0 >= 4 * NT) break;
-        const int gg = ln >> 4, rr = ln & 15;
-        float v8[8];
-        int off, kd, rt, kb;
-        // (one LDS array per call: a pointer chosen at run time would be a flat access)
-        auto rows = [&](const float* src) __attribute__((always_inline)) {   // row t, K = channels
-          const float* row = src + (16 * rt + rr) * XP + 32 * kb;
-          const f32x4 a = *reinterpret_cast<const f32x4*>(row + 4 * gg), b = *reinterpret_cast<const f32x4*>(row + 16 + 4 * gg);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            v8[e] = a[e];
-            v8[4 + e] = b[e];
-          }
-        };
-        auto cols = [&](const float* src) __attribute__((always_inline)) {   // row = channel, K = positions
-#pragma unroll
-          for (int e = 0; e < 8; ++e) v8[e] = src[kappa<bf16_t>(gg, e) * XP + 16 * rt + rr];
-        };
-        if (field < 2) {   // KG, KR
-          rt = pair / (DK / 32);
-          kb = pair % (DK / 32);
-          off = field == 0 ? R::KG_OFF : R::KR_OFF;
-          kd = DK;
-          if (field == 0) rows(skg);
-          else rows(skr);
-        } else {           // KG^T, QG^T, KR^T
-          rt = pair;
-          kb = 0;
-          off = field == 2 ? R::KGT_OFF : field == 3 ? R::QGT_OFF : R::KRT_OFF;
-          kd = C;
-          if (field == 3) cols(sqg);
-          else cols(skr);
-        }
-        u32x4 h, l;
-        split8(v8, h, l);
-        float* tile = rc + off + (rt * (kd / 16) + 2 * kb) * 256 + 4 * ln;
-        *reinterpret_cast<u32x4*>(tile) = h;
-        *reinterpret_cast<u32x4*>(tile + 256) = l;
-      }
-      lds_barrier();   // the level rows below overwrite QG and KR
-    }
     // S and M below the diagonal by recursive halving.  Level h (16, 8, 4, 2,
     // 1) splits the chunk into blocks of 2h positions around their midpoints
     // m: entry (t, j) with t in the upper and j in the lower half of one block
     // is sum over channels of (x_t G(t, m)) (y_j G(m, j)), every factor a
-    // product of at most h gates.  The channel threads write all five levels'
-    // rescaled rows at once; then each level is two 16 x 16 products over the
-    // channels (rows u = block * h + offset in the half: S from the x rows,
-    // M from the query rows, both against the y rows), on fp32 matrix cores,
-    // of which the blocks' h x h diagonal quadrants are the level's entries.
-    if (tid < DK) {
-      const int ch = tid;
-      auto rescale = [&](auto ll) __attribute__((always_inline)) {
+    // product of at most h gates.  The channel threads write each level's
+    // rescaled rows; each level is then two 16 x 16 products over the channels
+    // (rows u = block * h + offset in the half: S from the x rows, M from the
+    // query rows, both against the y rows), on fp32 matrix cores, of which the
+    // blocks' h x h diagonal quadrants are the level's entries.  Levels 4, 2
+    // and 1 sit past QG and KR in the shared buffer: their rows are written
+    // while the other waves write the split record, and their products run
+    // while the rows of levels 16 and 8 are written over QG and KR.
+    {
+      constexpr int CW = (DK + 63) / 64;   // the waves that hold channel threads
+      static_assert(kPThreads / 64 - CW >= 6, "six whole waves beside the channel threads");
+      const int wv = tid >> 6, ln = tid & 63, rr = ln & 15, gg = ln >> 4;
+      auto rescale = [&](auto ll) __attribute__((always_inline)) {   // level ll's rows (channel threads)
         constexpr int L = decltype(ll)::value, h = (C / 2) >> L;
+        const int ch = tid;
         float* X = slev + L * 3 * 16 * XP;
 #pragma unroll
         for (int lo = 0; lo < C; lo += 2 * h) {
@@ -423,19 +383,10 @@ __global__ __launch_bounds__(kPThreads) void chunk_bwd_prep_kernel(const T* q, c
           }
         }
       };
-      rescale(std::integral_constant<int, 0>{});
-      rescale(std::integral_constant<int, 1>{});
-      rescale(std::integral_constant<int, 2>{});
-      rescale(std::integral_constant<int, 3>{});
-      rescale(std::integral_constant<int, 4>{});
-    }
-    lds_barrier();
-    {
-      // tile w of the ten (level w / 2, S or M), and tile 8 + w for waves 0
-      // and 1; lane (g, r) takes the 16-byte channel groups 16 s + 4 g of row
-      // r of both operands, K step e of group s being channel 16 s + 4 g + e
-      const int wv = tid >> 6, ln = tid & 63, rr = ln & 15, gg = ln >> 4;
-      for (int tt = wv; tt < 10; tt += kPThreads / 64) {
+      // tile tt (level tt / 2; S for even tt, M for odd) by one whole wave:
+      // lane (g, r) takes the 16-byte channel groups 16 s + 4 g of row r of
+      // both operands, K step e of group s being channel 16 s + 4 g + e
+      auto tile = [&](int tt) __attribute__((always_inline)) {
         const int L = tt >> 1, h = (C / 2) >> L;
         const float* A = slev + (L * 3 + (tt & 1)) * 16 * XP + rr * XP + 4 * gg;
         const float* B = slev + (L * 3 + 2) * 16 * XP + rr * XP + 4 * gg;
@@ -457,16 +408,87 @@ __global__ __launch_bounds__(kPThreads) void chunk_bwd_prep_kernel(const T* q, c
             else sS[t * SP + j] = acc[e];
           }
         }
+      };
+      if constexpr (RS) lds_barrier();   // KG, QG and KR are in LDS
+      if (tid < DK) {
+        rescale(std::integral_constant<int, 2>{});
+        rescale(std::integral_constant<int, 3>{});
+        rescale(std::integral_constant<int, 4>{});
+      } else if constexpr (RS) {
+        // KG, KR (C x DK) and QG^T, KR^T (DK x C) as split fragment pairs,
+        // the threads past the channel waves writing whole 16-byte hi and lo
+        // fragments: a task is one lane of one pair (row tile rt, K block kb)
+        // of one field.  (Barriers for the LDS data only: the record stores
+        // drain meanwhile.)
+        constexpr int NT = 4 * DK;   // tasks per field: 64 lanes x (2 (DK / 32) pairs, or DK / 16)
+        constexpr int NWT = kPThreads - 64 * CW;
+        static_assert(NT % 64 == 0 && NWT % 64 == 0, "whole waves per field");
+        const int wt = tid - 64 * CW;
+#pragma unroll
+        for (int i = 0; i < (4 * NT + NWT - 1) / NWT; ++i) {
+          const int task0 = wt + i * NWT, f0 = task0 / NT;
+          // fields 0 KG, 1 KR, 3 QG^T, 4 KR^T (2, KG^T, is replaced by -K~G^T below)
+          const int field = f0 < 2 ? f0 : f0 + 1, task = task0 + (f0 < 2 ? 0 : NT);
+          const int pair = (task % NT) / 64, ln = task % 64;
+          if (task0 >= 4 * NT) break;
+          const int gg = ln >> 4, rr = ln & 15;
+          float v8[8];
+          int off, kd, rt, kb;
+          // (one LDS array per call: a pointer chosen at run time would be a flat access)
+          auto rows = [&](const float* src) __attribute__((always_inline)) {   // row t, K = channels
+            const float* row = src + (16 * rt + rr) * XP + 32 * kb;
+            const f32x4 a = *reinterpret_cast<const f32x4*>(row + 4 * gg), b = *reinterpret_cast<const f32x4*>(row + 16 + 4 * gg);
+  #pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              v8[e] = a[e];
+              v8[4 + e] = b[e];
+            }
+          };
+          auto cols = [&](const float* src) __attribute__((always_inline)) {   // row = channel, K = positions
+  #pragma unroll
+            for (int e = 0; e < 8; ++e) v8[e] = src[kappa<bf16_t>(gg, e) * XP + 16 * rt + rr];
+          };
+          if (field < 2) {   // KG, KR
+            rt = pair / (DK / 32);
+            kb = pair % (DK / 32);
+            off = field == 0 ? R::KG_OFF : R::KR_OFF;
+            kd = DK;
+            if (field == 0) rows(skg);
+            else rows(skr);
+          } else {           // KG^T, QG^T, KR^T
+            rt = pair;
+            kb = 0;
+            off = field == 2 ? R::KGT_OFF : field == 3 ? R::QGT_OFF : R::KRT_OFF;
+            kd = C;
+            if (field == 3) cols(sqg);
+            else cols(skr);
+          }
+          u32x4 h, l;
+          split8(v8, h, l);
+          float* tile = rc + off + (rt * (kd / 16) + 2 * kb) * 256 + 4 * ln;
+          *reinterpret_cast<u32x4*>(tile) = h;
+          *reinterpret_cast<u32x4*>(tile + 256) = l;
+        }
       }
+      lds_barrier();   // the rows of levels 4, 2 and 1 are written; QG and KR are read
+      if (tid < DK) {
+        rescale(std::integral_constant<int, 0>{});
+        rescale(std::integral_constant<int, 1>{});
+      } else if (wv >= CW && wv < CW + 6) {
+        tile(4 + wv - CW);
+      }
+      lds_barrier();
+      if (wv < 4) tile(wv);   // levels 16 and 8
+      lds_barrier();
     }
-    lds_barrier();
     // T = (I + B)^-1, B = Diag(beta) S strictly lower, unit lower triangular,
     // by 16 x 16 blocks: the diagonal blocks T11 = (I + B11)^-1 and
     // T22 = (I + B22)^-1 by forward substitution, one column per thread held in
-    // registers (T[i][j] = -beta_i sum_{l < i} S[i][l] T[l][j] for i > j; the
-    // block's rows of S and its betas are read into registers first, 16 bytes
-    // at a time and the same by every lane), then T21 = -T22 (B21 T11) as two
-    // 16 x 16 products, one entry per thread.
+    // registers (T[i][j] = -beta_i sum_{l < i} S[i][l] T[l][j] for i > j; each
+    // row of S is read as the solve reaches it, 16 bytes at a time and the
+    // same by every lane), then T21 = -T22 (B21 T11) as two 16 x 16 products,
+    // one entry per thread.  Meanwhile the waves past the first store S and
+    // M^T, which are final, to the record.
     constexpr int HB = C / 2;
     static_assert(HB % 4 == 0, "whole 16-byte groups per block row");
     if (tid < C) {
@@ -490,6 +512,28 @@ __global__ __launch_bounds__(kPThreads) void chunk_bwd_prep_kernel(const T* q, c
       if (o == 0)
 #pragma unroll
         for (int i = 0; i < HB; ++i) sT[i * CP + HB + j] = 0.f;   // T12
+    } else if (tid >= 64) {
+      if constexpr (RS) {
+        if (tid < 3 * 64) {   // M^T as split pairs: 2 row tiles x 64 lanes
+          const int rt = tid / 64 - 1, ln = tid % 64, gg = ln >> 4, i = 16 * rt + (ln & 15);
+          float v8[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v8[e] = sM[kappa<bf16_t>(gg, e) * CP + i];
+          u32x4 h, l;
+          split8(v8, h, l);
+          float* tile = rc + R::MT_OFF + (rt * (C / 16)) * 256 + 4 * ln;
+          *reinterpret_cast<u32x4*>(tile) = h;
+          *reinterpret_cast<u32x4*>(tile + 256) = l;
+        } else {
+          for (int e = tid - 3 * 64; e < C * C; e += kPThreads - 3 * 64) rc[R::S_OFF + e] = sS[(e / C) * SP + e % C];
+        }
+      } else {
+        for (int e = tid - 64; e < C * C; e += kPThreads - 64) {
+          const int i = e / C, j = e % C;
+          rc[R::MT_OFF + frag_off(i, j, C)] = sM[j * CP + i];
+          rc[R::S_OFF + e] = sS[i * SP + j];
+        }
+      }
     }
     lds_barrier();
     float* sW = slev;   // B21 T11 (the level rows are consumed)
@@ -540,28 +584,28 @@ __global__ __launch_bounds__(kPThreads) void chunk_bwd_prep_kernel(const T* q, c
     }
     for (int e = tid; e < C * C; e += kPThreads) {
       const int i = e / C, j = e % C;
-      const int fo = frag_off(i, j, C);
       if constexpr (!RS) {
-        rc[R::MT_OFF + fo] = sM[j * CP + i];
+        const int fo = frag_off(i, j, C);
         rc[R::TB_OFF + fo] = sT[i * CP + j] * sb[j];
         rc[R::TBT_OFF + fo] = sT[j * CP + i] * sb[i];
       }
       rc[R::T_OFF + e] = sT[i * CP + j];
-      rc[R::S_OFF + e] = sS[i * SP + j];
     }
-    if constexpr (RS) {   // M^T, TB as split pairs: 2 row tiles, one K block, 64 lanes each
-      static_assert(2 * 2 * 64 <= kPThreads, "one task per thread");
-      if (tid < 2 * 2 * 64) {
-        const int field = tid / 128, rt = (tid / 64) % 2, ln = tid % 64, gg = ln >> 4, i = 16 * rt + (ln & 15);
+    if constexpr (RS) {   // TB as split pairs: 2 row tiles, one K block, 64 lanes each
+      if (tid < 2 * 64) {
+        // the rounded product T beta is split: its lo part is not the exact
+        // product's, which fusing it into the split's subtraction would give
+#pragma clang fp contract(off)
+        const int rt = tid / 64, ln = tid % 64, gg = ln >> 4, i = 16 * rt + (ln & 15);
         float v8[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int j = kappa<bf16_t>(gg, e);
-          v8[e] = field == 0 ? sM[j * CP + i] : field == 1 ? sT[i * CP + j] * sb[j] : sT[j * CP + i] * sb[i];
+          v8[e] = sT[i * CP + j] * sb[j];
         }
         u32x4 h, l;
         split8(v8, h, l);
-        float* tile = rc + (field == 0 ? R::MT_OFF : field == 1 ? R::TB_OFF : R::TBT_OFF) + (rt * (C / 16)) * 256 + 4 * ln;
+        float* tile = rc + R::TB_OFF + (rt * (C / 16)) * 256 + 4 * ln;
         *reinterpret_cast<u32x4*>(tile) = h;
         *reinterpret_cast<u32x4*>(tile + 256) = l;
       }
