@@ -19,9 +19,11 @@
 // the sequential passes and of grad's value-slice loop take split bf16 pairs,
 // about 16 bits, on bf16 matrix cores):
 //   prep    (resident workgroups looping over chunks) S, M by recursive
-//           halving, T by forward substitution, TB, KG, KR, QG, Gamma_C -> a
-//           per-chunk record (with the transposes the sequential kernels
-//           contract along);
+//           halving (every level's rescaled rows written at once, each
+//           level's cross blocks as 16 x 16 fp32 matrix-core tiles), T by
+//           forward substitution, TB, KG, KR, QG, Gamma_C -> a per-chunk
+//           record (with the transposes the sequential kernels contract
+//           along);
 //   states  (sequential, per head and 16-column value slice; two slices per
 //           wave with split products once one per wave would put two
 //           workgroups on every CU) chunk-start states;
